@@ -1,0 +1,437 @@
+"""Pins of the fp64 oracle against what the pages and mathematics fix (CPU only).
+
+Every check here is independent of the oracle's own formulas: closed forms, library
+routines the oracle does not call, brute force, literature values and invariants.
+"""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy import integrate, linalg, stats
+
+import oracle as O
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _noise_free_tokens(q, lam):
+    """2d tokens +-sqrt(d) sqrt(lambda_i) q_i: mean 0, covariance exactly Q Lambda Q^T."""
+    d = q.shape[0]
+    cols = [math.sqrt(d) * math.sqrt(lam[i]) * q[:, i] for i in range(d)]
+    return np.array(cols + [-c for c in cols])
+
+
+# ---------------------------------------------------------------- statistics / rotations
+def test_calib_stats_matches_numpy_cov():
+    x = synth.draw(1, 0, 0, synth.K, "calib", 1024, dtype="f32")
+    mu, c = O.calib_stats(x)
+    assert np.allclose(mu, np.mean(x.astype(np.float64), axis=0), rtol=0, atol=1e-13)
+    assert np.allclose(c, np.cov(x.astype(np.float64), rowvar=False, bias=True), rtol=1e-12, atol=1e-15)
+
+
+def test_klt_orthogonal_and_decorrelating():
+    x = synth.draw(2, 0, 3, synth.V, "calib", 1024, dtype="bf16")
+    mu, c = O.calib_stats(x)
+    r, s2 = O.rotation_klt(c)
+    d = c.shape[0]
+    assert np.abs(r @ r.T - np.eye(d)).max() < 1e-10
+    rc = r @ c @ r.T
+    assert np.abs(rc - np.diag(np.diag(rc))).max() < 1e-10 * np.abs(c).max()
+    assert np.allclose(np.diag(rc), s2, rtol=0, atol=1e-12 * s2.max())
+    assert abs(np.trace(c) - s2.sum()) < 1e-12 * np.trace(c)
+    assert np.all(np.diff(s2) <= 0)
+    # sign rule: largest-magnitude entry of each row is positive
+    assert np.all(r[np.arange(d), np.argmax(np.abs(r), axis=1)] > 0)
+
+
+def test_klt_noise_free_closed_form():
+    q, lam, _ = synth.basis(1, 0, 0, synth.K)
+    x = _noise_free_tokens(q, lam)
+    mu, c = O.calib_stats(x)
+    assert np.abs(mu).max() < 1e-14
+    r, s2 = O.rotation_klt(c)
+    assert np.abs(s2 - lam).max() < 1e-12
+    assert np.abs(np.abs(r @ q) - np.eye(128)).max() < 1e-10
+
+
+def test_wht_matches_scipy_hadamard():
+    rng = np.random.default_rng(0)
+    a = rng.standard_normal((128, 128))
+    c = a @ a.T
+    r, s2 = O.rotation_wht(c)
+    h = linalg.hadamard(128) / math.sqrt(128)
+    assert np.array_equal(r, h)
+    assert np.abs(r @ r.T - np.eye(128)).max() < 1e-12
+    e0 = np.zeros(128)
+    e0[0] = 1.0
+    assert np.allclose(r @ e0, np.full(128, 1 / math.sqrt(128)), rtol=0, atol=1e-15)
+    assert np.allclose(s2, np.diag(h @ c @ h.T), rtol=1e-12)
+
+
+def test_wht_flattens_variances_klt_compacts():
+    q, lam, _ = synth.basis(4, 0, 0, synth.K)
+    c = q @ np.diag(lam) @ q.T
+    _, s2w = O.rotation_wht(c)
+    _, s2k = O.rotation_klt(c)
+    assert s2w.max() / s2w.min() < 50.0          # Hadamard equalises variances
+    assert s2k.max() / s2k.min() > 1000.0        # the KLT compacts energy
+    assert s2k[:16].sum() / s2k.sum() > 0.85
+
+
+def test_identity_rotation():
+    c = np.diag(np.arange(1.0, 9.0))
+    r, s2 = O.rotation_identity(c)
+    assert np.array_equal(r, np.eye(8)) and np.array_equal(s2, np.arange(1.0, 9.0))
+
+
+# ---------------------------------------------------------------- water-filling
+def test_budget_integerisation():
+    assert [O.bits_budget(b, 128) for b in (2.0, 2.76, 4.0, 1.33)] == [256, 353, 512, 170]
+
+
+def _check_certificate(s2, bits, max_bits=8):
+    d = len(s2)
+    for i in range(d):
+        if bits[i] == 0:
+            continue
+        for j in range(d):
+            if bits[j] >= max_bits:
+                continue
+            # moving one bit from i to j cannot help
+            gain_j = s2[j] * 4.0 ** (-bits[j])             # marginal value of j's next bit
+            loss_i = s2[i] * 4.0 ** (-(bits[i] - 1))       # value of i's last bit
+            assert gain_j <= loss_i * (1 + 1e-15)
+
+
+@pytest.mark.parametrize("budget", [0, 1, 37, 170, 256, 353, 512, 1000, 1024])
+def test_waterfill_sum_range_certificate(budget):
+    x = synth.draw(2, 0, 0, synth.K, "calib", 1024, dtype="bf16")
+    _, c = O.calib_stats(x)
+    _, s2 = O.rotation_klt(c)
+    b = O.waterfill_bits(s2, budget)
+    assert b.sum() == budget and b.min() >= 0 and b.max() <= 8
+    assert np.all(np.diff(b) <= 0)       # descending variances -> non-increasing bits
+    _check_certificate(s2, b)
+
+
+def test_waterfill_bruteforce_d4():
+    rng = np.random.default_rng(7)
+    for trial in range(6):
+        s2 = np.sort(rng.lognormal(0, 2, 4))[::-1]
+        if trial == 5:
+            s2 = np.array([1.0, 0.25, 0.25, 0.0])     # exact ties and a dead channel
+        for budget in range(0, 33):
+            best = min(
+                (a for a in itertools.product(range(9), repeat=4) if sum(a) == budget),
+                key=lambda a: sum(s2[i] * 4.0 ** (-a[i]) for i in range(4)))
+            got = O.waterfill_bits(s2, budget)
+            dist_best = sum(s2[i] * 4.0 ** (-best[i]) for i in range(4))
+            dist_got = sum(s2[i] * 4.0 ** (-got[i]) for i in range(4))
+            assert dist_got <= dist_best * (1 + 1e-15) + 1e-300
+
+
+def test_waterfill_tie_rule_prefers_lower_channel():
+    s2 = np.array([1.0, 1.0, 1.0])
+    assert list(O.waterfill_bits(s2, 4)) == [2, 1, 1]
+    s2 = np.array([1.0, 4.0])            # 4 * 4^-1 == 1 * 4^0: ties between (1,1) and (0,0)
+    assert list(O.waterfill_bits(s2, 2)) == [1, 1]
+
+
+def test_waterfill_vs_continuous_closed_form():
+    rng = np.random.default_rng(3)
+    for _ in range(40):
+        d = 128
+        s2 = np.sort(rng.lognormal(0, 2.5, d))[::-1]
+        budget = int(rng.integers(20, 600))
+        theta, dist, rate = O.waterfill_theta(s2, budget)
+        assert abs(rate.sum() - budget) < 1e-9
+        assert np.allclose(dist, np.minimum(theta, s2), rtol=0, atol=0)
+        b = O.waterfill_bits(s2, budget)
+        unc = (b < 8) & (b > 0)
+        assert np.all(np.abs(b[unc] - rate[unc]) <= 1.0 + 1e-12)
+
+
+def test_waterfill_noise_free_histograms():
+    """Histograms on sigma^2 = i^-1.5 (derived with the tie rule; two budgets hit exact ties)."""
+    s2 = synth.spectrum(128)
+    want = {256: {6: 1, 5: 4, 4: 7, 3: 19, 2: 48, 1: 49},
+            353: {7: 1, 6: 2, 5: 6, 4: 15, 3: 36, 2: 68},
+            512: {8: 1, 7: 4, 6: 7, 5: 19, 4: 48, 3: 49},
+            170: {6: 1, 5: 1, 4: 4, 3: 10, 2: 25, 1: 63, 0: 24}}
+    for budget, hist in want.items():
+        b = O.waterfill_bits(s2, budget)
+        got = {int(k): int(v) for k, v in zip(*np.unique(b, return_counts=True))}
+        assert got == hist, (budget, got)
+
+
+def test_waterfill_rejects_bad_budget():
+    with pytest.raises(ValueError):
+        O.waterfill_bits(np.ones(4), 33)
+    with pytest.raises(ValueError):
+        O.waterfill_bits(np.ones(4), -1)
+
+
+# ---------------------------------------------------------------- quantizer step g(b)
+def test_g1_closed_form():
+    assert abs(O.optimal_step(1) - 2 * math.sqrt(2 / math.pi)) < 1e-14
+    assert abs(O.uniform_quantizer_mse(1, O.optimal_step(1)) - (1 - 2 / math.pi)) < 1e-14
+
+
+def test_g_matches_max_1960_table():
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "max1960_uniform_gaussian.txt"))
+            if l.strip() and not l.startswith("#")]
+    for b, _levels, step in rows:
+        assert abs(O.optimal_step(int(b)) - float(step)) <= 6e-4 * float(step)
+
+
+@pytest.mark.parametrize("b", range(1, 9))
+def test_mse_closed_form_vs_quadrature_and_minimum(b):
+    g = O.optimal_step(b)
+    levels = 2 ** b
+
+    def q(z):
+        k = np.clip(np.floor(z / g + levels / 2), 0, levels - 1)
+        return (k - levels / 2 + 0.5) * g
+
+    edges = [(k - levels / 2) * g for k in range(1, levels)]
+    pts = [-np.inf] + edges + [np.inf]
+    quad = sum(integrate.quad(lambda z: (z - q(0.5 * (a + c) if np.isfinite(a) and np.isfinite(c)
+                                                   else (a + 1e-9 if np.isfinite(a) else c - 1e-9))) ** 2
+                              * stats.norm.pdf(z), a, c, epsabs=1e-14, epsrel=1e-12)[0]
+               for a, c in zip(pts[:-1], pts[1:]))
+    assert abs(quad - O.uniform_quantizer_mse(b, g)) < 1e-10
+    for f in (1 - 1e-3, 1 + 1e-3):
+        assert O.uniform_quantizer_mse(b, g * f) > O.uniform_quantizer_mse(b, g)
+    h = 1e-6 * g
+    fd = (O.uniform_quantizer_mse(b, g + h) - O.uniform_quantizer_mse(b, g - h)) / (2 * h)
+    assert abs(fd) < 1e-6
+
+
+def test_mse_monte_carlo():
+    rng = np.random.default_rng(11)
+    z = rng.standard_normal(2_000_000)
+    for b in (1, 2, 3, 4, 6, 8):
+        g = O.optimal_step(b)
+        levels = 2 ** b
+        k = np.clip(np.floor(z / g + levels / 2), 0, levels - 1)
+        e2 = (z - (k - levels / 2 + 0.5) * g) ** 2
+        se = e2.std() / math.sqrt(z.size)
+        assert abs(e2.mean() - O.uniform_quantizer_mse(b, g)) < 3.5 * se
+
+
+# ---------------------------------------------------------------- encode / decode
+def _art_identity(d, bits, delta, o=None):
+    bits = np.asarray(bits)
+    o = np.zeros(d) if o is None else np.asarray(o, dtype=np.float64)
+    delta = np.asarray(delta, dtype=np.float64)
+    inv = np.where(bits > 0, 1.0 / delta, 0.0)
+    return {"R": np.eye(d), "o": o, "delta": np.where(bits > 0, delta, 0.0), "inv_delta": inv,
+            "bits": bits}
+
+
+def test_encode_edges_go_up_and_special_values():
+    bits = np.array([2, 3, 1, 0])
+    art = _art_identity(4, bits, [0.25, 0.5, 1.0, 1.0])
+    # edges of channel 0 (2 bits, step 1/4, offset 0): -0.25, 0, 0.25
+    x = np.array([[-0.25, 0.0, 0.0, 5.0], [0.0, -1.0, -1e-3, 0.0], [0.25, 1.5, 7.0, 0.0],
+                  [-7.0, -9.0, np.inf, 0.0], [np.nan, np.nan, np.nan, 0.0], [np.inf, -np.inf, 0.0, 0.0]])
+    c = O.encode_codes(x, art)
+    # row 3: channel 2 sees +inf (clamped to the top code); channels 0/1 see -7 + 0*inf = NaN -> 0.
+    # row 5: every channel meets 0*inf = NaN in y = R x, so every code is 0.
+    assert c.tolist() == [[1, 4, 1, 0], [2, 2, 0, 0], [3, 7, 1, 0], [0, 0, 1, 0], [0, 0, 0, 0], [0, 0, 0, 0]]
+
+
+def test_quantization_error_bounded_by_half_step():
+    x = synth.draw(1, 0, 0, synth.K, "calib", 1024, dtype="f32")
+    art = O.calibrate(x, "klt", 2.0)
+    xc = synth.draw(1, 0, 0, synth.K, "context", 2048, dtype="f32")
+    codes = O.encode_codes(xc, art)
+    y = xc.astype(np.float64) @ art["R"].T
+    yh = O.dequantize(codes, art)
+    bits = art["bits"]
+    top = (1 << bits) - 1
+    for i in np.nonzero(bits)[0]:
+        inner = (codes[:, i] > 0) & (codes[:, i] < top[i])
+        assert np.all(np.abs(yh[inner, i] - y[inner, i]) <= art["delta"][i] / 2 * (1 + 1e-12))
+    assert np.allclose(yh[:, bits == 0], art["o"][bits == 0][None, :])
+    assert np.allclose(O.reconstruct(codes, art), yh @ art["R"])
+
+
+def test_per_channel_mse_matches_gaussian_closed_form():
+    """On Gaussian data the per-channel MSE is eps(b_i) sigma_i^2 (3.5 SE)."""
+    rng = np.random.default_rng(5)
+    d = 16
+    q = synth.haar_orthogonal(rng, d)
+    lam = np.arange(1, d + 1) ** -1.0
+    cal = (rng.standard_normal((200_000, d)) * np.sqrt(lam)) @ q.T
+    art = O.calibrate(cal, "klt", 3.0)
+    x = (rng.standard_normal((200_000, d)) * np.sqrt(lam)) @ q.T
+    codes = O.encode_codes(x, art)
+    err = (O.dequantize(codes, art) - x @ art["R"].T) ** 2
+    for i in range(d):
+        b = int(art["bits"][i])
+        want = art["sigma2"][i] * (O.uniform_quantizer_mse(b, O.optimal_step(b)) if b else 1.0)
+        se = err[:, i].std() / math.sqrt(err.shape[0])
+        assert abs(err[:, i].mean() - want) < 3.5 * se + 1e-3 * want
+
+
+# ---------------------------------------------------------------- packed formats
+def test_pack_k_hand_example():
+    """d=4 with bits (3,2,1,0): B=6 bits/token; planes (0,0),(0,1),(0,2),(1,0),(1,1),(2,0)."""
+    bits = [3, 2, 1, 0]
+    codes = np.array([[5, 2, 1, 0], [3, 1, 0, 0]])
+    w = O.pack_k(codes, bits)
+    assert w.size == 2 * 6
+    # token 0: c0=5 -> planes 1,0,1 ; c1=2 -> 0,1 ; c2=1 -> 1  => bits 0..5 = 1,0,1,0,1,1
+    # token 1 at bits 6..11: c0=3 -> 1,1,0 ; c1=1 -> 1,0 ; c2=0 -> 0
+    expect = (1 << 0) | (1 << 2) | (1 << 4) | (1 << 5) | (1 << 6) | (1 << 7) | (1 << 9)
+    assert int(w[0]) == expect and not w[1:].any()
+
+
+def test_pack_v_hand_example():
+    bits = [3, 0, 1]
+    # fields: (0,0,w2), (0,2,w1), (2,0,w1) -> words [0,4) w2, [4,6) w1 ch0 bit2, [6,8) w1 ch2
+    codes = np.zeros((64, 3), dtype=np.int64)
+    codes[5, 0] = 6        # t=5: G=0 r=1 m=1 -> low field value 2 at 8m+2r = 10, bit2 at 8+0+1=9
+    codes[37, 2] = 1       # t=37: G=2 r=1 m=1 -> w1 offset 32*1 + 8 + 0 + 1 = 41
+    w = O.pack_v(codes, bits)
+    assert w.size == 8
+    assert int(w[0]) == (2 << 10)
+    assert int(w[4]) == (1 << 9)
+    assert int(w[6 + 1]) == (1 << (41 - 32))
+    assert sum(int(v) != 0 for v in w) == 3
+
+
+def test_pack_roundtrip_and_sizes():
+    rng = np.random.default_rng(1)
+    for bits in ([8, 7, 6, 5, 4, 3, 2, 1, 0, 0, 3], [1] * 11, [2, 0, 0, 8]):
+        bits = np.array(bits)
+        for n in (1, 63, 64, 65, 130):
+            codes = rng.integers(0, 1 << bits, size=(n, bits.size))
+            wk, wv = O.pack_k(codes, bits), O.pack_v(codes, bits)
+            assert wk.size == wv.size == O.packed_words(bits.sum(), n) == -(-n // 64) * 2 * bits.sum()
+            assert np.array_equal(O.unpack_k(wk, bits, n), codes)
+            assert np.array_equal(O.unpack_v(wv, bits, n), codes)
+
+
+def test_v_field_positions_are_bijective():
+    for w in (1, 2, 4):
+        pos = sorted(O.aatc_oracle._v_pos(t, w) for t in range(64))
+        assert pos == list(range(0, 64 * w, w))
+
+
+# ---------------------------------------------------------------- scores and attention
+def test_rotated_domain_scores_equal_plain_scores():
+    x = synth.draw(1, 0, 0, synth.K, "calib", 1024, dtype="f32")
+    art = O.calibrate(x, "klt", 2.0)
+    q = np.random.default_rng(2).standard_normal(128)
+    y = x.astype(np.float64) @ art["R"].T           # full-precision "codes"
+    s_rot = O.rotated_scores(q, art["R"], y)
+    s = x.astype(np.float64) @ q
+    assert np.abs(s_rot - s).max() <= 1e-12 * np.abs(s).max()
+
+
+def test_compressed_score_linear_form():
+    """sum_i alpha_i c_i + beta == scale q.x_hat with alpha = scale (Rq) Delta (affine dequant)."""
+    x = synth.draw(1, 0, 0, synth.K, "calib", 1024, dtype="f32")
+    art = O.calibrate(x, "klt", 2.0)
+    xc = synth.draw(1, 0, 0, synth.K, "context", 300, dtype="f32")
+    codes = O.encode_codes(xc, art)
+    q = np.random.default_rng(4).standard_normal(128)
+    scale = 1 / math.sqrt(128)
+    qt = art["R"] @ q
+    bits = art["bits"]
+    alpha = scale * qt * art["delta"]
+    half = np.where(bits > 0, 2.0 ** (np.maximum(bits, 1) - 1) - 0.5, 0.0)
+    beta = scale * np.sum(qt * (art["o"] - art["delta"] * half))
+    lhs = codes @ alpha + beta
+    rhs = scale * (O.reconstruct(codes, art) @ q)
+    assert np.abs(lhs - rhs).max() <= 1e-12 * np.abs(rhs).max()
+
+
+def test_attention_streaming_equals_direct():
+    rng = np.random.default_rng(9)
+    for n in (1, 5, 64, 1000):
+        q = rng.standard_normal(128) * 3
+        k = rng.standard_normal((n, 128))
+        v = rng.standard_normal((n, 128))
+        o1, l1 = O.attention(q, k, v)
+        o2, l2 = O.attention_streaming(q, k, v, chunk=13)
+        assert np.abs(o1 - o2).max() < 1e-13 and abs(l1 - l2) < 1e-12
+
+
+def test_attention_vs_mpmath():
+    mpmath = pytest.importorskip("mpmath")
+    mpmath.mp.dps = 50
+    rng = np.random.default_rng(10)
+    for n in (1, 3, 16):
+        q = rng.standard_normal(8) * 4
+        k = rng.standard_normal((n, 8))
+        v = rng.standard_normal((n, 8))
+        out, lse = O.attention(q, k, v)
+        s = [mpmath.mpf(1) / mpmath.sqrt(8) * mpmath.fsum(mpmath.mpf(float(q[j])) * mpmath.mpf(float(k[t, j]))
+                                                          for j in range(8)) for t in range(n)]
+        e = [mpmath.e ** st for st in s]
+        z = mpmath.fsum(e)
+        for j in range(8):
+            ref = mpmath.fsum(e[t] * mpmath.mpf(float(v[t, j])) for t in range(n)) / z
+            assert abs(float(ref) - out[j]) < 1e-14 * max(1.0, abs(float(ref)))
+        assert abs(float(mpmath.log(z)) - lse) < 1e-13
+
+
+def test_attention_special_cases():
+    x = synth.draw(1, 0, 0, synth.K, "calib", 1024, dtype="f32")
+    xv = synth.draw(1, 0, 0, synth.V, "calib", 1024, dtype="f32")
+    art_k0 = O.calibrate(x, "klt", 0.0)                  # every K channel at 0 bits
+    art_v0 = O.calibrate(xv, "klt", 0.0)
+    art_v = O.calibrate(xv, "klt", 2.0)
+    ck = O.encode_codes(synth.draw(1, 0, 0, synth.K, "context", 50, dtype="f32"), art_k0)
+    cv = O.encode_codes(synth.draw(1, 0, 0, synth.V, "context", 50, dtype="f32"), art_v)
+    q = np.random.default_rng(1).standard_normal((1, 128))
+    out, _ = O.decode_attention(q, [ck], [cv], [art_k0], [art_v])
+    assert np.allclose(out[0], O.reconstruct(cv, art_v).mean(0), atol=1e-12)
+    cv0 = O.encode_codes(synth.draw(1, 0, 0, synth.V, "context", 50, dtype="f32"), art_v0)
+    art_k = O.calibrate(x, "klt", 2.0)
+    ck2 = O.encode_codes(synth.draw(1, 0, 0, synth.K, "context", 50, dtype="f32"), art_k)
+    out, _ = O.decode_attention(q, [ck2], [cv0], [art_k], [art_v0])
+    assert np.allclose(out[0], art_v0["mu"], atol=1e-12)     # R^T o = mu
+    out, _ = O.decode_attention(q, [ck2[:1]], [cv[:1]], [art_k], [art_v])
+    assert np.allclose(out[0], O.reconstruct(cv[:1], art_v)[0], atol=1e-12)
+
+
+# ---------------------------------------------------------------- token tiers and segments
+def test_token_tiers_budget_monotone_bruteforce():
+    d = 128
+    s2 = synth.spectrum(d)
+    dist = O.tier_distortions([s2, s2], d)
+    assert dist[0] > dist[1] > dist[2] > dist[3] == 0.0
+    a = synth.zipf_mass(5, 0, 0, 4096)
+    tiers = O.token_tiers(a, dist, d, 2.76)
+    assert tiers.sum() * d <= 2.76 * a.size * d
+    order = np.argsort(a)
+    assert np.all(np.diff(tiers[order]) >= 0)        # more attention mass, never fewer bits
+    rng = np.random.default_rng(0)
+    for _ in range(5):
+        a = rng.dirichlet(np.ones(6))
+        lam = float(rng.uniform(1e-6, 1e-3))
+        got = O.aatc_oracle._tiers_at(a * a, dist, lam, d)
+        best = min(itertools.product(O.aatc_oracle.TIERS, repeat=6),
+                   key=lambda ts: (sum(a[t] ** 2 * dist[O.aatc_oracle.TIERS.index(ts[t])] + lam * d * ts[t]
+                                       for t in range(6))))
+        cost = lambda ts: sum(a[t] ** 2 * dist[O.aatc_oracle.TIERS.index(ts[t])] + lam * d * ts[t]
+                              for t in range(6))
+        assert cost(tuple(got)) <= cost(best) * (1 + 1e-12)
+
+
+def test_segment_attention_excludes_evicted():
+    rng = np.random.default_rng(2)
+    k = rng.standard_normal((10, 8))
+    v = rng.standard_normal((10, 8))
+    q = rng.standard_normal(8)
+    keep = np.array([1, 1, 0, 1, 0, 1, 1, 1, 0, 1], dtype=bool)
+    out, lse = O.segment_attention(q, [(k[keep][:3], v[keep][:3]), (k[keep][3:], v[keep][3:])])
+    ref, lref = O.attention(q, k[keep], v[keep])
+    assert np.allclose(out, ref, atol=1e-14) and abs(lse - lref) < 1e-13
