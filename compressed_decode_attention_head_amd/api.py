@@ -1,0 +1,182 @@
+"""Python face of libaatc: the same calls as include/aatc.h on numpy arrays and torch tensors.
+
+Every step of the compression path runs inside libaatc (host solver in C++, device steps in
+HIP kernels).  This module only validates shapes, allocates with torch and passes pointers.
+"""
+import ctypes
+
+import numpy as np
+
+from . import _native as N
+
+__all__ = ["calibrate", "calib_view", "validate", "bits_budget", "packed_bytes", "v_tiles",
+           "CompressedKVCache", "AatcError"]
+
+AatcError = N.AatcError
+
+
+def _np_dtype_code(x):
+    if x.dtype == np.float32:
+        return N.DTYPE["f32"]
+    if x.dtype == np.float64:
+        return N.DTYPE["f64"]
+    if x.dtype == np.uint16:        # raw bf16 bits
+        return N.DTYPE["bf16"]
+    raise TypeError("calibration data must be float32, float64 or bf16 bits (uint16)")
+
+
+def calibrate(x, rotation="klt", bits_per_elem=2.0, max_bits=8, d=128):
+    """aatc_calibrate on host rows x [M, d]; returns the artefact blob (uint8 array)."""
+    L = N.lib()
+    x = np.ascontiguousarray(x)
+    if x.ndim != 2:
+        raise ValueError("x must be [n_calib, d]")
+    p = N.CalibParams(d, N.ROTATION[rotation], float(bits_per_elem), int(max_bits), 0)
+    nbytes = L.aatc_calib_bytes(d) or N.CALIB_DTYPE.itemsize
+    out = np.zeros(nbytes, dtype=np.uint8)
+    N.check(L.aatc_calibrate(ctypes.byref(p), x.ctypes.data, _np_dtype_code(x), x.shape[0], x.shape[1],
+                             out.ctypes.data, out.nbytes))
+    return out
+
+
+def calib_view(blob):
+    """Read-only structured view of a blob (fields as in struct aatc_calib)."""
+    return np.frombuffer(np.asarray(blob, dtype=np.uint8).tobytes()[:N.CALIB_DTYPE.itemsize],
+                         dtype=N.CALIB_DTYPE)[0]
+
+
+def validate(blob):
+    blob = np.ascontiguousarray(blob, dtype=np.uint8)
+    N.check(N.lib().aatc_calib_validate(blob.ctypes.data, blob.nbytes))
+
+
+def v_tiles(blob):
+    blob = np.ascontiguousarray(blob, dtype=np.uint8)
+    return int(N.lib().aatc_calib_v_tiles(blob.ctypes.data))
+
+
+def bits_budget(bits_per_elem, d=128):
+    return int(N.lib().aatc_bits_budget(float(bits_per_elem), d))
+
+
+def packed_bytes(total_bits, n_tokens):
+    return int(N.lib().aatc_packed_bytes(int(total_bits), int(n_tokens)))
+
+
+def _stream_ptr(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+class CompressedKVCache:
+    """One layer's compressed K/V cache on the GPU: per-head artefacts + packed tiles.
+
+    k_blobs / v_blobs: one artefact per KV head (from ``calibrate``).  Memory is
+    [batch][n_kv_heads][capacity/64 tiles][2B words] per tensor (uint32 as torch.int32).
+    """
+
+    def __init__(self, k_blobs, v_blobs, batch, capacity_tokens, device="cuda"):
+        import torch
+        if capacity_tokens % 64:
+            raise ValueError("capacity_tokens must be a multiple of 64")
+        if len(k_blobs) != len(v_blobs) or not k_blobs:
+            raise ValueError("need one K and one V artefact per KV head")
+        for b in list(k_blobs) + list(v_blobs):
+            validate(b)
+        kb = {int(calib_view(b)["total_bits"]) for b in k_blobs}
+        vb = {int(calib_view(b)["total_bits"]) for b in v_blobs}
+        if len(kb) != 1 or len(vb) != 1:
+            raise ValueError("all heads of a tensor must share the bit budget")
+        self.batch, self.n_kv, self.capacity = int(batch), len(k_blobs), int(capacity_tokens)
+        self.k_bits, self.v_bits = kb.pop(), vb.pop()
+        self.v_tiles = max(v_tiles(b) for b in v_blobs)
+        dev = torch.device(device)
+        if dev.type == "cuda" and dev.index is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
+        self.device = dev
+        self.k_blobs_host = [np.asarray(b, dtype=np.uint8) for b in k_blobs]
+        self.v_blobs_host = [np.asarray(b, dtype=np.uint8) for b in v_blobs]
+        self.k_calib = torch.from_numpy(np.concatenate(self.k_blobs_host)).to(self.device)
+        self.v_calib = torch.from_numpy(np.concatenate(self.v_blobs_host)).to(self.device)
+        tiles = self.capacity // 64
+        self.k_codes = torch.zeros(max(4, self.batch * self.n_kv * tiles * 2 * self.k_bits), dtype=torch.int32,
+                                   device=self.device)
+        self.v_codes = torch.zeros(max(4, self.batch * self.n_kv * tiles * 2 * self.v_bits), dtype=torch.int32,
+                                   device=self.device)
+        self._struct = N.Cache(self.batch, self.n_kv, 128, self.k_bits, self.v_bits, self.v_tiles,
+                               self.capacity, self.k_calib.data_ptr(), self.v_calib.data_ptr(),
+                               self.k_codes.data_ptr(), self.v_codes.data_ptr())
+
+    @property
+    def struct(self):
+        return self._struct
+
+    def codes(self, which):
+        """Packed words of one tensor as [batch, n_kv, capacity/64 * 2B] int32 (a view)."""
+        c = self.k_codes if which == 0 else self.v_codes
+        bits = self.k_bits if which == 0 else self.v_bits
+        return c[: self.batch * self.n_kv * (self.capacity // 64) * 2 * bits].view(self.batch, self.n_kv, -1)
+
+    @staticmethod
+    def _dt(t):
+        import torch
+        if t.dtype == torch.float32:
+            return N.DTYPE["f32"]
+        if t.dtype == torch.bfloat16:
+            return N.DTYPE["bf16"]
+        raise TypeError("float32 or bfloat16 tensors only")
+
+    def encode(self, which, x, token_offset=0, stream=None):
+        """aatc_encode: x [batch, n_kv, n, 128] (any strides, channel stride 1)."""
+        if x.dim() != 4 or x.shape[0] != self.batch or x.shape[1] != self.n_kv or x.shape[3] != 128:
+            raise ValueError("x must be [batch, n_kv_heads, n, 128]")
+        if x.stride(3) != 1:
+            raise ValueError("channel stride must be 1")
+        if x.device != self.device:
+            raise ValueError("x must live on the cache's device")
+        st = (ctypes.c_int64 * 3)(x.stride(0), x.stride(1), x.stride(2))
+        N.check(N.lib().aatc_encode(ctypes.byref(self._struct), int(which), x.data_ptr(), self._dt(x), st,
+                                    int(token_offset), int(x.shape[2]), _stream_ptr(stream)))
+
+    def decode(self, which, token_offset, n_tokens, out_dtype="f32", stream=None):
+        """aatc_decode: reconstruction x_hat [batch, n_kv, n, 128]."""
+        import torch
+        dt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+        out = torch.empty((self.batch, self.n_kv, int(n_tokens), 128), dtype=dt, device=self.device)
+        st = (ctypes.c_int64 * 3)(out.stride(0), out.stride(1), out.stride(2))
+        N.check(N.lib().aatc_decode(ctypes.byref(self._struct), int(which), int(token_offset), int(n_tokens),
+                                    out.data_ptr(), N.DTYPE[out_dtype], st, _stream_ptr(stream)))
+        return out
+
+    def workspace_bytes(self, n_q_heads, max_seq_len):
+        return int(N.lib().aatc_decode_attn_workspace_bytes(ctypes.byref(self._struct), int(n_q_heads),
+                                                            int(max_seq_len)))
+
+    def new_workspace(self, n_q_heads, max_seq_len):
+        """Zero-filled decode-attention workspace (each call leaves it zero-filled again)."""
+        import torch
+        return torch.zeros(self.workspace_bytes(n_q_heads, max_seq_len), dtype=torch.uint8, device=self.device)
+
+    def decode_attn(self, q, max_seq_len, seq_lens=None, scale=0.0, workspace=None, out=None, lse=None,
+                    stream=None):
+        """aatc_decode_attn: q [batch, n_q_heads, 128] fp32 -> (out [batch, n_q_heads, 128], lse [batch, n_q])."""
+        import torch
+        if q.dtype != torch.float32 or not q.is_contiguous() or q.dim() != 3 or q.shape[0] != self.batch:
+            raise ValueError("q must be a contiguous fp32 [batch, n_q_heads, 128] tensor")
+        n_q = q.shape[1]
+        if workspace is None:
+            workspace = self.new_workspace(n_q, max_seq_len)
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty((self.batch, n_q), dtype=torch.float32, device=self.device)
+        sl = 0
+        if seq_lens is not None:
+            if seq_lens.dtype != torch.int32 or seq_lens.device != self.device or seq_lens.numel() != self.batch:
+                raise ValueError("seq_lens must be an int32 [batch] tensor on the cache's device")
+            sl = seq_lens.data_ptr()
+        N.check(N.lib().aatc_decode_attn(ctypes.byref(self._struct), q.data_ptr(), int(n_q), sl or None,
+                                         int(max_seq_len), float(scale), out.data_ptr(), lse.data_ptr(),
+                                         workspace.data_ptr(), workspace.numel(), _stream_ptr(stream)))
+        return out, lse

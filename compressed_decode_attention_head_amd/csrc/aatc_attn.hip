@@ -1,0 +1,165 @@
+// Decode attention on the packed cache: host-side plan, validation and launch.
+// The kernel (and the method it implements) is described in aatc_attn_kernel.h.
+#include "aatc_attn_kernel.h"
+
+namespace {
+
+using namespace aatc_attn;
+
+constexpr size_t kLdsLimit = 160 * 1024;
+constexpr size_t kStaticLds = 1024;          // __shared__ scalars of the kernel (rounded up)
+
+int vtiles_bucket(int vt) {
+  if (vt <= 8) return 8;
+  if (vt <= 12) return 12;
+  if (vt <= 16) return 16;
+  if (vt <= 24) return 24;
+  return -1;
+}
+
+int round1k(int64_t x) { return static_cast<int>((x + 1023) / 1024 * 1024); }
+
+struct Plan {
+  int NP, NVB, LIMBS, S, tpw, half, chunk, nbuf, ks, vs;
+  size_t lds;
+  size_t part_bytes, cnt_bytes;
+  bool fits;
+};
+
+// Tiles per wave fill 256 CUs x 8 waves once; each wave keeps as many of its tiles in LDS
+// as fit (all of them when possible, else double-buffered chunks, else single chunks).
+Plan make_plan(const aatc_cache* c, int n_q, int64_t max_seq) {
+  Plan p;
+  const int kb = c->k_bits, vb = c->v_bits;
+  p.NP = kb > 0 ? (kb + 127) / 128 : 1;
+  p.half = (kb > 0 && kb - 128 * (p.NP - 1) <= 64) ? 1 : 0;
+  p.NVB = vtiles_bucket(c->v_tiles);
+  const int group = c->n_kv_heads > 0 ? n_q / c->n_kv_heads : 1;
+  p.LIMBS = group <= 4 ? 3 : 2;
+  const int64_t ntiles = (max_seq + 63) / 64;
+  const int64_t seqs = static_cast<int64_t>(c->batch) * c->n_kv_heads;
+  const int64_t target_waves = 256 * WAVES;
+  int64_t tpw = (ntiles * seqs + target_waves - 1) / target_waves;
+  if (tpw < 1) tpw = 1;
+  if (tpw > 64) tpw = 64;
+  p.tpw = static_cast<int>(tpw);
+  int64_t S = (ntiles + WAVES * tpw - 1) / (WAVES * tpw);
+  if (S < 1) S = 1;
+  p.S = static_cast<int>(S);
+  const size_t fixed = UNION_BYTES + PL_BYTES + kStaticLds;
+  const size_t per_wave = (kLdsLimit - fixed) / WAVES;
+  auto area = [&](int ch, int nbuf) {
+    const int ks = kb > 0 ? round1k(8LL * kb * ch + 16) : 0;
+    const int vs = vb > 0 ? round1k(8LL * vb * ch + 16) : 0;
+    return static_cast<size_t>(nbuf) * (ks + vs);
+  };
+  p.chunk = 1;
+  p.nbuf = 1;
+  p.fits = false;
+  if (area(p.tpw, 1) <= per_wave) {
+    p.chunk = p.tpw;
+    p.nbuf = 1;
+    p.fits = true;
+  } else {
+    for (int ch = p.tpw - 1; ch >= 1; --ch)
+      if (area(ch, 2) <= per_wave) { p.chunk = ch; p.nbuf = 2; p.fits = true; break; }
+    if (!p.fits && area(1, 1) <= per_wave) { p.chunk = 1; p.nbuf = 1; p.fits = true; }
+  }
+  p.ks = kb > 0 ? round1k(8LL * kb * p.chunk + 16) : 0;
+  p.vs = vb > 0 ? round1k(8LL * vb * p.chunk + 16) : 0;
+  // the finalize reuses the tile area for 8 x S slot weights
+  size_t tiles = static_cast<size_t>(WAVES) * p.nbuf * (p.ks + p.vs);
+  if (tiles < static_cast<size_t>(8) * p.S * 4) tiles = static_cast<size_t>(8) * p.S * 4;
+  p.lds = UNION_BYTES + PL_BYTES + tiles;
+  if (p.lds + kStaticLds > kLdsLimit) p.fits = false;
+  p.part_bytes = static_cast<size_t>(seqs) * p.S * 8 * PROW_MAX * 4;
+  p.cnt_bytes = static_cast<size_t>(seqs) * 4;
+  return p;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+bool dispatch(const Plan& p, const AttnArgs& a, dim3 grid, hipStream_t st, hipError_t* err) {
+  bool found = false;
+  switch (p.NP) {
+    case 1: *err = launch_np<1>(p.NVB, p.LIMBS, a, grid, p.lds, st, &found); break;
+    case 2: *err = launch_np<2>(p.NVB, p.LIMBS, a, grid, p.lds, st, &found); break;
+    case 3: *err = launch_np<3>(p.NVB, p.LIMBS, a, grid, p.lds, st, &found); break;
+    case 4: *err = launch_np<4>(p.NVB, p.LIMBS, a, grid, p.lds, st, &found); break;
+  }
+  return found;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t aatc_decode_attn_workspace_bytes(const aatc_cache* c, int32_t n_q_heads, int64_t max_seq_len) {
+  if (!c || max_seq_len < 0 || n_q_heads < 1) return 0;
+  const Plan p = make_plan(c, n_q_heads, max_seq_len);
+  return align256(p.part_bytes) + align256(p.cnt_bytes);
+}
+
+aatc_status aatc_decode_attn(const aatc_cache* c, const float* q, int32_t n_q, const int32_t* seq_lens,
+                             int64_t max_seq, float scale, float* out, float* lse, void* ws, size_t ws_bytes,
+                             void* stream) {
+  aatc::clear_error();
+  if (!c || !q || !out || !ws) return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "null pointer");
+  if (c->d != AATC_D) return aatc::fail(AATC_ERR_UNSUPPORTED, "d=%d (only 128)", c->d);
+  if (c->batch < 1 || c->n_kv_heads < 1 || n_q < 1) return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "shape");
+  if (n_q % c->n_kv_heads) return aatc::fail(AATC_ERR_UNSUPPORTED, "n_q_heads %% n_kv_heads != 0");
+  const int group = n_q / c->n_kv_heads;
+  if (group > AATC_MAX_GROUP) return aatc::fail(AATC_ERR_UNSUPPORTED, "GQA group %d > 8", group);
+  if (c->k_bits < 0 || c->k_bits > 512 || c->v_bits < 0 || c->v_bits > 512)
+    return aatc::fail(AATC_ERR_UNSUPPORTED, "k_bits %d / v_bits %d: decode attention handles 0..512 bits per vector",
+                      c->k_bits, c->v_bits);
+  if (vtiles_bucket(c->v_tiles) < 0 || c->v_tiles < 0)
+    return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "v_tiles %d", c->v_tiles);
+  if (!c->k_calib || !c->v_calib || (!c->k_codes && c->k_bits > 0) || (!c->v_codes && c->v_bits > 0))
+    return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "null cache pointer");
+  if ((reinterpret_cast<uintptr_t>(c->k_codes) & 15) || (reinterpret_cast<uintptr_t>(c->v_codes) & 15) ||
+      (reinterpret_cast<uintptr_t>(ws) & 255))
+    return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "codes must be 16-byte and workspace 256-byte aligned");
+  if (max_seq < 0 || max_seq > c->capacity_tokens)
+    return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "max_seq_len %lld > capacity", (long long)max_seq);
+  const Plan p = make_plan(c, n_q, max_seq);
+  const size_t need = align256(p.part_bytes) + align256(p.cnt_bytes);
+  if (ws_bytes < need) return aatc::fail(AATC_ERR_BUFFER_TOO_SMALL, "workspace %zu < %zu", ws_bytes, need);
+  if (!p.fits) return aatc::fail(AATC_ERR_UNSUPPORTED, "tiles of %d+%d bits do not fit LDS", c->k_bits, c->v_bits);
+  AttnArgs a;
+  a.kcal = static_cast<const aatc_calib*>(c->k_calib);
+  a.vcal = static_cast<const aatc_calib*>(c->v_calib);
+  a.kcodes = static_cast<const uint32_t*>(c->k_codes);
+  a.vcodes = static_cast<const uint32_t*>(c->v_codes);
+  a.tiles_per_seq = c->capacity_tokens / 64;
+  a.n_kv = c->n_kv_heads;
+  a.n_q = n_q;
+  a.group = group;
+  a.seq_lens = seq_lens;
+  a.max_seq = max_seq;
+  a.q = q;
+  a.scale2 = (scale > 0.f ? scale : 1.0f / sqrtf(static_cast<float>(AATC_D))) * 1.4426950408889634f;
+  a.out = out;
+  a.lse = lse;
+  char* w = static_cast<char*>(ws);
+  a.part = reinterpret_cast<float*>(w);
+  a.counters = reinterpret_cast<unsigned*>(w + align256(p.part_bytes));
+  a.S = p.S;
+  a.tpw = p.tpw;
+  a.kB = c->k_bits;
+  a.vB = c->v_bits;
+  a.np_half = p.half;
+  a.chunk = p.chunk;
+  a.nbuf = p.nbuf;
+  a.ks_bytes = p.ks;
+  a.vs_bytes = p.vs;
+  auto st = static_cast<hipStream_t>(stream);
+  const dim3 grid(p.S, c->n_kv_heads, c->batch);
+  hipError_t err = hipSuccess;
+  const bool ok = dispatch(p, a, grid, st, &err);
+  if (!ok) return aatc::fail(AATC_ERR_UNSUPPORTED, "plan NP=%d NVB=%d", p.NP, p.NVB);
+  if (err != hipSuccess) return aatc::fail(AATC_ERR_HIP, "decode_attn launch: %s", hipGetErrorString(err));
+  return AATC_OK;
+}
+
+}  // extern "C"

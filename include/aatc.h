@@ -1,0 +1,253 @@
+/*
+ * aatc.h -- C ABI of the MI355X (gfx950) transform-coded KV-cache library.
+ *
+ * The method (page "KV Cache Compression Through the Lens of Transform Coding", Key points
+ * and Full text; page "SPECTRA: Pushing the KV Cache Beyond the 2-Bit Cliff via Spectral
+ * Transform Coding", Abstract): per KV head, rotate the cached vectors into a decorrelating
+ * basis computed from calibration statistics (KLT), or a Walsh-Hadamard basis (page
+ * "Ablation, Statistical Inference, and Validation for KV-Cache Compression", first
+ * abstract); give each rotated channel 0..8 bits by reverse water-filling under a
+ * bits-per-element budget; quantize each channel with a uniform scalar quantizer and pack
+ * the codes at a fixed number of bits per token (page "SPHERICAL KV ...", NOVA-KV abstract:
+ * fixed per-token bit count).  Decode attention reads the packed codes directly: the query
+ * is rotated once, scores are formed in the rotated domain and values are dequantized and
+ * rotated back only after the softmax-weighted sum (page "Ablation ...", OCTOPUS abstract:
+ * keys are never materialised).
+ *
+ * Conventions for every call:
+ *  - Every call returns an aatc_status.  Arguments are validated on the host before any
+ *    device work is queued; on an error nothing is written and aatc_last_error() (per
+ *    thread) holds a message.  No C++ exception crosses this interface.
+ *  - Device calls only enqueue work on `stream` (a hipStream_t; NULL = the default
+ *    stream).  Faults during execution surface at the caller's next synchronisation.
+ *  - The caller owns and frees every buffer.  The library allocates no device memory and
+ *    keeps no device state between calls.
+ *  - Head dimension d is 128.  Channel stride is 1 in every tensor; other strides are in
+ *    elements.
+ *  - Concurrent calls that write the same cache tile are a caller race.
+ */
+#ifndef AATC_H
+#define AATC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  AATC_OK = 0,
+  AATC_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad shape, range or stride */
+  AATC_ERR_UNSUPPORTED = 2,      /* d != 128, GQA group > 8, dtype not handled */
+  AATC_ERR_BUDGET = 3,           /* bits per vector outside [0, 8d] */
+  AATC_ERR_NUMERICAL = 4,        /* non-finite calibration data, eigensolver did not converge */
+  AATC_ERR_BAD_ARTEFACT = 5,     /* calibration blob magic/version/checksum/contents wrong */
+  AATC_ERR_BUFFER_TOO_SMALL = 6, /* output blob or workspace smaller than required */
+  AATC_ERR_HIP = 7               /* a HIP launch failed; message in aatc_last_error() */
+} aatc_status;
+
+typedef enum { AATC_F32 = 0, AATC_BF16 = 1, AATC_F64 = 2 } aatc_dtype;
+typedef enum { AATC_ROT_KLT = 0, AATC_ROT_WHT = 1, AATC_ROT_IDENTITY = 2 } aatc_rotation;
+
+#define AATC_D 128
+#define AATC_TILE 64             /* tokens per packed tile */
+#define AATC_MAX_BITS 8
+#define AATC_MAX_FIELDS 384      /* 3 fields per channel at most (7 = 4+2+1) */
+#define AATC_MAX_GROUP 8         /* q heads per KV head handled by decode attention */
+#define AATC_MAGIC 0x43544141u   /* "AATC" */
+#define AATC_VERSION 1u
+
+/*
+ * Calibration artefact of one (layer, KV head, tensor K|V): a plain-old-data blob that is
+ * written by aatc_calibrate on the host, copied byte for byte to device memory by the
+ * caller, and read there by the kernels.  A cache tensor uses n_kv_heads consecutive blobs.
+ *
+ * Packed formats (fixed per-token bit count B = total_bits; a 64-token tile is exactly
+ * 64*B bits = 2B little-endian uint32 words; string bit s is bit s%32 of word s/32; tile j of
+ * sequence (b,h) starts at word ((b*n_kv_heads + h)*tiles_per_seq + j)*2B):
+ *
+ *  K tiles, token-major bit-planes.  Token t (0..63) owns string bits [tB, tB+B).  Its plane
+ *    p (plane_channel[p], plane_bit[p]) sits at bit tB+p; planes are ordered by channel
+ *    ascending, then code bit ascending (plane (i,k) holds bit k of code c_i).
+ *
+ *  V tiles, field-major.  Channel i's code is split by the binary expansion of b_i into
+ *    fields of width 4, 2, 1 (8 = 4+4), low code bits in the widest field.  Fields are
+ *    ordered by width descending, channel ascending, shift ascending; field f of width w owns
+ *    the 2w words starting at field_word[f].  Token t = 16G + 4r + m (G,r,m in 0..3) stores
+ *    its w-bit value LSB-first at this bit offset of the field's 64w-bit string:
+ *       w=1: 32*(G/2) + 8m + 4*(G%2) + r
+ *       w=2: 32G + 8m + 2r
+ *       w=4: 64G + 32*(r/2) + 8m + 4*(r%2)
+ *    (so that four tokens' values land in the four bytes of one word after a shift).
+ *
+ * Quantizer (mid-rise, per channel): for b_i >= 1,
+ *    c_i = clamp(floor((y_i - o_i) * inv_delta_i + 2^(b_i-1)), 0, 2^b_i - 1),  y = R x,
+ *    evaluated in fp64 with separately rounded operations; NaN -> 0; +-Inf -> clamp ends.
+ *    Reconstruction y_hat_i = o_i + delta_i (c_i - 2^(b_i-1) + 1/2); b_i = 0 gives o_i;
+ *    x_hat = R^T y_hat.
+ */
+typedef struct aatc_calib {
+  uint32_t magic;          /* AATC_MAGIC */
+  uint32_t version;        /* AATC_VERSION */
+  int32_t d;               /* 128 */
+  int32_t rotation;        /* aatc_rotation */
+  int32_t total_bits;      /* B = sum_i bits[i] */
+  int32_t max_bits;        /* 8 */
+  int32_t n_coded;         /* channels with bits > 0 */
+  int32_t n_fields;        /* V fields = n_fields4 + n_fields2 + n_fields1 */
+  int32_t n_fields4, n_fields2, n_fields1;
+  int32_t n_calib;         /* calibration rows used */
+  uint64_t checksum;       /* FNV-1a 64 of the whole blob with this field set to 0 */
+  double R[AATC_D * AATC_D];         /* row i = rotated channel i (orthogonal) */
+  double mu[AATC_D];                 /* calibration mean (original basis) */
+  double o[AATC_D];                  /* per-channel offset R mu */
+  double sigma2[AATC_D];             /* rotated-channel variance */
+  double delta[AATC_D];              /* quantizer step (0 for b_i = 0) */
+  double inv_delta[AATC_D];          /* 1/delta, correctly rounded (0 for b_i = 0) */
+  float R32[AATC_D * AATC_D];        /* fp32 copy of R */
+  float o32[AATC_D];
+  float delta32[AATC_D];
+  uint8_t bits[AATC_D];              /* b_i in 0..8 */
+  uint8_t plane_channel[AATC_D * AATC_MAX_BITS];
+  uint8_t plane_bit[AATC_D * AATC_MAX_BITS];
+  uint16_t field_channel[AATC_MAX_FIELDS];
+  uint8_t field_shift[AATC_MAX_FIELDS];
+  uint8_t field_width[AATC_MAX_FIELDS];
+  uint16_t field_word[AATC_MAX_FIELDS];
+  int16_t channel_field[AATC_D * 3];  /* fields of channel i, -1 padded */
+  uint8_t reserved[64];
+} aatc_calib;
+
+typedef struct {
+  int32_t d;               /* 128 */
+  int32_t rotation;        /* aatc_rotation */
+  double bits_per_elem;    /* average budget b; B = floor(b*d + 1/2) */
+  int32_t max_bits;        /* per-channel cap, 8 (1..8) */
+  int32_t reserved;
+} aatc_calib_params;
+
+/* A compressed cache of one layer, one tensor pair: every pointer is device memory.
+ * k_codes/v_codes hold batch*n_kv_heads*(capacity_tokens/64) tiles of 2*k_bits (2*v_bits)
+ * words.  k_calib/v_calib point at n_kv_heads consecutive aatc_calib blobs whose
+ * total_bits equal k_bits / v_bits (checked by the kernels: a mismatching head is skipped
+ * and its decode-attention outputs are NaN).  A tensor with 0 bits may pass NULL codes. */
+typedef struct {
+  int32_t batch;
+  int32_t n_kv_heads;
+  int32_t d;                /* 128 */
+  int32_t k_bits;           /* B of every K blob */
+  int32_t v_bits;           /* B of every V blob */
+  int32_t v_tiles;          /* max over the V blobs of aatc_calib_v_tiles() (<= 24) */
+  int64_t capacity_tokens;  /* tokens per (b,h); multiple of 64 */
+  const void* k_calib;
+  const void* v_calib;
+  void* k_codes;
+  void* v_codes;
+} aatc_cache;
+
+/* Status text; thread-local message of the last failing call on this thread. */
+const char* aatc_status_string(aatc_status s);
+const char* aatc_last_error(void);
+
+/* Sizes.  aatc_calib_bytes(d) = sizeof(aatc_calib) for d = 128, 0 otherwise.
+ * aatc_bits_budget = floor(b*d + 1/2), or -1 when outside [0, 8d].
+ * aatc_packed_bytes = ceil(n/64) * 8 * total_bits (one (b,h) sequence). */
+size_t aatc_calib_bytes(int32_t d);
+int32_t aatc_bits_budget(double bits_per_elem, int32_t d);
+size_t aatc_packed_bytes(int32_t total_bits, int64_t n_tokens);
+
+/*
+ * aatc_calibrate -- host, synchronous, fp64.  [AATC Full text: "allocates bits over a
+ * calibration set"; SPECTRA Abstract: a coordinate system computed from the cache's own
+ * statistics; RDKV abstract: reverse water-filling applied once after prefill]
+ *   mean and centred covariance (1/M) of the n_calib rows of x_host (row r at
+ *   x_host + r*row_stride elements, dtype F32/BF16/F64); rotation R (KLT: eigenvectors of
+ *   the covariance, descending eigenvalues, largest-magnitude entry of each row positive;
+ *   WHT: Sylvester Hadamard / sqrt(d); IDENTITY); integer reverse water-filling of
+ *   B = floor(b*d+1/2) bits over the rotated variances (the B largest candidates
+ *   sigma_i^2 4^-k, k < max_bits, ordered by value desc, channel asc, bit asc); quantizer
+ *   step delta_i = sigma_i g(b_i) where g(b) minimises the MSE of the 2^b-level mid-rise
+ *   uniform quantizer on N(0,1); offset o = R mu; packing tables.
+ *   Writes one aatc_calib into calib_host (calib_bytes >= aatc_calib_bytes(d)).
+ *   Errors: d != 128 -> UNSUPPORTED; B outside [0, 8d] or max_bits outside 1..8 -> BUDGET;
+ *   n_calib < 2, null pointers, row_stride < d -> INVALID_ARGUMENT; a non-finite value ->
+ *   NUMERICAL; small blob -> BUFFER_TOO_SMALL.  Zero-variance channels get 0 bits unless the
+ *   budget exceeds 8 x (positive-variance channels).
+ */
+aatc_status aatc_calibrate(const aatc_calib_params* params, const void* x_host, aatc_dtype dtype,
+                           int64_t n_calib, int64_t row_stride, void* calib_host,
+                           size_t calib_bytes);
+
+/* Checks magic, version, d, checksum and internal consistency of a host blob. */
+aatc_status aatc_calib_validate(const void* calib_host, size_t calib_bytes);
+
+/* Number of 16-field column groups decode attention uses for a V blob:
+ * ceil(n_fields4/16) + ceil(n_fields2/16) + ceil(n_fields1/16) (0..24); -1 for a bad blob. */
+int32_t aatc_calib_v_tiles(const void* calib_host);
+
+/*
+ * aatc_encode -- device, async.  Quantizes and packs tokens [token_offset, token_offset +
+ * n_tokens) of every (b,h) of tensor `which` (0 = K, 1 = V) into the cache.
+ *   x_dev: element (b,h,t,j) at x_dev[b*strides[0] + h*strides[1] + t*strides[2] + j],
+ *   t relative to token_offset; dtype F32 or BF16.  Rotation and quantization run in fp64.
+ *   In every tile it touches, tokens before token_offset are preserved and tokens at or
+ *   after token_offset + n_tokens are cleared to zero (append-only cache).
+ *   Errors: bad which/dtype/pointers, token_offset < 0, n_tokens < 0, token_offset +
+ *   n_tokens > capacity -> INVALID_ARGUMENT; d != 128 -> UNSUPPORTED; launch -> HIP.
+ */
+aatc_status aatc_encode(const aatc_cache* cache, int32_t which, const void* x_dev, aatc_dtype dtype,
+                        const int64_t strides[3], int64_t token_offset, int64_t n_tokens,
+                        void* stream);
+
+/*
+ * aatc_decode -- device, async.  Reconstructs x_hat = R^T y_hat (fp64, stored as F32 or BF16)
+ * for tokens [token_offset, token_offset + n_tokens) of every (b,h) into out_dev with the
+ * same stride convention as aatc_encode.  Used for checks and for promoting tokens back to
+ * full precision (page "SPHERICAL KV ...", QEvict abstract: a quantized window is
+ * dequantized and promoted), never on the per-token decode path.
+ */
+aatc_status aatc_decode(const aatc_cache* cache, int32_t which, int64_t token_offset,
+                        int64_t n_tokens, void* out_dev, aatc_dtype out_dtype,
+                        const int64_t strides[3], void* stream);
+
+/* Workspace bytes aatc_decode_attn needs for this cache, q-head count and longest sequence. */
+size_t aatc_decode_attn_workspace_bytes(const aatc_cache* cache, int32_t n_q_heads,
+                                        int64_t max_seq_len);
+
+/*
+ * aatc_decode_attn -- device, async; one decode step over the compressed cache.
+ * [SPECTRA Abstract and RDKV abstract: the whole cache is re-read at every generated token;
+ *  NOVA-KV abstract: decode is bandwidth-bound]
+ *   q_dev: fp32 [batch][n_q_heads][128]; q head g reads KV head g / (n_q_heads/n_kv_heads)
+ *   (contiguous groups, 1..8 q heads per KV head).  seq_lens_dev: int32 [batch] tokens
+ *   visible per sequence (each <= max_seq_len <= capacity), or NULL for max_seq_len.
+ *   softmax_scale <= 0 selects 1/sqrt(128).
+ *   out_dev: fp32 [batch][n_q_heads][128] = sum_t softmax_t(scale q.k_hat_t) v_hat_t with
+ *   k_hat, v_hat the reconstructions of aatc_decode, computed as: q~ = R_K q once; scores
+ *   from the packed K bits weighted by q~ delta^K (the reconstruction offset cancels in the
+ *   softmax); online softmax; softmax-weighted sums of the packed V codes; the affine V
+ *   dequantization and R_V^T applied once to the sum.  lse_dev (nullable): fp32
+ *   [batch][n_q_heads] natural-log sum of exp of the scores.  A sequence with 0 visible
+ *   tokens yields out = 0, lse = -inf.
+ *   workspace_dev: >= aatc_decode_attn_workspace_bytes(...) bytes of device memory holding fp64
+ *   accumulators and per-sequence counters.  It must be zero-filled once before its first use;
+ *   every call that runs to completion leaves it zero-filled again, so no clearing (and no
+ *   memset node in a captured graph) is needed between calls.  Calls that share a workspace
+ *   must not overlap in time.
+ *   Limits: k_bits and v_bits <= 512 (4 bits/element), q-head group <= 8.  A score range
+ *   (sum of |plane weights|) above ~1000 in log2 units underflows the fp64 accumulators; the
+ *   affected outputs are NaN rather than wrong.
+ *   Errors: group > 8 or not an integer, bits > 512 -> UNSUPPORTED; bad pointers, seq length >
+ *   capacity -> INVALID_ARGUMENT; workspace too small -> BUFFER_TOO_SMALL; launch -> HIP.
+ */
+aatc_status aatc_decode_attn(const aatc_cache* cache, const float* q_dev, int32_t n_q_heads,
+                             const int32_t* seq_lens_dev, int64_t max_seq_len, float softmax_scale,
+                             float* out_dev, float* lse_dev, void* workspace_dev,
+                             size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AATC_H */

@@ -23,7 +23,7 @@ PURPOSE = {"Q": 0, "calib": 1, "context": 2, "query": 3, "outlier": 4, "zipf": 5
            "append": 6, "device": 7}
 
 __all__ = ["ROOT_SEED", "K", "V", "PURPOSE", "seed_seq", "rng", "haar_orthogonal",
-           "spectrum", "outlier_coords", "basis", "draw", "round_bf16", "to_dtype",
+           "spectrum", "outlier_coords", "basis", "draw", "round_bf16", "bf16_bits", "to_dtype",
            "draw_device", "queries", "zipf_mass", "torch_dtype"]
 
 
@@ -62,6 +62,11 @@ def round_bf16(x):
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
     u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
     return u.astype(np.uint32).view(np.float32)
+
+
+def bf16_bits(x):
+    """Raw bf16 bit patterns (uint16) of float values that are exactly representable in bf16."""
+    return (np.ascontiguousarray(x, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
 
 
 def to_dtype(x, dtype):

@@ -1,0 +1,187 @@
+"""GPU parity: libaatc's HIP path against the fp64 oracle on the same seeded inputs.
+
+Bars: codes and packed words bit-exact (a mismatch is allowed only within 1e-5 of a bin edge,
+at a rate <= 1e-6); reconstruction within 1e-6 max|x_hat|; decode attention max abs error
+<= 2e-3 against the oracle's fp64 attention on the dequantized cache.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+from gpu_helpers import Case, excused_mismatch_report, unpack_all
+
+pytestmark = pytest.mark.gpu
+
+ATOL_ATTN = 2e-3
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _check_codes(case, cache, tensor):
+    words = cache.codes(tensor).cpu().numpy().view(np.uint32)
+    bits_lib = None
+    from compressed_decode_attention_head_amd import api
+    blobs = cache.k_blobs_host if tensor == synth.K else cache.v_blobs_host
+    total_codes = 0
+    for b in range(case.batch):
+        for h in range(case.n_kv):
+            bits = np.asarray(api.calib_view(blobs[h])["bits"], dtype=np.int64)
+            assert np.array_equal(bits, case.art[tensor][h]["bits"])
+            B = int(bits.sum())
+            nw = O.packed_words(B, case.n)
+            got_words = words[b, h, :nw]
+            got = unpack_all(got_words, bits, case.n, tensor)
+            want = case.codes[tensor][b, h]
+            n_bad, n_unexc = excused_mismatch_report(case.x[tensor][b, h], case.art[tensor][h], got, want)
+            assert n_unexc == 0, (b, h, n_bad)
+            total_codes += want.size
+            if n_bad == 0:
+                ref_words = (O.pack_k if tensor == synth.K else O.pack_v)(want, bits)
+                assert np.array_equal(got_words, ref_words), (b, h)
+            else:
+                assert n_bad <= 1e-6 * total_codes + 1
+
+
+CASES = {
+    "cfg1": dict(cfg=1, n_kv=1, group=1, n_tokens=4096, dtype="f32", rotation="klt", bpe_k=2.0),
+    "cfg2s": dict(cfg=2, n_kv=2, group=4, n_tokens=1000, dtype="bf16", rotation="klt", bpe_k=2.76),
+    "cfg3s": dict(cfg=3, n_kv=2, group=4, n_tokens=300, batch=2, dtype="bf16", rotation="klt", bpe_k=4.0),
+    "cfg4s": dict(cfg=4, n_kv=2, group=7, n_tokens=777, dtype="bf16", rotation="wht", bpe_k=1.33,
+                  marginal="t3"),
+}
+
+
+@pytest.fixture(scope="module", params=sorted(CASES))
+def built(request):
+    torch = _torch()
+    case = Case(**CASES[request.param])
+    cache = case.make_cache()
+    for t in (synth.K, synth.V):
+        cache.encode(t, case.torch_x(t))
+    torch.cuda.synchronize()
+    return request.param, case, cache
+
+
+def test_encode_codes_and_words(built):
+    name, case, cache = built
+    print("case", name, flush=True)
+    for t in (synth.K, synth.V):
+        _check_codes(case, cache, t)
+
+
+def test_decode_reconstruction(built):
+    torch = _torch()
+    name, case, cache = built
+    for t in (synth.K, synth.V):
+        xh = cache.decode(t, 0, case.n).cpu().numpy().astype(np.float64)
+        for b in range(case.batch):
+            for h in range(case.n_kv):
+                ref = O.reconstruct(case.codes[t][b, h], case.art[t][h])
+                err = np.abs(xh[b, h] - ref).max()
+                assert err <= 1e-6 * np.abs(ref).max(), (name, t, b, h, err)
+
+
+def test_decode_attention(built):
+    torch = _torch()
+    name, case, cache = built
+    q = torch.from_numpy(case.q.astype(np.float32)).cuda()
+    out, lse = cache.decode_attn(q, case.n)
+    torch.cuda.synchronize()
+    ref, lref = case.oracle_attention()
+    err = np.abs(out.cpu().numpy() - ref).max()
+    lerr = np.abs(lse.cpu().numpy() - lref).max()
+    print(name, "attn max abs err", err, "lse err", lerr, flush=True)
+    assert err <= ATOL_ATTN, err
+    assert lerr <= 5e-3, lerr
+
+
+def test_ragged_seq_lens_and_empty():
+    torch = _torch()
+    case = Case(cfg=2, n_kv=2, group=4, n_tokens=333, batch=3, rotation="klt", bpe_k=2.76)
+    cache = case.make_cache(capacity=384)
+    for t in (synth.K, synth.V):
+        cache.encode(t, case.torch_x(t))
+    seq = np.array([333, 65, 0], dtype=np.int32)
+    q = torch.from_numpy(case.q.astype(np.float32)).cuda()
+    out, lse = cache.decode_attn(q, 333, seq_lens=torch.from_numpy(seq).cuda())
+    torch.cuda.synchronize()
+    ref, lref = case.oracle_attention(seq_lens=seq)
+    o = out.cpu().numpy()
+    assert np.abs(o[:2] - ref[:2]).max() <= ATOL_ATTN
+    assert np.all(o[2] == 0.0) and np.all(np.isneginf(lse.cpu().numpy()[2]))
+    assert np.abs(lse.cpu().numpy()[:2] - lref[:2]).max() <= 5e-3
+
+
+@pytest.mark.parametrize("group", [1, 3, 8])
+def test_gqa_groups(group):
+    torch = _torch()
+    case = Case(cfg=2, n_kv=2, group=group, n_tokens=200, rotation="klt", bpe_k=2.0)
+    cache = case.make_cache()
+    for t in (synth.K, synth.V):
+        cache.encode(t, case.torch_x(t))
+    out, _ = cache.decode_attn(torch.from_numpy(case.q.astype(np.float32)).cuda(), case.n)
+    ref, _ = case.oracle_attention()
+    assert np.abs(out.cpu().numpy() - ref).max() <= ATOL_ATTN
+
+
+def test_zero_bit_tensors():
+    """All K channels at 0 bits: uniform softmax; all V channels at 0 bits: output = mu_V."""
+    torch = _torch()
+    for bk, bv in ((0.0, 2.0), (2.0, 0.0)):
+        case = Case(cfg=2, n_kv=1, group=4, n_tokens=150, rotation="klt", bpe_k=bk, bpe_v=bv)
+        cache = case.make_cache()
+        for t in (synth.K, synth.V):
+            cache.encode(t, case.torch_x(t))
+        out, _ = cache.decode_attn(torch.from_numpy(case.q.astype(np.float32)).cuda(), case.n)
+        ref, _ = case.oracle_attention()
+        assert np.abs(out.cpu().numpy() - ref).max() <= ATOL_ATTN, (bk, bv)
+
+
+def test_append_matches_one_shot_pack():
+    """Prefill 100 tokens, then append 1, 7 and 20 tokens: words equal the one-shot pack."""
+    torch = _torch()
+    case = Case(cfg=3, n_kv=2, group=4, n_tokens=128, batch=2, rotation="klt", bpe_k=4.0)
+    cache = case.make_cache(capacity=192)
+    for t in (synth.K, synth.V):
+        x = case.torch_x(t)
+        cache.encode(t, x[:, :, :100])
+        off = 100
+        for step in (1, 7, 20):
+            cache.encode(t, x[:, :, off:off + step], token_offset=off)
+            off += step
+    torch.cuda.synchronize()
+    case.n = 128
+    for t in (synth.K, synth.V):
+        _check_codes(case, cache, t)
+    out, _ = cache.decode_attn(torch.from_numpy(case.q.astype(np.float32)).cuda(), 128)
+    ref, _ = case.oracle_attention()
+    assert np.abs(out.cpu().numpy() - ref).max() <= ATOL_ATTN
+
+
+def test_device_error_paths():
+    torch = _torch()
+    from compressed_decode_attention_head_amd import api
+    case = Case(cfg=2, n_kv=1, group=4, n_tokens=64, rotation="klt", bpe_k=2.0)
+    cache = case.make_cache()
+    x = case.torch_x(synth.K)
+    with pytest.raises(api.AatcError) as e:
+        cache.encode(0, x, token_offset=10)            # beyond capacity
+    assert e.value.name == "AATC_ERR_INVALID_ARGUMENT"
+    q = torch.zeros((1, 9, 128), dtype=torch.float32, device="cuda")
+    with pytest.raises(api.AatcError) as e:
+        cache.decode_attn(q, 64)                        # group 9 > 8
+    assert e.value.name == "AATC_ERR_UNSUPPORTED"
+    q = torch.zeros((1, 4, 128), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(api.AatcError) as e:
+        cache.decode_attn(q, 64, workspace=ws)
+    assert e.value.name == "AATC_ERR_BUFFER_TOO_SMALL"
+    with pytest.raises(api.AatcError) as e:
+        cache.decode_attn(q, 128)                       # longer than capacity
+    assert e.value.name == "AATC_ERR_INVALID_ARGUMENT"

@@ -1,0 +1,175 @@
+"""CPU tests of libaatc's host side: exports, calibration parity with the oracle, error paths.
+
+No GPU is touched: only aatc_calibrate / aatc_calib_validate / size helpers are called.
+"""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+from compressed_decode_attention_head_amd import _native as N
+from compressed_decode_attention_head_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return N.lib()
+
+
+def test_exports_match_header(L):
+    hdr = open(os.path.join(ROOT, "include", "aatc.h")).read()
+    names = set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?(aatc_[a-z_0-9]+)\(", hdr, re.M))
+    assert names, "no declarations parsed"
+    assert names == set(N.EXPORTS), names ^ set(N.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_struct_size_and_sizes(L):
+    assert L.aatc_calib_bytes(128) == N.CALIB_DTYPE.itemsize
+    assert L.aatc_calib_bytes(64) == 0
+    assert [L.aatc_bits_budget(b, 128) for b in (2.0, 2.76, 4.0, 1.33, 0.0, 8.0)] == [256, 353, 512, 170, 0, 1024]
+    assert L.aatc_bits_budget(8.01, 128) == -1 and L.aatc_bits_budget(-1.0, 128) == -1
+    assert L.aatc_packed_bytes(170, 131072) == 131072 // 64 * 8 * 170
+    assert L.aatc_packed_bytes(353, 65) == 2 * 8 * 353
+
+
+def _cal(cfg, head=0, tensor=synth.K, dtype="bf16", marginal="gauss"):
+    return synth.draw(cfg, 0, head, tensor, "calib", 1024, dtype=dtype, marginal=marginal)
+
+
+def _bits16(x):
+    return (np.ascontiguousarray(x, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("cfg,rot,bpe,tensor", [(1, "klt", 2.0, synth.K), (2, "klt", 2.76, synth.V),
+                                                (3, "klt", 4.0, synth.K), (4, "wht", 1.33, synth.V),
+                                                (2, "identity", 2.76, synth.K)])
+def test_calibrate_matches_oracle(cfg, rot, bpe, tensor):
+    dtype = "f32" if cfg == 1 else "bf16"
+    x = _cal(cfg, 1, tensor, dtype=dtype, marginal="t3" if cfg == 4 else "gauss")
+    blob = api.calibrate(x if dtype == "f32" else _bits16(x), rot, bpe)
+    api.validate(blob)
+    c = api.calib_view(blob)
+    ref = O.calibrate(x, rot, bpe)
+    assert int(c["total_bits"]) == ref["B"]
+    assert np.array_equal(c["bits"].astype(np.int64), ref["bits"])
+    assert np.abs(c["mu"] - ref["mu"]).max() < 1e-13
+    R = c["R"].reshape(128, 128)
+    assert np.abs(R - ref["R"]).max() < 1e-9
+    assert np.abs(c["sigma2"] - ref["sigma2"]).max() < 1e-12 * ref["sigma2"].max()
+    assert np.abs(c["o"] - ref["o"]).max() < 1e-10 * (1 + np.abs(ref["o"]).max())
+    coded = ref["bits"] > 0
+    assert np.all(np.abs(c["delta"][coded] / ref["delta"][coded] - 1) < 1e-11)
+    assert np.array_equal(c["delta"][~coded], np.zeros((~coded).sum()))
+    assert np.array_equal(c["inv_delta"][coded], 1.0 / c["delta"][coded])
+    assert np.array_equal(c["R32"], R.astype(np.float32).ravel())
+
+
+def test_quantizer_step_matches_oracle_all_widths():
+    """sigma=1 channels at every width: delta/sigma must equal the oracle's g(b) to 1e-13."""
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((4096, 128))
+    x = (x - x.mean(0)) / x.std(0)
+    for bpe in (1.0, 2.0, 3.0, 5.0, 8.0):
+        blob = api.calibrate(x.astype(np.float64), "identity", bpe)
+        c = api.calib_view(blob)
+        for i in range(128):
+            b = int(c["bits"][i])
+            if b:
+                assert abs(c["delta"][i] / math.sqrt(c["sigma2"][i]) - O.optimal_step(b)) < 1e-13
+
+
+def test_noise_free_klt_pin_f64():
+    q, lam, _ = synth.basis(1, 0, 0, synth.K)
+    d = 128
+    cols = [math.sqrt(d) * math.sqrt(lam[i]) * q[:, i] for i in range(d)]
+    x = np.array(cols + [-c for c in cols])
+    blob = api.calibrate(x, "klt", 2.0)
+    c = api.calib_view(blob)
+    R = c["R"].reshape(128, 128)
+    assert np.abs(R @ R.T - np.eye(128)).max() < 1e-10
+    assert np.abs(c["sigma2"] - lam).max() < 1e-12
+    assert np.abs(np.abs(R @ q) - np.eye(128)).max() < 1e-10
+    hist = {int(k): int(v) for k, v in zip(*np.unique(c["bits"], return_counts=True))}
+    assert hist == {6: 1, 5: 4, 4: 7, 3: 19, 2: 48, 1: 49}
+
+
+def test_layout_tables_match_oracle():
+    x = _cal(2, 0, synth.V)
+    blob = api.calibrate(_bits16(x), "klt", 2.76)
+    c = api.calib_view(blob)
+    bits = c["bits"].astype(np.int64)
+    fields = O.v_fields(bits)
+    nf = int(c["n_fields"])
+    assert nf == len(fields)
+    got = [(int(c["field_channel"][k]), int(c["field_shift"][k]), int(c["field_width"][k])) for k in range(nf)]
+    assert got == fields
+    word = np.concatenate([[0], np.cumsum([2 * f[2] for f in fields])])[:-1]
+    assert np.array_equal(c["field_word"][:nf], word)
+    planes = [(i, k) for i in range(128) for k in range(bits[i])]
+    B = int(c["total_bits"])
+    assert list(zip(c["plane_channel"][:B].tolist(), c["plane_bit"][:B].tolist())) == planes
+    assert api.v_tiles(blob) == sum(-(-n // 16) for n in (int(c["n_fields4"]), int(c["n_fields2"]),
+                                                         int(c["n_fields1"])))
+
+
+def test_zero_variance_channels_get_no_bits():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((512, 128))
+    x[:, 5] = 3.0
+    x[:, 77] = -1.0
+    blob = api.calibrate(x, "identity", 2.0)
+    c = api.calib_view(blob)
+    assert c["bits"][5] == 0 and c["bits"][77] == 0
+    assert c["o"][5] == 3.0 and c["o"][77] == -1.0
+
+
+def _status(fn):
+    with pytest.raises(api.AatcError) as e:
+        fn()
+    return e.value.name
+
+
+def test_calibrate_error_paths(L):
+    x = np.random.default_rng(0).standard_normal((64, 128))
+    assert _status(lambda: api.calibrate(x, "klt", 8.5)) == "AATC_ERR_BUDGET"
+    assert _status(lambda: api.calibrate(x, "klt", -0.5)) == "AATC_ERR_BUDGET"
+    assert _status(lambda: api.calibrate(x[:1], "klt", 2.0)) == "AATC_ERR_INVALID_ARGUMENT"
+    bad = x.copy()
+    bad[3, 4] = np.nan
+    assert _status(lambda: api.calibrate(bad, "klt", 2.0)) == "AATC_ERR_NUMERICAL"
+    bad[3, 4] = np.inf
+    assert _status(lambda: api.calibrate(bad, "klt", 2.0)) == "AATC_ERR_NUMERICAL"
+    assert _status(lambda: api.calibrate(x[:, :64], "klt", 2.0, d=64)) == "AATC_ERR_UNSUPPORTED"
+    p = N.CalibParams(128, 0, 2.0, 8, 0)
+    out = np.zeros(100, dtype=np.uint8)
+    assert L.aatc_calibrate(ctypes.byref(p), x.ctypes.data, 2, 64, 128, out.ctypes.data, out.nbytes) == 6
+    assert L.aatc_calibrate(ctypes.byref(p), None, 2, 64, 128, out.ctypes.data, out.nbytes) == 1
+    assert L.aatc_calibrate(ctypes.byref(p), x.ctypes.data, 2, 64, 100, out.ctypes.data, out.nbytes) == 1
+    p = N.CalibParams(128, 0, 2.0, 9, 0)
+    big = np.zeros(N.CALIB_DTYPE.itemsize, dtype=np.uint8)
+    assert L.aatc_calibrate(ctypes.byref(p), x.ctypes.data, 2, 64, 128, big.ctypes.data, big.nbytes) == 3
+
+
+def test_validate_detects_corruption():
+    x = np.random.default_rng(0).standard_normal((256, 128))
+    blob = api.calibrate(x, "klt", 2.0)
+    api.validate(blob)
+    for off in (0, 100, 5000, N.CALIB_DTYPE.itemsize - 70):
+        b = blob.copy()
+        b[off] ^= 0x40
+        assert _status(lambda: api.validate(b)) == "AATC_ERR_BAD_ARTEFACT"
+    assert _status(lambda: api.validate(blob[:100])) == "AATC_ERR_BUFFER_TOO_SMALL"
+
+
+def test_status_strings(L):
+    for s in range(8):
+        assert L.aatc_status_string(s)
