@@ -154,9 +154,9 @@ class CompressedKVCache:
                                                             int(max_seq_len)))
 
     def new_workspace(self, n_q_heads, max_seq_len):
-        """Zero-filled decode-attention workspace (each call leaves it zero-filled again)."""
+        """Decode-attention workspace (partial records; its contents need no initialisation)."""
         import torch
-        return torch.zeros(self.workspace_bytes(n_q_heads, max_seq_len), dtype=torch.uint8, device=self.device)
+        return torch.empty(self.workspace_bytes(n_q_heads, max_seq_len), dtype=torch.uint8, device=self.device)
 
     def decode_attn(self, q, max_seq_len, seq_lens=None, scale=0.0, workspace=None, out=None, lse=None,
                     stream=None):

@@ -1,5 +1,6 @@
 // Decode attention on the packed cache: host-side plan, validation and launch.
 // The kernel (and the method it implements) is described in aatc_attn_kernel.h.
+#define AATC_ATTN_COMBINE_TU
 #include "aatc_attn_kernel.h"
 
 namespace {
@@ -7,7 +8,7 @@ namespace {
 using namespace aatc_attn;
 
 constexpr size_t kLdsLimit = 160 * 1024;
-constexpr size_t kStaticLds = 1024;          // __shared__ scalars of the kernel (rounded up)
+constexpr size_t kStaticLds = 2048;          // __shared__ scalars of the kernel (rounded up)
 
 int vtiles_bucket(int vt) {
   if (vt <= 8) return 8;
@@ -20,34 +21,38 @@ int vtiles_bucket(int vt) {
 int round1k(int64_t x) { return static_cast<int>((x + 1023) / 1024 * 1024); }
 
 struct Plan {
-  int NP, NVB, LIMBS, S, tpw, half, chunk, nbuf, ks, vs;
+  int NP, NVB, LIMBS, WAVES, S, tpw, half, chunk, nbuf, ks, vs, prec;
   size_t lds;
-  size_t part_bytes, cnt_bytes;
+  size_t part_bytes, offs_bytes;
+  int SC, rec_bytes;
+  size_t comb_lds;
   bool fits;
 };
 
-// Tiles per wave fill 256 CUs x 8 waves once; each wave keeps as many of its tiles in LDS
-// as fit (all of them when possible, else double-buffered chunks, else single chunks).
+// Tiles per wave fill 256 CUs x WAVES waves once; each wave keeps as many of its tiles in
+// LDS as fit (all of them when possible, else double-buffered chunks, else single chunks).
 Plan make_plan(const aatc_cache* c, int n_q, int64_t max_seq) {
   Plan p;
   const int kb = c->k_bits, vb = c->v_bits;
   p.NP = kb > 0 ? (kb + 127) / 128 : 1;
   p.half = (kb > 0 && kb - 128 * (p.NP - 1) <= 64) ? 1 : 0;
   p.NVB = vtiles_bucket(c->v_tiles);
+  p.WAVES = waves_for(p.NP, p.NVB);
   const int group = c->n_kv_heads > 0 ? n_q / c->n_kv_heads : 1;
   p.LIMBS = group <= 4 ? 3 : 2;
+  p.prec = PHDR + 16 * (c->v_tiles > 0 ? c->v_tiles : 1);
   const int64_t ntiles = (max_seq + 63) / 64;
   const int64_t seqs = static_cast<int64_t>(c->batch) * c->n_kv_heads;
-  const int64_t target_waves = 256 * WAVES;
+  const int64_t target_waves = 256 * static_cast<int64_t>(p.WAVES);
   int64_t tpw = (ntiles * seqs + target_waves - 1) / target_waves;
   if (tpw < 1) tpw = 1;
   if (tpw > 64) tpw = 64;
   p.tpw = static_cast<int>(tpw);
-  int64_t S = (ntiles + WAVES * tpw - 1) / (WAVES * tpw);
+  int64_t S = (ntiles + p.WAVES * tpw - 1) / (p.WAVES * tpw);
   if (S < 1) S = 1;
   p.S = static_cast<int>(S);
-  const size_t fixed = UNION_BYTES + PL_BYTES + kStaticLds;
-  const size_t per_wave = (kLdsLimit - fixed) / WAVES;
+  const size_t fixed = UNION_BYTES + static_cast<size_t>(p.WAVES) * PL_WAVE + TAB_BYTES + DMA_PAD + kStaticLds;
+  const size_t per_wave = (kLdsLimit - fixed) / p.WAVES;
   auto area = [&](int ch, int nbuf) {
     const int ks = kb > 0 ? round1k(8LL * kb * ch + 16) : 0;
     const int vs = vb > 0 ? round1k(8LL * vb * ch + 16) : 0;
@@ -67,13 +72,22 @@ Plan make_plan(const aatc_cache* c, int n_q, int64_t max_seq) {
   }
   p.ks = kb > 0 ? round1k(8LL * kb * p.chunk + 16) : 0;
   p.vs = vb > 0 ? round1k(8LL * vb * p.chunk + 16) : 0;
-  // the finalize reuses the tile area for 8 x S slot weights
-  size_t tiles = static_cast<size_t>(WAVES) * p.nbuf * (p.ks + p.vs);
-  if (tiles < static_cast<size_t>(8) * p.S * 4) tiles = static_cast<size_t>(8) * p.S * 4;
-  p.lds = UNION_BYTES + PL_BYTES + tiles;
+  // the workgroup merge reuses the tile area: WAVES x NVB x 32 lanes x float4
+  size_t tiles = static_cast<size_t>(p.WAVES) * p.nbuf * (p.ks + p.vs) + DMA_PAD;
+  const size_t merge = static_cast<size_t>(p.WAVES) * p.NVB * 32 * 16;
+  if (tiles < merge) tiles = merge;
+  p.lds = UNION_BYTES + static_cast<size_t>(p.WAVES) * PL_WAVE + TAB_BYTES + tiles;
   if (p.lds + kStaticLds > kLdsLimit) p.fits = false;
-  p.part_bytes = static_cast<size_t>(seqs) * p.S * 8 * PROW_MAX * 4;
-  p.cnt_bytes = static_cast<size_t>(seqs) * 4;
+  p.part_bytes = static_cast<size_t>(seqs) * p.S * group * p.prec * 4;
+  p.offs_bytes = static_cast<size_t>(seqs) * 8 * 4;
+  // combine: a chunk of records per LDS fill (at most 64 KB, at most 1024 splits)
+  int sc = static_cast<int>((64 * 1024) / (p.prec * 4));
+  if (sc > 1024) sc = 1024;
+  if (sc > p.S) sc = p.S;
+  if (sc < 1) sc = 1;
+  p.SC = sc;
+  p.rec_bytes = round1k(static_cast<int64_t>(sc) * p.prec * 4);
+  p.comb_lds = static_cast<size_t>(p.rec_bytes) + CR_BYTES;
   return p;
 }
 
@@ -97,7 +111,7 @@ extern "C" {
 size_t aatc_decode_attn_workspace_bytes(const aatc_cache* c, int32_t n_q_heads, int64_t max_seq_len) {
   if (!c || max_seq_len < 0 || n_q_heads < 1) return 0;
   const Plan p = make_plan(c, n_q_heads, max_seq_len);
-  return align256(p.part_bytes) + align256(p.cnt_bytes);
+  return align256(p.part_bytes) + align256(p.offs_bytes);
 }
 
 aatc_status aatc_decode_attn(const aatc_cache* c, const float* q, int32_t n_q, const int32_t* seq_lens,
@@ -123,7 +137,7 @@ aatc_status aatc_decode_attn(const aatc_cache* c, const float* q, int32_t n_q, c
   if (max_seq < 0 || max_seq > c->capacity_tokens)
     return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "max_seq_len %lld > capacity", (long long)max_seq);
   const Plan p = make_plan(c, n_q, max_seq);
-  const size_t need = align256(p.part_bytes) + align256(p.cnt_bytes);
+  const size_t need = align256(p.part_bytes) + align256(p.offs_bytes);
   if (ws_bytes < need) return aatc::fail(AATC_ERR_BUFFER_TOO_SMALL, "workspace %zu < %zu", ws_bytes, need);
   if (!p.fits) return aatc::fail(AATC_ERR_UNSUPPORTED, "tiles of %d+%d bits do not fit LDS", c->k_bits, c->v_bits);
   AttnArgs a;
@@ -143,9 +157,10 @@ aatc_status aatc_decode_attn(const aatc_cache* c, const float* q, int32_t n_q, c
   a.lse = lse;
   char* w = static_cast<char*>(ws);
   a.part = reinterpret_cast<float*>(w);
-  a.counters = reinterpret_cast<unsigned*>(w + align256(p.part_bytes));
+  a.offs = reinterpret_cast<float*>(w + align256(p.part_bytes));
   a.S = p.S;
   a.tpw = p.tpw;
+  a.prec = p.prec;
   a.kB = c->k_bits;
   a.vB = c->v_bits;
   a.np_half = p.half;
@@ -159,6 +174,27 @@ aatc_status aatc_decode_attn(const aatc_cache* c, const float* q, int32_t n_q, c
   const bool ok = dispatch(p, a, grid, st, &err);
   if (!ok) return aatc::fail(AATC_ERR_UNSUPPORTED, "plan NP=%d NVB=%d", p.NP, p.NVB);
   if (err != hipSuccess) return aatc::fail(AATC_ERR_HIP, "decode_attn launch: %s", hipGetErrorString(err));
+  CombArgs cb;
+  cb.vcal = a.vcal;
+  cb.part = a.part;
+  cb.offs = a.offs;
+  cb.n_kv = c->n_kv_heads;
+  cb.n_q = n_q;
+  cb.group = group;
+  cb.S = p.S;
+  cb.prec = p.prec;
+  cb.SC = p.SC;
+  cb.rec_bytes = p.rec_bytes;
+  cb.seq_lens = seq_lens;
+  cb.max_seq = max_seq;
+  cb.out = out;
+  cb.lse = lse;
+  err = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_combine), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(p.comb_lds));
+  if (err != hipSuccess) return aatc::fail(AATC_ERR_HIP, "decode_attn combine attribute: %s", hipGetErrorString(err));
+  hipLaunchKernelGGL(k_attn_combine, dim3(group, c->n_kv_heads, c->batch), dim3(CNT), p.comb_lds, st, cb);
+  err = hipGetLastError();
+  if (err != hipSuccess) return aatc::fail(AATC_ERR_HIP, "decode_attn combine launch: %s", hipGetErrorString(err));
   return AATC_OK;
 }
 

@@ -230,14 +230,11 @@ size_t aatc_decode_attn_workspace_bytes(const aatc_cache* cache, int32_t n_q_hea
  *   dequantization and R_V^T applied once to the sum.  lse_dev (nullable): fp32
  *   [batch][n_q_heads] natural-log sum of exp of the scores.  A sequence with 0 visible
  *   tokens yields out = 0, lse = -inf.
- *   workspace_dev: >= aatc_decode_attn_workspace_bytes(...) bytes of device memory holding fp64
- *   accumulators and per-sequence counters.  It must be zero-filled once before its first use;
- *   every call that runs to completion leaves it zero-filled again, so no clearing (and no
- *   memset node in a captured graph) is needed between calls.  Calls that share a workspace
- *   must not overlap in time.
- *   Limits: k_bits and v_bits <= 512 (4 bits/element), q-head group <= 8.  A score range
- *   (sum of |plane weights|) above ~1000 in log2 units underflows the fp64 accumulators; the
- *   affected outputs are NaN rather than wrong.
+ *   workspace_dev: >= aatc_decode_attn_workspace_bytes(...) bytes of device memory, 256-byte
+ *   aligned, for the per-split partial records of the two kernels the call launches on
+ *   `stream`; its contents need no initialisation.  Calls that share a workspace must be
+ *   ordered (same stream) or not overlap in time.
+ *   Limits: k_bits and v_bits <= 512 (4 bits/element), q-head group <= 8, v_tiles <= 24.
  *   Errors: group > 8 or not an integer, bits > 512 -> UNSUPPORTED; bad pointers, seq length >
  *   capacity -> INVALID_ARGUMENT; workspace too small -> BUFFER_TOO_SMALL; launch -> HIP.
  */
