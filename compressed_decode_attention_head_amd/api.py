@@ -100,9 +100,10 @@ class CompressedKVCache:
         self.k_calib = torch.from_numpy(np.concatenate(self.k_blobs_host)).to(self.device)
         self.v_calib = torch.from_numpy(np.concatenate(self.v_blobs_host)).to(self.device)
         tiles = self.capacity // 64
-        self.k_codes = torch.zeros(max(4, self.batch * self.n_kv * tiles * 2 * self.k_bits), dtype=torch.int32,
+        # + 4 words: decode attention copies whole 16-byte units, up to 15 bytes past the end
+        self.k_codes = torch.zeros(4 + self.batch * self.n_kv * tiles * 2 * self.k_bits, dtype=torch.int32,
                                    device=self.device)
-        self.v_codes = torch.zeros(max(4, self.batch * self.n_kv * tiles * 2 * self.v_bits), dtype=torch.int32,
+        self.v_codes = torch.zeros(4 + self.batch * self.n_kv * tiles * 2 * self.v_bits, dtype=torch.int32,
                                    device=self.device)
         self._struct = N.Cache(self.batch, self.n_kv, 128, self.k_bits, self.v_bits, self.v_tiles,
                                self.capacity, self.k_calib.data_ptr(), self.v_calib.data_ptr(),

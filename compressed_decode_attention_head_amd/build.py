@@ -44,6 +44,8 @@ def _compile(src):
 
 def build(verbose=False):
     os.makedirs(OBJ, exist_ok=True)
+    if os.path.exists(LIB):
+        os.remove(LIB)          # a failed build must not leave an older library behind
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"

@@ -8,10 +8,10 @@ namespace {
 using namespace aatc_attn;
 
 constexpr size_t kLdsLimit = 160 * 1024;
-constexpr size_t kStaticLds = 2048;          // __shared__ scalars of the kernel (rounded up)
+// __shared__ arrays of the kernel: the probability rows plus scalars (rounded up)
+constexpr size_t kStaticLds = static_cast<size_t>(CW) * TG * PROW_BYTES + 2048;
 
 int vtiles_bucket(int vt) {
-  if (vt <= 8) return 8;
   if (vt <= 12) return 12;
   if (vt <= 16) return 16;
   if (vt <= 24) return 24;
@@ -21,7 +21,8 @@ int vtiles_bucket(int vt) {
 int round1k(int64_t x) { return static_cast<int>((x + 1023) / 1024 * 1024); }
 
 struct Plan {
-  int NP, NVB, LIMBS, WAVES, S, tpw, half, chunk, nbuf, ks, vs, prec;
+  int NP, NVB, LIMBS, S, tpw, half, prec;
+  int nslot, slot_bytes, ksz, gs;
   size_t lds;
   size_t part_bytes, offs_bytes;
   int SC, rec_bytes;
@@ -29,54 +30,49 @@ struct Plan {
   bool fits;
 };
 
-// Tiles per wave fill 256 CUs x WAVES waves once; each wave keeps as many of its tiles in
-// LDS as fit (all of them when possible, else double-buffered chunks, else single chunks).
+int round16(int64_t x) { return static_cast<int>((x + 15) / 16 * 16); }
+
+// Tiles per wave fill 256 CUs x CW waves once; each wave gets a ring of LDS slots (one tile
+// each), as many as fit, at most its tile count.  A wave copies the next group's tiles while it
+// computes on the current group, so groups of gs tiles want 2 gs slots.
 Plan make_plan(const aatc_cache* c, int n_q, int64_t max_seq) {
   Plan p;
   const int kb = c->k_bits, vb = c->v_bits;
   p.NP = kb > 0 ? (kb + 127) / 128 : 1;
   p.half = (kb > 0 && kb - 128 * (p.NP - 1) <= 64) ? 1 : 0;
   p.NVB = vtiles_bucket(c->v_tiles);
-  p.WAVES = waves_for(p.NP, p.NVB);
   const int group = c->n_kv_heads > 0 ? n_q / c->n_kv_heads : 1;
   p.LIMBS = group <= 4 ? 3 : 2;
   p.prec = PHDR + 16 * (c->v_tiles > 0 ? c->v_tiles : 1);
   const int64_t ntiles = (max_seq + 63) / 64;
   const int64_t seqs = static_cast<int64_t>(c->batch) * c->n_kv_heads;
-  const int64_t target_waves = 256 * static_cast<int64_t>(p.WAVES);
+  const int64_t target_waves = 256 * static_cast<int64_t>(CW);
   int64_t tpw = (ntiles * seqs + target_waves - 1) / target_waves;
   if (tpw < 1) tpw = 1;
-  if (tpw > 64) tpw = 64;
   p.tpw = static_cast<int>(tpw);
-  int64_t S = (ntiles + p.WAVES * tpw - 1) / (p.WAVES * tpw);
+  int64_t S = (ntiles + CW * tpw - 1) / (CW * tpw);
   if (S < 1) S = 1;
   p.S = static_cast<int>(S);
-  const size_t fixed = UNION_BYTES + static_cast<size_t>(p.WAVES) * PL_WAVE + TAB_BYTES + DMA_PAD + kStaticLds;
-  const size_t per_wave = (kLdsLimit - fixed) / p.WAVES;
-  auto area = [&](int ch, int nbuf) {
-    const int ks = kb > 0 ? round1k(8LL * kb * ch + 16) : 0;
-    const int vs = vb > 0 ? round1k(8LL * vb * ch + 16) : 0;
-    return static_cast<size_t>(nbuf) * (ks + vs);
-  };
-  p.chunk = 1;
-  p.nbuf = 1;
-  p.fits = false;
-  if (area(p.tpw, 1) <= per_wave) {
-    p.chunk = p.tpw;
-    p.nbuf = 1;
-    p.fits = true;
+  // slot: K bytes of a tile (plus up to 15 bytes of alignment), then V
+  p.ksz = kb > 0 ? round16(8LL * kb + 16) : 0;
+  const int vsz = vb > 0 ? round16(8LL * vb + 16) : 0;
+  p.slot_bytes = p.ksz + vsz > 0 ? p.ksz + vsz : 16;
+  const size_t avail = kLdsLimit - kStaticLds - FIXED_LDS - DMA_PAD;
+  int ns = static_cast<int>(avail / (static_cast<size_t>(CW) * p.slot_bytes));
+  if (ns > p.tpw) ns = p.tpw;
+  p.nslot = ns;
+  p.fits = ns >= 1;
+  if (ns >= p.tpw) {
+    p.gs = p.tpw < TG ? p.tpw : TG;      // every tile has its own slot
   } else {
-    for (int ch = p.tpw - 1; ch >= 1; --ch)
-      if (area(ch, 2) <= per_wave) { p.chunk = ch; p.nbuf = 2; p.fits = true; break; }
-    if (!p.fits && area(1, 1) <= per_wave) { p.chunk = 1; p.nbuf = 1; p.fits = true; }
+    p.gs = ns / 2 < TG ? ns / 2 : TG;
+    if (p.gs < 1) p.gs = 1;
   }
-  p.ks = kb > 0 ? round1k(8LL * kb * p.chunk + 16) : 0;
-  p.vs = vb > 0 ? round1k(8LL * vb * p.chunk + 16) : 0;
-  // the workgroup merge reuses the tile area: WAVES x NVB x 32 lanes x float4
-  size_t tiles = static_cast<size_t>(p.WAVES) * p.nbuf * (p.ks + p.vs) + DMA_PAD;
-  const size_t merge = static_cast<size_t>(p.WAVES) * p.NVB * 32 * 16;
-  if (tiles < merge) tiles = merge;
-  p.lds = UNION_BYTES + static_cast<size_t>(p.WAVES) * PL_WAVE + TAB_BYTES + tiles;
+  size_t ring = static_cast<size_t>(CW) * (ns > 0 ? ns : 1) * p.slot_bytes + DMA_PAD;
+  // the merge reuses the ring: CW x NVB x 32 lanes x float4
+  const size_t merge = static_cast<size_t>(CW) * p.NVB * 32 * 16;
+  if (ring < merge) ring = merge;
+  p.lds = FIXED_LDS + ring;
   if (p.lds + kStaticLds > kLdsLimit) p.fits = false;
   p.part_bytes = static_cast<size_t>(seqs) * p.S * group * p.prec * 4;
   p.offs_bytes = static_cast<size_t>(seqs) * 8 * 4;
@@ -93,13 +89,14 @@ Plan make_plan(const aatc_cache* c, int n_q, int64_t max_seq) {
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-bool dispatch(const Plan& p, const AttnArgs& a, dim3 grid, hipStream_t st, hipError_t* err) {
+bool dispatch(const Plan& p, const AttnArgs& a, const aatc_calib* kc, const aatc_calib* vc, dim3 grid, hipStream_t st,
+              hipError_t* err) {
   bool found = false;
   switch (p.NP) {
-    case 1: *err = launch_np<1>(p.NVB, p.LIMBS, a, grid, p.lds, st, &found); break;
-    case 2: *err = launch_np<2>(p.NVB, p.LIMBS, a, grid, p.lds, st, &found); break;
-    case 3: *err = launch_np<3>(p.NVB, p.LIMBS, a, grid, p.lds, st, &found); break;
-    case 4: *err = launch_np<4>(p.NVB, p.LIMBS, a, grid, p.lds, st, &found); break;
+    case 1: *err = launch_np<1>(p.half, p.NVB, p.LIMBS, a, kc, vc, grid, p.lds, st, &found); break;
+    case 2: *err = launch_np<2>(p.half, p.NVB, p.LIMBS, a, kc, vc, grid, p.lds, st, &found); break;
+    case 3: *err = launch_np<3>(p.half, p.NVB, p.LIMBS, a, kc, vc, grid, p.lds, st, &found); break;
+    case 4: *err = launch_np<4>(p.half, p.NVB, p.LIMBS, a, kc, vc, grid, p.lds, st, &found); break;
   }
   return found;
 }
@@ -141,8 +138,8 @@ aatc_status aatc_decode_attn(const aatc_cache* c, const float* q, int32_t n_q, c
   if (ws_bytes < need) return aatc::fail(AATC_ERR_BUFFER_TOO_SMALL, "workspace %zu < %zu", ws_bytes, need);
   if (!p.fits) return aatc::fail(AATC_ERR_UNSUPPORTED, "tiles of %d+%d bits do not fit LDS", c->k_bits, c->v_bits);
   AttnArgs a;
-  a.kcal = static_cast<const aatc_calib*>(c->k_calib);
-  a.vcal = static_cast<const aatc_calib*>(c->v_calib);
+  const aatc_calib* kcal = static_cast<const aatc_calib*>(c->k_calib);
+  const aatc_calib* vcal = static_cast<const aatc_calib*>(c->v_calib);
   a.kcodes = static_cast<const uint32_t*>(c->k_codes);
   a.vcodes = static_cast<const uint32_t*>(c->v_codes);
   a.tiles_per_seq = c->capacity_tokens / 64;
@@ -153,8 +150,6 @@ aatc_status aatc_decode_attn(const aatc_cache* c, const float* q, int32_t n_q, c
   a.max_seq = max_seq;
   a.q = q;
   a.scale2 = (scale > 0.f ? scale : 1.0f / sqrtf(static_cast<float>(AATC_D))) * 1.4426950408889634f;
-  a.out = out;
-  a.lse = lse;
   char* w = static_cast<char*>(ws);
   a.part = reinterpret_cast<float*>(w);
   a.offs = reinterpret_cast<float*>(w + align256(p.part_bytes));
@@ -163,19 +158,17 @@ aatc_status aatc_decode_attn(const aatc_cache* c, const float* q, int32_t n_q, c
   a.prec = p.prec;
   a.kB = c->k_bits;
   a.vB = c->v_bits;
-  a.np_half = p.half;
-  a.chunk = p.chunk;
-  a.nbuf = p.nbuf;
-  a.ks_bytes = p.ks;
-  a.vs_bytes = p.vs;
+  a.nslot = p.nslot;
+  a.slot_bytes = p.slot_bytes;
+  a.ksz = p.ksz;
+  a.gs = p.gs;
   auto st = static_cast<hipStream_t>(stream);
   const dim3 grid(p.S, c->n_kv_heads, c->batch);
   hipError_t err = hipSuccess;
-  const bool ok = dispatch(p, a, grid, st, &err);
+  const bool ok = dispatch(p, a, kcal, vcal, grid, st, &err);
   if (!ok) return aatc::fail(AATC_ERR_UNSUPPORTED, "plan NP=%d NVB=%d", p.NP, p.NVB);
   if (err != hipSuccess) return aatc::fail(AATC_ERR_HIP, "decode_attn launch: %s", hipGetErrorString(err));
   CombArgs cb;
-  cb.vcal = a.vcal;
   cb.part = a.part;
   cb.offs = a.offs;
   cb.n_kv = c->n_kv_heads;
@@ -192,7 +185,7 @@ aatc_status aatc_decode_attn(const aatc_cache* c, const float* q, int32_t n_q, c
   err = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_combine), hipFuncAttributeMaxDynamicSharedMemorySize,
                             static_cast<int>(p.comb_lds));
   if (err != hipSuccess) return aatc::fail(AATC_ERR_HIP, "decode_attn combine attribute: %s", hipGetErrorString(err));
-  hipLaunchKernelGGL(k_attn_combine, dim3(group, c->n_kv_heads, c->batch), dim3(CNT), p.comb_lds, st, cb);
+  hipLaunchKernelGGL(k_attn_combine, dim3(group, c->n_kv_heads, c->batch), dim3(CNT), p.comb_lds, st, cb, vcal);
   err = hipGetLastError();
   if (err != hipSuccess) return aatc::fail(AATC_ERR_HIP, "decode_attn combine launch: %s", hipGetErrorString(err));
   return AATC_OK;

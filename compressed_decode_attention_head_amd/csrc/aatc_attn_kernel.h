@@ -19,20 +19,24 @@
 //   scores, LIMBS=3: 4 q-head slots x 3 limbs (22-bit weights), GQA <= 4;
 //   values: 8 q-head slots x 2 limbs of a 14-bit probability.
 //
-// k_attn_main, grid (S splits, KV heads, batch), WAVES waves per workgroup; a workgroup owns
-// a contiguous range of 64-token tiles of one sequence, each wave `tpw` consecutive tiles:
-//   1. the K tables and the queries, then the wave's tiles, are copied straight from HBM into
-//      LDS with global_load_lds (no registers); the small tables land first,
-//   2. while the tiles fly, the workgroup rotates the queries and builds the limb weights,
-//   3. each wave streams its tiles out of LDS: scores -> online softmax -> PV, int32 sums,
-//   4. the waves merge in LDS and the workgroup writes one partial record per q head:
+// k_attn_main, grid (S splits, KV heads, batch): a workgroup of CW waves owns a contiguous
+// range of 64-token tiles of one sequence, each wave `tpw` consecutive tiles.  Each wave
+//   1. copies its share of the K tables and the queries, and its first tiles, straight from
+//      HBM into LDS with global_load_lds (no registers), into a ring of per-wave tile slots,
+//   2. rotates the queries and builds the limb weights with the others while they fly,
+//   3. streams its tiles out of LDS in groups, keeping the next tiles' copies in flight:
+//      scores -> one running-max update per group -> probability rows -> PV, all in int32,
+//   4. merges with the others in LDS; the workgroup writes one partial record per q head:
 //      (running max, sum of probabilities, softmax-weighted code sum per V field column).
+// Waves synchronise through LDS counters with wavefront-scope ordering only (a workgroup
+// barrier would first wait for every copy in flight); every such wait is bounded.
 // k_attn_combine, grid (q heads per KV head, KV heads, batch): merges the S records of a
 // q head, folds field columns into channel code sums, dequantizes, applies R_V^T and writes
 // out and lse.  The kernel boundary orders the records; no atomics, no workspace clearing.
 #pragma once
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cmath>
 #include <cstdint>
 
@@ -46,20 +50,21 @@ constexpr int PS = 16383;                 // probability scale: 14-bit fixed poi
 // to 16383 and none exceeds it
 constexpr float PKN_BIAS = -2.000067f;
 constexpr int PHDR = 4;                   // record header floats: max (log2 units), sum, 0, 0
-constexpr int UNION_BYTES = 3 * 8 * D * 4;    // prologue q / q~ / alpha
+constexpr int CW = 8;                     // waves per workgroup
+constexpr int NTH = CW * 64;
+constexpr int AHEAD = 2;                  // tiles a wave copies before its prologue
+constexpr int TG = 4;                     // at most this many tiles per score group
+constexpr int UNION_BYTES = 3 * 8 * D * 4;    // q / q~ / alpha
 constexpr int TAB_BYTES = 2304;           // K delta32 | o32 | bits | plane_channel | plane_bit
-constexpr int PL_WAVE = 16 * 64;          // one wave's probability limb rows (16 x 64 bytes)
-constexpr int DMA_PAD = 1024;             // LDS slack after the tile areas (bounded over-reads)
+constexpr int WA_BYTES = 4 * 2 * 4 * 64 * 4;  // limb weight operands, NP <= 4
+constexpr int FIXED_LDS = UNION_BYTES + TAB_BYTES + WA_BYTES;   // then the ring
+constexpr int PROW_BYTES = 16 * 64;       // probability rows of one tile (16 rows x 64 bytes)
+constexpr int DMA_PAD = 1024;             // LDS slack after the ring (bounded over-reads)
+constexpr int SPIN_LIMIT = 1 << 22;       // polls before a wait gives up (results become NaN)
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
 
-// Waves per workgroup of the main kernel: 16 (four per SIMD) while the accumulators leave
-// room for it, else 8.
-constexpr int waves_for(int np, int nvb) { return (np + nvb) > 0 ? 8 : 8; }
-
 struct AttnArgs {
-  const aatc_calib* kcal;
-  const aatc_calib* vcal;
   const uint32_t* kcodes;
   const uint32_t* vcodes;
   int64_t tiles_per_seq;
@@ -68,16 +73,19 @@ struct AttnArgs {
   int64_t max_seq;
   const float* q;
   float scale2;                       // softmax scale * log2(e)
-  float* out;
-  float* lse;
   float* part;                        // [batch*n_kv][S][group][prec] partial records
   float* offs;                        // [batch*n_kv][8] lse offset per q head (log2 units)
   int S, tpw, prec;                   // splits per sequence, tiles per wave, floats per record
   int kB, vB;
-  int np_half;                        // 1 if the last K pair carries <= 64 planes
-  int chunk;                          // tiles per LDS chunk
-  int nbuf;                           // 1 or 2 chunk buffers per wave
-  int ks_bytes, vs_bytes;             // K / V area of one chunk buffer (multiples of 1024)
+  int nslot;                          // ring slots per compute wave (>= 1)
+  int slot_bytes, ksz;                // bytes per slot (K area first, ksz bytes)
+  int gs;                             // tiles per score group, 1..TG, <= nslot
+};
+
+// Wave handshakes, in static LDS.
+struct Sync {
+  int arrive[CW];                     // barriers passed, per wave
+  int broken;                         // a bounded wait gave up
 };
 
 __device__ inline int row_max16_i(int x) {
@@ -96,14 +104,61 @@ __device__ inline unsigned row_sum16_u(unsigned x) {
   return x;
 }
 
-__device__ inline float wave_max(float x) {
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
+// Value of lane (lane ^ M) for M in {1, 2, 4, 8, 16, 32}, without a round trip through LDS
+// memory (DPP, swizzle and permlane forms).
+template <int M>
+__device__ inline float xor_lanes(float x, int lane) {
+  const int xi = __float_as_int(x);
+  if (M == 1) return __int_as_float(__builtin_amdgcn_update_dpp(0, xi, 0xB1, 0xf, 0xf, false));   // quad [1,0,3,2]
+  if (M == 2) return __int_as_float(__builtin_amdgcn_update_dpp(0, xi, 0x4E, 0xf, 0xf, false));   // quad [2,3,0,1]
+  if (M == 4) return __int_as_float(__builtin_amdgcn_ds_swizzle(xi, 0x101F));                     // xor 4 in 32
+  if (M == 8) return __int_as_float(__builtin_amdgcn_update_dpp(0, xi, 0x128, 0xf, 0xf, false));  // row_ror 8
+  if (M == 16) return __int_as_float(__builtin_amdgcn_ds_swizzle(xi, 0x401F));                    // xor 16 in 32
+  const auto p = __builtin_amdgcn_permlane32_swap(static_cast<unsigned>(xi), static_cast<unsigned>(xi), false, false);
+  return __int_as_float(static_cast<int>(lane < 32 ? p[1] : p[0]));
 }
 
-__device__ inline float wave_sum(float x) {
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  return x;
+__device__ inline float wave_max_x(float x) {
+  const int lane = threadIdx.x & 63;
+  x = fmaxf(x, xor_lanes<1>(x, lane));
+  x = fmaxf(x, xor_lanes<2>(x, lane));
+  x = fmaxf(x, xor_lanes<4>(x, lane));
+  x = fmaxf(x, xor_lanes<8>(x, lane));
+  x = fmaxf(x, xor_lanes<16>(x, lane));
+  return fmaxf(x, xor_lanes<32>(x, lane));
+}
+
+__device__ inline float wave_sum_x(float x) {
+  const int lane = threadIdx.x & 63;
+  x += xor_lanes<1>(x, lane);
+  x += xor_lanes<2>(x, lane);
+  x += xor_lanes<4>(x, lane);
+  x += xor_lanes<8>(x, lane);
+  x += xor_lanes<16>(x, lane);
+  return x + xor_lanes<32>(x, lane);
+}
+
+// Unnormalised Walsh-Hadamard transform (Sylvester order) of the 128 values x0 = v[lane],
+// x1 = v[64 + lane] held by one wave: butterflies on index bit 6 in registers, bits 0..5
+// across lanes (their order does not matter).
+template <int M>
+__device__ inline void fwht_stage(float& x0, float& x1, int lane) {
+  const float p0 = xor_lanes<M>(x0, lane), p1 = xor_lanes<M>(x1, lane);
+  const float sg = (lane & M) ? -1.f : 1.f;
+  x0 = fmaf(sg, x0, p0);
+  x1 = fmaf(sg, x1, p1);
+}
+
+__device__ inline void fwht128(float& x0, float& x1, int lane) {
+  const float t = x0;
+  x0 = t + x1;
+  x1 = t - x1;
+  fwht_stage<1>(x0, x1, lane);
+  fwht_stage<2>(x0, x1, lane);
+  fwht_stage<4>(x0, x1, lane);
+  fwht_stage<8>(x0, x1, lane);
+  fwht_stage<16>(x0, x1, lane);
+  fwht_stage<32>(x0, x1, lane);
 }
 
 // Orders this wave's LDS accesses for the compiler.  A wavefront's LDS instructions execute
@@ -114,7 +169,8 @@ __device__ inline void wave_sync_lds() {
   __builtin_amdgcn_wave_barrier();
 }
 
-// Waits until at most n (0..63) vector-memory instructions of this wave are outstanding.
+// Waits until at most n (0..63) vector-memory instructions of this wave are outstanding
+// (n outside 0..63: until none are).
 __device__ inline void wait_vmcnt(int n) {
 #define AATC_VMW(k) case k: __builtin_amdgcn_s_waitcnt(((k) & 15) | (((k) >> 4) << 14) | (7 << 4) | (15 << 8)); break;
   switch (n) {
@@ -129,6 +185,34 @@ __device__ inline void wait_vmcnt(int n) {
     default: __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); break;
   }
 #undef AATC_VMW
+}
+
+// LDS accesses the compiler does not order against copies in flight.  Any atomic or
+// volatile LDS access is preceded by a wait for every outstanding vector-memory instruction,
+// copies into LDS included; these hand-written forms are not (the load waits for itself).
+__device__ inline uint32_t lds_addr(const void* p) { return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p)); }
+__device__ inline int lds_load_now(const int* p) {
+  int v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(p)) : "memory");
+  return v;
+}
+__device__ inline void lds_store(int* p, int v) {
+  asm volatile("ds_write_b32 %0, %1" : : "v"(lds_addr(p)), "v"(v) : "memory");
+}
+
+// Barrier of the CW waves on per-wave LDS flags (`phase` counts the barriers this wave has
+// passed).  Unlike s_barrier with a workgroup fence it does not wait for this wave's copies in
+// flight: a wave's LDS operations complete in issue order, so its writes before the flag are
+// visible once the flag is.  Bounded: after SPIN_LIMIT polls the workgroup is marked broken.
+__device__ inline void compute_barrier(Sync* sy, int& phase, int lane) {
+  ++phase;
+  if (lane == 0) lds_store(&sy->arrive[__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)], phase);
+  for (int it = 0; it < SPIN_LIMIT; ++it) {
+    const int v = lane < CW ? lds_load_now(&sy->arrive[lane]) : phase;
+    if (__builtin_amdgcn_ballot_w64(v < phase) == 0) return;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  if (lane == 0) lds_store(&sy->broken, 1);
 }
 
 // Plane base (within a token's B-bit string) of the K window that lane group `grp` reads for
@@ -153,20 +237,6 @@ struct Lim<3> {
   __device__ static int limb(int l, int v) { return l == 0 ? (v >> 14) : (l == 1 ? ((v >> 7) & 127) : (v & 127)); }
 };
 
-// Copies bytes [start, start + n*1024) (start aligned down to 16) of one sequence's packed
-// words into LDS, 16 bytes per lane per instruction; lanes past `end` re-read the last valid
-// 16 bytes (their LDS slots are padding).
-__device__ inline void dma_block(const char* start, const char* end, const char* base, uint8_t* dst, int n,
-                                 int lane) {
-  const char* last = reinterpret_cast<const char*>((reinterpret_cast<uintptr_t>(end) - 16) & ~static_cast<uintptr_t>(15));
-  last = last < base ? base : last;            // allocations are >= 16 bytes and 16-byte aligned
-  for (int ii = 0; ii < n; ++ii) {
-    const char* p = start + (ii * 64 + lane) * 16;
-    p = p > last ? last : p;
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(p), dst + ii * 1024, 16, 0, 0);
-  }
-}
-
 // Copies nwords 32-bit words src[0..nwords) to LDS dst[0..nwords), 64 words per instruction,
 // instruction k issued by wave k % WAVES.  Lanes past nwords re-read src[0]; their LDS words
 // (up to the next multiple of 64) are padding.  Returns the running instruction index.
@@ -181,155 +251,184 @@ __device__ inline int dma_words(const void* src, void* dst, int nwords, int k, i
   return k;
 }
 
-template <int NP, int NVB, int LIMBS>
-__global__ __launch_bounds__(waves_for(NP, NVB) * 64) void k_attn_main(AttnArgs a) {
-  constexpr int WAVES = waves_for(NP, NVB);
-  constexpr int NT = WAVES * 64;
+// Copies the 16-byte units covering bytes [p, p + n) (p rounded down to 16) to LDS dst, one
+// instruction per 64 units (lanes past the last unit idle).  Returns the instructions issued.
+__device__ inline int dma_bytes(const char* p, int n, uint8_t* dst, int lane) {
+  const char* a = reinterpret_cast<const char*>(reinterpret_cast<uintptr_t>(p) & ~static_cast<uintptr_t>(15));
+  const int units = static_cast<int>((p + n - a + 15) >> 4);
+  int ni = 0;
+  for (int i = 0; i < units; i += 64, ++ni)
+    if (i + lane < units)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(a + (i + lane) * 16), dst + i * 16, 16, 0, 0);
+  return ni;
+}
+
+template <int NP, bool HALF, int NVB, int LIMBS>
+__global__ __launch_bounds__(NTH) void k_attn_main(AttnArgs a, const aatc_calib* __restrict__ kcal,
+                                                   const aatc_calib* __restrict__ vcal) {
   using LM = Lim<LIMBS>;
   extern __shared__ __align__(16) unsigned char smem[];
   float* qs = reinterpret_cast<float*>(smem);                       // [8][128]   q
-  float* qt = qs + 8 * D;                                           // [8][128]   R_K q
+  float* qt = qs + 8 * D;                                           // [8][128]   R_K q (KLT)
   float* al = qt + 8 * D;                                           // [8][128]   alpha
-  uint8_t* pl = smem + UNION_BYTES;                                 // [WAVES][16][64] P limbs
-  int* wa_lds = reinterpret_cast<int*>(pl);                         // [NP*2*4*64] (prologue)
-  uint8_t* tab = pl + WAVES * PL_WAVE;
+  uint8_t* tab = smem + UNION_BYTES;
   float* t_delta = reinterpret_cast<float*>(tab);                   // [128]
   float* t_o = t_delta + D;                                         // [128]
   const uint8_t* t_bits = tab + 1024;                               // [128]
   const uint8_t* t_pch = tab + 1280;                                // [<=512]
   const uint8_t* t_pbit = tab + 1792;                               // [<=512]
-  uint8_t* chunks = tab + TAB_BYTES;                                // [WAVES][nbuf][ks+vs]
-  float* mg = reinterpret_cast<float*>(chunks);                     // merge: [WAVES][NVB][32 lanes][4]
-  __shared__ float s_m[WAVES][8], s_l[WAVES][8];
+  int* wa_lds = reinterpret_cast<int*>(smem + UNION_BYTES + TAB_BYTES);        // [NP*2*4*64]
+  uint8_t* ring = smem + FIXED_LDS;                                 // [CW][nslot][slot]
+  // probability limb rows live in their own static array: no tile copy can write them, so
+  // reading them needs no wait on the copies in flight
+  __shared__ __align__(16) uint8_t pl[CW * TG * PROW_BYTES];        // [CW][TG][16][64]
+  float* mg = reinterpret_cast<float*>(ring);                       // merge: [CW][NVB][32][4]
+  __shared__ float s_m[CW][8], s_l[CW][8];
   __shared__ float s_M[8], s_L[8], esc[8];
   __shared__ int wexp[8];
+  __shared__ Sync sy;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);      // wave-uniform, kept scalar
   const int n16 = lane & 15, grp = lane >> 4;
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int bh = b * a.n_kv + h;
-  const aatc_calib* kc = a.kcal + h;
-  const aatc_calib* vc = a.vcal + h;
+  const aatc_calib* kc = kcal + h;
+  const aatc_calib* vc = vcal + h;
   const int G = a.group;
   const int Bk = a.kB, Bv = a.vB;
-  int64_t seq = a.seq_lens ? static_cast<int64_t>(a.seq_lens[b]) : a.max_seq;
-  seq = seq < 0 ? 0 : (seq > a.max_seq ? a.max_seq : seq);     // never read past the cache
-  const int64_t ntiles = (seq + 63) / 64;
-  const int64_t t0 = (static_cast<int64_t>(s) * WAVES + wave) * a.tpw;
-  const int64_t t1 = t0 + a.tpw < ntiles ? t0 + a.tpw : ntiles;
-
-  // ---- 1. K tables and queries to LDS (first, so they land before the tiles)
-  {
-    int k = 0;
-    k = dma_words<WAVES>(a.q + (static_cast<int64_t>(b) * a.n_q + h * G) * D, qs, G * D, k, wave, lane);
-    k = dma_words<WAVES>(kc->delta32, t_delta, D, k, wave, lane);
-    k = dma_words<WAVES>(kc->o32, t_o, D, k, wave, lane);
-    k = dma_words<WAVES>(kc->bits, tab + 1024, D / 4, k, wave, lane);
-    k = dma_words<WAVES>(kc->plane_channel, tab + 1280, (Bk + 3) / 4, k, wave, lane);
-    k = dma_words<WAVES>(kc->plane_bit, tab + 1792, (Bk + 3) / 4, k, wave, lane);
-    for (int e = G * D + tid; e < 8 * D; e += NT) qs[e] = 0.f;
-  }
-
-  // ---- 2. this wave's tiles: chunk 0 (and chunk 1 when double-buffered)
-  const bool half = a.np_half != 0;
+  int64_t seq64 = a.seq_lens ? static_cast<int64_t>(a.seq_lens[b]) : a.max_seq;
+  seq64 = seq64 < 0 ? 0 : (seq64 > a.max_seq ? a.max_seq : seq64);     // never read past the cache
+  const int seq = static_cast<int>(seq64);                      // tokens per sequence < 2^31
+  const int ntiles = (seq + 63) / 64;
+  const int NS = a.nslot;
   const int64_t kbytes = 8 * static_cast<int64_t>(Bk), vbytes = 8 * static_cast<int64_t>(Bv);
   const char* kseq = reinterpret_cast<const char*>(a.kcodes) + static_cast<int64_t>(bh) * a.tiles_per_seq * kbytes;
   const char* vseq = reinterpret_cast<const char*>(a.vcodes) + static_cast<int64_t>(bh) * a.tiles_per_seq * vbytes;
-  const char* kend = kseq + a.tiles_per_seq * kbytes;
-  const char* vend = vseq + a.tiles_per_seq * vbytes;
-  const int CH = a.chunk, NBUF = a.nbuf;
-  const int nki = Bk > 0 ? a.ks_bytes >> 10 : 0, nvi = Bv > 0 ? a.vs_bytes >> 10 : 0;
-  uint8_t* wbuf = chunks + static_cast<size_t>(wave) * NBUF * (a.ks_bytes + a.vs_bytes);
-  // the copies depend on arguments only; the blob headers are checked after they are issued
-  const int64_t ntile_w = t1 > t0 ? t1 - t0 : 0;
-  const int nchunks_dma = static_cast<int>((ntile_w + CH - 1) / CH);
-  // K/V data of chunk c start this many bytes into their areas (16-byte alignment)
-  auto kpad = [&](int c) { return static_cast<int>(reinterpret_cast<uintptr_t>(kseq + (t0 + c * CH) * kbytes) & 15); };
-  auto vpad = [&](int c) { return static_cast<int>(reinterpret_cast<uintptr_t>(vseq + (t0 + c * CH) * vbytes) & 15); };
-  auto issue = [&](int c, int buf) {
-    uint8_t* kb = wbuf + buf * (a.ks_bytes + a.vs_bytes);
-    const char* ks = kseq + (t0 + c * CH) * kbytes;
-    const char* vs = vseq + (t0 + c * CH) * vbytes;
-    dma_block(reinterpret_cast<const char*>(reinterpret_cast<uintptr_t>(ks) & ~static_cast<uintptr_t>(15)), kend,
-              reinterpret_cast<const char*>(a.kcodes), kb, nki, lane);
-    dma_block(reinterpret_cast<const char*>(reinterpret_cast<uintptr_t>(vs) & ~static_cast<uintptr_t>(15)), vend,
-              reinterpret_cast<const char*>(a.vcodes), kb + a.ks_bytes, nvi, lane);
+  auto first_tile = [&](int w) { return (s * CW + w) * a.tpw; };
+  auto tiles_of = [&](int w) {
+    const int t0 = first_tile(w);
+    const int n = ntiles - t0 < a.tpw ? ntiles - t0 : a.tpw;
+    return n > 0 ? n : 0;
   };
-  int inflight = 0;
-  if (nchunks_dma > 0) { issue(0, 0); inflight += nki + nvi; }
-  if (nchunks_dma > 1 && NBUF == 2) { issue(1, 1); inflight += nki + nvi; }
-  const int n4 = vc->n_fields4, n2 = vc->n_fields2, n1 = vc->n_fields1;
+  auto slot_of = [&](int w, int r) { return ring + (w * NS + r % NS) * a.slot_bytes; };
+
+  const int n4 = vc->n_fields4, n2 = vc->n_fields2, n1 = vc->n_fields1;   // scalar loads
   const int T4 = (n4 + 15) >> 4, T2 = (n2 + 15) >> 4, T1 = (n1 + 15) >> 4;
   const int NV = T4 + T2 + T1;
   const bool ok = kc->magic == AATC_MAGIC && vc->magic == AATC_MAGIC && kc->total_bits == Bk &&
-                  vc->total_bits == Bv && NV <= NVB && PHDR + 16 * NV <= a.prec;
-  // a bad blob streams nothing (issued copies are still waited for below) and yields NaN
-  const int nchunks = ok ? nchunks_dma : 0;
-  wait_vmcnt(inflight);                  // this wave's table copies have landed
-  __syncthreads();
-
-  // ---- 3. prologue: q~ = R_K q, alpha, exponents, lse offsets, limb weights
+                  vc->total_bits == Bv && n4 >= 0 && n2 >= 0 && n1 >= 0 && NV <= NVB && PHDR + 16 * NV <= a.prec;
   const int rot = kc->rotation;
-  if (rot == AATC_ROT_WHT) {
-    // Sylvester-ordered fast Walsh-Hadamard transform, one wave per head slot, then 1/sqrt(128)
-    if (wave < 8) {
-      float x0 = qs[wave * D + lane], x1 = qs[wave * D + 64 + lane];
-      const float y = x0;
-      x0 = y + x1;
-      x1 = y - x1;
-#pragma unroll
-      for (int len = 1; len < 64; len <<= 1) {
-        const float o0 = __shfl_xor(x0, len), o1 = __shfl_xor(x1, len);
-        const bool hi = (lane & len) != 0;
-        x0 = hi ? o0 - x0 : x0 + o0;
-        x1 = hi ? o1 - x1 : x1 + o1;
-      }
-      qt[wave * D + lane] = x0 * 0.08838834764831845f;
-      qt[wave * D + 64 + lane] = x1 * 0.08838834764831845f;
+  const int nw = ok ? tiles_of(wave) : 0;   // a bad blob streams nothing
+  const int tw0 = first_tile(wave);
+
+  if (tid < CW) sy.arrive[tid] = 0;
+  if (tid == 0) sy.broken = 0;
+  __syncthreads();                       // the only workgroup barrier (no copy in flight yet)
+  int phase = 0;
+
+  // ---- 1. copies: this wave's share of the tables, then its first tiles
+  {
+    int k = 0;
+    k = dma_words<CW>(a.q + (static_cast<int64_t>(b) * a.n_q + h * G) * D, qs, G * D, k, wave, lane);
+    k = dma_words<CW>(kc->delta32, t_delta, D, k, wave, lane);
+    k = dma_words<CW>(kc->o32, t_o, D, k, wave, lane);
+    k = dma_words<CW>(kc->bits, tab + 1024, D / 4, k, wave, lane);
+    k = dma_words<CW>(kc->plane_channel, tab + 1280, (Bk + 3) / 4, k, wave, lane);
+    k = dma_words<CW>(kc->plane_bit, tab + 1792, (Bk + 3) / 4, k, wave, lane);
+  }
+  // tile r of this wave goes to ring slot r % NS; copies are issued in tile order, so tile r
+  // has landed once at most (instructions issued after it) copies are outstanding
+  auto kaddr = [&](int r) { return kseq + (tw0 + r) * kbytes; };
+  auto vaddr = [&](int r) { return vseq + (tw0 + r) * vbytes; };
+  auto ninstr = [&](int r) {
+    const int uk = Bk > 0 ? static_cast<int>((((reinterpret_cast<uintptr_t>(kaddr(r)) & 15) + kbytes + 15) >> 4)) : 0;
+    const int uv = Bv > 0 ? static_cast<int>((((reinterpret_cast<uintptr_t>(vaddr(r)) & 15) + vbytes + 15) >> 4)) : 0;
+    return ((uk + 63) >> 6) + ((uv + 63) >> 6);
+  };
+  int nxt = 0;                           // next tile of this wave to copy
+  auto issue_upto = [&](int limit) {     // copy tiles [nxt, min(limit, nw))
+    const int lim = limit < nw ? limit : nw;
+    for (; nxt < lim; ++nxt) {
+      uint8_t* sl = slot_of(wave, nxt);
+      if (Bk > 0) dma_bytes(kaddr(nxt), static_cast<int>(kbytes), sl, lane);
+      if (Bv > 0) dma_bytes(vaddr(nxt), static_cast<int>(vbytes), sl + a.ksz, lane);
     }
-  } else if (rot == AATC_ROT_KLT) {
-    // row i of R_K: NT/128 threads per row, eight q heads per thread
-    constexpr int TPR = NT / D, CPT = D / TPR;
+  };
+  auto wait_tile = [&](int r) {
+    int after = 0;
+    for (int t = r + 1; t < nxt; ++t) after += ninstr(t);
+    wait_vmcnt(after);
+  };
+  issue_upto(AHEAD < NS ? AHEAD : NS);
+  {
+    int after = 0;                       // this wave's table copies have landed ...
+    for (int t = 0; t < nxt; ++t) after += ninstr(t);
+    wait_vmcnt(after);
+  }
+  compute_barrier(&sy, phase, lane);     // ... and so have everyone else's
+
+  // ---- 1. prologue: q~ = R_K q, alpha, exponents, lse offsets, limb weights
+  // wave x (< 8) owns head slot x: q~ at channels lane and 64 + lane
+  float y0 = 0.f, y1 = 0.f;
+  if (rot == AATC_ROT_KLT) {
+    // row i of R_K: 4 threads per row, eight q heads per thread
+    constexpr int TPR = CW * 64 / D, CPT = D / TPR;
+    static_assert(TPR == 4, "threads per row");
     const int i = tid / TPR, qq = tid % TPR;
     float part[8];
 #pragma unroll
     for (int g = 0; g < 8; ++g) part[g] = 0.f;
     const float2* row = reinterpret_cast<const float2*>(kc->R32 + i * D + CPT * qq);
-#pragma unroll
+#pragma unroll 4
     for (int c2 = 0; c2 < CPT / 2; ++c2) {
-      const float2 r = row[c2];
+      const float2 rr = row[c2];
       const int j = CPT * qq + 2 * c2;
 #pragma unroll
-      for (int g = 0; g < 8; ++g) part[g] += r.x * qs[g * D + j] + r.y * qs[g * D + j + 1];
+      for (int g = 0; g < 8; ++g) part[g] += rr.x * qs[g * D + j] + rr.y * qs[g * D + j + 1];
     }
 #pragma unroll
-    for (int g = 0; g < 8; ++g)
-#pragma unroll
-      for (int o = 1; o < TPR; o <<= 1) part[g] += __shfl_xor(part[g], o);
+    for (int g = 0; g < 8; ++g) {
+      part[g] += xor_lanes<1>(part[g], lane);
+      part[g] += xor_lanes<2>(part[g], lane);
+    }
     if (qq == 0)
 #pragma unroll
       for (int g = 0; g < 8; ++g) qt[g * D + i] = part[g];
+    compute_barrier(&sy, phase, lane);
+    y0 = qt[wave * D + lane];
+    y1 = qt[wave * D + 64 + lane];
   } else {
-    for (int e = tid; e < 8 * D; e += NT) qt[e] = qs[e];
+    y0 = qs[wave * D + lane];
+    y1 = qs[wave * D + 64 + lane];
+    if (rot == AATC_ROT_WHT) {
+      // Sylvester-ordered fast Walsh-Hadamard transform across the wave, then 1/sqrt(128)
+      fwht128(y0, y1, lane);
+      y0 *= 0.08838834764831845f;
+      y1 *= 0.08838834764831845f;
+    }
   }
-  __syncthreads();
-  if (wave < 8) {
-    // one wave per head slot: alpha, the lse offset and the weight exponent
+  {
+    // alpha, the lse offset and the weight exponent of head slot `wave` (zero past G)
     const int g = wave;
+    if (g >= G) {
+      y0 = 0.f;
+      y1 = 0.f;
+    }
     float m = 0.f, off = 0.f;
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int i = lane + 64 * r;
       const int bi = t_bits[i];
-      const float v = qt[g * D + i];
+      const float v = r ? y1 : y0;
       const float alpha = bi ? v * t_delta[i] * a.scale2 : 0.f;
       al[g * D + i] = alpha;
       if (bi) m = fmaxf(m, fabsf(alpha) * static_cast<float>(1 << (bi - 1)));
       const float o = bi ? t_o[i] - t_delta[i] * (static_cast<float>(1 << (bi - 1)) - 0.5f) : t_o[i];
       off += v * o * a.scale2;
     }
-    m = wave_max(m);
-    off = wave_sum(off);
+    m = wave_max_x(m);
+    off = wave_sum_x(off);
     int e = 0;
     if (m > 0.f) {
       frexpf(m, &e);
@@ -341,23 +440,32 @@ __global__ __launch_bounds__(waves_for(NP, NVB) * 64) void k_attn_main(AttnArgs 
       if (s == 0 && g < G) a.offs[bh * 8 + g] = off;
     }
   }
-  __syncthreads();
+  compute_barrier(&sy, phase, lane);
   {
-    const int nw = NP * 2 * 4 * 64;
+    // limb operand dwords: (pair u, half hh, dword j, lane) -> 4 bytes m of row (lane%16)
+    const int nwd = NP * 2 * 4 * 64;
     const int wmaxq = (1 << LM::WBITS) - 1;
-    for (int e = tid; e < nw; e += NT) {
+    for (int e = tid; e < nwd; e += CW * 64) {
       const int ln = e & 63, jj = (e >> 6) & 3, hh = (e >> 8) & 1, u = e >> 9;
       const int row = ln & 15, lg = ln >> 4;
       const int l = row / LM::PROW;
       const int g = row % LM::PROW;
-      const bool hp = half && u == NP - 1;
-      uint32_t word = 0;
+      const bool hp = HALF && u == NP - 1;
+      const bool live = g < G && l < LIMBS && !(hp && hh);
+      int chs[4], kbs[4];
+#pragma unroll
       for (int m = 0; m < 4; ++m) {
         const int p = plane_base(u, lg, hp) + 8 * m + (hp ? jj : 4 * hh + jj);
+        const bool in = live && p < Bk;
+        chs[m] = in ? t_pch[p] : -1;
+        kbs[m] = in ? t_pbit[p] : 0;
+      }
+      uint32_t word = 0;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
         int val = 0;
-        if (p < Bk && g < G && l < LIMBS && !(hp && hh)) {
-          const int ch = t_pch[p], kb = t_pbit[p];
-          int wq = static_cast<int>(rintf(ldexpf(al[g * D + ch], kb + wexp[g])));
+        if (chs[m] >= 0) {
+          int wq = static_cast<int>(rintf(ldexpf(al[g * D + chs[m]], kbs[m] + wexp[g])));
           wq = wq > wmaxq ? wmaxq : (wq < -wmaxq ? -wmaxq : wq);
           val = LM::limb(l, wq);
         }
@@ -366,7 +474,7 @@ __global__ __launch_bounds__(waves_for(NP, NVB) * 64) void k_attn_main(AttnArgs 
       wa_lds[e] = static_cast<int>(word);
     }
   }
-  __syncthreads();
+  compute_barrier(&sy, phase, lane);
   v4i wa[NP][2];
 #pragma unroll
   for (int u = 0; u < NP; ++u)
@@ -374,9 +482,6 @@ __global__ __launch_bounds__(waves_for(NP, NVB) * 64) void k_attn_main(AttnArgs 
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
       for (int j = 0; j < 4; ++j) wa[u][hh][j] = wa_lds[((u * 2 + hh) * 4 + j) * 64 + lane];
-  __syncthreads();                       // wa_lds aliases the probability rows
-  for (int e = tid; e < WAVES * PL_WAVE / 4; e += NT) reinterpret_cast<uint32_t*>(pl)[e] = 0u;
-  __syncthreads();
 
   // head slots this lane holds after the limb merge: LIMBS=2 pair a {0,4,1,5}[grp] and
   // pair b {2,6,3,7}[grp]; LIMBS=3 head grp
@@ -388,14 +493,24 @@ __global__ __launch_bounds__(waves_for(NP, NVB) * 64) void k_attn_main(AttnArgs 
   const int tok0 = 16 * (n16 >> 2) + 4 * (n16 & 3);
   int kofs[NP];
 #pragma unroll
-  for (int u = 0; u < NP; ++u) kofs[u] = tok0 * Bk + plane_base(u, grp, half && u == NP - 1);
-  uint8_t* pw = pl + wave * PL_WAVE;
+  for (int u = 0; u < NP; ++u) kofs[u] = tok0 * Bk + plane_base(u, grp, HALF && u == NP - 1);
+  uint8_t* pw = pl + wave * TG * PROW_BYTES;
   // probability rows (limb l, head slot x) = row 8l + x; dword n16 of a row sits in 16-byte
   // quad (n16/4) ^ (row%4)
   auto prow_addr = [&](int row) { return row * 64 + 16 * ((n16 >> 2) ^ (row & 3)) + 4 * (n16 & 3); };
   const int wa0 = prow_addr(ha), wa1 = prow_addr(8 + ha);
   const int wb0 = prow_addr(hb), wb1 = prow_addr(8 + hb);
   const int prd = n16 * 64 + 16 * (grp ^ (n16 & 3));
+  // LDS byte offset (within a tile's V area) of the V word(s) this lane reads for column group v
+  int voff[NVB];
+#pragma unroll
+  for (int v = 0; v < NVB; ++v) {
+    if (v < T4) voff[v] = 4 * (8 * ((v << 4) + n16) + 2 * grp);
+    else if (v < T4 + T2) voff[v] = 4 * (8 * n4 + 4 * (((v - T4) << 4) + n16) + grp);
+    else if (v < NV) voff[v] = 4 * (8 * n4 + 4 * n2 + 2 * (((v - T4 - T2) << 4) + n16) + (grp >> 1));
+    else voff[v] = 0;                    // unused group: harmless read of the tile's first words
+  }
+  const uint32_t sh1 = 4 * (grp & 1);
 
   v4i acc[NVB];
 #pragma unroll
@@ -404,82 +519,106 @@ __global__ __launch_bounds__(waves_for(NP, NVB) * 64) void k_attn_main(AttnArgs 
   unsigned la = 0, lb = 0;
   const v2u16 ones = {1, 1};
 
-  // ---- 4. stream the chunks out of LDS
-  if (!ok) wait_vmcnt(0);
-  for (int c = 0; c < nchunks; ++c) {
-    const int buf = NBUF == 2 ? (c & 1) : 0;
-    if (NBUF == 2 && c + 1 < nchunks) wait_vmcnt(nki + nvi);
-    else wait_vmcnt(0);
-    wave_sync_lds();
-    const uint8_t* kb = wbuf + buf * (a.ks_bytes + a.vs_bytes);
-    const uint32_t* kchunk = reinterpret_cast<const uint32_t*>(kb + kpad(c));
-    const uint32_t* vchunk = reinterpret_cast<const uint32_t*>(kb + a.ks_bytes + vpad(c));
-    const int64_t ctile0 = t0 + static_cast<int64_t>(c) * CH;
-    const int nt = static_cast<int>(t1 - ctile0 < CH ? t1 - ctile0 : CH);
-    for (int it = 0; it < nt; ++it) {
-      const int64_t tile = ctile0 + it;
-      const uint32_t* kl = kchunk + it * 2 * Bk;
-      const uint32_t* vl = vchunk + it * 2 * Bv;
-      // scores: 4 token groups; integer scores of head pair a / b (LIMBS=3: one head)
-      int sa[4], sb[4];
+  // ---- 2. stream this wave's tiles, groups of gs
+  bool started = false;
+#pragma unroll 1
+  for (int g0 = 0; g0 < nw; g0 += a.gs) {
+    const int ng = nw - g0 < a.gs ? nw - g0 : a.gs;
+
+    // opaque copies of the V class bounds: keeps the compiler from hoisting one condition
+    // register pair per column group out of the loop
+    int cT4 = T4, cT42 = T4 + T2, cNV = NV;
+    asm volatile("" : "+s"(cT4), "+s"(cT42), "+s"(cNV));
+    int sa[TG][4], sb[TG][4];
+    // scores, tile by tile as each lands: 4 token groups of 16 = 4 independent MFMA chains
+#pragma unroll
+    for (int g = 0; g < TG; ++g) {
+      const int rr = g0 + (g < ng ? g : 0);             // past the group's end: recompute, masked
+      if (g < ng) {
+        // keep AHEAD tiles in flight; slots of tiles before g0 are free, this group's are not
+        issue_upto(g0 + g + 1 + AHEAD < g0 + NS ? g0 + g + 1 + AHEAD : g0 + NS);
+        wait_tile(g0 + g);
+        wave_sync_lds();
+      }
+      const int64_t tile = tw0 + rr;
+      // opaque slot offset: per-(tile, tau, pair) addresses are not worth registers
+      int kt = static_cast<int>((slot_of(wave, rr) - ring) + ((reinterpret_cast<uintptr_t>(kseq) + tile * kbytes) & 15));
+      asm volatile("" : "+v"(kt));
+      const uint8_t* klt = ring + kt;
+      v4i cc[4];
 #pragma unroll
       for (int tau = 0; tau < 4; ++tau) {
-        v4i cc = {0, 0, 0, 0};
+        cc[tau] = v4i{0, 0, 0, 0};
 #pragma unroll
         for (int u = 0; u < NP; ++u) {
-          const bool hp = half && u == NP - 1;
+          const bool hp = HALF && u == NP - 1;
           const int o = kofs[u] + tau * Bk;
-          const uint32_t* w = kl + (o >> 5);
+          const uint32_t* w = reinterpret_cast<const uint32_t*>(klt) + (o >> 5);
           const uint32_t dw = __builtin_amdgcn_alignbit(w[1], w[0], static_cast<uint32_t>(o));
           v4i b0;
 #pragma unroll
           for (int j = 0; j < 4; ++j) b0[j] = static_cast<int>((dw >> j) & 0x01010101u);
-          cc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa[u][0], b0, cc, 0, 0, 0);
+          cc[tau] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa[u][0], b0, cc[tau], 0, 0, 0);
           if (!hp) {
             v4i b1;
 #pragma unroll
             for (int j = 0; j < 4; ++j) b1[j] = static_cast<int>((dw >> (j + 4)) & 0x01010101u);
-            cc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa[u][1], b1, cc, 0, 0, 0);
+            cc[tau] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa[u][1], b1, cc[tau], 0, 0, 0);
           }
         }
+      }
+#pragma unroll
+      for (int tau = 0; tau < 4; ++tau) {
         if (LIMBS == 2) {
-          const auto p01 = __builtin_amdgcn_permlane32_swap(static_cast<unsigned>(cc[0]), static_cast<unsigned>(cc[1]),
-                                                            false, false);
-          const auto p23 = __builtin_amdgcn_permlane32_swap(static_cast<unsigned>(cc[2]), static_cast<unsigned>(cc[3]),
-                                                            false, false);
-          sa[tau] = (static_cast<int>(p01[0]) << 7) + static_cast<int>(p01[1]);
-          sb[tau] = (static_cast<int>(p23[0]) << 7) + static_cast<int>(p23[1]);
+          const auto p01 = __builtin_amdgcn_permlane32_swap(static_cast<unsigned>(cc[tau][0]),
+                                                            static_cast<unsigned>(cc[tau][1]), false, false);
+          const auto p23 = __builtin_amdgcn_permlane32_swap(static_cast<unsigned>(cc[tau][2]),
+                                                            static_cast<unsigned>(cc[tau][3]), false, false);
+          sa[g][tau] = (static_cast<int>(p01[0]) << 7) + static_cast<int>(p01[1]);
+          sb[g][tau] = (static_cast<int>(p23[0]) << 7) + static_cast<int>(p23[1]);
         } else {
           // 4x4 transpose of 16-lane blocks: rows (limb l, head r) -> lane group = head
-          const auto x02 = __builtin_amdgcn_permlane32_swap(static_cast<unsigned>(cc[0]), static_cast<unsigned>(cc[2]),
-                                                            false, false);
-          const auto x13 = __builtin_amdgcn_permlane32_swap(static_cast<unsigned>(cc[1]), static_cast<unsigned>(cc[3]),
-                                                            false, false);
-          const auto y01 = __builtin_amdgcn_permlane16_swap(x02[0], x13[0], false, false);   // limb 0, limb 1
-          const auto y23 = __builtin_amdgcn_permlane16_swap(x02[1], x13[1], false, false);   // limb 2, unused
-          sa[tau] = (static_cast<int>(y01[0]) << 14) + (static_cast<int>(y01[1]) << 7) + static_cast<int>(y23[0]);
-          sb[tau] = 0;
+          const auto x02 = __builtin_amdgcn_permlane32_swap(static_cast<unsigned>(cc[tau][0]),
+                                                            static_cast<unsigned>(cc[tau][2]), false, false);
+          const auto x13 = __builtin_amdgcn_permlane32_swap(static_cast<unsigned>(cc[tau][1]),
+                                                            static_cast<unsigned>(cc[tau][3]), false, false);
+          const auto y01 = __builtin_amdgcn_permlane16_swap(x02[0], x13[0], false, false);   // limb 0, 1
+          const auto y23 = __builtin_amdgcn_permlane16_swap(x02[1], x13[1], false, false);   // limb 2, -
+          sa[g][tau] = (static_cast<int>(y01[0]) << 14) + (static_cast<int>(y01[1]) << 7) + static_cast<int>(y23[0]);
+          sb[g][tau] = INT_MIN;
         }
       }
-      const int64_t nvalid = seq - tile * 64;
-      const bool ragged = nvalid < 64;
-      if (ragged) {
+    }
+    // tiles past the group's end and tokens past the sequence's end take no part
+    const bool masked = ng < TG || seq - (tw0 + g0 + ng - 1) * 64 < 64;
+    if (masked) {
 #pragma unroll
-        for (int tau = 0; tau < 4; ++tau)
-          if (tok0 + tau >= nvalid) { sa[tau] = INT_MIN; sb[tau] = INT_MIN; }
+      for (int g = 0; g < TG; ++g) {
+        const int nvalid = g < ng ? seq - (tw0 + g0 + g) * 64 : 0;
+        if (nvalid < 64) {
+#pragma unroll
+          for (int tau = 0; tau < 4; ++tau)
+            if (tok0 + tau >= nvalid) { sa[g][tau] = INT_MIN; sb[g][tau] = INT_MIN; }
+        }
       }
-      // a tile has at least one visible token, so its maxima are real scores
-      const int ita = row_max16_i(max(max(sa[0], sa[1]), max(sa[2], sa[3])));
-      const int itb = LIMBS == 2 ? row_max16_i(max(max(sb[0], sb[1]), max(sb[2], sb[3]))) : INT_MIN;
-      // online softmax: rescale the integer accumulators when a running max grows
-      if (__ballot(ita > ima || itb > imb)) {
-        const int nma = max(ima, ita), nmb = max(imb, itb);
-        const float fa = (ima == INT_MIN) ? 0.f : __builtin_amdgcn_exp2f(static_cast<float>(ima - nma) * esa);
-        const float fb = (imb == INT_MIN) ? 0.f : __builtin_amdgcn_exp2f(static_cast<float>(imb - nmb) * esb);
+    }
+    // group maxima (every tile has a visible token, so they are real scores)
+    int mxa = INT_MIN, mxb = INT_MIN;
+#pragma unroll
+    for (int g = 0; g < TG; ++g) {
+      mxa = max(mxa, max(max(sa[g][0], sa[g][1]), max(sa[g][2], sa[g][3])));
+      if (LIMBS == 2) mxb = max(mxb, max(max(sb[g][0], sb[g][1]), max(sb[g][2], sb[g][3])));
+    }
+    mxa = row_max16_i(mxa);
+    if (LIMBS == 2) mxb = row_max16_i(mxb);
+    // online softmax: rescale the integer accumulators when a running max grows
+    if (__ballot(mxa > ima || mxb > imb)) {
+      const int nma = max(ima, mxa), nmb = max(imb, mxb);
+      if (started) {
+        const float fa = __builtin_amdgcn_exp2f(static_cast<float>(ima - nma) * esa);
+        const float fb = LIMBS == 2 ? __builtin_amdgcn_exp2f(static_cast<float>(imb - nmb) * esb) : 0.f;
         la = static_cast<unsigned>(rintf(static_cast<float>(la) * fa));
         lb = static_cast<unsigned>(rintf(static_cast<float>(lb) * fb));
-        ima = nma;
-        imb = nmb;
         float fr[4];
         if (LIMBS == 2) {
           // acc register r of lane group grp holds head 4*(grp&1)+r; the factor of head hd
@@ -508,81 +647,99 @@ __global__ __launch_bounds__(waves_for(NP, NVB) * 64) void k_attn_main(AttnArgs 
           for (int r = 0; r < 4; ++r)
             acc[v][r] = static_cast<int>(rintf(static_cast<float>(acc[v][r]) * fr[r]));
       }
-      // probabilities in 14-bit fixed point (pknorm rounds 65535 * x), two 7-bit limbs per
-      // byte row: the four tokens of this lane fill one dword per (head, limb)
-      {
-        float pa[4];
-#pragma unroll
-        for (int tau = 0; tau < 4; ++tau)
-          pa[tau] = __builtin_amdgcn_exp2f(fmaf(static_cast<float>(sa[tau] - ima), esa, PKN_BIAS));
-        if (ragged) {
-#pragma unroll
-          for (int tau = 0; tau < 4; ++tau) pa[tau] = (tok0 + tau >= nvalid) ? 0.f : pa[tau];
-        }
-        const v2u16 q01 = __builtin_amdgcn_cvt_pknorm_u16(pa[0], pa[1]);
-        const v2u16 q23 = __builtin_amdgcn_cvt_pknorm_u16(pa[2], pa[3]);
-        la = __builtin_amdgcn_udot2(q01, ones, la, false);
-        la = __builtin_amdgcn_udot2(q23, ones, la, false);
-        const uint32_t u01 = __builtin_bit_cast(uint32_t, q01), u23 = __builtin_bit_cast(uint32_t, q23);
-        const uint32_t hi = __builtin_amdgcn_perm((u23 >> 7) & 0x007F007Fu, (u01 >> 7) & 0x007F007Fu, 0x06040200u);
-        const uint32_t lo = __builtin_amdgcn_perm(u23 & 0x007F007Fu, u01 & 0x007F007Fu, 0x06040200u);
-        *reinterpret_cast<uint32_t*>(pw + wa0) = hi;
-        *reinterpret_cast<uint32_t*>(pw + wa1) = lo;
-      }
-      if (LIMBS == 2) {
-        float pb[4];
-#pragma unroll
-        for (int tau = 0; tau < 4; ++tau)
-          pb[tau] = __builtin_amdgcn_exp2f(fmaf(static_cast<float>(sb[tau] - imb), esb, PKN_BIAS));
-        if (ragged) {
-#pragma unroll
-          for (int tau = 0; tau < 4; ++tau) pb[tau] = (tok0 + tau >= nvalid) ? 0.f : pb[tau];
-        }
-        const v2u16 q01 = __builtin_amdgcn_cvt_pknorm_u16(pb[0], pb[1]);
-        const v2u16 q23 = __builtin_amdgcn_cvt_pknorm_u16(pb[2], pb[3]);
-        lb = __builtin_amdgcn_udot2(q01, ones, lb, false);
-        lb = __builtin_amdgcn_udot2(q23, ones, lb, false);
-        const uint32_t u01 = __builtin_bit_cast(uint32_t, q01), u23 = __builtin_bit_cast(uint32_t, q23);
-        const uint32_t hi = __builtin_amdgcn_perm((u23 >> 7) & 0x007F007Fu, (u01 >> 7) & 0x007F007Fu, 0x06040200u);
-        const uint32_t lo = __builtin_amdgcn_perm(u23 & 0x007F007Fu, u01 & 0x007F007Fu, 0x06040200u);
-        *reinterpret_cast<uint32_t*>(pw + wb0) = hi;
-        *reinterpret_cast<uint32_t*>(pw + wb1) = lo;
-      }
-      wave_sync_lds();
-      const uint4 pv = *reinterpret_cast<const uint4*>(pw + prd);
-      const v4i pA = {static_cast<int>(pv.x), static_cast<int>(pv.y), static_cast<int>(pv.z), static_cast<int>(pv.w)};
-      // PV on packed V fields (width-uniform column groups: w4 | w2 | w1); columns past a
-      // class's field count read neighbouring words and are never used
-#pragma unroll
-      for (int v = 0; v < NVB; ++v) {
-        if (v < NV) {
-          v4i bv;
-          if (v < T4) {
-            const uint2 d2 = *reinterpret_cast<const uint2*>(vl + 8 * ((v << 4) + n16) + 2 * grp);
-            const uint32_t m4 = 0x0F0F0F0Fu;
-            bv[0] = static_cast<int>(d2.x & m4);
-            bv[1] = static_cast<int>((d2.x >> 4) & m4);
-            bv[2] = static_cast<int>(d2.y & m4);
-            bv[3] = static_cast<int>((d2.y >> 4) & m4);
-          } else if (v < T4 + T2) {
-            const uint32_t d = vl[8 * n4 + 4 * (((v - T4) << 4) + n16) + grp];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) bv[r] = static_cast<int>((d >> (2 * r)) & 0x03030303u);
-          } else {
-            const uint32_t d = vl[8 * n4 + 4 * n2 + 2 * (((v - T4 - T2) << 4) + n16) + (grp >> 1)] >> (4 * (grp & 1));
-#pragma unroll
-            for (int r = 0; r < 4; ++r) bv[r] = static_cast<int>((d >> r) & 0x01010101u);
-          }
-          acc[v] = __builtin_amdgcn_mfma_i32_16x16x64_i8(pA, bv, acc[v], 0, 0, 0);
-        }
-      }
-      wave_sync_lds();
+      ima = nma;
+      imb = nmb;
     }
-    if (NBUF == 2 && c + 2 < nchunks) issue(c + 2, buf);
-    else if (NBUF == 1 && c + 1 < nchunks) issue(c + 1, 0);
+    started = true;
+    // probabilities in 14-bit fixed point (pknorm rounds 65535 * x), two 7-bit limbs; the
+    // four tokens of this lane fill one dword per (head, limb); tile g uses rows at g*1024
+#pragma unroll
+    for (int g = 0; g < TG; ++g) {
+      if (g < ng) {
+        uint8_t* pg = pw + g * PROW_BYTES;
+        {
+          float pa[4];
+#pragma unroll
+          for (int tau = 0; tau < 4; ++tau)
+            pa[tau] = __builtin_amdgcn_exp2f(fmaf(static_cast<float>(sa[g][tau] - ima), esa, PKN_BIAS));
+          if (masked) {
+#pragma unroll
+            for (int tau = 0; tau < 4; ++tau) pa[tau] = sa[g][tau] == INT_MIN ? 0.f : pa[tau];
+          }
+          const v2u16 q01 = __builtin_amdgcn_cvt_pknorm_u16(pa[0], pa[1]);
+          const v2u16 q23 = __builtin_amdgcn_cvt_pknorm_u16(pa[2], pa[3]);
+          la = __builtin_amdgcn_udot2(q01, ones, la, false);
+          la = __builtin_amdgcn_udot2(q23, ones, la, false);
+          const uint32_t u01 = __builtin_bit_cast(uint32_t, q01), u23 = __builtin_bit_cast(uint32_t, q23);
+          *reinterpret_cast<uint32_t*>(pg + wa0) =
+              __builtin_amdgcn_perm((u23 >> 7) & 0x007F007Fu, (u01 >> 7) & 0x007F007Fu, 0x06040200u);
+          *reinterpret_cast<uint32_t*>(pg + wa1) = __builtin_amdgcn_perm(u23 & 0x007F007Fu, u01 & 0x007F007Fu, 0x06040200u);
+        }
+        if (LIMBS == 2) {
+          float pb[4];
+#pragma unroll
+          for (int tau = 0; tau < 4; ++tau)
+            pb[tau] = __builtin_amdgcn_exp2f(fmaf(static_cast<float>(sb[g][tau] - imb), esb, PKN_BIAS));
+          if (masked) {
+#pragma unroll
+            for (int tau = 0; tau < 4; ++tau) pb[tau] = sb[g][tau] == INT_MIN ? 0.f : pb[tau];
+          }
+          const v2u16 q01 = __builtin_amdgcn_cvt_pknorm_u16(pb[0], pb[1]);
+          const v2u16 q23 = __builtin_amdgcn_cvt_pknorm_u16(pb[2], pb[3]);
+          lb = __builtin_amdgcn_udot2(q01, ones, lb, false);
+          lb = __builtin_amdgcn_udot2(q23, ones, lb, false);
+          const uint32_t u01 = __builtin_bit_cast(uint32_t, q01), u23 = __builtin_bit_cast(uint32_t, q23);
+          *reinterpret_cast<uint32_t*>(pg + wb0) =
+              __builtin_amdgcn_perm((u23 >> 7) & 0x007F007Fu, (u01 >> 7) & 0x007F007Fu, 0x06040200u);
+          *reinterpret_cast<uint32_t*>(pg + wb1) = __builtin_amdgcn_perm(u23 & 0x007F007Fu, u01 & 0x007F007Fu, 0x06040200u);
+        }
+      }
+    }
+    wave_sync_lds();
+    // PV on packed V fields (width-uniform column groups: w4 | w2 | w1); columns past a
+    // class's field count read neighbouring words and are never used
+#pragma unroll
+    for (int g = 0; g < TG; ++g) {
+      if (g < ng) {
+        const uint4 pv = *reinterpret_cast<const uint4*>(pw + g * PROW_BYTES + prd);
+        const v4i pA = {static_cast<int>(pv.x), static_cast<int>(pv.y), static_cast<int>(pv.z), static_cast<int>(pv.w)};
+        const int64_t tile = tw0 + g0 + g;
+        int vt = static_cast<int>((slot_of(wave, g0 + g) - ring) + a.ksz +
+                                  ((reinterpret_cast<uintptr_t>(vseq) + tile * vbytes) & 15));
+        asm volatile("" : "+v"(vt));
+        const uint8_t* vl = ring + vt;
+        uint32_t x0[NVB], x1[NVB];
+#pragma unroll
+        for (int v = 0; v < NVB; ++v) {         // unconditional: no per-read waits
+          x0[v] = *reinterpret_cast<const uint32_t*>(vl + voff[v]);
+          x1[v] = *reinterpret_cast<const uint32_t*>(vl + voff[v] + 4);
+        }
+#pragma unroll
+        for (int v = 0; v < NVB; ++v) {
+          if (v < cNV) {
+            v4i bv;
+            if (v < cT4) {
+              bv[0] = static_cast<int>(x0[v] & 0x0F0F0F0Fu);
+              bv[1] = static_cast<int>((x0[v] >> 4) & 0x0F0F0F0Fu);
+              bv[2] = static_cast<int>(x1[v] & 0x0F0F0F0Fu);
+              bv[3] = static_cast<int>((x1[v] >> 4) & 0x0F0F0F0Fu);
+            } else if (v < cT42) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) bv[r] = static_cast<int>((x0[v] >> (2 * r)) & 0x03030303u);
+            } else {
+              const uint32_t d = x0[v] >> sh1;
+#pragma unroll
+              for (int r = 0; r < 4; ++r) bv[r] = static_cast<int>((d >> r) & 0x01010101u);
+            }
+            acc[v] = __builtin_amdgcn_mfma_i32_16x16x64_i8(pA, bv, acc[v], 0, 0, 0);
+          }
+        }
+      }
+    }
+    wave_sync_lds();                     // the group's slots and rows are reused next
   }
 
-  // ---- 5. workgroup merge in LDS
+  // ---- 3. workgroup merge in LDS (the ring is idle now: every wave's tiles have landed)
   la = row_sum16_u(la);
   lb = row_sum16_u(lb);
   const float ma = ima == INT_MIN ? -INFINITY : static_cast<float>(ima) * esa;
@@ -599,17 +756,21 @@ __global__ __launch_bounds__(waves_for(NP, NVB) * 64) void k_attn_main(AttnArgs 
     s_m[wave][lane] = -INFINITY;
     s_l[wave][lane] = 0.f;
   }
-  __syncthreads();                       // every wave is done with its tile area
-  if (tid < 8) {
+  compute_barrier(&sy, phase, lane);     // every tile copy has landed and been read
+  if (wave == 0 && lane < 8) {
     float m = -INFINITY;
-    for (int w = 0; w < WAVES; ++w) m = fmaxf(m, s_m[w][tid]);
+#pragma unroll
+    for (int w = 0; w < CW; ++w) m = fmaxf(m, s_m[w][lane]);
     float l = 0.f;
-    for (int w = 0; w < WAVES; ++w)
-      if (s_m[w][tid] != -INFINITY) l += s_l[w][tid] * __builtin_amdgcn_exp2f(s_m[w][tid] - m);
-    s_M[tid] = m;
-    s_L[tid] = l;
+#pragma unroll
+    for (int w = 0; w < CW; ++w) {
+      const float mw = s_m[w][lane];
+      l += mw == -INFINITY ? 0.f : s_l[w][lane] * __builtin_amdgcn_exp2f(mw - m);
+    }
+    s_M[lane] = m;
+    s_L[lane] = l;
   }
-  __syncthreads();
+  compute_barrier(&sy, phase, lane);
   {
     // limb merge: lanes 0..31 (limb 0 rows) take the limb-1 rows of lanes 32..63; lane
     // group grp<2 then holds head slots 4*grp + r, scaled to the workgroup max
@@ -638,22 +799,23 @@ __global__ __launch_bounds__(waves_for(NP, NVB) * 64) void k_attn_main(AttnArgs 
       }
     }
   }
-  __syncthreads();
-  // ---- 6. partial records: [max, sum, 0, 0, column sums]
+  compute_barrier(&sy, phase, lane);
+  // ---- 4. partial records: [max, sum, 0, 0, column sums]
   {
+    const bool good = ok && __hip_atomic_load(&sy.broken, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 0;
     const int ncol = ok ? 16 * NV : 0;     // a bad blob's field count may not fit a record
     float* rec = a.part + (static_cast<int64_t>(bh) * a.S + s) * G * a.prec;
-    for (int e = tid; e < G * ncol; e += NT) {
-      const int hd = e / ncol, col = e - hd * ncol;
-      const int v = col >> 4, ln = (col & 15) + 16 * (hd >> 2), r = hd & 3;
-      float sum = 0.f;
-#pragma unroll 4
-      for (int w = 0; w < WAVES; ++w) sum += mg[((w * NVB + v) * 32 + ln) * 4 + r];
-      rec[hd * a.prec + PHDR + col] = sum;
-    }
+    for (int hd = 0; hd < G; ++hd)
+      for (int col = tid; col < ncol; col += CW * 64) {
+        const int v = col >> 4, ln = (col & 15) + 16 * (hd >> 2), r = hd & 3;
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < CW; ++w) sum += mg[((w * NVB + v) * 32 + ln) * 4 + r];
+        rec[hd * a.prec + PHDR + col] = sum;
+      }
     if (tid < G) {
       float* r0 = rec + tid * a.prec;
-      r0[0] = ok ? s_M[tid] : NAN;
+      r0[0] = good ? s_M[tid] : NAN;
       r0[1] = s_L[tid];
       r0[2] = 0.f;
       r0[3] = 0.f;
@@ -666,7 +828,6 @@ constexpr int CNT = 256;                 // combine threads (4 waves)
 constexpr int CR_BYTES = D * D * 4;      // LDS for R_V (fp32) when the rotation is a KLT
 
 struct CombArgs {
-  const aatc_calib* vcal;
   const float* part;
   const float* offs;
   int n_kv, n_q, group, S, prec;
@@ -693,7 +854,7 @@ __device__ inline int dma_records(const float* rec0, int64_t stride, int q4, int
   return k;
 }
 
-__global__ __launch_bounds__(CNT) void k_attn_combine(CombArgs a) {
+__global__ __launch_bounds__(CNT) void k_attn_combine(CombArgs a, const aatc_calib* __restrict__ vcal) {
   extern __shared__ __align__(16) unsigned char csm[];
   float* recs = reinterpret_cast<float*>(csm);                        // [SC][prec]
   float* rv = reinterpret_cast<float*>(csm + a.rec_bytes);            // [128][128] (KLT)
@@ -709,7 +870,7 @@ __global__ __launch_bounds__(CNT) void k_attn_combine(CombArgs a) {
   const int g = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int G = a.group, S = a.S, prec = a.prec, SC = a.SC, q4 = prec / 4;
   const int bh = b * a.n_kv + h;
-  const aatc_calib* vc = a.vcal + h;
+  const aatc_calib* vc = vcal + h;      // header fields come in as scalar loads
   const float* rec0 = a.part + (static_cast<int64_t>(bh) * S * G + g) * prec;
   const int64_t stride = static_cast<int64_t>(G) * prec;
 
@@ -739,46 +900,42 @@ __global__ __launch_bounds__(CNT) void k_attn_combine(CombArgs a) {
     if (c0 > 0) dma_records(rec0 + c0 * stride, stride, q4, n * q4, csm, 0, wave, lane);
     wait_vmcnt(0);
     __syncthreads();
-    // chunk max; rescale what is already summed
-    float m = -INFINITY;
-    bool nan = false;
-    for (int sp = tid; sp < n; sp += CNT) {
-      const float v = recs[sp * prec];
-      nan |= v != v;
-      m = fmaxf(m, v);
-    }
-    m = wave_max(m);
-    nan = __ballot(nan) != 0;
-    if (lane == 0) {
-      red[wave][0] = m;
-      red[wave][1] = nan ? 1.f : 0.f;
+    if (wave == 0) {
+      // chunk max, split weights and probability sum, in one wave
+      float m = -INFINITY;
+      bool nan = false;
+      for (int sp = lane; sp < n; sp += 64) {
+        const float v = recs[sp * prec];
+        nan |= v != v;
+        m = fmaxf(m, v);
+      }
+      m = wave_max_x(m);
+      const float nM = fmaxf(M, m);
+      float l = 0.f;
+      for (int sp = lane; sp < n; sp += 64) {
+        const float v = recs[sp * prec];
+        const float w = (v == -INFINITY || nM == -INFINITY) ? 0.f : exp2f(v - nM);
+        wsl[sp] = w;
+        l += w * recs[sp * prec + 1];
+      }
+      l = wave_sum_x(l);
+      const bool anynan = __ballot(nan) != 0;
+      if (lane == 0) {
+        red[0][0] = nM;
+        red[0][1] = l;
+        red[1][0] = anynan ? 1.f : 0.f;
+      }
     }
     __syncthreads();
-    float cm = -INFINITY;
-    for (int w = 0; w < CNT / 64; ++w) {
-      cm = fmaxf(cm, red[w][0]);
-      bad |= red[w][1] != 0.f;
-    }
-    const float nM = fmaxf(M, cm);
+    const float nM = red[0][0];
     const float fold = (M == -INFINITY) ? 0.f : exp2f(M - nM);
-    float l = 0.f;
-    for (int sp = tid; sp < n; sp += CNT) {
-      const float v = recs[sp * prec];
-      const float w = (v == -INFINITY || nM == -INFINITY) ? 0.f : exp2f(v - nM);
-      wsl[sp] = w;
-      l += w * recs[sp * prec + 1];
-    }
-    l = wave_sum(l);
-    __syncthreads();                      // red is reused; wsl is complete
-    if (lane == 0) red[wave][0] = l;
-    __syncthreads();
-    float lc = 0.f;
-    for (int w = 0; w < CNT / 64; ++w) lc += red[w][0];
-    L = L * fold + lc;
+    bad |= red[1][0] != 0.f;
+    L = L * fold + red[0][1];
     M = nM;
     for (int col = tid; col < ncol; col += CNT) {
       float sacc = csum[col] * fold;
-      for (int sp = 0; sp < n; ++sp) sacc += wsl[sp] * recs[sp * prec + PHDR + col];
+#pragma unroll 8
+      for (int sp = 0; sp < n; ++sp) sacc = fmaf(wsl[sp], recs[sp * prec + PHDR + col], sacc);
       csum[col] = sacc;
     }
     __syncthreads();                      // recs, wsl and red are reused by the next chunk
@@ -805,16 +962,7 @@ __global__ __launch_bounds__(CNT) void k_attn_combine(CombArgs a) {
   if (rot == AATC_ROT_WHT) {
     if (wave == 0) {
       float x0 = yt[lane], x1 = yt[64 + lane];
-      const float y = x0;
-      x0 = y + x1;
-      x1 = y - x1;
-#pragma unroll
-      for (int len = 1; len < 64; len <<= 1) {
-        const float o0 = __shfl_xor(x0, len), o1 = __shfl_xor(x1, len);
-        const bool hi = (lane & len) != 0;
-        x0 = hi ? o0 - x0 : x0 + o0;
-        x1 = hi ? o1 - x1 : x1 + o1;
-      }
+      fwht128(x0, x1, lane);
       csum[lane] = x0 * 0.08838834764831845f;
       csum[64 + lane] = x1 * 0.08838834764831845f;
     }
@@ -846,37 +994,50 @@ __global__ __launch_bounds__(CNT) void k_attn_combine(CombArgs a) {
 }
 #endif
 
-template <int NP, int NVB, int LIMBS>
-hipError_t launch_one(const AttnArgs& a, dim3 grid, size_t lds, hipStream_t st) {
-  const void* fn = reinterpret_cast<const void*>(&k_attn_main<NP, NVB, LIMBS>);
+template <int NP, bool HALF, int NVB, int LIMBS>
+hipError_t launch_one(const AttnArgs& a, const aatc_calib* kcal, const aatc_calib* vcal, dim3 grid, size_t lds,
+                      hipStream_t st) {
+  const void* fn = reinterpret_cast<const void*>(&k_attn_main<NP, HALF, NVB, LIMBS>);
   const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_attn_main<NP, NVB, LIMBS>), grid, dim3(waves_for(NP, NVB) * 64), lds, st, a);
+  hipLaunchKernelGGL((k_attn_main<NP, HALF, NVB, LIMBS>), grid, dim3(NTH), lds, st, a, kcal, vcal);
   return hipGetLastError();
 }
 
-template <int NP, int NVB>
-hipError_t launch_limbs(int limbs, const AttnArgs& a, dim3 grid, size_t lds, hipStream_t st) {
-  return limbs == 3 ? launch_one<NP, NVB, 3>(a, grid, lds, st) : launch_one<NP, NVB, 2>(a, grid, lds, st);
+template <int NP, bool HALF, int NVB>
+hipError_t launch_limbs(int limbs, const AttnArgs& a, const aatc_calib* kcal, const aatc_calib* vcal, dim3 grid,
+                        size_t lds, hipStream_t st) {
+  return limbs == 3 ? launch_one<NP, HALF, NVB, 3>(a, kcal, vcal, grid, lds, st)
+                    : launch_one<NP, HALF, NVB, 2>(a, kcal, vcal, grid, lds, st);
 }
 
-// One translation unit per NP instantiates this (all V buckets and limb modes).
-template <int NP>
-hipError_t launch_np(int nvb, int limbs, const AttnArgs& a, dim3 grid, size_t lds, hipStream_t st, bool* found) {
+template <int NP, bool HALF>
+hipError_t launch_nvb(int nvb, int limbs, const AttnArgs& a, const aatc_calib* kcal, const aatc_calib* vcal, dim3 grid,
+                      size_t lds, hipStream_t st, bool* found) {
   *found = true;
   switch (nvb) {
-    case 8: return launch_limbs<NP, 8>(limbs, a, grid, lds, st);
-    case 12: return launch_limbs<NP, 12>(limbs, a, grid, lds, st);
-    case 16: return launch_limbs<NP, 16>(limbs, a, grid, lds, st);
-    case 24: return launch_limbs<NP, 24>(limbs, a, grid, lds, st);
+    case 12: return launch_limbs<NP, HALF, 12>(limbs, a, kcal, vcal, grid, lds, st);
+    case 16: return launch_limbs<NP, HALF, 16>(limbs, a, kcal, vcal, grid, lds, st);
+    case 24: return launch_limbs<NP, HALF, 24>(limbs, a, kcal, vcal, grid, lds, st);
   }
   *found = false;
   return hipSuccess;
 }
 
-extern template hipError_t launch_np<1>(int, int, const AttnArgs&, dim3, size_t, hipStream_t, bool*);
-extern template hipError_t launch_np<2>(int, int, const AttnArgs&, dim3, size_t, hipStream_t, bool*);
-extern template hipError_t launch_np<3>(int, int, const AttnArgs&, dim3, size_t, hipStream_t, bool*);
-extern template hipError_t launch_np<4>(int, int, const AttnArgs&, dim3, size_t, hipStream_t, bool*);
+// One translation unit per NP instantiates this (both pair kinds, all V buckets and limb modes).
+template <int NP>
+hipError_t launch_np(int half, int nvb, int limbs, const AttnArgs& a, const aatc_calib* kcal, const aatc_calib* vcal,
+                     dim3 grid, size_t lds, hipStream_t st, bool* found) {
+  return half ? launch_nvb<NP, true>(nvb, limbs, a, kcal, vcal, grid, lds, st, found)
+              : launch_nvb<NP, false>(nvb, limbs, a, kcal, vcal, grid, lds, st, found);
+}
+
+#define AATC_LAUNCH_NP_SIG(N)                                                                                \
+  hipError_t launch_np<N>(int, int, int, const AttnArgs&, const aatc_calib*, const aatc_calib*, dim3, size_t, \
+                          hipStream_t, bool*)
+extern template AATC_LAUNCH_NP_SIG(1);
+extern template AATC_LAUNCH_NP_SIG(2);
+extern template AATC_LAUNCH_NP_SIG(3);
+extern template AATC_LAUNCH_NP_SIG(4);
 
 }  // namespace aatc_attn

@@ -2,5 +2,5 @@
 #include "aatc_attn_kernel.h"
 
 namespace aatc_attn {
-template hipError_t launch_np<3>(int, int, const AttnArgs&, dim3, size_t, hipStream_t, bool*);
+template AATC_LAUNCH_NP_SIG(3);
 }  // namespace aatc_attn

@@ -127,9 +127,14 @@ typedef struct {
   int32_t reserved;
 } aatc_calib_params;
 
+/* Readable bytes a codes buffer must have past its last sequence's words: decode attention
+ * copies whole 16-byte units. */
+#define AATC_CODES_SLACK 16
+
 /* A compressed cache of one layer, one tensor pair: every pointer is device memory.
  * k_codes/v_codes hold batch*n_kv_heads*(capacity_tokens/64) tiles of 2*k_bits (2*v_bits)
- * words.  k_calib/v_calib point at n_kv_heads consecutive aatc_calib blobs whose
+ * words, followed by AATC_CODES_SLACK readable bytes (contents unused).  k_calib/v_calib
+ * point at n_kv_heads consecutive aatc_calib blobs whose
  * total_bits equal k_bits / v_bits (checked by the kernels: a mismatching head is skipped
  * and its decode-attention outputs are NaN).  A tensor with 0 bits may pass NULL codes. */
 typedef struct {
