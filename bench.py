@@ -36,6 +36,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true")
     p.add_argument("--quiet", action="store_true")
+    p.add_argument("--copy-calib", action="store_true",
+                   help="also run one plain 256 MiB device copy (scales HBM counters of a profiler run)")
     return p.parse_args()
 
 
@@ -71,6 +73,33 @@ def build_layer(cfg, layer, n_tokens, device):
     q = synth.queries(cfg.idx, layer, cfg.n_q_heads, cfg.n_kv_heads, ksample)
     qt = torch.from_numpy(np.broadcast_to(q, (cfg.batch,) + q.shape).copy()).to(device)
     return cache, qt, ksample
+
+
+KERNEL_SRC = os.path.join(ROOT, "compressed_decode_attention_head_amd", "csrc", "aatc_attn_kernel.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_attn_main_qwen7b_128k_wht133_hbm_traffic.txt")
+
+
+def kernel_source_hash():
+    import hashlib
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the cache pass from the committed counter summary, or None when
+    the summary is missing or was taken on another version of the kernel source."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if "=" in line and not line.startswith("#"):
+                    k, v = line.split("=", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+            return None
+        return float(kv["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def algorithmic_bytes(cfg, n_tokens, cache):
@@ -215,7 +244,33 @@ def main():
     enc_tok_s = n_tokens * cfg.batch / (enc_ms * 1e-3)
     del x
 
-    achieved = codes_b / (call_ms * 1e-3) / 1e9
+    # --- the dominant kernel alone: the cache pass (aatc_decode_attn_partial -> k_attn_main),
+    # HIP events around each launch on the stream it runs on; then the merge kernel the same way
+    def time_each(fn):
+        for cache, q, ws, out, lse in layers:
+            fn(cache, q, ws, out, lse)
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(max(3, args.steps // 4)):
+            for (e0, e1), lay in zip(evs, layers):
+                e0.record(st)
+                fn(*lay)
+                e1.record(st)
+            torch.cuda.synchronize()
+            ms += [e0.elapsed_time(e1) for e0, e1 in evs]
+        return float(np.mean(ms))
+
+    part_ms = time_each(lambda cache, q, ws, out, lse: cache.decode_attn_partial(q, n_tokens, ws))
+    merge_ms = time_each(lambda cache, q, ws, out, lse: cache.decode_attn_merge(q.shape[1], n_tokens, ws, out, lse))
+    log(args, "cache pass %.2f us, merge %.2f us per layer" % (part_ms * 1e3, merge_ms * 1e3))
+    achieved = codes_b / (part_ms * 1e-3) / 1e9
+    traffic = measured_traffic()
+    if args.copy_calib:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     res = {
         "metric": "decode-attn compressed-KV GB/s & % HBM peak at 128K ctx; encode tokens/s",
         "value": round(gbs, 2),
@@ -239,9 +294,10 @@ def main():
         "encode_tokens_per_s": round(enc_tok_s, 1),
         "encode_note": "one layer prefill, all KV heads, K and V, fp64 rotation+quantize",
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "k_attn (one launch per layer)",
-                     "bytes_per_launch": codes_b, "launch_us": round(call_ms * 1e3, 3)},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "k_attn_main (the cache pass, one launch per layer)",
+                     "bytes_per_launch": codes_b, "launch_us": round(part_ms * 1e3, 3),
+                     "merge_kernel_us": round(merge_ms * 1e3, 3), "call_us": round(call_ms * 1e3, 3)},
     }
     if not args.no_cpu_baseline:
         log(args, "timing the oracle on the host")

@@ -88,6 +88,10 @@ def lib():
     L.aatc_decode_attn_workspace_bytes.argtypes = [ctypes.POINTER(Cache), i32, i64]
     L.aatc_decode_attn.restype = ctypes.c_int
     L.aatc_decode_attn.argtypes = [ctypes.POINTER(Cache), vp, i32, vp, i64, ctypes.c_float, vp, vp, vp, sz, vp]
+    L.aatc_decode_attn_partial.restype = ctypes.c_int
+    L.aatc_decode_attn_partial.argtypes = [ctypes.POINTER(Cache), vp, i32, vp, i64, ctypes.c_float, vp, sz, vp]
+    L.aatc_decode_attn_merge.restype = ctypes.c_int
+    L.aatc_decode_attn_merge.argtypes = [ctypes.POINTER(Cache), i32, vp, i64, vp, vp, vp, sz, vp]
     if L.aatc_calib_bytes(D) != CALIB_DTYPE.itemsize:
         raise RuntimeError("aatc_calib layout mismatch: library %d bytes, binding %d bytes"
                            % (L.aatc_calib_bytes(D), CALIB_DTYPE.itemsize))
@@ -102,4 +106,5 @@ def check(status):
 
 EXPORTS = ["aatc_status_string", "aatc_last_error", "aatc_calib_bytes", "aatc_bits_budget",
            "aatc_packed_bytes", "aatc_calibrate", "aatc_calib_validate", "aatc_calib_v_tiles",
-           "aatc_encode", "aatc_decode", "aatc_decode_attn_workspace_bytes", "aatc_decode_attn"]
+           "aatc_encode", "aatc_decode", "aatc_decode_attn_workspace_bytes", "aatc_decode_attn",
+           "aatc_decode_attn_partial", "aatc_decode_attn_merge"]

@@ -181,3 +181,28 @@ class CompressedKVCache:
                                          int(max_seq_len), float(scale), out.data_ptr(), lse.data_ptr(),
                                          workspace.data_ptr(), workspace.numel(), _stream_ptr(stream)))
         return out, lse
+
+    def _seq_ptr(self, seq_lens):
+        import torch
+        if seq_lens is None:
+            return None
+        if seq_lens.dtype != torch.int32 or seq_lens.device != self.device or seq_lens.numel() != self.batch:
+            raise ValueError("seq_lens must be an int32 [batch] tensor on the cache's device")
+        return seq_lens.data_ptr()
+
+    def decode_attn_partial(self, q, max_seq_len, workspace, seq_lens=None, scale=0.0, stream=None):
+        """aatc_decode_attn_partial: the cache pass; partial records go to `workspace`."""
+        import torch
+        if q.dtype != torch.float32 or not q.is_contiguous() or q.dim() != 3 or q.shape[0] != self.batch:
+            raise ValueError("q must be a contiguous fp32 [batch, n_q_heads, 128] tensor")
+        N.check(N.lib().aatc_decode_attn_partial(ctypes.byref(self._struct), q.data_ptr(), int(q.shape[1]),
+                                                 self._seq_ptr(seq_lens), int(max_seq_len), float(scale),
+                                                 workspace.data_ptr(), workspace.numel(), _stream_ptr(stream)))
+
+    def decode_attn_merge(self, n_q_heads, max_seq_len, workspace, out, lse=None, seq_lens=None, stream=None):
+        """aatc_decode_attn_merge: partial records in `workspace` -> out [batch, n_q, 128], lse."""
+        N.check(N.lib().aatc_decode_attn_merge(ctypes.byref(self._struct), int(n_q_heads), self._seq_ptr(seq_lens),
+                                               int(max_seq_len), out.data_ptr(),
+                                               lse.data_ptr() if lse is not None else None,
+                                               workspace.data_ptr(), workspace.numel(), _stream_ptr(stream)))
+        return out, lse

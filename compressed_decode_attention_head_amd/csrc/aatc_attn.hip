@@ -111,11 +111,13 @@ size_t aatc_decode_attn_workspace_bytes(const aatc_cache* c, int32_t n_q_heads, 
   return align256(p.part_bytes) + align256(p.offs_bytes);
 }
 
-aatc_status aatc_decode_attn(const aatc_cache* c, const float* q, int32_t n_q, const int32_t* seq_lens,
-                             int64_t max_seq, float scale, float* out, float* lse, void* ws, size_t ws_bytes,
-                             void* stream) {
-  aatc::clear_error();
-  if (!c || !q || !out || !ws) return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "null pointer");
+}  // extern "C"
+
+namespace {
+
+// Shared argument checks and plan of the three decode-attention entry points.
+aatc_status check_and_plan(const aatc_cache* c, int32_t n_q, int64_t max_seq, void* ws, size_t ws_bytes, Plan* p) {
+  if (!c || !ws) return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "null pointer");
   if (c->d != AATC_D) return aatc::fail(AATC_ERR_UNSUPPORTED, "d=%d (only 128)", c->d);
   if (c->batch < 1 || c->n_kv_heads < 1 || n_q < 1) return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "shape");
   if (n_q % c->n_kv_heads) return aatc::fail(AATC_ERR_UNSUPPORTED, "n_q_heads %% n_kv_heads != 0");
@@ -133,10 +135,15 @@ aatc_status aatc_decode_attn(const aatc_cache* c, const float* q, int32_t n_q, c
     return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "codes must be 16-byte and workspace 256-byte aligned");
   if (max_seq < 0 || max_seq > c->capacity_tokens)
     return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "max_seq_len %lld > capacity", (long long)max_seq);
-  const Plan p = make_plan(c, n_q, max_seq);
-  const size_t need = align256(p.part_bytes) + align256(p.offs_bytes);
+  *p = make_plan(c, n_q, max_seq);
+  const size_t need = align256(p->part_bytes) + align256(p->offs_bytes);
   if (ws_bytes < need) return aatc::fail(AATC_ERR_BUFFER_TOO_SMALL, "workspace %zu < %zu", ws_bytes, need);
-  if (!p.fits) return aatc::fail(AATC_ERR_UNSUPPORTED, "tiles of %d+%d bits do not fit LDS", c->k_bits, c->v_bits);
+  if (!p->fits) return aatc::fail(AATC_ERR_UNSUPPORTED, "tiles of %d+%d bits do not fit LDS", c->k_bits, c->v_bits);
+  return AATC_OK;
+}
+
+aatc_status launch_partial(const aatc_cache* c, const Plan& p, const float* q, int32_t n_q, const int32_t* seq_lens,
+                           int64_t max_seq, float scale, void* ws, hipStream_t st) {
   AttnArgs a;
   const aatc_calib* kcal = static_cast<const aatc_calib*>(c->k_calib);
   const aatc_calib* vcal = static_cast<const aatc_calib*>(c->v_calib);
@@ -145,7 +152,7 @@ aatc_status aatc_decode_attn(const aatc_cache* c, const float* q, int32_t n_q, c
   a.tiles_per_seq = c->capacity_tokens / 64;
   a.n_kv = c->n_kv_heads;
   a.n_q = n_q;
-  a.group = group;
+  a.group = n_q / c->n_kv_heads;
   a.seq_lens = seq_lens;
   a.max_seq = max_seq;
   a.q = q;
@@ -162,15 +169,21 @@ aatc_status aatc_decode_attn(const aatc_cache* c, const float* q, int32_t n_q, c
   a.slot_bytes = p.slot_bytes;
   a.ksz = p.ksz;
   a.gs = p.gs;
-  auto st = static_cast<hipStream_t>(stream);
   const dim3 grid(p.S, c->n_kv_heads, c->batch);
   hipError_t err = hipSuccess;
   const bool ok = dispatch(p, a, kcal, vcal, grid, st, &err);
   if (!ok) return aatc::fail(AATC_ERR_UNSUPPORTED, "plan NP=%d NVB=%d", p.NP, p.NVB);
   if (err != hipSuccess) return aatc::fail(AATC_ERR_HIP, "decode_attn launch: %s", hipGetErrorString(err));
+  return AATC_OK;
+}
+
+aatc_status launch_merge(const aatc_cache* c, const Plan& p, int32_t n_q, const int32_t* seq_lens, int64_t max_seq,
+                         float* out, float* lse, void* ws, hipStream_t st) {
+  const int group = n_q / c->n_kv_heads;
+  char* w = static_cast<char*>(ws);
   CombArgs cb;
-  cb.part = a.part;
-  cb.offs = a.offs;
+  cb.part = reinterpret_cast<const float*>(w);
+  cb.offs = reinterpret_cast<const float*>(w + align256(p.part_bytes));
   cb.n_kv = c->n_kv_heads;
   cb.n_q = n_q;
   cb.group = group;
@@ -182,13 +195,52 @@ aatc_status aatc_decode_attn(const aatc_cache* c, const float* q, int32_t n_q, c
   cb.max_seq = max_seq;
   cb.out = out;
   cb.lse = lse;
-  err = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_combine), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            static_cast<int>(p.comb_lds));
+  hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_combine),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(p.comb_lds));
   if (err != hipSuccess) return aatc::fail(AATC_ERR_HIP, "decode_attn combine attribute: %s", hipGetErrorString(err));
-  hipLaunchKernelGGL(k_attn_combine, dim3(group, c->n_kv_heads, c->batch), dim3(CNT), p.comb_lds, st, cb, vcal);
+  hipLaunchKernelGGL(k_attn_combine, dim3(group, c->n_kv_heads, c->batch), dim3(CNT), p.comb_lds, st, cb,
+                     static_cast<const aatc_calib*>(c->v_calib));
   err = hipGetLastError();
   if (err != hipSuccess) return aatc::fail(AATC_ERR_HIP, "decode_attn combine launch: %s", hipGetErrorString(err));
   return AATC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+aatc_status aatc_decode_attn(const aatc_cache* c, const float* q, int32_t n_q, const int32_t* seq_lens,
+                             int64_t max_seq, float scale, float* out, float* lse, void* ws, size_t ws_bytes,
+                             void* stream) {
+  aatc::clear_error();
+  if (!q || !out) return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "null pointer");
+  Plan p;
+  aatc_status r = check_and_plan(c, n_q, max_seq, ws, ws_bytes, &p);
+  if (r != AATC_OK) return r;
+  auto st = static_cast<hipStream_t>(stream);
+  r = launch_partial(c, p, q, n_q, seq_lens, max_seq, scale, ws, st);
+  if (r != AATC_OK) return r;
+  return launch_merge(c, p, n_q, seq_lens, max_seq, out, lse, ws, st);
+}
+
+aatc_status aatc_decode_attn_partial(const aatc_cache* c, const float* q, int32_t n_q, const int32_t* seq_lens,
+                                     int64_t max_seq, float scale, void* ws, size_t ws_bytes, void* stream) {
+  aatc::clear_error();
+  if (!q) return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "null pointer");
+  Plan p;
+  const aatc_status r = check_and_plan(c, n_q, max_seq, ws, ws_bytes, &p);
+  if (r != AATC_OK) return r;
+  return launch_partial(c, p, q, n_q, seq_lens, max_seq, scale, ws, static_cast<hipStream_t>(stream));
+}
+
+aatc_status aatc_decode_attn_merge(const aatc_cache* c, int32_t n_q, const int32_t* seq_lens, int64_t max_seq,
+                                   float* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  aatc::clear_error();
+  if (!out) return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "null pointer");
+  Plan p;
+  const aatc_status r = check_and_plan(c, n_q, max_seq, ws, ws_bytes, &p);
+  if (r != AATC_OK) return r;
+  return launch_merge(c, p, n_q, seq_lens, max_seq, out, lse, ws, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

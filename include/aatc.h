@@ -248,6 +248,29 @@ aatc_status aatc_decode_attn(const aatc_cache* cache, const float* q_dev, int32_
                              float* out_dev, float* lse_dev, void* workspace_dev,
                              size_t workspace_bytes, void* stream);
 
+/*
+ * aatc_decode_attn_partial and aatc_decode_attn_merge -- the two halves of aatc_decode_attn,
+ * launched by it back to back; called separately they let a caller time or overlap the halves,
+ * or merge the partial states of several sequence shards.  [SPECTRA Abstract: the cache pass
+ * is the bandwidth-bound part; the merge of split softmax states is the usual log-sum-exp
+ * combination]
+ *   _partial reads the packed cache once and writes, into workspace_dev, one partial record
+ *   per (sequence split, q head): running max, sum of probabilities and the softmax-weighted
+ *   V code sums of its tokens.  The record layout is internal to the library.
+ *   _merge reads those records (written by _partial with the same cache, n_q_heads,
+ *   seq_lens_dev and max_seq_len, earlier on the same stream or otherwise ordered before it)
+ *   and writes out_dev / lse_dev exactly as aatc_decode_attn does.
+ *   Arguments, ownership and errors as for aatc_decode_attn; each call validates them itself.
+ */
+aatc_status aatc_decode_attn_partial(const aatc_cache* cache, const float* q_dev, int32_t n_q_heads,
+                                     const int32_t* seq_lens_dev, int64_t max_seq_len,
+                                     float softmax_scale, void* workspace_dev, size_t workspace_bytes,
+                                     void* stream);
+aatc_status aatc_decode_attn_merge(const aatc_cache* cache, int32_t n_q_heads,
+                                   const int32_t* seq_lens_dev, int64_t max_seq_len, float* out_dev,
+                                   float* lse_dev, void* workspace_dev, size_t workspace_bytes,
+                                   void* stream);
+
 #ifdef __cplusplus
 }
 #endif

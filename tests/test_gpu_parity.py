@@ -101,6 +101,21 @@ def test_decode_attention(built):
     assert lerr <= 5e-3, lerr
 
 
+def test_partial_then_merge_equals_one_call(built):
+    """The two halves called separately give the one-shot result bit for bit."""
+    torch = _torch()
+    name, case, cache = built
+    q = torch.from_numpy(case.q.astype(np.float32)).cuda()
+    out1, lse1 = cache.decode_attn(q, case.n)
+    ws = cache.new_workspace(q.shape[1], case.n)
+    out2 = torch.full_like(q, float("nan"))
+    lse2 = torch.full_like(lse1, float("nan"))
+    cache.decode_attn_partial(q, case.n, ws)
+    cache.decode_attn_merge(q.shape[1], case.n, ws, out2, lse2)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2), name
+
+
 def test_ragged_seq_lens_and_empty():
     torch = _torch()
     case = Case(cfg=2, n_kv=2, group=4, n_tokens=333, batch=3, rotation="klt", bpe_k=2.76)
