@@ -45,6 +45,12 @@ class Cache(ctypes.Structure):
                 ("k_codes", ctypes.c_void_p), ("v_codes", ctypes.c_void_p)]
 
 
+class Segment(ctypes.Structure):
+    _fields_ = [("cache", ctypes.POINTER(Cache)), ("k_raw", ctypes.c_void_p), ("v_raw", ctypes.c_void_p),
+                ("raw_capacity", ctypes.c_int64), ("seq_lens_dev", ctypes.c_void_p),
+                ("max_seq_len", ctypes.c_int64)]
+
+
 class AatcError(RuntimeError):
     def __init__(self, status, msg):
         super().__init__("%s: %s" % (STATUS.get(status, status), msg))
@@ -92,6 +98,15 @@ def lib():
     L.aatc_decode_attn_partial.argtypes = [ctypes.POINTER(Cache), vp, i32, vp, i64, ctypes.c_float, vp, sz, vp]
     L.aatc_decode_attn_merge.restype = ctypes.c_int
     L.aatc_decode_attn_merge.argtypes = [ctypes.POINTER(Cache), i32, vp, i64, vp, vp, vp, sz, vp]
+    L.aatc_tier_distortions.restype = ctypes.c_int
+    L.aatc_tier_distortions.argtypes = [vp, i32, i32, i32, vp]
+    L.aatc_token_tiers.restype = ctypes.c_int
+    L.aatc_token_tiers.argtypes = [vp, i64, vp, i32, dbl, vp]
+    L.aatc_decode_attn_segments_workspace_bytes.restype = sz
+    L.aatc_decode_attn_segments_workspace_bytes.argtypes = [ctypes.POINTER(Segment), i32, i32, i32, i32]
+    L.aatc_decode_attn_segments.restype = ctypes.c_int
+    L.aatc_decode_attn_segments.argtypes = [ctypes.POINTER(Segment), i32, i32, i32, vp, i32, ctypes.c_float, vp,
+                                            vp, vp, sz, vp]
     if L.aatc_calib_bytes(D) != CALIB_DTYPE.itemsize:
         raise RuntimeError("aatc_calib layout mismatch: library %d bytes, binding %d bytes"
                            % (L.aatc_calib_bytes(D), CALIB_DTYPE.itemsize))
@@ -107,4 +122,5 @@ def check(status):
 EXPORTS = ["aatc_status_string", "aatc_last_error", "aatc_calib_bytes", "aatc_bits_budget",
            "aatc_packed_bytes", "aatc_calibrate", "aatc_calib_validate", "aatc_calib_v_tiles",
            "aatc_encode", "aatc_decode", "aatc_decode_attn_workspace_bytes", "aatc_decode_attn",
-           "aatc_decode_attn_partial", "aatc_decode_attn_merge"]
+           "aatc_decode_attn_partial", "aatc_decode_attn_merge", "aatc_tier_distortions",
+           "aatc_token_tiers", "aatc_decode_attn_segments_workspace_bytes", "aatc_decode_attn_segments"]

@@ -10,7 +10,7 @@ import numpy as np
 from . import _native as N
 
 __all__ = ["calibrate", "calib_view", "validate", "bits_budget", "packed_bytes", "v_tiles",
-           "CompressedKVCache", "AatcError"]
+           "tier_distortions", "token_tiers", "decode_attn_segments", "CompressedKVCache", "AatcError"]
 
 AatcError = N.AatcError
 
@@ -61,6 +61,68 @@ def bits_budget(bits_per_elem, d=128):
 
 def packed_bytes(total_bits, n_tokens):
     return int(N.lib().aatc_packed_bytes(int(total_bits), int(n_tokens)))
+
+
+def tier_distortions(sigma2_list, max_bits=8, d=128):
+    """aatc_tier_distortions: D(tau) for tiers (0, 2, 4, 16) from rotated variances [n, d]."""
+    s2 = np.ascontiguousarray(np.stack([np.asarray(x, dtype=np.float64) for x in sigma2_list]))
+    out = np.zeros(4, dtype=np.float64)
+    N.check(N.lib().aatc_tier_distortions(s2.ctypes.data, s2.shape[0], d, int(max_bits), out.ctypes.data))
+    return out
+
+
+def token_tiers(attn_mass, dist, avg_bits, d=128):
+    """aatc_token_tiers: tier (0, 2, 4 or 16) per token under an average bit budget."""
+    a = np.ascontiguousarray(attn_mass, dtype=np.float64)
+    dist = np.ascontiguousarray(dist, dtype=np.float64)
+    out = np.zeros(a.shape[0], dtype=np.int8)
+    N.check(N.lib().aatc_token_tiers(a.ctypes.data, a.shape[0], dist.ctypes.data, d, float(avg_bits),
+                                     out.ctypes.data))
+    return out
+
+
+def decode_attn_segments(segments, q, batch, n_kv_heads, scale=0.0, workspace=None, out=None, lse=None,
+                         stream=None):
+    """aatc_decode_attn_segments.  segments: list of dicts, each either
+    {"cache": CompressedKVCache, "seq_lens": int32 [batch, n_kv] tensor, "max_seq_len": n} or
+    {"k_raw": bf16 [batch, n_kv, cap, 128], "v_raw": same, "seq_lens": ..., "max_seq_len": n}."""
+    import torch
+    if q.dtype != torch.float32 or not q.is_contiguous() or q.dim() != 3 or q.shape[0] != batch:
+        raise ValueError("q must be a contiguous fp32 [batch, n_q_heads, 128] tensor")
+    arr = (N.Segment * len(segments))()
+    keep = []
+    for i, sg in enumerate(segments):
+        sl = sg.get("seq_lens")
+        if sl is not None:
+            if sl.dtype != torch.int32 or sl.numel() != batch * n_kv_heads or not sl.is_contiguous():
+                raise ValueError("segment seq_lens must be a contiguous int32 [batch, n_kv_heads] tensor")
+            arr[i].seq_lens_dev = sl.data_ptr()
+        arr[i].max_seq_len = int(sg["max_seq_len"])
+        if "cache" in sg:
+            arr[i].cache = ctypes.pointer(sg["cache"].struct)
+            keep.append(arr[i].cache)
+        else:
+            k, v = sg["k_raw"], sg["v_raw"]
+            if (k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16 or k.shape != v.shape or k.dim() != 4
+                    or not k.is_contiguous() or not v.is_contiguous() or k.shape[:2] != (batch, n_kv_heads)):
+                raise ValueError("raw segments are contiguous bf16 [batch, n_kv_heads, capacity, 128] tensors")
+            arr[i].k_raw, arr[i].v_raw = k.data_ptr(), v.data_ptr()
+            arr[i].raw_capacity = k.shape[2]
+    n_q = q.shape[1]
+    L = N.lib()
+    need = L.aatc_decode_attn_segments_workspace_bytes(arr, len(segments), batch, n_kv_heads, n_q)
+    if need == 0:
+        raise ValueError("invalid segments: " + L.aatc_last_error().decode())
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((batch, n_q), dtype=torch.float32, device=q.device)
+    N.check(L.aatc_decode_attn_segments(arr, len(segments), batch, n_kv_heads, q.data_ptr(), n_q, float(scale),
+                                        out.data_ptr(), lse.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                        _stream_ptr(stream)))
+    return out, lse
 
 
 def _stream_ptr(stream):

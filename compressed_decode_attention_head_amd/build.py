@@ -25,7 +25,7 @@ EXTRA = {"aatc_codec.hip": ["-ffp-contract=off"]}
 CXX = shutil.which("g++") or "g++"
 CXX_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-I", INCLUDE, "-I", CSRC, "-Wall"]
 
-SOURCES = ["aatc_host.cpp", "aatc_codec.hip", "aatc_attn.hip", "aatc_attn_np1.hip", "aatc_attn_np2.hip",
+SOURCES = ["aatc_host.cpp", "aatc_tiers.cpp", "aatc_codec.hip", "aatc_attn.hip", "aatc_attn_np1.hip", "aatc_attn_np2.hip",
            "aatc_attn_np3.hip", "aatc_attn_np4.hip"]
 
 

@@ -2,6 +2,9 @@
 // The kernel (and the method it implements) is described in aatc_attn_kernel.h.
 #define AATC_ATTN_COMBINE_TU
 #include "aatc_attn_kernel.h"
+#include "aatc_seg_kernel.h"
+
+#include <cstdio>
 
 namespace {
 
@@ -143,7 +146,7 @@ aatc_status check_and_plan(const aatc_cache* c, int32_t n_q, int64_t max_seq, vo
 }
 
 aatc_status launch_partial(const aatc_cache* c, const Plan& p, const float* q, int32_t n_q, const int32_t* seq_lens,
-                           int64_t max_seq, float scale, void* ws, hipStream_t st) {
+                           int seq_per_head, int64_t max_seq, float scale, void* ws, hipStream_t st) {
   AttnArgs a;
   const aatc_calib* kcal = static_cast<const aatc_calib*>(c->k_calib);
   const aatc_calib* vcal = static_cast<const aatc_calib*>(c->v_calib);
@@ -154,6 +157,7 @@ aatc_status launch_partial(const aatc_cache* c, const Plan& p, const float* q, i
   a.n_q = n_q;
   a.group = n_q / c->n_kv_heads;
   a.seq_lens = seq_lens;
+  a.seq_per_head = seq_per_head;
   a.max_seq = max_seq;
   a.q = q;
   a.scale2 = (scale > 0.f ? scale : 1.0f / sqrtf(static_cast<float>(AATC_D))) * 1.4426950408889634f;
@@ -177,8 +181,8 @@ aatc_status launch_partial(const aatc_cache* c, const Plan& p, const float* q, i
   return AATC_OK;
 }
 
-aatc_status launch_merge(const aatc_cache* c, const Plan& p, int32_t n_q, const int32_t* seq_lens, int64_t max_seq,
-                         float* out, float* lse, void* ws, hipStream_t st) {
+aatc_status launch_merge(const aatc_cache* c, const Plan& p, int32_t n_q, const int32_t* seq_lens, int seq_per_head,
+                         int64_t max_seq, float* out, float* lse, void* ws, hipStream_t st) {
   const int group = n_q / c->n_kv_heads;
   char* w = static_cast<char*>(ws);
   CombArgs cb;
@@ -192,6 +196,7 @@ aatc_status launch_merge(const aatc_cache* c, const Plan& p, int32_t n_q, const 
   cb.SC = p.SC;
   cb.rec_bytes = p.rec_bytes;
   cb.seq_lens = seq_lens;
+  cb.seq_per_head = seq_per_head;
   cb.max_seq = max_seq;
   cb.out = out;
   cb.lse = lse;
@@ -218,9 +223,9 @@ aatc_status aatc_decode_attn(const aatc_cache* c, const float* q, int32_t n_q, c
   aatc_status r = check_and_plan(c, n_q, max_seq, ws, ws_bytes, &p);
   if (r != AATC_OK) return r;
   auto st = static_cast<hipStream_t>(stream);
-  r = launch_partial(c, p, q, n_q, seq_lens, max_seq, scale, ws, st);
+  r = launch_partial(c, p, q, n_q, seq_lens, 0, max_seq, scale, ws, st);
   if (r != AATC_OK) return r;
-  return launch_merge(c, p, n_q, seq_lens, max_seq, out, lse, ws, st);
+  return launch_merge(c, p, n_q, seq_lens, 0, max_seq, out, lse, ws, st);
 }
 
 aatc_status aatc_decode_attn_partial(const aatc_cache* c, const float* q, int32_t n_q, const int32_t* seq_lens,
@@ -230,7 +235,7 @@ aatc_status aatc_decode_attn_partial(const aatc_cache* c, const float* q, int32_
   Plan p;
   const aatc_status r = check_and_plan(c, n_q, max_seq, ws, ws_bytes, &p);
   if (r != AATC_OK) return r;
-  return launch_partial(c, p, q, n_q, seq_lens, max_seq, scale, ws, static_cast<hipStream_t>(stream));
+  return launch_partial(c, p, q, n_q, seq_lens, 0, max_seq, scale, ws, static_cast<hipStream_t>(stream));
 }
 
 aatc_status aatc_decode_attn_merge(const aatc_cache* c, int32_t n_q, const int32_t* seq_lens, int64_t max_seq,
@@ -240,7 +245,140 @@ aatc_status aatc_decode_attn_merge(const aatc_cache* c, int32_t n_q, const int32
   Plan p;
   const aatc_status r = check_and_plan(c, n_q, max_seq, ws, ws_bytes, &p);
   if (r != AATC_OK) return r;
-  return launch_merge(c, p, n_q, seq_lens, max_seq, out, lse, ws, static_cast<hipStream_t>(stream));
+  return launch_merge(c, p, n_q, seq_lens, 0, max_seq, out, lse, ws, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+// ---- multi-segment decode attention -----------------------------------------------------------
+namespace {
+
+struct SegPlan {
+  int n_states;
+  size_t states_off, lse_off, attn_off, attn_bytes, total;
+};
+
+int64_t raw_chunks(const aatc_segment& sg) { return (sg.max_seq_len + aatc_seg::RCH - 1) / aatc_seg::RCH; }
+
+aatc_status seg_plan(const aatc_segment* segs, int32_t n_segs, int32_t batch, int32_t n_kv, int32_t n_q,
+                     SegPlan* sp) {
+  if (!segs || n_segs < 1) return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "no segments");
+  if (batch < 1 || n_kv < 1 || n_q < 1 || n_q % n_kv) return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "shape");
+  if (n_q / n_kv > AATC_MAX_GROUP) return aatc::fail(AATC_ERR_UNSUPPORTED, "GQA group %d > 8", n_q / n_kv);
+  int64_t states = 0;
+  size_t attn = 0;
+  for (int s = 0; s < n_segs; ++s) {
+    const aatc_segment& sg = segs[s];
+    if (sg.max_seq_len < 0) return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "segment %d: max_seq_len < 0", s);
+    if (sg.cache) {
+      const aatc_cache* c = sg.cache;
+      if (c->batch != batch || c->n_kv_heads != n_kv)
+        return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "segment %d: cache shape differs from the call", s);
+      const size_t w = aatc_decode_attn_workspace_bytes(c, n_q, sg.max_seq_len);
+      if (w > attn) attn = w;
+      states += 1;
+    } else {
+      if (!sg.k_raw || !sg.v_raw) return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "segment %d: null raw pointer", s);
+      if (sg.max_seq_len > sg.raw_capacity)
+        return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "segment %d: max_seq_len > raw_capacity", s);
+      if ((reinterpret_cast<uintptr_t>(sg.k_raw) & 15) || (reinterpret_cast<uintptr_t>(sg.v_raw) & 15))
+        return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "segment %d: raw tensors must be 16-byte aligned", s);
+      states += raw_chunks(sg) > 0 ? raw_chunks(sg) : 1;
+    }
+  }
+  if (states > (1 << 20)) return aatc::fail(AATC_ERR_UNSUPPORTED, "too many segment states");
+  const size_t bq = static_cast<size_t>(batch) * n_q;
+  sp->n_states = static_cast<int>(states);
+  sp->states_off = 0;
+  sp->lse_off = align256(static_cast<size_t>(states) * bq * AATC_D * 4);
+  sp->attn_off = sp->lse_off + align256(static_cast<size_t>(states) * bq * 4);
+  sp->attn_bytes = attn;
+  sp->total = sp->attn_off + align256(attn);
+  return AATC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t aatc_decode_attn_segments_workspace_bytes(const aatc_segment* segs, int32_t n_segs, int32_t batch,
+                                                 int32_t n_kv_heads, int32_t n_q_heads) {
+  SegPlan sp;
+  if (seg_plan(segs, n_segs, batch, n_kv_heads, n_q_heads, &sp) != AATC_OK) return 0;
+  return sp.total;
+}
+
+aatc_status aatc_decode_attn_segments(const aatc_segment* segs, int32_t n_segs, int32_t batch, int32_t n_kv,
+                                      const float* q, int32_t n_q, float scale, float* out, float* lse, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  aatc::clear_error();
+  if (!q || !out || !ws) return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "null pointer");
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "workspace not 256-byte aligned");
+  SegPlan sp;
+  aatc_status r = seg_plan(segs, n_segs, batch, n_kv, n_q, &sp);
+  if (r != AATC_OK) return r;
+  if (ws_bytes < sp.total) return aatc::fail(AATC_ERR_BUFFER_TOO_SMALL, "workspace %zu < %zu", ws_bytes, sp.total);
+  // validate every coded segment before launching anything
+  for (int s = 0; s < n_segs; ++s) {
+    if (!segs[s].cache) continue;
+    Plan p;
+    r = check_and_plan(segs[s].cache, n_q, segs[s].max_seq_len, static_cast<char*>(ws) + sp.attn_off, sp.attn_bytes,
+                       &p);
+    if (r != AATC_OK) {
+      char msg[400];
+      snprintf(msg, sizeof msg, "%s", aatc_last_error());
+      return aatc::fail(r, "segment %d: %s", s, msg);
+    }
+  }
+  auto st = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  float* out_states = reinterpret_cast<float*>(w + sp.states_off);
+  float* lse_states = reinterpret_cast<float*>(w + sp.lse_off);
+  void* attn_ws = w + sp.attn_off;
+  const int64_t bq = static_cast<int64_t>(batch) * n_q;
+  const float scale_v = scale > 0.f ? scale : 1.0f / sqrtf(static_cast<float>(AATC_D));
+  int state = 0;
+  for (int s = 0; s < n_segs; ++s) {
+    const aatc_segment& sg = segs[s];
+    if (sg.cache) {
+      Plan p;
+      r = check_and_plan(sg.cache, n_q, sg.max_seq_len, attn_ws, sp.attn_bytes, &p);
+      if (r != AATC_OK) return r;
+      r = launch_partial(sg.cache, p, q, n_q, sg.seq_lens_dev, 1, sg.max_seq_len, scale, attn_ws, st);
+      if (r != AATC_OK) return r;
+      r = launch_merge(sg.cache, p, n_q, sg.seq_lens_dev, 1, sg.max_seq_len, out_states + state * bq * AATC_D,
+                       lse_states + state * bq, attn_ws, st);
+      if (r != AATC_OK) return r;
+      state += 1;
+    } else {
+      aatc_seg::RawArgs ra;
+      ra.k = static_cast<const uint16_t*>(sg.k_raw);
+      ra.v = static_cast<const uint16_t*>(sg.v_raw);
+      ra.cap = sg.raw_capacity;
+      ra.seq_lens = sg.seq_lens_dev;
+      ra.max_seq = sg.max_seq_len;
+      ra.q = q;
+      ra.n_kv = n_kv;
+      ra.n_q = n_q;
+      ra.group = n_q / n_kv;
+      ra.scale2 = scale_v * 1.4426950408889634f;
+      ra.out_states = out_states;
+      ra.lse_states = lse_states;
+      ra.state0 = state;
+      ra.bq = bq;
+      const int64_t nc = raw_chunks(sg) > 0 ? raw_chunks(sg) : 1;
+      hipLaunchKernelGGL(aatc_seg::k_raw_attn, dim3(static_cast<unsigned>(nc), n_kv, batch), dim3(aatc_seg::RCH), 0,
+                         st, ra);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return aatc::fail(AATC_ERR_HIP, "raw segment launch: %s", hipGetErrorString(e));
+      state += static_cast<int>(nc);
+    }
+  }
+  hipLaunchKernelGGL(aatc_seg::k_merge_states, dim3(static_cast<unsigned>(bq)), dim3(AATC_D), 0, st, out_states,
+                     lse_states, sp.n_states, bq, out, lse);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return aatc::fail(AATC_ERR_HIP, "segment merge launch: %s", hipGetErrorString(e));
+  return AATC_OK;
 }
 
 }  // extern "C"

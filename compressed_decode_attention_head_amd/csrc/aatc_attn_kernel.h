@@ -70,6 +70,7 @@ struct AttnArgs {
   int64_t tiles_per_seq;
   int n_kv, n_q, group;
   const int32_t* seq_lens;
+  int seq_per_head;                   // seq_lens is [batch][n_kv] (else [batch])
   int64_t max_seq;
   const float* q;
   float scale2;                       // softmax scale * log2(e)
@@ -297,7 +298,7 @@ __global__ __launch_bounds__(NTH) void k_attn_main(AttnArgs a, const aatc_calib*
   const aatc_calib* vc = vcal + h;
   const int G = a.group;
   const int Bk = a.kB, Bv = a.vB;
-  int64_t seq64 = a.seq_lens ? static_cast<int64_t>(a.seq_lens[b]) : a.max_seq;
+  int64_t seq64 = a.seq_lens ? static_cast<int64_t>(a.seq_lens[a.seq_per_head ? bh : b]) : a.max_seq;
   seq64 = seq64 < 0 ? 0 : (seq64 > a.max_seq ? a.max_seq : seq64);     // never read past the cache
   const int seq = static_cast<int>(seq64);                      // tokens per sequence < 2^31
   const int ntiles = (seq + 63) / 64;
@@ -834,6 +835,7 @@ struct CombArgs {
   int SC;                                // splits per LDS chunk of records
   int rec_bytes;                         // LDS bytes of one chunk (multiple of 1024)
   const int32_t* seq_lens;
+  int seq_per_head;                      // seq_lens is [batch][n_kv] (else [batch])
   int64_t max_seq;
   float* out;
   float* lse;
@@ -885,7 +887,7 @@ __global__ __launch_bounds__(CNT) void k_attn_combine(CombArgs a, const aatc_cal
   k = dma_words<CNT / 64>(vc->field_shift, t_fs, 3 * D / 4, k, wave, lane);
   const int rot = vc->rotation;
   if (rot == AATC_ROT_KLT) k = dma_words<CNT / 64>(vc->R32, rv, D * D, k, wave, lane);
-  int64_t seq = a.seq_lens ? static_cast<int64_t>(a.seq_lens[b]) : a.max_seq;
+  int64_t seq = a.seq_lens ? static_cast<int64_t>(a.seq_lens[a.seq_per_head ? bh : b]) : a.max_seq;
   seq = seq < 0 ? 0 : (seq > a.max_seq ? a.max_seq : seq);
   const int n4 = vc->n_fields4, n2 = vc->n_fields2, n1 = vc->n_fields1;
   const int T4 = (n4 + 15) >> 4, T2 = (n2 + 15) >> 4;

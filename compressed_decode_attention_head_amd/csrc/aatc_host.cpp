@@ -239,7 +239,7 @@ double optimal_step(int b) {
 // ---- integer reverse water-filling ---------------------------------------------------------
 // The B largest candidates sigma_i^2 4^-k (k < max_bits) in the order (value desc,
 // channel asc, bit asc); exact in fp64 (ldexp).
-void waterfill(const double* s2, int d, int total, int max_bits, uint8_t* bits) {
+void waterfill_impl(const double* s2, int d, int total, int max_bits, uint8_t* bits) {
   struct C { double v; int i, k; };
   std::vector<C> c;
   c.reserve(d * max_bits);
@@ -255,6 +255,11 @@ void waterfill(const double* s2, int d, int total, int max_bits, uint8_t* bits) 
 }
 
 }  // namespace
+
+void waterfill(const double* s2, int d, int total, int max_bits, uint8_t* bits) {
+  waterfill_impl(s2, d, total, max_bits, bits);
+}
+
 }  // namespace aatc
 
 using namespace aatc;
@@ -366,7 +371,7 @@ aatc_status aatc_calibrate(const aatc_calib_params* p, const void* x, aatc_dtype
       c->sigma2[i] = s;
     }
   }
-  waterfill(c->sigma2, d, total, p->max_bits, c->bits);
+  waterfill_impl(c->sigma2, d, total, p->max_bits, c->bits);
 
   double smax = 0.0;
   for (int i = 0; i < d; ++i) smax = std::max(smax, std::sqrt(std::max(c->sigma2[i], 0.0)));

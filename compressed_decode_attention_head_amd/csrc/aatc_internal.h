@@ -16,6 +16,10 @@ void clear_error();
 // FNV-1a 64 over a blob with its checksum field treated as zero.
 uint64_t blob_checksum(const aatc_calib* c);
 
+// Integer reverse water-filling: the `total` largest candidates sigma_i^2 4^-k (k < max_bits)
+// in the order (value desc, channel asc, bit asc) -> bits[d].
+void waterfill(const double* s2, int d, int total, int max_bits, uint8_t* bits);
+
 // Layout derived from the per-channel bits (shared by calibrate and validate).
 void build_layout(aatc_calib* c);
 

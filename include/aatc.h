@@ -271,6 +271,68 @@ aatc_status aatc_decode_attn_merge(const aatc_cache* cache, int32_t n_q_heads,
                                    float* lse_dev, void* workspace_dev, size_t workspace_bytes,
                                    void* stream);
 
+/*
+ * Token tiers.  [SPHERICAL KV page, RDKV abstract: bit widths from full precision down to
+ * zero per token, by reverse water-filling once after prefill; AATC Key points: the output
+ * distortion factors over tokens and channels]  Tiers are 0 (evicted), 2 and 4 (coded with
+ * that many bits per element, same rotation, own water-filling) and 16 (raw bf16).
+ *
+ * aatc_tier_distortions -- host.  dist_out[j] for tiers {0,2,4,16}: sum over the n_tensors
+ *   rotated variance vectors sigma2[n_tensors][d] (e.g. K and V of one head) of
+ *   sum_i sigma2_i 4^-b_i(tau), b(tau) the water-filling at tau*d bits (aatc_calibrate's);
+ *   dist_out[0] = total variance, dist_out[3] = 0.
+ *   Errors: d != 128 -> UNSUPPORTED; max_bits outside 4..8 -> BUDGET; negative or non-finite
+ *   variance -> NUMERICAL; null pointers -> INVALID_ARGUMENT.
+ *
+ * aatc_token_tiers -- host.  For n tokens with attention mass attn_mass[n] >= 0, the tier of
+ *   each token minimising sum_t a_t^2 dist[tier_t] subject to sum_t tier_t * d <=
+ *   avg_bits * n * d: per token argmin of a_t^2 dist[j] + lambda d tier_j (ties to the lower
+ *   tier) with lambda bisected (200 steps) to the smallest value that fits the budget.
+ *   tiers_out[n] receives 0, 2, 4 or 16.
+ *   Errors: avg_bits outside [0, 16] -> BUDGET; negative or non-finite inputs -> NUMERICAL.
+ */
+aatc_status aatc_tier_distortions(const double* sigma2, int32_t n_tensors, int32_t d, int32_t max_bits,
+                                  double dist_out[4]);
+aatc_status aatc_token_tiers(const double* attn_mass, int64_t n, const double dist[4], int32_t d,
+                             double avg_bits, int8_t* tiers_out);
+
+/*
+ * One segment of a KV head's tokens for aatc_decode_attn_segments: either a coded cache
+ * (cache != NULL; its k_codes/v_codes hold this segment's tokens, compacted, under the
+ * segment's own artefacts) or raw bf16 tokens in the original basis (cache == NULL;
+ * k_raw/v_raw bf16 [batch][n_kv_heads][raw_capacity][128], 16-byte aligned).
+ * seq_lens_dev: int32 [batch][n_kv_heads] tokens of this segment per (b,h), each <=
+ * max_seq_len (NULL: max_seq_len everywhere); max_seq_len <= the segment's capacity.
+ */
+typedef struct {
+  const aatc_cache* cache;
+  const void* k_raw;
+  const void* v_raw;
+  int64_t raw_capacity;
+  const int32_t* seq_lens_dev;
+  int64_t max_seq_len;
+} aatc_segment;
+
+/* Workspace bytes of aatc_decode_attn_segments (0 for invalid arguments). */
+size_t aatc_decode_attn_segments_workspace_bytes(const aatc_segment* segs, int32_t n_segs,
+                                                 int32_t batch, int32_t n_kv_heads,
+                                                 int32_t n_q_heads);
+
+/*
+ * aatc_decode_attn_segments -- device, async.  One decode step whose softmax runs over the
+ * union of the segments' tokens (tier-0 tokens are in no segment).  [SPHERICAL KV page,
+ * RDKV abstract; softmax is order-invariant, so the union is the log-sum-exp merge of
+ * per-segment states]  Coded segments run the cache pass and merge of aatc_decode_attn with
+ * per-(b,h) lengths; raw segments run a dense bf16 pass in 256-token chunks; one final
+ * kernel merges all states.  q, out, lse, scale and GQA mapping as aatc_decode_attn.
+ *   Errors: as aatc_decode_attn, per segment; caches whose batch or n_kv_heads differ from the
+ *   call -> INVALID_ARGUMENT; workspace too small -> BUFFER_TOO_SMALL.
+ */
+aatc_status aatc_decode_attn_segments(const aatc_segment* segs, int32_t n_segs, int32_t batch,
+                                      int32_t n_kv_heads, const float* q_dev, int32_t n_q_heads,
+                                      float softmax_scale, float* out_dev, float* lse_dev,
+                                      void* workspace_dev, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

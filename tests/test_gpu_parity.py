@@ -200,3 +200,67 @@ def test_device_error_paths():
     with pytest.raises(api.AatcError) as e:
         cache.decode_attn(q, 128)                       # longer than capacity
     assert e.value.name == "AATC_ERR_INVALID_ARGUMENT"
+
+
+@pytest.mark.parametrize("avg_bits", [2.76, 1.0])
+def test_segments_tiers_match_oracle(avg_bits):
+    """Token tiers -> coded tier-2 and tier-4 caches (own water-filling, same rotation) + raw
+    bf16 tier-16 tokens; tier-0 tokens evicted; one softmax over the union."""
+    torch = _torch()
+    from compressed_decode_attention_head_amd import api
+    cfg, n_kv, group, n = 5, 2, 4, 900
+    n_q = n_kv * group
+    cal = {t: [synth.draw(cfg, 0, h, t, "calib", 1024) for h in range(n_kv)] for t in (synth.K, synth.V)}
+    x = {t: np.stack([synth.draw(cfg, 0, h, t, "context", n) for h in range(n_kv)]) for t in (synth.K, synth.V)}
+    arts = {(tau, t): [O.calibrate(c, "klt", float(tau)) for c in cal[t]] for tau in (2, 4) for t in (synth.K, synth.V)}
+    tiers = []
+    for h in range(n_kv):
+        dist = O.tier_distortions([arts[(2, synth.K)][h]["sigma2"], arts[(2, synth.V)][h]["sigma2"]], 128)
+        tiers.append(O.token_tiers(synth.zipf_mass(cfg, 0, h, n), dist, 128, avg_bits))
+    idx = {tau: [np.nonzero(tiers[h] == tau)[0] for h in range(n_kv)] for tau in (0, 2, 4, 16)}
+    if avg_bits < 2:
+        assert sum(len(i) for i in idx[0]) > 0          # some tokens are evicted
+    q = synth.queries(cfg, 0, n_q, n_kv, [x[synth.K][h] for h in range(n_kv)])
+
+    segs, keep = [], []
+    for tau in (2, 4, 16):
+        counts = [len(idx[tau][h]) for h in range(n_kv)]
+        cap = max(64, -(-max(counts) // 64) * 64)
+        sl = torch.tensor([counts], dtype=torch.int32, device="cuda")
+        xs = {t: np.zeros((1, n_kv, cap, 128), dtype=np.float32) for t in (synth.K, synth.V)}
+        for t in (synth.K, synth.V):
+            for h in range(n_kv):
+                xs[t][0, h, :counts[h]] = x[t][h][idx[tau][h]]
+        if tau == 16:
+            kr = torch.from_numpy(xs[synth.K]).to(torch.bfloat16).cuda()
+            vr = torch.from_numpy(xs[synth.V]).to(torch.bfloat16).cuda()
+            keep += [kr, vr, sl]
+            segs.append({"k_raw": kr, "v_raw": vr, "seq_lens": sl, "max_seq_len": max(counts)})
+        else:
+            blobs = {t: [api.calibrate(synth.bf16_bits(c), "klt", float(tau)) for c in cal[t]] for t in (synth.K, synth.V)}
+            cache = api.CompressedKVCache(blobs[synth.K], blobs[synth.V], 1, cap)
+            for t in (synth.K, synth.V):
+                cache.encode(t, torch.from_numpy(xs[t]).to(torch.bfloat16).cuda())
+            keep += [cache, sl]
+            segs.append({"cache": cache, "seq_lens": sl, "max_seq_len": max(counts)})
+    qt = torch.from_numpy(q[None].astype(np.float32)).cuda()
+    out, lse = api.decode_attn_segments(segs, qt, 1, n_kv)
+    torch.cuda.synchronize()
+
+    ref = np.zeros((n_q, 128))
+    lref = np.zeros(n_q)
+    for g in range(n_q):
+        h = g // group
+        parts = []
+        for tau in (2, 4):
+            ii = idx[tau][h]
+            rec = [O.reconstruct(O.encode_codes(x[t][h][ii], arts[(tau, t)][h]), arts[(tau, t)][h])
+                   for t in (synth.K, synth.V)]
+            parts.append((rec[0], rec[1]))
+        parts.append((x[synth.K][h][idx[16][h]], x[synth.V][h][idx[16][h]]))
+        ref[g], lref[g] = O.segment_attention(q[g], parts)
+    err = np.abs(out[0].cpu().numpy() - ref).max()
+    lerr = np.abs(lse[0].cpu().numpy() - lref).max()
+    print("segments", avg_bits, [[len(i) for i in idx[tau]] for tau in (0, 2, 4, 16)], "err", err, lerr, flush=True)
+    assert err <= ATOL_ATTN, err
+    assert lerr <= 5e-3, lerr

@@ -173,3 +173,45 @@ def test_validate_detects_corruption():
 def test_status_strings(L):
     for s in range(8):
         assert L.aatc_status_string(s)
+
+
+# ---------------------------------------------------------------- token tiers (host)
+def _head_sigma2(cfg, h):
+    return [O.calibrate(synth.draw(cfg, 0, h, t, "calib", 1024), "klt", 2.76)["sigma2"] for t in (synth.K, synth.V)]
+
+
+def test_tier_distortions_match_oracle():
+    for h in range(2):
+        s2 = _head_sigma2(5, h)
+        got = api.tier_distortions(s2)
+        want = O.tier_distortions(s2, 128)
+        assert got[3] == 0.0 and want[3] == 0.0
+        assert np.allclose(got, want, rtol=1e-12, atol=0.0), (got, want)
+    s2 = synth.spectrum(128)
+    assert np.allclose(api.tier_distortions([s2, s2]), O.tier_distortions([s2, s2], 128), rtol=1e-12, atol=0.0)
+
+
+@pytest.mark.parametrize("n,avg", [(4096, 2.76), (131072, 2.76), (4096, 0.5), (4096, 8.0), (300, 16.0),
+                                   (300, 0.0)])
+def test_token_tiers_match_oracle(n, avg):
+    """Same distortions in, the same tier per token out (both sides follow one bisection)."""
+    s2 = synth.spectrum(128)
+    dist = O.tier_distortions([s2, s2], 128)
+    a = synth.zipf_mass(5, 0, 0, n)
+    got = api.token_tiers(a, dist, avg)
+    want = O.token_tiers(a, dist, 128, avg)
+    assert np.array_equal(got.astype(np.int64), want.astype(np.int64))
+    assert got.astype(np.int64).sum() * 128 <= avg * n * 128
+
+
+def test_token_tiers_errors(L):
+    dist = np.array([1.0, 0.1, 0.01, 0.0])
+    with pytest.raises(N.AatcError) as e:
+        api.token_tiers(np.ones(4) / 4, dist, 17.0)
+    assert e.value.name == "AATC_ERR_BUDGET"
+    with pytest.raises(N.AatcError) as e:
+        api.token_tiers(np.array([0.5, -0.1, 0.3, 0.3]), dist, 2.0)
+    assert e.value.name == "AATC_ERR_NUMERICAL"
+    with pytest.raises(N.AatcError) as e:
+        api.tier_distortions([np.full(128, np.nan)])
+    assert e.value.name == "AATC_ERR_NUMERICAL"
