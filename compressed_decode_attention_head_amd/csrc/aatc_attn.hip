@@ -24,7 +24,7 @@ int vtiles_bucket(int vt) {
 int round1k(int64_t x) { return static_cast<int>((x + 1023) / 1024 * 1024); }
 
 struct Plan {
-  int NP, NVB, LIMBS, S, tpw, half, prec;
+  int NP, NVB, LIMBS, S, tpw, half, prec, prod;
   int nslot, slot_bytes, ksz, gs;
   size_t lds;
   size_t part_bytes, offs_bytes;
@@ -36,8 +36,7 @@ struct Plan {
 int round16(int64_t x) { return static_cast<int>((x + 15) / 16 * 16); }
 
 // Tiles per wave fill 256 CUs x CW waves once; each wave gets a ring of LDS slots (one tile
-// each), as many as fit, at most its tile count.  A wave copies the next group's tiles while it
-// computes on the current group, so groups of gs tiles want 2 gs slots.
+// each), as many as fit, at most its tile count.
 Plan make_plan(const aatc_cache* c, int n_q, int64_t max_seq) {
   Plan p;
   const int kb = c->k_bits, vb = c->v_bits;
@@ -65,8 +64,10 @@ Plan make_plan(const aatc_cache* c, int n_q, int64_t max_seq) {
   if (ns > p.tpw) ns = p.tpw;
   p.nslot = ns;
   p.fits = ns >= 1;
+  // one score group per wave when its tiles all fit (no running-max rescale at all);
+  // otherwise groups of half the slots, so that the next group's copies fly meanwhile
   if (ns >= p.tpw) {
-    p.gs = p.tpw < TG ? p.tpw : TG;      // every tile has its own slot
+    p.gs = p.tpw < TG ? p.tpw : TG;
   } else {
     p.gs = ns / 2 < TG ? ns / 2 : TG;
     if (p.gs < 1) p.gs = 1;
@@ -77,6 +78,13 @@ Plan make_plan(const aatc_cache* c, int n_q, int64_t max_seq) {
   if (ring < merge) ring = merge;
   p.lds = FIXED_LDS + ring;
   if (p.lds + kStaticLds > kLdsLimit) p.fits = false;
+  // copy waves issue every tile when all of a wave's tiles have slots and the copy count of one
+  // copy wave stays within what one wait can count
+  {
+    const int ik = kb > 0 ? (static_cast<int>((15 + 8LL * kb + 15) / 16) + 63) / 64 : 0;
+    const int iv = vb > 0 ? (static_cast<int>((15 + 8LL * vb + 15) / 16) + 63) / 64 : 0;
+    p.prod = (p.NVB == 12 && p.NP <= 2 && ns >= p.tpw && (CW / NPROD_MAX) * p.tpw * (ik + iv) <= 60) ? NPROD_MAX : 0;
+  }
   p.part_bytes = static_cast<size_t>(seqs) * p.S * group * p.prec * 4;
   p.offs_bytes = static_cast<size_t>(seqs) * 8 * 4;
   // combine: a chunk of records per LDS fill (at most 64 KB, at most 1024 splits)
@@ -173,6 +181,7 @@ aatc_status launch_partial(const aatc_cache* c, const Plan& p, const float* q, i
   a.slot_bytes = p.slot_bytes;
   a.ksz = p.ksz;
   a.gs = p.gs;
+  a.prod = p.prod;
   const dim3 grid(p.S, c->n_kv_heads, c->batch);
   hipError_t err = hipSuccess;
   const bool ok = dispatch(p, a, kcal, vcal, grid, st, &err);

@@ -39,6 +39,7 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "aatc_internal.h"
 
@@ -52,7 +53,6 @@ constexpr float PKN_BIAS = -2.000067f;
 constexpr int PHDR = 4;                   // record header floats: max (log2 units), sum, 0, 0
 constexpr int CW = 8;                     // waves per workgroup
 constexpr int NTH = CW * 64;
-constexpr int AHEAD = 2;                  // tiles a wave copies before its prologue
 constexpr int TG = 4;                     // at most this many tiles per score group
 constexpr int UNION_BYTES = 3 * 8 * D * 4;    // q / q~ / alpha
 constexpr int TAB_BYTES = 2304;           // K delta32 | o32 | bits | plane_channel | plane_bit
@@ -81,13 +81,19 @@ struct AttnArgs {
   int nslot;                          // ring slots per compute wave (>= 1)
   int slot_bytes, ksz;                // bytes per slot (K area first, ksz bytes)
   int gs;                             // tiles per score group, 1..TG, <= nslot
+  int prod;                           // copy waves (0 or NPROD_MAX) issue every tile copy
 };
+
+constexpr int NPROD_MAX = 4;              // copy waves of the producer form (one per SIMD)
 
 // Wave handshakes, in static LDS.
 struct Sync {
   int arrive[CW];                     // barriers passed, per wave
+  int landed[CW];                     // producer form: tiles of compute wave w in LDS
+  int tabs[NPROD_MAX];                // producer form: copy wave p's table copies in LDS
   int broken;                         // a bounded wait gave up
 };
+
 
 __device__ inline int row_max16_i(int x) {
   x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x121, 0xf, 0xf, false));
@@ -216,6 +222,15 @@ __device__ inline void compute_barrier(Sync* sy, int& phase, int lane) {
   if (lane == 0) lds_store(&sy->broken, 1);
 }
 
+// Waits (bounded) until *p >= v; on giving up marks the workgroup broken.
+__device__ inline void poll_ge(const int* p, int v, Sync* sy, int lane) {
+  for (int it = 0; it < SPIN_LIMIT; ++it) {
+    if (lds_load_now(p) >= v) return;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  if (lane == 0) lds_store(&sy->broken, 1);
+}
+
 // Plane base (within a token's B-bit string) of the K window that lane group `grp` reads for
 // MFMA pair u; a half pair (last pair with <= 64 planes) interleaves 4-plane groups so that
 // one MFMA covers 64 planes.
@@ -264,9 +279,9 @@ __device__ inline int dma_bytes(const char* p, int n, uint8_t* dst, int lane) {
   return ni;
 }
 
-template <int NP, bool HALF, int NVB, int LIMBS>
-__global__ __launch_bounds__(NTH) void k_attn_main(AttnArgs a, const aatc_calib* __restrict__ kcal,
-                                                   const aatc_calib* __restrict__ vcal) {
+template <int NP, bool HALF, int NVB, int LIMBS, int NPROD>
+__global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, const aatc_calib* __restrict__ kcal,
+                                                                 const aatc_calib* __restrict__ vcal) {
   using LM = Lim<LIMBS>;
   extern __shared__ __align__(16) unsigned char smem[];
   float* qs = reinterpret_cast<float*>(smem);                       // [8][128]   q
@@ -298,21 +313,74 @@ __global__ __launch_bounds__(NTH) void k_attn_main(AttnArgs a, const aatc_calib*
   const aatc_calib* vc = vcal + h;
   const int G = a.group;
   const int Bk = a.kB, Bv = a.vB;
-  int64_t seq64 = a.seq_lens ? static_cast<int64_t>(a.seq_lens[a.seq_per_head ? bh : b]) : a.max_seq;
-  seq64 = seq64 < 0 ? 0 : (seq64 > a.max_seq ? a.max_seq : seq64);     // never read past the cache
-  const int seq = static_cast<int>(seq64);                      // tokens per sequence < 2^31
-  const int ntiles = (seq + 63) / 64;
   const int NS = a.nslot;
   const int64_t kbytes = 8 * static_cast<int64_t>(Bk), vbytes = 8 * static_cast<int64_t>(Bv);
   const char* kseq = reinterpret_cast<const char*>(a.kcodes) + static_cast<int64_t>(bh) * a.tiles_per_seq * kbytes;
   const char* vseq = reinterpret_cast<const char*>(a.vcodes) + static_cast<int64_t>(bh) * a.tiles_per_seq * vbytes;
   auto first_tile = [&](int w) { return (s * CW + w) * a.tpw; };
+  auto slot_of = [&](int w, int r) { return ring + (w * NS + r % NS) * a.slot_bytes; };
+
+  const int tw0 = first_tile(wave);
+
+  // ---- 1. copies, issued before any load from memory: this wave's share of the queries and
+  // K tables, then as many of its tiles as its ring holds (usually all of them; they land
+  // while the prologue runs).  Until the sequence length is known, tiles up to max_seq are
+  // copied (they lie inside the cache); only tiles below the length are used.
+  // table copies of the WAVES copying waves, instruction k by wave k % WAVES
+  auto copy_tables = [&](auto waves_tag, int me) {
+    constexpr int WAVES = decltype(waves_tag)::value;
+    int k = 0;
+    k = dma_words<WAVES>(a.q + (static_cast<int64_t>(b) * a.n_q + h * G) * D, qs, G * D, k, me, lane);
+    k = dma_words<WAVES>(kc->delta32, t_delta, D, k, me, lane);
+    k = dma_words<WAVES>(kc->o32, t_o, D, k, me, lane);
+    k = dma_words<WAVES>(kc->bits, tab + 1024, D / 4, k, me, lane);
+    k = dma_words<WAVES>(kc->plane_channel, tab + 1280, (Bk + 3) / 4, k, me, lane);
+    k = dma_words<WAVES>(kc->plane_bit, tab + 1792, (Bk + 3) / 4, k, me, lane);
+  };
+  if (NPROD == 0) copy_tables(std::integral_constant<int, CW>(), wave);
+  // tile r of this wave goes to ring slot r % NS; copies are issued in tile order, so tile r
+  // has landed once at most (instructions issued after it) copies are outstanding
+  // tile r of compute wave w: its K and V bytes, the copy instructions they take, its slot
+  auto kaddr_w = [&](int w, int r) { return kseq + (first_tile(w) + r) * kbytes; };
+  auto vaddr_w = [&](int w, int r) { return vseq + (first_tile(w) + r) * vbytes; };
+  auto ninstr_w = [&](int w, int r) {
+    const int uk = Bk > 0 ? static_cast<int>((((reinterpret_cast<uintptr_t>(kaddr_w(w, r)) & 15) + kbytes + 15) >> 4)) : 0;
+    const int uv = Bv > 0 ? static_cast<int>((((reinterpret_cast<uintptr_t>(vaddr_w(w, r)) & 15) + vbytes + 15) >> 4)) : 0;
+    return ((uk + 63) >> 6) + ((uv + 63) >> 6);
+  };
+  auto copy_tile = [&](int w, int r) {
+    uint8_t* sl = slot_of(w, r);
+    if (Bk > 0) dma_bytes(kaddr_w(w, r), static_cast<int>(kbytes), sl, lane);
+    if (Bv > 0) dma_bytes(vaddr_w(w, r), static_cast<int>(vbytes), sl + a.ksz, lane);
+  };
+  auto ninstr = [&](int r) { return ninstr_w(wave, r); };
+  int nxt = 0;                           // next tile of this wave to copy (self-issue form)
+  auto issue_upto = [&](int limit, int nmax) {   // copy tiles [nxt, min(limit, nmax))
+    const int lim = limit < nmax ? limit : nmax;
+    for (; nxt < lim; ++nxt) copy_tile(wave, nxt);
+  };
+  auto wait_tile = [&](int r) {
+    int after = 0;
+    for (int t = r + 1; t < nxt; ++t) after += ninstr(t);
+    wait_vmcnt(after);
+  };
+  // tiles of compute wave w below max_seq (copied before the sequence length is known)
+  auto ncap_w = [&](int w) {
+    const int n = static_cast<int>((a.max_seq + 63) / 64) - first_tile(w);
+    return n < 0 ? 0 : (n < a.tpw ? n : a.tpw);
+  };
+  if (NPROD == 0) issue_upto(NS, ncap_w(wave));
+  asm volatile("" ::: "memory");         // the loads below stay behind the copies
+
+  int64_t seq64 = a.seq_lens ? static_cast<int64_t>(a.seq_lens[a.seq_per_head ? bh : b]) : a.max_seq;
+  seq64 = seq64 < 0 ? 0 : (seq64 > a.max_seq ? a.max_seq : seq64);     // never read past the cache
+  const int seq = static_cast<int>(seq64);                      // tokens per sequence < 2^31
+  const int ntiles = (seq + 63) / 64;
   auto tiles_of = [&](int w) {
     const int t0 = first_tile(w);
     const int n = ntiles - t0 < a.tpw ? ntiles - t0 : a.tpw;
     return n > 0 ? n : 0;
   };
-  auto slot_of = [&](int w, int r) { return ring + (w * NS + r % NS) * a.slot_bytes; };
 
   const int n4 = vc->n_fields4, n2 = vc->n_fields2, n1 = vc->n_fields1;   // scalar loads
   const int T4 = (n4 + 15) >> 4, T2 = (n2 + 15) >> 4, T1 = (n1 + 15) >> 4;
@@ -321,53 +389,56 @@ __global__ __launch_bounds__(NTH) void k_attn_main(AttnArgs a, const aatc_calib*
                   vc->total_bits == Bv && n4 >= 0 && n2 >= 0 && n1 >= 0 && NV <= NVB && PHDR + 16 * NV <= a.prec;
   const int rot = kc->rotation;
   const int nw = ok ? tiles_of(wave) : 0;   // a bad blob streams nothing
-  const int tw0 = first_tile(wave);
 
-  if (tid < CW) sy.arrive[tid] = 0;
-  if (tid == 0) sy.broken = 0;
-  __syncthreads();                       // the only workgroup barrier (no copy in flight yet)
-  int phase = 0;
-
-  // ---- 1. copies: this wave's share of the tables, then its first tiles
-  {
-    int k = 0;
-    k = dma_words<CW>(a.q + (static_cast<int64_t>(b) * a.n_q + h * G) * D, qs, G * D, k, wave, lane);
-    k = dma_words<CW>(kc->delta32, t_delta, D, k, wave, lane);
-    k = dma_words<CW>(kc->o32, t_o, D, k, wave, lane);
-    k = dma_words<CW>(kc->bits, tab + 1024, D / 4, k, wave, lane);
-    k = dma_words<CW>(kc->plane_channel, tab + 1280, (Bk + 3) / 4, k, wave, lane);
-    k = dma_words<CW>(kc->plane_bit, tab + 1792, (Bk + 3) / 4, k, wave, lane);
+  if (tid < CW) {
+    sy.arrive[tid] = 0;
+    sy.landed[tid] = 0;
   }
-  // tile r of this wave goes to ring slot r % NS; copies are issued in tile order, so tile r
-  // has landed once at most (instructions issued after it) copies are outstanding
-  auto kaddr = [&](int r) { return kseq + (tw0 + r) * kbytes; };
-  auto vaddr = [&](int r) { return vseq + (tw0 + r) * vbytes; };
-  auto ninstr = [&](int r) {
-    const int uk = Bk > 0 ? static_cast<int>((((reinterpret_cast<uintptr_t>(kaddr(r)) & 15) + kbytes + 15) >> 4)) : 0;
-    const int uv = Bv > 0 ? static_cast<int>((((reinterpret_cast<uintptr_t>(vaddr(r)) & 15) + vbytes + 15) >> 4)) : 0;
-    return ((uk + 63) >> 6) + ((uv + 63) >> 6);
-  };
-  int nxt = 0;                           // next tile of this wave to copy
-  auto issue_upto = [&](int limit) {     // copy tiles [nxt, min(limit, nw))
-    const int lim = limit < nw ? limit : nw;
-    for (; nxt < lim; ++nxt) {
-      uint8_t* sl = slot_of(wave, nxt);
-      if (Bk > 0) dma_bytes(kaddr(nxt), static_cast<int>(kbytes), sl, lane);
-      if (Bv > 0) dma_bytes(vaddr(nxt), static_cast<int>(vbytes), sl + a.ksz, lane);
-    }
-  };
-  auto wait_tile = [&](int r) {
-    int after = 0;
-    for (int t = r + 1; t < nxt; ++t) after += ninstr(t);
-    wait_vmcnt(after);
-  };
-  issue_upto(AHEAD < NS ? AHEAD : NS);
-  {
+  if (tid < NPROD_MAX) sy.tabs[tid] = 0;
+  if (tid == 0) sy.broken = 0;
+  // the only workgroup barrier: LDS writes done, then s_barrier, with no wait on the copies
+  __builtin_amdgcn_s_waitcnt(0xC07F);    // lgkmcnt(0); vmcnt and expcnt not waited on
+  __builtin_amdgcn_s_barrier();
+
+  if (NPROD > 0 && wave >= CW) {
+    // ---- copy wave p: the tables' share k % NPROD == p, then every tile of compute waves
+    // CPP*p .. CPP*p + CPP - 1 in the order they are consumed, publishing each as it lands.
+    // The compute waves never block on an issue queue that HBM drains.
+    constexpr int CPP = CW / (NPROD > 0 ? NPROD : 1);
+    const int p = wave - CW;
+    copy_tables(std::integral_constant<int, (NPROD > 0 ? NPROD : 1)>(), p);
+    wait_vmcnt(0);                       // the compute waves start their prologue on the tables
+    if (lane == 0) lds_store(&sy.tabs[p], 1);
+    int total = 0;
+    for (int r = 0; r < a.tpw; ++r)
+      for (int ci = 0; ci < CPP; ++ci) {
+        const int w = CPP * p + ci;
+        if (r < ncap_w(w)) {
+          copy_tile(w, r);
+          total += ninstr_w(w, r);
+        }
+      }
+    for (int r = 0; r < a.tpw; ++r)
+      for (int ci = 0; ci < CPP; ++ci) {
+        const int w = CPP * p + ci;
+        if (r < ncap_w(w)) {
+          total -= ninstr_w(w, r);
+          wait_vmcnt(total);             // copies complete in issue order
+          if (lane == 0) lds_store(&sy.landed[w], r + 1);
+        }
+      }
+    return;
+  }
+
+  int phase = 0;
+  if (NPROD == 0) {
     int after = 0;                       // this wave's table copies have landed ...
     for (int t = 0; t < nxt; ++t) after += ninstr(t);
     wait_vmcnt(after);
+    compute_barrier(&sy, phase, lane);   // ... and so have everyone else's
+  } else {
+    for (int q = 0; q < NPROD; ++q) poll_ge(&sy.tabs[q], 1, &sy, lane);
   }
-  compute_barrier(&sy, phase, lane);     // ... and so have everyone else's
 
   // ---- 1. prologue: q~ = R_K q, alpha, exponents, lse offsets, limb weights
   // wave x (< 8) owns head slot x: q~ at channels lane and 64 + lane
@@ -525,6 +596,7 @@ __global__ __launch_bounds__(NTH) void k_attn_main(AttnArgs a, const aatc_calib*
 #pragma unroll 1
   for (int g0 = 0; g0 < nw; g0 += a.gs) {
     const int ng = nw - g0 < a.gs ? nw - g0 : a.gs;
+    if (NPROD == 0) issue_upto(g0 + NS, nw);   // every free slot: tiles before g0 are done with
 
     // opaque copies of the V class bounds: keeps the compiler from hoisting one condition
     // register pair per column group out of the loop
@@ -536,9 +608,8 @@ __global__ __launch_bounds__(NTH) void k_attn_main(AttnArgs a, const aatc_calib*
     for (int g = 0; g < TG; ++g) {
       const int rr = g0 + (g < ng ? g : 0);             // past the group's end: recompute, masked
       if (g < ng) {
-        // keep AHEAD tiles in flight; slots of tiles before g0 are free, this group's are not
-        issue_upto(g0 + g + 1 + AHEAD < g0 + NS ? g0 + g + 1 + AHEAD : g0 + NS);
-        wait_tile(g0 + g);
+        if (NPROD > 0) poll_ge(&sy.landed[wave], g0 + g + 1, &sy, lane);
+        else wait_tile(g0 + g);
         wave_sync_lds();
       }
       const int64_t tile = tw0 + rr;
@@ -757,6 +828,7 @@ __global__ __launch_bounds__(NTH) void k_attn_main(AttnArgs a, const aatc_calib*
     s_m[wave][lane] = -INFINITY;
     s_l[wave][lane] = 0.f;
   }
+  wait_vmcnt(0);                         // copies of tiles past the sequence's end, if any
   compute_barrier(&sy, phase, lane);     // every tile copy has landed and been read
   if (wave == 0 && lane < 8) {
     float m = -INFINITY;
@@ -996,21 +1068,27 @@ __global__ __launch_bounds__(CNT) void k_attn_combine(CombArgs a, const aatc_cal
 }
 #endif
 
-template <int NP, bool HALF, int NVB, int LIMBS>
+template <int NP, bool HALF, int NVB, int LIMBS, int NPROD>
 hipError_t launch_one(const AttnArgs& a, const aatc_calib* kcal, const aatc_calib* vcal, dim3 grid, size_t lds,
                       hipStream_t st) {
-  const void* fn = reinterpret_cast<const void*>(&k_attn_main<NP, HALF, NVB, LIMBS>);
+  const void* fn = reinterpret_cast<const void*>(&k_attn_main<NP, HALF, NVB, LIMBS, NPROD>);
   const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_attn_main<NP, HALF, NVB, LIMBS>), grid, dim3(NTH), lds, st, a, kcal, vcal);
+  hipLaunchKernelGGL((k_attn_main<NP, HALF, NVB, LIMBS, NPROD>), grid, dim3((CW + NPROD) * 64), lds, st, a, kcal,
+                     vcal);
   return hipGetLastError();
 }
 
+// The producer form runs 12 waves, 3 per SIMD, so only the smallest V bucket with at most two
+// bit-plane pairs fits its registers.
 template <int NP, bool HALF, int NVB>
 hipError_t launch_limbs(int limbs, const AttnArgs& a, const aatc_calib* kcal, const aatc_calib* vcal, dim3 grid,
                         size_t lds, hipStream_t st) {
-  return limbs == 3 ? launch_one<NP, HALF, NVB, 3>(a, kcal, vcal, grid, lds, st)
-                    : launch_one<NP, HALF, NVB, 2>(a, kcal, vcal, grid, lds, st);
+  if (NVB == 12 && NP <= 2 && a.prod)
+    return limbs == 3 ? launch_one<NP, HALF, NVB, 3, NPROD_MAX>(a, kcal, vcal, grid, lds, st)
+                      : launch_one<NP, HALF, NVB, 2, NPROD_MAX>(a, kcal, vcal, grid, lds, st);
+  return limbs == 3 ? launch_one<NP, HALF, NVB, 3, 0>(a, kcal, vcal, grid, lds, st)
+                    : launch_one<NP, HALF, NVB, 2, 0>(a, kcal, vcal, grid, lds, st);
 }
 
 template <int NP, bool HALF>
