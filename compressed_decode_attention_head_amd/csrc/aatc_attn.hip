@@ -21,15 +21,11 @@ int vtiles_bucket(int vt) {
   return -1;
 }
 
-int round1k(int64_t x) { return static_cast<int>((x + 1023) / 1024 * 1024); }
-
 struct Plan {
   int NP, NVB, LIMBS, S, tpw, half, prec, prod;
   int nslot, slot_bytes, ksz, gs;
   size_t lds;
   size_t part_bytes, offs_bytes;
-  int SC, rec_bytes;
-  size_t comb_lds;
   bool fits;
 };
 
@@ -87,14 +83,6 @@ Plan make_plan(const aatc_cache* c, int n_q, int64_t max_seq) {
   }
   p.part_bytes = static_cast<size_t>(seqs) * p.S * group * p.prec * 4;
   p.offs_bytes = static_cast<size_t>(seqs) * 8 * 4;
-  // combine: a chunk of records per LDS fill (at most 64 KB, at most 1024 splits)
-  int sc = static_cast<int>((64 * 1024) / (p.prec * 4));
-  if (sc > 1024) sc = 1024;
-  if (sc > p.S) sc = p.S;
-  if (sc < 1) sc = 1;
-  p.SC = sc;
-  p.rec_bytes = round1k(static_cast<int64_t>(sc) * p.prec * 4);
-  p.comb_lds = static_cast<size_t>(p.rec_bytes) + CR_BYTES;
   return p;
 }
 
@@ -202,19 +190,14 @@ aatc_status launch_merge(const aatc_cache* c, const Plan& p, int32_t n_q, const 
   cb.group = group;
   cb.S = p.S;
   cb.prec = p.prec;
-  cb.SC = p.SC;
-  cb.rec_bytes = p.rec_bytes;
   cb.seq_lens = seq_lens;
   cb.seq_per_head = seq_per_head;
   cb.max_seq = max_seq;
   cb.out = out;
   cb.lse = lse;
-  hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_combine),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(p.comb_lds));
-  if (err != hipSuccess) return aatc::fail(AATC_ERR_HIP, "decode_attn combine attribute: %s", hipGetErrorString(err));
-  hipLaunchKernelGGL(k_attn_combine, dim3(group, c->n_kv_heads, c->batch), dim3(CNT), p.comb_lds, st, cb,
+  hipLaunchKernelGGL(k_attn_combine, dim3(group, c->n_kv_heads, c->batch), dim3(CNT), 0, st, cb,
                      static_cast<const aatc_calib*>(c->v_calib));
-  err = hipGetLastError();
+  const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return aatc::fail(AATC_ERR_HIP, "decode_attn combine launch: %s", hipGetErrorString(err));
   return AATC_OK;
 }

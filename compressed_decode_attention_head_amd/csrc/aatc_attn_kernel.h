@@ -85,6 +85,7 @@ struct AttnArgs {
 };
 
 constexpr int NPROD_MAX = 4;              // copy waves of the producer form (one per SIMD)
+constexpr int SELF = 2;                   // producer form: tiles a compute wave copies itself, first
 
 // Wave handshakes, in static LDS.
 struct Sync {
@@ -306,6 +307,15 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);      // wave-uniform, kept scalar
+  // the flags start at zero: the only workgroup barrier, before any load or copy
+  if (tid < CW) {
+    sy.arrive[tid] = 0;
+    sy.landed[tid] = 0;
+  }
+  if (tid < NPROD_MAX) sy.tabs[tid] = 0;
+  if (tid == 0) sy.broken = 0;
+  __builtin_amdgcn_s_waitcnt(0xC07F);    // lgkmcnt(0); vmcnt and expcnt not waited on
+  __builtin_amdgcn_s_barrier();
   const int n16 = lane & 15, grp = lane >> 4;
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int bh = b * a.n_kv + h;
@@ -370,6 +380,39 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
     return n < 0 ? 0 : (n < a.tpw ? n : a.tpw);
   };
   if (NPROD == 0) issue_upto(NS, ncap_w(wave));
+  // producer form: a copy wave sustains only a few GB/s, so the compute waves copy their own
+  // first SELF tiles (all eight waves issuing at once) and the copy waves the rest
+  if (NPROD > 0 && wave < CW) issue_upto(SELF, ncap_w(wave));
+  if (NPROD > 0 && wave >= CW) {
+    // ---- copy wave p: the tables' share k % NPROD == p, then every tile of compute waves
+    // CPP*p .. CPP*p + CPP - 1 in the order they are consumed, publishing each as it lands.
+    // The compute waves never block on an issue queue that HBM drains.
+    constexpr int CPP = CW / (NPROD > 0 ? NPROD : 1);
+    const int p = wave - CW;
+    copy_tables(std::integral_constant<int, (NPROD > 0 ? NPROD : 1)>(), p);
+    wait_vmcnt(0);                       // the compute waves start their prologue on the tables
+    if (lane == 0) lds_store(&sy.tabs[p], 1);
+    int total = 0;
+    for (int r = SELF; r < a.tpw; ++r)
+      for (int ci = 0; ci < CPP; ++ci) {
+        const int w = CPP * p + ci;
+        if (r < ncap_w(w)) {
+          copy_tile(w, r);
+          total += ninstr_w(w, r);
+        }
+      }
+    for (int r = SELF; r < a.tpw; ++r)
+      for (int ci = 0; ci < CPP; ++ci) {
+        const int w = CPP * p + ci;
+        if (r < ncap_w(w)) {
+          total -= ninstr_w(w, r);
+          wait_vmcnt(total);             // copies complete in issue order
+          if (lane == 0) lds_store(&sy.landed[w], r + 1);
+        }
+      }
+    return;
+  }
+
   asm volatile("" ::: "memory");         // the loads below stay behind the copies
 
   int64_t seq64 = a.seq_lens ? static_cast<int64_t>(a.seq_lens[a.seq_per_head ? bh : b]) : a.max_seq;
@@ -385,50 +428,15 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
   const int n4 = vc->n_fields4, n2 = vc->n_fields2, n1 = vc->n_fields1;   // scalar loads
   const int T4 = (n4 + 15) >> 4, T2 = (n2 + 15) >> 4, T1 = (n1 + 15) >> 4;
   const int NV = T4 + T2 + T1;
-  const bool ok = kc->magic == AATC_MAGIC && vc->magic == AATC_MAGIC && kc->total_bits == Bk &&
-                  vc->total_bits == Bv && n4 >= 0 && n2 >= 0 && n1 >= 0 && NV <= NVB && PHDR + 16 * NV <= a.prec;
+  // every header field is loaded at once: a short-circuit chain would wait for each in turn
+  const uint32_t kmag = kc->magic, vmag = vc->magic;
+  const int kbits = kc->total_bits, vbits = vc->total_bits;
+  const bool ok = (kmag == AATC_MAGIC) & (vmag == AATC_MAGIC) & (kbits == Bk) & (vbits == Bv) & (n4 >= 0) &
+                  (n2 >= 0) & (n1 >= 0) & (NV <= NVB) & (PHDR + 16 * NV <= a.prec);
   const int rot = kc->rotation;
   const int nw = ok ? tiles_of(wave) : 0;   // a bad blob streams nothing
 
-  if (tid < CW) {
-    sy.arrive[tid] = 0;
-    sy.landed[tid] = 0;
-  }
-  if (tid < NPROD_MAX) sy.tabs[tid] = 0;
-  if (tid == 0) sy.broken = 0;
-  // the only workgroup barrier: LDS writes done, then s_barrier, with no wait on the copies
-  __builtin_amdgcn_s_waitcnt(0xC07F);    // lgkmcnt(0); vmcnt and expcnt not waited on
-  __builtin_amdgcn_s_barrier();
 
-  if (NPROD > 0 && wave >= CW) {
-    // ---- copy wave p: the tables' share k % NPROD == p, then every tile of compute waves
-    // CPP*p .. CPP*p + CPP - 1 in the order they are consumed, publishing each as it lands.
-    // The compute waves never block on an issue queue that HBM drains.
-    constexpr int CPP = CW / (NPROD > 0 ? NPROD : 1);
-    const int p = wave - CW;
-    copy_tables(std::integral_constant<int, (NPROD > 0 ? NPROD : 1)>(), p);
-    wait_vmcnt(0);                       // the compute waves start their prologue on the tables
-    if (lane == 0) lds_store(&sy.tabs[p], 1);
-    int total = 0;
-    for (int r = 0; r < a.tpw; ++r)
-      for (int ci = 0; ci < CPP; ++ci) {
-        const int w = CPP * p + ci;
-        if (r < ncap_w(w)) {
-          copy_tile(w, r);
-          total += ninstr_w(w, r);
-        }
-      }
-    for (int r = 0; r < a.tpw; ++r)
-      for (int ci = 0; ci < CPP; ++ci) {
-        const int w = CPP * p + ci;
-        if (r < ncap_w(w)) {
-          total -= ninstr_w(w, r);
-          wait_vmcnt(total);             // copies complete in issue order
-          if (lane == 0) lds_store(&sy.landed[w], r + 1);
-        }
-      }
-    return;
-  }
 
   int phase = 0;
   if (NPROD == 0) {
@@ -608,7 +616,7 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
     for (int g = 0; g < TG; ++g) {
       const int rr = g0 + (g < ng ? g : 0);             // past the group's end: recompute, masked
       if (g < ng) {
-        if (NPROD > 0) poll_ge(&sy.landed[wave], g0 + g + 1, &sy, lane);
+        if (NPROD > 0 && g0 + g >= SELF) poll_ge(&sy.landed[wave], g0 + g + 1, &sy, lane);
         else wait_tile(g0 + g);
         wave_sync_lds();
       }
@@ -897,15 +905,14 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
 }
 
 // Merge of the S partial records of one (batch, KV head, q head); out and lse.
-constexpr int CNT = 256;                 // combine threads (4 waves)
-constexpr int CR_BYTES = D * D * 4;      // LDS for R_V (fp32) when the rotation is a KLT
+constexpr int CNT = 1024;                // combine threads: 4 split quarters x 256 columns
+constexpr int SPC = 64;                  // splits per pass (16 per quarter, held in registers)
+constexpr int MAXCOL = 16 * 24;          // field columns of a record, at most
 
 struct CombArgs {
   const float* part;
   const float* offs;
   int n_kv, n_q, group, S, prec;
-  int SC;                                // splits per LDS chunk of records
-  int rec_bytes;                         // LDS bytes of one chunk (multiple of 1024)
   const int32_t* seq_lens;
   int seq_per_head;                      // seq_lens is [batch][n_kv] (else [batch])
   int64_t max_seq;
@@ -914,108 +921,130 @@ struct CombArgs {
 };
 
 #ifdef AATC_ATTN_COMBINE_TU   // defined by the one translation unit that launches it
-// Copies n16 16-byte units, unit e = (record e / q4, quad e % q4) of records spaced `stride`
-// floats apart, into consecutive LDS quads; lanes past n16 re-read unit 0 (padding).
-__device__ inline int dma_records(const float* rec0, int64_t stride, int q4, int n16, uint8_t* dst, int k, int wave,
-                                  int lane) {
-  for (int i = 0; i < n16; i += 64, ++k)
-    if (k % (CNT / 64) == wave) {
-      const int e = i + lane < n16 ? i + lane : 0;
-      const int sp = e / q4, qd = e - sp * q4;
-      const float* p = rec0 + sp * stride + 4 * qd;
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(p), dst + i * 16, 16, 0, 0);
-    }
-  return k;
-}
-
+// Every input of the merge is read with ordinary loads issued at once at kernel entry (records,
+// V tables, R_V), so the kernel pays about one memory round trip before its arithmetic.
 __global__ __launch_bounds__(CNT) void k_attn_combine(CombArgs a, const aatc_calib* __restrict__ vcal) {
-  extern __shared__ __align__(16) unsigned char csm[];
-  float* recs = reinterpret_cast<float*>(csm);                        // [SC][prec]
-  float* rv = reinterpret_cast<float*>(csm + a.rec_bytes);            // [128][128] (KLT)
-  __shared__ __align__(16) float t_o[D], t_delta[D];
-  __shared__ __align__(16) uint8_t t_bits[256];
-  __shared__ __align__(16) int16_t t_cf[3 * D];
-  __shared__ __align__(16) uint8_t t_fs[512];
-  __shared__ float wsl[1024];
-  __shared__ float csum[3 * D];
-  __shared__ float yt[D];
-  __shared__ float red[CNT / 64][2];
+  __shared__ float wsl[SPC];
+  __shared__ float part4[4][MAXCOL];
+  __shared__ float csum[MAXCOL];
+  __shared__ float t_o[D], t_delta[D];
+  __shared__ int t_bits[D];
+  __shared__ int16_t t_cf[3 * D];
+  __shared__ uint8_t t_fs[AATC_MAX_FIELDS];
+  __shared__ float yt[D], res[D];
+  __shared__ float part8[8][D];
+  __shared__ float red[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int G = a.group, S = a.S, prec = a.prec, SC = a.SC, q4 = prec / 4;
+  const int G = a.group, S = a.S, prec = a.prec;
   const int bh = b * a.n_kv + h;
-  const aatc_calib* vc = vcal + h;      // header fields come in as scalar loads
+  const aatc_calib* vc = vcal + h;
   const float* rec0 = a.part + (static_cast<int64_t>(bh) * S * G + g) * prec;
   const int64_t stride = static_cast<int64_t>(G) * prec;
+  const int qtr = tid >> 8, cl = tid & 255;
 
-  // records of the first chunk, the V tables and (KLT) R_V, all in flight at once
-  int k = 0;
-  const int n0 = S < SC ? S : SC;
-  k = dma_records(rec0, stride, q4, n0 * q4, csm, k, wave, lane);
-  k = dma_words<CNT / 64>(vc->o32, t_o, D, k, wave, lane);
-  k = dma_words<CNT / 64>(vc->delta32, t_delta, D, k, wave, lane);
-  k = dma_words<CNT / 64>(vc->bits, t_bits, D / 4, k, wave, lane);
-  k = dma_words<CNT / 64>(vc->channel_field, t_cf, 3 * D / 2, k, wave, lane);
-  k = dma_words<CNT / 64>(vc->field_shift, t_fs, 3 * D / 4, k, wave, lane);
+  // the first pass's records (headers and this thread's column values) before anything that
+  // depends on a load: these are the long pole
+  float hm = -INFINITY, hl = 0.f;
+  float v0[SPC / 4], v1[SPC / 4];
+  auto load_pass = [&](int s0) {
+    const int n = S - s0 < SPC ? S - s0 : SPC;
+    // unconditional loads from clamped (always valid) addresses, masked afterwards: a load under
+    // a branch makes the compiler wait for every load before it at the join
+    const bool hv = lane < n;
+    const float* hp = rec0 + (s0 + (hv ? lane : 0)) * stride;
+    hm = hp[0];
+    hl = hp[1];
+    hm = hv ? hm : -INFINITY;
+    hl = hv ? hl : 0.f;
+    const bool cv0 = cl < prec - PHDR, cv1 = cl + 256 < prec - PHDR;   // record length: a kernel argument
+    const int o0 = PHDR + (cv0 ? cl : 0), o1 = PHDR + (cv1 ? cl + 256 : 0);
+#pragma unroll
+    for (int j = 0; j < SPC / 4; ++j) {
+      const int sp = qtr + 4 * j;
+      const bool sv = sp < n;
+      const float* rp = rec0 + (s0 + (sv ? sp : 0)) * stride;
+      v0[j] = rp[o0];
+      v1[j] = rp[o1];
+    }
+#pragma unroll
+    for (int j = 0; j < SPC / 4; ++j) {
+      const bool sv = qtr + 4 * j < n;
+      v0[j] = (sv && cv0) ? v0[j] : 0.f;
+      v1[j] = (sv && cv1) ? v1[j] : 0.f;
+    }
+  };
+  load_pass(0);
+  // tables and R_V, consumed last
+  const int ti = tid & (D - 1), tf = tid < 3 * D ? tid : 0;   // clamped table indexes
+  const float r_o = vc->o32[ti], r_d = vc->delta32[ti];
+  const int r_b = vc->bits[ti], r_cf = vc->channel_field[tf], r_fs = vc->field_shift[tf];
   const int rot = vc->rotation;
-  if (rot == AATC_ROT_KLT) k = dma_words<CNT / 64>(vc->R32, rv, D * D, k, wave, lane);
+  float rv[16];
+  if (rot == AATC_ROT_KLT) {
+    const int j = tid & (D - 1), e8 = tid >> 7;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) rv[k] = vc->R32[(16 * e8 + k) * D + j];
+  }
   int64_t seq = a.seq_lens ? static_cast<int64_t>(a.seq_lens[a.seq_per_head ? bh : b]) : a.max_seq;
   seq = seq < 0 ? 0 : (seq > a.max_seq ? a.max_seq : seq);
   const int n4 = vc->n_fields4, n2 = vc->n_fields2, n1 = vc->n_fields1;
   const int T4 = (n4 + 15) >> 4, T2 = (n2 + 15) >> 4;
   const int ncol_blob = 16 * (T4 + T2 + ((n1 + 15) >> 4));
-  bool bad = PHDR + ncol_blob > prec;      // fields that do not fit a record: NaN result
+  bool bad = PHDR + ncol_blob > prec || ncol_blob > MAXCOL || n4 < 0 || n2 < 0 || n1 < 0;
   const int ncol = bad ? 0 : ncol_blob;
-  for (int e = tid; e < 3 * D; e += CNT) csum[e] = 0.f;
+  const int c0 = cl, c1 = cl + 256;       // this thread's columns
 
-  float M = -INFINITY, L = 0.f;
-  for (int c0 = 0; c0 < S; c0 += SC) {
-    const int n = S - c0 < SC ? S - c0 : SC;
-    if (c0 > 0) dma_records(rec0 + c0 * stride, stride, q4, n * q4, csm, 0, wave, lane);
-    wait_vmcnt(0);
-    __syncthreads();
+  float M = -INFINITY, L = 0.f, acc0 = 0.f, acc1 = 0.f;
+  for (int s0 = 0; s0 < S; s0 += SPC) {
+    if (s0 > 0) load_pass(s0);
     if (wave == 0) {
-      // chunk max, split weights and probability sum, in one wave
-      float m = -INFINITY;
-      bool nan = false;
-      for (int sp = lane; sp < n; sp += 64) {
-        const float v = recs[sp * prec];
-        nan |= v != v;
-        m = fmaxf(m, v);
-      }
-      m = wave_max_x(m);
+      const bool nan = hm != hm;
+      const float m = wave_max_x(hm);
       const float nM = fmaxf(M, m);
-      float l = 0.f;
-      for (int sp = lane; sp < n; sp += 64) {
-        const float v = recs[sp * prec];
-        const float w = (v == -INFINITY || nM == -INFINITY) ? 0.f : exp2f(v - nM);
-        wsl[sp] = w;
-        l += w * recs[sp * prec + 1];
-      }
-      l = wave_sum_x(l);
+      const float w = (hm == -INFINITY || nM == -INFINITY) ? 0.f : exp2f(hm - nM);
+      if (lane < SPC) wsl[lane] = w;
+      const float l = wave_sum_x(w * hl);
       const bool anynan = __ballot(nan) != 0;
       if (lane == 0) {
-        red[0][0] = nM;
-        red[0][1] = l;
-        red[1][0] = anynan ? 1.f : 0.f;
+        red[0] = nM;
+        red[1] = l;
+        red[2] = anynan ? 1.f : 0.f;
       }
     }
     __syncthreads();
-    const float nM = red[0][0];
+    const float nM = red[0];
     const float fold = (M == -INFINITY) ? 0.f : exp2f(M - nM);
-    bad |= red[1][0] != 0.f;
-    L = L * fold + red[0][1];
+    bad |= red[2] != 0.f;
+    L = L * fold + red[1];
     M = nM;
-    for (int col = tid; col < ncol; col += CNT) {
-      float sacc = csum[col] * fold;
-#pragma unroll 8
-      for (int sp = 0; sp < n; ++sp) sacc = fmaf(wsl[sp], recs[sp * prec + PHDR + col], sacc);
-      csum[col] = sacc;
+    float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < SPC / 4; ++j) {
+      const float w = wsl[(qtr + 4 * j) & (SPC - 1)];
+      p0 = fmaf(w, v0[j], p0);
+      p1 = fmaf(w, v1[j], p1);
     }
-    __syncthreads();                      // recs, wsl and red are reused by the next chunk
+    acc0 = acc0 * fold + p0;
+    acc1 = acc1 * fold + p1;
+    __syncthreads();                     // wsl and red are rewritten by the next pass
   }
+  // quarters -> column sums; tables -> LDS
+  if (c0 < MAXCOL) part4[qtr][c0] = acc0;
+  if (c1 < MAXCOL) part4[qtr][c1] = acc1;
+  if (tid < D) {
+    t_o[tid] = r_o;
+    t_delta[tid] = r_d;
+    t_bits[tid] = r_b;
+  }
+  if (tid < 3 * D) t_cf[tid] = static_cast<int16_t>(r_cf);
+  if (tid < AATC_MAX_FIELDS) t_fs[tid] = static_cast<uint8_t>(r_fs);
+  __syncthreads();
+  if (tid < ncol) csum[tid] = (part4[0][tid] + part4[1][tid]) + (part4[2][tid] + part4[3][tid]);
+  __syncthreads();
   // fold field columns into channel code sums; y = o + delta (c_bar - 2^(b-1) + 1/2)
-  for (int i = tid; i < D; i += CNT) {
+  if (tid < D) {
+    const int i = tid;
     float cs = 0.f;
     for (int kk = 0; kk < 3; ++kk) {
       const int f = t_cf[3 * i + kk];
@@ -1032,34 +1061,31 @@ __global__ __launch_bounds__(CNT) void k_attn_combine(CombArgs a, const aatc_cal
     yt[i] = y;
   }
   __syncthreads();
-  float o = 0.f;
   if (rot == AATC_ROT_WHT) {
     if (wave == 0) {
       float x0 = yt[lane], x1 = yt[64 + lane];
       fwht128(x0, x1, lane);
-      csum[lane] = x0 * 0.08838834764831845f;
-      csum[64 + lane] = x1 * 0.08838834764831845f;
+      res[lane] = x0 * 0.08838834764831845f;
+      res[64 + lane] = x1 * 0.08838834764831845f;
     }
   } else if (rot == AATC_ROT_KLT) {
-    // out_j = sum_i R[i][j] y_i: two threads per output, 64 rows each
-    const int j = tid & 127, hf = tid >> 7;
-#pragma unroll 16
-    for (int i = 64 * hf; i < 64 * hf + 64; ++i) o = fmaf(rv[i * D + j], yt[i], o);
+    // out_j = sum_i R[i][j] y_i: eight threads per output, 16 rows each
+    const int j = tid & (D - 1), e8 = tid >> 7;
+    float o = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) o = fmaf(rv[k], yt[16 * e8 + k], o);
+    part8[e8][j] = o;
+    __syncthreads();
+    if (tid < D)
+      res[tid] = ((part8[0][tid] + part8[1][tid]) + (part8[2][tid] + part8[3][tid])) +
+                 ((part8[4][tid] + part8[5][tid]) + (part8[6][tid] + part8[7][tid]));
   } else if (tid < D) {
-    csum[tid] = yt[tid];
+    res[tid] = yt[tid];
   }
   __syncthreads();
-  if (rot == AATC_ROT_KLT) {
-    if (tid >= 128) csum[tid - 128] = o;
-    __syncthreads();
-    if (tid < 128) csum[128 + tid] = o + csum[tid];
-    __syncthreads();
-  }
-  const float* res = rot == AATC_ROT_KLT ? csum + 128 : csum;
   const int64_t qh = static_cast<int64_t>(b) * a.n_q + h * G + g;
   const bool empty = seq == 0;
-  for (int j = tid; j < D; j += CNT)
-    a.out[qh * D + j] = bad ? NAN : (L > 0.f ? res[j] : (empty ? 0.f : NAN));
+  if (tid < D) a.out[qh * D + tid] = bad ? NAN : (L > 0.f ? res[tid] : (empty ? 0.f : NAN));
   if (a.lse && tid == 0) {
     const float l2 = bad ? NAN : (L > 0.f ? M + log2f(L / static_cast<float>(PS)) + a.offs[bh * 8 + g]
                                           : (empty ? -INFINITY : NAN));
