@@ -1,0 +1,126 @@
+"""GPU parity at the workloads' full sizes, on sampled outputs the oracle computes one by one.
+
+Each case builds a whole layer at its real shape (every KV head, the full context) through the
+same C-ABI calls the benchmark times, then checks sampled KV heads against the fp64 oracle:
+packed codes (bit-exact up to the bin-edge excuse) and decode attention for every q head of the
+sampled KV heads (max abs error <= 2e-3, lse <= 5e-3).  Inputs are the seeded host draws, so
+both sides see identical values.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+from gpu_helpers import excused_mismatch_report, unpack_all
+
+pytestmark = pytest.mark.gpu
+
+ATOL_ATTN = 2e-3
+
+
+def _layer(cfg, n_tokens, sampled, n_encode=None):
+    """Calibrate every KV head (library and oracle), encode the first n_encode (default all)
+    context tokens on the GPU.  Returns (cache, q [batch, n_q, d] float32, host contexts of the
+    sampled (b, h), oracle arts, tails: tokens n_encode.. of every (tensor, b, h))."""
+    import torch
+    from compressed_decode_attention_head_amd import api
+    batch = cfg.batch
+    blobs, arts = {}, {}
+    for t in (synth.K, synth.V):
+        cal = [synth.draw(cfg.idx, 0, h, t, "calib", cfg.n_calib, dtype=cfg.dtype, marginal=cfg.marginal)
+               for h in range(cfg.n_kv_heads)]
+        blobs[t] = [api.calibrate(synth.bf16_bits(c), cfg.rotation, cfg.bits_per_elem) for c in cal]
+        arts[t] = {h: O.calibrate(cal[h], cfg.rotation, cfg.bits_per_elem) for h in {s[1] for s in sampled}}
+    cap = -(-n_tokens // 64) * 64
+    cache = api.CompressedKVCache(blobs[synth.K], blobs[synth.V], batch, cap)
+    n_enc = n_tokens if n_encode is None else n_encode
+    host, tails = {}, {}
+    keys_for_q = {}
+    for t in (synth.K, synth.V):
+        x = torch.empty((batch, cfg.n_kv_heads, n_enc, 128), dtype=torch.bfloat16, device="cuda")
+        for b in range(batch):
+            for h in range(cfg.n_kv_heads):
+                xh = synth.draw(cfg.idx, 0, h, t, "context", n_tokens, dtype=cfg.dtype, marginal=cfg.marginal,
+                                extra=b)
+                x[b, h] = torch.from_numpy(xh[:n_enc].astype(np.float32)).to(torch.bfloat16)
+                tails[(t, b, h)] = xh[n_enc:]
+                if (b, h) in sampled:
+                    host[(t, b, h)] = xh
+                if t == synth.K and b == 0:
+                    keys_for_q[h] = xh[:4096]
+        cache.encode(t, x)
+        del x
+    q = synth.queries(cfg.idx, 0, cfg.n_q_heads, cfg.n_kv_heads, [keys_for_q[h] for h in range(cfg.n_kv_heads)])
+    q = np.broadcast_to(q, (batch,) + q.shape).copy()
+    torch.cuda.synchronize()
+    return cache, q, host, arts, tails
+
+
+def _check_head(cfg, cache, q, host, arts, b, h, n, out, lse, check_codes):
+    group = cfg.n_q_heads // cfg.n_kv_heads
+    codes = {}
+    for t in (synth.K, synth.V):
+        codes[t] = O.encode_codes(host[(t, b, h)][:n], arts[t][h])
+        if check_codes:
+            # tiles are packed independently: the first 8192 tokens and the last tile (which
+            # holds appended tokens) stand for the whole sequence; unpacking in the oracle is slow
+            words = cache.codes(t)[b, h].cpu().numpy().view(np.uint32)
+            bits = arts[t][h]["bits"]
+            wpt = 2 * int(bits.sum())                       # words per 64-token tile
+            last = (n - 1) // 64
+            for t0, nt in ((0, min(n, 8192)), (64 * last, n - 64 * last)):
+                w = words[(t0 // 64) * wpt:(t0 // 64) * wpt + O.packed_words(int(bits.sum()), nt)]
+                got = unpack_all(w, bits, nt, t)
+                want = codes[t][t0:t0 + nt]
+                n_bad, n_unexc = excused_mismatch_report(host[(t, b, h)][t0:t0 + nt], arts[t][h], got, want)
+                assert n_unexc == 0 and n_bad <= 1e-6 * want.size + 1, (t, b, h, t0, n_bad)
+    ref, lref = O.decode_attention(q[b, h * group:(h + 1) * group], [codes[synth.K]], [codes[synth.V]],
+                                   [arts[synth.K][h]], [arts[synth.V][h]])
+    o = out[b, h * group:(h + 1) * group]
+    l = lse[b, h * group:(h + 1) * group]
+    err = float(np.abs(o - ref).max())
+    lerr = float(np.abs(l - lref).max())
+    print("config %d (b=%d, h=%d, n=%d): max abs err %.2e, lse err %.2e" % (cfg.idx, b, h, n, err, lerr), flush=True)
+    assert err <= ATOL_ATTN and lerr <= 5e-3, (err, lerr)
+
+
+@pytest.mark.parametrize("idx,sampled", [(4, [(0, 0), (0, 3)]), (2, [(0, 0), (0, 7)])])
+def test_fullsize_layer_sampled_heads(idx, sampled):
+    """128K-token WHT 1.33-bit layer (4 KV heads, 28 q heads) and 32K-token KLT 2.76-bit layer
+    (8 KV heads, 32 q heads): whole layer on the GPU, two KV heads checked against the oracle."""
+    import torch
+    cfg = synth.CONFIGS[idx]
+    n = cfg.n_tokens
+    cache, q, host, arts, _ = _layer(cfg, n, set(sampled))
+    qt = torch.from_numpy(q).cuda()
+    ws = cache.new_workspace(cfg.n_q_heads, n)
+    out = torch.empty_like(qt)
+    lse = torch.empty((cfg.batch, cfg.n_q_heads), dtype=torch.float32, device="cuda")
+    cache.decode_attn(qt, n, workspace=ws, out=out, lse=lse)
+    torch.cuda.synchronize()
+    o, l = out.cpu().numpy(), lse.cpu().numpy()
+    for i, (b, h) in enumerate(sampled):
+        _check_head(cfg, cache, q, host, arts, b, h, n, o, l, check_codes=(i == 0))
+
+
+def test_fullsize_batch16_append_sampled():
+    """Batch 16 x 8 KV heads x 8192 tokens, KLT 4.0 bits, then decode steps that each append one
+    encoded token per (b, h): sampled sequences checked after the appends."""
+    import torch
+    cfg = synth.CONFIGS[3]
+    n0, steps = cfg.n_tokens, 3
+    sampled = {(0, 0), (9, 5), (15, 7)}
+    cache, q, host, arts, tails = _layer(cfg, n0 + steps, sampled, n_encode=n0)
+    # decode steps: each appends one encoded token per (b, h) to the prefill
+    for s in range(steps):
+        for t in (synth.K, synth.V):
+            x = np.stack([np.stack([tails[(t, b, h)][s] for h in range(cfg.n_kv_heads)]) for b in range(cfg.batch)])
+            xt = torch.from_numpy(x[:, :, None, :].astype(np.float32)).to(torch.bfloat16).cuda()
+            cache.encode(t, xt, token_offset=n0 + s)
+    n = n0 + steps
+    qt = torch.from_numpy(q).cuda()
+    out, lse = cache.decode_attn(qt, n)
+    torch.cuda.synchronize()
+    o, l = out.cpu().numpy(), lse.cpu().numpy()
+    for i, (b, h) in enumerate(sorted(sampled)):
+        _check_head(cfg, cache, q, host, arts, b, h, n, o, l, check_codes=(i == 0))
