@@ -520,6 +520,9 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
       if (s == 0 && g < G) a.offs[bh * 8 + g] = off;
     }
   }
+  // producer form: this wave's own tiles (issued first) have long landed; waiting for them here,
+  // before the weights, keeps later register spill stores out of the wait
+  if (NPROD > 0) wait_vmcnt(0);
   compute_barrier(&sy, phase, lane);
   {
     // limb operand dwords: (pair u, half hh, dword j, lane) -> 4 bytes m of row (lane%16)
@@ -582,13 +585,16 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
   const int wb0 = prow_addr(hb), wb1 = prow_addr(8 + hb);
   const int prd = n16 * 64 + 16 * (grp ^ (n16 & 3));
   // LDS byte offset (within a tile's V area) of the V word(s) this lane reads for column group v
+  // (three candidates and a select per group: branches here cost more scalar issue than the
+  // arithmetic they would skip)
   int voff[NVB];
 #pragma unroll
   for (int v = 0; v < NVB; ++v) {
-    if (v < T4) voff[v] = 4 * (8 * ((v << 4) + n16) + 2 * grp);
-    else if (v < T4 + T2) voff[v] = 4 * (8 * n4 + 4 * (((v - T4) << 4) + n16) + grp);
-    else if (v < NV) voff[v] = 4 * (8 * n4 + 4 * n2 + 2 * (((v - T4 - T2) << 4) + n16) + (grp >> 1));
-    else voff[v] = 0;                    // unused group: harmless read of the tile's first words
+    const int o4 = 4 * (8 * ((v << 4) + n16) + 2 * grp);
+    const int o2 = 4 * (8 * n4 + 4 * (((v - T4) << 4) + n16) + grp);
+    const int o1 = 4 * (8 * n4 + 4 * n2 + 2 * (((v - T4 - T2) << 4) + n16) + (grp >> 1));
+    // unused group (v >= NV): a harmless read of the tile's first words
+    voff[v] = v < T4 ? o4 : (v < T4 + T2 ? o2 : (v < NV ? o1 : 0));
   }
   const uint32_t sh1 = 4 * (grp & 1);
 
@@ -616,8 +622,12 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
     for (int g = 0; g < TG; ++g) {
       const int rr = g0 + (g < ng ? g : 0);             // past the group's end: recompute, masked
       if (g < ng) {
-        if (NPROD > 0 && g0 + g >= SELF) poll_ge(&sy.landed[wave], g0 + g + 1, &sy, lane);
-        else wait_tile(g0 + g);
+        if (NPROD > 0) {
+          // its own copies (the first SELF tiles) were waited for before the weights
+          if (g0 + g >= SELF) poll_ge(&sy.landed[wave], g0 + g + 1, &sy, lane);
+        } else {
+          wait_tile(g0 + g);
+        }
         wave_sync_lds();
       }
       const int64_t tile = tw0 + rr;
