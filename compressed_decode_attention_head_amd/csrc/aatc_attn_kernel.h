@@ -798,21 +798,21 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
                                   ((reinterpret_cast<uintptr_t>(vseq) + tile * vbytes) & 15));
         asm volatile("" : "+v"(vt));
         const uint8_t* vl = ring + vt;
-        uint32_t x0[NVB], x1[NVB];
+        uint32_t x0[NVB];
 #pragma unroll
-        for (int v = 0; v < NVB; ++v) {         // unconditional: no per-read waits
+        for (int v = 0; v < NVB; ++v)           // unconditional: no per-read waits
           x0[v] = *reinterpret_cast<const uint32_t*>(vl + voff[v]);
-          x1[v] = *reinterpret_cast<const uint32_t*>(vl + voff[v] + 4);
-        }
 #pragma unroll
         for (int v = 0; v < NVB; ++v) {
           if (v < cNV) {
             v4i bv;
             if (v < cT4) {
+              // the second word only for nibble fields (registers are the scarce resource)
+              const uint32_t x1 = *reinterpret_cast<const uint32_t*>(vl + voff[v] + 4);
               bv[0] = static_cast<int>(x0[v] & 0x0F0F0F0Fu);
               bv[1] = static_cast<int>((x0[v] >> 4) & 0x0F0F0F0Fu);
-              bv[2] = static_cast<int>(x1[v] & 0x0F0F0F0Fu);
-              bv[3] = static_cast<int>((x1[v] >> 4) & 0x0F0F0F0Fu);
+              bv[2] = static_cast<int>(x1 & 0x0F0F0F0Fu);
+              bv[3] = static_cast<int>((x1 >> 4) & 0x0F0F0F0Fu);
             } else if (v < cT42) {
 #pragma unroll
               for (int r = 0; r < 4; ++r) bv[r] = static_cast<int>((x0[v] >> (2 * r)) & 0x03030303u);
