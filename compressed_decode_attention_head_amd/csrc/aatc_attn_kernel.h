@@ -19,17 +19,20 @@
 //   scores, LIMBS=3: 4 q-head slots x 3 limbs (22-bit weights), GQA <= 4;
 //   values: 8 q-head slots x 2 limbs of a 14-bit probability.
 //
-// k_attn_main, grid (S splits, KV heads, batch): a workgroup of CW waves owns a contiguous
-// range of 64-token tiles of one sequence, each wave `tpw` consecutive tiles.  Each wave
-//   1. copies its share of the K tables and the queries, and its first tiles, straight from
-//      HBM into LDS with global_load_lds (no registers), into a ring of per-wave tile slots,
-//   2. rotates the queries and builds the limb weights with the others while they fly,
-//   3. streams its tiles out of LDS in groups, keeping the next tiles' copies in flight:
-//      scores -> one running-max update per group -> probability rows -> PV, all in int32,
-//   4. merges with the others in LDS; the workgroup writes one partial record per q head:
-//      (running max, sum of probabilities, softmax-weighted code sum per V field column).
-// Waves synchronise through LDS counters with wavefront-scope ordering only (a workgroup
-// barrier would first wait for every copy in flight); every such wait is bounded.
+// k_attn_main, grid (S splits, KV heads, batch): a workgroup of CW compute waves owns a
+// contiguous range of 64-token tiles of one sequence, each wave `tpw` consecutive tiles.
+//   1. Tile copies go straight from HBM into per-wave rings of LDS slots with global_load_lds
+//      (no registers), issued before any load from memory.  In the producer form four extra
+//      copy waves copy the tables and all but each compute wave's first two tiles and publish
+//      every tile through an LDS flag as it lands; otherwise each compute wave copies its own.
+//   2. The compute waves rotate the queries and build the limb weights while tiles land.
+//   3. Each wave streams its tiles out of LDS in groups: scores -> one running-max update per
+//      group -> probability rows -> PV, all in int32.
+//   4. The waves merge in LDS; the workgroup writes one partial record per q head: (running
+//      max, sum of probabilities, softmax-weighted code sum per V field column).
+// Waves synchronise through LDS flags written and polled with hand-written ds instructions (an
+// atomic or volatile access, or a workgroup barrier, would first wait for every copy in
+// flight); every such wait is bounded.
 // k_attn_combine, grid (q heads per KV head, KV heads, batch): merges the S records of a
 // q head, folds field columns into channel code sums, dequantizes, applies R_V^T and writes
 // out and lse.  The kernel boundary orders the records; no atomics, no workspace clearing.
@@ -52,7 +55,6 @@ constexpr int PS = 16383;                 // probability scale: 14-bit fixed poi
 constexpr float PKN_BIAS = -2.000067f;
 constexpr int PHDR = 4;                   // record header floats: max (log2 units), sum, 0, 0
 constexpr int CW = 8;                     // waves per workgroup
-constexpr int NTH = CW * 64;
 constexpr int TG = 4;                     // at most this many tiles per score group
 constexpr int UNION_BYTES = 3 * 8 * D * 4;    // q / q~ / alpha
 constexpr int TAB_BYTES = 2304;           // K delta32 | o32 | bits | plane_channel | plane_bit
