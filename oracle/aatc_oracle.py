@@ -298,11 +298,11 @@ def reconstruct(codes, art):
 # V tiles -- field-major: channel i's code is split into fields by the binary expansion of
 #   b_i into widths {4,2,1} (8 = 4+4), low code bits in the widest field.  Fields are
 #   ordered by width descending, then channel ascending, then shift ascending.  A field of
-#   width w owns 2w consecutive words (64 tokens x w bits).  Token t = 16G + 4r + m
-#   (G, r, m in 0..3) stores its w-bit value LSB-first at bit offset
-#     w=1: 32*(G//2) + 8m + 4*(G%2) + r
-#     w=2: 32G + 8m + 2r
-#     w=4: 64G + 32*(r//2) + 8m + 4*(r%2)
+#   width w owns 2w consecutive words (64 tokens x w bits).  Bit b (LSB first) of the
+#   value of token t = 16G + 4r + m (G, r, m in 0..3) sits at bit offset
+#     w=1: 32*(G//2) + 8m + 2r + (G%2)
+#     w=2: 32G + ((8m + 2r + b + (G%2)) mod 32)      (odd G: the word rotated left by 1)
+#     w=4: 64G + 32*(r//2) + 8m + 4*(r%2) + b
 #   of the field's bit string.
 # ----------------------------------------------------------------------------------
 def packed_words(total_bits, n_tokens):
@@ -371,14 +371,15 @@ def v_fields(bits):
     return fields
 
 
-def _v_pos(t, w):
+def _v_bit(t, w, b):
+    """Offset of bit b of token t's w-bit value in its field's bit string (layout above)."""
     g, r, m = t // 16, (t // 4) % 4, t % 4
     if w == 1:
-        return 32 * (g // 2) + 8 * m + 4 * (g % 2) + r
+        return 32 * (g // 2) + 8 * m + 2 * r + (g % 2)
     if w == 2:
-        return 32 * g + 8 * m + 2 * r
+        return 32 * g + (8 * m + 2 * r + b + (g % 2)) % 32
     if w == 4:
-        return 64 * g + 32 * (r // 2) + 8 * m + 4 * (r % 2)
+        return 64 * g + 32 * (r // 2) + 8 * m + 4 * (r % 2) + b
     raise ValueError(w)
 
 
@@ -394,7 +395,8 @@ def pack_v(codes, bits):
         off = 0
         for (i, shift, w) in fields:
             val = (int(codes[t, i]) >> shift) & ((1 << w) - 1)
-            _set_bits(words, tile_base + off * 32 + _v_pos(t % TILE, w), val, w)
+            for b in range(w):
+                _set_bits(words, tile_base + off * 32 + _v_bit(t % TILE, w, b), (val >> b) & 1, 1)
             off += 2 * w
     return words
 
@@ -408,7 +410,8 @@ def unpack_v(words, bits, n):
         tile_base = (t // TILE) * 2 * b_total * 32
         off = 0
         for (i, shift, w) in fields:
-            codes[t, i] |= _get_bits(words, tile_base + off * 32 + _v_pos(t % TILE, w), w) << shift
+            for b in range(w):
+                codes[t, i] |= _get_bits(words, tile_base + off * 32 + _v_bit(t % TILE, w, b), 1) << (shift + b)
             off += 2 * w
     return codes
 

@@ -295,14 +295,18 @@ def test_pack_v_hand_example():
     bits = [3, 0, 1]
     # fields: (0,0,w2), (0,2,w1), (2,0,w1) -> words [0,4) w2, [4,6) w1 ch0 bit2, [6,8) w1 ch2
     codes = np.zeros((64, 3), dtype=np.int64)
-    codes[5, 0] = 6        # t=5: G=0 r=1 m=1 -> low field value 2 at 8m+2r = 10, bit2 at 8+0+1=9
-    codes[37, 2] = 1       # t=37: G=2 r=1 m=1 -> w1 offset 32*1 + 8 + 0 + 1 = 41
+    codes[5, 0] = 6        # t=5: G=0 r=1 m=1 -> low field value 2 at 8m+2r = 10, bit2 at 8+2+0 = 10
+    codes[37, 2] = 1       # t=37: G=2 r=1 m=1 -> w1 offset 32*1 + 8 + 2 + 0 = 42
+    codes[31, 0] = 2       # t=31: G=1 r=3 m=3 -> w2 in word 1 rotated by 1: bit 0 at 31, bit 1 wraps to 0
+    codes[20, 2] = 1       # t=20: G=1 r=1 m=0 -> w1 offset 0 + 0 + 2 + 1 = 3
     w = O.pack_v(codes, bits)
     assert w.size == 8
     assert int(w[0]) == (2 << 10)
-    assert int(w[4]) == (1 << 9)
-    assert int(w[6 + 1]) == (1 << (41 - 32))
-    assert sum(int(v) != 0 for v in w) == 3
+    assert int(w[1]) == 1
+    assert int(w[4]) == (1 << 10)
+    assert int(w[6]) == (1 << 3)
+    assert int(w[6 + 1]) == (1 << (42 - 32))
+    assert sum(int(v) != 0 for v in w) == 5
 
 
 def test_pack_roundtrip_and_sizes():
@@ -319,8 +323,28 @@ def test_pack_roundtrip_and_sizes():
 
 def test_v_field_positions_are_bijective():
     for w in (1, 2, 4):
-        pos = sorted(O.aatc_oracle._v_pos(t, w) for t in range(64))
-        assert pos == list(range(0, 64 * w, w))
+        pos = sorted(O.aatc_oracle._v_bit(t, w, b) for t in range(64) for b in range(w))
+        assert pos == list(range(64 * w))
+
+
+def test_v_lane_words_expand_by_uniform_shifts():
+    """The decode kernel's operand rule: lane group G of a 16-token block reads one word per
+    w<=2 field, rotates it right by G%2, and finds token 16G + 4r + m's value at bit 8m + 2r."""
+    rng = np.random.default_rng(3)
+    for w in (1, 2):
+        vals = rng.integers(0, 1 << w, size=64)
+        words = np.zeros(2 * w, dtype=np.uint32)
+        for t in range(64):
+            for b in range(w):
+                if (vals[t] >> b) & 1:
+                    s = O.aatc_oracle._v_bit(t, w, b)
+                    words[s // 32] |= np.uint32(1 << (s % 32))
+        for g in range(4):
+            x = int(words[g if w == 2 else g // 2])
+            d = ((x >> (g % 2)) | (x << (32 - g % 2))) & 0xFFFFFFFF if g % 2 else x
+            for r in range(4):
+                for m in range(4):
+                    assert (d >> (8 * m + 2 * r)) & ((1 << w) - 1) == vals[16 * g + 4 * r + m]
 
 
 # ---------------------------------------------------------------- scores and attention
