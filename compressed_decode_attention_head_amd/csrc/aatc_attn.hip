@@ -23,7 +23,7 @@ int vtiles_bucket(int vt) {
 
 struct Plan {
   int NP, NVB, LIMBS, S, tpw, half, prec, prod;
-  int nslot, slot_bytes, ksz, gs;
+  int nslot, slot_bytes, ksz, gs, wave_bytes;
   size_t lds;
   size_t part_bytes, offs_bytes;
   bool fits;
@@ -68,10 +68,10 @@ Plan make_plan(const aatc_cache* c, int n_q, int64_t max_seq) {
     p.gs = ns / 2 < TG ? ns / 2 : TG;
     if (p.gs < 1) p.gs = 1;
   }
-  size_t ring = static_cast<size_t>(CW) * (ns > 0 ? ns : 1) * p.slot_bytes + DMA_PAD;
-  // the merge reuses the ring: CW x NVB x 32 lanes x float4
-  const size_t merge = static_cast<size_t>(CW) * p.NVB * 32 * 16;
-  if (ring < merge) ring = merge;
+  // a wave's ring area holds its slots, and at the end its merge values (NVB x 32 lanes x float4)
+  p.wave_bytes = (ns > 0 ? ns : 1) * p.slot_bytes;
+  if (p.wave_bytes < p.NVB * 32 * 16) p.wave_bytes = p.NVB * 32 * 16;
+  const size_t ring = static_cast<size_t>(CW) * p.wave_bytes + DMA_PAD;
   p.lds = FIXED_LDS + ring;
   if (p.lds + kStaticLds > kLdsLimit) p.fits = false;
   // copy waves issue every tile when all of a wave's tiles have slots and the copy count of one
@@ -167,6 +167,7 @@ aatc_status launch_partial(const aatc_cache* c, const Plan& p, const float* q, i
   a.vB = c->v_bits;
   a.nslot = p.nslot;
   a.slot_bytes = p.slot_bytes;
+  a.wave_bytes = p.wave_bytes;
   a.ksz = p.ksz;
   a.gs = p.gs;
   a.prod = p.prod;

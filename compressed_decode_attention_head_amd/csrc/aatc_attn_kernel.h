@@ -56,8 +56,8 @@ constexpr float PKN_BIAS = -2.000067f;
 constexpr int PHDR = 4;                   // record header floats: max (log2 units), sum, 0, 0
 constexpr int CW = 8;                     // waves per workgroup
 constexpr int TG = 4;                     // at most this many tiles per score group
-constexpr int UNION_BYTES = 3 * 8 * D * 4;    // q / q~ / alpha
-constexpr int TAB_BYTES = 2304;           // K delta32 | o32 | bits | plane_channel | plane_bit
+constexpr int UNION_BYTES = 2 * 8 * D * 4;    // q / q~
+constexpr int TAB_BYTES = 1280;           // K delta32 | o32 | bits
 constexpr int WA_BYTES = 4 * 2 * 4 * 64 * 4;  // limb weight operands, NP <= 4
 constexpr int FIXED_LDS = UNION_BYTES + TAB_BYTES + WA_BYTES;   // then the ring
 constexpr int PROW_BYTES = 16 * 64;       // probability rows of one tile (16 rows x 64 bytes)
@@ -82,6 +82,8 @@ struct AttnArgs {
   int kB, vB;
   int nslot;                          // ring slots per compute wave (>= 1)
   int slot_bytes, ksz;                // bytes per slot (K area first, ksz bytes)
+  int wave_bytes;                     // ring bytes per compute wave: its slots, then (at the
+                                      // end) its [NVB][32][4] floats of the merge
   int gs;                             // tiles per score group, 1..TG, <= nslot
   int prod;                           // copy waves (0 or NPROD_MAX) issue every tile copy
 };
@@ -227,8 +229,10 @@ __device__ inline void compute_barrier(Sync* sy, int& phase, int lane) {
 
 // Waits (bounded) until *p >= v; on giving up marks the workgroup broken.
 __device__ inline void poll_ge(const int* p, int v, Sync* sy, int lane) {
+#pragma unroll 1
   for (int it = 0; it < SPIN_LIMIT; ++it) {
-    if (lds_load_now(p) >= v) return;
+    // every lane reads the same word: compare once, in a scalar register
+    if (__builtin_amdgcn_readfirstlane(lds_load_now(p)) >= v) return;
     __builtin_amdgcn_s_sleep(1);
   }
   if (lane == 0) lds_store(&sy->broken, 1);
@@ -289,22 +293,17 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
   extern __shared__ __align__(16) unsigned char smem[];
   float* qs = reinterpret_cast<float*>(smem);                       // [8][128]   q
   float* qt = qs + 8 * D;                                           // [8][128]   R_K q (KLT)
-  float* al = qt + 8 * D;                                           // [8][128]   alpha
   uint8_t* tab = smem + UNION_BYTES;
   float* t_delta = reinterpret_cast<float*>(tab);                   // [128]
   float* t_o = t_delta + D;                                         // [128]
   const uint8_t* t_bits = tab + 1024;                               // [128]
-  const uint8_t* t_pch = tab + 1280;                                // [<=512]
-  const uint8_t* t_pbit = tab + 1792;                               // [<=512]
   int* wa_lds = reinterpret_cast<int*>(smem + UNION_BYTES + TAB_BYTES);        // [NP*2*4*64]
-  uint8_t* ring = smem + FIXED_LDS;                                 // [CW][nslot][slot]
+  uint8_t* ring = smem + FIXED_LDS;                                 // [CW][wave_bytes]
   // probability limb rows live in their own static array: no tile copy can write them, so
   // reading them needs no wait on the copies in flight
   __shared__ __align__(16) uint8_t pl[CW * TG * PROW_BYTES];        // [CW][TG][16][64]
-  float* mg = reinterpret_cast<float*>(ring);                       // merge: [CW][NVB][32][4]
   __shared__ float s_m[CW][8], s_l[CW][8];
-  __shared__ float s_M[8], s_L[8], esc[8];
-  __shared__ int wexp[8];
+  __shared__ float esc[8];
   __shared__ Sync sy;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -330,7 +329,8 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
   const char* kseq = reinterpret_cast<const char*>(a.kcodes) + static_cast<int64_t>(bh) * a.tiles_per_seq * kbytes;
   const char* vseq = reinterpret_cast<const char*>(a.vcodes) + static_cast<int64_t>(bh) * a.tiles_per_seq * vbytes;
   auto first_tile = [&](int w) { return (s * CW + w) * a.tpw; };
-  auto slot_of = [&](int w, int r) { return ring + (w * NS + r % NS) * a.slot_bytes; };
+  // the producer form is planned only when every tile of a wave has its own slot
+  auto slot_of = [&](int w, int r) { return ring + w * a.wave_bytes + (NPROD > 0 ? r : r % NS) * a.slot_bytes; };
 
   const int tw0 = first_tile(wave);
 
@@ -346,8 +346,6 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
     k = dma_words<WAVES>(kc->delta32, t_delta, D, k, me, lane);
     k = dma_words<WAVES>(kc->o32, t_o, D, k, me, lane);
     k = dma_words<WAVES>(kc->bits, tab + 1024, D / 4, k, me, lane);
-    k = dma_words<WAVES>(kc->plane_channel, tab + 1280, (Bk + 3) / 4, k, me, lane);
-    k = dma_words<WAVES>(kc->plane_bit, tab + 1792, (Bk + 3) / 4, k, me, lane);
   };
   if (NPROD == 0) copy_tables(std::integral_constant<int, CW>(), wave);
   // tile r of this wave goes to ring slot r % NS; copies are issued in tile order, so tile r
@@ -498,13 +496,16 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
       y1 = 0.f;
     }
     float m = 0.f, off = 0.f;
+    float alr[2];
+    int bir[2];
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int i = lane + 64 * r;
       const int bi = t_bits[i];
       const float v = r ? y1 : y0;
       const float alpha = bi ? v * t_delta[i] * a.scale2 : 0.f;
-      al[g * D + i] = alpha;
+      alr[r] = alpha;
+      bir[r] = bi;
       if (bi) m = fmaxf(m, fabsf(alpha) * static_cast<float>(1 << (bi - 1)));
       const float o = bi ? t_o[i] - t_delta[i] * (static_cast<float>(1 << (bi - 1)) - 0.5f) : t_o[i];
       off += v * o * a.scale2;
@@ -517,48 +518,58 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
       e = LM::WBITS - e;                 // m * 2^e in [2^(WBITS-1), 2^WBITS)
     }
     if (lane == 0) {
-      wexp[g] = e;
       esc[g] = (m > 0.f) ? ldexpf(1.f, -e) : 0.f;
       if (s == 0 && g < G) a.offs[bh * 8 + g] = off;
+    }
+    // limb operand rows of head slot g (the wave's own, so no other wave writes their dwords):
+    // LIMBS=2 rows g and 8+g; LIMBS=3 rows g, 4+g, 8+g for g < 4 and the spare row 8+g else.
+    // Operand dword (pair u, half hh, dword j, lane) holds bytes m of row lane%16, lane group
+    // lane/16 (the plane_base windows).  First zero them, then write each plane's limbs.
+    const int nrows = (LIMBS == 3 && g >= 4) ? 1 : LIMBS;
+    auto row_of = [&](int l) { return LIMBS == 2 ? 8 * l + g : (g < 4 ? 4 * l + g : 8 + g); };
+    for (int k = lane; k < nrows * NP * 32; k += 64) {
+      const int l = k / (NP * 32), c = (k >> 2) % (NP * 8), lg = k & 3;
+      wa_lds[c * 64 + lg * 16 + row_of(l)] = 0;
+    }
+    // plane index of this lane's channels' bit 0: prefix sums of the bit counts, one ballot
+    // per bit level
+    const uint64_t below = (1ull << lane) - 1ull;
+    int pb0 = 0, pb1 = 0, tot0 = 0;
+    int kmax = 0;
+    for (int k = 1; k <= AATC_MAX_BITS; ++k) {
+      const uint64_t b0 = __ballot(bir[0] >= k), b1 = __ballot(bir[1] >= k);
+      if ((b0 | b1) == 0) break;
+      kmax = k;
+      pb0 += __popcll(b0 & below);
+      pb1 += __popcll(b1 & below);
+      tot0 += __popcll(b0);
+    }
+    pb1 += tot0;
+    uint8_t* wab = reinterpret_cast<uint8_t*>(wa_lds);
+    const int wmaxq = (1 << LM::WBITS) - 1;
+    if (g < G) {
+      for (int kb = 0; kb < kmax; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          if (kb < bir[r]) {
+            const int p = (r ? pb1 : pb0) + kb;
+            const int u = p >> 7, pp = p & 127, q = pp & 31;
+            const bool hp = HALF && u == NP - 1;
+            const int lg = hp ? 2 * (pp >> 5) + ((pp >> 2) & 1) : (pp >> 5);
+            const int hh = hp ? 0 : ((q >> 2) & 1);
+            const int dw = ((u * 2 + hh) * 4 + (q & 3)) * 64 + lg * 16;
+            int wq = static_cast<int>(rintf(ldexpf(alr[r], kb + e)));
+            wq = wq > wmaxq ? wmaxq : (wq < -wmaxq ? -wmaxq : wq);
+#pragma unroll
+            for (int l = 0; l < LIMBS; ++l) wab[4 * (dw + row_of(l)) + (q >> 3)] = static_cast<uint8_t>(LM::limb(l, wq));
+          }
+        }
+      }
     }
   }
   // producer form: this wave's own tiles (issued first) have long landed; waiting for them here,
   // before the weights, keeps later register spill stores out of the wait
   if (NPROD > 0) wait_vmcnt(0);
-  compute_barrier(&sy, phase, lane);
-  {
-    // limb operand dwords: (pair u, half hh, dword j, lane) -> 4 bytes m of row (lane%16)
-    const int nwd = NP * 2 * 4 * 64;
-    const int wmaxq = (1 << LM::WBITS) - 1;
-    for (int e = tid; e < nwd; e += CW * 64) {
-      const int ln = e & 63, jj = (e >> 6) & 3, hh = (e >> 8) & 1, u = e >> 9;
-      const int row = ln & 15, lg = ln >> 4;
-      const int l = row / LM::PROW;
-      const int g = row % LM::PROW;
-      const bool hp = HALF && u == NP - 1;
-      const bool live = g < G && l < LIMBS && !(hp && hh);
-      int chs[4], kbs[4];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int p = plane_base(u, lg, hp) + 8 * m + (hp ? jj : 4 * hh + jj);
-        const bool in = live && p < Bk;
-        chs[m] = in ? t_pch[p] : -1;
-        kbs[m] = in ? t_pbit[p] : 0;
-      }
-      uint32_t word = 0;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        int val = 0;
-        if (chs[m] >= 0) {
-          int wq = static_cast<int>(rintf(ldexpf(al[g * D + chs[m]], kbs[m] + wexp[g])));
-          wq = wq > wmaxq ? wmaxq : (wq < -wmaxq ? -wmaxq : wq);
-          val = LM::limb(l, wq);
-        }
-        word |= (static_cast<uint32_t>(val) & 0xffu) << (8 * m);
-      }
-      wa_lds[e] = static_cast<int>(word);
-    }
-  }
   compute_barrier(&sy, phase, lane);
   v4i wa[NP][2];
 #pragma unroll
@@ -586,19 +597,17 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
   const int wa0 = prow_addr(ha), wa1 = prow_addr(8 + ha);
   const int wb0 = prow_addr(hb), wb1 = prow_addr(8 + hb);
   const int prd = n16 * 64 + 16 * (grp ^ (n16 & 3));
-  // LDS byte offset (within a tile's V area) of the V word(s) this lane reads for column group v
-  // (three candidates and a select per group: branches here cost more scalar issue than the
-  // arithmetic they would skip)
+  // LDS byte offset (within a tile's V area) of the V word(s) this lane reads for column group v:
+  // a scalar part (the group's class and position) plus one of three lane parts
+  const int L4 = 32 * n16 + 8 * grp, L2 = 16 * n16 + 4 * grp, L1 = 8 * n16 + 4 * (grp >> 1);
   int voff[NVB];
 #pragma unroll
   for (int v = 0; v < NVB; ++v) {
-    const int o4 = 4 * (8 * ((v << 4) + n16) + 2 * grp);
-    const int o2 = 4 * (8 * n4 + 4 * (((v - T4) << 4) + n16) + grp);
-    const int o1 = 4 * (8 * n4 + 4 * n2 + 2 * (((v - T4 - T2) << 4) + n16) + (grp >> 1));
+    const int s4 = 512 * v, s2 = 32 * n4 + 256 * (v - T4), s1 = 32 * n4 + 16 * n2 + 128 * (v - T4 - T2);
     // unused group (v >= NV): a harmless read of the tile's first words
-    voff[v] = v < T4 ? o4 : (v < T4 + T2 ? o2 : (v < NV ? o1 : 0));
+    voff[v] = v < T4 ? s4 + L4 : (v < T4 + T2 ? s2 + L2 : (v < NV ? s1 + L1 : 0));
   }
-  const uint32_t sh1 = 4 * (grp & 1);
+  const uint32_t rot1 = grp & 1;
 
   v4i acc[NVB];
 #pragma unroll
@@ -807,21 +816,21 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
 #pragma unroll
         for (int v = 0; v < NVB; ++v) {
           if (v < cNV) {
+            // 2- and 1-bit fields: one rotation by the lane group's parity, then the same
+            // shifts for both widths; only the mask differs (a scalar select)
             v4i bv;
-            if (v < cT4) {
-              // the second word only for nibble fields (registers are the scarce resource)
+            const uint32_t msk = v < cT42 ? 0x03030303u : 0x01010101u;
+            const uint32_t d = __builtin_amdgcn_alignbit(x0[v], x0[v], rot1);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) bv[r] = static_cast<int>((d >> (2 * r)) & msk);
+            if (__builtin_expect(v < cT4, 0)) {
+              // nibble fields (first in the tile): the second word only here (registers are
+              // the scarce resource)
               const uint32_t x1 = *reinterpret_cast<const uint32_t*>(vl + voff[v] + 4);
               bv[0] = static_cast<int>(x0[v] & 0x0F0F0F0Fu);
               bv[1] = static_cast<int>((x0[v] >> 4) & 0x0F0F0F0Fu);
               bv[2] = static_cast<int>(x1 & 0x0F0F0F0Fu);
               bv[3] = static_cast<int>((x1 >> 4) & 0x0F0F0F0Fu);
-            } else if (v < cT42) {
-#pragma unroll
-              for (int r = 0; r < 4; ++r) bv[r] = static_cast<int>((x0[v] >> (2 * r)) & 0x03030303u);
-            } else {
-              const uint32_t d = x0[v] >> sh1;
-#pragma unroll
-              for (int r = 0; r < 4; ++r) bv[r] = static_cast<int>((d >> r) & 0x01010101u);
             }
             acc[v] = __builtin_amdgcn_mfma_i32_16x16x64_i8(pA, bv, acc[v], 0, 0, 0);
           }
@@ -831,7 +840,9 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
     wave_sync_lds();                     // the group's slots and rows are reused next
   }
 
-  // ---- 3. workgroup merge in LDS (the ring is idle now: every wave's tiles have landed)
+  // ---- 3. workgroup merge in LDS: each wave parks its limb-merged code sums (unscaled) in its
+  // own ring area once every copy into it has landed; one barrier; then every thread scales
+  // and sums the CW waves' values of its record entries
   la = row_sum16_u(la);
   lb = row_sum16_u(lb);
   const float ma = ima == INT_MIN ? -INFINITY : static_cast<float>(ima) * esa;
@@ -848,32 +859,13 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
     s_m[wave][lane] = -INFINITY;
     s_l[wave][lane] = 0.f;
   }
-  wait_vmcnt(0);                         // copies of tiles past the sequence's end, if any
-  compute_barrier(&sy, phase, lane);     // every tile copy has landed and been read
-  if (wave == 0 && lane < 8) {
-    float m = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < CW; ++w) m = fmaxf(m, s_m[w][lane]);
-    float l = 0.f;
-#pragma unroll
-    for (int w = 0; w < CW; ++w) {
-      const float mw = s_m[w][lane];
-      l += mw == -INFINITY ? 0.f : s_l[w][lane] * __builtin_amdgcn_exp2f(mw - m);
-    }
-    s_M[lane] = m;
-    s_L[lane] = l;
-  }
-  compute_barrier(&sy, phase, lane);
+  wait_vmcnt(0);                         // this wave's own copies, past the sequence's end too
+  if (NPROD > 0 && ncap_w(wave) > SELF)  // and the copy waves' ones into its slots
+    poll_ge(&sy.landed[wave], ncap_w(wave), &sy, lane);
   {
-    // limb merge: lanes 0..31 (limb 0 rows) take the limb-1 rows of lanes 32..63; lane
-    // group grp<2 then holds head slots 4*grp + r, scaled to the workgroup max
-    float f[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int hd = 4 * (grp & 1) + r;
-      const float mine = s_m[wave][hd];
-      f[r] = (mine == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mine - s_M[hd]);
-    }
+    // limb merge: lanes 0..31 (limb 0 rows) take the limb-1 rows of lanes 32..63; lane group
+    // grp<2 then holds head slots 4*grp + r
+    float4* mgw = reinterpret_cast<float4*>(ring + wave * a.wave_bytes);
 #pragma unroll
     for (int v = 0; v < NVB; ++v) {
       if (v < NV) {
@@ -882,36 +874,51 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
         for (int r = 0; r < 4; ++r) {
           const auto sw = __builtin_amdgcn_permlane32_swap(static_cast<unsigned>(acc[v][r]),
                                                            static_cast<unsigned>(acc[v][r]), false, false);
-          const float c = (128.f * static_cast<float>(acc[v][r]) + static_cast<float>(static_cast<int>(sw[1]))) * f[r];
+          const float c = 128.f * static_cast<float>(acc[v][r]) + static_cast<float>(static_cast<int>(sw[1]));
           if (r == 0) o.x = c;
           if (r == 1) o.y = c;
           if (r == 2) o.z = c;
           if (r == 3) o.w = c;
         }
-        if (lane < 32) reinterpret_cast<float4*>(mg)[(wave * NVB + v) * 32 + lane] = o;
+        if (lane < 32) mgw[v * 32 + lane] = o;
       }
     }
   }
   compute_barrier(&sy, phase, lane);
-  // ---- 4. partial records: [max, sum, 0, 0, column sums]
-  {
+  // ---- 4. partial records: [max, sum, 0, 0, column sums]; wave x writes q head x's record,
+  // every wave's values scaled to the workgroup max of that head
+  if (wave < G) {
+    const int hd = wave;
     const bool good = ok && __hip_atomic_load(&sy.broken, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 0;
     const int ncol = ok ? 16 * NV : 0;     // a bad blob's field count may not fit a record
-    float* rec = a.part + (static_cast<int64_t>(bh) * a.S + s) * G * a.prec;
-    for (int hd = 0; hd < G; ++hd)
-      for (int col = tid; col < ncol; col += CW * 64) {
-        const int v = col >> 4, ln = (col & 15) + 16 * (hd >> 2), r = hd & 3;
-        float sum = 0.f;
+    float* rec = a.part + ((static_cast<int64_t>(bh) * a.S + s) * G + hd) * a.prec;
+    float mw[CW], f[CW];
+    float m = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < CW; ++w) sum += mg[((w * NVB + v) * 32 + ln) * 4 + r];
-        rec[hd * a.prec + PHDR + col] = sum;
-      }
-    if (tid < G) {
-      float* r0 = rec + tid * a.prec;
-      r0[0] = good ? s_M[tid] : NAN;
-      r0[1] = s_L[tid];
-      r0[2] = 0.f;
-      r0[3] = 0.f;
+    for (int w = 0; w < CW; ++w) {
+      mw[w] = s_m[w][hd];
+      m = fmaxf(m, mw[w]);
+    }
+    float l = 0.f;
+#pragma unroll
+    for (int w = 0; w < CW; ++w) {
+      f[w] = mw[w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[w] - m);
+      l += s_l[w][hd] * f[w];
+    }
+    const int r = hd & 3;
+    for (int col = lane; col < ncol; col += 64) {
+      const int ln = (col & 15) + 16 * (hd >> 2);
+      const int o = ((col >> 4) * 32 + ln) * 4 + r;
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < CW; ++w) sum += reinterpret_cast<const float*>(ring + w * a.wave_bytes)[o] * f[w];
+      rec[PHDR + col] = sum;
+    }
+    if (lane == 0) {
+      rec[0] = good ? m : NAN;
+      rec[1] = l;
+      rec[2] = 0.f;
+      rec[3] = 0.f;
     }
   }
 }

@@ -75,30 +75,39 @@ __device__ void tile_gemm(const AT* A, const double* __restrict__ R, double* mch
   }
 }
 
-// Token index inside a tile from the bit offset of a value slot in a V field string.
-__device__ inline int v_token(int vpos, int w) {
-  int G, r, m;
-  if (w == 1) {
-    G = 2 * (vpos >> 5) + ((vpos & 7) >> 2);
-    m = (vpos & 31) >> 3;
-    r = vpos & 3;
-  } else if (w == 2) {
-    G = vpos >> 5;
-    m = (vpos & 31) >> 3;
-    r = (vpos & 7) >> 1;
-  } else {
-    G = vpos >> 6;
-    m = (vpos & 31) >> 3;
-    r = 2 * ((vpos >> 5) & 1) + ((vpos & 7) >> 2);
-  }
-  return 16 * G + 4 * r + m;
+// V field strings (2w words per field and tile).  Bit b of the w-bit value of token
+// t = 16G + 4r + m sits at string bit
+//   w=1: 32(G/2) + 8m + 2r + G%2,   w=2: 32G + (8m + 2r + b + G%2) mod 32,
+//   w=4: 64G + 32(r/2) + 8m + 4(r%2) + b,
+// so the attention kernel expands every w<=2 word with one per-lane rotation and shared shifts.
+__device__ inline int v_bit(int t, int w, int b) {
+  const int G = t >> 4, r = (t >> 2) & 3, m = t & 3;
+  if (w == 1) return 32 * (G >> 1) + 8 * m + 2 * r + (G & 1);
+  if (w == 2) return 32 * G + ((8 * m + 2 * r + b + (G & 1)) & 31);
+  return 64 * G + 32 * (r >> 1) + 8 * m + 4 * (r & 1) + b;
 }
 
-__device__ inline int v_pos(int t, int w) {
-  const int G = t >> 4, r = (t >> 2) & 3, m = t & 3;
-  if (w == 1) return 32 * (G >> 1) + 8 * m + 4 * (G & 1) + r;
-  if (w == 2) return 32 * G + 8 * m + 2 * r;
-  return 64 * G + 32 * (r >> 1) + 8 * m + 4 * (r & 1);
+// Token and value bit held by bit q of word j of a field string (the inverse of v_bit).
+__device__ inline int v_token(int j, int q, int w, int* bit) {
+  int G, r, m;
+  if (w == 1) {
+    G = 2 * j + (q & 1);
+    m = q >> 3;
+    r = (q & 7) >> 1;
+    *bit = 0;
+  } else if (w == 2) {
+    const int u = (q - (j & 1)) & 31;
+    G = j;
+    m = u >> 3;
+    r = (u & 7) >> 1;
+    *bit = u & 1;
+  } else {
+    G = j >> 1;
+    m = q >> 3;
+    r = 2 * (j & 1) + ((q & 7) >> 2);
+    *bit = q & 3;
+  }
+  return 16 * G + 4 * r + m;
 }
 
 struct CodecArgs {
@@ -194,9 +203,8 @@ __global__ __launch_bounds__(THREADS) void k_encode(CodecArgs a) {
       const int j = w - c->field_word[f];
       uint32_t word = 0, mask_keep = 0;
       for (int q = 0; q < 32; ++q) {
-        const int pos = 32 * j + q;
-        const int bit = pos % wd;
-        const int t = v_token(pos - bit, wd);
+        int bit;
+        const int t = v_token(j, q, wd, &bit);
         const int64_t at = tok0 + t;
         if (at >= a.tok_off && at < a.tok_off + a.n_tok) {
           word |= static_cast<uint32_t>((cs[t * D + ch] >> (sh + bit)) & 1) << q;
@@ -248,8 +256,11 @@ __global__ __launch_bounds__(THREADS) void k_decode(CodecArgs a) {
           const int f = c->channel_field[3 * i + k];
           if (f < 0) break;
           const int wd = c->field_width[f];
-          const int pos = 32 * c->field_word[f] + v_pos(t, wd);
-          const int v = (in[pos >> 5] >> (pos & 31)) & ((1 << wd) - 1);
+          int v = 0;
+          for (int bb = 0; bb < wd; ++bb) {
+            const int pos = 32 * c->field_word[f] + v_bit(t, wd, bb);
+            v |= static_cast<int>((in[pos >> 5] >> (pos & 31)) & 1u) << bb;
+          }
           code |= v << c->field_shift[f];
         }
       }
