@@ -68,9 +68,9 @@ Plan make_plan(const aatc_cache* c, int n_q, int64_t max_seq) {
     p.gs = ns / 2 < TG ? ns / 2 : TG;
     if (p.gs < 1) p.gs = 1;
   }
-  // a wave's ring area holds its slots, and at the end its merge values (NVB x 32 lanes x float4)
+  // a wave's ring area holds its slots, and at the end its merge values
   p.wave_bytes = (ns > 0 ? ns : 1) * p.slot_bytes;
-  if (p.wave_bytes < p.NVB * 32 * 16) p.wave_bytes = p.NVB * 32 * 16;
+  if (p.wave_bytes < p.NVB * merge_group_bytes(p.NVB)) p.wave_bytes = p.NVB * merge_group_bytes(p.NVB);
   const size_t ring = static_cast<size_t>(CW) * p.wave_bytes + DMA_PAD;
   p.lds = FIXED_LDS + ring;
   if (p.lds + kStaticLds > kLdsLimit) p.fits = false;

@@ -88,6 +88,11 @@ struct AttnArgs {
   int prod;                           // copy waves (0 or NPROD_MAX) issue every tile copy
 };
 
+// Merge area per column group and wave: up to 12 groups every lane's raw int32 sums (both
+// probability limbs, combined when the records are written); more groups fold the limbs in
+// registers first (32 lanes x float4), to fit the ring.
+constexpr int merge_group_bytes(int nvb) { return nvb <= 12 ? 64 * 16 : 32 * 16; }
+
 constexpr int NPROD_MAX = 4;              // copy waves of the producer form (one per SIMD)
 constexpr int SELF = 2;                   // producer form: tiles a compute wave copies itself, first
 
@@ -148,6 +153,25 @@ __device__ inline float wave_sum_x(float x) {
   x += xor_lanes<8>(x, lane);
   x += xor_lanes<16>(x, lane);
   return x + xor_lanes<32>(x, lane);
+}
+
+// Wave max of m and wave sum of x together: each stage's two exchanges are in flight at once.
+__device__ inline void wave_max_sum_x(float& m, float& x) {
+  const int lane = threadIdx.x & 63;
+  m = fmaxf(m, xor_lanes<1>(m, lane));
+  x += xor_lanes<1>(x, lane);
+  m = fmaxf(m, xor_lanes<2>(m, lane));
+  x += xor_lanes<2>(x, lane);
+  const float m4 = xor_lanes<4>(m, lane), x4 = xor_lanes<4>(x, lane);
+  m = fmaxf(m, m4);
+  x += x4;
+  m = fmaxf(m, xor_lanes<8>(m, lane));
+  x += xor_lanes<8>(x, lane);
+  const float m16 = xor_lanes<16>(m, lane), x16 = xor_lanes<16>(x, lane);
+  m = fmaxf(m, m16);
+  x += x16;
+  m = fmaxf(m, xor_lanes<32>(m, lane));
+  x += xor_lanes<32>(x, lane);
 }
 
 // Unnormalised Walsh-Hadamard transform (Sylvester order) of the 128 values x0 = v[lane],
@@ -436,7 +460,42 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
   const int rot = kc->rotation;
   const int nw = ok ? tiles_of(wave) : 0;   // a bad blob streams nothing
 
+  // ---- stream set-up that needs no table: it runs while the tables are in flight
+  // head slots this lane holds after the limb merge: LIMBS=2 pair a {0,4,1,5}[grp] and
+  // pair b {2,6,3,7}[grp]; LIMBS=3 head grp
+  const int ha = LIMBS == 2 ? (grp & 1) * 4 + (grp >> 1) : grp;
+  const int hb = ha + 2;
+  // score lane n16 of token group tau holds token 16*(n16/4) + 4*(n16%4) + tau, so that the
+  // probability bytes it packs are the PV operand's K order (token 16*grp + 4*i + byte)
+  const int tok0 = 16 * (n16 >> 2) + 4 * (n16 & 3);
+  int kofs[NP];
+#pragma unroll
+  for (int u = 0; u < NP; ++u) kofs[u] = tok0 * Bk + plane_base(u, grp, HALF && u == NP - 1);
+  uint8_t* pw = pl + wave * TG * PROW_BYTES;
+  // probability rows (limb l, head slot x) = row 8l + x; dword n16 of a row sits in 16-byte
+  // quad (n16/4) ^ (row%4)
+  auto prow_addr = [&](int row) { return row * 64 + 16 * ((n16 >> 2) ^ (row & 3)) + 4 * (n16 & 3); };
+  const int wa0 = prow_addr(ha), wa1 = prow_addr(8 + ha);
+  const int wb0 = prow_addr(hb), wb1 = prow_addr(8 + hb);
+  const int prd = n16 * 64 + 16 * (grp ^ (n16 & 3));
+  // LDS byte offset (within a tile's V area) of the V word(s) this lane reads for column group v:
+  // a scalar part (the group's class and position) plus one of three lane parts
+  const int L4 = 32 * n16 + 8 * grp, L2 = 16 * n16 + 4 * grp, L1 = 8 * n16 + 4 * (grp >> 1);
+  int voff[NVB];
+#pragma unroll
+  for (int v = 0; v < NVB; ++v) {
+    const int s4 = 512 * v, s2 = 32 * n4 + 256 * (v - T4), s1 = 32 * n4 + 16 * n2 + 128 * (v - T4 - T2);
+    // unused group (v >= NV): a harmless read of the tile's first words
+    voff[v] = v < T4 ? s4 + L4 : (v < T4 + T2 ? s2 + L2 : (v < NV ? s1 + L1 : 0));
+  }
+  const uint32_t rot1 = grp & 1;
 
+  v4i acc[NVB];
+#pragma unroll
+  for (int v = 0; v < NVB; ++v) acc[v] = v4i{0, 0, 0, 0};
+  int ima = INT_MIN, imb = INT_MIN;       // running integer score maxima (INT_MIN: none yet)
+  unsigned la = 0, lb = 0;
+  const v2u16 ones = {1, 1};
 
   int phase = 0;
   if (NPROD == 0) {
@@ -496,22 +555,27 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
       y1 = 0.f;
     }
     float m = 0.f, off = 0.f;
-    float alr[2];
+    float alr[2], dl[2], ol[2];
     int bir[2];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int r = 0; r < 2; ++r) {        // every table read issued before any is used
       const int i = lane + 64 * r;
-      const int bi = t_bits[i];
+      bir[r] = t_bits[i];
+      dl[r] = t_delta[i];
+      ol[r] = t_o[i];
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int bi = bir[r];
       const float v = r ? y1 : y0;
-      const float alpha = bi ? v * t_delta[i] * a.scale2 : 0.f;
+      const float half = static_cast<float>((1 << bi) >> 1);   // 2^(b-1), 0 for b = 0
+      const float alpha = bi ? v * dl[r] * a.scale2 : 0.f;
       alr[r] = alpha;
-      bir[r] = bi;
-      if (bi) m = fmaxf(m, fabsf(alpha) * static_cast<float>(1 << (bi - 1)));
-      const float o = bi ? t_o[i] - t_delta[i] * (static_cast<float>(1 << (bi - 1)) - 0.5f) : t_o[i];
+      m = fmaxf(m, fabsf(alpha) * half);
+      const float o = bi ? ol[r] - dl[r] * (half - 0.5f) : ol[r];
       off += v * o * a.scale2;
     }
-    m = wave_max_x(m);
-    off = wave_sum_x(off);
+    wave_max_sum_x(m, off);
     int e = 0;
     if (m > 0.f) {
       frexpf(m, &e);
@@ -579,42 +643,7 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
 #pragma unroll
       for (int j = 0; j < 4; ++j) wa[u][hh][j] = wa_lds[((u * 2 + hh) * 4 + j) * 64 + lane];
 
-  // head slots this lane holds after the limb merge: LIMBS=2 pair a {0,4,1,5}[grp] and
-  // pair b {2,6,3,7}[grp]; LIMBS=3 head grp
-  const int ha = LIMBS == 2 ? (grp & 1) * 4 + (grp >> 1) : grp;
-  const int hb = ha + 2;
   const float esa = esc[ha], esb = LIMBS == 2 ? esc[hb] : 0.f;
-  // score lane n16 of token group tau holds token 16*(n16/4) + 4*(n16%4) + tau, so that the
-  // probability bytes it packs are the PV operand's K order (token 16*grp + 4*i + byte)
-  const int tok0 = 16 * (n16 >> 2) + 4 * (n16 & 3);
-  int kofs[NP];
-#pragma unroll
-  for (int u = 0; u < NP; ++u) kofs[u] = tok0 * Bk + plane_base(u, grp, HALF && u == NP - 1);
-  uint8_t* pw = pl + wave * TG * PROW_BYTES;
-  // probability rows (limb l, head slot x) = row 8l + x; dword n16 of a row sits in 16-byte
-  // quad (n16/4) ^ (row%4)
-  auto prow_addr = [&](int row) { return row * 64 + 16 * ((n16 >> 2) ^ (row & 3)) + 4 * (n16 & 3); };
-  const int wa0 = prow_addr(ha), wa1 = prow_addr(8 + ha);
-  const int wb0 = prow_addr(hb), wb1 = prow_addr(8 + hb);
-  const int prd = n16 * 64 + 16 * (grp ^ (n16 & 3));
-  // LDS byte offset (within a tile's V area) of the V word(s) this lane reads for column group v:
-  // a scalar part (the group's class and position) plus one of three lane parts
-  const int L4 = 32 * n16 + 8 * grp, L2 = 16 * n16 + 4 * grp, L1 = 8 * n16 + 4 * (grp >> 1);
-  int voff[NVB];
-#pragma unroll
-  for (int v = 0; v < NVB; ++v) {
-    const int s4 = 512 * v, s2 = 32 * n4 + 256 * (v - T4), s1 = 32 * n4 + 16 * n2 + 128 * (v - T4 - T2);
-    // unused group (v >= NV): a harmless read of the tile's first words
-    voff[v] = v < T4 ? s4 + L4 : (v < T4 + T2 ? s2 + L2 : (v < NV ? s1 + L1 : 0));
-  }
-  const uint32_t rot1 = grp & 1;
-
-  v4i acc[NVB];
-#pragma unroll
-  for (int v = 0; v < NVB; ++v) acc[v] = v4i{0, 0, 0, 0};
-  int ima = INT_MIN, imb = INT_MIN;       // running integer score maxima (INT_MIN: none yet)
-  unsigned la = 0, lb = 0;
-  const v2u16 ones = {1, 1};
 
   // ---- 2. stream this wave's tiles, groups of gs
   bool started = false;
@@ -862,7 +891,15 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
   wait_vmcnt(0);                         // this wave's own copies, past the sequence's end too
   if (NPROD > 0 && ncap_w(wave) > SELF)  // and the copy waves' ones into its slots
     poll_ge(&sy.landed[wave], ncap_w(wave), &sy, lane);
-  {
+  constexpr bool RAW = merge_group_bytes(NVB) == 64 * 16;
+  if (RAW) {
+    // every lane's sums as they are: lane group grp, register r holds row 4*grp + r (limb
+    // grp/2, head slot 4*(grp%2) + r)
+    v4i* mgw = reinterpret_cast<v4i*>(ring + wave * a.wave_bytes);
+#pragma unroll
+    for (int v = 0; v < NVB; ++v)
+      if (v < NV) mgw[v * 64 + lane] = acc[v];
+  } else {
     // limb merge: lanes 0..31 (limb 0 rows) take the limb-1 rows of lanes 32..63; lane group
     // grp<2 then holds head slots 4*grp + r
     float4* mgw = reinterpret_cast<float4*>(ring + wave * a.wave_bytes);
@@ -908,10 +945,19 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
     const int r = hd & 3;
     for (int col = lane; col < ncol; col += 64) {
       const int ln = (col & 15) + 16 * (hd >> 2);
-      const int o = ((col >> 4) * 32 + ln) * 4 + r;
       float sum = 0.f;
+      if (RAW) {
+        const int o = ((col >> 4) * 64 + ln) * 4 + r;     // limb 0; limb 1 is 32 lanes on
 #pragma unroll
-      for (int w = 0; w < CW; ++w) sum += reinterpret_cast<const float*>(ring + w * a.wave_bytes)[o] * f[w];
+        for (int w = 0; w < CW; ++w) {
+          const int* mw_ = reinterpret_cast<const int*>(ring + w * a.wave_bytes);
+          sum += fmaf(128.f, static_cast<float>(mw_[o]), static_cast<float>(mw_[o + 128])) * f[w];
+        }
+      } else {
+        const int o = ((col >> 4) * 32 + ln) * 4 + r;
+#pragma unroll
+        for (int w = 0; w < CW; ++w) sum += reinterpret_cast<const float*>(ring + w * a.wave_bytes)[o] * f[w];
+      }
       rec[PHDR + col] = sum;
     }
     if (lane == 0) {
