@@ -121,16 +121,26 @@ __device__ inline unsigned row_sum16_u(unsigned x) {
   return x;
 }
 
-// Value of lane (lane ^ M) for M in {1, 2, 4, 8, 16, 32}, without a round trip through LDS
-// memory (DPP, swizzle and permlane forms).
+// Value of lane (lane ^ M) for M in {1, 2, 4, 8, 16, 32}, on the vector ALU alone (DPP and
+// permlane forms): no LDS round trip, which costs most while tile copies stream into LDS.
 template <int M>
 __device__ inline float xor_lanes(float x, int lane) {
   const int xi = __float_as_int(x);
   if (M == 1) return __int_as_float(__builtin_amdgcn_update_dpp(0, xi, 0xB1, 0xf, 0xf, false));   // quad [1,0,3,2]
   if (M == 2) return __int_as_float(__builtin_amdgcn_update_dpp(0, xi, 0x4E, 0xf, 0xf, false));   // quad [2,3,0,1]
-  if (M == 4) return __int_as_float(__builtin_amdgcn_ds_swizzle(xi, 0x101F));                     // xor 4 in 32
+  if (M == 4) {
+    // lanes 0-3 and 8-11 of each row take lane + 4 (row_shl:4, banks 0 and 2), the others
+    // lane - 4 (row_shr:4, banks 1 and 3)
+    const int t = __builtin_amdgcn_update_dpp(xi, xi, 0x104, 0xf, 0x5, false);
+    return __int_as_float(__builtin_amdgcn_update_dpp(t, xi, 0x114, 0xf, 0xA, false));
+  }
   if (M == 8) return __int_as_float(__builtin_amdgcn_update_dpp(0, xi, 0x128, 0xf, 0xf, false));  // row_ror 8
-  if (M == 16) return __int_as_float(__builtin_amdgcn_ds_swizzle(xi, 0x401F));                    // xor 16 in 32
+  if (M == 16) {
+    // odd rows of the first result hold the even rows' values, even rows of the second the
+    // odd rows' values
+    const auto p = __builtin_amdgcn_permlane16_swap(static_cast<unsigned>(xi), static_cast<unsigned>(xi), false, false);
+    return __int_as_float(static_cast<int>((lane & 16) ? p[0] : p[1]));
+  }
   const auto p = __builtin_amdgcn_permlane32_swap(static_cast<unsigned>(xi), static_cast<unsigned>(xi), false, false);
   return __int_as_float(static_cast<int>(lane < 32 ? p[1] : p[0]));
 }
