@@ -260,9 +260,44 @@ def main():
             ms += [e0.elapsed_time(e1) for e0, e1 in evs]
         return float(np.mean(ms))
 
-    part_ms = time_each(lambda cache, q, ws, out, lse: cache.decode_attn_partial(q, n_tokens, ws))
-    merge_ms = time_each(lambda cache, q, ws, out, lse: cache.decode_attn_merge(q.shape[1], n_tokens, ws, out, lse))
-    log(args, "cache pass %.2f us, merge %.2f us per layer" % (part_ms * 1e3, merge_ms * 1e3))
+    def time_graph(fn):
+        # one launch per layer captured back to back in a graph, replayed between events: the
+        # average launch duration without per-launch event and host overheads
+        if not graph_used:
+            return None
+        g2 = torch.cuda.CUDAGraph()
+        s3 = torch.cuda.Stream()
+        s3.wait_stream(st)
+        with torch.cuda.stream(s3):
+            for lay in layers:
+                fn(*lay)
+        st.wait_stream(s3)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g2):
+            for lay in layers:
+                fn(*lay)
+        g2.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = max(5, args.steps)
+        e0.record(st)
+        for _ in range(reps):
+            g2.replay()
+        e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps * len(layers))
+
+    part_fn = lambda cache, q, ws, out, lse: cache.decode_attn_partial(q, n_tokens, ws)
+    merge_fn = lambda cache, q, ws, out, lse: cache.decode_attn_merge(q.shape[1], n_tokens, ws, out, lse)
+    part_eager_ms = time_each(part_fn)
+    merge_eager_ms = time_each(merge_fn)
+    part_graph_ms = time_graph(part_fn)
+    merge_graph_ms = time_graph(merge_fn)
+    part_ms = part_graph_ms if part_graph_ms is not None else part_eager_ms
+    merge_ms = merge_graph_ms if merge_graph_ms is not None else merge_eager_ms
+    log(args, "cache pass %.2f us, merge %.2f us per layer (%s); eager with an event pair per launch: %.2f, %.2f us" % (
+        part_ms * 1e3, merge_ms * 1e3, "graph of back-to-back launches" if part_graph_ms is not None else "eager",
+        part_eager_ms * 1e3, merge_eager_ms * 1e3))
     achieved = codes_b / (part_ms * 1e-3) / 1e9
     traffic = measured_traffic()
     if args.copy_calib:
@@ -297,6 +332,8 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "k_attn_main (the cache pass, one launch per layer)",
                      "bytes_per_launch": codes_b, "launch_us": round(part_ms * 1e3, 3),
+                     "launch_timing": "graph of back-to-back launches" if part_graph_ms is not None else "eager events",
+                     "launch_us_eager_events": round(part_eager_ms * 1e3, 3),
                      "merge_kernel_us": round(merge_ms * 1e3, 3), "call_us": round(call_ms * 1e3, 3)},
     }
     if not args.no_cpu_baseline:
