@@ -74,11 +74,11 @@ typedef enum { AATC_ROT_KLT = 0, AATC_ROT_WHT = 1, AATC_ROT_IDENTITY = 2 } aatc_
  *  V tiles, field-major.  Channel i's code is split by the binary expansion of b_i into
  *    fields of width 4, 2, 1 (8 = 4+4), low code bits in the widest field.  Fields are
  *    ordered by width descending, channel ascending, shift ascending; field f of width w owns
- *    the 2w words starting at field_word[f].  Token t = 16G + 4r + m (G,r,m in 0..3) stores
- *    its w-bit value LSB-first at this bit offset of the field's 64w-bit string:
- *       w=1: 32*(G/2) + 8m + 4*(G%2) + r
- *       w=2: 32G + 8m + 2r
- *       w=4: 64G + 32*(r/2) + 8m + 4*(r%2)
+ *    the 2w words starting at field_word[f].  Bit b (LSB first) of the w-bit value of token
+ *    t = 16G + 4r + m (G,r,m in 0..3) sits at this bit offset of the field's 64w-bit string:
+ *       w=1: 32*(G/2) + 8m + 2r + (G%2)
+ *       w=2: 32G + ((8m + 2r + b + (G%2)) mod 32)      (odd G: the word rotated left by 1)
+ *       w=4: 64G + 32*(r/2) + 8m + 4*(r%2) + b
  *    (so that four tokens' values land in the four bytes of one word after a shift).
  *
  * Quantizer (mid-rise, per channel): for b_i >= 1,
