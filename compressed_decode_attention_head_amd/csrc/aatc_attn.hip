@@ -47,6 +47,9 @@ Plan make_plan(const aatc_cache* c, int n_q, int64_t max_seq) {
   const int64_t target_waves = 256 * static_cast<int64_t>(CW);
   int64_t tpw = (ntiles * seqs + target_waves - 1) / target_waves;
   if (tpw < 1) tpw = 1;
+  // at most 64 tiles per wave (more workgroups instead): keeps a wave's integer code sums and
+  // their limb combination (128 * high + low) inside int32
+  if (tpw > 64) tpw = 64;
   p.tpw = static_cast<int>(tpw);
   int64_t S = (ntiles + CW * tpw - 1) / (CW * tpw);
   if (S < 1) S = 1;

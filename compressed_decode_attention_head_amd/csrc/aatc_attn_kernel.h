@@ -932,9 +932,50 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
     }
   }
   compute_barrier(&sy, phase, lane);
-  // ---- 4. partial records: [max, sum, 0, 0, column sums]; wave x writes q head x's record,
-  // every wave's values scaled to the workgroup max of that head
-  if (wave < G) {
+  // ---- 4. partial records: [max, sum, 0, 0, column sums], every wave's values scaled to the
+  // workgroup max of their q head
+  if (RAW) {
+    // wave 2j + qd: head quad qd (heads 4qd..4qd+3), column 64j + lane; each of a column's
+    // sums is one 16-byte read per wave and limb (consecutive lanes, consecutive words)
+    const int qd = wave & 1, col = (wave >> 1) * 64 + lane;
+    const bool good = ok && __hip_atomic_load(&sy.broken, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 0;
+    const int ncol = ok ? 16 * NV : 0;     // a bad blob's field count may not fit a record
+    // factors 2^(m_w - M) of the quad's heads: lane k < 32 holds wave k/4, head 4qd + k%4
+    const int kw = (lane >> 2) & 7, kh = 4 * qd + (lane & 3);
+    float mk = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < CW; ++w) mk = fmaxf(mk, s_m[w][kh]);
+    const float own = s_m[kw][kh];
+    const float fk = own == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(own - mk);
+    auto fw = [&](int w, int r) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fk), 4 * w + r)); };
+    float sum[4] = {0.f, 0.f, 0.f, 0.f};
+    const int cc = col < ncol ? col : 0;
+    const int o = (cc >> 4) * 64 + 16 * qd + (cc & 15);     // limb 0; limb 1 is 32 lanes on
+    // (128 * limb 0 + limb 1 stays inside int32 while a wave streams at most 64 tiles)
+#pragma unroll
+    for (int w = 0; w < CW; ++w) {
+      const v4i* mw_ = reinterpret_cast<const v4i*>(ring + w * a.wave_bytes);
+      const v4i x0 = mw_[o], x1 = mw_[o + 32];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sum[r] = fmaf(static_cast<float>(x0[r] * 128 + x1[r]), fw(w, r), sum[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int hd = 4 * qd + r;
+      float* rec = a.part + ((static_cast<int64_t>(bh) * a.S + s) * G + (hd < G ? hd : 0)) * a.prec;
+      if (hd < G && col < ncol) rec[PHDR + col] = sum[r];
+      if (hd < G && wave < 2 && lane == 0) {
+        float l = 0.f;
+#pragma unroll
+        for (int w = 0; w < CW; ++w) l += s_l[w][hd] * fw(w, r);
+        const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mk), r));
+        rec[0] = good ? m : NAN;
+        rec[1] = l;
+        rec[2] = 0.f;
+        rec[3] = 0.f;
+      }
+    }
+  } else if (wave < G) {
     const int hd = wave;
     const bool good = ok && __hip_atomic_load(&sy.broken, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 0;
     const int ncol = ok ? 16 * NV : 0;     // a bad blob's field count may not fit a record
