@@ -37,6 +37,7 @@ MAX_BITS = 8
 
 __all__ = [
     "TILE", "MAX_BITS", "calib_stats", "rotation_klt", "rotation_wht", "rotation_identity",
+    "query_channel_weights",
     "bits_budget", "waterfill_bits", "waterfill_theta", "uniform_quantizer_mse",
     "uniform_quantizer_mse_deriv", "optimal_step", "quantizer_tables", "calibrate",
     "encode_codes", "dequantize", "reconstruct", "v_fields", "pack_k", "unpack_k",
@@ -112,11 +113,12 @@ def bits_budget(bits_per_elem, d):
     return int(math.floor(bits_per_elem * d + 0.5))
 
 
-def waterfill_bits(sigma2, total_bits, max_bits=MAX_BITS):
+def waterfill_bits(sigma2, total_bits, max_bits=MAX_BITS, weight=None):
     """Integer reverse water-filling: bits b_i in [0, max_bits] with sum b_i = B that
-    minimise sum_i sigma_i^2 4^(-b_i) (high-resolution distortion model).
+    minimise sum_i w_i sigma_i^2 4^(-b_i) (high-resolution distortion model; w_i = 1 unless
+    per-channel weights are given, as for the attention-aware allocation).
 
-    Greedy on the exact candidates v_ik = sigma_i^2 4^-k (k < max_bits): the B largest
+    Greedy on the exact candidates v_ik = (w_i sigma_i^2) 4^-k (k < max_bits): the B largest
     under the order (value desc, channel asc, bit asc) are granted.  The gains of one
     channel fall geometrically, so the greedy choice is optimal.
     """
@@ -124,12 +126,31 @@ def waterfill_bits(sigma2, total_bits, max_bits=MAX_BITS):
     d = s2.shape[0]
     if total_bits < 0 or total_bits > d * max_bits:
         raise ValueError("budget out of range")
+    if weight is not None:
+        w = np.asarray(weight, dtype=np.float64)
+        if w.shape != s2.shape or not np.all(np.isfinite(w)) or np.any(w < 0):
+            raise ValueError("channel weights must be finite and non-negative, one per channel")
+        s2 = w * s2
     cands = [(-math.ldexp(float(s2[i]), -2 * k), i, k) for i in range(d) for k in range(max_bits)]
     cands.sort()
     bits = np.zeros(d, dtype=np.int64)
     for _, i, _k in cands[:total_bits]:
         bits[i] += 1
     return bits
+
+
+def query_channel_weights(r, q_cal):
+    """Attention-aware key weights w_i = E[(R q)_i^2] over calibration queries q.
+
+    [AATC abstract: under a white-noise quantization model the expected attention-aware
+    distortion splits into key and value terms that factor over tokens and channels.]  With a
+    zero-mean key error e independent of q and of its other channels, the score error
+    q.(k - k_hat) = (R q).(R e) has E[(q.(k - k_hat))^2] = sum_i E[(R q)_i^2] E[(R e)_i^2]:
+    the key channels' distortions add with these weights.  The value path has no such factor
+    (uniform weights).
+    """
+    qr = np.asarray(q_cal, dtype=np.float64) @ np.asarray(r, dtype=np.float64).T
+    return (qr * qr).mean(axis=0)
 
 
 def waterfill_theta(sigma2, total_bits):
@@ -233,17 +254,22 @@ def quantizer_tables(r, mu, sigma2, bits):
     return o, delta, inv
 
 
-def calibrate(x_cal, rotation="klt", bits_per_elem=2.0, max_bits=MAX_BITS, total_bits=None):
-    """Full calibration of one (head, tensor): statistics, rotation, bits, quantizer tables."""
+def calibrate(x_cal, rotation="klt", bits_per_elem=2.0, max_bits=MAX_BITS, total_bits=None, q_cal=None):
+    """Full calibration of one (head, tensor): statistics, rotation, bits, quantizer tables.
+
+    q_cal (keys only): calibration queries of the head's q heads; the bits then minimise the
+    attention-aware distortion sum_i E[(R q)_i^2] sigma_i^2 4^-b_i instead of the cache MSE.
+    """
     mu, c = calib_stats(x_cal)
     rot = {"klt": rotation_klt, "wht": rotation_wht, "identity": rotation_identity}[rotation]
     r, s2 = rot(c)
     d = c.shape[0]
     b_total = bits_budget(bits_per_elem, d) if total_bits is None else int(total_bits)
-    bits = waterfill_bits(s2, b_total, max_bits)
+    weight = None if q_cal is None else query_channel_weights(r, q_cal)
+    bits = waterfill_bits(s2, b_total, max_bits, weight)
     o, delta, inv = quantizer_tables(r, mu, s2, bits)
     return {"R": r, "mu": mu, "C": c, "sigma2": s2, "bits": bits, "B": b_total,
-            "o": o, "delta": delta, "inv_delta": inv, "rotation": rotation}
+            "o": o, "delta": delta, "inv_delta": inv, "rotation": rotation, "weight": weight}
 
 
 # ----------------------------------------------------------------------------------

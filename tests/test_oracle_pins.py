@@ -174,6 +174,89 @@ def test_waterfill_rejects_bad_budget():
         O.waterfill_bits(np.ones(4), -1)
 
 
+# ---------------------------------------------------------------- attention-aware allocation
+def test_weighted_waterfill_bruteforce_d4():
+    """sum_i w_i sigma_i^2 4^-b_i at the allocation equals the exhaustive minimum."""
+    rng = np.random.default_rng(11)
+    for trial in range(6):
+        s2 = rng.lognormal(0, 2, 4)
+        w = rng.lognormal(0, 1.5, 4)
+        if trial == 5:
+            w = np.array([1.0, 0.0, 2.0, 0.5])          # a zero-weight channel
+        for budget in range(0, 33, 3):
+            best = min(sum(w[i] * s2[i] * 4.0 ** (-a[i]) for i in range(4))
+                       for a in itertools.product(range(9), repeat=4) if sum(a) == budget)
+            got = O.waterfill_bits(s2, budget, weight=w)
+            assert got.sum() == budget and got.max() <= 8
+            dist = sum(w[i] * s2[i] * 4.0 ** (-got[i]) for i in range(4))
+            assert dist <= best * (1 + 1e-14) + 1e-300
+
+
+def test_weighted_waterfill_special_cases():
+    s2 = synth.spectrum(128)
+    for budget in (170, 256, 353):
+        # unit weights are the unweighted allocation; power-of-two scaling is exact
+        assert np.array_equal(O.waterfill_bits(s2, budget, weight=np.ones(128)), O.waterfill_bits(s2, budget))
+        w = np.random.default_rng(budget).lognormal(0, 1, 128)
+        assert np.array_equal(O.waterfill_bits(s2, budget, weight=w), O.waterfill_bits(s2, budget, weight=8.0 * w))
+    # all weight on two channels: they take max_bits first
+    w = np.zeros(128)
+    w[[5, 77]] = 1.0
+    b = O.waterfill_bits(s2, 16, weight=w)
+    assert b[5] == 8 and b[77] == 8 and b.sum() == 16
+    with pytest.raises(ValueError):
+        O.waterfill_bits(s2, 16, weight=-w)
+
+
+def test_query_weights_sum_and_identity():
+    """sum_i E[(R q)_i^2] = E|q|^2 for orthogonal R; with R = I they are E[q_i^2]."""
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((500, 128)) * np.linspace(0.1, 3.0, 128)
+    x = synth.draw(2, 0, 0, synth.K, "calib", 1024, dtype="bf16")
+    _, c = O.calib_stats(x)
+    for rot in (O.rotation_klt, O.rotation_wht):
+        r, _ = rot(c)
+        w = O.query_channel_weights(r, q)
+        assert abs(w.sum() - (q * q).sum(axis=1).mean()) < 1e-9 * w.sum()
+    assert np.allclose(O.query_channel_weights(np.eye(128), q), (q * q).mean(axis=0), rtol=1e-14, atol=0)
+
+
+def test_score_error_decomposes_over_key_channels():
+    """AATC abstract: under white quantization noise the expected attention-aware (score)
+    distortion is additive over channels.  Monte Carlo: with independent zero-mean errors e_i of
+    variance D_i in the rotated basis, E[(q.(R^T e))^2] = sum_i E[(R q)_i^2] D_i."""
+    rng = np.random.default_rng(9)
+    r, _ = O.rotation_wht(np.eye(128))
+    q = rng.standard_normal((4000, 128)) * np.linspace(0.2, 2.0, 128)
+    dvar = rng.uniform(0.01, 1.0, 128)
+    e = rng.uniform(-1.0, 1.0, (4000, 128)) * np.sqrt(3.0 * dvar)    # variance dvar, zero mean
+    err = np.einsum("ni,ni->n", q, e @ r)                             # q . (R^T e)
+    want = (O.query_channel_weights(r, q) * dvar).sum()
+    assert abs((err * err).mean() - want) < 0.05 * want
+
+
+def test_attention_aware_bits_lower_score_error():
+    """Allocation weighted by the queries' rotated second moments gives a smaller score error
+    than the cache-MSE allocation at the same budget, on keys and queries whose energy sits in
+    different rotated channels (the situation the criterion targets)."""
+    x = synth.draw(1, 0, 0, synth.K, "calib", 1024, dtype="f32")
+    ctx = synth.draw(1, 0, 0, synth.K, "context", 2048, dtype="f32")
+    plain = O.calibrate(x, "klt", 2.0)
+    rng = np.random.default_rng(2)
+    # queries concentrated on the low-variance key directions
+    qw = np.concatenate([np.zeros(96), np.ones(32)]) * 3.0 + 0.05
+    q_cal = (rng.standard_normal((512, 128)) * qw) @ plain["R"]
+    q_test = (rng.standard_normal((512, 128)) * qw) @ plain["R"]
+    aware = O.calibrate(x, "klt", 2.0, q_cal=q_cal)
+    assert aware["bits"].sum() == plain["bits"].sum()
+    errs = []
+    for art in (plain, aware):
+        kh = O.reconstruct(O.encode_codes(ctx, art), art)
+        d = (q_test @ (ctx - kh).T)
+        errs.append(float((d * d).mean()))
+    assert errs[1] < 0.8 * errs[0], errs
+
+
 # ---------------------------------------------------------------- quantizer step g(b)
 def test_g1_closed_form():
     assert abs(O.optimal_step(1) - 2 * math.sqrt(2 / math.pi)) < 1e-14
