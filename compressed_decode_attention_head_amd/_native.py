@@ -34,7 +34,8 @@ CALIB_DTYPE = np.dtype([
 
 class CalibParams(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int32), ("rotation", ctypes.c_int32), ("bits_per_elem", ctypes.c_double),
-                ("max_bits", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("max_bits", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("channel_weight", ctypes.POINTER(ctypes.c_double))]
 
 
 class Cache(ctypes.Structure):
@@ -82,6 +83,8 @@ def lib():
     L.aatc_packed_bytes.argtypes = [i32, i64]
     L.aatc_calibrate.restype = ctypes.c_int
     L.aatc_calibrate.argtypes = [ctypes.POINTER(CalibParams), vp, ctypes.c_int, i64, i64, vp, sz]
+    L.aatc_query_channel_weights.restype = ctypes.c_int
+    L.aatc_query_channel_weights.argtypes = [vp, sz, vp, ctypes.c_int, i64, i64, vp]
     L.aatc_calib_validate.restype = ctypes.c_int
     L.aatc_calib_validate.argtypes = [vp, sz]
     L.aatc_calib_v_tiles.restype = i32
@@ -120,7 +123,8 @@ def check(status):
 
 
 EXPORTS = ["aatc_status_string", "aatc_last_error", "aatc_calib_bytes", "aatc_bits_budget",
-           "aatc_packed_bytes", "aatc_calibrate", "aatc_calib_validate", "aatc_calib_v_tiles",
+           "aatc_packed_bytes", "aatc_calibrate", "aatc_query_channel_weights", "aatc_calib_validate",
+           "aatc_calib_v_tiles",
            "aatc_encode", "aatc_decode", "aatc_decode_attn_workspace_bytes", "aatc_decode_attn",
            "aatc_decode_attn_partial", "aatc_decode_attn_merge", "aatc_tier_distortions",
            "aatc_token_tiers", "aatc_decode_attn_segments_workspace_bytes", "aatc_decode_attn_segments"]

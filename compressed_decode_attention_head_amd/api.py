@@ -25,18 +25,39 @@ def _np_dtype_code(x):
     raise TypeError("calibration data must be float32, float64 or bf16 bits (uint16)")
 
 
-def calibrate(x, rotation="klt", bits_per_elem=2.0, max_bits=8, d=128):
-    """aatc_calibrate on host rows x [M, d]; returns the artefact blob (uint8 array)."""
+def calibrate(x, rotation="klt", bits_per_elem=2.0, max_bits=8, d=128, channel_weight=None):
+    """aatc_calibrate on host rows x [M, d]; returns the artefact blob (uint8 array).
+    channel_weight: optional d weights of the rotated channels (query_channel_weights)."""
     L = N.lib()
     x = np.ascontiguousarray(x)
     if x.ndim != 2:
         raise ValueError("x must be [n_calib, d]")
-    p = N.CalibParams(d, N.ROTATION[rotation], float(bits_per_elem), int(max_bits), 0)
+    wptr = None
+    if channel_weight is not None:
+        w = np.ascontiguousarray(channel_weight, dtype=np.float64)
+        if w.shape != (d,):
+            raise ValueError("channel_weight must have d entries")
+        wptr = w.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+    p = N.CalibParams(d, N.ROTATION[rotation], float(bits_per_elem), int(max_bits), 0, wptr)
     nbytes = L.aatc_calib_bytes(d) or N.CALIB_DTYPE.itemsize
     out = np.zeros(nbytes, dtype=np.uint8)
     N.check(L.aatc_calibrate(ctypes.byref(p), x.ctypes.data, _np_dtype_code(x), x.shape[0], x.shape[1],
                              out.ctypes.data, out.nbytes))
     return out
+
+
+def query_channel_weights(blob, q):
+    """aatc_query_channel_weights: attention-aware key weights E[(R q)_i^2] over the host query
+    rows q [n, d] (float32, float64 or bf16 bits) for a key blob's rotation."""
+    L = N.lib()
+    q = np.ascontiguousarray(q)
+    if q.ndim != 2:
+        raise ValueError("q must be [n, d]")
+    blob = np.ascontiguousarray(blob, dtype=np.uint8)
+    w = np.zeros(q.shape[1], dtype=np.float64)
+    N.check(L.aatc_query_channel_weights(blob.ctypes.data, blob.nbytes, q.ctypes.data, _np_dtype_code(q), q.shape[0],
+                                         q.shape[1], w.ctypes.data))
+    return w
 
 
 def calib_view(blob):

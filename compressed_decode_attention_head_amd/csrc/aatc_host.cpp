@@ -313,6 +313,12 @@ aatc_status aatc_calibrate(const aatc_calib_params* p, const void* x, aatc_dtype
   if (stride < AATC_D) return fail(AATC_ERR_INVALID_ARGUMENT, "row_stride < d");
   if (out_bytes < sizeof(aatc_calib)) return fail(AATC_ERR_BUFFER_TOO_SMALL, "calib buffer %zu < %zu",
                                                   out_bytes, sizeof(aatc_calib));
+  if (p->channel_weight)
+    for (int i = 0; i < AATC_D; ++i) {
+      const double w = p->channel_weight[i];
+      if (!std::isfinite(w)) return fail(AATC_ERR_NUMERICAL, "channel_weight[%d] is not finite", i);
+      if (w < 0.0) return fail(AATC_ERR_INVALID_ARGUMENT, "channel_weight[%d] = %g < 0", i, w);
+    }
   std::vector<double> xs;
   bool ok;
   switch (dt) {
@@ -371,7 +377,14 @@ aatc_status aatc_calibrate(const aatc_calib_params* p, const void* x, aatc_dtype
       c->sigma2[i] = s;
     }
   }
-  waterfill_impl(c->sigma2, d, total, p->max_bits, c->bits);
+  if (p->channel_weight) {
+    // attention-aware: the candidates are w_i sigma_i^2 4^-k
+    double ws2[AATC_D];
+    for (int i = 0; i < d; ++i) ws2[i] = p->channel_weight[i] * c->sigma2[i];
+    waterfill_impl(ws2, d, total, p->max_bits, c->bits);
+  } else {
+    waterfill_impl(c->sigma2, d, total, p->max_bits, c->bits);
+  }
 
   double smax = 0.0;
   for (int i = 0; i < d; ++i) smax = std::max(smax, std::sqrt(std::max(c->sigma2[i], 0.0)));
@@ -413,6 +426,37 @@ aatc_status aatc_calib_validate(const void* blob, size_t bytes) {
   std::memcpy(&tmp, c, sizeof(tmp));
   build_layout(&tmp);
   if (std::memcmp(&tmp, c, sizeof(tmp)) != 0) return fail(AATC_ERR_BAD_ARTEFACT, "layout tables");
+  return AATC_OK;
+}
+
+aatc_status aatc_query_channel_weights(const void* blob, size_t bytes, const void* q, aatc_dtype dt, int64_t n,
+                                       int64_t stride, double* w) {
+  const aatc_status st = aatc_calib_validate(blob, bytes);   // clears the error, or sets it
+  if (st != AATC_OK) return st;
+  if (!q || !w) return fail(AATC_ERR_INVALID_ARGUMENT, "null pointer");
+  if (n < 1) return fail(AATC_ERR_INVALID_ARGUMENT, "n=%lld < 1", (long long)n);
+  if (stride < AATC_D) return fail(AATC_ERR_INVALID_ARGUMENT, "row_stride < d");
+  std::vector<double> qs;
+  bool ok;
+  switch (dt) {
+    case AATC_F32: ok = read_rows<float>(q, n, stride, qs); break;
+    case AATC_BF16: ok = read_rows<bf16_tag>(q, n, stride, qs); break;
+    case AATC_F64: ok = read_rows<double>(q, n, stride, qs); break;
+    default: return fail(AATC_ERR_UNSUPPORTED, "dtype %d", (int)dt);
+  }
+  if (!ok) return fail(AATC_ERR_NUMERICAL, "non-finite query value");
+  const auto* c = static_cast<const aatc_calib*>(blob);
+  const int d = AATC_D;
+  std::vector<double> acc(d, 0.0);
+  for (int64_t r = 0; r < n; ++r) {
+    const double* qr = qs.data() + r * d;
+    for (int i = 0; i < d; ++i) {
+      double y = 0.0;
+      for (int k = 0; k < d; ++k) y += c->R[i * d + k] * qr[k];
+      acc[i] += y * y;
+    }
+  }
+  for (int i = 0; i < d; ++i) w[i] = acc[i] / static_cast<double>(n);
   return AATC_OK;
 }
 

@@ -125,6 +125,9 @@ typedef struct {
   double bits_per_elem;    /* average budget b; B = floor(b*d + 1/2) */
   int32_t max_bits;        /* per-channel cap, 8 (1..8) */
   int32_t reserved;
+  const double* channel_weight;  /* NULL: the cache-MSE allocation; else d weights w_i >= 0 of
+                                    the rotated channels (attention-aware keys: see
+                                    aatc_query_channel_weights) */
 } aatc_calib_params;
 
 /* Readable bytes a codes buffer must have past its last sequence's words: decode attention
@@ -171,18 +174,36 @@ size_t aatc_packed_bytes(int32_t total_bits, int64_t n_tokens);
  *   the covariance, descending eigenvalues, largest-magnitude entry of each row positive;
  *   WHT: Sylvester Hadamard / sqrt(d); IDENTITY); integer reverse water-filling of
  *   B = floor(b*d+1/2) bits over the rotated variances (the B largest candidates
- *   sigma_i^2 4^-k, k < max_bits, ordered by value desc, channel asc, bit asc); quantizer
+ *   w_i sigma_i^2 4^-k, k < max_bits, ordered by value desc, channel asc, bit asc; w_i = 1
+ *   unless params->channel_weight is given, which then makes the allocation minimise
+ *   sum_i w_i sigma_i^2 4^-b_i, the weighted, attention-aware distortion); quantizer
  *   step delta_i = sigma_i g(b_i) where g(b) minimises the MSE of the 2^b-level mid-rise
  *   uniform quantizer on N(0,1); offset o = R mu; packing tables.
  *   Writes one aatc_calib into calib_host (calib_bytes >= aatc_calib_bytes(d)).
  *   Errors: d != 128 -> UNSUPPORTED; B outside [0, 8d] or max_bits outside 1..8 -> BUDGET;
- *   n_calib < 2, null pointers, row_stride < d -> INVALID_ARGUMENT; a non-finite value ->
- *   NUMERICAL; small blob -> BUFFER_TOO_SMALL.  Zero-variance channels get 0 bits unless the
- *   budget exceeds 8 x (positive-variance channels).
+ *   n_calib < 2, null pointers, row_stride < d, a negative channel weight ->
+ *   INVALID_ARGUMENT; a non-finite value or weight -> NUMERICAL; small blob ->
+ *   BUFFER_TOO_SMALL.  Zero-variance (or zero-weight) channels get 0 bits unless the budget
+ *   exceeds 8 x (the other channels).
  */
 aatc_status aatc_calibrate(const aatc_calib_params* params, const void* x_host, aatc_dtype dtype,
                            int64_t n_calib, int64_t row_stride, void* calib_host,
                            size_t calib_bytes);
+
+/*
+ * aatc_query_channel_weights -- host, synchronous, fp64.  [AATC abstract: under a white-noise
+ * quantization model the expected attention-aware distortion decomposes into key and value
+ * terms that factor across tokens and channels]  For a key blob's rotation R and n calibration
+ * queries q (row r at q_host + r*row_stride elements, dtype F32/BF16/F64: the query heads
+ * that share the KV head), w_out[i] = (1/n) sum_r ((R q_r)_i)^2.  The expected squared score
+ * error of a zero-mean white key error is sum_i w_i E[e_i^2], so passing w as channel_weight
+ * to aatc_calibrate (on the same keys, which gives the same R) allocates the key bits to
+ * minimise the score error instead of the cache MSE.
+ *   Errors: the blob's aatc_calib_validate status; n < 1, null pointers, row_stride < d ->
+ *   INVALID_ARGUMENT; a non-finite query -> NUMERICAL.
+ */
+aatc_status aatc_query_channel_weights(const void* calib_host, size_t calib_bytes, const void* q_host,
+                                       aatc_dtype dtype, int64_t n, int64_t row_stride, double* w_out);
 
 /* Checks magic, version, d, checksum and internal consistency of a host blob. */
 aatc_status aatc_calib_validate(const void* calib_host, size_t calib_bytes);

@@ -145,6 +145,29 @@ def test_gqa_groups(group):
     assert np.abs(out.cpu().numpy() - ref).max() <= ATOL_ATTN
 
 
+def test_attention_aware_key_allocation():
+    """Key bits allocated by the calibration queries' rotated second moments (library: query
+    weights, then a weighted calibration): same bits as the oracle's, attention within the bar."""
+    torch = _torch()
+    case = Case(cfg=2, n_kv=2, group=4, n_tokens=300, rotation="klt", bpe_k=2.76, aware=True)
+    plain = Case(cfg=2, n_kv=2, group=4, n_tokens=300, rotation="klt", bpe_k=2.76)
+    from compressed_decode_attention_head_amd import api
+    for h, blob in enumerate(case.blobs(synth.K)):
+        assert np.array_equal(api.calib_view(blob)["bits"].astype(np.int64), case.art[synth.K][h]["bits"])
+    assert any(not np.array_equal(case.art[synth.K][h]["bits"], plain.art[synth.K][h]["bits"]) for h in range(2))
+    cache = case.make_cache()
+    for t in (synth.K, synth.V):
+        cache.encode(t, case.torch_x(t))
+    _check_codes(case, cache, synth.K)
+    out, lse = cache.decode_attn(torch.from_numpy(case.q.astype(np.float32)).cuda(), case.n)
+    torch.cuda.synchronize()
+    ref, lref = case.oracle_attention()
+    err = np.abs(out.cpu().numpy() - ref).max()
+    print("attention-aware keys: attn max abs err", err, flush=True)
+    assert err <= ATOL_ATTN
+    assert np.abs(lse.cpu().numpy() - lref).max() <= 5e-3
+
+
 def test_zero_bit_tensors():
     """All K channels at 0 bits: uniform softmax; all V channels at 0 bits: output = mu_V."""
     torch = _torch()

@@ -73,6 +73,57 @@ def test_calibrate_matches_oracle(cfg, rot, bpe, tensor):
     assert np.array_equal(c["R32"], R.astype(np.float32).ravel())
 
 
+@pytest.mark.parametrize("cfg,rot,bpe", [(2, "klt", 2.76), (4, "wht", 1.33)])
+def test_attention_aware_calibration_matches_oracle(cfg, rot, bpe):
+    """Query weights and the weighted allocation: library (C++) against the oracle."""
+    x = _cal(cfg, 1, synth.K, marginal="t3" if cfg == 4 else "gauss")
+    rng = np.random.default_rng(cfg)
+    ref0 = O.calibrate(x, rot, bpe)
+    # calibration queries: a few dominant rotated directions plus a floor
+    qw = np.where(np.arange(128) % 7 == 0, 4.0, 0.3)
+    q = (rng.standard_normal((256, 128)) * qw) @ ref0["R"]
+    ref = O.calibrate(x, rot, bpe, q_cal=q)
+    blob0 = api.calibrate(_bits16(x), rot, bpe)
+    w = api.query_channel_weights(blob0, q)
+    assert np.abs(w - ref["weight"]).max() < 1e-10 * ref["weight"].max()
+    blob = api.calibrate(_bits16(x), rot, bpe, channel_weight=w)
+    api.validate(blob)
+    c = api.calib_view(blob)
+    assert np.array_equal(c["bits"].astype(np.int64), ref["bits"])
+    assert int(c["total_bits"]) == ref["B"]
+    assert not np.array_equal(ref["bits"], ref0["bits"])      # the weights moved bits
+    # same statistics and rotation as the unweighted blob; only the allocation differs
+    assert np.array_equal(c["R"], api.calib_view(blob0)["R"])
+
+
+def test_attention_aware_errors(L):
+    x = _cal(2, 0, synth.K)
+    blob = api.calibrate(_bits16(x), "klt", 2.0)
+    w = np.ones(128)
+    w[3] = -1.0
+    with pytest.raises(N.AatcError) as e:
+        api.calibrate(_bits16(x), "klt", 2.0, channel_weight=w)
+    assert e.value.status == 1
+    w[3] = float("nan")
+    with pytest.raises(N.AatcError) as e:
+        api.calibrate(_bits16(x), "klt", 2.0, channel_weight=w)
+    assert e.value.status == 4
+    q = np.ones((4, 128), dtype=np.float32)
+    q[2, 5] = np.inf
+    with pytest.raises(N.AatcError) as e:
+        api.query_channel_weights(blob, q)
+    assert e.value.status == 4
+    bad = blob.copy()
+    bad[200] ^= 1
+    with pytest.raises(N.AatcError) as e:
+        api.query_channel_weights(bad, np.ones((4, 128), dtype=np.float32))
+    assert e.value.status == 5
+    wout = np.zeros(128)
+    qq = np.ones((4, 128), dtype=np.float32)
+    assert L.aatc_query_channel_weights(blob.ctypes.data, blob.nbytes, qq.ctypes.data, 0, 0, 128, wout.ctypes.data) == 1
+    assert L.aatc_query_channel_weights(blob.ctypes.data, blob.nbytes, qq.ctypes.data, 0, 4, 100, wout.ctypes.data) == 1
+
+
 def test_quantizer_step_matches_oracle_all_widths():
     """sigma=1 channels at every width: delta/sigma must equal the oracle's g(b) to 1e-13."""
     rng = np.random.default_rng(0)
