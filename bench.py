@@ -35,6 +35,7 @@ def parse():
     p.add_argument("--tokens", type=int, default=0, help="override context length")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true")
+    p.add_argument("--no-dense", action="store_true", help="skip the dense bf16 comparator")
     p.add_argument("--quiet", action="store_true")
     p.add_argument("--copy-calib", action="store_true",
                    help="also run one plain 256 MiB device copy (scales HBM counters of a profiler run)")
@@ -143,6 +144,64 @@ def cpu_baseline(cfg, n_tokens):
             "sample": "1 KV head x %d tokens x %d q heads (decode attention = reconstruct + fp64 softmax "
                       "attention), %d reps; encode %.0f tokens/s (K+V, 1 head)" % (sample, cfg.group, reps,
                                                                                  sample / enc)}
+
+
+def dense_comparator(args, cfg, n_tokens, qs, dev, st, ms_compressed_step):
+    """The same decode step over an uncompressed bf16 cache (aatc_decode_attn_dense): one call per
+    layer, same queries, timed the same way (graph replay, inputs resident in HBM)."""
+    import torch
+    import synth
+    from compressed_decode_attention_head_amd import api
+    lays = []
+    for l in range(len(qs)):
+        k = torch.empty((cfg.batch, cfg.n_kv_heads, n_tokens, 128), dtype=torch.bfloat16, device=dev)
+        v = torch.empty_like(k)
+        for b in range(cfg.batch):
+            for h in range(cfg.n_kv_heads):
+                k[b, h] = synth.draw_device(cfg.idx, l, h, synth.K, n_tokens, dtype="bf16", marginal=cfg.marginal,
+                                            device=dev, extra=b)
+                v[b, h] = synth.draw_device(cfg.idx, l, h, synth.V, n_tokens, dtype="bf16", marginal=cfg.marginal,
+                                            device=dev, extra=b)
+        lays.append((k, v))
+    ws = torch.empty(api.decode_attn_dense_workspace_bytes(cfg.batch, cfg.n_kv_heads, cfg.n_q_heads, n_tokens),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty_like(qs[0])
+    lse = torch.empty((cfg.batch, cfg.n_q_heads), dtype=torch.float32, device=dev)
+
+    def dstep():
+        for (k, v), q in zip(lays, qs):
+            api.decode_attn_dense(k, v, q, n_tokens, workspace=ws, out=out, lse=lse)
+
+    runner = dstep
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        s2 = torch.cuda.Stream()
+        s2.wait_stream(st)
+        with torch.cuda.stream(s2):
+            dstep()
+        st.wait_stream(s2)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            dstep()
+        runner = g.replay
+    for _ in range(args.warmup):
+        runner()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(args.steps):
+        runner()
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    layer_bytes = 2 * cfg.batch * cfg.n_kv_heads * n_tokens * 128 * 2
+    gbs = layer_bytes * len(qs) / (ms * 1e-3) / 1e9
+    del lays
+    return {"kernels": "k_dense_attn + k_merge_states (aatc_decode_attn_dense, one call per layer)",
+            "bytes_per_layer": layer_bytes, "ms_per_step": round(ms, 4),
+            "us_per_layer": round(ms * 1e3 / len(qs), 3), "gbs": round(gbs, 1),
+            "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "speedup_compressed_vs_dense": round(ms / ms_compressed_step, 3)}
 
 
 def main():
@@ -336,6 +395,11 @@ def main():
                      "launch_us_eager_events": round(part_eager_ms * 1e3, 3),
                      "merge_kernel_us": round(merge_ms * 1e3, 3), "call_us": round(call_ms * 1e3, 3)},
     }
+    if not args.no_dense:
+        log(args, "timing the dense bf16 comparator")
+        res["dense_bf16"] = dense_comparator(args, cfg, n_tokens, [lay[1] for lay in layers], dev, st, ms_step)
+        log(args, "dense bf16: %.2f us per layer, %.0f GB/s; compressed step is %.2fx faster" % (
+            res["dense_bf16"]["us_per_layer"], res["dense_bf16"]["gbs"], res["dense_bf16"]["speedup_compressed_vs_dense"]))
     if not args.no_cpu_baseline:
         log(args, "timing the oracle on the host")
         res["cpu_baseline"] = cpu_baseline(cfg, n_tokens)

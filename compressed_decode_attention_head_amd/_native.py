@@ -110,6 +110,10 @@ def lib():
     L.aatc_decode_attn_segments.restype = ctypes.c_int
     L.aatc_decode_attn_segments.argtypes = [ctypes.POINTER(Segment), i32, i32, i32, vp, i32, ctypes.c_float, vp,
                                             vp, vp, sz, vp]
+    L.aatc_decode_attn_dense_workspace_bytes.restype = sz
+    L.aatc_decode_attn_dense_workspace_bytes.argtypes = [i32, i32, i32, i64]
+    L.aatc_decode_attn_dense.restype = ctypes.c_int
+    L.aatc_decode_attn_dense.argtypes = [vp, vp, i32, i32, i64, vp, i64, vp, i32, ctypes.c_float, vp, vp, vp, sz, vp]
     if L.aatc_calib_bytes(D) != CALIB_DTYPE.itemsize:
         raise RuntimeError("aatc_calib layout mismatch: library %d bytes, binding %d bytes"
                            % (L.aatc_calib_bytes(D), CALIB_DTYPE.itemsize))
@@ -127,4 +131,5 @@ EXPORTS = ["aatc_status_string", "aatc_last_error", "aatc_calib_bytes", "aatc_bi
            "aatc_calib_v_tiles",
            "aatc_encode", "aatc_decode", "aatc_decode_attn_workspace_bytes", "aatc_decode_attn",
            "aatc_decode_attn_partial", "aatc_decode_attn_merge", "aatc_tier_distortions",
-           "aatc_token_tiers", "aatc_decode_attn_segments_workspace_bytes", "aatc_decode_attn_segments"]
+           "aatc_token_tiers", "aatc_decode_attn_segments_workspace_bytes", "aatc_decode_attn_segments",
+           "aatc_decode_attn_dense_workspace_bytes", "aatc_decode_attn_dense"]

@@ -146,6 +146,46 @@ def decode_attn_segments(segments, q, batch, n_kv_heads, scale=0.0, workspace=No
     return out, lse
 
 
+def decode_attn_dense_workspace_bytes(batch, n_kv_heads, n_q_heads, max_seq_len):
+    """aatc_decode_attn_dense_workspace_bytes."""
+    need = N.lib().aatc_decode_attn_dense_workspace_bytes(batch, n_kv_heads, n_q_heads, max_seq_len)
+    if need == 0:
+        raise ValueError("invalid shape: " + N.lib().aatc_last_error().decode())
+    return need
+
+
+def decode_attn_dense(k, v, q, max_seq_len, seq_lens=None, scale=0.0, workspace=None, out=None, lse=None,
+                      stream=None):
+    """aatc_decode_attn_dense: softmax attention over an uncompressed bf16 cache.
+    k, v: contiguous bf16 [batch, n_kv, capacity, 128]; q: contiguous fp32 [batch, n_q, 128];
+    seq_lens: contiguous int32 [batch, n_kv] or None (max_seq_len everywhere)."""
+    import torch
+    if (k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16 or k.shape != v.shape or k.dim() != 4
+            or not k.is_contiguous() or not v.is_contiguous()):
+        raise ValueError("k and v must be contiguous bf16 [batch, n_kv_heads, capacity, 128] tensors")
+    batch, n_kv, cap = k.shape[0], k.shape[1], k.shape[2]
+    if q.dtype != torch.float32 or not q.is_contiguous() or q.dim() != 3 or q.shape[0] != batch:
+        raise ValueError("q must be a contiguous fp32 [batch, n_q_heads, 128] tensor")
+    sl = 0
+    if seq_lens is not None:
+        if seq_lens.dtype != torch.int32 or seq_lens.numel() != batch * n_kv or not seq_lens.is_contiguous():
+            raise ValueError("seq_lens must be a contiguous int32 [batch, n_kv_heads] tensor")
+        sl = seq_lens.data_ptr()
+    n_q = q.shape[1]
+    L = N.lib()
+    if workspace is None:
+        workspace = torch.empty(decode_attn_dense_workspace_bytes(batch, n_kv, n_q, max_seq_len), dtype=torch.uint8,
+                                device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((batch, n_q), dtype=torch.float32, device=q.device)
+    N.check(L.aatc_decode_attn_dense(k.data_ptr(), v.data_ptr(), batch, n_kv, cap, sl or None, int(max_seq_len),
+                                     q.data_ptr(), n_q, float(scale), out.data_ptr(), lse.data_ptr(),
+                                     workspace.data_ptr(), workspace.numel(), _stream_ptr(stream)))
+    return out, lse
+
+
 def _stream_ptr(stream):
     import torch
     s = stream if stream is not None else torch.cuda.current_stream()

@@ -2,6 +2,7 @@
 // The kernel (and the method it implements) is described in aatc_attn_kernel.h.
 #define AATC_ATTN_COMBINE_TU
 #include "aatc_attn_kernel.h"
+#include "aatc_dense_kernel.h"
 #include "aatc_seg_kernel.h"
 
 #include <cstdio>
@@ -254,13 +255,16 @@ struct SegPlan {
   size_t states_off, lse_off, attn_off, attn_bytes, total;
 };
 
-int64_t raw_chunks(const aatc_segment& sg) { return (sg.max_seq_len + aatc_seg::RCH - 1) / aatc_seg::RCH; }
+int64_t raw_chunks(const aatc_segment& sg) {
+  return (sg.max_seq_len + aatc_dense::CHUNK - 1) / aatc_dense::CHUNK;
+}
 
 aatc_status seg_plan(const aatc_segment* segs, int32_t n_segs, int32_t batch, int32_t n_kv, int32_t n_q,
                      SegPlan* sp) {
   if (!segs || n_segs < 1) return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "no segments");
   if (batch < 1 || n_kv < 1 || n_q < 1 || n_q % n_kv) return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "shape");
   if (n_q / n_kv > AATC_MAX_GROUP) return aatc::fail(AATC_ERR_UNSUPPORTED, "GQA group %d > 8", n_q / n_kv);
+  if (batch > 65535 || n_kv > 65535) return aatc::fail(AATC_ERR_UNSUPPORTED, "batch or n_kv_heads > 65535");
   int64_t states = 0;
   size_t attn = 0;
   for (int s = 0; s < n_segs; ++s) {
@@ -310,6 +314,7 @@ aatc_status aatc_decode_attn_segments(const aatc_segment* segs, int32_t n_segs, 
   aatc::clear_error();
   if (!q || !out || !ws) return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "null pointer");
   if (reinterpret_cast<uintptr_t>(ws) & 255) return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "workspace not 256-byte aligned");
+  if (reinterpret_cast<uintptr_t>(q) & 15) return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "q not 16-byte aligned");
   SegPlan sp;
   aatc_status r = seg_plan(segs, n_segs, batch, n_kv, n_q, &sp);
   if (r != AATC_OK) return r;
@@ -347,7 +352,7 @@ aatc_status aatc_decode_attn_segments(const aatc_segment* segs, int32_t n_segs, 
       if (r != AATC_OK) return r;
       state += 1;
     } else {
-      aatc_seg::RawArgs ra;
+      aatc_dense::DenseArgs ra;
       ra.k = static_cast<const uint16_t*>(sg.k_raw);
       ra.v = static_cast<const uint16_t*>(sg.v_raw);
       ra.cap = sg.raw_capacity;
@@ -363,18 +368,49 @@ aatc_status aatc_decode_attn_segments(const aatc_segment* segs, int32_t n_segs, 
       ra.state0 = state;
       ra.bq = bq;
       const int64_t nc = raw_chunks(sg) > 0 ? raw_chunks(sg) : 1;
-      hipLaunchKernelGGL(aatc_seg::k_raw_attn, dim3(static_cast<unsigned>(nc), n_kv, batch), dim3(aatc_seg::RCH), 0,
-                         st, ra);
+      hipLaunchKernelGGL(aatc_dense::k_dense_attn, dim3(static_cast<unsigned>(nc), n_kv, batch),
+                         dim3(aatc_dense::NW * 64), 0, st, ra);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return aatc::fail(AATC_ERR_HIP, "raw segment launch: %s", hipGetErrorString(e));
       state += static_cast<int>(nc);
     }
   }
-  hipLaunchKernelGGL(aatc_seg::k_merge_states, dim3(static_cast<unsigned>(bq)), dim3(AATC_D), 0, st, out_states,
+  hipLaunchKernelGGL(aatc_seg::k_merge_states, dim3(static_cast<unsigned>(bq)), dim3(aatc_seg::MW * 64), 0, st, out_states,
                      lse_states, sp.n_states, bq, out, lse);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return aatc::fail(AATC_ERR_HIP, "segment merge launch: %s", hipGetErrorString(e));
   return AATC_OK;
+}
+
+// ---- dense bf16 decode attention: one raw segment ------------------------------------------
+static aatc_segment dense_segment(const void* k, const void* v, int64_t capacity, const int32_t* seq_lens,
+                                  int64_t max_seq) {
+  aatc_segment sg;
+  sg.cache = nullptr;
+  sg.k_raw = k;
+  sg.v_raw = v;
+  sg.raw_capacity = capacity;
+  sg.seq_lens_dev = seq_lens;
+  sg.max_seq_len = max_seq;
+  return sg;
+}
+
+size_t aatc_decode_attn_dense_workspace_bytes(int32_t batch, int32_t n_kv_heads, int32_t n_q_heads,
+                                              int64_t max_seq_len) {
+  static const char dummy[16] __attribute__((aligned(16))) = {0};
+  const aatc_segment sg = dense_segment(dummy, dummy, max_seq_len, nullptr, max_seq_len);
+  return aatc_decode_attn_segments_workspace_bytes(&sg, 1, batch, n_kv_heads, n_q_heads);
+}
+
+aatc_status aatc_decode_attn_dense(const void* k_dev, const void* v_dev, int32_t batch, int32_t n_kv_heads,
+                                   int64_t capacity_tokens, const int32_t* seq_lens_dev, int64_t max_seq_len,
+                                   const float* q_dev, int32_t n_q_heads, float softmax_scale, float* out_dev,
+                                   float* lse_dev, void* workspace_dev, size_t workspace_bytes, void* stream) {
+  aatc::clear_error();
+  if (capacity_tokens < 0) return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "capacity_tokens < 0");
+  const aatc_segment sg = dense_segment(k_dev, v_dev, capacity_tokens, seq_lens_dev, max_seq_len);
+  return aatc_decode_attn_segments(&sg, 1, batch, n_kv_heads, q_dev, n_q_heads, softmax_scale, out_dev, lse_dev,
+                                   workspace_dev, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -344,15 +344,45 @@ size_t aatc_decode_attn_segments_workspace_bytes(const aatc_segment* segs, int32
  * union of the segments' tokens (tier-0 tokens are in no segment).  [SPHERICAL KV page,
  * RDKV abstract; softmax is order-invariant, so the union is the log-sum-exp merge of
  * per-segment states]  Coded segments run the cache pass and merge of aatc_decode_attn with
- * per-(b,h) lengths; raw segments run a dense bf16 pass in 256-token chunks; one final
- * kernel merges all states.  q, out, lse, scale and GQA mapping as aatc_decode_attn.
+ * per-(b,h) lengths; raw segments run the dense bf16 pass of aatc_decode_attn_dense in
+ * 2048-token chunks; one final kernel merges all states.  q (16-byte aligned), out, lse, scale
+ * and GQA mapping as aatc_decode_attn.
  *   Errors: as aatc_decode_attn, per segment; caches whose batch or n_kv_heads differ from the
- *   call -> INVALID_ARGUMENT; workspace too small -> BUFFER_TOO_SMALL.
+ *   call, misaligned q -> INVALID_ARGUMENT; batch or n_kv_heads > 65535 -> UNSUPPORTED;
+ *   workspace too small -> BUFFER_TOO_SMALL.
  */
 aatc_status aatc_decode_attn_segments(const aatc_segment* segs, int32_t n_segs, int32_t batch,
                                       int32_t n_kv_heads, const float* q_dev, int32_t n_q_heads,
                                       float softmax_scale, float* out_dev, float* lse_dev,
                                       void* workspace_dev, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of aatc_decode_attn_dense (0 for invalid arguments). */
+size_t aatc_decode_attn_dense_workspace_bytes(int32_t batch, int32_t n_kv_heads, int32_t n_q_heads,
+                                              int64_t max_seq_len);
+
+/*
+ * aatc_decode_attn_dense -- device, async; one decode step of plain softmax attention over an
+ * uncompressed bf16 cache, the full-precision baseline that the compressed cache is compared
+ * with.  [SPHERICAL KV page, RDKV abstract: speedup over the full cache, which is re-read from
+ * HBM at every decode step]
+ *   k_dev, v_dev: bf16 [batch][n_kv_heads][capacity_tokens][128], 16-byte aligned, read only.
+ *   seq_lens_dev: int32 [batch][n_kv_heads] visible tokens per (b,h) (each <= max_seq_len), or
+ *   NULL for max_seq_len; max_seq_len <= capacity_tokens.  q_dev: fp32 [batch][n_q_heads][128],
+ *   16-byte aligned; q head g reads KV head g / (n_q_heads/n_kv_heads), group 1..8.
+ *   out_dev = sum_t softmax_t(scale q.k_t) v_t, fp32 [batch][n_q_heads][128]; lse_dev
+ *   (nullable) the natural-log sum of exp of the scores; 0 visible tokens -> out 0, lse -inf.
+ *   Scores use q as a bf16 high part plus a bf16 low part and the probabilities likewise, with
+ *   fp32 accumulation; K and V enter exactly.
+ *   workspace_dev: >= aatc_decode_attn_dense_workspace_bytes(...) bytes, 256-byte aligned, no
+ *   initialisation needed; one state per 2048-token chunk and q head.
+ *   Errors: as aatc_decode_attn_segments with one raw segment.
+ */
+aatc_status aatc_decode_attn_dense(const void* k_dev, const void* v_dev, int32_t batch,
+                                   int32_t n_kv_heads, int64_t capacity_tokens,
+                                   const int32_t* seq_lens_dev, int64_t max_seq_len,
+                                   const float* q_dev, int32_t n_q_heads, float softmax_scale,
+                                   float* out_dev, float* lse_dev, void* workspace_dev,
+                                   size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -266,3 +266,38 @@ def test_token_tiers_errors(L):
     with pytest.raises(N.AatcError) as e:
         api.tier_distortions([np.full(128, np.nan)])
     assert e.value.name == "AATC_ERR_NUMERICAL"
+
+
+def test_dense_workspace_bytes(L):
+    """One state per 2048-token chunk and q head: [states][batch*n_q][128] fp32 outputs, then
+    [states][batch*n_q] fp32 lse, each padded to 256 bytes."""
+    def al(x):
+        return -(-x // 256) * 256
+    for b, n_kv, n_q, n in ((1, 4, 28, 131072), (2, 2, 8, 3000), (1, 1, 1, 0), (3, 1, 8, 2048)):
+        states, bq = max(1, -(-n // 2048)), b * n_q
+        assert L.aatc_decode_attn_dense_workspace_bytes(b, n_kv, n_q, n) == al(states * bq * 512) + al(states * bq * 4)
+    assert L.aatc_decode_attn_dense_workspace_bytes(1, 4, 30, 100) == 0      # 30 q heads over 4 KV heads
+    assert L.aatc_decode_attn_dense_workspace_bytes(1, 1, 9, 100) == 0       # group of 9
+    assert L.aatc_decode_attn_dense_workspace_bytes(1, 1, 1, -1) == 0
+
+
+def test_dense_argument_errors(L):
+    """Every case fails host-side validation before a launch; the fake device addresses are
+    never dereferenced."""
+    ok = 1 << 20
+
+    def call(k=ok, v=ok, batch=1, n_kv=1, cap=64, max_seq=64, q=ok, n_q=1, out=ok, ws=ok, ws_bytes=1 << 20):
+        return N.STATUS[L.aatc_decode_attn_dense(k, v, batch, n_kv, cap, None, max_seq, q, n_q, 0.0, out, None, ws,
+                                                 ws_bytes, None)]
+    assert call(k=None) == "AATC_ERR_INVALID_ARGUMENT"
+    assert call(out=None) == "AATC_ERR_INVALID_ARGUMENT"
+    assert call(v=ok + 8) == "AATC_ERR_INVALID_ARGUMENT"
+    assert call(q=ok + 4) == "AATC_ERR_INVALID_ARGUMENT"
+    assert call(ws=ok + 16) == "AATC_ERR_INVALID_ARGUMENT"
+    assert call(max_seq=65) == "AATC_ERR_INVALID_ARGUMENT"
+    assert call(cap=-1, max_seq=0) == "AATC_ERR_INVALID_ARGUMENT"
+    assert call(batch=0) == "AATC_ERR_INVALID_ARGUMENT"
+    assert call(n_q=9) == "AATC_ERR_UNSUPPORTED"
+    assert call(n_kv=2, n_q=3) == "AATC_ERR_INVALID_ARGUMENT"
+    assert call(batch=70000) == "AATC_ERR_UNSUPPORTED"
+    assert call(ws_bytes=16) == "AATC_ERR_BUFFER_TOO_SMALL"
