@@ -12,7 +12,9 @@ Sources (cited by page title and section; no line numbers):
             precision down to zero bits per token or channel by reverse water-filling,
             once after prefill; the cache is re-read from HBM at every decode step.
   [NOVA]    same page, third abstract (NOVA-KV): decode is bandwidth-bound; a fixed
-            per-token bit count / fixed-width layout is required.
+            per-token bit count / fixed-width layout is required; the key transform that
+            is optimal for the attention-aware distortion is not orthogonal, and under it
+            that distortion becomes plain MSE of the transformed coefficients.
   [ABL]     "Ablation, Statistical Inference, and Validation for KV-Cache Compression",
             first abstract: Walsh-Hadamard transform followed by a scalar MSE quantizer.
   [OCTOPUS] same page, third abstract: keys are reconstructed on the fly inside the
@@ -37,7 +39,7 @@ MAX_BITS = 8
 
 __all__ = [
     "TILE", "MAX_BITS", "calib_stats", "rotation_klt", "rotation_wht", "rotation_identity",
-    "query_channel_weights",
+    "query_channel_weights", "query_moment", "transform_nova", "NOVA_EIG_FLOOR",
     "bits_budget", "waterfill_bits", "waterfill_theta", "uniform_quantizer_mse",
     "uniform_quantizer_mse_deriv", "optimal_step", "quantizer_tables", "calibrate",
     "encode_codes", "dequantize", "reconstruct", "v_fields", "pack_k", "unpack_k",
@@ -103,6 +105,41 @@ def rotation_identity(c):
     """No rotation (per-channel quantization baseline)."""
     c = np.asarray(c, dtype=np.float64)
     return np.eye(c.shape[0]), np.diag(c).copy()
+
+
+# Non-orthogonal key transform  [NOVA third abstract: closed-form key transform from
+# calibration statistics, not orthogonal, with a generalized Parseval relation]
+#
+# The attention-aware error of a key error e is (q.e)^2, of mean e^T S e with S = E[q q^T].
+# A transform y = T x turns it into plain MSE of y exactly when T^-T S T^-1 = I, i.e.
+# T = U S^(1/2) with U orthogonal; U is then the KLT of the whitened keys S^(1/2) x, so the
+# coefficients are decorrelated with variances the eigenvalues of S^(1/2) C S^(1/2).  Scores
+# use q.x = (P q).y with P = T^-T = U S^(-1/2); reconstruction is x = T^-1 y = P^T y.
+# ----------------------------------------------------------------------------------
+NOVA_EIG_FLOOR = 1e-6   # eigenvalues of S below this fraction of the largest are raised to it
+
+
+def query_moment(q):
+    """Second moment S = E[q q^T] (not centred) of query rows q [n, d]."""
+    q = np.asarray(q, dtype=np.float64)
+    return (q.T @ q) / q.shape[0]
+
+
+def transform_nova(c, s):
+    """Key transform from the key covariance c and the query second moment s.
+
+    Returns (T, P, sigma2): coefficients y = T x, the query transform P = T^-T (rows of P
+    and of T share the KLT sign rule of U), and sigma2_i = var(y_i).
+    """
+    w, v = np.linalg.eigh(np.asarray(s, dtype=np.float64))
+    if not w.max() > 0:
+        raise ValueError("query second moment has no positive eigenvalue")
+    w = np.maximum(w, NOVA_EIG_FLOOR * w.max())
+    s_half = (v * np.sqrt(w)) @ v.T
+    s_ihalf = (v / np.sqrt(w)) @ v.T
+    m = s_half @ np.asarray(c, dtype=np.float64) @ s_half
+    u, lam = rotation_klt(0.5 * (m + m.T))
+    return u @ s_half, u @ s_ihalf, lam
 
 
 # ----------------------------------------------------------------------------------
@@ -257,18 +294,31 @@ def quantizer_tables(r, mu, sigma2, bits):
 def calibrate(x_cal, rotation="klt", bits_per_elem=2.0, max_bits=MAX_BITS, total_bits=None, q_cal=None):
     """Full calibration of one (head, tensor): statistics, rotation, bits, quantizer tables.
 
-    q_cal (keys only): calibration queries of the head's q heads; the bits then minimise the
-    attention-aware distortion sum_i E[(R q)_i^2] sigma_i^2 4^-b_i instead of the cache MSE.
+    q_cal (keys only): calibration queries of the head's q heads.  With an orthogonal
+    rotation the bits then minimise the attention-aware distortion
+    sum_i E[(R q)_i^2] sigma_i^2 4^-b_i instead of the cache MSE.  rotation="nova" needs q_cal:
+    the transform is transform_nova(C, query_moment(q_cal)), under which that distortion is
+    the plain MSE of the coefficients, so the bits use unit weights.
+
+    The artefact's "E" is the encoder matrix (y = E x) and "R" the matrix of the query
+    (q~ = R q) and of reconstruction (x = R^T y); they are the same matrix except for "nova".
     """
     mu, c = calib_stats(x_cal)
-    rot = {"klt": rotation_klt, "wht": rotation_wht, "identity": rotation_identity}[rotation]
-    r, s2 = rot(c)
     d = c.shape[0]
     b_total = bits_budget(bits_per_elem, d) if total_bits is None else int(total_bits)
-    weight = None if q_cal is None else query_channel_weights(r, q_cal)
+    if rotation == "nova":
+        if q_cal is None:
+            raise ValueError("the nova transform needs calibration queries")
+        e, r, s2 = transform_nova(c, query_moment(q_cal))
+        weight = None
+    else:
+        rot = {"klt": rotation_klt, "wht": rotation_wht, "identity": rotation_identity}[rotation]
+        r, s2 = rot(c)
+        e = r
+        weight = None if q_cal is None else query_channel_weights(r, q_cal)
     bits = waterfill_bits(s2, b_total, max_bits, weight)
-    o, delta, inv = quantizer_tables(r, mu, s2, bits)
-    return {"R": r, "mu": mu, "C": c, "sigma2": s2, "bits": bits, "B": b_total,
+    o, delta, inv = quantizer_tables(e, mu, s2, bits)
+    return {"R": r, "E": e, "mu": mu, "C": c, "sigma2": s2, "bits": bits, "B": b_total,
             "o": o, "delta": delta, "inv_delta": inv, "rotation": rotation, "weight": weight}
 
 
@@ -278,14 +328,15 @@ def calibrate(x_cal, rotation="klt", bits_per_elem=2.0, max_bits=MAX_BITS, total
 def encode_codes(x, art):
     """Codes c[N, d] (0 for 0-bit channels) of rows x [N, d].
 
-    y = R x in fp64; u = (y - o) * (1/Delta) + 2^(b-1) as separately rounded fp64 operations;
+    y = E x in fp64 (E = R for orthogonal rotations); u = (y - o) * (1/Delta) + 2^(b-1) as
+    separately rounded fp64 operations;
     c = clamp(floor(u), 0, 2^b - 1) (half-open bins: a value on an edge goes up);
     NaN -> 0, +-Inf -> the clamp ends.
     """
     x = np.asarray(x, dtype=np.float64)
     bits = np.asarray(art["bits"])
     with np.errstate(invalid="ignore", over="ignore"):
-        y = x @ np.asarray(art["R"]).T
+        y = x @ np.asarray(art.get("E", art["R"])).T
         half = np.where(bits > 0, np.ldexp(1.0, np.maximum(bits, 1) - 1), 0.0)
         u = (y - art["o"][None, :]) * art["inv_delta"][None, :]
         u = u + half[None, :]
@@ -307,7 +358,7 @@ def dequantize(codes, art):
 
 
 def reconstruct(codes, art):
-    """x_hat = R^T y_hat."""
+    """x_hat = R^T y_hat (for "nova", R^T = E^-1)."""
     return dequantize(codes, art) @ np.asarray(art["R"])
 
 

@@ -81,7 +81,7 @@ def excused_mismatch_report(x, art, got, want):
     bad = np.argwhere(got != want)
     if bad.size == 0:
         return 0, 0
-    y = np.asarray(x, dtype=np.float64) @ art["R"].T
+    y = np.asarray(x, dtype=np.float64) @ art.get("E", art["R"]).T
     unexcused = 0
     for t, i in bad:
         b = int(art["bits"][i])

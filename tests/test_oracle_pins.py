@@ -257,6 +257,105 @@ def test_attention_aware_bits_lower_score_error():
     assert errs[1] < 0.8 * errs[0], errs
 
 
+# ---------------------------------------------------------------- non-orthogonal key transform
+def _aniso_queries(rng, n, basis, scales):
+    return (rng.standard_normal((n, 128)) * scales) @ basis
+
+
+def test_nova_identity_moment_is_klt():
+    """With E[q q^T] = I the attention-aware distortion is the cache MSE, and the transform is the
+    KLT itself; with a I it is sqrt(a) times the KLT (same bits)."""
+    x = synth.draw(2, 0, 0, synth.K, "calib", 1024, dtype="bf16")
+    klt = O.calibrate(x, "klt", 2.76)
+    for a in (1.0, 4.0):
+        q = np.vstack([math.sqrt(256.0 * a) * np.eye(128), np.zeros((128, 128))])   # moment a I, exactly
+        assert np.array_equal(O.query_moment(q), a * np.eye(128))
+        nova = O.calibrate(x, "nova", 2.76, q_cal=q)
+        sa = math.sqrt(a)
+        assert np.abs(nova["E"] - sa * klt["R"]).max() < 1e-9 * sa
+        assert np.abs(nova["R"] - klt["R"] / sa).max() < 1e-9
+        assert np.allclose(nova["sigma2"], a * klt["sigma2"], rtol=1e-9, atol=1e-12 * a * klt["sigma2"].max())
+        assert np.array_equal(nova["bits"], klt["bits"])
+
+
+def test_nova_generalized_parseval():
+    """NOVA abstract: under the key transform the attention-aware distortion is MSE in the
+    transform domain: the mean over the calibration queries of (q . T^-1 e)^2 is |e|^2 for every
+    coefficient error e (exactly, for the sample second moment)."""
+    rng = np.random.default_rng(21)
+    x = synth.draw(4, 0, 1, synth.K, "calib", 1024, dtype="bf16")
+    _, c = O.calib_stats(x)
+    q = _aniso_queries(rng, 3000, synth.haar_orthogonal(rng, 128), np.geomspace(0.05, 3.0, 128))
+    t, p, _ = O.transform_nova(c, O.query_moment(q))
+    for _ in range(5):
+        e = rng.standard_normal(128) * rng.uniform(0.1, 2.0, 128)
+        err = q @ (p.T @ e)                              # q . (T^-1 e), with T^-1 = P^T
+        assert abs((err * err).mean() - e @ e) < 1e-9 * (e @ e)
+
+
+def test_nova_transform_properties():
+    """P = T^-T; T C T^T is diagonal with the returned variances in descending order; scores
+    in the coefficient domain equal the original scores; the artefact's offset is T mu."""
+    rng = np.random.default_rng(22)
+    x = synth.draw(1, 0, 0, synth.K, "calib", 1024, dtype="f32")
+    mu, c = O.calib_stats(x)
+    q = _aniso_queries(rng, 2000, synth.haar_orthogonal(rng, 128), np.linspace(0.1, 3.0, 128))
+    art = O.calibrate(x, "nova", 2.0, q_cal=q)
+    t, p, s2 = art["E"], art["R"], art["sigma2"]
+    assert np.abs(p @ t.T - np.eye(128)).max() < 1e-9
+    cov_y = t @ c @ t.T
+    off = cov_y - np.diag(np.diag(cov_y))
+    assert np.abs(off).max() < 1e-9 * s2.max()
+    assert np.allclose(np.diag(cov_y), s2, rtol=1e-8, atol=1e-12 * s2.max())
+    assert np.all(np.diff(s2) <= 0)
+    keys = synth.draw(1, 0, 0, synth.K, "context", 300, dtype="f32")
+    for g in range(7):
+        s_orig = keys @ q[g]
+        s_coef = O.rotated_scores(q[g], p, keys @ t.T)
+        assert np.abs(s_orig - s_coef).max() < 1e-9 * np.abs(s_orig).max()
+    assert np.allclose(art["o"], t @ mu, rtol=0, atol=1e-12 * np.abs(t @ mu).max())
+    # reconstruction is P^T y_hat = T^-1 y_hat
+    codes = O.encode_codes(keys, art)
+    assert np.allclose(O.reconstruct(codes, art), np.linalg.solve(t, O.dequantize(codes, art).T).T, atol=1e-9)
+
+
+def test_nova_rank_deficient_queries_floor():
+    """Queries confined to a 16-dimensional subspace: eigenvalues of E[q q^T] are raised to
+    1e-6 of the largest, so the transform stays finite and invertible."""
+    rng = np.random.default_rng(23)
+    x = synth.draw(2, 0, 0, synth.K, "calib", 1024, dtype="bf16")
+    _, c = O.calib_stats(x)
+    basis = synth.haar_orthogonal(rng, 128)[:16]
+    q = rng.standard_normal((500, 16)) @ basis
+    t, p, s2 = O.transform_nova(c, O.query_moment(q))
+    assert np.all(np.isfinite(t)) and np.all(np.isfinite(p)) and np.all(s2 >= 0)
+    assert np.abs(p @ t.T - np.eye(128)).max() < 1e-6
+    with pytest.raises(ValueError):
+        O.transform_nova(c, np.zeros((128, 128)))
+
+
+def test_nova_lower_score_error_than_orthogonal():
+    """Queries whose anisotropy is not aligned with the keys' principal axes: the non-orthogonal
+    transform gives a much smaller score error than the KLT, with or without query-weighted bits,
+    at the same budget (calibration and test queries are separate draws)."""
+    x = synth.draw(4, 0, 0, synth.K, "calib", 1024, dtype="f32")
+    ctx = synth.draw(4, 0, 0, synth.K, "context", 2048, dtype="f32")
+    rng = np.random.default_rng(5)
+    basis = synth.haar_orthogonal(rng, 128)
+    for scales in (np.linspace(0.1, 3.0, 128), np.geomspace(0.05, 3.0, 128)):
+        q_cal = _aniso_queries(rng, 8192, basis, scales)
+        q_test = _aniso_queries(rng, 512, basis, scales)
+        arts = [O.calibrate(x, "klt", 2.0), O.calibrate(x, "klt", 2.0, q_cal=q_cal),
+                O.calibrate(x, "nova", 2.0, q_cal=q_cal)]
+        assert len({int(a["bits"].sum()) for a in arts}) == 1
+        errs = []
+        for art in arts:
+            kh = O.reconstruct(O.encode_codes(ctx, art), art)
+            d = q_test @ (ctx - kh).T
+            errs.append(float((d * d).mean()))
+        assert errs[2] < 0.7 * min(errs[:2]), errs
+
+
 # ---------------------------------------------------------------- quantizer step g(b)
 def test_g1_closed_form():
     assert abs(O.optimal_step(1) - 2 * math.sqrt(2 / math.pi)) < 1e-14
