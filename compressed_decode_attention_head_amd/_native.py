@@ -12,7 +12,7 @@ STATUS = {0: "AATC_OK", 1: "AATC_ERR_INVALID_ARGUMENT", 2: "AATC_ERR_UNSUPPORTED
           4: "AATC_ERR_NUMERICAL", 5: "AATC_ERR_BAD_ARTEFACT", 6: "AATC_ERR_BUFFER_TOO_SMALL",
           7: "AATC_ERR_HIP"}
 DTYPE = {"f32": 0, "bf16": 1, "f64": 2}
-ROTATION = {"klt": 0, "wht": 1, "identity": 2}
+ROTATION = {"klt": 0, "wht": 1, "identity": 2, "nova": 3}
 D = 128
 MAX_FIELDS = 384
 
@@ -28,14 +28,15 @@ CALIB_DTYPE = np.dtype([
     ("bits", "u1", (D,)), ("plane_channel", "u1", (D * 8,)), ("plane_bit", "u1", (D * 8,)),
     ("field_channel", "<u2", (MAX_FIELDS,)), ("field_shift", "u1", (MAX_FIELDS,)),
     ("field_width", "u1", (MAX_FIELDS,)), ("field_word", "<u2", (MAX_FIELDS,)),
-    ("channel_field", "<i2", (D * 3,)), ("reserved", "u1", (64,)),
+    ("channel_field", "<i2", (D * 3,)), ("E", "<f8", (D * D,)), ("reserved", "u1", (64,)),
 ], align=True)
 
 
 class CalibParams(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int32), ("rotation", ctypes.c_int32), ("bits_per_elem", ctypes.c_double),
                 ("max_bits", ctypes.c_int32), ("reserved", ctypes.c_int32),
-                ("channel_weight", ctypes.POINTER(ctypes.c_double))]
+                ("channel_weight", ctypes.POINTER(ctypes.c_double)),
+                ("query_moment", ctypes.POINTER(ctypes.c_double))]
 
 
 class Cache(ctypes.Structure):
@@ -110,6 +111,8 @@ def lib():
     L.aatc_decode_attn_segments.restype = ctypes.c_int
     L.aatc_decode_attn_segments.argtypes = [ctypes.POINTER(Segment), i32, i32, i32, vp, i32, ctypes.c_float, vp,
                                             vp, vp, sz, vp]
+    L.aatc_query_moment.restype = ctypes.c_int
+    L.aatc_query_moment.argtypes = [vp, ctypes.c_int, i64, i64, vp]
     L.aatc_decode_attn_dense_workspace_bytes.restype = sz
     L.aatc_decode_attn_dense_workspace_bytes.argtypes = [i32, i32, i32, i64]
     L.aatc_decode_attn_dense.restype = ctypes.c_int
@@ -132,4 +135,4 @@ EXPORTS = ["aatc_status_string", "aatc_last_error", "aatc_calib_bytes", "aatc_bi
            "aatc_encode", "aatc_decode", "aatc_decode_attn_workspace_bytes", "aatc_decode_attn",
            "aatc_decode_attn_partial", "aatc_decode_attn_merge", "aatc_tier_distortions",
            "aatc_token_tiers", "aatc_decode_attn_segments_workspace_bytes", "aatc_decode_attn_segments",
-           "aatc_decode_attn_dense_workspace_bytes", "aatc_decode_attn_dense"]
+           "aatc_decode_attn_dense_workspace_bytes", "aatc_decode_attn_dense", "aatc_query_moment"]

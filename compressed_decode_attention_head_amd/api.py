@@ -25,9 +25,10 @@ def _np_dtype_code(x):
     raise TypeError("calibration data must be float32, float64 or bf16 bits (uint16)")
 
 
-def calibrate(x, rotation="klt", bits_per_elem=2.0, max_bits=8, d=128, channel_weight=None):
+def calibrate(x, rotation="klt", bits_per_elem=2.0, max_bits=8, d=128, channel_weight=None, query_moment=None):
     """aatc_calibrate on host rows x [M, d]; returns the artefact blob (uint8 array).
-    channel_weight: optional d weights of the rotated channels (query_channel_weights)."""
+    channel_weight: optional d weights of the rotated channels (query_channel_weights).
+    query_moment: the d x d E[q q^T] of calibration queries (query_moment), for rotation "nova"."""
     L = N.lib()
     x = np.ascontiguousarray(x)
     if x.ndim != 2:
@@ -38,7 +39,13 @@ def calibrate(x, rotation="klt", bits_per_elem=2.0, max_bits=8, d=128, channel_w
         if w.shape != (d,):
             raise ValueError("channel_weight must have d entries")
         wptr = w.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
-    p = N.CalibParams(d, N.ROTATION[rotation], float(bits_per_elem), int(max_bits), 0, wptr)
+    mptr = None
+    if query_moment is not None:
+        mom = np.ascontiguousarray(query_moment, dtype=np.float64)
+        if mom.shape != (d, d):
+            raise ValueError("query_moment must be d x d")
+        mptr = mom.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+    p = N.CalibParams(d, N.ROTATION[rotation], float(bits_per_elem), int(max_bits), 0, wptr, mptr)
     nbytes = L.aatc_calib_bytes(d) or N.CALIB_DTYPE.itemsize
     out = np.zeros(nbytes, dtype=np.uint8)
     N.check(L.aatc_calibrate(ctypes.byref(p), x.ctypes.data, _np_dtype_code(x), x.shape[0], x.shape[1],
@@ -58,6 +65,18 @@ def query_channel_weights(blob, q):
     N.check(L.aatc_query_channel_weights(blob.ctypes.data, blob.nbytes, q.ctypes.data, _np_dtype_code(q), q.shape[0],
                                          q.shape[1], w.ctypes.data))
     return w
+
+
+def query_moment(q):
+    """aatc_query_moment: E[q q^T] (d x d, fp64) over the host query rows q [n, d] (float32,
+    float64 or bf16 bits), the input of the "nova" key transform."""
+    L = N.lib()
+    q = np.ascontiguousarray(q)
+    if q.ndim != 2:
+        raise ValueError("q must be [n, d]")
+    m = np.zeros((q.shape[1], q.shape[1]), dtype=np.float64)
+    N.check(L.aatc_query_moment(q.ctypes.data, _np_dtype_code(q), q.shape[0], q.shape[1], m.ctypes.data))
+    return m
 
 
 def calib_view(blob):

@@ -467,7 +467,8 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
   const int kbits = kc->total_bits, vbits = vc->total_bits;
   const bool ok = (kmag == AATC_MAGIC) & (vmag == AATC_MAGIC) & (kbits == Bk) & (vbits == Bv) & (n4 >= 0) &
                   (n2 >= 0) & (n1 >= 0) & (NV <= NVB) & (PHDR + 16 * NV <= a.prec);
-  const int rot = kc->rotation;
+  // a NOVA blob holds its query transform E^-T where a KLT blob holds R: the same GEMV
+  const int rot = kc->rotation == AATC_ROT_NOVA ? AATC_ROT_KLT : kc->rotation;
   const int nw = ok ? tiles_of(wave) : 0;   // a bad blob streams nothing
 
   // ---- stream set-up that needs no table: it runs while the tables are in flight
@@ -1095,7 +1096,8 @@ __global__ __launch_bounds__(CNT) void k_attn_combine(CombArgs a, const aatc_cal
   const int ti = tid & (D - 1), tf = tid < 3 * D ? tid : 0;   // clamped table indexes
   const float r_o = vc->o32[ti], r_d = vc->delta32[ti];
   const int r_b = vc->bits[ti], r_cf = vc->channel_field[tf], r_fs = vc->field_shift[tf];
-  const int rot = vc->rotation;
+  // NOVA: R_V^T is E^-1, applied by the same GEMV as a KLT blob's R^T
+  const int rot = vc->rotation == AATC_ROT_NOVA ? AATC_ROT_KLT : vc->rotation;
   float rv[16];
   if (rot == AATC_ROT_KLT) {
     const int j = tid & (D - 1), e8 = tid >> 7;

@@ -148,7 +148,7 @@ __global__ __launch_bounds__(THREADS) void k_encode(CodecArgs a) {
     xs[e] = v;
   }
   double acc[4][8];
-  tile_gemm<true>(xs, c->R, mchunk, acc);
+  tile_gemm<true>(xs, c->E, mchunk, acc);       // y = E x
   // quantize: u = (y - o) * inv + 2^(b-1); c = clamp(floor(u), 0, 2^b - 1); NaN -> 0
   const int tb = tid >> 4, cb = tid & 15;
   for (int bb = 0; bb < 8; ++bb) {

@@ -239,6 +239,30 @@ double optimal_step(int b) {
 // ---- integer reverse water-filling ---------------------------------------------------------
 // The B largest candidates sigma_i^2 4^-k (k < max_bits) in the order (value desc,
 // channel asc, bit asc); exact in fp64 (ldexp).
+// KLT of a symmetric d x d matrix: rows of r = eigenvectors in descending eigenvalue order
+// (stable), the largest-magnitude entry of each row made positive (first index on ties);
+// s2 = the eigenvalues, clamped at 0.
+bool klt_rows(const std::vector<double>& sym, int d, double* r, double* s2) {
+  std::vector<double> a = sym, v;
+  if (!jacobi_eig(a, v, d)) return false;
+  std::vector<int> order(d);
+  for (int i = 0; i < d; ++i) order[i] = i;
+  std::stable_sort(order.begin(), order.end(), [&](int i, int j) { return a[i * d + i] > a[j * d + j]; });
+  for (int row = 0; row < d; ++row) {
+    const int col = order[row];
+    int jmax = 0;
+    for (int k = 1; k < d; ++k)
+      if (std::fabs(v[k * d + col]) > std::fabs(v[jmax * d + col])) jmax = k;
+    const double sg = v[jmax * d + col] < 0 ? -1.0 : 1.0;
+    for (int k = 0; k < d; ++k) r[row * d + k] = sg * v[k * d + col];
+    s2[row] = std::max(a[col * d + col], 0.0);
+  }
+  return true;
+}
+
+// Eigenvalues of the query second moment below this fraction of the largest are raised to it.
+constexpr double kNovaEigFloor = 1e-6;
+
 void waterfill_impl(const double* s2, int d, int total, int max_bits, uint8_t* bits) {
   struct C { double v; int i, k; };
   std::vector<C> c;
@@ -301,8 +325,20 @@ aatc_status aatc_calibrate(const aatc_calib_params* p, const void* x, aatc_dtype
   clear_error();
   if (!p || !x || !out) return fail(AATC_ERR_INVALID_ARGUMENT, "null pointer");
   if (p->d != AATC_D) return fail(AATC_ERR_UNSUPPORTED, "d=%d (only 128)", p->d);
-  if (p->rotation < AATC_ROT_KLT || p->rotation > AATC_ROT_IDENTITY)
+  if (p->rotation < AATC_ROT_KLT || p->rotation > AATC_ROT_NOVA)
     return fail(AATC_ERR_INVALID_ARGUMENT, "rotation %d", p->rotation);
+  if (p->rotation == AATC_ROT_NOVA) {
+    if (!p->query_moment) return fail(AATC_ERR_INVALID_ARGUMENT, "NOVA needs query_moment");
+    const double* s = p->query_moment;
+    for (int i = 0; i < AATC_D * AATC_D; ++i)
+      if (!std::isfinite(s[i])) return fail(AATC_ERR_NUMERICAL, "query_moment[%d] is not finite", i);
+    for (int i = 0; i < AATC_D; ++i)
+      for (int j = i + 1; j < AATC_D; ++j) {
+        const double a = s[i * AATC_D + j], b = s[j * AATC_D + i];
+        if (std::fabs(a - b) > 1e-12 * (std::fabs(a) + std::fabs(b)) + 1e-300)
+          return fail(AATC_ERR_INVALID_ARGUMENT, "query_moment is not symmetric at (%d, %d)", i, j);
+      }
+  }
   if (p->max_bits < 1 || p->max_bits > AATC_MAX_BITS)
     return fail(AATC_ERR_BUDGET, "max_bits=%d (1..8)", p->max_bits);
   const int32_t total = aatc_bits_budget(p->bits_per_elem, p->d);
@@ -343,20 +379,53 @@ aatc_status aatc_calibrate(const aatc_calib_params* p, const void* x, aatc_dtype
   mean_cov(xs, n, c->mu, cov);
 
   if (p->rotation == AATC_ROT_KLT) {
-    std::vector<double> a = cov, v;
+    if (!klt_rows(cov, d, c->R, c->sigma2)) return fail(AATC_ERR_NUMERICAL, "Jacobi eigensolver did not converge");
+  } else if (p->rotation == AATC_ROT_NOVA) {
+    // S = V diag(s) V^T with s floored; S^(+-1/2); KLT U of M = S^(1/2) C S^(1/2);
+    // E = U S^(1/2), R = U S^(-1/2)
+    std::vector<double> a(p->query_moment, p->query_moment + d * d), v;
     if (!jacobi_eig(a, v, d)) return fail(AATC_ERR_NUMERICAL, "Jacobi eigensolver did not converge");
-    std::vector<int> order(d);
-    for (int i = 0; i < d; ++i) order[i] = i;
-    std::stable_sort(order.begin(), order.end(), [&](int i, int j) { return a[i * d + i] > a[j * d + j]; });
-    for (int r = 0; r < d; ++r) {
-      const int col = order[r];
-      int jmax = 0;
-      for (int k = 1; k < d; ++k)
-        if (std::fabs(v[k * d + col]) > std::fabs(v[jmax * d + col])) jmax = k;
-      const double sg = v[jmax * d + col] < 0 ? -1.0 : 1.0;
-      for (int k = 0; k < d; ++k) c->R[r * d + k] = sg * v[k * d + col];
-      c->sigma2[r] = std::max(a[col * d + col], 0.0);
-    }
+    double smax = 0.0;
+    for (int i = 0; i < d; ++i) smax = std::max(smax, a[i * d + i]);
+    if (!(smax > 0.0)) return fail(AATC_ERR_NUMERICAL, "query moment has no positive eigenvalue");
+    std::vector<double> sh(d * d, 0.0), sih(d * d, 0.0), ev(d);
+    for (int k = 0; k < d; ++k) ev[k] = std::max(a[k * d + k], kNovaEigFloor * smax);
+    for (int i = 0; i < d; ++i)
+      for (int j = 0; j < d; ++j) {
+        double h = 0.0, ih = 0.0;
+        for (int k = 0; k < d; ++k) {
+          const double vv = v[i * d + k] * v[j * d + k];
+          h += vv * std::sqrt(ev[k]);
+          ih += vv / std::sqrt(ev[k]);
+        }
+        sh[i * d + j] = h;
+        sih[i * d + j] = ih;
+      }
+    std::vector<double> tmp(d * d, 0.0), m(d * d, 0.0);
+    for (int i = 0; i < d; ++i)          // tmp = S^(1/2) C
+      for (int k = 0; k < d; ++k) {
+        const double sik = sh[i * d + k];
+        for (int j = 0; j < d; ++j) tmp[i * d + j] += sik * cov[k * d + j];
+      }
+    for (int i = 0; i < d; ++i)          // m = tmp S^(1/2)
+      for (int k = 0; k < d; ++k) {
+        const double tik = tmp[i * d + k];
+        for (int j = 0; j < d; ++j) m[i * d + j] += tik * sh[k * d + j];
+      }
+    for (int i = 0; i < d; ++i)
+      for (int j = i + 1; j < d; ++j) m[i * d + j] = m[j * d + i] = 0.5 * (m[i * d + j] + m[j * d + i]);
+    std::vector<double> u(d * d);
+    if (!klt_rows(m, d, u.data(), c->sigma2)) return fail(AATC_ERR_NUMERICAL, "Jacobi eigensolver did not converge");
+    for (int i = 0; i < d; ++i)
+      for (int j = 0; j < d; ++j) {
+        double e = 0.0, r = 0.0;
+        for (int k = 0; k < d; ++k) {
+          e += u[i * d + k] * sh[k * d + j];
+          r += u[i * d + k] * sih[k * d + j];
+        }
+        c->E[i * d + j] = e;
+        c->R[i * d + j] = r;
+      }
   } else {
     for (int i = 0; i < d; ++i)
       for (int j = 0; j < d; ++j) {
@@ -377,6 +446,7 @@ aatc_status aatc_calibrate(const aatc_calib_params* p, const void* x, aatc_dtype
       c->sigma2[i] = s;
     }
   }
+  if (p->rotation != AATC_ROT_NOVA) std::memcpy(c->E, c->R, sizeof(c->R));
   if (p->channel_weight) {
     // attention-aware: the candidates are w_i sigma_i^2 4^-k
     double ws2[AATC_D];
@@ -391,7 +461,7 @@ aatc_status aatc_calibrate(const aatc_calib_params* p, const void* x, aatc_dtype
   const double ref = smax > 0 ? smax : 1.0;
   for (int i = 0; i < d; ++i) {
     double o = 0.0;
-    for (int j = 0; j < d; ++j) o += c->R[i * d + j] * c->mu[j];
+    for (int j = 0; j < d; ++j) o += c->E[i * d + j] * c->mu[j];
     c->o[i] = o;
     if (c->bits[i]) {
       const double sg = std::sqrt(std::max(c->sigma2[i], 0.0));
@@ -457,6 +527,32 @@ aatc_status aatc_query_channel_weights(const void* blob, size_t bytes, const voi
     }
   }
   for (int i = 0; i < d; ++i) w[i] = acc[i] / static_cast<double>(n);
+  return AATC_OK;
+}
+
+aatc_status aatc_query_moment(const void* q, aatc_dtype dt, int64_t n, int64_t stride, double* out) {
+  clear_error();
+  if (!q || !out) return fail(AATC_ERR_INVALID_ARGUMENT, "null pointer");
+  if (n < 1) return fail(AATC_ERR_INVALID_ARGUMENT, "n=%lld < 1", (long long)n);
+  if (stride < AATC_D) return fail(AATC_ERR_INVALID_ARGUMENT, "row_stride < d");
+  std::vector<double> qs;
+  bool ok;
+  switch (dt) {
+    case AATC_F32: ok = read_rows<float>(q, n, stride, qs); break;
+    case AATC_BF16: ok = read_rows<bf16_tag>(q, n, stride, qs); break;
+    case AATC_F64: ok = read_rows<double>(q, n, stride, qs); break;
+    default: return fail(AATC_ERR_UNSUPPORTED, "dtype %d", (int)dt);
+  }
+  if (!ok) return fail(AATC_ERR_NUMERICAL, "non-finite query value");
+  const int d = AATC_D;
+  std::vector<double> acc(d * d, 0.0);
+  for (int64_t r = 0; r < n; ++r) {
+    const double* qr = qs.data() + r * d;
+    for (int i = 0; i < d; ++i)
+      for (int j = i; j < d; ++j) acc[i * d + j] += qr[i] * qr[j];
+  }
+  for (int i = 0; i < d; ++i)
+    for (int j = i; j < d; ++j) out[i * d + j] = out[j * d + i] = acc[i * d + j] / static_cast<double>(n);
   return AATC_OK;
 }
 

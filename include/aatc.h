@@ -48,7 +48,7 @@ typedef enum {
 } aatc_status;
 
 typedef enum { AATC_F32 = 0, AATC_BF16 = 1, AATC_F64 = 2 } aatc_dtype;
-typedef enum { AATC_ROT_KLT = 0, AATC_ROT_WHT = 1, AATC_ROT_IDENTITY = 2 } aatc_rotation;
+typedef enum { AATC_ROT_KLT = 0, AATC_ROT_WHT = 1, AATC_ROT_IDENTITY = 2, AATC_ROT_NOVA = 3 } aatc_rotation;
 
 #define AATC_D 128
 #define AATC_TILE 64             /* tokens per packed tile */
@@ -56,7 +56,7 @@ typedef enum { AATC_ROT_KLT = 0, AATC_ROT_WHT = 1, AATC_ROT_IDENTITY = 2 } aatc_
 #define AATC_MAX_FIELDS 384      /* 3 fields per channel at most (7 = 4+2+1) */
 #define AATC_MAX_GROUP 8         /* q heads per KV head handled by decode attention */
 #define AATC_MAGIC 0x43544141u   /* "AATC" */
-#define AATC_VERSION 1u
+#define AATC_VERSION 2u
 
 /*
  * Calibration artefact of one (layer, KV head, tensor K|V): a plain-old-data blob that is
@@ -99,9 +99,10 @@ typedef struct aatc_calib {
   int32_t n_fields4, n_fields2, n_fields1;
   int32_t n_calib;         /* calibration rows used */
   uint64_t checksum;       /* FNV-1a 64 of the whole blob with this field set to 0 */
-  double R[AATC_D * AATC_D];         /* row i = rotated channel i (orthogonal) */
+  double R[AATC_D * AATC_D];         /* query transform q~ = R q and reconstruction x = R^T y;
+                                        orthogonal, except NOVA: R = E^-T */
   double mu[AATC_D];                 /* calibration mean (original basis) */
-  double o[AATC_D];                  /* per-channel offset R mu */
+  double o[AATC_D];                  /* per-channel offset E mu */
   double sigma2[AATC_D];             /* rotated-channel variance */
   double delta[AATC_D];              /* quantizer step (0 for b_i = 0) */
   double inv_delta[AATC_D];          /* 1/delta, correctly rounded (0 for b_i = 0) */
@@ -116,6 +117,7 @@ typedef struct aatc_calib {
   uint8_t field_width[AATC_MAX_FIELDS];
   uint16_t field_word[AATC_MAX_FIELDS];
   int16_t channel_field[AATC_D * 3];  /* fields of channel i, -1 padded */
+  double E[AATC_D * AATC_D];         /* encoder: coefficients y = E x (E = R except NOVA) */
   uint8_t reserved[64];
 } aatc_calib;
 
@@ -128,6 +130,9 @@ typedef struct {
   const double* channel_weight;  /* NULL: the cache-MSE allocation; else d weights w_i >= 0 of
                                     the rotated channels (attention-aware keys: see
                                     aatc_query_channel_weights) */
+  const double* query_moment;    /* AATC_ROT_NOVA only: d x d row-major second moment
+                                    E[q q^T] of calibration queries (aatc_query_moment);
+                                    NULL otherwise */
 } aatc_calib_params;
 
 /* Readable bytes a codes buffer must have past its last sequence's words: decode attention
@@ -178,11 +183,19 @@ size_t aatc_packed_bytes(int32_t total_bits, int64_t n_tokens);
  *   unless params->channel_weight is given, which then makes the allocation minimise
  *   sum_i w_i sigma_i^2 4^-b_i, the weighted, attention-aware distortion); quantizer
  *   step delta_i = sigma_i g(b_i) where g(b) minimises the MSE of the 2^b-level mid-rise
- *   uniform quantizer on N(0,1); offset o = R mu; packing tables.
+ *   uniform quantizer on N(0,1); offset o = E mu; packing tables.  E = R for KLT, WHT and
+ *   IDENTITY.
+ *   NOVA [SPHERICAL KV page, NOVA-KV abstract: a closed-form key transform from calibration
+ *   statistics that is not orthogonal and turns the attention-aware distortion into MSE of
+ *   the transformed coefficients]: with S = params->query_moment (eigenvalues below 1e-6 of
+ *   the largest raised to it), E = U S^(1/2) where the rows of U are the KLT (as above) of
+ *   S^(1/2) C S^(1/2), sigma2 its eigenvalues, and R = E^-T = U S^(-1/2): decode attention
+ *   scores q.x as (R q).(E x) and reconstructs x = R^T y, so the kernels run unchanged.
  *   Writes one aatc_calib into calib_host (calib_bytes >= aatc_calib_bytes(d)).
  *   Errors: d != 128 -> UNSUPPORTED; B outside [0, 8d] or max_bits outside 1..8 -> BUDGET;
- *   n_calib < 2, null pointers, row_stride < d, a negative channel weight ->
- *   INVALID_ARGUMENT; a non-finite value or weight -> NUMERICAL; small blob ->
+ *   n_calib < 2, null pointers, row_stride < d, a negative channel weight, NOVA without a
+ *   query moment or a moment that is not symmetric -> INVALID_ARGUMENT; a non-finite value,
+ *   weight or moment, a moment with no positive eigenvalue -> NUMERICAL; small blob ->
  *   BUFFER_TOO_SMALL.  Zero-variance (or zero-weight) channels get 0 bits unless the budget
  *   exceeds 8 x (the other channels).
  */
@@ -204,6 +217,17 @@ aatc_status aatc_calibrate(const aatc_calib_params* params, const void* x_host, 
  */
 aatc_status aatc_query_channel_weights(const void* calib_host, size_t calib_bytes, const void* q_host,
                                        aatc_dtype dtype, int64_t n, int64_t row_stride, double* w_out);
+
+/*
+ * aatc_query_moment -- host, synchronous, fp64.  [SPHERICAL KV page, NOVA-KV abstract: the key
+ * transform comes from key and query calibration statistics]  moment_out[d*d] (row-major) =
+ * (1/n) sum_r q_r q_r^T over n query rows (row r at q_host + r*row_stride elements, dtype
+ * F32/BF16/F64), the second moment (not centred) that aatc_calibrate's NOVA transform takes.
+ *   Errors: n < 1, null pointers, row_stride < d -> INVALID_ARGUMENT; a non-finite query ->
+ *   NUMERICAL.
+ */
+aatc_status aatc_query_moment(const void* q_host, aatc_dtype dtype, int64_t n, int64_t row_stride,
+                              double* moment_out);
 
 /* Checks magic, version, d, checksum and internal consistency of a host blob. */
 aatc_status aatc_calib_validate(const void* calib_host, size_t calib_bytes);

@@ -14,9 +14,12 @@ class Case:
     """Synthetic layer: per-head calibration, context K/V and queries, oracle artefacts."""
 
     def __init__(self, cfg, n_kv, group, n_tokens, batch=1, dtype="bf16", rotation="klt", bpe_k=2.0,
-                 bpe_v=None, marginal="gauss", layer=0, n_calib=1024, aware=False):
+                 bpe_v=None, marginal="gauss", layer=0, n_calib=1024, aware=False, v_rotation=None,
+                 n_q_cal=512):
         self.cfg, self.n_kv, self.group, self.n, self.batch = cfg, n_kv, group, n_tokens, batch
         self.dtype, self.rotation, self.layer = dtype, rotation, layer
+        self.v_rotation = rotation if v_rotation is None else v_rotation
+        aware = aware or rotation == "nova"          # the non-orthogonal key transform needs queries
         self.bpe_k, self.bpe_v = bpe_k, bpe_k if bpe_v is None else bpe_v
         self.n_q = n_kv * group
         self.cal = {}
@@ -30,11 +33,11 @@ class Case:
         self.q = np.stack([synth.queries(cfg, layer, self.n_q, n_kv, [self.x[synth.K][b, h] for h in range(n_kv)])
                            for b in range(batch)])  # [b, n_q, d]
         # attention-aware keys: calibration queries drawn like the decode queries (their KV
-        # head's key generator), 512 per head
-        self.q_cal = [synth.draw(cfg, layer, h, synth.K, "query", 512, dtype="f64", extra=50000) if aware else None
-                      for h in range(n_kv)]
+        # head's key generator), n_q_cal per head
+        self.q_cal = [synth.draw(cfg, layer, h, synth.K, "query", n_q_cal, dtype="f64", extra=50000) if aware
+                      else None for h in range(n_kv)]
         self.art = {synth.K: [O.calibrate(c, rotation, self.bpe_k, q_cal=qc) for c, qc in zip(self.cal[synth.K], self.q_cal)],
-                    synth.V: [O.calibrate(c, rotation, self.bpe_v) for c in self.cal[synth.V]]}
+                    synth.V: [O.calibrate(c, self.v_rotation, self.bpe_v) for c in self.cal[synth.V]]}
         self.codes = {t: np.stack([np.stack([O.encode_codes(self.x[t][b, h], self.art[t][h])
                                              for h in range(n_kv)]) for b in range(batch)])
                       for t in (synth.K, synth.V)}
@@ -45,10 +48,15 @@ class Case:
         out = []
         for h, c in enumerate(self.cal[tensor]):
             xc = c if self.dtype == "f32" else bits16(c)
-            blob = api.calibrate(xc, self.rotation, bpe)
-            if tensor == synth.K and self.q_cal[h] is not None:
-                w = api.query_channel_weights(blob, self.q_cal[h])
-                blob = api.calibrate(xc, self.rotation, bpe, channel_weight=w)
+            if tensor == synth.V:
+                blob = api.calibrate(xc, self.v_rotation, bpe)
+            elif self.rotation == "nova":
+                blob = api.calibrate(xc, "nova", bpe, query_moment=api.query_moment(self.q_cal[h]))
+            else:
+                blob = api.calibrate(xc, self.rotation, bpe)
+                if self.q_cal[h] is not None:
+                    w = api.query_channel_weights(blob, self.q_cal[h])
+                    blob = api.calibrate(xc, self.rotation, bpe, channel_weight=w)
             out.append(blob)
         return out
 

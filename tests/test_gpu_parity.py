@@ -168,6 +168,37 @@ def test_attention_aware_key_allocation():
     assert np.abs(lse.cpu().numpy() - lref).max() <= 5e-3
 
 
+@pytest.mark.parametrize("cfg,group,bpe,v_rot,marginal", [(2, 4, 2.76, "klt", "gauss"), (4, 7, 1.33, "wht", "t3")])
+def test_nova_key_transform(cfg, group, bpe, v_rot, marginal):
+    """Non-orthogonal key transform (library: query moment, then a NOVA calibration): the
+    encoder's E x codes, the decoder's E^-1 y_hat, and decode attention through the query
+    transform E^-T, all against the oracle."""
+    torch = _torch()
+    from compressed_decode_attention_head_amd import api
+    case = Case(cfg=cfg, n_kv=2, group=group, n_tokens=700, rotation="nova", v_rotation=v_rot, bpe_k=bpe,
+                marginal=marginal, n_q_cal=2048)
+    for h, blob in enumerate(case.blobs(synth.K)):
+        c = api.calib_view(blob)
+        assert int(c["rotation"]) == 3
+        assert np.array_equal(c["bits"].astype(np.int64), case.art[synth.K][h]["bits"])
+    cache = case.make_cache()
+    for t in (synth.K, synth.V):
+        cache.encode(t, case.torch_x(t))
+    _check_codes(case, cache, synth.K)
+    xh = cache.decode(synth.K, 0, case.n).cpu().numpy().astype(np.float64)
+    for h in range(case.n_kv):
+        ref = O.reconstruct(case.codes[synth.K][0, h], case.art[synth.K][h])
+        assert np.abs(xh[0, h] - ref).max() <= 1e-6 * np.abs(ref).max(), h
+    out, lse = cache.decode_attn(torch.from_numpy(case.q.astype(np.float32)).cuda(), case.n)
+    torch.cuda.synchronize()
+    ref, lref = case.oracle_attention()
+    err = np.abs(out.cpu().numpy() - ref).max()
+    lerr = np.abs(lse.cpu().numpy() - lref).max()
+    print("nova keys cfg", cfg, "attn max abs err", err, "lse err", lerr, flush=True)
+    assert err <= ATOL_ATTN
+    assert lerr <= 5e-3
+
+
 def test_zero_bit_tensors():
     """All K channels at 0 bits: uniform softmax; all V channels at 0 bits: output = mu_V."""
     torch = _torch()

@@ -96,6 +96,82 @@ def test_attention_aware_calibration_matches_oracle(cfg, rot, bpe):
     assert np.array_equal(c["R"], api.calib_view(blob0)["R"])
 
 
+def _nova_queries(seed, n, scales):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((n, 128)) * scales) @ synth.haar_orthogonal(rng, 128)
+
+
+def test_query_moment_matches_numpy():
+    q = _nova_queries(3, 777, np.geomspace(0.05, 3.0, 128))
+    for qq in (q, q.astype(np.float32), _bits16(synth.round_bf16(q))):
+        want = O.query_moment(qq.astype(np.float64) if qq.dtype != np.uint16
+                              else (qq.astype(np.uint32) << 16).view(np.float32).astype(np.float64))
+        got = api.query_moment(qq)
+        assert np.array_equal(got, got.T)
+        assert np.abs(got - want).max() < 1e-13 * np.abs(want).max()
+
+
+@pytest.mark.parametrize("cfg,bpe,scales", [(2, 2.76, "geo"), (4, 1.33, "ramp"), (1, 2.0, "geo")])
+def test_nova_calibration_matches_oracle(cfg, bpe, scales):
+    """The non-orthogonal key transform: library (C++, Jacobi) against the oracle (LAPACK)."""
+    dtype = "f32" if cfg == 1 else "bf16"
+    x = _cal(cfg, 1, synth.K, dtype=dtype, marginal="t3" if cfg == 4 else "gauss")
+    sc = np.geomspace(0.05, 3.0, 128) if scales == "geo" else np.linspace(0.1, 3.0, 128)
+    q = _nova_queries(cfg, 2048, sc)
+    ref = O.calibrate(x, "nova", bpe, q_cal=q)
+    blob = api.calibrate(x if dtype == "f32" else _bits16(x), "nova", bpe, query_moment=api.query_moment(q))
+    api.validate(blob)
+    c = api.calib_view(blob)
+    assert int(c["rotation"]) == 3 and int(c["total_bits"]) == ref["B"]
+    assert np.array_equal(c["bits"].astype(np.int64), ref["bits"])
+    E, R = c["E"].reshape(128, 128), c["R"].reshape(128, 128)
+    assert np.abs(E - ref["E"]).max() < 1e-8 * np.abs(ref["E"]).max()
+    assert np.abs(R - ref["R"]).max() < 1e-8 * np.abs(ref["R"]).max()
+    assert np.abs(R @ E.T - np.eye(128)).max() < 1e-9
+    assert np.abs(c["sigma2"] - ref["sigma2"]).max() < 1e-10 * ref["sigma2"].max()
+    assert np.abs(c["o"] - ref["o"]).max() < 1e-9 * (1 + np.abs(ref["o"]).max())
+    coded = ref["bits"] > 0
+    assert np.all(np.abs(c["delta"][coded] / ref["delta"][coded] - 1) < 1e-9)
+    assert np.array_equal(c["R32"], R.astype(np.float32).ravel())
+
+
+def test_orthogonal_blobs_encode_with_r():
+    """Every other rotation stores E = R."""
+    x = _cal(2, 0, synth.K)
+    for rot in ("klt", "wht", "identity"):
+        c = api.calib_view(api.calibrate(_bits16(x), rot, 2.0))
+        assert np.array_equal(c["E"], c["R"])
+
+
+def test_nova_errors(L):
+    x = _bits16(_cal(2, 0, synth.K))
+    with pytest.raises(N.AatcError) as e:
+        api.calibrate(x, "nova", 2.0)                                   # no query moment
+    assert e.value.status == 1
+    m = api.query_moment(_nova_queries(1, 300, np.ones(128)))
+    bad = m.copy()
+    bad[3, 7] += 1e-3
+    with pytest.raises(N.AatcError) as e:
+        api.calibrate(x, "nova", 2.0, query_moment=bad)                 # not symmetric
+    assert e.value.status == 1
+    bad = m.copy()
+    bad[5, 5] = np.nan
+    with pytest.raises(N.AatcError) as e:
+        api.calibrate(x, "nova", 2.0, query_moment=bad)
+    assert e.value.status == 4
+    with pytest.raises(N.AatcError) as e:
+        api.calibrate(x, "nova", 2.0, query_moment=np.zeros((128, 128)))
+    assert e.value.status == 4
+    with pytest.raises(N.AatcError) as e:
+        api.query_moment(np.full((3, 128), np.inf, dtype=np.float32))
+    assert e.value.status == 4
+    out = np.zeros((128, 128))
+    qq = np.ones((4, 128), dtype=np.float32)
+    assert L.aatc_query_moment(qq.ctypes.data, 0, 0, 128, out.ctypes.data) == 1
+    assert L.aatc_query_moment(qq.ctypes.data, 0, 4, 100, out.ctypes.data) == 1
+    assert L.aatc_query_moment(None, 0, 4, 128, out.ctypes.data) == 1
+
+
 def test_attention_aware_errors(L):
     x = _cal(2, 0, synth.K)
     blob = api.calibrate(_bits16(x), "klt", 2.0)
