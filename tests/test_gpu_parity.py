@@ -199,6 +199,32 @@ def test_nova_key_transform(cfg, group, bpe, v_rot, marginal):
     assert lerr <= 5e-3
 
 
+@pytest.mark.parametrize("dtype,cfg", [("bf16", 4), ("f32", 1)])
+def test_encode_unaligned_rows_and_wht_appends(dtype, cfg):
+    """Encoder paths the other cases do not take: rows that are not 16-byte aligned (a view with
+    a 131-element token stride, offset by one element) go through scalar loads; a Walsh-Hadamard
+    cache is filled by a prefill and three appends, so partial tiles keep their earlier tokens."""
+    torch = _torch()
+    case = Case(cfg=cfg, n_kv=2, group=4, n_tokens=300, dtype=dtype, rotation="wht", bpe_k=1.33 if cfg == 4 else 2.0)
+    for t in (synth.K, synth.V):
+        cache = case.make_cache(capacity=320)
+        x = case.torch_x(t)
+        big = torch.zeros((case.batch, case.n_kv, case.n, 131), dtype=x.dtype, device=x.device)
+        big[..., 1:129] = x
+        view = big[..., 1:129]
+        assert view.stride(2) == 131 and (view.data_ptr() % 16) != 0
+        cache.encode(t, view)
+        torch.cuda.synchronize()
+        _check_codes(case, cache, t)
+        cache2 = case.make_cache(capacity=320)
+        off = 0
+        for step in (100, 1, 7, 192):
+            cache2.encode(t, x[:, :, off:off + step], token_offset=off)
+            off += step
+        torch.cuda.synchronize()
+        assert torch.equal(cache.codes(t), cache2.codes(t))
+
+
 def test_zero_bit_tensors():
     """All K channels at 0 bits: uniform softmax; all V channels at 0 bits: output = mu_V."""
     torch = _torch()
