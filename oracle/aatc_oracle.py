@@ -40,6 +40,7 @@ MAX_BITS = 8
 __all__ = [
     "TILE", "MAX_BITS", "calib_stats", "rotation_klt", "rotation_wht", "rotation_identity",
     "query_channel_weights", "query_moment", "transform_nova", "NOVA_EIG_FLOOR",
+    "allocation_distortion", "value_term_weight", "joint_kv_split",
     "bits_budget", "waterfill_bits", "waterfill_theta", "uniform_quantizer_mse",
     "uniform_quantizer_mse_deriv", "optimal_step", "quantizer_tables", "calibrate",
     "encode_codes", "dequantize", "reconstruct", "v_fields", "pack_k", "unpack_k",
@@ -174,6 +175,59 @@ def waterfill_bits(sigma2, total_bits, max_bits=MAX_BITS, weight=None):
     for _, i, _k in cands[:total_bits]:
         bits[i] += 1
     return bits
+
+
+def allocation_distortion(sigma2, bits, weight=None):
+    """High-resolution distortion sum_i w_i sigma_i^2 4^-b_i of an allocation."""
+    s2 = np.asarray(sigma2, dtype=np.float64)
+    if weight is not None:
+        s2 = np.asarray(weight, dtype=np.float64) * s2
+    return float(sum(math.ldexp(float(s2[i]), -2 * int(bits[i])) for i in range(s2.shape[0])))
+
+
+def value_term_weight(c_v, scale=None):
+    """lambda = scale^2 tr(C_V): how much a unit of key score-distortion costs in output error,
+    relative to a unit of value distortion, for attention spread over typical tokens.
+
+    First order in the errors, with out = sum_t p_t v_t: a score error ds_t moves the output by
+    sum_t p_t ds_t (v_t - out), a value error e_t by sum_t p_t e_t.  With independent zero-mean
+    errors the mean squared output errors are sum_t p_t^2 E[ds_t^2] |v_t - out|^2 and
+    sum_t p_t^2 E|e_t|^2; E[ds_t^2] = scale^2 x (the attention-aware key distortion), and
+    |v_t - out|^2 averages tr(C_V) when out is near the values' mean.
+    """
+    c_v = np.asarray(c_v, dtype=np.float64)
+    if scale is None:
+        scale = 1.0 / math.sqrt(c_v.shape[0])
+    return scale * scale * float(np.trace(c_v))
+
+
+def joint_kv_split(k_sigma2, v_sigma2, lam, total_bits, max_bits=MAX_BITS, k_weight=None):
+    """Split T = total_bits bits per (key, value) vector pair between K and V for a layer whose
+    heads all share B_K (and B_V = T - B_K): the B_K minimising
+        sum_h lam_h D_K,h(B_K) + D_V,h(T - B_K)
+    with D the water-filled distortions (keys with their attention-aware weights).  Among
+    values within 1e-12 (relative) of the minimum the smallest B_K is taken.
+
+    k_sigma2, v_sigma2: per-head variance vectors; lam: per-head weights (value_term_weight);
+    k_weight: per-head key weights or None.  Returns (B_K, B_V, distortion).
+    """
+    heads = len(k_sigma2)
+    d = len(k_sigma2[0])
+    cap = d * max_bits
+    lo, hi = max(0, total_bits - cap), min(total_bits, cap)
+    if lo > hi:
+        raise ValueError("budget out of range")
+    kw = [None] * heads if k_weight is None else k_weight
+    dist = []
+    for bk in range(lo, hi + 1):
+        tot = 0.0
+        for h in range(heads):
+            tot += lam[h] * allocation_distortion(k_sigma2[h], waterfill_bits(k_sigma2[h], bk, max_bits, kw[h]), kw[h])
+            tot += allocation_distortion(v_sigma2[h], waterfill_bits(v_sigma2[h], total_bits - bk, max_bits))
+        dist.append(tot)
+    best = min(dist)
+    i = next(j for j, v in enumerate(dist) if v <= best * (1.0 + 1e-12))
+    return lo + i, total_bits - lo - i, dist[i]
 
 
 def query_channel_weights(r, q_cal):

@@ -257,6 +257,103 @@ def test_attention_aware_bits_lower_score_error():
     assert errs[1] < 0.8 * errs[0], errs
 
 
+# ---------------------------------------------------------------- joint K/V budget split
+def test_joint_split_brute_force():
+    """The split is the exhaustive optimum over every pair of allocations with the same total
+    (d = 3 channels per tensor, up to 3 bits each, one head)."""
+    rng = np.random.default_rng(31)
+    for _ in range(20):
+        ks, vs = rng.uniform(0.01, 4.0, 3), rng.uniform(0.01, 4.0, 3)
+        lam, total = float(rng.uniform(0.1, 3.0)), int(rng.integers(0, 19))
+        best = min(lam * O.allocation_distortion(ks, bk) + O.allocation_distortion(vs, bv)
+                   for bk in itertools.product(range(4), repeat=3) for bv in itertools.product(range(4), repeat=3)
+                   if sum(bk) + sum(bv) == total)
+        bk, bv, dist = O.joint_kv_split([ks], [vs], [lam], total, max_bits=3)
+        assert bk + bv == total and abs(dist - best) <= 1e-12 * best
+
+
+def test_joint_split_limits_symmetry_and_scaling():
+    s2 = synth.spectrum(128)
+    T = 2 * 256
+    # no weight on keys -> every bit to V (up to its cap); a dominant key term -> every bit to K
+    assert O.joint_kv_split([s2], [s2], [0.0], T)[:2] == (0, T)
+    assert O.joint_kv_split([s2], [s2], [1e12], T)[:2] == (T, 0)
+    assert O.joint_kv_split([s2], [s2], [0.0], 1100)[:2] == (1100 - 1024, 1024)
+    # identical spectra with unit weight: the even split (353: no tie at the threshold); at 256
+    # candidates 256 and 257 tie, so 255 + 257 has the same distortion and the smaller B_K wins
+    assert O.joint_kv_split([s2], [s2], [1.0], 2 * 353)[:2] == (353, 353)
+    assert O.joint_kv_split([s2], [s2], [1.0], T)[:2] == (255, 257)
+    # scaling V's variances and lambda by the same power of two changes nothing
+    v2 = s2[::-1].copy() * 0.5
+    a = O.joint_kv_split([s2], [v2], [0.3], T)
+    b = O.joint_kv_split([s2], [4.0 * v2], [1.2], T)
+    assert a[:2] == b[:2] and abs(4.0 * a[2] - b[2]) <= 1e-12 * b[2]
+    # key weights act as a per-channel lambda
+    w = np.full(128, 2.0)
+    assert O.joint_kv_split([s2], [v2], [0.3], T, k_weight=[w])[:2] == O.joint_kv_split([s2], [v2], [0.6], T)[:2]
+
+
+def test_first_order_output_error_terms():
+    """The two error terms behind the split, checked by Monte Carlo on one attention row: small
+    independent score errors ds_t move the output by E|d out|^2 = sum_t p_t^2 E[ds^2] |v_t - out|^2,
+    small value errors e_t by sum_t p_t^2 E|e|^2."""
+    rng = np.random.default_rng(33)
+    n, d = 200, 16
+    s = rng.standard_normal(n) * 1.5
+    v = rng.standard_normal((n, d))
+    p = np.exp(s - s.max())
+    p /= p.sum()
+    out = p @ v
+    eps = 1e-4
+    ks, vs = [], []
+    for _ in range(3000):
+        ds = rng.standard_normal(n) * eps
+        p2 = np.exp(s + ds - (s + ds).max())
+        p2 /= p2.sum()
+        ks.append(((p2 @ v - out) ** 2).sum())
+        e = rng.standard_normal((n, d)) * eps
+        vs.append(((p @ (v + e) - out) ** 2).sum())
+    want_k = (p * p * ((v - out) ** 2).sum(axis=1)).sum() * eps * eps
+    want_v = (p * p).sum() * d * eps * eps
+    assert abs(np.mean(ks) / want_k - 1) < 0.08 and abs(np.mean(vs) / want_v - 1) < 0.08
+    assert abs(O.value_term_weight(np.diag(np.arange(1.0, 5.0))) - 10.0 / 4.0) < 1e-15
+
+
+def test_joint_split_lowers_attention_error():
+    """At 2 bits per element, the split from the calibration statistics (attention-aware key
+    weights from queries scaled like the decode queries) gives a lower attention-output error than
+    the equal split, at the same total bits."""
+    cfg, n_kv, group, n, bpe = 2, 2, 4, 2048, 2.0
+    B = O.bits_budget(bpe, 128)
+    calk = [synth.draw(cfg, 0, h, synth.K, "calib", 1024) for h in range(n_kv)]
+    calv = [synth.draw(cfg, 0, h, synth.V, "calib", 1024) for h in range(n_kv)]
+    ctxk = [synth.draw(cfg, 0, h, synth.K, "context", n) for h in range(n_kv)]
+    ctxv = [synth.draw(cfg, 0, h, synth.V, "context", n) for h in range(n_kv)]
+    qcal = []
+    for h in range(n_kv):
+        qr = synth.draw(cfg, 0, h, synth.K, "query", 2048, dtype="f64", extra=50000)
+        qcal.append(qr * (2.0 / (calk[h] @ qr.T / math.sqrt(128)).std(axis=0))[:, None])
+    q = synth.queries(cfg, 0, n_kv * group, n_kv, ctxk)
+    ka = [O.calibrate(calk[h], "klt", bpe, q_cal=qcal[h]) for h in range(n_kv)]
+    va = [O.calibrate(calv[h], "klt", bpe) for h in range(n_kv)]
+    bk, bv, _ = O.joint_kv_split([a["sigma2"] for a in ka], [a["sigma2"] for a in va],
+                                 [O.value_term_weight(a["C"]) for a in va], 2 * B, k_weight=[a["weight"] for a in ka])
+    assert bk + bv == 2 * B and bk != B
+
+    def err(bk_, bv_):
+        e = 0.0
+        for h in range(n_kv):
+            kart = O.calibrate(calk[h], "klt", bk_ / 128, q_cal=qcal[h])
+            vart = O.calibrate(calv[h], "klt", bv_ / 128)
+            kh = O.reconstruct(O.encode_codes(ctxk[h], kart), kart)
+            vh = O.reconstruct(O.encode_codes(ctxv[h], vart), vart)
+            for g in range(h * group, (h + 1) * group):
+                e += float(((O.attention(q[g], ctxk[h], ctxv[h])[0] - O.attention(q[g], kh, vh)[0]) ** 2).sum())
+        return e
+
+    assert err(bk, bv) < 0.7 * err(B, B)
+
+
 # ---------------------------------------------------------------- non-orthogonal key transform
 def _aniso_queries(rng, n, basis, scales):
     return (rng.standard_normal((n, 128)) * scales) @ basis
