@@ -111,6 +111,8 @@ def lib():
     L.aatc_decode_attn_segments.restype = ctypes.c_int
     L.aatc_decode_attn_segments.argtypes = [ctypes.POINTER(Segment), i32, i32, i32, vp, i32, ctypes.c_float, vp,
                                             vp, vp, sz, vp]
+    L.aatc_joint_kv_split.restype = ctypes.c_int
+    L.aatc_joint_kv_split.argtypes = [vp, vp, i32, vp, ctypes.c_float, i32, vp, vp]
     L.aatc_query_moment.restype = ctypes.c_int
     L.aatc_query_moment.argtypes = [vp, ctypes.c_int, i64, i64, vp]
     L.aatc_decode_attn_dense_workspace_bytes.restype = sz
@@ -135,4 +137,5 @@ EXPORTS = ["aatc_status_string", "aatc_last_error", "aatc_calib_bytes", "aatc_bi
            "aatc_encode", "aatc_decode", "aatc_decode_attn_workspace_bytes", "aatc_decode_attn",
            "aatc_decode_attn_partial", "aatc_decode_attn_merge", "aatc_tier_distortions",
            "aatc_token_tiers", "aatc_decode_attn_segments_workspace_bytes", "aatc_decode_attn_segments",
-           "aatc_decode_attn_dense_workspace_bytes", "aatc_decode_attn_dense", "aatc_query_moment"]
+           "aatc_decode_attn_dense_workspace_bytes", "aatc_decode_attn_dense", "aatc_query_moment",
+           "aatc_joint_kv_split"]

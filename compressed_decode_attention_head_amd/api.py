@@ -79,6 +79,26 @@ def query_moment(q):
     return m
 
 
+def joint_kv_split(k_blobs, v_blobs, total_bits, k_weight=None, scale=0.0):
+    """aatc_joint_kv_split: (B_K, B_V) for a layer's per-head K and V blobs (host uint8 arrays),
+    optional key weights [n_heads, d] (query_channel_weights) and total bits per (K, V) pair."""
+    L = N.lib()
+    if len(k_blobs) != len(v_blobs) or not k_blobs:
+        raise ValueError("one K and one V blob per head")
+    kb = np.ascontiguousarray(np.concatenate([np.asarray(b, dtype=np.uint8) for b in k_blobs]))
+    vb = np.ascontiguousarray(np.concatenate([np.asarray(b, dtype=np.uint8) for b in v_blobs]))
+    wp = None
+    if k_weight is not None:
+        w = np.ascontiguousarray(k_weight, dtype=np.float64)
+        if w.shape != (len(k_blobs), N.D):
+            raise ValueError("k_weight must be [n_heads, d]")
+        wp = w.ctypes.data
+    bk, bv = ctypes.c_int32(), ctypes.c_int32()
+    N.check(L.aatc_joint_kv_split(kb.ctypes.data, vb.ctypes.data, len(k_blobs), wp, float(scale), int(total_bits),
+                                  ctypes.byref(bk), ctypes.byref(bv)))
+    return bk.value, bv.value
+
+
 def calib_view(blob):
     """Read-only structured view of a blob (fields as in struct aatc_calib)."""
     return np.frombuffer(np.asarray(blob, dtype=np.uint8).tobytes()[:N.CALIB_DTYPE.itemsize],

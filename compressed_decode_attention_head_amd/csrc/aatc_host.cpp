@@ -556,6 +556,65 @@ aatc_status aatc_query_moment(const void* q, aatc_dtype dt, int64_t n, int64_t s
   return AATC_OK;
 }
 
+aatc_status aatc_joint_kv_split(const void* kblobs, const void* vblobs, int32_t n_heads, const double* kw,
+                                float scale, int32_t total, int32_t* bk_out, int32_t* bv_out) {
+  clear_error();
+  if (!kblobs || !vblobs || !bk_out || !bv_out) return fail(AATC_ERR_INVALID_ARGUMENT, "null pointer");
+  if (n_heads < 1) return fail(AATC_ERR_INVALID_ARGUMENT, "n_heads=%d < 1", n_heads);
+  const auto* kc = static_cast<const aatc_calib*>(kblobs);
+  const auto* vc = static_cast<const aatc_calib*>(vblobs);
+  const int d = AATC_D;
+  int max_k = AATC_MAX_BITS, max_v = AATC_MAX_BITS;
+  for (int h = 0; h < n_heads; ++h) {
+    aatc_status st = aatc_calib_validate(kc + h, sizeof(aatc_calib));
+    if (st == AATC_OK) st = aatc_calib_validate(vc + h, sizeof(aatc_calib));
+    if (st != AATC_OK) return st;
+    max_k = std::min(max_k, static_cast<int>(kc[h].max_bits));
+    max_v = std::min(max_v, static_cast<int>(vc[h].max_bits));
+  }
+  if (kw)
+    for (int64_t i = 0; i < static_cast<int64_t>(n_heads) * d; ++i) {
+      if (!std::isfinite(kw[i])) return fail(AATC_ERR_NUMERICAL, "k_weight[%lld] is not finite", (long long)i);
+      if (kw[i] < 0.0) return fail(AATC_ERR_INVALID_ARGUMENT, "k_weight[%lld] < 0", (long long)i);
+    }
+  if (total < 0 || total > d * (max_k + max_v))
+    return fail(AATC_ERR_BUDGET, "total_bits %d outside [0, %d]", total, d * (max_k + max_v));
+  const double sc = scale > 0.f ? static_cast<double>(scale) : 1.0 / std::sqrt(static_cast<double>(d));
+  std::vector<double> ks(static_cast<size_t>(n_heads) * d), lam(n_heads);
+  for (int h = 0; h < n_heads; ++h) {
+    double tr = 0.0;
+    for (int i = 0; i < d; ++i) {
+      ks[h * d + i] = kw ? kw[h * d + i] * kc[h].sigma2[i] : kc[h].sigma2[i];
+      tr += vc[h].sigma2[i];
+    }
+    lam[h] = sc * sc * tr;
+  }
+  auto dist = [&](const double* s2, int budget, int max_bits) {
+    uint8_t bits[AATC_D];
+    waterfill_impl(s2, d, budget, max_bits, bits);
+    double t = 0.0;
+    for (int i = 0; i < d; ++i) t += std::ldexp(s2[i], -2 * bits[i]);
+    return t;
+  };
+  const int lo = std::max(0, total - d * max_v), hi = std::min(total, d * max_k);
+  std::vector<double> tot(hi - lo + 1);
+  for (int bk = lo; bk <= hi; ++bk) {
+    double t = 0.0;
+    for (int h = 0; h < n_heads; ++h) {
+      t += lam[h] * dist(&ks[h * d], bk, max_k);
+      t += dist(vc[h].sigma2, total - bk, max_v);
+    }
+    tot[bk - lo] = t;
+  }
+  double best = tot[0];
+  for (double t : tot) best = std::min(best, t);
+  int pick = 0;
+  while (!(tot[pick] <= best * (1.0 + 1e-12))) ++pick;
+  *bk_out = lo + pick;
+  *bv_out = total - lo - pick;
+  return AATC_OK;
+}
+
 int32_t aatc_calib_v_tiles(const void* blob) {
   if (!blob) return -1;
   const auto* c = static_cast<const aatc_calib*>(blob);

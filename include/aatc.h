@@ -229,6 +229,33 @@ aatc_status aatc_query_channel_weights(const void* calib_host, size_t calib_byte
 aatc_status aatc_query_moment(const void* q_host, aatc_dtype dtype, int64_t n, int64_t row_stride,
                               double* moment_out);
 
+/*
+ * aatc_joint_kv_split -- host, synchronous, fp64.  [AATC abstract: the expected
+ * attention-aware distortion splits into a key term and a value term]  How to share
+ * total_bits bits per (key, value) vector pair between the K and V caches of one layer, whose
+ * heads all use the same B_K (and B_V = total_bits - B_K):
+ *   B_K = argmin sum_h lambda_h D_K,h(B_K) + D_V,h(total_bits - B_K),
+ *   D(B) = sum_i w_i sigma2_i 4^-b_i(B) with b(B) the water-filling of aatc_calibrate at the
+ *   blob's max_bits (keys: w = k_weight row of the head, or 1; values: w = 1), and
+ *   lambda_h = scale^2 sum_i sigma2_V,h,i (scale = softmax_scale, or 1/sqrt(d) if <= 0): to
+ *   first order a score error ds_t moves the output by sum_t p_t ds_t (v_t - out) and a value
+ *   error e_t by sum_t p_t e_t, so with independent errors the two mean squares are
+ *   sum_t p_t^2 |v_t - out|^2 scale^2 D_K and sum_t p_t^2 D_V, and |v_t - out|^2 averages
+ *   tr(C_V) when the output sits near the values' mean.  Among values within 1e-12 (relative)
+ *   of the minimum the smallest B_K is taken.  The blobs' allocations are ignored: only their
+ *   sigma2 and max_bits are used, so any budget may have produced them; calibrate again with
+ *   bits_per_elem = B_K/d and B_V/d.
+ *   k_calib_host / v_calib_host: n_heads consecutive blobs each; k_weight: NULL or
+ *   [n_heads][d] fp64 (aatc_query_channel_weights of each head; NULL for NOVA keys, whose
+ *   coefficients already carry the query statistics).
+ *   Errors: a blob's aatc_calib_validate status; n_heads < 1, null pointers, a negative weight
+ *   -> INVALID_ARGUMENT; a non-finite weight -> NUMERICAL; total_bits outside
+ *   [0, d (max_bits_K + max_bits_V)] -> BUDGET.
+ */
+aatc_status aatc_joint_kv_split(const void* k_calib_host, const void* v_calib_host, int32_t n_heads,
+                                const double* k_weight, float softmax_scale, int32_t total_bits,
+                                int32_t* k_bits_out, int32_t* v_bits_out);
+
 /* Checks magic, version, d, checksum and internal consistency of a host blob. */
 aatc_status aatc_calib_validate(const void* calib_host, size_t calib_bytes);
 

@@ -225,6 +225,37 @@ def test_encode_unaligned_rows_and_wht_appends(dtype, cfg):
         assert torch.equal(cache.codes(t), cache2.codes(t))
 
 
+def test_joint_kv_split_cache():
+    """A layer calibrated with the joint K/V split (library: query weights, split, calibration at
+    B_K and B_V): the split equals the oracle's, K and V carry different bit counts, and decode
+    attention matches the oracle."""
+    torch = _torch()
+    from compressed_decode_attention_head_amd import api
+    probe = Case(cfg=2, n_kv=2, group=4, n_tokens=64, rotation="klt", bpe_k=2.0, aware=True)
+    kb = probe.blobs(synth.K)
+    vb = probe.blobs(synth.V)
+    w = np.stack([api.query_channel_weights(kb[h], probe.q_cal[h]) for h in range(2)])
+    bk, bv = api.joint_kv_split(kb, vb, 512, k_weight=w)
+    want = O.joint_kv_split([a["sigma2"] for a in probe.art[synth.K]], [a["sigma2"] for a in probe.art[synth.V]],
+                            [O.value_term_weight(a["C"]) for a in probe.art[synth.V]], 512,
+                            k_weight=[a["weight"] for a in probe.art[synth.K]])
+    assert (bk, bv) == want[:2] and bk != bv
+    case = Case(cfg=2, n_kv=2, group=4, n_tokens=500, rotation="klt", bpe_k=bk / 128, bpe_v=bv / 128, aware=True)
+    cache = case.make_cache()
+    assert (cache.k_bits, cache.v_bits) == (bk, bv)
+    for t in (synth.K, synth.V):
+        cache.encode(t, case.torch_x(t))
+    for t in (synth.K, synth.V):
+        _check_codes(case, cache, t)
+    out, lse = cache.decode_attn(torch.from_numpy(case.q.astype(np.float32)).cuda(), case.n)
+    torch.cuda.synchronize()
+    ref, lref = case.oracle_attention()
+    err = np.abs(out.cpu().numpy() - ref).max()
+    print("joint split", bk, bv, "attn max abs err", err, flush=True)
+    assert err <= ATOL_ATTN
+    assert np.abs(lse.cpu().numpy() - lref).max() <= 5e-3
+
+
 def test_zero_bit_tensors():
     """All K channels at 0 bits: uniform softmax; all V channels at 0 bits: output = mu_V."""
     torch = _torch()

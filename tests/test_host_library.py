@@ -172,6 +172,53 @@ def test_nova_errors(L):
     assert L.aatc_query_moment(None, 0, 4, 128, out.ctypes.data) == 1
 
 
+@pytest.mark.parametrize("cfg,rot,bpe,aware", [(2, "klt", 2.0, True), (4, "wht", 1.33, True), (3, "klt", 4.0, False)])
+def test_joint_kv_split_matches_oracle(cfg, rot, bpe, aware):
+    """The layer's K/V split: library (C++) against the oracle on the same blobs' statistics."""
+    n_kv = 3
+    calk = [_cal(cfg, h, synth.K) for h in range(n_kv)]
+    calv = [_cal(cfg, h, synth.V) for h in range(n_kv)]
+    kb = [api.calibrate(_bits16(c), rot, bpe) for c in calk]
+    vb = [api.calibrate(_bits16(c), rot, bpe) for c in calv]
+    ka = [O.calibrate(c, rot, bpe) for c in calk]
+    va = [O.calibrate(c, rot, bpe) for c in calv]
+    w = None
+    if aware:
+        rng = np.random.default_rng(cfg)
+        qs = [rng.standard_normal((400, 128)) * np.linspace(0.2, 3.0, 128) for _ in range(n_kv)]
+        w = np.stack([api.query_channel_weights(kb[h], qs[h]) for h in range(n_kv)])
+    T = 2 * O.bits_budget(bpe, 128)
+    got = api.joint_kv_split(kb, vb, T, k_weight=w)
+    want = O.joint_kv_split([a["sigma2"] for a in ka], [a["sigma2"] for a in va],
+                            [O.value_term_weight(a["C"]) for a in va], T,
+                            k_weight=None if w is None else list(w))
+    assert got == want[:2], (got, want)
+    assert sum(got) == T
+
+
+def test_joint_kv_split_errors(L):
+    x = _bits16(_cal(2, 0, synth.K))
+    kb = api.calibrate(x, "klt", 2.0)
+    with pytest.raises(N.AatcError) as e:
+        api.joint_kv_split([kb], [kb], 2049)
+    assert e.value.name == "AATC_ERR_BUDGET"
+    with pytest.raises(N.AatcError) as e:
+        api.joint_kv_split([kb], [kb], 256, k_weight=-np.ones((1, 128)))
+    assert e.value.name == "AATC_ERR_INVALID_ARGUMENT"
+    with pytest.raises(N.AatcError) as e:
+        api.joint_kv_split([kb], [kb], 256, k_weight=np.full((1, 128), np.nan))
+    assert e.value.name == "AATC_ERR_NUMERICAL"
+    bad = kb.copy()
+    bad[300] ^= 1
+    with pytest.raises(N.AatcError) as e:
+        api.joint_kv_split([kb], [bad], 256)
+    assert e.value.name == "AATC_ERR_BAD_ARTEFACT"
+    out = ctypes.c_int32()
+    assert L.aatc_joint_kv_split(kb.ctypes.data, kb.ctypes.data, 0, None, 0.0, 256, ctypes.byref(out),
+                                 ctypes.byref(out)) == 1
+    assert api.joint_kv_split([kb], [kb], 0) == (0, 0)
+
+
 def test_attention_aware_errors(L):
     x = _cal(2, 0, synth.K)
     blob = api.calibrate(_bits16(x), "klt", 2.0)
