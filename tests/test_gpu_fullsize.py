@@ -124,3 +124,57 @@ def test_fullsize_batch16_append_sampled():
     o, l = out.cpu().numpy(), lse.cpu().numpy()
     for i, (b, h) in enumerate(sorted(sampled)):
         _check_head(cfg, cache, q, host, arts, b, h, n, o, l, check_codes=(i == 0))
+
+
+def test_fullsize_nova_keys_joint_split():
+    """The 128K-token Qwen-shaped layer with the non-orthogonal key transform on K (query
+    second moments from 2048 calibration queries per head, scaled like the decode queries) and
+    the joint K/V split of 2 x 170 bits: library split equal to the oracle's, whole layer on the
+    GPU, KV heads 0 and 3 checked against the oracle (codes of head 0 too)."""
+    import torch
+    from compressed_decode_attention_head_amd import api
+    cfg = synth.CONFIGS[4]
+    n, n_kv = cfg.n_tokens, cfg.n_kv_heads
+    sampled = [(0, 0), (0, 3)]
+    cal = {t: [synth.draw(cfg.idx, 0, h, t, "calib", cfg.n_calib, dtype=cfg.dtype, marginal=cfg.marginal)
+               for h in range(n_kv)] for t in (synth.K, synth.V)}
+    q_cal = []
+    for h in range(n_kv):
+        qr = synth.draw(cfg.idx, 0, h, synth.K, "query", 2048, dtype="f64", extra=50000)
+        q_cal.append(qr * (2.0 / (cal[synth.K][h] @ qr.T / np.sqrt(128)).std(axis=0))[:, None])
+    moments = [api.query_moment(qc) for qc in q_cal]
+    total = 2 * O.bits_budget(cfg.bits_per_elem, 128)
+    kb0 = [api.calibrate(synth.bf16_bits(cal[synth.K][h]), "nova", cfg.bits_per_elem, query_moment=moments[h])
+           for h in range(n_kv)]
+    vb0 = [api.calibrate(synth.bf16_bits(c), cfg.rotation, cfg.bits_per_elem) for c in cal[synth.V]]
+    bk, bv = api.joint_kv_split(kb0, vb0, total)
+    ka0 = [O.calibrate(cal[synth.K][h], "nova", cfg.bits_per_elem, q_cal=q_cal[h]) for h in range(n_kv)]
+    va0 = [O.calibrate(c, cfg.rotation, cfg.bits_per_elem) for c in cal[synth.V]]
+    want = O.joint_kv_split([a["sigma2"] for a in ka0], [a["sigma2"] for a in va0],
+                            [O.value_term_weight(a["C"]) for a in va0], total)
+    assert (bk, bv) == want[:2], ((bk, bv), want)
+    blobs = {synth.K: [api.calibrate(synth.bf16_bits(cal[synth.K][h]), "nova", bk / 128, query_moment=moments[h])
+                       for h in range(n_kv)],
+             synth.V: [api.calibrate(synth.bf16_bits(c), cfg.rotation, bv / 128) for c in cal[synth.V]]}
+    arts = {synth.K: {h: O.calibrate(cal[synth.K][h], "nova", bk / 128, q_cal=q_cal[h]) for h in (0, 3)},
+            synth.V: {h: O.calibrate(cal[synth.V][h], cfg.rotation, bv / 128) for h in (0, 3)}}
+    cache = api.CompressedKVCache(blobs[synth.K], blobs[synth.V], 1, n)
+    host, keys_for_q = {}, {}
+    for t in (synth.K, synth.V):
+        x = torch.empty((1, n_kv, n, 128), dtype=torch.bfloat16, device="cuda")
+        for h in range(n_kv):
+            xh = synth.draw(cfg.idx, 0, h, t, "context", n, dtype=cfg.dtype, marginal=cfg.marginal)
+            x[0, h] = torch.from_numpy(xh.astype(np.float32)).to(torch.bfloat16)
+            if h in (0, 3):
+                host[(t, 0, h)] = xh
+            if t == synth.K:
+                keys_for_q[h] = xh[:4096]
+        cache.encode(t, x)
+        del x
+    q = synth.queries(cfg.idx, 0, cfg.n_q_heads, n_kv, [keys_for_q[h] for h in range(n_kv)])[None]
+    out, lse = cache.decode_attn(torch.from_numpy(q).cuda(), n)
+    torch.cuda.synchronize()
+    print("nova keys, joint split", bk, bv, flush=True)
+    o, l = out.cpu().numpy(), lse.cpu().numpy()
+    for i, (b, h) in enumerate(sampled):
+        _check_head(cfg, cache, q, host, arts, b, h, n, o, l, check_codes=(i == 0))
