@@ -12,7 +12,12 @@
  * fixed per-token bit count).  Decode attention reads the packed codes directly: the query
  * is rotated once, scores are formed in the rotated domain and values are dequantized and
  * rotated back only after the softmax-weighted sum (page "Ablation ...", OCTOPUS abstract:
- * keys are never materialised).
+ * keys are never materialised).  Also here:
+ *  - attention-aware key bits (query channel weights) and a joint K/V bit split (AATC
+ *    abstract);
+ *  - a non-orthogonal key transform from query statistics (NOVA-KV abstract);
+ *  - token tiers with multi-segment attention (RDKV abstract);
+ *  - a dense bf16 decode attention as the full-cache comparator.
  *
  * Conventions for every call:
  *  - Every call returns an aatc_status.  Arguments are validated on the host before any
@@ -267,7 +272,9 @@ int32_t aatc_calib_v_tiles(const void* calib_host);
  * aatc_encode -- device, async.  Quantizes and packs tokens [token_offset, token_offset +
  * n_tokens) of every (b,h) of tensor `which` (0 = K, 1 = V) into the cache.
  *   x_dev: element (b,h,t,j) at x_dev[b*strides[0] + h*strides[1] + t*strides[2] + j],
- *   t relative to token_offset; dtype F32 or BF16.  Rotation and quantization run in fp64.
+ *   t relative to token_offset; dtype F32 or BF16.  The blob's encoder y = E x (E = R except
+ *   for NOVA keys) and the quantizer run in fp64.  Any 16-byte aligned rows are read with
+ *   vector loads, others element by element; the result is the same.
  *   In every tile it touches, tokens before token_offset are preserved and tokens at or
  *   after token_offset + n_tokens are cleared to zero (append-only cache).
  *   Errors: bad which/dtype/pointers, token_offset < 0, n_tokens < 0, token_offset +
