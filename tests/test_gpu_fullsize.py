@@ -178,3 +178,72 @@ def test_fullsize_nova_keys_joint_split():
     o, l = out.cpu().numpy(), lse.cpu().numpy()
     for i, (b, h) in enumerate(sampled):
         _check_head(cfg, cache, q, host, arts, b, h, n, o, l, check_codes=(i == 0))
+
+
+@pytest.mark.parametrize("avg_bits", [2.76, 2.0])
+def test_fullsize_token_tiers_segments(avg_bits):
+    """The 128K-token tiered Llama-shaped layer (8 KV heads, 32 q heads) at its 2.76 bits per
+    element on average, and at 2.0, where tokens are also evicted: tiers from the library's solver on each head's Zipf attention mass (equal to the
+    oracle's for the sampled heads), tier-2 and tier-4 coded caches with their own bits and the
+    same rotation, raw bf16 tier-16 tokens, evicted tier-0 tokens; one multi-segment decode step
+    on the GPU, KV heads 0 and 5 (all 4 q heads each) against the oracle's segment attention."""
+    import torch
+    from compressed_decode_attention_head_amd import api
+    cfg = synth.CONFIGS[5]
+    n, n_kv, n_q = cfg.n_tokens, cfg.n_kv_heads, cfg.n_q_heads
+    group = n_q // n_kv
+    sampled = (0, 5)
+    cal = {t: [synth.draw(cfg.idx, 0, h, t, "calib", cfg.n_calib) for h in range(n_kv)] for t in (synth.K, synth.V)}
+    blobs = {(tau, t): [api.calibrate(synth.bf16_bits(c), "klt", float(tau)) for c in cal[t]]
+             for tau in (2, 4) for t in (synth.K, synth.V)}
+    x = {t: [synth.draw(cfg.idx, 0, h, t, "context", n) for h in range(n_kv)] for t in (synth.K, synth.V)}
+    tiers = []
+    for h in range(n_kv):
+        s2 = [api.calib_view(blobs[(2, t)][h])["sigma2"] for t in (synth.K, synth.V)]
+        tiers.append(api.token_tiers(synth.zipf_mass(cfg.idx, 0, h, n), api.tier_distortions(s2), avg_bits))
+    arts = {(tau, t): {h: O.calibrate(cal[t][h], "klt", float(tau)) for h in sampled} for tau in (2, 4)
+            for t in (synth.K, synth.V)}
+    for h in sampled:
+        dist = O.tier_distortions([arts[(2, synth.K)][h]["sigma2"], arts[(2, synth.V)][h]["sigma2"]], 128)
+        assert np.array_equal(tiers[h], O.token_tiers(synth.zipf_mass(cfg.idx, 0, h, n), dist, 128, avg_bits)), h
+    idx = {tau: [np.nonzero(tiers[h] == tau)[0] for h in range(n_kv)] for tau in (0, 2, 4, 16)}
+    assert all(len(idx[tau][h]) > 0 for tau in (2, 4, 16) for h in sampled)
+    assert (avg_bits >= 2.5) == all(len(idx[0][h]) == 0 for h in sampled)     # eviction at 2.0 only
+    q = synth.queries(cfg.idx, 0, n_q, n_kv, [x[synth.K][h][:4096] for h in range(n_kv)])
+    segs, keep = [], []
+    for tau in (2, 4, 16):
+        counts = [len(idx[tau][h]) for h in range(n_kv)]
+        cap = max(64, -(-max(counts) // 64) * 64)
+        sl = torch.tensor([counts], dtype=torch.int32, device="cuda")
+        xt = {}
+        for t in (synth.K, synth.V):
+            xt[t] = torch.zeros((1, n_kv, cap, 128), dtype=torch.bfloat16, device="cuda")
+            for h in range(n_kv):
+                xt[t][0, h, :counts[h]] = torch.from_numpy(x[t][h][idx[tau][h]].astype(np.float32)).to(torch.bfloat16)
+        if tau == 16:
+            keep += [xt[synth.K], xt[synth.V], sl]
+            segs.append({"k_raw": xt[synth.K], "v_raw": xt[synth.V], "seq_lens": sl, "max_seq_len": max(counts)})
+        else:
+            cache = api.CompressedKVCache(blobs[(tau, synth.K)], blobs[(tau, synth.V)], 1, cap)
+            for t in (synth.K, synth.V):
+                cache.encode(t, xt[t])
+            keep += [cache, sl]
+            segs.append({"cache": cache, "seq_lens": sl, "max_seq_len": max(counts)})
+        del xt
+    out, lse = api.decode_attn_segments(segs, torch.from_numpy(q[None]).cuda(), 1, n_kv)
+    torch.cuda.synchronize()
+    o, l = out[0].cpu().numpy(), lse[0].cpu().numpy()
+    for h in sampled:
+        parts = []
+        for tau in (2, 4):
+            ii = idx[tau][h]
+            rec = [O.reconstruct(O.encode_codes(x[t][h][ii], arts[(tau, t)][h]), arts[(tau, t)][h])
+                   for t in (synth.K, synth.V)]
+            parts.append((rec[0], rec[1]))
+        parts.append((x[synth.K][h][idx[16][h]], x[synth.V][h][idx[16][h]]))
+        for g in range(h * group, (h + 1) * group):
+            ref, lref = O.segment_attention(q[g], parts)
+            err, lerr = float(np.abs(o[g] - ref).max()), abs(float(l[g]) - lref)
+            print("tiers 128K head %d q %d: tokens per tier %s, max abs err %.2e, lse err %.2e"
+                  % (h, g, [len(idx[tau][h]) for tau in (0, 2, 4, 16)], err, lerr), flush=True)
+            assert err <= ATOL_ATTN and lerr <= 5e-3, (h, g, err, lerr)
