@@ -154,13 +154,24 @@ static_assert(2 * AATC_D * AATC_MAX_BITS * 4 <= kMc, "packed words fit the stagi
 
 // u = (y - o) * (1/Delta) + 2^(b-1) as separately rounded fp64 operations; code =
 // clamp(floor(u), 0, 2^b - 1), NaN -> 0.  On [0, 2^b - 1) truncation is the floor.
+// Branch-free: the clamp runs in fp64 (NaN fails u >= 0), so the conversion is always in range.
 __device__ inline int quantize(double y, double o, double inv, int bi) {
-  if (!bi) return 0;
   double u = (y - o) * inv;
-  u = u + static_cast<double>(1 << (bi - 1));
-  if (!(u >= 0.0)) return 0;
-  const int top = (1 << bi) - 1;
-  return u >= static_cast<double>(top) ? top : static_cast<int>(u);
+  u = u + static_cast<double>(1 << (bi > 0 ? bi - 1 : 0));
+  const double top = static_cast<double>((1 << bi) - 1);
+  const double uc = u >= 0.0 ? fmin(u, top) : 0.0;
+  return bi > 0 ? static_cast<int>(uc) : 0;
+}
+
+// The fp64 value of another lane of the same quad, by a DPP quad permutation (CTRL 0xB1: lane ^ 1,
+// 0x4E: lane ^ 2) of both halves: no LDS round trip.
+template <int CTRL>
+__device__ inline double quad_xor(double x) {
+  const unsigned long long u = static_cast<unsigned long long>(__double_as_longlong(x));
+  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(u & 0xffffffffu), CTRL, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(u >> 32), CTRL, 0xf, 0xf, false);
+  return __longlong_as_double(static_cast<long long>((static_cast<unsigned long long>(static_cast<unsigned>(hi)) << 32) |
+                                                     static_cast<unsigned>(lo)));
 }
 
 // Workgroup barrier that waits for this wave's LDS operations only (global loads stay in flight).
@@ -346,12 +357,15 @@ __device__ __attribute__((noinline)) void encode_tiles(const CodecArgs& a) {
             v[k + m] = x0 - x1;
           }
 #pragma unroll
-      for (int m = 1; m <= 2; m <<= 1)
+      for (int k = 0; k < 32; ++k) {
+        const double pv = quad_xor<0xB1>(v[k]);      // lane ^ 1
+        v[k] = (q4 & 1) ? pv - v[k] : v[k] + pv;
+      }
 #pragma unroll
-        for (int k = 0; k < 32; ++k) {
-          const double pv = __shfl_xor(v[k], m);
-          v[k] = (q4 & m) ? pv - v[k] : v[k] + pv;
-        }
+      for (int k = 0; k < 32; ++k) {
+        const double pv = quad_xor<0x4E>(v[k]);      // lane ^ 2
+        v[k] = (q4 & 2) ? pv - v[k] : v[k] + pv;
+      }
 #pragma unroll
       for (int k = 0; k < 32; ++k)
         cp[k >> 2] |= static_cast<uint32_t>(quantize(v[k] * rs, t_o[i0 + k], t_inv[i0 + k], t_bits[i0 + k]))
