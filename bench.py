@@ -86,9 +86,12 @@ def kernel_source_hash():
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic():
+def measured_traffic(cfg, n_tokens):
     """HBM bytes per launch of the cache pass from the committed counter summary, or None when
-    the summary is missing or was taken on another version of the kernel source."""
+    the summary is missing, was taken on another version of the kernel source, or covers
+    another workload (it covers the 128K Qwen-shaped layer)."""
+    if cfg.idx != 4 or n_tokens != cfg.n_tokens:
+        return None
     try:
         kv = {}
         with open(TRAFFIC_FILE) as f:
@@ -358,7 +361,7 @@ def main():
         part_ms * 1e3, merge_ms * 1e3, "graph of back-to-back launches" if part_graph_ms is not None else "eager",
         part_eager_ms * 1e3, merge_eager_ms * 1e3))
     achieved = codes_b / (part_ms * 1e-3) / 1e9
-    traffic = measured_traffic()
+    traffic = measured_traffic(cfg, n_tokens)
     if args.copy_calib:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

@@ -671,16 +671,22 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
     // scores, tile by tile as each lands: 4 token groups of 16 = 4 independent MFMA chains
 #pragma unroll
     for (int g = 0; g < TG; ++g) {
-      const int rr = g0 + (g < ng ? g : 0);             // past the group's end: recompute, masked
-      if (g < ng) {
-        if (NPROD > 0) {
-          // its own copies (the first SELF tiles) were waited for before the weights
-          if (g0 + g >= SELF) poll_ge(&sy.landed[wave], g0 + g + 1, &sy, lane);
-        } else {
-          wait_tile(g0 + g);
+      if (g >= ng) {                                    // past the group's end: no tile, masked
+#pragma unroll
+        for (int tau = 0; tau < 4; ++tau) {
+          sa[g][tau] = INT_MIN;
+          sb[g][tau] = INT_MIN;
         }
-        wave_sync_lds();
+        continue;
       }
+      const int rr = g0 + g;
+      if (NPROD > 0) {
+        // its own copies (the first SELF tiles) were waited for before the weights
+        if (g0 + g >= SELF) poll_ge(&sy.landed[wave], g0 + g + 1, &sy, lane);
+      } else {
+        wait_tile(g0 + g);
+      }
+      wave_sync_lds();
       const int64_t tile = tw0 + rr;
       // opaque slot offset: per-(tile, tau, pair) addresses are not worth registers
       int kt = static_cast<int>((slot_of(wave, rr) - ring) + ((reinterpret_cast<uintptr_t>(kseq) + tile * kbytes) & 15));
