@@ -36,6 +36,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true")
     p.add_argument("--no-dense", action="store_true", help="skip the dense bf16 comparator")
+    p.add_argument("--no-tiers", action="store_true", help="skip the tiered-layer measurement")
     p.add_argument("--quiet", action="store_true")
     p.add_argument("--copy-calib", action="store_true",
                    help="also run one plain 256 MiB device copy (scales HBM counters of a profiler run)")
@@ -205,6 +206,98 @@ def dense_comparator(args, cfg, n_tokens, qs, dev, st, ms_compressed_step):
             "us_per_layer": round(ms * 1e3 / len(qs), 3), "gbs": round(gbs, 1),
             "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
             "speedup_compressed_vs_dense": round(ms / ms_compressed_step, 3)}
+
+
+def tiered_segments(args, dev, st):
+    """One decode step over the 128K tiered Llama-shaped layers: token tiers (0 evicted, 2 and 4
+    bits coded, 16 raw bf16) from each KV head's Zipf attention mass at the workload's 2.76 bits
+    per element on average (the library's solver), tier-2 and tier-4 caches with their own bits
+    and the same rotation, one aatc_decode_attn_segments call per layer; graph replay over
+    n_layers independent layers.  Bytes are the compressed codes and raw rows the call reads."""
+    import torch
+    import synth
+    from compressed_decode_attention_head_amd import api
+    cfg = synth.CONFIGS[5]
+    n, n_kv, n_q, n_layers = cfg.n_tokens, cfg.n_kv_heads, cfg.n_q_heads, cfg.n_layers
+    K, V = synth.K, synth.V
+    calls, keep = [], []
+    total_bytes, pop = 0, {0: 0, 2: 0, 4: 0, 16: 0}
+    for l in range(n_layers):
+        blobs = {(tau, t): [api.calibrate(synth.bf16_bits(synth.draw(cfg.idx, l, h, t, "calib", cfg.n_calib)), "klt",
+                                          float(tau)) for h in range(n_kv)] for tau in (2, 4) for t in (K, V)}
+        tiers = []
+        for h in range(n_kv):
+            s2 = [api.calib_view(blobs[(2, t)][h])["sigma2"] for t in (K, V)]
+            tiers.append(api.token_tiers(synth.zipf_mass(cfg.idx, l, h, n), api.tier_distortions(s2),
+                                         cfg.bits_per_elem))
+        ctx = {t: [synth.draw_device(cfg.idx, l, h, t, n, device=dev) for h in range(n_kv)] for t in (K, V)}
+        ksample = [ctx[K][h][:4096].float().cpu().numpy() for h in range(n_kv)]
+        segs = []
+        for tau in (0, 2, 4, 16):
+            pop[tau] += int(sum((tr == tau).sum() for tr in tiers))
+        for tau in (2, 4, 16):
+            idx = [torch.from_numpy(np.nonzero(tiers[h] == tau)[0]).to(dev) for h in range(n_kv)]
+            counts = [int(i.numel()) for i in idx]
+            cap = max(64, -(-max(counts) // 64) * 64)
+            sl = torch.tensor([counts], dtype=torch.int32, device=dev)
+            xt = {}
+            for t in (K, V):
+                xt[t] = torch.zeros((1, n_kv, cap, 128), dtype=torch.bfloat16, device=dev)
+                for h in range(n_kv):
+                    xt[t][0, h, :counts[h]] = ctx[t][h].index_select(0, idx[h])
+            if tau == 16:
+                segs.append({"k_raw": xt[K], "v_raw": xt[V], "seq_lens": sl, "max_seq_len": max(counts)})
+                keep += [xt[K], xt[V], sl]
+                total_bytes += sum(counts) * 2 * 128 * 2
+            else:
+                cache = api.CompressedKVCache(blobs[(tau, K)], blobs[(tau, V)], 1, cap, device=dev)
+                for t in (K, V):
+                    cache.encode(t, xt[t])
+                segs.append({"cache": cache, "seq_lens": sl, "max_seq_len": max(counts)})
+                keep += [cache, sl]
+                total_bytes += sum(counts) * (cache.k_bits + cache.v_bits) // 8
+                del xt
+        del ctx
+        q = torch.from_numpy(synth.queries(cfg.idx, l, n_q, n_kv, ksample)[None]).to(dev)
+        ws = torch.empty(api.decode_attn_segments_workspace_bytes(segs, 1, n_kv, n_q), dtype=torch.uint8, device=dev)
+        out = torch.empty_like(q)
+        lse = torch.empty((1, n_q), dtype=torch.float32, device=dev)
+        calls.append((segs, q, ws, out, lse))
+    torch.cuda.synchronize()
+
+    def tstep():
+        for segs, q, ws, out, lse in calls:
+            api.decode_attn_segments(segs, q, 1, n_kv, workspace=ws, out=out, lse=lse)
+
+    runner = tstep
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        s2 = torch.cuda.Stream()
+        s2.wait_stream(st)
+        with torch.cuda.stream(s2):
+            tstep()
+        st.wait_stream(s2)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            tstep()
+        runner = g.replay
+    for _ in range(args.warmup):
+        runner()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(args.steps):
+        runner()
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    tot = sum(pop.values())
+    return {"workload": cfg.name, "layers_per_step": n_layers, "avg_bits": cfg.bits_per_elem,
+            "tier_fractions": {str(t): round(pop[t] / tot, 4) for t in (0, 2, 4, 16)},
+            "bytes_per_step": total_bytes, "ms_per_step": round(ms, 4),
+            "us_per_layer": round(ms * 1e3 / n_layers, 3), "gbs": round(total_bytes / (ms * 1e-3) / 1e9, 1),
+            "calls": "aatc_decode_attn_segments: cache pass + merge per coded tier, dense pass for raw, "
+                     "one state merge"}
 
 
 def main():
@@ -403,6 +496,11 @@ def main():
         res["dense_bf16"] = dense_comparator(args, cfg, n_tokens, [lay[1] for lay in layers], dev, st, ms_step)
         log(args, "dense bf16: %.2f us per layer, %.0f GB/s; compressed step is %.2fx faster" % (
             res["dense_bf16"]["us_per_layer"], res["dense_bf16"]["gbs"], res["dense_bf16"]["speedup_compressed_vs_dense"]))
+    if not args.no_tiers:
+        log(args, "timing the tiered 128K layer")
+        res["tiers"] = tiered_segments(args, dev, st)
+        log(args, "tiers: %.2f us per layer, %.0f GB/s, tier fractions %s" % (
+            res["tiers"]["us_per_layer"], res["tiers"]["gbs"], res["tiers"]["tier_fractions"]))
     if not args.no_cpu_baseline:
         log(args, "timing the oracle on the host")
         res["cpu_baseline"] = cpu_baseline(cfg, n_tokens)

@@ -141,14 +141,8 @@ def token_tiers(attn_mass, dist, avg_bits, d=128):
     return out
 
 
-def decode_attn_segments(segments, q, batch, n_kv_heads, scale=0.0, workspace=None, out=None, lse=None,
-                         stream=None):
-    """aatc_decode_attn_segments.  segments: list of dicts, each either
-    {"cache": CompressedKVCache, "seq_lens": int32 [batch, n_kv] tensor, "max_seq_len": n} or
-    {"k_raw": bf16 [batch, n_kv, cap, 128], "v_raw": same, "seq_lens": ..., "max_seq_len": n}."""
+def _segments_struct(segments, batch, n_kv_heads):
     import torch
-    if q.dtype != torch.float32 or not q.is_contiguous() or q.dim() != 3 or q.shape[0] != batch:
-        raise ValueError("q must be a contiguous fp32 [batch, n_q_heads, 128] tensor")
     arr = (N.Segment * len(segments))()
     keep = []
     for i, sg in enumerate(segments):
@@ -168,6 +162,27 @@ def decode_attn_segments(segments, q, batch, n_kv_heads, scale=0.0, workspace=No
                 raise ValueError("raw segments are contiguous bf16 [batch, n_kv_heads, capacity, 128] tensors")
             arr[i].k_raw, arr[i].v_raw = k.data_ptr(), v.data_ptr()
             arr[i].raw_capacity = k.shape[2]
+    return arr, keep
+
+
+def decode_attn_segments_workspace_bytes(segments, batch, n_kv_heads, n_q_heads):
+    """aatc_decode_attn_segments_workspace_bytes for the same segment list as decode_attn_segments."""
+    arr, _keep = _segments_struct(segments, batch, n_kv_heads)
+    need = N.lib().aatc_decode_attn_segments_workspace_bytes(arr, len(segments), batch, n_kv_heads, n_q_heads)
+    if need == 0:
+        raise ValueError("invalid segments: " + N.lib().aatc_last_error().decode())
+    return need
+
+
+def decode_attn_segments(segments, q, batch, n_kv_heads, scale=0.0, workspace=None, out=None, lse=None,
+                         stream=None):
+    """aatc_decode_attn_segments.  segments: list of dicts, each either
+    {"cache": CompressedKVCache, "seq_lens": int32 [batch, n_kv] tensor, "max_seq_len": n} or
+    {"k_raw": bf16 [batch, n_kv, cap, 128], "v_raw": same, "seq_lens": ..., "max_seq_len": n}."""
+    import torch
+    if q.dtype != torch.float32 or not q.is_contiguous() or q.dim() != 3 or q.shape[0] != batch:
+        raise ValueError("q must be a contiguous fp32 [batch, n_q_heads, 128] tensor")
+    arr, _keep = _segments_struct(segments, batch, n_kv_heads)
     n_q = q.shape[1]
     L = N.lib()
     need = L.aatc_decode_attn_segments_workspace_bytes(arr, len(segments), batch, n_kv_heads, n_q)
