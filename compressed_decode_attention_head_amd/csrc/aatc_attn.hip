@@ -255,8 +255,19 @@ struct SegPlan {
   size_t states_off, lse_off, attn_off, attn_bytes, total;
 };
 
-int64_t raw_chunks(const aatc_segment& sg) {
-  return (sg.max_seq_len + aatc_dense::CHUNK - 1) / aatc_dense::CHUNK;
+// Tokens per dense workgroup: the longest chunk, halved (down to one block per wave) while the
+// launch would have fewer workgroups than the chip has compute units.
+int raw_chunk(const aatc_segment& sg, int32_t batch, int32_t n_kv) {
+  int chunk = aatc_dense::CHUNK;
+  const int64_t seqs = static_cast<int64_t>(batch) * n_kv;
+  while (chunk > aatc_dense::MIN_CHUNK && (sg.max_seq_len + chunk - 1) / chunk * seqs < 256) chunk >>= 1;
+  return chunk;
+}
+
+int64_t raw_chunks(const aatc_segment& sg, int32_t batch, int32_t n_kv) {
+  const int chunk = raw_chunk(sg, batch, n_kv);
+  const int64_t nc = (sg.max_seq_len + chunk - 1) / chunk;
+  return nc > 0 ? nc : 1;
 }
 
 aatc_status seg_plan(const aatc_segment* segs, int32_t n_segs, int32_t batch, int32_t n_kv, int32_t n_q,
@@ -283,7 +294,7 @@ aatc_status seg_plan(const aatc_segment* segs, int32_t n_segs, int32_t batch, in
         return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "segment %d: max_seq_len > raw_capacity", s);
       if ((reinterpret_cast<uintptr_t>(sg.k_raw) & 15) || (reinterpret_cast<uintptr_t>(sg.v_raw) & 15))
         return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "segment %d: raw tensors must be 16-byte aligned", s);
-      states += raw_chunks(sg) > 0 ? raw_chunks(sg) : 1;
+      states += raw_chunks(sg, batch, n_kv);
     }
   }
   if (states > (1 << 20)) return aatc::fail(AATC_ERR_UNSUPPORTED, "too many segment states");
@@ -367,7 +378,8 @@ aatc_status aatc_decode_attn_segments(const aatc_segment* segs, int32_t n_segs, 
       ra.lse_states = lse_states;
       ra.state0 = state;
       ra.bq = bq;
-      const int64_t nc = raw_chunks(sg) > 0 ? raw_chunks(sg) : 1;
+      ra.chunk = raw_chunk(sg, batch, n_kv);
+      const int64_t nc = raw_chunks(sg, batch, n_kv);
       hipLaunchKernelGGL(aatc_dense::k_dense_attn, dim3(static_cast<unsigned>(nc), n_kv, batch),
                          dim3(aatc_dense::NW * 64), 0, st, ra);
       const hipError_t e = hipGetLastError();

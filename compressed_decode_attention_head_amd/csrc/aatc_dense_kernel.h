@@ -3,8 +3,8 @@
 //
 // Page "SPHERICAL KV ..." (RDKV abstract): the full-precision cache that the compressed cache
 // is measured against is re-read from HBM at every decode step.  This is that step for a bf16
-// cache [batch][n_kv][capacity][128]: each workgroup takes CHUNK consecutive tokens of one
-// (batch, KV head) and all q heads of its GQA group, and writes one split-softmax state per q
+// cache [batch][n_kv][capacity][128]: each workgroup takes a chunk of consecutive tokens of one
+// (batch, KV head) -- CHUNK, or a power-of-two fraction of it for short segments -- and all q heads of its GQA group, and writes one split-softmax state per q
 // head (normalised output and log-sum-exp); k_merge_states merges the states.
 //
 // One wave handles 32 tokens per step on v_mfma_f32_16x16x32_bf16:
@@ -32,7 +32,8 @@ namespace aatc_dense {
 
 constexpr int D = AATC_D;
 constexpr int NW = 8;                      // waves per workgroup
-constexpr int CHUNK = 2048;                // tokens per workgroup (one state per q head)
+constexpr int CHUNK = 2048;                // longest token chunk per workgroup (one state per q head)
+constexpr int MIN_CHUNK = NW * 32;         // one 32-token block per wave
 constexpr int MAXG = AATC_MAX_GROUP;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -50,6 +51,7 @@ struct DenseArgs {
   float* out_states;                     // [n_states][batch * n_q][128]
   float* lse_states;                     // [n_states][batch * n_q]
   int state0;                            // state index of chunk 0
+  int chunk;                             // tokens per workgroup: MIN_CHUNK * 2^i <= CHUNK
   int64_t bq;                            // batch * n_q
 };
 
@@ -108,8 +110,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 8)))
   const int64_t bh = static_cast<int64_t>(b) * a.n_kv + h;
   int64_t seq = a.seq_lens ? static_cast<int64_t>(a.seq_lens[bh]) : a.max_seq;
   seq = seq < 0 ? 0 : (seq > a.max_seq ? a.max_seq : seq);
-  const int64_t t_begin = static_cast<int64_t>(c) * CHUNK;
-  const int nt = seq - t_begin <= 0 ? 0 : (seq - t_begin < CHUNK ? static_cast<int>(seq - t_begin) : CHUNK);
+  const int64_t t_begin = static_cast<int64_t>(c) * a.chunk;
+  const int nt = seq - t_begin <= 0 ? 0 : (seq - t_begin < a.chunk ? static_cast<int>(seq - t_begin) : a.chunk);
 
   // query operand: column g, contraction d = 32 kk + 8 qq + 0..7, scaled, split hi + lo
   uint4 qh[4], ql[4];

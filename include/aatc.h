@@ -403,7 +403,8 @@ size_t aatc_decode_attn_segments_workspace_bytes(const aatc_segment* segs, int32
  * RDKV abstract; softmax is order-invariant, so the union is the log-sum-exp merge of
  * per-segment states]  Coded segments run the cache pass and merge of aatc_decode_attn with
  * per-(b,h) lengths; raw segments run the dense bf16 pass of aatc_decode_attn_dense in
- * 2048-token chunks; one final kernel merges all states.  q (16-byte aligned), out, lse, scale
+ * token chunks of 2048, halved (down to 256) while fewer than 256 workgroups would run; one
+ * final kernel merges all states.  q (16-byte aligned), out, lse, scale
  * and GQA mapping as aatc_decode_attn.
  *   Errors: as aatc_decode_attn, per segment; caches whose batch or n_kv_heads differ from the
  *   call, misaligned q -> INVALID_ARGUMENT; batch or n_kv_heads > 65535 -> UNSUPPORTED;
@@ -432,7 +433,8 @@ size_t aatc_decode_attn_dense_workspace_bytes(int32_t batch, int32_t n_kv_heads,
  *   Scores use q as a bf16 high part plus a bf16 low part and the probabilities likewise, with
  *   fp32 accumulation; K and V enter exactly.
  *   workspace_dev: >= aatc_decode_attn_dense_workspace_bytes(...) bytes, 256-byte aligned, no
- *   initialisation needed; one state per 2048-token chunk and q head.
+ *   initialisation needed; one state per token chunk (2048 tokens, or down to 256 when fewer
+ *   than 256 workgroups would run) and q head.
  *   Errors: as aatc_decode_attn_segments with one raw segment.
  */
 aatc_status aatc_decode_attn_dense(const void* k_dev, const void* v_dev, int32_t batch,

@@ -69,8 +69,10 @@ def _check(k, v, q, out, lse, lens):
 
 
 @pytest.mark.parametrize("batch,n_kv,group,n_tokens,cap,ragged", [
-    (1, 2, 7, 5000, 5005, False),        # three 2048-token chunks, a ragged 32-token block at the end
-    (1, 1, 1, 2049, 2049, False),        # one token past a chunk boundary, group of 1
+    (1, 2, 7, 5000, 5005, False),        # 20 chunks of 256 tokens, a ragged 32-token block at the end
+    (1, 1, 1, 2049, 2049, False),        # one token past a 256-token chunk boundary, group of 1
+    (4, 8, 2, 9000, 9000, False),        # 1024-token chunks (2048 would give 160 workgroups)
+    (8, 8, 1, 8200, 8256, False),        # 2048-token chunks (320 workgroups), ragged last chunk
     (1, 1, 8, 4096, 4096, False),        # group of 8
     (1, 3, 3, 64, 70, False),
     (2, 2, 4, 2100, 2112, True),         # per-(b,h) lengths 0, 1, 33, 2100

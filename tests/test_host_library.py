@@ -392,12 +392,15 @@ def test_token_tiers_errors(L):
 
 
 def test_dense_workspace_bytes(L):
-    """One state per 2048-token chunk and q head: [states][batch*n_q][128] fp32 outputs, then
-    [states][batch*n_q] fp32 lse, each padded to 256 bytes."""
+    """One state per token chunk and q head: [states][batch*n_q][128] fp32 outputs, then
+    [states][batch*n_q] fp32 lse, each padded to 256 bytes.  Chunks hold 2048 tokens, halved
+    down to 256 while the grid (chunks x batch x KV heads) is below 256 workgroups."""
     def al(x):
         return -(-x // 256) * 256
-    for b, n_kv, n_q, n in ((1, 4, 28, 131072), (2, 2, 8, 3000), (1, 1, 1, 0), (3, 1, 8, 2048)):
-        states, bq = max(1, -(-n // 2048)), b * n_q
+    for b, n_kv, n_q, n, chunk in ((1, 4, 28, 131072, 2048), (2, 2, 8, 3000, 256), (1, 1, 1, 0, 256),
+                                   (3, 1, 8, 2048, 256), (4, 8, 16, 9000, 1024), (8, 8, 8, 8200, 2048),
+                                   (1, 8, 32, 3700, 256), (1, 4, 28, 65536, 1024)):
+        states, bq = max(1, -(-n // chunk)), b * n_q
         assert L.aatc_decode_attn_dense_workspace_bytes(b, n_kv, n_q, n) == al(states * bq * 512) + al(states * bq * 4)
     assert L.aatc_decode_attn_dense_workspace_bytes(1, 4, 30, 100) == 0      # 30 q heads over 4 KV heads
     assert L.aatc_decode_attn_dense_workspace_bytes(1, 1, 9, 100) == 0       # group of 9
