@@ -375,3 +375,26 @@ def test_segments_tiers_match_oracle(avg_bits):
     print("segments", avg_bits, [[len(i) for i in idx[tau]] for tau in (0, 2, 4, 16)], "err", err, lerr, flush=True)
     assert err <= ATOL_ATTN, err
     assert lerr <= 5e-3, lerr
+
+    # the same call captured in a graph, replayed with eager work (another call, which reuses
+    # nothing of the graph's buffers) between the replays, equals the eager result
+    ws = torch.empty(api.decode_attn_segments_workspace_bytes(segs, 1, n_kv, n_q), dtype=torch.uint8, device="cuda")
+    go, gl = torch.empty_like(out), torch.empty_like(lse)
+    s2 = torch.cuda.Stream()
+    s2.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s2):
+        api.decode_attn_segments(segs, qt, 1, n_kv, workspace=ws, out=go, lse=gl)
+    torch.cuda.current_stream().wait_stream(s2)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        api.decode_attn_segments(segs, qt, 1, n_kv, workspace=ws, out=go, lse=gl)
+    for rep in range(3):
+        go.fill_(float("nan"))
+        gl.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(go, out) and torch.equal(gl, lse), rep
+        api.decode_attn_segments(segs, qt * 0.5, 1, n_kv)
+        torch.cuda.synchronize()
+    print("segments graph replays equal the eager call", flush=True)
