@@ -296,6 +296,7 @@ def tiered_segments(args, dev, st):
             "tier_fractions": {str(t): round(pop[t] / tot, 4) for t in (0, 2, 4, 16)},
             "bytes_per_step": total_bytes, "ms_per_step": round(ms, 4),
             "us_per_layer": round(ms * 1e3 / n_layers, 3), "gbs": round(total_bytes / (ms * 1e-3) / 1e9, 1),
+            "frac_of_peak": round(total_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "calls": "aatc_decode_attn_segments: cache pass + merge per coded tier, dense pass for raw, "
                      "one state merge"}
 
