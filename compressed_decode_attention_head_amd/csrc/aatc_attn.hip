@@ -126,9 +126,9 @@ aatc_status check_and_plan(const aatc_cache* c, int32_t n_q, int64_t max_seq, vo
   if (n_q % c->n_kv_heads) return aatc::fail(AATC_ERR_UNSUPPORTED, "n_q_heads %% n_kv_heads != 0");
   const int group = n_q / c->n_kv_heads;
   if (group > AATC_MAX_GROUP) return aatc::fail(AATC_ERR_UNSUPPORTED, "GQA group %d > 8", group);
-  if (c->k_bits < 0 || c->k_bits > 512 || c->v_bits < 0 || c->v_bits > 512)
-    return aatc::fail(AATC_ERR_UNSUPPORTED, "k_bits %d / v_bits %d: decode attention handles 0..512 bits per vector",
-                      c->k_bits, c->v_bits);
+  if (c->k_bits < 0 || c->k_bits > AATC_MAX_ATTN_BITS || c->v_bits < 0 || c->v_bits > AATC_MAX_ATTN_BITS)
+    return aatc::fail(AATC_ERR_UNSUPPORTED, "k_bits %d / v_bits %d: decode attention handles 0..%d bits per vector",
+                      c->k_bits, c->v_bits, AATC_MAX_ATTN_BITS);
   if (vtiles_bucket(c->v_tiles) < 0 || c->v_tiles < 0)
     return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "v_tiles %d", c->v_tiles);
   if (!c->k_calib || !c->v_calib || (!c->k_codes && c->k_bits > 0) || (!c->v_codes && c->v_bits > 0))

@@ -1,7 +1,7 @@
 // Decode attention that reads the packed cache directly (gfx950): two kernels per step.
 //
 // Page "SPECTRA ..." (Abstract) and page "SPHERICAL KV ..." (RDKV abstract): the cache is
-// re-read in full at every generated token, so decode is bound by HBM reads of the cache;
+// read again in full for each new token, so decode is bound by HBM reads of the cache;
 // page "Ablation ..." (OCTOPUS abstract): keys are reconstructed on the fly, never
 // materialised.  Here nothing is reconstructed per token at all:
 //
@@ -53,7 +53,8 @@ constexpr int PS = 16383;                 // probability scale: 14-bit fixed poi
 // log2(16383 / 65535) - 2^-20: pknorm(x) = rint(65535 x), so a token at the running max maps
 // to 16383 and none exceeds it
 constexpr float PKN_BIAS = -2.000067f;
-constexpr int PHDR = 4;                   // record header floats: max (log2 units), sum, 0, 0
+constexpr int PHDR = 4;                   // record header floats: max (log2 units), sum of the
+                                          // rounded probabilities, sum of the unrounded ones, 0
 constexpr int CW = 8;                     // waves per workgroup
 constexpr int TG = 4;                     // at most this many tiles per score group
 constexpr int UNION_BYTES = 2 * 8 * D * 4;    // q / q~
@@ -110,6 +111,14 @@ __device__ inline int row_max16_i(int x) {
   x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x122, 0xf, 0xf, false));
   x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x124, 0xf, 0xf, false));
   x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x128, 0xf, 0xf, false));
+  return x;
+}
+
+__device__ inline float row_sum16_f(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xf, 0xf, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xf, 0xf, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xf, 0xf, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));
   return x;
 }
 
@@ -272,6 +281,35 @@ __device__ inline void poll_ge(const int* p, int v, Sync* sy, int lane) {
   if (lane == 0) lds_store(&sy->broken, 1);
 }
 
+// Whole-power-of-two step that keeps a group's maximum mx below a reference of im * es + sh
+// (log2 units, im an integer score anchor): 0 when it already is, else the k with
+// im * es + sh + k >= mx * es + 2^-16 (the margin absorbs the rounding of the product).
+__device__ inline int ref_shift(int mx, int im, float es, int sh) {
+  if (mx == INT_MIN || im == INT_MIN) return 0;
+  const float x = static_cast<float>(mx - im) * es - static_cast<float>(sh) + 1.52587890625e-5f;
+  return x > 0.f ? static_cast<int>(ceilf(x)) : 0;
+}
+
+// x / 2^k rounded to nearest (k >= 0; 0 for k >= 32).
+__device__ inline unsigned shift_round(unsigned x, int k) {
+  if (k <= 0) return x;
+  if (k >= 32) return 0u;
+  return static_cast<unsigned>((static_cast<uint64_t>(x) + (1ull << (k - 1))) >> k);
+}
+
+// Exact rescale by 2^-k of a probability-weighted code sum held as two limbs: lanes 0..31 hold
+// the high limb (weight 128) and lane + 32 the low limb of the same (head, column).  The pair is
+// recombined, divided with one rounding and split again (high = value / 128, low = value % 128);
+// the value 128 * high + low stays below 2^31 while a wave streams at most 64 tiles.
+__device__ inline int shift_limbs(int x, int k, int lane) {
+  const auto p = __builtin_amdgcn_permlane32_swap(static_cast<unsigned>(x), static_cast<unsigned>(x), false, false);
+  const unsigned partner = lane < 32 ? p[1] : p[0];
+  const unsigned hi = lane < 32 ? static_cast<unsigned>(x) : partner;
+  const unsigned lo = lane < 32 ? partner : static_cast<unsigned>(x);
+  const unsigned v = shift_round((hi << 7) + lo, k);
+  return static_cast<int>(lane < 32 ? (v >> 7) : (v & 127u));
+}
+
 // Plane base (within a token's B-bit string) of the K window that lane group `grp` reads for
 // MFMA pair u; a half pair (last pair with <= 64 planes) interleaves 4-plane groups so that
 // one MFMA covers 64 planes.
@@ -336,7 +374,7 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
   // probability limb rows live in their own static array: no tile copy can write them, so
   // reading them needs no wait on the copies in flight
   __shared__ __align__(16) uint8_t pl[CW * TG * PROW_BYTES];        // [CW][TG][16][64]
-  __shared__ float s_m[CW][8], s_l[CW][8];
+  __shared__ float s_m[CW][8], s_l[CW][8], s_e[CW][8];
   __shared__ float esc[8];
   __shared__ Sync sy;
 
@@ -504,8 +542,11 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
   v4i acc[NVB];
 #pragma unroll
   for (int v = 0; v < NVB; ++v) acc[v] = v4i{0, 0, 0, 0};
-  int ima = INT_MIN, imb = INT_MIN;       // running integer score maxima (INT_MIN: none yet)
-  unsigned la = 0, lb = 0;
+  int ima = INT_MIN, imb = INT_MIN;       // integer score anchors: the first group's maxima
+  int sha = 0, shb = 0;                   // reference = anchor (log2 units) + this power of two
+  float bia = PKN_BIAS, bib = PKN_BIAS;   // PKN_BIAS - sha, PKN_BIAS - shb
+  unsigned la = 0, lb = 0;               // sums of the rounded probabilities (PV's weights)
+  float ea = 0.f, eb = 0.f;               // sums of the unrounded ones (for the lse)
   const v2u16 ones = {1, 1};
 
   int phase = 0;
@@ -758,46 +799,45 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
     }
     mxa = row_max16_i(mxa);
     if (LIMBS == 2) mxb = row_max16_i(mxb);
-    // online softmax: rescale the integer accumulators when a running max grows
-    if (__ballot(mxa > ima || mxb > imb)) {
-      const int nma = max(ima, mxa), nmb = max(imb, mxb);
-      if (started) {
-        const float fa = __builtin_amdgcn_exp2f(static_cast<float>(ima - nma) * esa);
-        const float fb = LIMBS == 2 ? __builtin_amdgcn_exp2f(static_cast<float>(imb - nmb) * esb) : 0.f;
-        la = static_cast<unsigned>(rintf(static_cast<float>(la) * fa));
-        lb = static_cast<unsigned>(rintf(static_cast<float>(lb) * fb));
-        float fr[4];
+    // online softmax.  The first group anchors each head's reference at its integer maximum;
+    // a later group whose maximum passes the reference raises it by a whole power of two, so
+    // that the accumulators are rescaled exactly (no rounding of the high limb on its own)
+    if (!started) {
+      ima = mxa;
+      imb = mxb;
+      started = true;
+    } else {
+      const int ka = ref_shift(mxa, ima, esa, sha);
+      const int kb = LIMBS == 2 ? ref_shift(mxb, imb, esb, shb) : 0;
+      if (__ballot((ka | kb) != 0)) {
+        la = shift_round(la, ka);
+        lb = shift_round(lb, kb);
+        ea = ldexpf(ea, -ka);
+        eb = ldexpf(eb, -kb);
+        int kr[4];
         if (LIMBS == 2) {
-          // acc register r of lane group grp holds head 4*(grp&1)+r; the factor of head hd
+          // acc register r of lane group grp holds head 4*(grp&1)+r; the shift of head hd
           // lives in pair a (heads {0,4,1,5} in lane groups 0..3) or pair b ({2,6,3,7})
-          const float f0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fa), 0));
-          const float f4 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fa), 16));
-          const float f1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fa), 32));
-          const float f5 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fa), 48));
-          const float f2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fb), 0));
-          const float f6 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fb), 16));
-          const float f3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fb), 32));
-          const float f7 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fb), 48));
           const bool odd = grp & 1;
-          fr[0] = odd ? f4 : f0;
-          fr[1] = odd ? f5 : f1;
-          fr[2] = odd ? f6 : f2;
-          fr[3] = odd ? f7 : f3;
+          kr[0] = odd ? __builtin_amdgcn_readlane(ka, 16) : __builtin_amdgcn_readlane(ka, 0);
+          kr[1] = odd ? __builtin_amdgcn_readlane(ka, 48) : __builtin_amdgcn_readlane(ka, 32);
+          kr[2] = odd ? __builtin_amdgcn_readlane(kb, 16) : __builtin_amdgcn_readlane(kb, 0);
+          kr[3] = odd ? __builtin_amdgcn_readlane(kb, 48) : __builtin_amdgcn_readlane(kb, 32);
         } else {
-          // acc register r holds head r (rows 8l + r); head r's factor lives in lane group r
+          // acc register r holds head r (rows 8l + r); head r's shift lives in lane group r
 #pragma unroll
-          for (int r = 0; r < 4; ++r) fr[r] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fa), 16 * r));
+          for (int r = 0; r < 4; ++r) kr[r] = __builtin_amdgcn_readlane(ka, 16 * r);
         }
 #pragma unroll
         for (int v = 0; v < NVB; ++v)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            acc[v][r] = static_cast<int>(rintf(static_cast<float>(acc[v][r]) * fr[r]));
+          for (int r = 0; r < 4; ++r) acc[v][r] = shift_limbs(acc[v][r], kr[r], lane);
+        sha += ka;
+        shb += kb;
+        bia = PKN_BIAS - static_cast<float>(sha);
+        bib = PKN_BIAS - static_cast<float>(shb);
       }
-      ima = nma;
-      imb = nmb;
     }
-    started = true;
     // probabilities in 14-bit fixed point (pknorm rounds 65535 * x), two 7-bit limbs; the
     // four tokens of this lane fill one dword per (head, limb); tile g uses rows at g*1024
 #pragma unroll
@@ -808,7 +848,7 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
           float pa[4];
 #pragma unroll
           for (int tau = 0; tau < 4; ++tau)
-            pa[tau] = __builtin_amdgcn_exp2f(fmaf(static_cast<float>(sa[g][tau] - ima), esa, PKN_BIAS));
+            pa[tau] = __builtin_amdgcn_exp2f(fmaf(static_cast<float>(sa[g][tau] - ima), esa, bia));
           if (masked) {
 #pragma unroll
             for (int tau = 0; tau < 4; ++tau) pa[tau] = sa[g][tau] == INT_MIN ? 0.f : pa[tau];
@@ -817,6 +857,7 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
           const v2u16 q23 = __builtin_amdgcn_cvt_pknorm_u16(pa[2], pa[3]);
           la = __builtin_amdgcn_udot2(q01, ones, la, false);
           la = __builtin_amdgcn_udot2(q23, ones, la, false);
+          ea += (pa[0] + pa[1]) + (pa[2] + pa[3]);
           const uint32_t u01 = __builtin_bit_cast(uint32_t, q01), u23 = __builtin_bit_cast(uint32_t, q23);
           *reinterpret_cast<uint32_t*>(pg + wa0) =
               __builtin_amdgcn_perm((u23 >> 7) & 0x007F007Fu, (u01 >> 7) & 0x007F007Fu, 0x06040200u);
@@ -826,7 +867,7 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
           float pb[4];
 #pragma unroll
           for (int tau = 0; tau < 4; ++tau)
-            pb[tau] = __builtin_amdgcn_exp2f(fmaf(static_cast<float>(sb[g][tau] - imb), esb, PKN_BIAS));
+            pb[tau] = __builtin_amdgcn_exp2f(fmaf(static_cast<float>(sb[g][tau] - imb), esb, bib));
           if (masked) {
 #pragma unroll
             for (int tau = 0; tau < 4; ++tau) pb[tau] = sb[g][tau] == INT_MIN ? 0.f : pb[tau];
@@ -835,6 +876,7 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
           const v2u16 q23 = __builtin_amdgcn_cvt_pknorm_u16(pb[2], pb[3]);
           lb = __builtin_amdgcn_udot2(q01, ones, lb, false);
           lb = __builtin_amdgcn_udot2(q23, ones, lb, false);
+          eb += (pb[0] + pb[1]) + (pb[2] + pb[3]);
           const uint32_t u01 = __builtin_bit_cast(uint32_t, q01), u23 = __builtin_bit_cast(uint32_t, q23);
           *reinterpret_cast<uint32_t*>(pg + wb0) =
               __builtin_amdgcn_perm((u23 >> 7) & 0x007F007Fu, (u01 >> 7) & 0x007F007Fu, 0x06040200u);
@@ -891,19 +933,24 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
   // and sums the CW waves' values of its record entries
   la = row_sum16_u(la);
   lb = row_sum16_u(lb);
-  const float ma = ima == INT_MIN ? -INFINITY : static_cast<float>(ima) * esa;
-  const float mb = imb == INT_MIN ? -INFINITY : static_cast<float>(imb) * esb;
+  ea = row_sum16_f(ea) * 65535.f;        // the units of la: pknorm rounds 65535 x
+  eb = row_sum16_f(eb) * 65535.f;
+  const float ma = ima == INT_MIN ? -INFINITY : static_cast<float>(ima) * esa + static_cast<float>(sha);
+  const float mb = imb == INT_MIN ? -INFINITY : static_cast<float>(imb) * esb + static_cast<float>(shb);
   if (n16 == 0) {
     s_m[wave][ha] = ma;
     s_l[wave][ha] = static_cast<float>(la);
+    s_e[wave][ha] = ea;
     if (LIMBS == 2) {
       s_m[wave][hb] = mb;
       s_l[wave][hb] = static_cast<float>(lb);
+      s_e[wave][hb] = eb;
     }
   }
   if (LIMBS == 3 && lane >= 4 && lane < 8) {
     s_m[wave][lane] = -INFINITY;
     s_l[wave][lane] = 0.f;
+    s_e[wave][lane] = 0.f;
   }
   wait_vmcnt(0);                         // this wave's own copies, past the sequence's end too
   if (NPROD > 0 && ncap_w(wave) > SELF)  // and the copy waves' ones into its slots
@@ -972,13 +1019,16 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
       float* rec = a.part + ((static_cast<int64_t>(bh) * a.S + s) * G + (hd < G ? hd : 0)) * a.prec;
       if (hd < G && col < ncol) rec[PHDR + col] = sum[r];
       if (hd < G && wave < 2 && lane == 0) {
-        float l = 0.f;
+        float l = 0.f, le = 0.f;
 #pragma unroll
-        for (int w = 0; w < CW; ++w) l += s_l[w][hd] * fw(w, r);
+        for (int w = 0; w < CW; ++w) {
+          l += s_l[w][hd] * fw(w, r);
+          le += s_e[w][hd] * fw(w, r);
+        }
         const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mk), r));
         rec[0] = good ? m : NAN;
         rec[1] = l;
-        rec[2] = 0.f;
+        rec[2] = le;
         rec[3] = 0.f;
       }
     }
@@ -994,11 +1044,12 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
       mw[w] = s_m[w][hd];
       m = fmaxf(m, mw[w]);
     }
-    float l = 0.f;
+    float l = 0.f, le = 0.f;
 #pragma unroll
     for (int w = 0; w < CW; ++w) {
       f[w] = mw[w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[w] - m);
       l += s_l[w][hd] * f[w];
+      le += s_e[w][hd] * f[w];
     }
     const int r = hd & 3;
     for (int col = lane; col < ncol; col += 64) {
@@ -1021,7 +1072,7 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
     if (lane == 0) {
       rec[0] = good ? m : NAN;
       rec[1] = l;
-      rec[2] = 0.f;
+      rec[2] = le;
       rec[3] = 0.f;
     }
   }
@@ -1068,7 +1119,7 @@ __global__ __launch_bounds__(CNT) void k_attn_combine(CombArgs a, const aatc_cal
 
   // the first pass's records (headers and this thread's column values) before anything that
   // depends on a load: these are the long pole
-  float hm = -INFINITY, hl = 0.f;
+  float hm = -INFINITY, hl = 0.f, he = 0.f;
   float v0[SPC / 4], v1[SPC / 4];
   auto load_pass = [&](int s0) {
     const int n = S - s0 < SPC ? S - s0 : SPC;
@@ -1078,8 +1129,10 @@ __global__ __launch_bounds__(CNT) void k_attn_combine(CombArgs a, const aatc_cal
     const float* hp = rec0 + (s0 + (hv ? lane : 0)) * stride;
     hm = hp[0];
     hl = hp[1];
+    he = hp[2];
     hm = hv ? hm : -INFINITY;
     hl = hv ? hl : 0.f;
+    he = hv ? he : 0.f;
     const bool cv0 = cl < prec - PHDR, cv1 = cl + 256 < prec - PHDR;   // record length: a kernel argument
     const int o0 = PHDR + (cv0 ? cl : 0), o1 = PHDR + (cv1 ? cl + 256 : 0);
 #pragma unroll
@@ -1119,7 +1172,9 @@ __global__ __launch_bounds__(CNT) void k_attn_combine(CombArgs a, const aatc_cal
   const int ncol = bad ? 0 : ncol_blob;
   const int c0 = cl, c1 = cl + 256;       // this thread's columns
 
-  float M = -INFINITY, L = 0.f, acc0 = 0.f, acc1 = 0.f;
+  // L sums the rounded probabilities that weighted the code sums (it normalises the output);
+  // LE the unrounded ones (the lse: rounding each token to 14 bits would bias it low)
+  float M = -INFINITY, L = 0.f, LE = 0.f, acc0 = 0.f, acc1 = 0.f;
   for (int s0 = 0; s0 < S; s0 += SPC) {
     if (s0 > 0) load_pass(s0);
     if (wave == 0) {
@@ -1128,12 +1183,13 @@ __global__ __launch_bounds__(CNT) void k_attn_combine(CombArgs a, const aatc_cal
       const float nM = fmaxf(M, m);
       const float w = (hm == -INFINITY || nM == -INFINITY) ? 0.f : exp2f(hm - nM);
       if (lane < SPC) wsl[lane] = w;
-      const float l = wave_sum_x(w * hl);
+      const float l = wave_sum_x(w * hl), le = wave_sum_x(w * he);
       const bool anynan = __ballot(nan) != 0;
       if (lane == 0) {
         red[0] = nM;
         red[1] = l;
         red[2] = anynan ? 1.f : 0.f;
+        red[3] = le;
       }
     }
     __syncthreads();
@@ -1141,6 +1197,7 @@ __global__ __launch_bounds__(CNT) void k_attn_combine(CombArgs a, const aatc_cal
     const float fold = (M == -INFINITY) ? 0.f : exp2f(M - nM);
     bad |= red[2] != 0.f;
     L = L * fold + red[1];
+    LE = LE * fold + red[3];
     M = nM;
     float p0 = 0.f, p1 = 0.f;
 #pragma unroll
@@ -1211,7 +1268,7 @@ __global__ __launch_bounds__(CNT) void k_attn_combine(CombArgs a, const aatc_cal
   const bool empty = seq == 0;
   if (tid < D) a.out[qh * D + tid] = bad ? NAN : (L > 0.f ? res[tid] : (empty ? 0.f : NAN));
   if (a.lse && tid == 0) {
-    const float l2 = bad ? NAN : (L > 0.f ? M + log2f(L / static_cast<float>(PS)) + a.offs[bh * 8 + g]
+    const float l2 = bad ? NAN : (L > 0.f ? M + log2f(LE / static_cast<float>(PS)) + a.offs[bh * 8 + g]
                                           : (empty ? -INFINITY : NAN));
     a.lse[qh] = l2 * 0.69314718055994530942f;
   }
@@ -1234,9 +1291,11 @@ hipError_t launch_one(const AttnArgs& a, const aatc_calib* kcal, const aatc_cali
 template <int NP, bool HALF, int NVB>
 hipError_t launch_limbs(int limbs, const AttnArgs& a, const aatc_calib* kcal, const aatc_calib* vcal, dim3 grid,
                         size_t lds, hipStream_t st) {
-  if (NVB == 12 && NP <= 2 && a.prod)
-    return limbs == 3 ? launch_one<NP, HALF, NVB, 3, NPROD_MAX>(a, kcal, vcal, grid, lds, st)
-                      : launch_one<NP, HALF, NVB, 2, NPROD_MAX>(a, kcal, vcal, grid, lds, st);
+  if constexpr (NVB == 12 && NP <= 2) {
+    if (a.prod)
+      return limbs == 3 ? launch_one<NP, HALF, NVB, 3, NPROD_MAX>(a, kcal, vcal, grid, lds, st)
+                        : launch_one<NP, HALF, NVB, 2, NPROD_MAX>(a, kcal, vcal, grid, lds, st);
+  }
   return limbs == 3 ? launch_one<NP, HALF, NVB, 3, 0>(a, kcal, vcal, grid, lds, st)
                     : launch_one<NP, HALF, NVB, 2, 0>(a, kcal, vcal, grid, lds, st);
 }

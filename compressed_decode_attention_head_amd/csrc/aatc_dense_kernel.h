@@ -1,8 +1,8 @@
 // Dense bf16 decode attention on the matrix cores (gfx950), the full-cache comparator of the
 // compressed path and the kernel of raw bf16 token segments.
 //
-// Page "SPHERICAL KV ..." (RDKV abstract): the full-precision cache that the compressed cache
-// is measured against is re-read from HBM at every decode step.  This is that step for a bf16
+// Page "SPHERICAL KV ..." (RDKV abstract): the compressed cache is compared with the
+// full-precision one, which every decode step reads from HBM again.  This is that step for a bf16
 // cache [batch][n_kv][capacity][128]: each workgroup takes a chunk of consecutive tokens of one
 // (batch, KV head) -- CHUNK, or a power-of-two fraction of it for short segments -- and all q heads of its GQA group, and writes one split-softmax state per q
 // head (normalised output and log-sum-exp); k_merge_states merges the states.

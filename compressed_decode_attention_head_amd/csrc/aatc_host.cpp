@@ -577,8 +577,11 @@ aatc_status aatc_joint_kv_split(const void* kblobs, const void* vblobs, int32_t 
       if (!std::isfinite(kw[i])) return fail(AATC_ERR_NUMERICAL, "k_weight[%lld] is not finite", (long long)i);
       if (kw[i] < 0.0) return fail(AATC_ERR_INVALID_ARGUMENT, "k_weight[%lld] < 0", (long long)i);
     }
-  if (total < 0 || total > d * (max_k + max_v))
-    return fail(AATC_ERR_BUDGET, "total_bits %d outside [0, %d]", total, d * (max_k + max_v));
+  // each tensor stays within what decode attention reads (AATC_MAX_ATTN_BITS per vector)
+  const int cap_k = std::min(d * max_k, AATC_MAX_ATTN_BITS), cap_v = std::min(d * max_v, AATC_MAX_ATTN_BITS);
+  if (total < 0 || total > cap_k + cap_v)
+    return fail(AATC_ERR_BUDGET, "total_bits %d outside [0, %d] (each tensor at most %d bits per vector)", total,
+                cap_k + cap_v, AATC_MAX_ATTN_BITS);
   const double sc = scale > 0.f ? static_cast<double>(scale) : 1.0 / std::sqrt(static_cast<double>(d));
   std::vector<double> ks(static_cast<size_t>(n_heads) * d), lam(n_heads);
   for (int h = 0; h < n_heads; ++h) {
@@ -596,7 +599,7 @@ aatc_status aatc_joint_kv_split(const void* kblobs, const void* vblobs, int32_t 
     for (int i = 0; i < d; ++i) t += std::ldexp(s2[i], -2 * bits[i]);
     return t;
   };
-  const int lo = std::max(0, total - d * max_v), hi = std::min(total, d * max_k);
+  const int lo = std::max(0, total - cap_v), hi = std::min(total, cap_k);
   std::vector<double> tot(hi - lo + 1);
   for (int bk = lo; bk <= hi; ++bk) {
     double t = 0.0;

@@ -60,6 +60,7 @@ typedef enum { AATC_ROT_KLT = 0, AATC_ROT_WHT = 1, AATC_ROT_IDENTITY = 2, AATC_R
 #define AATC_MAX_BITS 8
 #define AATC_MAX_FIELDS 384      /* 3 fields per channel at most (7 = 4+2+1) */
 #define AATC_MAX_GROUP 8         /* q heads per KV head handled by decode attention */
+#define AATC_MAX_ATTN_BITS 512   /* bits per K or V vector decode attention reads (4 per element) */
 #define AATC_MAGIC 0x43544141u   /* "AATC" */
 #define AATC_VERSION 2u
 
@@ -209,9 +210,9 @@ aatc_status aatc_calibrate(const aatc_calib_params* params, const void* x_host, 
                            size_t calib_bytes);
 
 /*
- * aatc_query_channel_weights -- host, synchronous, fp64.  [AATC abstract: under a white-noise
- * quantization model the expected attention-aware distortion decomposes into key and value
- * terms that factor across tokens and channels]  For a key blob's rotation R and n calibration
+ * aatc_query_channel_weights -- host, synchronous, fp64.  [AATC abstract: when quantization
+ * errors are modelled as white noise, the mean attention-aware error is a sum of a key part
+ * and a value part, each separable over tokens and over channels]  For a key blob's rotation R and n calibration
  * queries q (row r at q_host + r*row_stride elements, dtype F32/BF16/F64: the query heads
  * that share the KV head), w_out[i] = (1/n) sum_r ((R q_r)_i)^2.  The expected squared score
  * error of a zero-mean white key error is sum_i w_i E[e_i^2], so passing w as channel_weight
@@ -253,9 +254,11 @@ aatc_status aatc_query_moment(const void* q_host, aatc_dtype dtype, int64_t n, i
  *   k_calib_host / v_calib_host: n_heads consecutive blobs each; k_weight: NULL or
  *   [n_heads][d] fp64 (aatc_query_channel_weights of each head; NULL for NOVA keys, whose
  *   coefficients already carry the query statistics).
+ *   B_K and B_V are each limited to min(d max_bits, AATC_MAX_ATTN_BITS), so that the split
+ *   never asks for a cache that aatc_decode_attn rejects.
  *   Errors: a blob's aatc_calib_validate status; n_heads < 1, null pointers, a negative weight
  *   -> INVALID_ARGUMENT; a non-finite weight -> NUMERICAL; total_bits outside
- *   [0, d (max_bits_K + max_bits_V)] -> BUDGET.
+ *   [0, min(d max_bits_K, AATC_MAX_ATTN_BITS) + min(d max_bits_V, AATC_MAX_ATTN_BITS)] -> BUDGET.
  */
 aatc_status aatc_joint_kv_split(const void* k_calib_host, const void* v_calib_host, int32_t n_heads,
                                 const double* k_weight, float softmax_scale, int32_t total_bits,
@@ -301,7 +304,7 @@ size_t aatc_decode_attn_workspace_bytes(const aatc_cache* cache, int32_t n_q_hea
 
 /*
  * aatc_decode_attn -- device, async; one decode step over the compressed cache.
- * [SPECTRA Abstract and RDKV abstract: the whole cache is re-read at every generated token;
+ * [SPECTRA Abstract and RDKV abstract: every decode step reads the whole cache again;
  *  NOVA-KV abstract: decode is bandwidth-bound]
  *   q_dev: fp32 [batch][n_q_heads][128]; q head g reads KV head g / (n_q_heads/n_kv_heads)
  *   (contiguous groups, 1..8 q heads per KV head).  seq_lens_dev: int32 [batch] tokens
@@ -318,8 +321,9 @@ size_t aatc_decode_attn_workspace_bytes(const aatc_cache* cache, int32_t n_q_hea
  *   aligned, for the per-split partial records of the two kernels the call launches on
  *   `stream`; its contents need no initialisation.  Calls that share a workspace must be
  *   ordered (same stream) or not overlap in time.
- *   Limits: k_bits and v_bits <= 512 (4 bits/element), q-head group <= 8, v_tiles <= 24.
- *   Errors: group > 8 or not an integer, bits > 512 -> UNSUPPORTED; bad pointers, seq length >
+ *   Limits: k_bits and v_bits <= AATC_MAX_ATTN_BITS (512, 4 bits/element), q-head group <= 8,
+ *   v_tiles <= 24.  (aatc_encode and aatc_decode take up to 8d bits.)
+ *   Errors: group > 8 or not an integer, bits > AATC_MAX_ATTN_BITS -> UNSUPPORTED; bad pointers, seq length >
  *   capacity -> INVALID_ARGUMENT; workspace too small -> BUFFER_TOO_SMALL; launch -> HIP.
  */
 aatc_status aatc_decode_attn(const aatc_cache* cache, const float* q_dev, int32_t n_q_heads,
@@ -422,8 +426,8 @@ size_t aatc_decode_attn_dense_workspace_bytes(int32_t batch, int32_t n_kv_heads,
 /*
  * aatc_decode_attn_dense -- device, async; one decode step of plain softmax attention over an
  * uncompressed bf16 cache, the full-precision baseline that the compressed cache is compared
- * with.  [SPHERICAL KV page, RDKV abstract: speedup over the full cache, which is re-read from
- * HBM at every decode step]
+ * with.  [SPHERICAL KV page, RDKV abstract: speedup over the full cache, which every decode
+ * step reads from HBM again]
  *   k_dev, v_dev: bf16 [batch][n_kv_heads][capacity_tokens][128], 16-byte aligned, read only.
  *   seq_lens_dev: int32 [batch][n_kv_heads] visible tokens per (b,h) (each <= max_seq_len), or
  *   NULL for max_seq_len; max_seq_len <= capacity_tokens.  q_dev: fp32 [batch][n_q_heads][128],

@@ -10,7 +10,7 @@ Sources (cited by page title and section; no line numbers):
             on the few channels that carry the signal.
   [RDKV]    "SPHERICAL KV: ..." page, first abstract (RDKV): bit widths from full
             precision down to zero bits per token or channel by reverse water-filling,
-            once after prefill; the cache is re-read from HBM at every decode step.
+            once after prefill; every decode step reads the cache from HBM again.
   [NOVA]    same page, third abstract (NOVA-KV): decode is bandwidth-bound; a fixed
             per-token bit count / fixed-width layout is required; the key transform that
             is optimal for the attention-aware distortion is not orthogonal, and under it
@@ -38,12 +38,12 @@ TILE = 64          # tokens per packed tile
 MAX_BITS = 8
 
 __all__ = [
-    "TILE", "MAX_BITS", "calib_stats", "rotation_klt", "rotation_wht", "rotation_identity",
+    "TILE", "MAX_BITS", "calib_stats", "rotation_klt", "hadamard_signs", "rotation_wht", "rotation_identity",
     "query_channel_weights", "query_moment", "transform_nova", "NOVA_EIG_FLOOR",
     "allocation_distortion", "value_term_weight", "joint_kv_split",
     "bits_budget", "waterfill_bits", "waterfill_theta", "uniform_quantizer_mse",
     "uniform_quantizer_mse_deriv", "optimal_step", "quantizer_tables", "calibrate",
-    "encode_codes", "dequantize", "reconstruct", "v_fields", "pack_k", "unpack_k",
+    "rotate", "encode_codes", "dequantize", "reconstruct", "v_fields", "pack_k", "unpack_k",
     "pack_v", "unpack_v", "packed_words", "attention", "attention_streaming",
     "decode_attention", "rotated_scores", "tier_distortions", "token_tiers",
     "segment_attention",
@@ -51,8 +51,8 @@ __all__ = [
 
 
 # ----------------------------------------------------------------------------------
-# Calibration statistics  [AATC Full text: bits are allocated "over a calibration set";
-# SPECTRA Abstract: the coordinate system is "computed from its own statistics"]
+# Calibration statistics  [AATC Full text: the bit allocation is made on calibration data;
+# SPECTRA Abstract: the basis comes from the statistics of the cache itself]
 # ----------------------------------------------------------------------------------
 def calib_stats(x):
     """Mean and centred covariance (1/M normalisation) of calibration rows x [M, d]."""
@@ -87,18 +87,24 @@ def rotation_klt(c):
     return r, np.maximum(w[order], 0.0)
 
 
-def rotation_wht(c):
-    """Walsh-Hadamard rotation in Sylvester (natural) order, scaled to be orthogonal.
-
-    R_ij = (-1)^popcount(i & j) / sqrt(d); sigma2 = diag(R C R^T).
-    """
-    c = np.asarray(c, dtype=np.float64)
-    d = c.shape[0]
-    if d & (d - 1):
+def hadamard_signs(d):
+    """Sylvester (natural-order) Hadamard matrix H_ij = (-1)^popcount(i & j), entries +-1."""
+    if d < 1 or d & (d - 1):
         raise ValueError("WHT needs a power-of-two dimension")
     i = np.arange(d)
     par = np.array([[bin(a & b).count("1") & 1 for b in i] for a in i])
-    r = np.where(par == 1, -1.0, 1.0) / math.sqrt(d)
+    return np.where(par == 1, -1.0, 1.0)
+
+
+def rotation_wht(c):
+    """Walsh-Hadamard rotation in Sylvester (natural) order, scaled to be orthogonal.
+
+    R_ij = (-1)^popcount(i & j) / sqrt(d); sigma2 = diag(R C R^T).  (The encoder applies it as
+    the exact +-1 sums H x times one rounded 1/sqrt(d): see rotate.)
+    """
+    c = np.asarray(c, dtype=np.float64)
+    d = c.shape[0]
+    r = hadamard_signs(d) / math.sqrt(d)
     return r, np.einsum("ij,jk,ik->i", r, c, r)
 
 
@@ -201,7 +207,7 @@ def value_term_weight(c_v, scale=None):
     return scale * scale * float(np.trace(c_v))
 
 
-def joint_kv_split(k_sigma2, v_sigma2, lam, total_bits, max_bits=MAX_BITS, k_weight=None):
+def joint_kv_split(k_sigma2, v_sigma2, lam, total_bits, max_bits=MAX_BITS, k_weight=None, tensor_cap=None):
     """Split T = total_bits bits per (key, value) vector pair between K and V for a layer whose
     heads all share B_K (and B_V = T - B_K): the B_K minimising
         sum_h lam_h D_K,h(B_K) + D_V,h(T - B_K)
@@ -209,11 +215,13 @@ def joint_kv_split(k_sigma2, v_sigma2, lam, total_bits, max_bits=MAX_BITS, k_wei
     values within 1e-12 (relative) of the minimum the smallest B_K is taken.
 
     k_sigma2, v_sigma2: per-head variance vectors; lam: per-head weights (value_term_weight);
-    k_weight: per-head key weights or None.  Returns (B_K, B_V, distortion).
+    k_weight: per-head key weights or None; tensor_cap: largest B_K and B_V allowed (None: d
+    times max_bits), e.g. the most bits per vector a decode kernel reads.
+    Returns (B_K, B_V, distortion).
     """
     heads = len(k_sigma2)
     d = len(k_sigma2[0])
-    cap = d * max_bits
+    cap = d * max_bits if tensor_cap is None else min(d * max_bits, int(tensor_cap))
     lo, hi = max(0, total_bits - cap), min(total_bits, cap)
     if lo > hi:
         raise ValueError("budget out of range")
@@ -233,8 +241,8 @@ def joint_kv_split(k_sigma2, v_sigma2, lam, total_bits, max_bits=MAX_BITS, k_wei
 def query_channel_weights(r, q_cal):
     """Attention-aware key weights w_i = E[(R q)_i^2] over calibration queries q.
 
-    [AATC abstract: under a white-noise quantization model the expected attention-aware
-    distortion splits into key and value terms that factor over tokens and channels.]  With a
+    [AATC abstract: with quantization errors modelled as white noise, the mean attention-aware
+    error is a key part plus a value part, each separable over tokens and channels.]  With a
     zero-mean key error e independent of q and of its other channels, the score error
     q.(k - k_hat) = (R q).(R e) has E[(q.(k - k_hat))^2] = sum_i E[(R q)_i^2] E[(R e)_i^2]:
     the key channels' distortions add with these weights.  The value path has no such factor
@@ -379,18 +387,34 @@ def calibrate(x_cal, rotation="klt", bits_per_elem=2.0, max_bits=MAX_BITS, total
 # ----------------------------------------------------------------------------------
 # Encode / dequantize / reconstruct
 # ----------------------------------------------------------------------------------
+def rotate(x, art):
+    """Transform coefficients y = E x of rows x [N, d] in fp64 (E = R for orthogonal rotations).
+
+    Walsh-Hadamard: y = (H x) * (1/sqrt(d)), the +-1 sums H x taken exactly (fp64 holds every
+    partial sum of bf16 inputs exactly) and then one multiply by 1/sqrt(d) rounded to fp64, the
+    same definition R x with R = H / sqrt(d) has, without rounding each product separately.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if art.get("rotation") == "wht":
+        d = x.shape[-1]
+        with np.errstate(invalid="ignore", over="ignore"):
+            return (x @ hadamard_signs(d).T) * (1.0 / math.sqrt(d))
+    with np.errstate(invalid="ignore", over="ignore"):
+        return x @ np.asarray(art.get("E", art["R"])).T
+
+
 def encode_codes(x, art):
     """Codes c[N, d] (0 for 0-bit channels) of rows x [N, d].
 
-    y = E x in fp64 (E = R for orthogonal rotations); u = (y - o) * (1/Delta) + 2^(b-1) as
-    separately rounded fp64 operations;
+    y = rotate(x) in fp64; u = (y - o) * (1/Delta) + 2^(b-1) as separately rounded fp64
+    operations;
     c = clamp(floor(u), 0, 2^b - 1) (half-open bins: a value on an edge goes up);
     NaN -> 0, +-Inf -> the clamp ends.
     """
     x = np.asarray(x, dtype=np.float64)
     bits = np.asarray(art["bits"])
+    y = rotate(x, art)
     with np.errstate(invalid="ignore", over="ignore"):
-        y = x @ np.asarray(art.get("E", art["R"])).T
         half = np.where(bits > 0, np.ldexp(1.0, np.maximum(bits, 1) - 1), 0.0)
         u = (y - art["o"][None, :]) * art["inv_delta"][None, :]
         u = u + half[None, :]
@@ -621,10 +645,9 @@ def decode_attention(q, k_codes, v_codes, k_arts, v_arts, scale=None, seq_lens=N
 
 
 # ----------------------------------------------------------------------------------
-# Token tiers (joint token x channel allocation)  [RDKV abstract: "a bit-width ranging
-# from full precision down to zero bits guided by reverse water-filling, applied once
-# after the prefilling stage"; AATC Key points: distortion factors across tokens and
-# channels]
+# Token tiers (joint token x channel allocation)  [RDKV abstract: each token gets a width
+# between zero bits and full precision from reverse water-filling, decided once when prefill
+# ends; AATC Key points: the distortion separates over tokens and channels]
 # ----------------------------------------------------------------------------------
 TIERS = (0, 2, 4, 16)
 
@@ -655,10 +678,11 @@ def _tiers_at(weights, dist, lam, d):
     return np.array(TIERS)[np.argmin(costs, axis=1)]
 
 
-def token_tiers(attn_mass, dist, d, avg_bits):
+def token_tiers(attn_mass, dist, d, avg_bits, return_lambda=False):
     """Tier per token in {0,2,4,16} minimising sum_t a_t^2 D(tau_t) subject to
     sum_t tau_t d <= avg_bits * N * d, via a Lagrange multiplier found by bisection
-    (the smallest multiplier, hence the largest total, that meets the budget)."""
+    (the smallest multiplier, hence the largest total, that meets the budget).
+    With return_lambda the multiplier is returned too: (tiers, lambda)."""
     a = np.asarray(attn_mass, dtype=np.float64)
     w = a * a
     n = a.shape[0]
@@ -668,18 +692,20 @@ def token_tiers(attn_mass, dist, d, avg_bits):
     def total(lam):
         return float(np.sum(_tiers_at(w, dist, lam, d)) * d)
 
-    if total(0.0) <= budget:
-        return _tiers_at(w, dist, 0.0, d)
-    lo, hi = 0.0, 1.0
-    while total(hi) > budget:
-        hi *= 2.0
-    for _ in range(200):
-        mid = 0.5 * (lo + hi)
-        if total(mid) > budget:
-            lo = mid
-        else:
-            hi = mid
-    return _tiers_at(w, dist, hi, d)
+    lam = 0.0
+    if total(0.0) > budget:
+        lo, hi = 0.0, 1.0
+        while total(hi) > budget:
+            hi *= 2.0
+        for _ in range(200):
+            mid = 0.5 * (lo + hi)
+            if total(mid) > budget:
+                lo = mid
+            else:
+                hi = mid
+        lam = hi
+    tiers = _tiers_at(w, dist, lam, d)
+    return (tiers, lam) if return_lambda else tiers
 
 
 def segment_attention(q, segments, scale=None):

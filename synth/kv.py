@@ -24,7 +24,7 @@ PURPOSE = {"Q": 0, "calib": 1, "context": 2, "query": 3, "outlier": 4, "zipf": 5
 
 __all__ = ["ROOT_SEED", "K", "V", "PURPOSE", "seed_seq", "rng", "haar_orthogonal",
            "spectrum", "outlier_coords", "basis", "draw", "round_bf16", "bf16_bits", "to_dtype",
-           "draw_device", "queries", "zipf_mass", "torch_dtype"]
+           "draw_device", "queries", "peaked_queries", "zipf_mass", "torch_dtype"]
 
 
 def seed_seq(cfg, layer, head, tensor, purpose, extra=0):
@@ -140,6 +140,31 @@ def queries(cfg, layer, n_q_heads, n_kv_heads, keys, d=128, target_std=2.0):
         s = kh @ qr / np.sqrt(d)
         sd = s.std()
         out[g] = qr * (target_std / sd if sd > 0 else 1.0)
+    return out.astype(np.float32)
+
+
+def peaked_queries(cfg, layer, n_q_heads, n_kv_heads, keys, d=128, margin=12.0):
+    """Near one-hot queries: q head g points along one seeded key k_t of its KV head, scaled so
+    that the score q.k_t/sqrt(d) exceeds every other score over ``keys[h]`` by ``margin``
+    (e^-12 ~ 6e-6 for the runner-up's weight at the default).  Returns float32 [n_q_heads, d]."""
+    group = n_q_heads // n_kv_heads
+    out = np.zeros((n_q_heads, d), dtype=np.float64)
+    for g in range(n_q_heads):
+        h = g // group
+        kh = np.asarray(keys[h], dtype=np.float64)
+        norms = np.einsum("ij,ij->i", kh, kh)
+        # among the 64 longest keys, in a seeded order, the first whose own direction scores it
+        # above every other key
+        cand = np.argsort(-norms, kind="stable")[:64]
+        cand = cand[rng(cfg, layer, h, K, "query", extra=2000 + g).permutation(cand.size)]
+        for t in cand:
+            s = kh @ (kh[t] / np.sqrt(d))
+            gap = s[t] - np.max(np.delete(s, t))
+            if gap > 0:
+                break
+        if not gap > 0:
+            raise ValueError("no key dominates its own direction")
+        out[g] = kh[t] * (margin / gap)
     return out.astype(np.float32)
 
 

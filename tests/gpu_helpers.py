@@ -72,14 +72,26 @@ class Case:
         cap = capacity or -(-self.n // 64) * 64
         return api.CompressedKVCache(self.blobs(synth.K), self.blobs(synth.V), self.batch, cap, device=device)
 
-    def oracle_attention(self, seq_lens=None, scale=None):
+    def queries(self, mode):
+        """Queries [batch, n_q, d] float32 at another temperature: a float is the std of the
+        scores over the context (the default queries have 2.0); "peaked" points each q head at
+        one key, 12 above every other score (near one-hot attention)."""
+        keys = [[self.x[synth.K][b, h] for h in range(self.n_kv)] for b in range(self.batch)]
+        if mode == "peaked":
+            return np.stack([synth.peaked_queries(self.cfg, self.layer, self.n_q, self.n_kv, keys[b])
+                             for b in range(self.batch)])
+        return np.stack([synth.queries(self.cfg, self.layer, self.n_q, self.n_kv, keys[b], target_std=float(mode))
+                         for b in range(self.batch)])
+
+    def oracle_attention(self, seq_lens=None, scale=None, q=None):
+        q = self.q if q is None else q
         out = np.zeros((self.batch, self.n_q, 128))
         lse = np.zeros((self.batch, self.n_q))
         for b in range(self.batch):
             n = self.n if seq_lens is None else int(seq_lens[b])
             ks = [self.codes[synth.K][b, h][:n] for h in range(self.n_kv)]
             vs = [self.codes[synth.V][b, h][:n] for h in range(self.n_kv)]
-            out[b], lse[b] = O.decode_attention(self.q[b], ks, vs, self.art[synth.K], self.art[synth.V], scale)
+            out[b], lse[b] = O.decode_attention(q[b], ks, vs, self.art[synth.K], self.art[synth.V], scale)
         return out, lse
 
 
@@ -89,7 +101,7 @@ def excused_mismatch_report(x, art, got, want):
     bad = np.argwhere(got != want)
     if bad.size == 0:
         return 0, 0
-    y = np.asarray(x, dtype=np.float64) @ art.get("E", art["R"]).T
+    y = O.rotate(x, art)
     unexcused = 0
     for t, i in bad:
         b = int(art["bits"][i])
@@ -100,6 +112,19 @@ def excused_mismatch_report(x, art, got, want):
         if abs(y[t, i] - e) > tol:
             unexcused += 1
     return len(bad), unexcused
+
+
+def assert_codes_match(x, art, got, want, dtype, what=""):
+    """Codes bit-exact up to the bin-edge excuse: every mismatch excused, and at most
+    floor(1e-6 x codes) of them in this comparison (so none below a million codes).  Walsh-Hadamard
+    coefficients of bf16 rows are exact sums times one rounded constant on both sides, so there
+    no mismatch at all is allowed."""
+    n_bad, n_unexc = excused_mismatch_report(x, art, got, want)
+    assert n_unexc == 0, (what, n_bad, n_unexc)
+    assert n_bad <= int(1e-6 * want.size), (what, n_bad, want.size)
+    if art.get("rotation") == "wht" and dtype == "bf16":
+        assert n_bad == 0, (what, n_bad)
+    return n_bad
 
 
 def unpack_all(words, bits, n, tensor):

@@ -11,7 +11,7 @@ import pytest
 
 import oracle as O
 import synth
-from gpu_helpers import Case, excused_mismatch_report, unpack_all
+from gpu_helpers import Case, assert_codes_match, unpack_all
 
 pytestmark = pytest.mark.gpu
 
@@ -28,7 +28,6 @@ def _check_codes(case, cache, tensor):
     bits_lib = None
     from compressed_decode_attention_head_amd import api
     blobs = cache.k_blobs_host if tensor == synth.K else cache.v_blobs_host
-    total_codes = 0
     for b in range(case.batch):
         for h in range(case.n_kv):
             bits = np.asarray(api.calib_view(blobs[h])["bits"], dtype=np.int64)
@@ -38,14 +37,10 @@ def _check_codes(case, cache, tensor):
             got_words = words[b, h, :nw]
             got = unpack_all(got_words, bits, case.n, tensor)
             want = case.codes[tensor][b, h]
-            n_bad, n_unexc = excused_mismatch_report(case.x[tensor][b, h], case.art[tensor][h], got, want)
-            assert n_unexc == 0, (b, h, n_bad)
-            total_codes += want.size
+            n_bad = assert_codes_match(case.x[tensor][b, h], case.art[tensor][h], got, want, case.dtype, (b, h))
             if n_bad == 0:
                 ref_words = (O.pack_k if tensor == synth.K else O.pack_v)(want, bits)
                 assert np.array_equal(got_words, ref_words), (b, h)
-            else:
-                assert n_bad <= 1e-6 * total_codes + 1
 
 
 CASES = {
@@ -97,6 +92,24 @@ def test_decode_attention(built):
     err = np.abs(out.cpu().numpy() - ref).max()
     lerr = np.abs(lse.cpu().numpy() - lref).max()
     print(name, "attn max abs err", err, "lse err", lerr, flush=True)
+    assert err <= ATOL_ATTN, err
+    assert lerr <= 5e-3, lerr
+
+
+@pytest.mark.parametrize("mode", [0.5, 4.0, 8.0, "peaked"])
+def test_decode_attention_temperature(built, mode):
+    """Sharper and flatter attention than the default score std of 2: the fixed-point weights and
+    probabilities of the cache pass stay within the bar at score std 0.5, 4 and 8 and for near
+    one-hot queries."""
+    torch = _torch()
+    name, case, cache = built
+    qh = case.queries(mode)
+    out, lse = cache.decode_attn(torch.from_numpy(qh).cuda(), case.n)
+    torch.cuda.synchronize()
+    ref, lref = case.oracle_attention(q=qh)
+    err = np.abs(out.cpu().numpy() - ref).max()
+    lerr = np.abs(lse.cpu().numpy() - lref).max()
+    print(name, "queries", mode, "attn max abs err", err, "lse err", lerr, flush=True)
     assert err <= ATOL_ATTN, err
     assert lerr <= 5e-3, lerr
 
@@ -225,22 +238,26 @@ def test_encode_unaligned_rows_and_wht_appends(dtype, cfg):
         assert torch.equal(cache.codes(t), cache2.codes(t))
 
 
-def test_joint_kv_split_cache():
+@pytest.mark.parametrize("cfg,bpe,aware", [(2, 2.0, True), (2, 2.76, True), (3, 4.0, False)])
+def test_joint_kv_split_cache(cfg, bpe, aware):
     """A layer calibrated with the joint K/V split (library: query weights, split, calibration at
-    B_K and B_V): the split equals the oracle's, K and V carry different bit counts, and decode
-    attention matches the oracle."""
+    B_K and B_V) at 2 x 256, 2 x 353 (attention-aware keys) and 2 x 512 bits: the split equals
+    the oracle's (both limited to the 512 bits decode attention reads, which binds at the last
+    two budgets), and the calibrate -> encode -> decode attention chain matches the oracle."""
     torch = _torch()
     from compressed_decode_attention_head_amd import api
-    probe = Case(cfg=2, n_kv=2, group=4, n_tokens=64, rotation="klt", bpe_k=2.0, aware=True)
+    probe = Case(cfg=cfg, n_kv=2, group=4, n_tokens=64, rotation="klt", bpe_k=bpe, aware=aware)
     kb = probe.blobs(synth.K)
     vb = probe.blobs(synth.V)
-    w = np.stack([api.query_channel_weights(kb[h], probe.q_cal[h]) for h in range(2)])
-    bk, bv = api.joint_kv_split(kb, vb, 512, k_weight=w)
+    w = np.stack([api.query_channel_weights(kb[h], probe.q_cal[h]) for h in range(2)]) if aware else None
+    total = 2 * O.bits_budget(bpe, 128)
+    bk, bv = api.joint_kv_split(kb, vb, total, k_weight=w)
     want = O.joint_kv_split([a["sigma2"] for a in probe.art[synth.K]], [a["sigma2"] for a in probe.art[synth.V]],
-                            [O.value_term_weight(a["C"]) for a in probe.art[synth.V]], 512,
-                            k_weight=[a["weight"] for a in probe.art[synth.K]])
-    assert (bk, bv) == want[:2] and bk != bv
-    case = Case(cfg=2, n_kv=2, group=4, n_tokens=500, rotation="klt", bpe_k=bk / 128, bpe_v=bv / 128, aware=True)
+                            [O.value_term_weight(a["C"]) for a in probe.art[synth.V]], total,
+                            k_weight=[a["weight"] for a in probe.art[synth.K]] if aware else None, tensor_cap=512)
+    assert (bk, bv) == want[:2] and max(bk, bv) <= 512
+    case = Case(cfg=cfg, n_kv=2, group=4, n_tokens=500, rotation="klt", bpe_k=bk / 128, bpe_v=bv / 128,
+                aware=aware)
     cache = case.make_cache()
     assert (cache.k_bits, cache.v_bits) == (bk, bv)
     for t in (synth.K, synth.V):

@@ -172,9 +172,11 @@ def test_nova_errors(L):
     assert L.aatc_query_moment(None, 0, 4, 128, out.ctypes.data) == 1
 
 
-@pytest.mark.parametrize("cfg,rot,bpe,aware", [(2, "klt", 2.0, True), (4, "wht", 1.33, True), (3, "klt", 4.0, False)])
+@pytest.mark.parametrize("cfg,rot,bpe,aware", [(2, "klt", 2.0, True), (4, "wht", 1.33, True), (3, "klt", 4.0, False),
+                                               (2, "klt", 2.76, True), (3, "klt", 4.0, True)])
 def test_joint_kv_split_matches_oracle(cfg, rot, bpe, aware):
-    """The layer's K/V split: library (C++) against the oracle on the same blobs' statistics."""
+    """The layer's K/V split: library (C++) against the oracle on the same blobs' statistics,
+    both limited to the 512 bits per vector that decode attention reads."""
     n_kv = 3
     calk = [_cal(cfg, h, synth.K) for h in range(n_kv)]
     calv = [_cal(cfg, h, synth.V) for h in range(n_kv)]
@@ -191,9 +193,30 @@ def test_joint_kv_split_matches_oracle(cfg, rot, bpe, aware):
     got = api.joint_kv_split(kb, vb, T, k_weight=w)
     want = O.joint_kv_split([a["sigma2"] for a in ka], [a["sigma2"] for a in va],
                             [O.value_term_weight(a["C"]) for a in va], T,
-                            k_weight=None if w is None else list(w))
+                            k_weight=None if w is None else list(w), tensor_cap=512)
     assert got == want[:2], (got, want)
-    assert sum(got) == T
+    assert sum(got) == T and max(got) <= 512
+
+
+def test_joint_kv_split_decode_cap_binds():
+    """At 4 bits per element the unconstrained split gives V more than the 512 bits per vector
+    decode attention reads; the library's split is then the cap's corner (512, 512), which the
+    oracle's capped split also gives, and a budget past 2 x 512 is refused."""
+    n_kv = 3
+    calk = [_cal(3, h, synth.K) for h in range(n_kv)]
+    calv = [_cal(3, h, synth.V) for h in range(n_kv)]
+    ka = [O.calibrate(c, "klt", 4.0) for c in calk]
+    va = [O.calibrate(c, "klt", 4.0) for c in calv]
+    args = ([a["sigma2"] for a in ka], [a["sigma2"] for a in va], [O.value_term_weight(a["C"]) for a in va], 1024)
+    free = O.joint_kv_split(*args)
+    assert max(free[:2]) > 512                     # the cap is not idle at this budget
+    assert O.joint_kv_split(*args, tensor_cap=512)[:2] == (512, 512)
+    kb = [api.calibrate(_bits16(c), "klt", 4.0) for c in calk]
+    vb = [api.calibrate(_bits16(c), "klt", 4.0) for c in calv]
+    assert api.joint_kv_split(kb, vb, 1024) == (512, 512)
+    with pytest.raises(N.AatcError) as e:
+        api.joint_kv_split(kb, vb, 1025)
+    assert e.value.name == "AATC_ERR_BUDGET"
 
 
 def test_joint_kv_split_errors(L):

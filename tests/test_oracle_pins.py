@@ -71,6 +71,29 @@ def test_wht_matches_scipy_hadamard():
     assert np.allclose(s2, np.diag(h @ c @ h.T), rtol=1e-12)
 
 
+def test_wht_encoder_takes_exact_sums():
+    """For bf16 rows every +-1 sum of H x is exact in integer units of the row's smallest power of
+    two; the encoder's coefficients equal those exact sums times 1/sqrt(d) rounded to fp64, with
+    one rounding, while multiplying by the rounded matrix H/sqrt(d) rounds every product and
+    differs in some coefficients."""
+    x = synth.draw(4, 0, 1, synth.K, "context", 64, dtype="bf16", marginal="t3").astype(np.float64)
+    art = O.calibrate(synth.draw(4, 0, 1, synth.K, "calib", 1024, dtype="bf16", marginal="t3"), "wht", 1.33)
+    y = O.rotate(x, art)
+    h = linalg.hadamard(128).astype(np.int64)
+    s = 1.0 / math.sqrt(128)
+    for t in range(x.shape[0]):
+        m, e = np.frexp(x[t])
+        e0 = int(e[x[t] != 0].min()) - 9            # bf16: 8 significant bits
+        n = np.array([int(v) for v in np.ldexp(x[t], -e0)], dtype=np.int64)
+        assert np.array_equal(np.ldexp(n.astype(np.float64), e0), x[t])
+        exact = h @ n                               # integer sums, no rounding
+        assert np.abs(exact).max() < 2 ** 53
+        want = np.ldexp(exact.astype(np.float64), e0) * s
+        assert np.array_equal(y[t], want), t
+    rounded = x @ (h / math.sqrt(128)).T
+    assert np.any(rounded != y)
+
+
 def test_wht_flattens_variances_klt_compacts():
     q, lam, _ = synth.basis(4, 0, 0, synth.K)
     c = q @ np.diag(lam) @ q.T
@@ -727,6 +750,83 @@ def test_token_tiers_budget_monotone_bruteforce():
         cost = lambda ts: sum(a[t] ** 2 * dist[O.aatc_oracle.TIERS.index(ts[t])] + lam * d * ts[t]
                               for t in range(6))
         assert cost(tuple(got)) <= cost(best) * (1 + 1e-12)
+
+
+def _bits_from_histogram(hist):
+    """Non-increasing bit vector with the given {bits: channels} histogram (KLT channel order)."""
+    return np.concatenate([np.full(c, b, dtype=np.int64) for b, c in sorted(hist.items(), reverse=True)])
+
+
+def test_tier_distortions_closed_form_on_noise_free_spectrum():
+    """D(tau) = sum_i s_i 4^-b_i(tau) with b(tau) the allocation of tau*d bits: on s_i = i^-1.5 the
+    allocations at 256 and 512 bits are the derived histograms (tie rule included), so D(2) and
+    D(4) follow from them alone; D(0) is the total variance, D(16) = 0; several tensors add, and a
+    tensor scaled by 4 has the same bits and 4 times the distortion."""
+    s2 = synth.spectrum(128)
+    b2 = _bits_from_histogram({6: 1, 5: 4, 4: 7, 3: 19, 2: 48, 1: 49})
+    b4 = _bits_from_histogram({8: 1, 7: 4, 6: 7, 5: 19, 4: 48, 3: 49})
+    assert b2.sum() == 256 and b4.sum() == 512
+    want = np.array([math.fsum(s2), math.fsum(s2 * 4.0 ** -b2), math.fsum(s2 * 4.0 ** -b4), 0.0])
+    got = O.tier_distortions([s2], 128)
+    assert np.allclose(got, want, rtol=1e-14, atol=0.0), (got, want)
+    assert got[3] == 0.0
+    got2 = O.tier_distortions([s2, 4.0 * s2], 128)
+    assert np.allclose(got2, 5.0 * want, rtol=1e-14, atol=0.0)
+
+
+_TIERS = (0, 2, 4, 16)
+
+
+def _tiers_by_enumeration(w, dist, d, budget):
+    """Brute force over every tier assignment of len(w) tokens: the Lagrangian solutions are the
+    vertices of the lower convex hull of (bits, sum_t w_t D(tier_t)); the one with the most bits
+    within the budget is what the smallest fitting multiplier picks.  Returns (assignment, bits, cost)."""
+    best = {}
+    for ts in itertools.product(range(4), repeat=len(w)):
+        b = d * sum(_TIERS[k] for k in ts)
+        c = sum(w[t] * dist[k] for t, k in enumerate(ts))
+        if b not in best or c < best[b][0]:
+            best[b] = (c, ts)
+    hull = []
+    for x in sorted(best):
+        p = (x, best[x][0])
+        while len(hull) >= 2:
+            (x1, y1), (x2, y2) = hull[-2], hull[-1]
+            if (x2 - x1) * (p[1] - y1) - (y2 - y1) * (p[0] - x1) <= 0:
+                hull.pop()
+            else:
+                break
+        hull.append(p)
+    bits, cost = max(p for p in hull if p[0] <= budget)
+    return tuple(_TIERS[k] for k in best[bits][1]), bits, cost
+
+
+def test_token_tiers_match_enumeration():
+    """token_tiers against the enumeration of all 4^6 assignments, with weights a_t^2: same tiers
+    (hence optimal for the constrained problem at its own bit total, and the largest such total
+    within the budget); a multiplier 1e-9 smaller than the returned one overshoots the budget
+    (the argmin found by enumeration); and the a_t-weighted enumeration differs in some cases,
+    so a_t^2 is what decides."""
+    d = 128
+    s2 = synth.spectrum(d)
+    dist = O.tier_distortions([s2, s2], d)
+    rng = np.random.default_rng(5)
+    differ = 0
+    for trial in range(24):
+        a = rng.dirichlet(np.full(6, 0.3))
+        avg = float(rng.choice([1.0, 2.0, 2.76, 4.0, 6.0]))
+        budget = avg * 6 * d
+        want, wbits, _ = _tiers_by_enumeration(a * a, dist, d, budget)
+        got, lam = O.token_tiers(a, dist, d, avg, return_lambda=True)
+        assert tuple(int(v) for v in got) == want, (trial, got, want)
+        if lam > 0:
+            lam2 = lam * (1.0 - 1e-9)
+            over = min(itertools.product(range(4), repeat=6),
+                       key=lambda ts: sum(a[t] ** 2 * dist[k] + lam2 * d * _TIERS[k] for t, k in enumerate(ts)))
+            assert d * sum(_TIERS[k] for k in over) > budget, trial
+        if _tiers_by_enumeration(a, dist, d, budget)[0] != want:
+            differ += 1
+    assert differ >= 5
 
 
 def test_segment_attention_excludes_evicted():
