@@ -359,6 +359,22 @@ class CompressedKVCache:
                                          workspace.data_ptr(), workspace.numel(), _stream_ptr(stream)))
         return out, lse
 
+    def decode_attn_noalloc(self, q, max_seq_len, out, lse=None, seq_lens=None, scale=0.0, stream=None):
+        """aatc_decode_attn_noalloc: aatc_decode_attn with the library's static per-GPU workspace;
+        out (and lse, if given) are the caller's [batch, n_q_heads, 128] / [batch, n_q] fp32 tensors."""
+        import torch
+        if q.dtype != torch.float32 or not q.is_contiguous() or q.dim() != 3 or q.shape[0] != self.batch:
+            raise ValueError("q must be a contiguous fp32 [batch, n_q_heads, 128] tensor")
+        if out.shape != q.shape or out.dtype != torch.float32 or not out.is_contiguous():
+            raise ValueError("out must be a contiguous fp32 tensor shaped like q")
+        if lse is not None and (lse.shape != q.shape[:2] or lse.dtype != torch.float32 or not lse.is_contiguous()):
+            raise ValueError("lse must be a contiguous fp32 [batch, n_q_heads] tensor")
+        N.check(N.lib().aatc_decode_attn_noalloc(ctypes.byref(self._struct), q.data_ptr(), int(q.shape[1]),
+                                                 self._seq_ptr(seq_lens), int(max_seq_len), float(scale),
+                                                 out.data_ptr(), None if lse is None else lse.data_ptr(),
+                                                 _stream_ptr(stream)))
+        return out, lse
+
     def _seq_ptr(self, seq_lens):
         import torch
         if seq_lens is None:

@@ -6,6 +6,13 @@
 #include "aatc_seg_kernel.h"
 
 #include <cstdio>
+#include <mutex>
+
+// Workspace of aatc_decode_attn_noalloc: a fixed array in device memory, one copy per GPU the
+// library runs on, kept until the process ends.  Host code never passes its name to a kernel
+// (on the host it is only a stand-in for the symbol): it uses the device address that
+// hipGetSymbolAddress returns, once per device.
+static __device__ __align__(256) unsigned char scratch[AATC_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -118,9 +125,9 @@ size_t aatc_decode_attn_workspace_bytes(const aatc_cache* c, int32_t n_q_heads, 
 
 namespace {
 
-// Shared argument checks and plan of the three decode-attention entry points.
-aatc_status check_and_plan(const aatc_cache* c, int32_t n_q, int64_t max_seq, void* ws, size_t ws_bytes, Plan* p) {
-  if (!c || !ws) return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "null pointer");
+// Shared argument checks and plan of the decode-attention entry points (all but the workspace).
+aatc_status check_cache_and_plan(const aatc_cache* c, int32_t n_q, int64_t max_seq, Plan* p) {
+  if (!c) return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "null pointer");
   if (c->d != AATC_D) return aatc::fail(AATC_ERR_UNSUPPORTED, "d=%d (only 128)", c->d);
   if (c->batch < 1 || c->n_kv_heads < 1 || n_q < 1) return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "shape");
   if (n_q % c->n_kv_heads) return aatc::fail(AATC_ERR_UNSUPPORTED, "n_q_heads %% n_kv_heads != 0");
@@ -133,15 +140,25 @@ aatc_status check_and_plan(const aatc_cache* c, int32_t n_q, int64_t max_seq, vo
     return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "v_tiles %d", c->v_tiles);
   if (!c->k_calib || !c->v_calib || (!c->k_codes && c->k_bits > 0) || (!c->v_codes && c->v_bits > 0))
     return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "null cache pointer");
-  if ((reinterpret_cast<uintptr_t>(c->k_codes) & 15) || (reinterpret_cast<uintptr_t>(c->v_codes) & 15) ||
-      (reinterpret_cast<uintptr_t>(ws) & 255))
-    return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "codes must be 16-byte and workspace 256-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(c->k_codes) & 15) || (reinterpret_cast<uintptr_t>(c->v_codes) & 15))
+    return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "codes must be 16-byte aligned");
   if (max_seq < 0 || max_seq > c->capacity_tokens)
     return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "max_seq_len %lld > capacity", (long long)max_seq);
   *p = make_plan(c, n_q, max_seq);
-  const size_t need = align256(p->part_bytes) + align256(p->offs_bytes);
-  if (ws_bytes < need) return aatc::fail(AATC_ERR_BUFFER_TOO_SMALL, "workspace %zu < %zu", ws_bytes, need);
   if (!p->fits) return aatc::fail(AATC_ERR_UNSUPPORTED, "tiles of %d+%d bits do not fit LDS", c->k_bits, c->v_bits);
+  return AATC_OK;
+}
+
+size_t plan_workspace(const Plan& p) { return align256(p.part_bytes) + align256(p.offs_bytes); }
+
+aatc_status check_and_plan(const aatc_cache* c, int32_t n_q, int64_t max_seq, void* ws, size_t ws_bytes, Plan* p) {
+  if (!ws) return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "null pointer");
+  if (reinterpret_cast<uintptr_t>(ws) & 255)
+    return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  const aatc_status r = check_cache_and_plan(c, n_q, max_seq, p);
+  if (r != AATC_OK) return r;
+  const size_t need = plan_workspace(*p);
+  if (ws_bytes < need) return aatc::fail(AATC_ERR_BUFFER_TOO_SMALL, "workspace %zu < %zu", ws_bytes, need);
   return AATC_OK;
 }
 
@@ -218,6 +235,59 @@ aatc_status aatc_decode_attn(const aatc_cache* c, const float* q, int32_t n_q, c
   if (!q || !out) return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "null pointer");
   Plan p;
   aatc_status r = check_and_plan(c, n_q, max_seq, ws, ws_bytes, &p);
+  if (r != AATC_OK) return r;
+  auto st = static_cast<hipStream_t>(stream);
+  r = launch_partial(c, p, q, n_q, seq_lens, 0, max_seq, scale, ws, st);
+  if (r != AATC_OK) return r;
+  return launch_merge(c, p, n_q, seq_lens, 0, max_seq, out, lse, ws, st);
+}
+
+}  // extern "C"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];            // device address of `scratch` on each device, once known
+
+// The current device's copy of `scratch`, looked up on the first call on that device.
+aatc_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return aatc::fail(AATC_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return aatc::fail(AATC_ERR_UNSUPPORTED, "device %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return aatc::fail(AATC_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return AATC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+aatc_status aatc_decode_attn_noalloc(const aatc_cache* c, const float* q, int32_t n_q, const int32_t* seq_lens,
+                                     int64_t max_seq, float scale, float* out, float* lse, void* stream) {
+  aatc::clear_error();
+  if (!q || !out) return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "null pointer");
+  // every argument is checked before the scratch address is looked up
+  Plan p;
+  aatc_status r = check_cache_and_plan(c, n_q, max_seq, &p);
+  if (r != AATC_OK) return r;
+  const size_t need = plan_workspace(p);
+  if (need > AATC_NOALLOC_SCRATCH_BYTES)
+    return aatc::fail(AATC_ERR_BUFFER_TOO_SMALL,
+                      "this step needs %zu bytes of partial records, more than the %u-byte static workspace of "
+                      "aatc_decode_attn_noalloc (call aatc_decode_attn with a workspace instead)",
+                      need, static_cast<unsigned>(AATC_NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  r = scratch_address(&ws);
   if (r != AATC_OK) return r;
   auto st = static_cast<hipStream_t>(stream);
   r = launch_partial(c, p, q, n_q, seq_lens, 0, max_seq, scale, ws, st);

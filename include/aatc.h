@@ -332,6 +332,25 @@ aatc_status aatc_decode_attn(const aatc_cache* cache, const float* q_dev, int32_
                              size_t workspace_bytes, void* stream);
 
 /*
+ * aatc_decode_attn_noalloc -- device, async; aatc_decode_attn without a caller workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  It allocates nothing: the partial records go to a static
+ * array of AATC_NOALLOC_SCRATCH_BYTES in device memory, one per GPU, held until the process
+ * ends; its device address is looked up once per device on the first call there (the current
+ * device, which must be the one `stream` belongs to).
+ *   Arguments, results and errors as aatc_decode_attn, minus the workspace.  A step whose
+ *   records need more than AATC_NOALLOC_SCRATCH_BYTES (aatc_decode_attn_workspace_bytes) ->
+ *   BUFFER_TOO_SMALL before anything is queued.
+ *   Every call on one GPU uses that GPU's single array, so calls that may overlap in time on one
+ *   GPU (different streams, or other threads) race; order them on one stream.  The array keeps
+ *   the last call's records; nothing in it needs clearing between calls.
+ */
+#define AATC_NOALLOC_SCRATCH_BYTES (8u << 20)
+aatc_status aatc_decode_attn_noalloc(const aatc_cache* cache, const float* q_dev, int32_t n_q_heads,
+                                     const int32_t* seq_lens_dev, int64_t max_seq_len, float softmax_scale,
+                                     float* out_dev, float* lse_dev, void* stream);
+
+/*
  * aatc_decode_attn_partial and aatc_decode_attn_merge -- the two halves of aatc_decode_attn,
  * launched by it back to back; called separately they let a caller time or overlap the halves,
  * or merge the partial states of several sequence shards.  [SPECTRA Abstract: the cache pass
