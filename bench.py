@@ -23,6 +23,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+FP64_PEAK_TFLOPS = 78.6
 
 
 def parse():
@@ -40,6 +41,10 @@ def parse():
     p.add_argument("--quiet", action="store_true")
     p.add_argument("--copy-calib", action="store_true",
                    help="also run one plain 256 MiB device copy (scales HBM counters of a profiler run)")
+    p.add_argument("--no-encode", action="store_true", help="skip the encode rooflines")
+    p.add_argument("--no-folded", action="store_true", help="skip the folded all-layers launch")
+    p.add_argument("--no-loops", action="store_true", help="skip the append + decode loops")
+    p.add_argument("--only-headline", action="store_true", help="headline step and roofline only")
     return p.parse_args()
 
 
@@ -48,7 +53,7 @@ def log(args, *a):
         print(*a, file=sys.stderr, flush=True)
 
 
-def build_layer(cfg, layer, n_tokens, device):
+def build_layer(cfg, layer, n_tokens, device, capacity=None):
     """Calibrate (host), draw the context on the GPU, encode it; returns (cache, q, host key sample)."""
     import torch
     import synth
@@ -58,7 +63,7 @@ def build_layer(cfg, layer, n_tokens, device):
         for t, dst in ((synth.K, kb), (synth.V, vb)):
             cal = synth.draw(cfg.idx, layer, h, t, "calib", cfg.n_calib, dtype=cfg.dtype, marginal=cfg.marginal)
             dst.append(api.calibrate(cal if cfg.dtype == "f32" else synth.bf16_bits(cal), cfg.rotation, cfg.bits_per_elem))
-    cap = -(-n_tokens // 64) * 64
+    cap = -(-max(n_tokens, capacity or 0) // 64) * 64
     cache = api.CompressedKVCache(kb, vb, cfg.batch, cap, device=device)
     ksample = []
     for t in (synth.K, synth.V):
@@ -114,40 +119,295 @@ def algorithmic_bytes(cfg, n_tokens, cache):
     return codes, codes + tables + qo
 
 
-def cpu_baseline(cfg, n_tokens):
-    """The oracle on a bounded sample: one KV head's decode attention over a token sample."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def oracle_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] + [1]))
+    except Exception:  # pragma: no cover
+        return os.cpu_count()
+
+
+# token samples of the oracle per workload: about 3-5 s of host work each
+CPU_SAMPLE = {1: 4096, 2: 8192, 3: 8192, 4: 16384}
+
+
+def cpu_baseline_config(idx, min_s=2.0):
+    """The oracle on one KV head of one workload: calibrate (K and V), encode a token sample (K and
+    V), and decode attention of the head's q-head group over the sample, repeated for min_s."""
     import oracle as O
     import synth
-    sample = min(n_tokens, 16384)
-    h = 0
-    arts = [O.calibrate(synth.draw(cfg.idx, 0, h, t, "calib", cfg.n_calib, dtype=cfg.dtype, marginal=cfg.marginal),
-                        cfg.rotation, cfg.bits_per_elem) for t in (synth.K, synth.V)]
-    xs = [synth.draw(cfg.idx, 0, h, t, "context", sample, dtype=cfg.dtype, marginal=cfg.marginal)
+    cfg = synth.CONFIGS[idx]
+    sample = min(cfg.n_tokens, CPU_SAMPLE[idx])
+    cals = [synth.draw(cfg.idx, 0, 0, t, "calib", cfg.n_calib, dtype=cfg.dtype, marginal=cfg.marginal)
+            for t in (synth.K, synth.V)]
+    t0 = time.perf_counter()
+    arts = [O.calibrate(c, cfg.rotation, cfg.bits_per_elem) for c in cals]
+    cal_s = (time.perf_counter() - t0) / 2
+    xs = [synth.draw(cfg.idx, 0, 0, t, "context", sample, dtype=cfg.dtype, marginal=cfg.marginal)
           for t in (synth.K, synth.V)]
+    t0 = time.perf_counter()
     codes = [O.encode_codes(xs[i], arts[i]) for i in range(2)]
+    enc_s = time.perf_counter() - t0
     q = synth.queries(cfg.idx, 0, cfg.group, 1, [xs[0]])
     t0 = time.perf_counter()
     reps = 0
     while True:
         O.decode_attention(q, [codes[0]], [codes[1]], [arts[0]], [arts[1]])
         reps += 1
-        if time.perf_counter() - t0 > 10.0:
+        if time.perf_counter() - t0 > min_s:
             break
     dt = (time.perf_counter() - t0) / reps
     nbytes = sample * (arts[0]["B"] + arts[1]["B"]) / 8.0
-    t1 = time.perf_counter()
-    for t in range(2):
-        O.encode_codes(xs[t], arts[t])
-    enc = time.perf_counter() - t1
+    return {"workload": cfg.name, "sample": "1 KV head x %d tokens x %d q heads" % (sample, cfg.group),
+            "calibrate_s_per_tensor": round(cal_s, 4),
+            "encode_tokens_per_s": round(sample / enc_s, 1),
+            "decode_attn_s": round(dt, 5), "decode_attn_gbs": round(nbytes / dt / 1e9, 5), "reps": reps}
+
+
+def cpu_baseline(cfg, n_tokens):
+    """The oracle as it stands on the host cores: the headline workload's decode attention in the
+    metric's unit, plus calibrate / encode / decode figures for each of the four workloads."""
+    per = {str(i): cpu_baseline_config(i) for i in (1, 2, 3, 4)}
+    head = per[str(cfg.idx)] if str(cfg.idx) in per else per["4"]
+    return {"value": head["decode_attn_gbs"], "unit": "GB/s", "cores": oracle_threads(), "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": "%s: %s (decode attention = reconstruct + fp64 softmax attention; the same "
+                      "algorithmic compressed bytes per second as the GPU figure)" % (head["workload"], head["sample"]),
+            "per_workload": per}
+
+
+def gpu_info():
+    """Device name and the shader / memory clocks rocm-smi reports (None where unavailable)."""
+    import re
+    import subprocess
+    import torch
+    info = {"name": torch.cuda.get_device_name(0), "sclk_mhz": None, "mclk_mhz": None}
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
+        for line in r.stdout.splitlines():
+            m = re.search(r"(sclk|mclk) clock level: \d+: \((\d+)Mhz\)", line)
+            if m and info[m.group(1) + "_mhz"] is None:
+                info[m.group(1) + "_mhz"] = int(m.group(2))
     except Exception:  # pragma: no cover
-        cores = os.cpu_count()
-    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": int(cores), "kind": "oracle",
-            "sample": "1 KV head x %d tokens x %d q heads (decode attention = reconstruct + fp64 softmax "
-                      "attention), %d reps; encode %.0f tokens/s (K+V, 1 head)" % (sample, cfg.group, reps,
-                                                                                 sample / enc)}
+        pass
+    return info
+
+
+def timed_graph(fn, reps, st):
+    """Capture fn() in a graph, replay it reps times between HIP events on stream st; returns ms
+    per replay (the launches back to back, without host overheads)."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    s2 = torch.cuda.Stream()
+    s2.wait_stream(st)
+    with torch.cuda.stream(s2):
+        fn()
+    st.wait_stream(s2)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        fn()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(reps):
+        g.replay()
+    e1.record(st)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def read_probe(dev, st, nbytes=1 << 30, reps=20):
+    """Plain streaming read of a 1 GiB buffer (aatc_probe_read): the read bandwidth this GPU
+    delivers to a kernel that does nothing else."""
+    import torch
+    from compressed_decode_attention_head_amd import api
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    sink = torch.empty(2048 * 16, dtype=torch.uint8, device=dev)
+    ms = timed_graph(lambda: api.probe_read(buf, sink), reps, st)
+    del buf
+    return {"kernel": "k_read_probe (aatc_probe_read: 16-byte non-temporal loads, nothing else)",
+            "bytes": nbytes, "us": round(ms * 1e3, 2), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+
+
+def cold_layer_latency(dev, st, cache, q, n_tokens, ws, out, lse, reps=7):
+    """One layer's decode step (aatc_decode_attn: cache pass + merge) right after writing 512 MB of
+    other memory, so that neither the cache nor the tables sit in the last-level cache; the median
+    of reps, with an event pair around the call on its stream."""
+    import torch
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    ms = []
+    for r in range(reps):
+        flush.fill_(r & 255)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        cache.decode_attn(q, n_tokens, workspace=ws, out=out, lse=lse)
+        e1.record(st)
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    del flush
+    return float(np.median(ms))
+
+
+def encode_rooflines(args, dev, st):
+    """Encode (aatc_encode: rotate, quantize, pack) against its roofline, inputs above the 256 MB
+    last-level cache: four independent 128K-token layers' keys (4 x 134 MB of bf16) of the
+    Walsh-Hadamard 1.33-bit workload against HBM bandwidth, and four 32K-token layers' keys
+    (4 x 67 MB) of the KLT 2.76-bit workload against the fp64 peak (2 d^2 flops per vector)."""
+    import torch
+    import synth
+    from compressed_decode_attention_head_amd import api
+    res = {}
+    for idx, n_lay in ((4, 4), (2, 4)):
+        cfg = synth.CONFIGS[idx]
+        n = cfg.n_tokens
+        caches, xs = [], []
+        for l in range(n_lay):
+            kb, vb = [], []
+            for h in range(cfg.n_kv_heads):
+                for t, dst in ((synth.K, kb), (synth.V, vb)):
+                    cal = synth.draw(cfg.idx, l, h, t, "calib", cfg.n_calib, dtype=cfg.dtype, marginal=cfg.marginal)
+                    dst.append(api.calibrate(synth.bf16_bits(cal), cfg.rotation, cfg.bits_per_elem))
+            caches.append(api.CompressedKVCache(kb, vb, 1, n, device=dev))
+            x = torch.empty((1, cfg.n_kv_heads, n, 128), dtype=torch.bfloat16, device=dev)
+            for h in range(cfg.n_kv_heads):
+                x[0, h] = synth.draw_device(cfg.idx, l, h, synth.K, n, dtype="bf16", marginal=cfg.marginal, device=dev)
+            xs.append(x)
+        torch.cuda.synchronize()
+
+        def enc():
+            for c, x in zip(caches, xs):
+                c.encode(synth.K, x)
+
+        ms = timed_graph(enc, max(3, args.steps // 4), st) / n_lay
+        vectors = cfg.n_kv_heads * n
+        kbits = caches[0].k_bits
+        nbytes = vectors * (128 * 2 + kbits / 8.0)
+        flops = vectors * 2.0 * 128 * 128
+        ent = {"workload": cfg.name, "rotation": cfg.rotation, "kernel": "k_encode",
+               "vectors_per_launch": vectors, "us_per_launch": round(ms * 1e3, 2),
+               "vectors_per_s": round(vectors / (ms * 1e-3), 1),
+               "tokens_per_s_k_and_v": round(n / (ms * 1e-3) / 2, 1),
+               "bytes_per_launch": nbytes, "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+               "layers_cycled": n_lay, "input_mb_cycled": round(n_lay * vectors * 256 / 1e6, 1)}
+        if cfg.rotation == "wht":
+            ent["roofline"] = {"bound": "hbm", "achieved": ent["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                               "frac": round(ent["gbs"] / HBM_PEAK_GBS, 4)}
+        else:
+            tf = flops / (ms * 1e-3) / 1e12
+            ent["roofline"] = {"bound": "fp64", "achieved": round(tf, 2), "peak": FP64_PEAK_TFLOPS, "unit": "TFLOP/s",
+                               "frac": round(tf / FP64_PEAK_TFLOPS, 4), "flops_per_launch": flops}
+        res[cfg.rotation] = ent
+        del caches, xs
+        torch.cuda.synchronize()
+    return res
+
+
+def folded_launch(args, cfg, layers, dev, st, n_tokens):
+    """Every layer's cache in one launch: the 28 layers' KV heads folded into the head axis of a
+    single cache (112 KV heads, 784 q heads), so one cache pass streams all 624 MB.  The queries of
+    different layers are not available together during real decoding; this separates the
+    stream rate of the pass from the fixed costs of a launch."""
+    import torch
+    from compressed_decode_attention_head_amd import api
+    kb = [b for lay in layers for b in lay[0].k_blobs_host]
+    vb = [b for lay in layers for b in lay[0].v_blobs_host]
+    big = api.CompressedKVCache(kb, vb, cfg.batch, layers[0][0].capacity, device=dev)
+    kw = layers[0][0].k_codes.numel() - 4
+    vw = layers[0][0].v_codes.numel() - 4
+    for l, lay in enumerate(layers):
+        big.k_codes[l * kw:(l + 1) * kw].copy_(lay[0].k_codes[:kw])
+        big.v_codes[l * vw:(l + 1) * vw].copy_(lay[0].v_codes[:vw])
+    q = torch.cat([lay[1] for lay in layers], dim=1).contiguous()
+    ws = big.new_workspace(q.shape[1], n_tokens)
+    out = torch.empty_like(q)
+    lse = torch.empty((cfg.batch, q.shape[1]), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    # the folded call gives every layer's result of the per-layer calls (up to the order of the
+    # split merge, which depends on the number of splits)
+    ref = []
+    for lay in layers:
+        o, _ = lay[0].decode_attn(lay[1], n_tokens)
+        ref.append(o)
+    big.decode_attn(q, n_tokens, workspace=ws, out=out, lse=lse)
+    torch.cuda.synchronize()
+    diff = float((torch.cat(ref, dim=1) - out).abs().max())
+    reps = max(5, args.steps)
+    part = timed_graph(lambda: big.decode_attn_partial(q, n_tokens, ws), reps, st)
+    call = timed_graph(lambda: big.decode_attn(q, n_tokens, workspace=ws, out=out, lse=lse), reps, st)
+    nbytes = len(layers) * cfg.batch * cfg.n_kv_heads * n_tokens * (big.k_bits + big.v_bits) / 8.0
+    del big
+    return {"layers_folded": len(layers), "kv_heads": len(kb), "q_heads": int(q.shape[1]),
+            "bytes_per_launch": nbytes, "cache_pass_us": round(part * 1e3, 2), "call_us": round(call * 1e3, 2),
+            "cache_pass_gbs": round(nbytes / (part * 1e-3) / 1e9, 1),
+            "cache_pass_frac_of_peak": round(nbytes / (part * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "call_gbs": round(nbytes / (call * 1e-3) / 1e9, 1),
+            "max_abs_diff_vs_per_layer_calls": diff}
+
+
+def append_decode_loop(args, dev, st):
+    """The batch-16 workload as a decode loop: 4 layers of 16 sequences x 8 KV heads with 8192
+    prefill tokens (KLT, 4 bits per element), then 64 steps; each step appends one encoded K and V
+    token per sequence and head to every layer (aatc_encode at the next offset) and runs every
+    layer's decode attention over the grown cache.  Eager launches, timed with HIP events."""
+    import torch
+    import synth
+    cfg = synth.CONFIGS[3]
+    steps, n0 = cfg.decode_steps, cfg.n_tokens
+    cap = n0 + steps
+    lays = []
+    for l in range(cfg.n_layers):
+        cache, q, _ = build_layer(cfg, l, n0, dev, capacity=cap)
+        new = {}
+        for t in (synth.K, synth.V):
+            x = torch.empty((cfg.batch, cfg.n_kv_heads, steps, 128), dtype=torch.bfloat16, device=dev)
+            for b in range(cfg.batch):
+                for h in range(cfg.n_kv_heads):
+                    x[b, h] = synth.draw_device(cfg.idx, l, h, t, steps, dtype="bf16", device=dev, extra=1000 + b)
+            new[t] = x
+        ws = cache.new_workspace(cfg.n_q_heads, cap)
+        out = torch.empty_like(q)
+        lse = torch.empty((cfg.batch, cfg.n_q_heads), dtype=torch.float32, device=dev)
+        lays.append((cache, q, new, ws, out, lse))
+    torch.cuda.synchronize()
+
+    def run(s):
+        for cache, q, new, ws, out, lse in lays:
+            for t in (synth.K, synth.V):
+                cache.encode(t, new[t][:, :, s:s + 1], token_offset=n0 + s)
+            cache.decode_attn(q, n0 + s + 1, workspace=ws, out=out, lse=lse)
+
+    run(0)                                         # warm: the first step's encode rewrites the same token
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for s_ in range(steps):
+        run(s_)
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    kb, vb = lays[0][0].k_bits, lays[0][0].v_bits
+    avg_tokens = n0 + (steps + 1) / 2.0
+    nbytes = cfg.n_layers * cfg.batch * cfg.n_kv_heads * avg_tokens * (kb + vb) / 8.0
+    del lays
+    return {"workload": cfg.name, "layers": cfg.n_layers, "steps": steps, "prefill_tokens": n0,
+            "ms_per_step": round(ms, 4), "us_per_layer_step": round(ms * 1e3 / cfg.n_layers, 2),
+            "decode_tokens_per_s": round(cfg.batch * 1e3 / ms, 1),
+            "cache_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "calls_per_layer_step": "aatc_encode K + aatc_encode V (1 token per sequence and head) + aatc_decode_attn",
+            "timing": "eager launches, HIP events around all steps"}
 
 
 def dense_comparator(args, cfg, n_tokens, qs, dev, st, ms_compressed_step):
@@ -220,7 +480,7 @@ def tiered_segments(args, dev, st):
     cfg = synth.CONFIGS[5]
     n, n_kv, n_q, n_layers = cfg.n_tokens, cfg.n_kv_heads, cfg.n_q_heads, cfg.n_layers
     K, V = synth.K, synth.V
-    calls, keep = [], []
+    calls, keep, raws = [], [], []
     total_bytes, pop = 0, {0: 0, 2: 0, 4: 0, 16: 0}
     for l in range(n_layers):
         blobs = {(tau, t): [api.calibrate(synth.bf16_bits(synth.draw(cfg.idx, l, h, t, "calib", cfg.n_calib)), "klt",
@@ -238,7 +498,8 @@ def tiered_segments(args, dev, st):
         for tau in (2, 4, 16):
             idx = [torch.from_numpy(np.nonzero(tiers[h] == tau)[0]).to(dev) for h in range(n_kv)]
             counts = [int(i.numel()) for i in idx]
-            cap = max(64, -(-max(counts) // 64) * 64)
+            # the raw tier has room for the tokens the decode loop appends
+            cap = max(64, -(-(max(counts) + (cfg.decode_steps if tau == 16 else 0)) // 64) * 64)
             sl = torch.tensor([counts], dtype=torch.int32, device=dev)
             xt = {}
             for t in (K, V):
@@ -249,6 +510,7 @@ def tiered_segments(args, dev, st):
                 segs.append({"k_raw": xt[K], "v_raw": xt[V], "seq_lens": sl, "max_seq_len": max(counts)})
                 keep += [xt[K], xt[V], sl]
                 total_bytes += sum(counts) * 2 * 128 * 2
+                raw = (xt[K], xt[V], counts)
             else:
                 cache = api.CompressedKVCache(blobs[(tau, K)], blobs[(tau, V)], 1, cap, device=dev)
                 for t in (K, V):
@@ -263,6 +525,7 @@ def tiered_segments(args, dev, st):
         out = torch.empty_like(q)
         lse = torch.empty((1, n_q), dtype=torch.float32, device=dev)
         calls.append((segs, q, ws, out, lse))
+        raws.append(raw)
     torch.cuda.synchronize()
 
     def tstep():
@@ -292,13 +555,57 @@ def tiered_segments(args, dev, st):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
     tot = sum(pop.values())
-    return {"workload": cfg.name, "layers_per_step": n_layers, "avg_bits": cfg.bits_per_elem,
-            "tier_fractions": {str(t): round(pop[t] / tot, 4) for t in (0, 2, 4, 16)},
-            "bytes_per_step": total_bytes, "ms_per_step": round(ms, 4),
-            "us_per_layer": round(ms * 1e3 / n_layers, 3), "gbs": round(total_bytes / (ms * 1e-3) / 1e9, 1),
-            "frac_of_peak": round(total_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "calls": "aatc_decode_attn_segments: cache pass + merge per coded tier, dense pass for raw, "
-                     "one state merge"}
+    res = {"workload": cfg.name, "layers_per_step": n_layers, "avg_bits": cfg.bits_per_elem,
+           "tier_fractions": {str(t): round(pop[t] / tot, 4) for t in (0, 2, 4, 16)},
+           "bytes_per_step": total_bytes, "ms_per_step": round(ms, 4),
+           "us_per_layer": round(ms * 1e3 / n_layers, 3), "gbs": round(total_bytes / (ms * 1e-3) / 1e9, 1),
+           "frac_of_peak": round(total_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "calls": "aatc_decode_attn_segments: cache pass + merge per coded tier, dense pass for raw, "
+                    "one state merge"}
+    if not args.no_loops:
+        res["decode_loop"] = tiered_append_loop(cfg, calls, raws, dev, st)
+    return res
+
+
+def tiered_append_loop(cfg, calls, raws, dev, st):
+    """The tiered workload's decode loop: 256 steps, each appending one token per KV head to every
+    layer's raw bf16 tier (tokens after prefill are kept at full precision) and running every
+    layer's multi-segment decode attention over the grown raw tier.  Eager launches, HIP events."""
+    import torch
+    import synth
+    from compressed_decode_attention_head_amd import api
+    steps = cfg.decode_steps
+    n_kv, n_q = cfg.n_kv_heads, cfg.n_q_heads
+    loop = []
+    for l, ((segs, q, ws, out, lse), (rk, rv, counts)) in enumerate(zip(calls, raws)):
+        sl = torch.tensor([counts], dtype=torch.int32, device=dev)
+        segs2 = [dict(sg) for sg in segs]
+        segs2[-1]["seq_lens"] = sl                 # the raw tier is the last segment
+        segs2[-1]["max_seq_len"] = max(counts) + steps
+        ws2 = torch.empty(api.decode_attn_segments_workspace_bytes(segs2, 1, n_kv, n_q), dtype=torch.uint8,
+                          device=dev)
+        new = [torch.stack([synth.draw_device(cfg.idx, l, h, t, steps, device=dev, extra=2000) for h in range(n_kv)])
+               for t in (synth.K, synth.V)]      # [n_kv, steps, 128] each
+        base = torch.tensor(counts, dtype=torch.int64, device=dev)
+        loop.append((segs2, q, ws2, out, lse, rk, rv, new, base, sl))
+    heads = torch.arange(n_kv, device=dev)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for s_ in range(steps):
+        for segs2, q, ws2, out, lse, rk, rv, new, base, sl in loop:
+            pos = base + s_
+            rk[0, heads, pos] = new[0][:, s_]
+            rv[0, heads, pos] = new[1][:, s_]
+            sl += 1
+            api.decode_attn_segments(segs2, q, 1, n_kv, workspace=ws2, out=out, lse=lse)
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"steps": steps, "layers": len(loop), "ms_per_step": round(ms, 4),
+            "us_per_layer_step": round(ms * 1e3 / len(loop), 2), "decode_tokens_per_s": round(1e3 / ms, 1),
+            "calls_per_layer_step": "2 row writes into the raw tier, a length increment, aatc_decode_attn_segments",
+            "timing": "eager launches, HIP events around all steps"}
 
 
 def main():
@@ -312,6 +619,8 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU", file=sys.stderr)
         sys.exit(1)
+    if args.only_headline:
+        args.no_dense = args.no_tiers = args.no_cpu_baseline = args.no_encode = args.no_folded = args.no_loops = True
     cfg = synth.CONFIGS[args.config]
     n_tokens = args.tokens or cfg.n_tokens
     n_layers = args.layers or cfg.n_layers
@@ -325,7 +634,7 @@ def main():
         out = torch.empty_like(q)
         lse = torch.empty((cfg.batch, cfg.n_q_heads), dtype=torch.float32, device=dev)
         layers.append((cache, q, ws, out, lse))
-        log(args, "layer %d ready" % l)
+    log(args, "%d layers ready" % n_layers)
     torch.cuda.synchronize()
     codes_b, alg_b = algorithmic_bytes(cfg, n_tokens, layers[0][0])
 
@@ -350,7 +659,7 @@ def main():
     call_ms = float(np.mean(call_ms))
     log(args, "decode_attn call: %.2f us per layer" % (call_ms * 1e3))
 
-    # --- timed steps (graph replay of the whole step unless --no-graph)
+    # --- timed steps (graph replay of the whole step unless --no-graph), an event per step
     runner = step
     graph_used = False
     if not args.no_graph:
@@ -371,34 +680,15 @@ def main():
     for _ in range(args.warmup):
         runner()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(st)
-    for _ in range(args.steps):
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    marks[0].record(st)
+    for i in range(args.steps):
         runner()
-    e1.record(st)
+        marks[i + 1].record(st)
     torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / args.steps
+    ms_step = marks[0].elapsed_time(marks[-1]) / args.steps
+    per_step = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
     gbs = codes_b * n_layers / (ms_step * 1e-3) / 1e9
-
-    # --- encode throughput (prefill of one layer: all heads, K and V)
-    cache0 = layers[0][0]
-    x = torch.empty((cfg.batch, cfg.n_kv_heads, n_tokens, 128), dtype=synth.torch_dtype(cfg.dtype), device=dev)
-    for h in range(cfg.n_kv_heads):
-        x[0, h] = synth.draw_device(cfg.idx, 0, h, synth.K, n_tokens, dtype=cfg.dtype, marginal=cfg.marginal,
-                                    device=dev)
-    cache0.encode(0, x)
-    torch.cuda.synchronize()
-    ee0, ee1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = 3
-    ee0.record(st)
-    for _ in range(reps):
-        cache0.encode(0, x)
-        cache0.encode(1, x)
-    ee1.record(st)
-    torch.cuda.synchronize()
-    enc_ms = ee0.elapsed_time(ee1) / reps
-    enc_tok_s = n_tokens * cfg.batch / (enc_ms * 1e-3)
-    del x
 
     # --- the dominant kernel alone: the cache pass (aatc_decode_attn_partial -> k_attn_main),
     # HIP events around each launch on the stream it runs on; then the merge kernel the same way
@@ -421,27 +711,7 @@ def main():
         # average launch duration without per-launch event and host overheads
         if not graph_used:
             return None
-        g2 = torch.cuda.CUDAGraph()
-        s3 = torch.cuda.Stream()
-        s3.wait_stream(st)
-        with torch.cuda.stream(s3):
-            for lay in layers:
-                fn(*lay)
-        st.wait_stream(s3)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g2):
-            for lay in layers:
-                fn(*lay)
-        g2.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = max(5, args.steps)
-        e0.record(st)
-        for _ in range(reps):
-            g2.replay()
-        e1.record(st)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / (reps * len(layers))
+        return timed_graph(lambda: [fn(*lay) for lay in layers], max(5, args.steps), st) / len(layers)
 
     part_fn = lambda cache, q, ws, out, lse: cache.decode_attn_partial(q, n_tokens, ws)
     merge_fn = lambda cache, q, ws, out, lse: cache.decode_attn_merge(q.shape[1], n_tokens, ws, out, lse)
@@ -456,6 +726,10 @@ def main():
         part_eager_ms * 1e3, merge_eager_ms * 1e3))
     achieved = codes_b / (part_ms * 1e-3) / 1e9
     traffic = measured_traffic(cfg, n_tokens)
+    c0, q0, ws0, out0, lse0 = layers[0]
+    cold_ms = cold_layer_latency(dev, st, c0, q0, n_tokens, ws0, out0, lse0)
+    probe = read_probe(dev, st)
+    log(args, "cold layer %.2f us; read probe %.0f GB/s" % (cold_ms * 1e3, probe["gbs"]))
     if args.copy_calib:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -478,30 +752,56 @@ def main():
         "config": {"workload": cfg.name, "layers_per_step": n_layers, "batch": cfg.batch,
                    "n_q_heads": cfg.n_q_heads, "n_kv_heads": cfg.n_kv_heads, "context": n_tokens,
                    "rotation": cfg.rotation, "bits_per_elem": cfg.bits_per_elem,
-                   "k_bits": cache0.k_bits, "v_bits": cache0.v_bits,
-                   "compression_vs_bf16": round(16 * 128 * 2 / (cache0.k_bits + cache0.v_bits), 3),
+                   "k_bits": layers[0][0].k_bits, "v_bits": layers[0][0].v_bits,
+                   "compression_vs_bf16": round(16 * 128 * 2 / (layers[0][0].k_bits + layers[0][0].v_bits), 3),
                    "graph": graph_used},
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
-        "encode_tokens_per_s": round(enc_tok_s, 1),
-        "encode_note": "one layer prefill, all KV heads, K and V, fp64 rotation+quantize",
+        "step_ms_percentiles": {"p10": round(float(np.percentile(per_step, 10)), 4),
+                                "p50": round(float(np.percentile(per_step, 50)), 4),
+                                "p90": round(float(np.percentile(per_step, 90)), 4)},
+        "cold_layer_us": round(cold_ms * 1e3, 2),
+        "cold_layer_note": "one layer's aatc_decode_attn right after a 512 MB write (median of 7)",
+        "read_probe": probe,
+        "pct_of_read_probe": round(100.0 * gbs / probe["gbs"], 2),
+        "gpu": gpu_info(),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "frac_of_read_probe": round(achieved / probe["gbs"], 4),
                      "kernel": "k_attn_main (the cache pass, one launch per layer)",
                      "bytes_per_launch": codes_b, "launch_us": round(part_ms * 1e3, 3),
                      "launch_timing": "graph of back-to-back launches" if part_graph_ms is not None else "eager events",
                      "launch_us_eager_events": round(part_eager_ms * 1e3, 3),
                      "merge_kernel_us": round(merge_ms * 1e3, 3), "call_us": round(call_ms * 1e3, 3)},
     }
+    if not args.no_folded and cfg.batch == 1:
+        log(args, "timing the folded all-layers launch")
+        res["folded_layers"] = folded_launch(args, cfg, layers, dev, st, n_tokens)
+        log(args, "folded: %.1f us, %.0f GB/s cache pass" % (res["folded_layers"]["cache_pass_us"],
+                                                           res["folded_layers"]["cache_pass_gbs"]))
     if not args.no_dense:
         log(args, "timing the dense bf16 comparator")
         res["dense_bf16"] = dense_comparator(args, cfg, n_tokens, [lay[1] for lay in layers], dev, st, ms_step)
         log(args, "dense bf16: %.2f us per layer, %.0f GB/s; compressed step is %.2fx faster" % (
             res["dense_bf16"]["us_per_layer"], res["dense_bf16"]["gbs"], res["dense_bf16"]["speedup_compressed_vs_dense"]))
+    del layers
+    torch.cuda.synchronize()
+    if not args.no_encode:
+        log(args, "timing encode")
+        enc = encode_rooflines(args, dev, st)
+        res["encode_tokens_per_s"] = enc["wht"]["tokens_per_s_k_and_v"]
+        res["encode_note"] = ("tokens/s of one 128K layer's prefill, all KV heads, K and V (k_encode over inputs "
+                              "cycled through 4 layers, above the last-level cache)")
+        res["encode_roofline"] = enc
+        log(args, "encode: WHT %.0f GB/s, KLT %.1f TFLOP/s" % (enc["wht"]["gbs"], enc["klt"]["roofline"]["achieved"]))
     if not args.no_tiers:
         log(args, "timing the tiered 128K layer")
         res["tiers"] = tiered_segments(args, dev, st)
         log(args, "tiers: %.2f us per layer, %.0f GB/s, tier fractions %s" % (
             res["tiers"]["us_per_layer"], res["tiers"]["gbs"], res["tiers"]["tier_fractions"]))
+    if not args.no_loops:
+        log(args, "timing the batch-16 append + decode loop")
+        res["append_decode_loop"] = append_decode_loop(args, dev, st)
+        log(args, "loop: %.3f ms per step" % res["append_decode_loop"]["ms_per_step"])
     if not args.no_cpu_baseline:
         log(args, "timing the oracle on the host")
         res["cpu_baseline"] = cpu_baseline(cfg, n_tokens)

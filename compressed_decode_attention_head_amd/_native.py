@@ -99,6 +99,10 @@ def lib():
     L.aatc_decode_attn.restype = ctypes.c_int
     L.aatc_decode_attn.argtypes = [ctypes.POINTER(Cache), vp, i32, vp, i64, ctypes.c_float, vp, vp, vp, sz, vp]
     L.aatc_decode_attn_partial.restype = ctypes.c_int
+    L.aatc_probe_read_sink_bytes.restype = sz
+    L.aatc_probe_read_sink_bytes.argtypes = []
+    L.aatc_probe_read.restype = ctypes.c_int
+    L.aatc_probe_read.argtypes = [vp, sz, vp, vp]
     L.aatc_decode_attn_noalloc.restype = ctypes.c_int
     L.aatc_decode_attn_noalloc.argtypes = [ctypes.POINTER(Cache), vp, i32, vp, i64, ctypes.c_float, vp, vp, vp]
     L.aatc_decode_attn_partial.argtypes = [ctypes.POINTER(Cache), vp, i32, vp, i64, ctypes.c_float, vp, sz, vp]
@@ -137,6 +141,7 @@ EXPORTS = ["aatc_status_string", "aatc_last_error", "aatc_calib_bytes", "aatc_bi
            "aatc_packed_bytes", "aatc_calibrate", "aatc_query_channel_weights", "aatc_calib_validate",
            "aatc_calib_v_tiles",
            "aatc_encode", "aatc_decode", "aatc_decode_attn_workspace_bytes", "aatc_decode_attn", "aatc_decode_attn_noalloc",
+           "aatc_probe_read_sink_bytes", "aatc_probe_read",
            "aatc_decode_attn_partial", "aatc_decode_attn_merge", "aatc_tier_distortions",
            "aatc_token_tiers", "aatc_decode_attn_segments_workspace_bytes", "aatc_decode_attn_segments",
            "aatc_decode_attn_dense_workspace_bytes", "aatc_decode_attn_dense", "aatc_query_moment",

@@ -240,6 +240,16 @@ def decode_attn_dense(k, v, q, max_seq_len, seq_lens=None, scale=0.0, workspace=
     return out, lse
 
 
+def probe_read(buf, sink=None, stream=None):
+    """aatc_probe_read: one streaming read of the device tensor `buf` (measurement helper)."""
+    import torch
+    if sink is None:
+        sink = torch.empty(N.lib().aatc_probe_read_sink_bytes(), dtype=torch.uint8, device=buf.device)
+    N.check(N.lib().aatc_probe_read(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(),
+                                    _stream_ptr(stream)))
+    return sink
+
+
 def _stream_ptr(stream):
     import torch
     s = stream if stream is not None else torch.cuda.current_stream()

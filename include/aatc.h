@@ -467,6 +467,18 @@ aatc_status aatc_decode_attn_dense(const void* k_dev, const void* v_dev, int32_t
                                    float* out_dev, float* lse_dev, void* workspace_dev,
                                    size_t workspace_bytes, void* stream);
 
+/*
+ * Measurement helper (not a step of the method).  aatc_probe_read -- device, async: reads
+ * `bytes` of device memory at src once with 16-byte loads and writes one XOR digest per
+ * workgroup to sink (aatc_probe_read_sink_bytes() bytes), so that the read bandwidth a plain
+ * streaming kernel reaches on this GPU can be timed beside the decode-attention pass.
+ *   Errors: null pointers, src or sink not 16-byte aligned, bytes 0 or not a multiple of 16 ->
+ *   INVALID_ARGUMENT; launch -> HIP.
+ */
+#define AATC_PROBE_WORKGROUPS 2048
+size_t aatc_probe_read_sink_bytes(void);
+aatc_status aatc_probe_read(const void* src, size_t bytes, void* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -32,7 +32,7 @@ Everything is fp64 NumPy/SciPy.  Inputs in fp32/bf16 are read as their exact fp6
 import math
 
 import numpy as np
-from scipy import optimize, special
+from scipy import linalg, optimize, special
 
 TILE = 64          # tokens per packed tile
 MAX_BITS = 8
@@ -42,7 +42,8 @@ __all__ = [
     "query_channel_weights", "query_moment", "transform_nova", "NOVA_EIG_FLOOR",
     "allocation_distortion", "value_term_weight", "joint_kv_split",
     "bits_budget", "waterfill_bits", "waterfill_theta", "uniform_quantizer_mse",
-    "uniform_quantizer_mse_deriv", "optimal_step", "quantizer_tables", "calibrate",
+    "uniform_quantizer_mse_deriv", "optimal_step", "lloyd_max_gaussian", "lloyd_max_mse",
+    "quantizer_tables", "calibrate",
     "rotate", "encode_codes", "dequantize", "reconstruct", "v_fields", "pack_k", "unpack_k",
     "pack_v", "unpack_v", "packed_words", "attention", "attention_streaming",
     "decode_attention", "rotated_scores", "tier_distortions", "token_tiers",
@@ -334,6 +335,81 @@ def optimal_step(b):
                            xtol=1e-300, rtol=4 * np.finfo(float).eps, maxiter=500)
 
 
+# ----------------------------------------------------------------------------------
+# Lloyd-Max scalar quantizer  [SPHERICAL KV page, NOVA-KV abstract: fixed-width uniform
+# scalar quantizers lose at low rates; "Ablation ..." page, OCTOPUS abstract: each coordinate
+# is quantized with the Lloyd-Max quantizer of the marginal it follows]
+#
+# The codebook of a channel with b bits is the MSE-optimal 2^b-level quantizer of N(0,1),
+# scaled by the channel's standard deviation and centred on its offset: reconstruction
+# y_hat = o + sigma l_c, cell boundaries at o + sigma t_k.  Lloyd's necessary conditions fix it:
+# every level is the mean of N(0,1) over its cell, every threshold the midpoint of its two
+# levels; for a log-concave density they have one solution.
+# ----------------------------------------------------------------------------------
+def _lm_centroids(t):
+    """Mean of N(0,1) over each cell [t_k, t_(k+1)) of the positive half-line (t_0 = 0, last cell
+    unbounded), with the cells' masses and the densities at the boundaries."""
+    tt = np.concatenate([t, [np.inf]])
+    dens = np.where(np.isinf(tt), 0.0, _phi(np.where(np.isinf(tt), 0.0, tt)))
+    tail = np.where(np.isinf(tt), 0.0, _upper_tail(np.where(np.isinf(tt), 0.0, tt)))
+    mass = tail[:-1] - tail[1:]
+    return (dens[:-1] - dens[1:]) / mass, mass, dens
+
+
+def lloyd_max_gaussian(b):
+    """Levels (2^b, ascending) and thresholds (2^b - 1, ascending) of the 2^b-level Lloyd-Max
+    quantizer of N(0,1).  By symmetry only the positive half is solved: h = 2^(b-1) levels
+    y_1 < ... < y_h, thresholds t_0 = 0 and t_k = (y_k + y_(k+1)) / 2.  Lloyd iterations
+    (levels <- cell means) bring the levels near the fixed point; Newton steps on
+    y - centroid(y) = 0, whose Jacobian is tridiagonal, then converge to rounding level."""
+    if b < 1:
+        raise ValueError("b >= 1")
+    h = 2 ** (b - 1)
+    if h == 1:
+        y = np.array([math.sqrt(2.0 / math.pi)])
+    else:
+        y = (np.arange(h) + 0.5) * (1.0 + 0.5 * b) / h       # a uniform start
+
+        def thresholds(y):
+            return np.concatenate([[0.0], 0.5 * (y[:-1] + y[1:])])
+
+        for _ in range(200):
+            y = _lm_centroids(thresholds(y))[0]
+        for _ in range(60):
+            t = thresholds(y)
+            c, mass, dens = _lm_centroids(t)
+            # d c_k / d t_k (left edge) and d c_k / d t_(k+1) (right edge)
+            dl = dens[:-1] * (c - t) / mass
+            dr = dens[1:] * (np.concatenate([t[1:], [0.0]]) - c) / mass
+            dl[0] = 0.0                                  # t_0 = 0 is fixed
+            # Jacobian of F(y) = y - c(y): t_k (k >= 1) moves with y_(k-1) and y_k by 1/2 each
+            diag = 1.0 - 0.5 * (dl + np.concatenate([dr[:-1], [0.0]]))
+            sub = -0.5 * dl[1:]                          # F_k with respect to y_(k-1)
+            sup = -0.5 * dr[:-1]                         # F_k with respect to y_(k+1)
+            ab = np.zeros((3, h))
+            ab[0, 1:] = sup
+            ab[1] = diag
+            ab[2, :-1] = sub
+            step = linalg.solve_banded((1, 1), ab, -(y - c))
+            y = y + step
+            if np.abs(step).max() <= 1e-17 * y.max():
+                break
+    t_pos = 0.5 * (y[:-1] + y[1:])
+    levels = np.concatenate([-y[::-1], y])
+    thresholds = np.concatenate([-t_pos[::-1], [0.0], t_pos])
+    return levels, thresholds
+
+
+def lloyd_max_mse(b):
+    """E[(Z - Q(Z))^2] of the Lloyd-Max quantizer of N(0,1): by the centroid condition it is
+    1 - sum_k P(cell k) l_k^2."""
+    levels, th = lloyd_max_gaussian(b)
+    edges = np.concatenate([[-np.inf], th, [np.inf]])
+    cdf = np.where(np.isinf(edges), (edges > 0).astype(float), special.ndtr(np.where(np.isinf(edges), 0.0, edges)))
+    mass = np.diff(cdf)
+    return float(1.0 - np.sum(mass * levels * levels))
+
+
 def quantizer_tables(r, mu, sigma2, bits):
     """Per-channel offset o = R mu, step Delta_i = sigma_i g(b_i) and 1/Delta_i.
 
@@ -353,8 +429,13 @@ def quantizer_tables(r, mu, sigma2, bits):
     return o, delta, inv
 
 
-def calibrate(x_cal, rotation="klt", bits_per_elem=2.0, max_bits=MAX_BITS, total_bits=None, q_cal=None):
+def calibrate(x_cal, rotation="klt", bits_per_elem=2.0, max_bits=MAX_BITS, total_bits=None, q_cal=None,
+              quantizer="uniform"):
     """Full calibration of one (head, tensor): statistics, rotation, bits, quantizer tables.
+
+    quantizer="uniform": the mid-rise uniform quantizer with step sigma_i g(b_i);
+    quantizer="lloyd-max": channel i's codebook is the Lloyd-Max quantizer of N(0,1) with b_i
+    bits scaled by s_i (sigma_i, or the coded-zero-variance substitute of quantizer_tables).
 
     q_cal (keys only): calibration queries of the head's q heads.  With an orthogonal
     rotation the bits then minimise the attention-aware distortion
@@ -380,8 +461,20 @@ def calibrate(x_cal, rotation="klt", bits_per_elem=2.0, max_bits=MAX_BITS, total
         weight = None if q_cal is None else query_channel_weights(r, q_cal)
     bits = waterfill_bits(s2, b_total, max_bits, weight)
     o, delta, inv = quantizer_tables(e, mu, s2, bits)
-    return {"R": r, "E": e, "mu": mu, "C": c, "sigma2": s2, "bits": bits, "B": b_total,
-            "o": o, "delta": delta, "inv_delta": inv, "rotation": rotation, "weight": weight}
+    art = {"R": r, "E": e, "mu": mu, "C": c, "sigma2": s2, "bits": bits, "B": b_total,
+           "o": o, "delta": delta, "inv_delta": inv, "rotation": rotation, "weight": weight,
+           "quantizer": quantizer}
+    if quantizer == "lloyd-max":
+        sig = np.sqrt(np.asarray(s2, dtype=np.float64))
+        ref = sig.max() if sig.max() > 0 else 1.0
+        scale = np.where(bits > 0, np.where(sig > 0, sig, math.ldexp(ref, -40)), 0.0)
+        with np.errstate(divide="ignore"):
+            inv_scale = np.where(scale > 0, 1.0 / np.where(scale > 0, scale, 1.0), 0.0)
+        art["scale"], art["inv_scale"] = scale, inv_scale
+        art["lm"] = {int(b): lloyd_max_gaussian(int(b)) for b in set(int(v) for v in bits) if b > 0}
+    elif quantizer != "uniform":
+        raise ValueError(quantizer)
+    return art
 
 
 # ----------------------------------------------------------------------------------
@@ -414,6 +507,21 @@ def encode_codes(x, art):
     x = np.asarray(x, dtype=np.float64)
     bits = np.asarray(art["bits"])
     y = rotate(x, art)
+    if art.get("quantizer") == "lloyd-max":
+        # z = (y - o) * (1/s) as separately rounded fp64 operations; the code is the number of
+        # thresholds at or below z (a value on a threshold goes up); NaN -> 0
+        c = np.zeros(y.shape, dtype=np.int64)
+        with np.errstate(invalid="ignore", over="ignore"):
+            z = (y - art["o"][None, :]) * art["inv_scale"][None, :]
+        for i in range(y.shape[1]):
+            b = int(bits[i])
+            if b == 0:
+                continue
+            th = art["lm"][b][1]
+            zi = z[:, i]
+            ci = np.searchsorted(th, zi, side="right")
+            c[:, i] = np.where(np.isnan(zi), 0, ci)
+        return c
     with np.errstate(invalid="ignore", over="ignore"):
         half = np.where(bits > 0, np.ldexp(1.0, np.maximum(bits, 1) - 1), 0.0)
         u = (y - art["o"][None, :]) * art["inv_delta"][None, :]
@@ -427,8 +535,17 @@ def encode_codes(x, art):
 
 
 def dequantize(codes, art):
-    """y_hat_i = o_i + Delta_i (c_i - 2^(b_i-1) + 1/2) for b_i >= 1, o_i for b_i = 0."""
+    """y_hat_i = o_i + Delta_i (c_i - 2^(b_i-1) + 1/2) for b_i >= 1, o_i for b_i = 0
+    (Lloyd-Max: o_i + s_i l_(b_i)[c_i])."""
     bits = np.asarray(art["bits"])
+    if art.get("quantizer") == "lloyd-max":
+        codes = np.asarray(codes)
+        yh = np.repeat(art["o"][None, :], codes.shape[0], axis=0).astype(np.float64)
+        for i in range(codes.shape[1]):
+            b = int(bits[i])
+            if b:
+                yh[:, i] = art["o"][i] + art["scale"][i] * art["lm"][b][0][codes[:, i]]
+        return yh
     half = np.where(bits > 0, np.ldexp(1.0, np.maximum(bits, 1) - 1), 0.0)
     yh = art["o"][None, :] + art["delta"][None, :] * (np.asarray(codes, dtype=np.float64) - half[None, :] + 0.5)
     yh[:, bits == 0] = art["o"][bits == 0][None, :]

@@ -525,6 +525,96 @@ def test_mse_monte_carlo():
 
 
 # ---------------------------------------------------------------- encode / decode
+def _max1960_nonuniform():
+    rows = {}
+    with open(os.path.join(GOLDEN, "max1960_nonuniform_gaussian.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                n, kind, *vals = line.split()
+                rows[(int(n), kind)] = [float(v) for v in vals]
+    return rows
+
+
+def test_lloyd_max_matches_max_1960_table():
+    """Levels, interval end points and MSE of the 2-, 4-, 8- and 16-level Gaussian Lloyd-Max
+    quantizers against Max's 1960 table (four significant digits)."""
+    tab = _max1960_nonuniform()
+    for b in (1, 2, 3, 4):
+        n = 2 ** b
+        levels, th = O.lloyd_max_gaussian(b)
+        assert levels.shape == (n,) and th.shape == (n - 1,)
+        assert np.all(np.diff(levels) > 0) and np.allclose(levels, -levels[::-1], rtol=0, atol=1e-15)
+        y = tab[(n, "y")]
+        assert np.allclose(levels[n // 2:], y, rtol=6e-4, atol=0), (b, levels[n // 2:], y)
+        if (n, "x") in tab:
+            assert np.allclose(th[n // 2:], tab[(n, "x")], rtol=6e-4, atol=0), (b, th[n // 2:])
+        assert abs(O.lloyd_max_mse(b) - tab[(n, "mse")][0]) <= 6e-4 * tab[(n, "mse")][0], b
+
+
+@pytest.mark.parametrize("b", [1, 2, 3, 5, 8])
+def test_lloyd_max_conditions_by_quadrature(b):
+    """The two Lloyd conditions, checked by numerical quadrature (not the closed form the solver
+    uses): every level is the mean of N(0,1) over its cell (to 1e-12) and every threshold the
+    midpoint of its levels; the MSE by quadrature equals lloyd_max_mse and is below the uniform
+    quantizer's (equal at one bit, where both are +-sqrt(2/pi))."""
+    levels, th = O.lloyd_max_gaussian(b)
+    edges = np.concatenate([[-np.inf], th, [np.inf]])
+    mse = 0.0
+    for k in range(2 ** b):
+        lo, hi = edges[k], edges[k + 1]
+        # tail masses from the survival function on the positive side (no cancellation near 1)
+        mass = stats.norm.sf(lo) - stats.norm.sf(hi) if lo >= 0 else stats.norm.cdf(hi) - stats.norm.cdf(lo)
+        m1 = integrate.quad(lambda z: z * stats.norm.pdf(z), lo, hi, epsabs=1e-15, epsrel=1e-13, limit=200)[0]
+        assert abs(m1 / mass - levels[k]) <= 1e-12 * max(1.0, abs(levels[k])), (b, k)
+        mse += integrate.quad(lambda z: (z - levels[k]) ** 2 * stats.norm.pdf(z), lo, hi,
+                              epsabs=1e-16, epsrel=1e-13, limit=200)[0]
+    assert np.allclose(th, 0.5 * (levels[:-1] + levels[1:]), rtol=0, atol=1e-15)
+    assert abs(mse - O.lloyd_max_mse(b)) <= 1e-11
+    uni = O.uniform_quantizer_mse(b, O.optimal_step(b))
+    if b == 1:
+        assert abs(levels[1] - math.sqrt(2 / math.pi)) < 1e-15 and abs(mse - uni) < 1e-12
+    else:
+        assert mse < uni
+
+
+def test_lloyd_max_encode_decode():
+    """Lloyd-Max caches: codes count the thresholds at or below z = (y - o)/s (a value on a
+    threshold goes up; NaN -> 0, +-Inf -> the ends), reconstruction is o + s l[c], and on Gaussian
+    channels the per-channel MSE is s^2 times the table's MSE (3 standard errors)."""
+    x = synth.draw(1, 0, 0, synth.K, "calib", 1024, dtype="f64")
+    assert np.array_equal(O.calibrate(x, "klt", 2.76, quantizer="lloyd-max")["bits"], O.calibrate(x, "klt", 2.76)["bits"])
+    # identity rotation: y = x exactly, so inputs can sit exactly on a channel's thresholds
+    art = O.calibrate(x, "identity", 2.76, quantizer="lloyd-max")
+    i = int(np.argmax(art["bits"] == 3))
+    levels, th = O.lloyd_max_gaussian(3)
+    s, o = art["scale"][i], art["o"][i]
+    zz = np.concatenate([th, [np.nan, np.inf, -np.inf, 0.0]])
+    xs = np.tile(art["o"], (zz.size, 1))
+    xs[:, i] = o + s * zz
+    z = (xs[:, i] - o) * art["inv_scale"][i]        # the encoder's fp64 expression
+    codes = O.encode_codes(xs, art)
+    got = codes[:, i]
+    for k in range(7):                               # at (or within rounding of) threshold k
+        assert got[k] == (k + 1 if z[k] >= th[k] else k), (k, z[k], th[k])
+    assert got[7] == 0 and got[8] == 7 and got[9] == 0 and got[10] == 4
+    yh = O.dequantize(codes, art)
+    assert np.array_equal(yh[:, i], o + s * levels[got])
+    # Monte Carlo on exactly Gaussian rotated coefficients
+    rng = np.random.default_rng(11)
+    n = 200000
+    sig = np.sqrt(art["sigma2"])
+    yy = art["o"][None, :] + rng.standard_normal((n, 128)) * sig[None, :]
+    cc = O.encode_codes(yy @ art["R"], art)
+    err = O.dequantize(cc, art) - O.rotate(yy @ art["R"], art)
+    for j in range(128):
+        b = int(art["bits"][j])
+        if b == 0 or sig[j] == 0:
+            continue
+        e2 = err[:, j] ** 2
+        want = sig[j] ** 2 * O.lloyd_max_mse(b)
+        assert abs(e2.mean() - want) <= 3 * e2.std() / math.sqrt(n) + 1e-12 * want, (j, b)
+
+
 def _art_identity(d, bits, delta, o=None):
     bits = np.asarray(bits)
     o = np.zeros(d) if o is None else np.asarray(o, dtype=np.float64)
