@@ -15,6 +15,8 @@ DTYPE = {"f32": 0, "bf16": 1, "f64": 2}
 ROTATION = {"klt": 0, "wht": 1, "identity": 2, "nova": 3}
 D = 128
 MAX_FIELDS = 384
+LEVELS = 510
+QUANTIZER = {"uniform": 0, "lloyd-max": 1}
 
 # numpy mirror of struct aatc_calib (checked against aatc_calib_bytes at load time)
 CALIB_DTYPE = np.dtype([
@@ -28,13 +30,16 @@ CALIB_DTYPE = np.dtype([
     ("bits", "u1", (D,)), ("plane_channel", "u1", (D * 8,)), ("plane_bit", "u1", (D * 8,)),
     ("field_channel", "<u2", (MAX_FIELDS,)), ("field_shift", "u1", (MAX_FIELDS,)),
     ("field_width", "u1", (MAX_FIELDS,)), ("field_word", "<u2", (MAX_FIELDS,)),
-    ("channel_field", "<i2", (D * 3,)), ("E", "<f8", (D * D,)), ("reserved", "u1", (64,)),
+    ("channel_field", "<i2", (D * 3,)), ("E", "<f8", (D * D,)),
+    ("quantizer", "<i4"), ("pad0", "<i4"), ("scale", "<f8", (D,)), ("inv_scale", "<f8", (D,)),
+    ("scale32", "<f4", (D,)), ("level", "<f8", (LEVELS,)), ("thresh", "<f8", (LEVELS,)),
+    ("level32", "<f4", (LEVELS,)), ("reserved", "u1", (64,)),
 ], align=True)
 
 
 class CalibParams(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int32), ("rotation", ctypes.c_int32), ("bits_per_elem", ctypes.c_double),
-                ("max_bits", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("max_bits", ctypes.c_int32), ("quantizer", ctypes.c_int32),
                 ("channel_weight", ctypes.POINTER(ctypes.c_double)),
                 ("query_moment", ctypes.POINTER(ctypes.c_double))]
 
@@ -42,6 +47,7 @@ class CalibParams(ctypes.Structure):
 class Cache(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("d", ctypes.c_int32),
                 ("k_bits", ctypes.c_int32), ("v_bits", ctypes.c_int32), ("v_tiles", ctypes.c_int32),
+                ("quantizer", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("capacity_tokens", ctypes.c_int64),
                 ("k_calib", ctypes.c_void_p), ("v_calib", ctypes.c_void_p),
                 ("k_codes", ctypes.c_void_p), ("v_codes", ctypes.c_void_p)]

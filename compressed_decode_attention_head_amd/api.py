@@ -25,10 +25,12 @@ def _np_dtype_code(x):
     raise TypeError("calibration data must be float32, float64 or bf16 bits (uint16)")
 
 
-def calibrate(x, rotation="klt", bits_per_elem=2.0, max_bits=8, d=128, channel_weight=None, query_moment=None):
+def calibrate(x, rotation="klt", bits_per_elem=2.0, max_bits=8, d=128, channel_weight=None, query_moment=None,
+              quantizer="uniform"):
     """aatc_calibrate on host rows x [M, d]; returns the artefact blob (uint8 array).
     channel_weight: optional d weights of the rotated channels (query_channel_weights).
-    query_moment: the d x d E[q q^T] of calibration queries (query_moment), for rotation "nova"."""
+    query_moment: the d x d E[q q^T] of calibration queries (query_moment), for rotation "nova".
+    quantizer: "uniform" or "lloyd-max"."""
     L = N.lib()
     x = np.ascontiguousarray(x)
     if x.ndim != 2:
@@ -45,7 +47,8 @@ def calibrate(x, rotation="klt", bits_per_elem=2.0, max_bits=8, d=128, channel_w
         if mom.shape != (d, d):
             raise ValueError("query_moment must be d x d")
         mptr = mom.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
-    p = N.CalibParams(d, N.ROTATION[rotation], float(bits_per_elem), int(max_bits), 0, wptr, mptr)
+    p = N.CalibParams(d, N.ROTATION[rotation], float(bits_per_elem), int(max_bits), N.QUANTIZER[quantizer], wptr,
+                      mptr)
     nbytes = L.aatc_calib_bytes(d) or N.CALIB_DTYPE.itemsize
     out = np.zeros(nbytes, dtype=np.uint8)
     N.check(L.aatc_calibrate(ctypes.byref(p), x.ctypes.data, _np_dtype_code(x), x.shape[0], x.shape[1],
@@ -292,8 +295,13 @@ class CompressedKVCache:
                                    device=self.device)
         self.v_codes = torch.zeros(4 + self.batch * self.n_kv * tiles * 2 * self.v_bits, dtype=torch.int32,
                                    device=self.device)
+        kq = {int(calib_view(b)["quantizer"]) for b in k_blobs}
+        vq = {int(calib_view(b)["quantizer"]) for b in v_blobs}
+        if len(kq) != 1 or len(vq) != 1:
+            raise ValueError("all heads of a tensor must share the quantizer")
+        self.quantizer = kq.pop() | (vq.pop() << 1)
         self._struct = N.Cache(self.batch, self.n_kv, 128, self.k_bits, self.v_bits, self.v_tiles,
-                               self.capacity, self.k_calib.data_ptr(), self.v_calib.data_ptr(),
+                               self.quantizer, 0, self.capacity, self.k_calib.data_ptr(), self.v_calib.data_ptr(),
                                self.k_codes.data_ptr(), self.v_codes.data_ptr())
 
     @property

@@ -2,6 +2,7 @@
 // The kernel (and the method it implements) is described in aatc_attn_kernel.h.
 #define AATC_ATTN_COMBINE_TU
 #include "aatc_attn_kernel.h"
+#include "aatc_attn_lm.h"
 #include "aatc_dense_kernel.h"
 #include "aatc_seg_kernel.h"
 
@@ -30,6 +31,7 @@ int vtiles_bucket(int vt) {
 }
 
 struct Plan {
+  bool lm;                               // the level pass (k_attn_lm): a Lloyd-Max tensor
   int NP, NVB, LIMBS, S, tpw, half, prec, prod;
   int nslot, slot_bytes, ksz, gs, wave_bytes;
   size_t lds;
@@ -43,6 +45,26 @@ int round16(int64_t x) { return static_cast<int>((x + 15) / 16 * 16); }
 // each), as many as fit, at most its tile count.
 Plan make_plan(const aatc_cache* c, int n_q, int64_t max_seq) {
   Plan p;
+  p.lm = c->quantizer != 0;
+  if (p.lm) {
+    // the level pass: about two workgroups per CU, each a contiguous range of tiles
+    const int group = c->n_kv_heads > 0 ? n_q / c->n_kv_heads : 1;
+    const int64_t ntiles = (max_seq + 63) / 64;
+    const int64_t seqs = static_cast<int64_t>(c->batch) * c->n_kv_heads;
+    int64_t tpw = (ntiles * seqs + 511) / 512;
+    if (tpw < 1) tpw = 1;
+    p.tpw = static_cast<int>(tpw);
+    int64_t S = (ntiles + tpw - 1) / tpw;
+    p.S = static_cast<int>(S < 1 ? 1 : S);
+    p.prec = aatc_lm::PHDR + AATC_D;
+    p.NP = p.NVB = p.LIMBS = p.half = p.prod = 0;
+    p.nslot = p.slot_bytes = p.ksz = p.gs = p.wave_bytes = 0;
+    p.lds = 0;
+    p.fits = true;
+    p.part_bytes = static_cast<size_t>(seqs) * p.S * group * p.prec * 4;
+    p.offs_bytes = static_cast<size_t>(seqs) * 8 * 4;
+    return p;
+  }
   const int kb = c->k_bits, vb = c->v_bits;
   p.NP = kb > 0 ? (kb + 127) / 128 : 1;
   p.half = (kb > 0 && kb - 128 * (p.NP - 1) <= 64) ? 1 : 0;
@@ -136,6 +158,7 @@ aatc_status check_cache_and_plan(const aatc_cache* c, int32_t n_q, int64_t max_s
   if (c->k_bits < 0 || c->k_bits > AATC_MAX_ATTN_BITS || c->v_bits < 0 || c->v_bits > AATC_MAX_ATTN_BITS)
     return aatc::fail(AATC_ERR_UNSUPPORTED, "k_bits %d / v_bits %d: decode attention handles 0..%d bits per vector",
                       c->k_bits, c->v_bits, AATC_MAX_ATTN_BITS);
+  if (c->quantizer < 0 || c->quantizer > 3) return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "quantizer %d", c->quantizer);
   if (vtiles_bucket(c->v_tiles) < 0 || c->v_tiles < 0)
     return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "v_tiles %d", c->v_tiles);
   if (!c->k_calib || !c->v_calib || (!c->k_codes && c->k_bits > 0) || (!c->v_codes && c->v_bits > 0))
@@ -162,8 +185,40 @@ aatc_status check_and_plan(const aatc_cache* c, int32_t n_q, int64_t max_seq, vo
   return AATC_OK;
 }
 
+aatc_status launch_level_pass(const aatc_cache* c, const Plan& p, const float* q, int32_t n_q,
+                              const int32_t* seq_lens, int seq_per_head, int64_t max_seq, float scale, void* ws,
+                              hipStream_t st) {
+  aatc_lm::LmArgs a;
+  a.kcodes = static_cast<const uint32_t*>(c->k_codes);
+  a.vcodes = static_cast<const uint32_t*>(c->v_codes);
+  a.tiles_per_seq = c->capacity_tokens / 64;
+  a.n_kv = c->n_kv_heads;
+  a.n_q = n_q;
+  a.group = n_q / c->n_kv_heads;
+  a.seq_lens = seq_lens;
+  a.seq_per_head = seq_per_head;
+  a.max_seq = max_seq;
+  a.q = q;
+  a.scale2 = (scale > 0.f ? scale : 1.0f / sqrtf(static_cast<float>(AATC_D))) * 1.4426950408889634f;
+  char* w = static_cast<char*>(ws);
+  a.part = reinterpret_cast<float*>(w);
+  a.offs = reinterpret_cast<float*>(w + align256(p.part_bytes));
+  a.S = p.S;
+  a.tpw = p.tpw;
+  a.prec = p.prec;
+  a.kB = c->k_bits;
+  a.vB = c->v_bits;
+  a.quant = c->quantizer;
+  hipLaunchKernelGGL(aatc_lm::k_attn_lm, dim3(p.S, c->n_kv_heads, c->batch), dim3(aatc_lm::THREADS), 0, st, a,
+                     static_cast<const aatc_calib*>(c->k_calib), static_cast<const aatc_calib*>(c->v_calib));
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return aatc::fail(AATC_ERR_HIP, "decode_attn level pass launch: %s", hipGetErrorString(err));
+  return AATC_OK;
+}
+
 aatc_status launch_partial(const aatc_cache* c, const Plan& p, const float* q, int32_t n_q, const int32_t* seq_lens,
                            int seq_per_head, int64_t max_seq, float scale, void* ws, hipStream_t st) {
+  if (p.lm) return launch_level_pass(c, p, q, n_q, seq_lens, seq_per_head, max_seq, scale, ws, st);
   AttnArgs a;
   const aatc_calib* kcal = static_cast<const aatc_calib*>(c->k_calib);
   const aatc_calib* vcal = static_cast<const aatc_calib*>(c->v_calib);
@@ -217,6 +272,7 @@ aatc_status launch_merge(const aatc_cache* c, const Plan& p, int32_t n_q, const 
   cb.max_seq = max_seq;
   cb.out = out;
   cb.lse = lse;
+  cb.lm = p.lm ? 1 : 0;
   hipLaunchKernelGGL(k_attn_combine, dim3(group, c->n_kv_heads, c->batch), dim3(CNT), 0, st, cb,
                      static_cast<const aatc_calib*>(c->v_calib));
   const hipError_t err = hipGetLastError();

@@ -503,8 +503,10 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
   // every header field is loaded at once: a short-circuit chain would wait for each in turn
   const uint32_t kmag = kc->magic, vmag = vc->magic;
   const int kbits = kc->total_bits, vbits = vc->total_bits;
+  // (Lloyd-Max blobs take the level pass: their levels are not affine in the codes)
+  const int kq = kc->quantizer, vq = vc->quantizer;
   const bool ok = (kmag == AATC_MAGIC) & (vmag == AATC_MAGIC) & (kbits == Bk) & (vbits == Bv) & (n4 >= 0) &
-                  (n2 >= 0) & (n1 >= 0) & (NV <= NVB) & (PHDR + 16 * NV <= a.prec);
+                  (n2 >= 0) & (n1 >= 0) & (NV <= NVB) & (PHDR + 16 * NV <= a.prec) & (kq == 0) & (vq == 0);
   // a NOVA blob holds its query transform E^-T where a KLT blob holds R: the same GEMV
   const int rot = kc->rotation == AATC_ROT_NOVA ? AATC_ROT_KLT : kc->rotation;
   const int nw = ok ? tiles_of(wave) : 0;   // a bad blob streams nothing
@@ -1092,6 +1094,7 @@ struct CombArgs {
   int64_t max_seq;
   float* out;
   float* lse;
+  int lm;                                // records of the level pass: one column per channel
 };
 
 #ifdef AATC_ATTN_COMBINE_TU   // defined by the one translation unit that launches it
@@ -1153,7 +1156,7 @@ __global__ __launch_bounds__(CNT) void k_attn_combine(CombArgs a, const aatc_cal
   load_pass(0);
   // tables and R_V, consumed last
   const int ti = tid & (D - 1), tf = tid < 3 * D ? tid : 0;   // clamped table indexes
-  const float r_o = vc->o32[ti], r_d = vc->delta32[ti];
+  const float r_o = vc->o32[ti], r_d = a.lm ? vc->scale32[ti] : vc->delta32[ti];
   const int r_b = vc->bits[ti], r_cf = vc->channel_field[tf], r_fs = vc->field_shift[tf];
   // NOVA: R_V^T is E^-1, applied by the same GEMV as a KLT blob's R^T
   const int rot = vc->rotation == AATC_ROT_NOVA ? AATC_ROT_KLT : vc->rotation;
@@ -1167,7 +1170,7 @@ __global__ __launch_bounds__(CNT) void k_attn_combine(CombArgs a, const aatc_cal
   seq = seq < 0 ? 0 : (seq > a.max_seq ? a.max_seq : seq);
   const int n4 = vc->n_fields4, n2 = vc->n_fields2, n1 = vc->n_fields1;
   const int T4 = (n4 + 15) >> 4, T2 = (n2 + 15) >> 4;
-  const int ncol_blob = 16 * (T4 + T2 + ((n1 + 15) >> 4));
+  const int ncol_blob = a.lm ? D : 16 * (T4 + T2 + ((n1 + 15) >> 4));
   bool bad = PHDR + ncol_blob > prec || ncol_blob > MAXCOL || n4 < 0 || n2 < 0 || n1 < 0;
   const int ncol = bad ? 0 : ncol_blob;
   const int c0 = cl, c1 = cl + 256;       // this thread's columns
@@ -1223,8 +1226,12 @@ __global__ __launch_bounds__(CNT) void k_attn_combine(CombArgs a, const aatc_cal
   __syncthreads();
   if (tid < ncol) csum[tid] = (part4[0][tid] + part4[1][tid]) + (part4[2][tid] + part4[3][tid]);
   __syncthreads();
-  // fold field columns into channel code sums; y = o + delta (c_bar - 2^(b-1) + 1/2)
-  if (tid < D) {
+  // fold field columns into channel code sums; y = o + delta (c_bar - 2^(b-1) + 1/2); records
+  // of the level pass hold each channel's weighted level sum: y = o + scale l_bar
+  if (tid < D && a.lm) {
+    const int i = tid;
+    yt[i] = (t_bits[i] && L > 0.f && i < ncol) ? t_o[i] + t_delta[i] * (csum[i] / L) : t_o[i];
+  } else if (tid < D) {
     const int i = tid;
     float cs = 0.f;
     for (int kk = 0; kk < 3; ++kk) {

@@ -149,7 +149,8 @@ constexpr size_t kTabFw = kTabPb + 2 * D;               // u16 first word of eac
 constexpr size_t kTabFs = kTabFw + 2 * AATC_MAX_FIELDS; // u8 width | shift << 4 of each field
 constexpr size_t kTabFc = kTabFs + AATC_MAX_FIELDS;     // u8 channel of each field
 constexpr size_t kTabWf = kTabFc + AATC_MAX_FIELDS;     // u16 field of each V word [2*1024]
-constexpr size_t kEncodeLds = kTabWf + 2 * 2 * AATC_D * AATC_MAX_BITS;
+constexpr size_t kTabTh = kTabWf + 2 * 2 * AATC_D * AATC_MAX_BITS;   // fp64 Lloyd-Max thresholds
+constexpr size_t kEncodeLds = kTabTh + 8 * AATC_LEVELS;
 static_assert(2 * AATC_D * AATC_MAX_BITS * 4 <= kMc, "packed words fit the staging area");
 
 // u = (y - o) * (1/Delta) + 2^(b-1) as separately rounded fp64 operations; code =
@@ -161,6 +162,18 @@ __device__ inline int quantize(double y, double o, double inv, int bi) {
   const double top = static_cast<double>((1 << bi) - 1);
   const double uc = u >= 0.0 ? fmin(u, top) : 0.0;
   return bi > 0 ? static_cast<int>(uc) : 0;
+}
+
+// Lloyd-Max: z = (y - o) * (1/s) as separately rounded fp64 operations; the code is the number
+// of the b-bit table's 2^b - 1 ascending thresholds at or below z, by a b-step binary search
+// (NaN compares false: code 0; +-Inf: the ends).
+__device__ inline int quantize_lm(double y, double o, double inv, int bi, const double* thr) {
+  const double z = (y - o) * inv;
+  const double* t = thr + (1 << bi) - 2;
+  int c = 0;
+  for (int st = (1 << bi) >> 1; st > 0; st >>= 1)
+    if (z >= t[c + st - 1]) c += st;
+  return bi > 0 ? c : 0;
 }
 
 // The fp64 value of another lane of the same quad, by a DPP quad permutation (CTRL 0xB1: lane ^ 1,
@@ -228,19 +241,23 @@ __device__ __attribute__((noinline)) void encode_tiles(const CodecArgs& a) {
   uint8_t* t_fs = smem + kTabFs;
   uint8_t* t_fc = smem + kTabFc;
   uint16_t* t_wf = reinterpret_cast<uint16_t*>(smem + kTabWf);
+  double* t_th = reinterpret_cast<double*>(smem + kTabTh);
   const int tid = threadIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
   const aatc_calib* c = a.calib + h;
   const int B = c->total_bits, nf = c->n_fields;
   constexpr bool wht = WHT;
   const double rs = c->R[0];                           // WHT: 1/sqrt(d) as the blob holds it
+  const bool lm = c->quantizer == AATC_QUANT_LLOYD_MAX;
 
   // ---- tables, once per workgroup
   if (tid < D) {
     t_o[tid] = c->o[tid];
-    t_inv[tid] = c->inv_delta[tid];
+    t_inv[tid] = lm ? c->inv_scale[tid] : c->inv_delta[tid];
     t_bits[tid] = c->bits[tid];
   }
+  if (lm)
+    for (int k = tid; k < AATC_LEVELS; k += THREADS) t_th[k] = c->thresh[k];
   for (int f = tid; f < nf; f += THREADS) {
     const int fw = c->field_word[f], wd = c->field_width[f];
     t_fw[f] = static_cast<uint16_t>(fw);
@@ -368,7 +385,8 @@ __device__ __attribute__((noinline)) void encode_tiles(const CodecArgs& a) {
       }
 #pragma unroll
       for (int k = 0; k < 32; ++k)
-        cp[k >> 2] |= static_cast<uint32_t>(quantize(v[k] * rs, t_o[i0 + k], t_inv[i0 + k], t_bits[i0 + k]))
+        cp[k >> 2] |= static_cast<uint32_t>(lm ? quantize_lm(v[k] * rs, t_o[i0 + k], t_inv[i0 + k], t_bits[i0 + k], t_th)
+                                                : quantize(v[k] * rs, t_o[i0 + k], t_inv[i0 + k], t_bits[i0 + k]))
                       << (8 * (k & 3));
     } else {
       double acc[4][8];
@@ -379,7 +397,9 @@ __device__ __attribute__((noinline)) void encode_tiles(const CodecArgs& a) {
 #pragma unroll
         for (int aa = 0; aa < 4; ++aa) {
           const int n = 8 * aa + bb;
-          cp[n >> 2] |= static_cast<uint32_t>(quantize(acc[aa][bb], t_o[i], t_inv[i], t_bits[i])) << (8 * (n & 3));
+          cp[n >> 2] |= static_cast<uint32_t>(lm ? quantize_lm(acc[aa][bb], t_o[i], t_inv[i], t_bits[i], t_th)
+                                                  : quantize(acc[aa][bb], t_o[i], t_inv[i], t_bits[i]))
+                        << (8 * (n & 3));
         }
       }
     }
@@ -574,8 +594,8 @@ __global__ __launch_bounds__(THREADS) void k_decode(CodecArgs a) {
           code |= v << c->field_shift[f];
         }
       }
-      const double half = ldexp(1.0, bi - 1);
-      y = c->o[i] + c->delta[i] * ((static_cast<double>(code) - half) + 0.5);
+      // o + scale * level: the uniform quantizer's level is c - 2^(b-1) + 1/2, Lloyd-Max's the table's
+      y = c->o[i] + c->scale[i] * c->level[(1 << bi) - 2 + code];
     }
     ys[e] = y;
   }

@@ -236,6 +236,92 @@ double optimal_step(int b) {
   return 0.5 * (lo + hi);
 }
 
+// ---- Lloyd-Max quantizer of N(0,1) ----------------------------------------------------------
+// Page "SPHERICAL KV ..." (NOVA-KV abstract) and page "Ablation ..." (OCTOPUS abstract).  The
+// 2^b-level MSE-optimal quantizer is the solution of Lloyd's conditions: each level the mean of
+// N(0,1) over its cell, each threshold the midpoint of its two levels.  The quantizer is
+// symmetric, so the h = 2^(b-1) positive levels are solved with cells [t_(k-1), t_k), t_0 = 0,
+// t_k = (y_k + y_(k+1)) / 2, the last cell unbounded: Lloyd iterations from a uniform start,
+// then Newton steps on y - centroid(y) = 0 (tridiagonal Jacobian, Thomas algorithm).
+void lm_centroids(const std::vector<double>& y, std::vector<double>& c, std::vector<double>& dl,
+                  std::vector<double>& dr) {
+  const int h = static_cast<int>(y.size());
+  c.assign(h, 0.0);
+  dl.assign(h, 0.0);
+  dr.assign(h, 0.0);
+  for (int k = 0; k < h; ++k) {
+    const double lo = k == 0 ? 0.0 : 0.5 * (y[k - 1] + y[k]);
+    const bool last = k == h - 1;
+    const double hi = last ? 0.0 : 0.5 * (y[k] + y[k + 1]);
+    const double plo = phi(lo), phi_hi = last ? 0.0 : phi(hi);
+    const double mass = upper_tail(lo) - (last ? 0.0 : upper_tail(hi));
+    c[k] = (plo - phi_hi) / mass;
+    // d centroid / d lower edge and d centroid / d upper edge
+    dl[k] = k == 0 ? 0.0 : plo * (c[k] - lo) / mass;
+    dr[k] = last ? 0.0 : phi_hi * (hi - c[k]) / mass;
+  }
+}
+
+void lloyd_max_half(int b, std::vector<double>& y) {
+  const int h = 1 << (b - 1);
+  y.assign(h, 0.0);
+  if (h == 1) {
+    y[0] = std::sqrt(2.0 / 3.14159265358979323846);
+    return;
+  }
+  for (int k = 0; k < h; ++k) y[k] = (k + 0.5) * (1.0 + 0.5 * b) / h;
+  std::vector<double> c, dl, dr;
+  for (int it = 0; it < 200; ++it) {
+    lm_centroids(y, c, dl, dr);
+    y = c;
+  }
+  std::vector<double> a(h), bd(h), cu(h), rhs(h);
+  for (int it = 0; it < 60; ++it) {
+    lm_centroids(y, c, dl, dr);
+    // row k of J = I - d c / d y: sub (y_(k-1)) = -dl_k / 2, diag = 1 - (dl_k + dr_k) / 2,
+    // sup (y_(k+1)) = -dr_k / 2
+    for (int k = 0; k < h; ++k) {
+      a[k] = -0.5 * dl[k];
+      bd[k] = 1.0 - 0.5 * (dl[k] + dr[k]);
+      cu[k] = -0.5 * dr[k];
+      rhs[k] = c[k] - y[k];
+    }
+    for (int k = 1; k < h; ++k) {        // forward elimination
+      const double m = a[k] / bd[k - 1];
+      bd[k] -= m * cu[k - 1];
+      rhs[k] -= m * rhs[k - 1];
+    }
+    double mx = 0.0;
+    for (int k = h - 1; k >= 0; --k) {   // back substitution
+      const double st = (rhs[k] - (k + 1 < h ? cu[k] * rhs[k + 1] : 0.0)) / bd[k];
+      rhs[k] = st;
+      mx = std::max(mx, std::fabs(st));
+    }
+    for (int k = 0; k < h; ++k) y[k] += rhs[k];
+    if (mx <= 1e-17 * y[h - 1]) break;
+  }
+}
+
+// Standardized levels (and Lloyd-Max thresholds) of b = 1..8 bits into the blob's tables.
+void fill_levels(aatc_calib* c) {
+  for (int b = 1; b <= AATC_MAX_BITS; ++b) {
+    const int n = 1 << b, h = n >> 1, off = n - 2;
+    if (c->quantizer == AATC_QUANT_LLOYD_MAX) {
+      std::vector<double> y;
+      lloyd_max_half(b, y);
+      for (int k = 0; k < h; ++k) {
+        c->level[off + h + k] = y[k];
+        c->level[off + h - 1 - k] = -y[k];
+      }
+      for (int k = 0; k + 1 < n; ++k) c->thresh[off + k] = 0.5 * (c->level[off + k] + c->level[off + k + 1]);
+      c->thresh[off + h - 1] = 0.0;
+    } else {
+      for (int k = 0; k < n; ++k) c->level[off + k] = k - h + 0.5;
+    }
+  }
+  for (int k = 0; k < AATC_LEVELS; ++k) c->level32[k] = static_cast<float>(c->level[k]);
+}
+
 // ---- integer reverse water-filling ---------------------------------------------------------
 // The B largest candidates sigma_i^2 4^-k (k < max_bits) in the order (value desc,
 // channel asc, bit asc); exact in fp64 (ldexp).
@@ -341,6 +427,8 @@ aatc_status aatc_calibrate(const aatc_calib_params* p, const void* x, aatc_dtype
   }
   if (p->max_bits < 1 || p->max_bits > AATC_MAX_BITS)
     return fail(AATC_ERR_BUDGET, "max_bits=%d (1..8)", p->max_bits);
+  if (p->quantizer != AATC_QUANT_UNIFORM && p->quantizer != AATC_QUANT_LLOYD_MAX)
+    return fail(AATC_ERR_INVALID_ARGUMENT, "quantizer %d", p->quantizer);
   const int32_t total = aatc_bits_budget(p->bits_per_elem, p->d);
   if (total < 0 || total > p->max_bits * p->d)
     return fail(AATC_ERR_BUDGET, "bits_per_elem=%g gives B outside [0, %d]", p->bits_per_elem,
@@ -374,6 +462,7 @@ aatc_status aatc_calibrate(const aatc_calib_params* p, const void* x, aatc_dtype
   c->total_bits = total;
   c->max_bits = p->max_bits;
   c->n_calib = static_cast<int32_t>(n);
+  c->quantizer = p->quantizer;
   const int d = AATC_D;
   std::vector<double> cov;
   mean_cov(xs, n, c->mu, cov);
@@ -465,13 +554,18 @@ aatc_status aatc_calibrate(const aatc_calib_params* p, const void* x, aatc_dtype
     c->o[i] = o;
     if (c->bits[i]) {
       const double sg = std::sqrt(std::max(c->sigma2[i], 0.0));
-      c->delta[i] = (sg > 0 ? sg : std::ldexp(ref, -40)) * optimal_step(c->bits[i]);
+      const double s0 = sg > 0 ? sg : std::ldexp(ref, -40);
+      c->delta[i] = s0 * optimal_step(c->bits[i]);
       c->inv_delta[i] = 1.0 / c->delta[i];
+      c->scale[i] = c->quantizer == AATC_QUANT_LLOYD_MAX ? s0 : c->delta[i];
+      c->inv_scale[i] = 1.0 / c->scale[i];
     }
     c->o32[i] = static_cast<float>(c->o[i]);
     c->delta32[i] = static_cast<float>(c->delta[i]);
+    c->scale32[i] = static_cast<float>(c->scale[i]);
   }
   for (int i = 0; i < d * d; ++i) c->R32[i] = static_cast<float>(c->R[i]);
+  fill_levels(c);
   build_layout(c);
   c->checksum = blob_checksum(c);
   return AATC_OK;
@@ -485,12 +579,18 @@ aatc_status aatc_calib_validate(const void* blob, size_t bytes) {
   if (c->magic != AATC_MAGIC || c->version != AATC_VERSION) return fail(AATC_ERR_BAD_ARTEFACT, "magic/version");
   if (c->d != AATC_D) return fail(AATC_ERR_BAD_ARTEFACT, "d=%d", c->d);
   if (c->checksum != blob_checksum(c)) return fail(AATC_ERR_BAD_ARTEFACT, "checksum mismatch");
+  if (c->quantizer != AATC_QUANT_UNIFORM && c->quantizer != AATC_QUANT_LLOYD_MAX)
+    return fail(AATC_ERR_BAD_ARTEFACT, "quantizer %d", c->quantizer);
   int sum = 0;
   for (int i = 0; i < AATC_D; ++i) {
     if (c->bits[i] > AATC_MAX_BITS) return fail(AATC_ERR_BAD_ARTEFACT, "bits[%d]=%d", i, c->bits[i]);
     sum += c->bits[i];
     if (c->bits[i] && !(c->delta[i] > 0.0)) return fail(AATC_ERR_BAD_ARTEFACT, "delta[%d]", i);
+    if (c->bits[i] && !(c->scale[i] > 0.0)) return fail(AATC_ERR_BAD_ARTEFACT, "scale[%d]", i);
   }
+  for (int b = 1; b <= AATC_MAX_BITS; ++b)          // level tables strictly increasing
+    for (int k = (1 << b) - 2; k + 1 < (1 << (b + 1)) - 2; ++k)
+      if (!(c->level[k] < c->level[k + 1])) return fail(AATC_ERR_BAD_ARTEFACT, "level table of %d bits", b);
   if (sum != c->total_bits) return fail(AATC_ERR_BAD_ARTEFACT, "bits sum %d != %d", sum, c->total_bits);
   aatc_calib tmp;
   std::memcpy(&tmp, c, sizeof(tmp));

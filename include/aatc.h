@@ -54,6 +54,7 @@ typedef enum {
 
 typedef enum { AATC_F32 = 0, AATC_BF16 = 1, AATC_F64 = 2 } aatc_dtype;
 typedef enum { AATC_ROT_KLT = 0, AATC_ROT_WHT = 1, AATC_ROT_IDENTITY = 2, AATC_ROT_NOVA = 3 } aatc_rotation;
+typedef enum { AATC_QUANT_UNIFORM = 0, AATC_QUANT_LLOYD_MAX = 1 } aatc_quantizer;
 
 #define AATC_D 128
 #define AATC_TILE 64             /* tokens per packed tile */
@@ -62,7 +63,8 @@ typedef enum { AATC_ROT_KLT = 0, AATC_ROT_WHT = 1, AATC_ROT_IDENTITY = 2, AATC_R
 #define AATC_MAX_GROUP 8         /* q heads per KV head handled by decode attention */
 #define AATC_MAX_ATTN_BITS 512   /* bits per K or V vector decode attention reads (4 per element) */
 #define AATC_MAGIC 0x43544141u   /* "AATC" */
-#define AATC_VERSION 2u
+#define AATC_VERSION 3u
+#define AATC_LEVELS 510          /* level-table entries: 2^b for each b = 1..8, table b at 2^b - 2 */
 
 /*
  * Calibration artefact of one (layer, KV head, tensor K|V): a plain-old-data blob that is
@@ -87,11 +89,20 @@ typedef enum { AATC_ROT_KLT = 0, AATC_ROT_WHT = 1, AATC_ROT_IDENTITY = 2, AATC_R
  *       w=4: 64G + 32*(r/2) + 8m + 4*(r%2) + b
  *    (so that four tokens' values land in the four bytes of one word after a shift).
  *
- * Quantizer (mid-rise, per channel): for b_i >= 1,
- *    c_i = clamp(floor((y_i - o_i) * inv_delta_i + 2^(b_i-1)), 0, 2^b_i - 1),  y = R x,
+ * Quantizer, uniform (mid-rise, per channel): for b_i >= 1,
+ *    c_i = clamp(floor((y_i - o_i) * inv_delta_i + 2^(b_i-1)), 0, 2^b_i - 1),  y = E x,
  *    evaluated in fp64 with separately rounded operations; NaN -> 0; +-Inf -> clamp ends.
  *    Reconstruction y_hat_i = o_i + delta_i (c_i - 2^(b_i-1) + 1/2); b_i = 0 gives o_i;
  *    x_hat = R^T y_hat.
+ * Quantizer, Lloyd-Max (page "SPHERICAL KV ...", NOVA-KV abstract: fixed-width uniform scalar
+ *    quantizers lose at low rates; page "Ablation ...", OCTOPUS abstract: coordinates quantized
+ *    with the Lloyd-Max quantizer of their marginal): channel i uses the 2^b_i-level
+ *    MSE-optimal quantizer of N(0,1), scaled by scale_i (the channel's standard deviation):
+ *    z = (y_i - o_i) * inv_scale_i (fp64, separately rounded), c_i = the number of
+ *    thresholds t_(b,k) <= z (NaN -> 0), y_hat_i = o_i + scale_i l_(b,c).  Codes keep b_i bits, so
+ *    the packed formats are the same.
+ * Either way y_hat_i = o_i + scale_i level[2^b - 2 + c] with scale_i = delta_i and level =
+ * c - 2^(b-1) + 1/2 for the uniform quantizer.
  */
 typedef struct aatc_calib {
   uint32_t magic;          /* AATC_MAGIC */
@@ -124,6 +135,16 @@ typedef struct aatc_calib {
   uint16_t field_word[AATC_MAX_FIELDS];
   int16_t channel_field[AATC_D * 3];  /* fields of channel i, -1 padded */
   double E[AATC_D * AATC_D];         /* encoder: coefficients y = E x (E = R except NOVA) */
+  int32_t quantizer;                 /* aatc_quantizer */
+  int32_t pad0;
+  double scale[AATC_D];              /* reconstruction scale: delta (uniform), sigma (Lloyd-Max);
+                                        0 for b_i = 0 */
+  double inv_scale[AATC_D];          /* 1/scale, correctly rounded (0 for b_i = 0) */
+  float scale32[AATC_D];
+  double level[AATC_LEVELS];         /* standardized reconstruction levels of b = 1..8 bits */
+  double thresh[AATC_LEVELS];        /* Lloyd-Max: the 2^b - 1 standardized thresholds of each b,
+                                        ascending, at 2^b - 2 (uniform: 0) */
+  float level32[AATC_LEVELS];
   uint8_t reserved[64];
 } aatc_calib;
 
@@ -132,7 +153,7 @@ typedef struct {
   int32_t rotation;        /* aatc_rotation */
   double bits_per_elem;    /* average budget b; B = floor(b*d + 1/2) */
   int32_t max_bits;        /* per-channel cap, 8 (1..8) */
-  int32_t reserved;
+  int32_t quantizer;       /* aatc_quantizer: 0 uniform (default), 1 Lloyd-Max */
   const double* channel_weight;  /* NULL: the cache-MSE allocation; else d weights w_i >= 0 of
                                     the rotated channels (attention-aware keys: see
                                     aatc_query_channel_weights) */
@@ -158,6 +179,9 @@ typedef struct {
   int32_t k_bits;           /* B of every K blob */
   int32_t v_bits;           /* B of every V blob */
   int32_t v_tiles;          /* max over the V blobs of aatc_calib_v_tiles() (<= 24) */
+  int32_t quantizer;        /* bit 0: the K blobs are Lloyd-Max, bit 1: the V blobs (checked by the
+                               kernels like k_bits / v_bits) */
+  int32_t reserved;         /* 0 */
   int64_t capacity_tokens;  /* tokens per (b,h); multiple of 64 */
   const void* k_calib;
   const void* v_calib;
@@ -314,7 +338,10 @@ size_t aatc_decode_attn_workspace_bytes(const aatc_cache* cache, int32_t n_q_hea
  *   k_hat, v_hat the reconstructions of aatc_decode, computed as: q~ = R_K q once; scores
  *   from the packed K bits weighted by q~ delta^K (the reconstruction offset cancels in the
  *   softmax); online softmax; softmax-weighted sums of the packed V codes; the affine V
- *   dequantization and R_V^T applied once to the sum.  lse_dev (nullable): fp32
+ *   dequantization and R_V^T applied once to the sum.  When either tensor is Lloyd-Max
+ *   (cache->quantizer != 0) the levels are not affine in the codes: the cache pass then decodes
+ *   each tile's codes to levels through the blobs' level tables and sums probability-weighted V
+ *   levels instead (a separate kernel, same arguments and results).  lse_dev (nullable): fp32
  *   [batch][n_q_heads] natural-log sum of exp of the scores.  A sequence with 0 visible
  *   tokens yields out = 0, lse = -inf.
  *   workspace_dev: >= aatc_decode_attn_workspace_bytes(...) bytes of device memory, 256-byte

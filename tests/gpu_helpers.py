@@ -15,7 +15,7 @@ class Case:
 
     def __init__(self, cfg, n_kv, group, n_tokens, batch=1, dtype="bf16", rotation="klt", bpe_k=2.0,
                  bpe_v=None, marginal="gauss", layer=0, n_calib=1024, aware=False, v_rotation=None,
-                 n_q_cal=512):
+                 n_q_cal=512, quant_k="uniform", quant_v="uniform"):
         self.cfg, self.n_kv, self.group, self.n, self.batch = cfg, n_kv, group, n_tokens, batch
         self.dtype, self.rotation, self.layer = dtype, rotation, layer
         self.v_rotation = rotation if v_rotation is None else v_rotation
@@ -36,8 +36,10 @@ class Case:
         # head's key generator), n_q_cal per head
         self.q_cal = [synth.draw(cfg, layer, h, synth.K, "query", n_q_cal, dtype="f64", extra=50000) if aware
                       else None for h in range(n_kv)]
-        self.art = {synth.K: [O.calibrate(c, rotation, self.bpe_k, q_cal=qc) for c, qc in zip(self.cal[synth.K], self.q_cal)],
-                    synth.V: [O.calibrate(c, self.v_rotation, self.bpe_v) for c in self.cal[synth.V]]}
+        self.quant = {synth.K: quant_k, synth.V: quant_v}
+        self.art = {synth.K: [O.calibrate(c, rotation, self.bpe_k, q_cal=qc, quantizer=quant_k)
+                              for c, qc in zip(self.cal[synth.K], self.q_cal)],
+                    synth.V: [O.calibrate(c, self.v_rotation, self.bpe_v, quantizer=quant_v) for c in self.cal[synth.V]]}
         self.codes = {t: np.stack([np.stack([O.encode_codes(self.x[t][b, h], self.art[t][h])
                                              for h in range(n_kv)]) for b in range(batch)])
                       for t in (synth.K, synth.V)}
@@ -48,15 +50,16 @@ class Case:
         out = []
         for h, c in enumerate(self.cal[tensor]):
             xc = c if self.dtype == "f32" else bits16(c)
+            qz = self.quant[tensor]
             if tensor == synth.V:
-                blob = api.calibrate(xc, self.v_rotation, bpe)
+                blob = api.calibrate(xc, self.v_rotation, bpe, quantizer=qz)
             elif self.rotation == "nova":
-                blob = api.calibrate(xc, "nova", bpe, query_moment=api.query_moment(self.q_cal[h]))
+                blob = api.calibrate(xc, "nova", bpe, query_moment=api.query_moment(self.q_cal[h]), quantizer=qz)
             else:
-                blob = api.calibrate(xc, self.rotation, bpe)
+                blob = api.calibrate(xc, self.rotation, bpe, quantizer=qz)
                 if self.q_cal[h] is not None:
                     w = api.query_channel_weights(blob, self.q_cal[h])
-                    blob = api.calibrate(xc, self.rotation, bpe, channel_weight=w)
+                    blob = api.calibrate(xc, self.rotation, bpe, channel_weight=w, quantizer=qz)
             out.append(blob)
         return out
 

@@ -335,6 +335,35 @@ def _status(fn):
     return e.value.name
 
 
+@pytest.mark.parametrize("cfg,rot,bpe", [(2, "klt", 2.76), (3, "klt", 4.0), (4, "wht", 1.33)])
+def test_lloyd_max_calibration_matches_oracle(cfg, rot, bpe):
+    """A Lloyd-Max blob: the same bits as the uniform one, scale = the channel's standard
+    deviation, and standardized level and threshold tables of every width equal to the oracle's
+    Lloyd-Max quantizer (the library solves Lloyd's conditions on its own)."""
+    x = _cal(cfg, marginal="t3" if cfg == 4 else "gauss")
+    blob = api.calibrate(_bits16(x), rot, bpe, quantizer="lloyd-max")
+    api.validate(blob)
+    v = api.calib_view(blob)
+    art = O.calibrate(x, rot, bpe, quantizer="lloyd-max")
+    assert int(v["quantizer"]) == 1
+    assert np.array_equal(v["bits"].astype(np.int64), art["bits"])
+    coded = art["bits"] > 0
+    assert np.allclose(v["scale"][coded], art["scale"][coded], rtol=1e-9, atol=0)
+    assert np.all(v["scale"][~coded] == 0)
+    assert np.array_equal(v["inv_scale"][coded], 1.0 / v["scale"][coded])
+    for b in range(1, 9):
+        off, n = 2 ** b - 2, 2 ** b
+        lv, th = O.lloyd_max_gaussian(b)
+        assert np.allclose(v["level"][off:off + n], lv, rtol=0, atol=2e-12), b
+        assert np.allclose(v["thresh"][off:off + n - 1], th, rtol=0, atol=2e-12), b
+        assert np.array_equal(v["level32"][off:off + n], v["level"][off:off + n].astype(np.float32))
+    u = api.calib_view(api.calibrate(_bits16(x), rot, bpe))
+    assert int(u["quantizer"]) == 0 and np.array_equal(u["scale"], u["delta"])
+    for b in range(1, 9):
+        off, n = 2 ** b - 2, 2 ** b
+        assert np.array_equal(u["level"][off:off + n], np.arange(n) - n / 2 + 0.5), b
+
+
 def test_calibrate_error_paths(L):
     x = np.random.default_rng(0).standard_normal((64, 128))
     assert _status(lambda: api.calibrate(x, "klt", 8.5)) == "AATC_ERR_BUDGET"
