@@ -44,6 +44,7 @@ def parse():
     p.add_argument("--no-encode", action="store_true", help="skip the encode rooflines")
     p.add_argument("--no-folded", action="store_true", help="skip the folded all-layers launch")
     p.add_argument("--no-loops", action="store_true", help="skip the append + decode loops")
+    p.add_argument("--no-lloyd-max", action="store_true", help="skip the Lloyd-Max caches")
     p.add_argument("--only-headline", action="store_true", help="headline step and roofline only")
     return p.parse_args()
 
@@ -53,16 +54,21 @@ def log(args, *a):
         print(*a, file=sys.stderr, flush=True)
 
 
-def build_layer(cfg, layer, n_tokens, device, capacity=None):
+def build_layer(cfg, layer, n_tokens, device, capacity=None, quantizer="uniform", heads=None, batch=None):
     """Calibrate (host), draw the context on the GPU, encode it; returns (cache, q, host key sample)."""
     import torch
     import synth
     from compressed_decode_attention_head_amd import api
+    from dataclasses import replace
+    if heads is not None or batch is not None:
+        cfg = replace(cfg, n_kv_heads=heads or cfg.n_kv_heads, batch=batch or cfg.batch,
+                      n_q_heads=(heads or cfg.n_kv_heads) * cfg.group)
     kb, vb = [], []
     for h in range(cfg.n_kv_heads):
         for t, dst in ((synth.K, kb), (synth.V, vb)):
             cal = synth.draw(cfg.idx, layer, h, t, "calib", cfg.n_calib, dtype=cfg.dtype, marginal=cfg.marginal)
-            dst.append(api.calibrate(cal if cfg.dtype == "f32" else synth.bf16_bits(cal), cfg.rotation, cfg.bits_per_elem))
+            dst.append(api.calibrate(cal if cfg.dtype == "f32" else synth.bf16_bits(cal), cfg.rotation, cfg.bits_per_elem,
+                                     quantizer=quantizer))
     cap = -(-max(n_tokens, capacity or 0) // 64) * 64
     cache = api.CompressedKVCache(kb, vb, cfg.batch, cap, device=device)
     ksample = []
@@ -204,10 +210,24 @@ def gpu_info():
     return info
 
 
+USE_GRAPHS = True
+
+
 def timed_graph(fn, reps, st):
     """Capture fn() in a graph, replay it reps times between HIP events on stream st; returns ms
-    per replay (the launches back to back, without host overheads)."""
+    per replay (the launches back to back, without host overheads).  With --no-graph: eager
+    calls between the events."""
     import torch
+    if not USE_GRAPHS:
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(reps):
+            fn()
+        e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
     g = torch.cuda.CUDAGraph()
     s2 = torch.cuda.Stream()
     s2.wait_stream(st)
@@ -408,6 +428,52 @@ def append_decode_loop(args, dev, st):
             "cache_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
             "calls_per_layer_step": "aatc_encode K + aatc_encode V (1 token per sequence and head) + aatc_decode_attn",
             "timing": "eager launches, HIP events around all steps"}
+
+
+def lloyd_max_pass(args, dev, st):
+    """Lloyd-Max caches (K and V) of the 32K-token 2.76-bit layer (12 layers, 277 MB) and of the
+    batch-16 x 8K 4-bit layer (4 layers, 537 MB): one aatc_decode_attn per layer (the level pass
+    k_attn_lm + the merge), graph replay over the layers, beside the reconstruction MSE of the
+    same context under the uniform and the Lloyd-Max quantizer (aatc_decode on the GPU, one head)."""
+    import torch
+    import synth
+    res = {}
+    for idx, n_lay in ((2, 12), (3, 4)):
+        cfg = synth.CONFIGS[idx]
+        n = cfg.n_tokens
+        lays = []
+        for l in range(n_lay):
+            cache, q, _ = build_layer(cfg, l, n, dev, quantizer="lloyd-max")
+            ws = cache.new_workspace(cfg.n_q_heads, n)
+            lays.append((cache, q, ws, torch.empty_like(q),
+                         torch.empty((cfg.batch, cfg.n_q_heads), dtype=torch.float32, device=dev)))
+        torch.cuda.synchronize()
+        reps = max(5, args.steps)
+        ms = timed_graph(lambda: [c.decode_attn(q, n, workspace=w, out=o, lse=e) for c, q, w, o, e in lays], reps, st)
+        part = timed_graph(lambda: [c.decode_attn_partial(q, n, w) for c, q, w, o, e in lays], reps, st)
+        kb, vb = lays[0][0].k_bits, lays[0][0].v_bits
+        nbytes = cfg.batch * cfg.n_kv_heads * n * (kb + vb) / 8.0
+        # reconstruction error of head 0's keys, both quantizers, same context
+        mse = {}
+        x = torch.empty((1, 1, n, 128), dtype=torch.bfloat16, device=dev)
+        x[0, 0] = synth.draw_device(cfg.idx, 0, 0, synth.K, n, dtype="bf16", device=dev)
+        for qz in ("uniform", "lloyd-max"):
+            c1, _, _ = build_layer(cfg, 0, 64, dev, quantizer=qz, heads=1, batch=1, capacity=n)
+            c1.encode(synth.K, x)
+            xh = c1.decode(synth.K, 0, n)
+            mse[qz] = float(((xh.float() - x.float()) ** 2).mean())
+        res["config%d" % idx] = {
+            "workload": cfg.name, "layers": n_lay, "kernel": "k_attn_lm (level pass) + k_attn_combine",
+            "bytes_per_layer": nbytes, "us_per_layer": round(ms * 1e3 / n_lay, 2),
+            "cache_pass_us": round(part * 1e3 / n_lay, 2),
+            "cache_pass_gbs": round(nbytes / (part * 1e-3 / n_lay) / 1e9, 1),
+            "cache_pass_frac_of_peak": round(nbytes / (part * 1e-3 / n_lay) / 1e9 / HBM_PEAK_GBS, 4),
+            "step_gbs": round(nbytes / (ms * 1e-3 / n_lay) / 1e9, 1),
+            "key_reconstruction_mse": {"uniform": mse["uniform"], "lloyd-max": mse["lloyd-max"],
+                                       "reduction": round(1 - mse["lloyd-max"] / mse["uniform"], 4)}}
+        del lays
+        torch.cuda.synchronize()
+    return res
 
 
 def dense_comparator(args, cfg, n_tokens, qs, dev, st, ms_compressed_step):
@@ -619,8 +685,11 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU", file=sys.stderr)
         sys.exit(1)
+    global USE_GRAPHS
+    USE_GRAPHS = not args.no_graph
     if args.only_headline:
         args.no_dense = args.no_tiers = args.no_cpu_baseline = args.no_encode = args.no_folded = args.no_loops = True
+        args.no_lloyd_max = True
     cfg = synth.CONFIGS[args.config]
     n_tokens = args.tokens or cfg.n_tokens
     n_layers = args.layers or cfg.n_layers
@@ -798,6 +867,11 @@ def main():
         res["tiers"] = tiered_segments(args, dev, st)
         log(args, "tiers: %.2f us per layer, %.0f GB/s, tier fractions %s" % (
             res["tiers"]["us_per_layer"], res["tiers"]["gbs"], res["tiers"]["tier_fractions"]))
+    if not args.no_lloyd_max:
+        log(args, "timing Lloyd-Max caches")
+        res["lloyd_max"] = lloyd_max_pass(args, dev, st)
+        log(args, "Lloyd-Max: %s" % {k: (v["us_per_layer"], v["key_reconstruction_mse"]["reduction"])
+                                     for k, v in res["lloyd_max"].items()})
     if not args.no_loops:
         log(args, "timing the batch-16 append + decode loop")
         res["append_decode_loop"] = append_decode_loop(args, dev, st)

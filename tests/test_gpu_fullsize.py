@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 ATOL_ATTN = 2e-3
 
 
-def _layer(cfg, n_tokens, sampled, n_encode=None):
+def _layer(cfg, n_tokens, sampled, n_encode=None, quantizer="uniform"):
     """Calibrate every KV head (library and oracle), encode the first n_encode (default all)
     context tokens on the GPU.  Returns (cache, q [batch, n_q, d] float32, host contexts of the
     sampled (b, h), oracle arts, tails: tokens n_encode.. of every (tensor, b, h))."""
@@ -29,8 +29,10 @@ def _layer(cfg, n_tokens, sampled, n_encode=None):
     for t in (synth.K, synth.V):
         cal = [synth.draw(cfg.idx, 0, h, t, "calib", cfg.n_calib, dtype=cfg.dtype, marginal=cfg.marginal)
                for h in range(cfg.n_kv_heads)]
-        blobs[t] = [api.calibrate(synth.bf16_bits(c), cfg.rotation, cfg.bits_per_elem) for c in cal]
-        arts[t] = {h: O.calibrate(cal[h], cfg.rotation, cfg.bits_per_elem) for h in {s[1] for s in sampled}}
+        blobs[t] = [api.calibrate(synth.bf16_bits(c), cfg.rotation, cfg.bits_per_elem, quantizer=quantizer)
+                    for c in cal]
+        arts[t] = {h: O.calibrate(cal[h], cfg.rotation, cfg.bits_per_elem, quantizer=quantizer)
+                   for h in {s[1] for s in sampled}}
     cap = -(-n_tokens // 64) * 64
     cache = api.CompressedKVCache(blobs[synth.K], blobs[synth.V], batch, cap)
     n_enc = n_tokens if n_encode is None else n_encode
@@ -120,6 +122,72 @@ def test_fullsize_layer_sampled_heads(idx, sampled):
         more.append(("std %s" % mode if mode != "peaked" else "peaked", qm, om.cpu().numpy(), lm.cpu().numpy()))
     for i, (b, h) in enumerate(sampled):
         _check_head(cfg, cache, q, host, arts, b, h, n, o, l, check_codes=(i == 0), more=more)
+
+
+@pytest.mark.parametrize("idx,sampled", [(2, [(0, 0), (0, 7)]), (3, [(0, 0), (9, 5), (15, 7)])])
+def test_fullsize_lloyd_max_layer(idx, sampled):
+    """Lloyd-Max caches at full size: the 32K-token 2.76-bit layer (8 KV heads) and the
+    batch-16 x 8K 4-bit layer, K and V Lloyd-Max, whole layer on the GPU (the level pass), sampled
+    sequences' codes and attention against the oracle."""
+    import torch
+    cfg = synth.CONFIGS[idx]
+    n = cfg.n_tokens
+    cache, q, host, arts, _ = _layer(cfg, n, set(sampled), quantizer="lloyd-max")
+    assert cache.quantizer == 3
+    out, lse = cache.decode_attn(torch.from_numpy(q).cuda(), n)
+    torch.cuda.synchronize()
+    o, l = out.cpu().numpy(), lse.cpu().numpy()
+    for i, (b, h) in enumerate(sampled):
+        _check_head(cfg, cache, q, host, arts, b, h, n, o, l, check_codes=(i == 0))
+
+
+def test_fullsize_append_loop_64_steps():
+    """The batch-16 workload's decode loop for all of its 64 steps on two sequences' worth of
+    cache: each step encodes one new K and V token per (b, h) at the next offset and runs decode
+    attention over the grown cache; the codes of every appended token and the attention of steps
+    1, 17, 33 and 64 are checked against the oracle."""
+    import torch
+    cfg = synth.CONFIGS[3]
+    n0, steps = cfg.n_tokens, cfg.decode_steps
+    sampled = {(0, 0), (1, 3)}
+    batch = 2
+    from dataclasses import replace
+    cfg2 = replace(cfg, batch=batch)
+    cache, q, host, arts, tails = _layer(cfg2, n0 + steps, sampled, n_encode=n0)
+    qt = torch.from_numpy(q).cuda()
+    group = cfg.n_q_heads // cfg.n_kv_heads
+    for s_ in range(steps):
+        for t in (synth.K, synth.V):
+            x = np.stack([np.stack([tails[(t, b, h)][s_] for h in range(cfg.n_kv_heads)]) for b in range(batch)])
+            cache.encode(t, torch.from_numpy(x[:, :, None, :].astype(np.float32)).to(torch.bfloat16).cuda(),
+                         token_offset=n0 + s_)
+        n = n0 + s_ + 1
+        if s_ + 1 in (1, 17, 33, 64):
+            out, lse = cache.decode_attn(qt, n)
+            torch.cuda.synchronize()
+            o, l = out.cpu().numpy(), lse.cpu().numpy()
+            for b, h in sorted(sampled):
+                ref, lref = O.decode_attention(q[b, h * group:(h + 1) * group],
+                                               [O.encode_codes(host[(synth.K, b, h)][:n], arts[synth.K][h])],
+                                               [O.encode_codes(host[(synth.V, b, h)][:n], arts[synth.V][h])],
+                                               [arts[synth.K][h]], [arts[synth.V][h]])
+                err = float(np.abs(o[b, h * group:(h + 1) * group] - ref).max())
+                lerr = float(np.abs(l[b, h * group:(h + 1) * group] - lref).max())
+                print("append step %d (b=%d, h=%d, %d tokens): max abs err %.2e, lse err %.2e" % (s_ + 1, b, h, n, err, lerr),
+                      flush=True)
+                assert err <= ATOL_ATTN and lerr <= 5e-3
+    # every appended token's codes (the last two tiles hold them)
+    n = n0 + steps
+    for t in (synth.K, synth.V):
+        for b, h in sorted(sampled):
+            art = arts[t][h]
+            B = int(art["bits"].sum())
+            words = cache.codes(t)[b, h].cpu().numpy().view(np.uint32)
+            first = n0 // 64
+            w = words[first * 2 * B:first * 2 * B + O.packed_words(B, n - n0)]
+            got = unpack_all(w, art["bits"], n - n0, t)
+            want = O.encode_codes(host[(t, b, h)][n0:n], art)
+            assert_codes_match(host[(t, b, h)][n0:n], art, got, want, cfg.dtype, ("append", t, b, h))
 
 
 def test_fullsize_batch16_append_sampled():

@@ -415,3 +415,74 @@ def test_segments_tiers_match_oracle(avg_bits):
         api.decode_attn_segments(segs, qt * 0.5, 1, n_kv)
         torch.cuda.synchronize()
     print("segments graph replays equal the eager call", flush=True)
+
+
+def test_segments_raw_tier_appends_64_steps():
+    """The tiered workload's decode loop: after prefill (tiers from the oracle's solver at 2.76
+    bits per element), 64 steps each append one token per KV head to the raw bf16 tier (a row
+    write and a length increment on the device) and run the multi-segment decode attention; the
+    results of steps 1, 32 and 64 match the oracle's segment attention with the appended tokens."""
+    torch = _torch()
+    from compressed_decode_attention_head_amd import api
+    cfg, n_kv, group, n, steps = 5, 2, 4, 600, 64
+    n_q = n_kv * group
+    cal = {t: [synth.draw(cfg, 0, h, t, "calib", 1024) for h in range(n_kv)] for t in (synth.K, synth.V)}
+    x = {t: np.stack([synth.draw(cfg, 0, h, t, "context", n + steps) for h in range(n_kv)]) for t in (synth.K, synth.V)}
+    arts = {(tau, t): [O.calibrate(c, "klt", float(tau)) for c in cal[t]] for tau in (2, 4) for t in (synth.K, synth.V)}
+    tiers = []
+    for h in range(n_kv):
+        dist = O.tier_distortions([arts[(2, synth.K)][h]["sigma2"], arts[(2, synth.V)][h]["sigma2"]], 128)
+        tiers.append(O.token_tiers(synth.zipf_mass(cfg, 0, h, n), dist, 128, 2.76))
+    idx = {tau: [np.nonzero(tiers[h] == tau)[0] for h in range(n_kv)] for tau in (2, 4, 16)}
+    q = synth.queries(cfg, 0, n_q, n_kv, [x[synth.K][h][:n] for h in range(n_kv)])
+    segs, keep = [], []
+    for tau in (2, 4, 16):
+        counts = [len(idx[tau][h]) for h in range(n_kv)]
+        cap = max(64, -(-(max(counts) + (steps if tau == 16 else 0)) // 64) * 64)
+        xs = {t: np.zeros((1, n_kv, cap, 128), dtype=np.float32) for t in (synth.K, synth.V)}
+        for t in (synth.K, synth.V):
+            for h in range(n_kv):
+                xs[t][0, h, :counts[h]] = x[t][h][idx[tau][h]]
+        sl = torch.tensor([counts], dtype=torch.int32, device="cuda")
+        if tau == 16:
+            kr = torch.from_numpy(xs[synth.K]).to(torch.bfloat16).cuda()
+            vr = torch.from_numpy(xs[synth.V]).to(torch.bfloat16).cuda()
+            keep += [kr, vr, sl]
+            raw = (kr, vr, torch.tensor(counts, dtype=torch.int64, device="cuda"), sl)
+            segs.append({"k_raw": kr, "v_raw": vr, "seq_lens": sl, "max_seq_len": max(counts) + steps})
+        else:
+            blobs = {t: [api.calibrate(synth.bf16_bits(c), "klt", float(tau)) for c in cal[t]] for t in (synth.K, synth.V)}
+            cache = api.CompressedKVCache(blobs[synth.K], blobs[synth.V], 1, cap)
+            for t in (synth.K, synth.V):
+                cache.encode(t, torch.from_numpy(xs[t]).to(torch.bfloat16).cuda())
+            keep += [cache, sl]
+            segs.append({"cache": cache, "seq_lens": sl, "max_seq_len": max(counts)})
+    kr, vr, base, sl = raw
+    new = {t: torch.from_numpy(np.ascontiguousarray(x[t][:, n:n + steps]).astype(np.float32)).to(torch.bfloat16).cuda()
+           for t in (synth.K, synth.V)}
+    heads = torch.arange(n_kv, device="cuda")
+    qt = torch.from_numpy(q[None].astype(np.float32)).cuda()
+    coded = {}
+    for h in range(n_kv):
+        coded[h] = []
+        for tau in (2, 4):
+            ii = idx[tau][h]
+            rec = [O.reconstruct(O.encode_codes(x[t][h][ii], arts[(tau, t)][h]), arts[(tau, t)][h]) for t in (synth.K, synth.V)]
+            coded[h].append((rec[0], rec[1]))
+    for s_ in range(steps):
+        kr[0, heads, base + s_] = new[synth.K][:, s_]
+        vr[0, heads, base + s_] = new[synth.V][:, s_]
+        sl += 1
+        out, lse = api.decode_attn_segments(segs, qt, 1, n_kv)
+        if s_ + 1 in (1, 32, 64):
+            torch.cuda.synchronize()
+            o, l = out[0].cpu().numpy(), lse[0].cpu().numpy()
+            err = lerr = 0.0
+            for g in range(n_q):
+                h = g // group
+                rawk = np.concatenate([x[synth.K][h][idx[16][h]], x[synth.K][h][n:n + s_ + 1]])
+                rawv = np.concatenate([x[synth.V][h][idx[16][h]], x[synth.V][h][n:n + s_ + 1]])
+                ref, lref = O.segment_attention(q[g], coded[h] + [(rawk, rawv)])
+                err, lerr = max(err, float(np.abs(o[g] - ref).max())), max(lerr, abs(float(l[g]) - lref))
+            print("raw-tier append step %d: max abs err %.2e, lse err %.2e" % (s_ + 1, err, lerr), flush=True)
+            assert err <= ATOL_ATTN and lerr <= 5e-3
