@@ -296,8 +296,12 @@ aatc_status aatc_calib_validate(const void* calib_host, size_t calib_bytes);
 int32_t aatc_calib_v_tiles(const void* calib_host);
 
 /*
- * aatc_encode -- device, async.  Quantizes and packs tokens [token_offset, token_offset +
- * n_tokens) of every (b,h) of tensor `which` (0 = K, 1 = V) into the cache.
+ * aatc_encode -- device, async.  [page "Ablation, Statistical Inference, and Validation for
+ * KV-Cache Compression", first abstract: a Walsh-Hadamard transform followed by a scalar MSE
+ * quantizer; page "SPHERICAL KV ...", NOVA-KV abstract: a fixed number of bits per token; page
+ * "SPECTRA ...", Abstract: the cache is coded in the rotated coordinates]  Quantizes and packs
+ * tokens [token_offset, token_offset + n_tokens) of every (b,h) of tensor `which` (0 = K, 1 = V)
+ * into the cache.
  *   x_dev: element (b,h,t,j) at x_dev[b*strides[0] + h*strides[1] + t*strides[2] + j],
  *   t relative to token_offset; dtype F32 or BF16.  The blob's encoder y = E x (E = R except
  *   for NOVA keys) and the quantizer run in fp64.  Any 16-byte aligned rows are read with
