@@ -292,7 +292,8 @@ aatc_status aatc_joint_kv_split(const void* k_calib_host, const void* v_calib_ho
 aatc_status aatc_calib_validate(const void* calib_host, size_t calib_bytes);
 
 /* Number of 16-field column groups decode attention uses for a V blob:
- * ceil(n_fields4/16) + ceil(n_fields2/16) + ceil(n_fields1/16) (0..24); -1 for a bad blob. */
+ * ceil(n_fields4/16) + ceil(n_fields2/16) + ceil(n_fields1/16) (0..24); -1 for a null blob or
+ * a wrong magic or d (the checksum is aatc_calib_validate's job). */
 int32_t aatc_calib_v_tiles(const void* calib_host);
 
 /*
