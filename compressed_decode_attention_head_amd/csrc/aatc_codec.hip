@@ -125,44 +125,44 @@ struct CodecArgs {
 };
 
 // ---------------------------------------------------------------------------------------
-// Encode.  Grid (G, KV heads, batch); a workgroup loads its head's quantizer and packing tables
-// into LDS once, then walks tiles tile0 + blockIdx.x, + G, ...  Per tile:
-//  1. the x rows into LDS as fp32.  With 16-byte aligned rows the next tile's rows are loaded
-//     into registers while this tile computes: the barriers here wait for LDS only, and LDS
-//     atomics are written by hand, so nothing waits for those loads before their use;
-//  2. y = E x in fp64.  A Walsh-Hadamard blob runs the fast transform: thread = (token,
-//     quarter of the channels), five butterfly stages in registers and two across lanes,
-//     then one multiply by the blob's 1/sqrt(d) (its R[0]); other blobs run the 64x128x128
-//     GEMM with E staged through LDS;
-//  3. codes stay in the thread's registers;
-//  4. the tile's packed words are OR-ed together in LDS: for K each thread appends its
-//     channels' codes as one contiguous bit run per token (planes are ordered by channel), for
-//     V it ORs each field value at its bit position; then one writer per word.
+// Encode.  Grid (G, KV heads, batch) of 4-wave workgroups.  A workgroup loads its head's
+// quantizer and packing tables into LDS once (its only barriers); after that every wave works
+// alone on half tiles: 32 consecutive tokens of one sequence, whose packed words no other half
+// tile touches (K: the 32 B bits of the half tile are B whole words; V: w words of every w-bit
+// field).  Per half tile:
+//  1. rows straight from memory into registers (16-byte aligned bf16 rows of a Walsh-Hadamard
+//     blob: the next half tile's rows are in flight while this one computes);
+//  2. y = E x in fp64:
+//     - Walsh-Hadamard: lane = (token, half of the channels, split on channel bit 3); six
+//       butterfly stages in registers over the other channel bits and one with the partner lane
+//       (a DPP quad permutation), all exact on bf16 rows, then one multiply by the blob's
+//       1/sqrt(d) (its R[0]);
+//     - other rotations: v_mfma_f64_16x16x4f64 with E as the A operand (16 output channels x 4
+//       input channels) and the rows as B (4 input channels x 16 tokens), two token blocks x 8
+//       channel blocks of accumulators per wave.  The contraction runs over the input channels
+//       in the order 32 g + s (g = the lane's k slot, s = the step), so each lane reads one
+//       contiguous 32-channel chunk of its rows and one of each E row it needs;
+//  3. the quantizer in fp64, separately rounded (this file is built without contraction);
+//  4. packing in the wave's own LDS area: K runs of consecutive channels OR-ed into the half
+//     tile's token-major bit string, V codes stored channel-major and gathered per word;
+//  5. the words to memory, keeping the bits of tokens before the first one written.
 // ---------------------------------------------------------------------------------------
-constexpr int KCE = 16;                                 // rows of E per GEMM staging chunk
-constexpr size_t kXs = T * D * 4;                       // x tile, fp32
-constexpr size_t kMc = KCE * D * 8;                     // E chunk, fp64; the packed words overlay it
-constexpr size_t kTabO = kXs + kMc;                     // fp64 o[128], 1/delta[128]
-constexpr size_t kTabBits = kTabO + 2 * D * 8;          // u8 bits[128]
-constexpr size_t kTabPb = kTabBits + D;                 // u16 first plane of each channel [128]
-constexpr size_t kTabFw = kTabPb + 2 * D;               // u16 first word of each field
-constexpr size_t kTabFs = kTabFw + 2 * AATC_MAX_FIELDS; // u8 width | shift << 4 of each field
-constexpr size_t kTabFc = kTabFs + AATC_MAX_FIELDS;     // u8 channel of each field
-constexpr size_t kTabWf = kTabFc + AATC_MAX_FIELDS;     // u16 field of each V word [2*1024]
-constexpr size_t kTabTh = kTabWf + 2 * 2 * AATC_D * AATC_MAX_BITS;   // fp64 Lloyd-Max thresholds
-constexpr size_t kEncodeLds = kTabTh + 8 * AATC_LEVELS;
-static_assert(2 * AATC_D * AATC_MAX_BITS * 4 <= kMc, "packed words fit the staging area");
-
-// u = (y - o) * (1/Delta) + 2^(b-1) as separately rounded fp64 operations; code =
-// clamp(floor(u), 0, 2^b - 1), NaN -> 0.  On [0, 2^b - 1) truncation is the floor.
-// Branch-free: the clamp runs in fp64 (NaN fails u >= 0), so the conversion is always in range.
-__device__ inline int quantize(double y, double o, double inv, int bi) {
-  double u = (y - o) * inv;
-  u = u + static_cast<double>(1 << (bi > 0 ? bi - 1 : 0));
-  const double top = static_cast<double>((1 << bi) - 1);
-  const double uc = u >= 0.0 ? fmin(u, top) : 0.0;
-  return bi > 0 ? static_cast<int>(uc) : 0;
-}
+constexpr int HT = 32;                                      // tokens of a half tile
+constexpr int WAVES = THREADS / 64;
+constexpr size_t kQ = 0;                                    // fp64 {o, 1/scale, 2^(b-1), 2^b - 1} per channel
+constexpr size_t kTBits = kQ + 32 * D;                      // u8 bits[128]
+constexpr size_t kTPb = kTBits + D;                         // u16 first plane of each channel
+constexpr size_t kTFw = kTPb + 2 * D;                       // u16 first word of each field
+constexpr size_t kTFs = kTFw + 2 * AATC_MAX_FIELDS;         // u8 width | shift << 4 of each field
+constexpr size_t kTFc = kTFs + AATC_MAX_FIELDS;             // u8 channel of each field
+constexpr size_t kTHf = kTFc + AATC_MAX_FIELDS;             // u16 field of each word of a half tile
+constexpr size_t kTTh = kTHf + 2 * AATC_D * AATC_MAX_BITS;  // fp64 Lloyd-Max thresholds
+constexpr size_t kWave = kTTh + 8 * AATC_LEVELS;            // per wave: rows, then K words or V codes
+constexpr int XLD = D + 4;                                  // fp32 row stride of the GEMM rows
+constexpr size_t kWaveBytes = HT * XLD * 4;                 // 32 fp32 rows; >= 4096 B of words or codes
+constexpr size_t kEncodeLds = kWave + WAVES * kWaveBytes;
+static_assert(kTTh % 16 == 0 && kWave % 16 == 0, "LDS tables aligned");
+static_assert(AATC_D * AATC_MAX_BITS * 4 <= kWaveBytes, "a half tile's K words (B <= 1024) fit the wave area");
 
 // Lloyd-Max: z = (y - o) * (1/s) as separately rounded fp64 operations; the code is the number
 // of the b-bit table's 2^b - 1 ascending thresholds at or below z, by a b-step binary search
@@ -187,365 +187,385 @@ __device__ inline double quad_xor(double x) {
                                                      static_cast<unsigned>(lo)));
 }
 
-// Workgroup barrier that waits for this wave's LDS operations only (global loads stay in flight).
-__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 // LDS OR without a return value, not ordered by the compiler against global loads in flight.
 __device__ inline void lds_or(uint32_t* p, uint32_t v) {
   asm volatile("ds_or_b32 %0, %1" : : "v"(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p))), "v"(v) : "memory");
 }
-// OR the low n (1..32) bits of v into the bit string S at bit position pos.
-__device__ inline void or_bits(uint32_t* S, int pos, uint32_t v) {
-  if (!v) return;
-  const int w = pos >> 5, sh = pos & 31;
-  lds_or(S + w, v << sh);
-  if (sh && (v >> (32 - sh))) lds_or(S + w + 1, v >> (32 - sh));
+
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline double bf16_lo(uint32_t w) { return static_cast<double>(__uint_as_float(w << 16)); }
+__device__ inline double bf16_hi(uint32_t w) { return static_cast<double>(__uint_as_float(w & 0xffff0000u)); }
+
+// Code of value y of a channel whose table row is q = {o, 1/scale, 2^(b-1), 2^b - 1}.  Uniform:
+// clamp(floor((y - o) * (1/Delta) + 2^(b-1)), 0, 2^b - 1) with NaN -> 0; the clamp runs in fp64
+// (fmax returns 0 for NaN), so the conversion always truncates a value in [0, 2^b - 1].
+// Lloyd-Max: the b-bit table's threshold count (quantize_lm).
+__device__ inline int code_of(double y, const double* q, int bi, bool lm, const double* thr) {
+  if (lm) return quantize_lm(y, q[0], q[1], bi, thr);
+  double u = (y - q[0]) * q[1];
+  u = u + q[2];
+  return static_cast<int>(fmin(fmax(u, 0.0), q[3]));
 }
 
-// y = E x for the tile (A = x in LDS), fp64, as tile_gemm but with LDS-only barriers.
-__device__ void tile_gemm_e(const float* A, const double* __restrict__ E, double* mchunk, double acc[4][8]) {
-  const int tid = threadIdx.x;
-  const int tb = tid >> 4, cb = tid & 15;
-  for (int aa = 0; aa < 4; ++aa)
-    for (int bb = 0; bb < 8; ++bb) acc[aa][bb] = 0.0;
-  for (int k0 = 0; k0 < D; k0 += KCE) {
-    lds_barrier();
-    for (int e = tid; e < KCE * D; e += THREADS) {
-      const int kk = e / D, i = e % D;   // mchunk[kk][i] = E(i, k0+kk)
-      mchunk[kk * D + i] = E[i * D + k0 + kk];
+// OR the run v (at most 64 bits, higher bits zero) into the bit string S at bit position pos;
+// words the run does not reach are not touched.
+__device__ inline void or_run(uint32_t* S, int pos, uint64_t v) {
+  if (!v) return;
+  const int w = pos >> 5, sh = pos & 31;
+  const uint64_t lo = v << sh;
+  const uint32_t top = sh ? static_cast<uint32_t>(v >> (64 - sh)) : 0u;
+  if (static_cast<uint32_t>(lo)) lds_or(S + w, static_cast<uint32_t>(lo));
+  if (static_cast<uint32_t>(lo >> 32)) lds_or(S + w + 1, static_cast<uint32_t>(lo >> 32));
+  if (top) lds_or(S + w + 2, top);
+}
+
+__device__ inline const double* tq_row(const double* qtab, int i) { return qtab + 4 * i; }
+
+// A half tile's K words (the B words of its 32 tokens' bit string, built in S) to memory; bits
+// of tokens before lo keep their value.
+__device__ inline void write_k_words(const uint32_t* S, uint32_t* out, int B, int lo, int lane) {
+  for (int u = lane; u < B; u += 64) {
+    uint32_t word = S[u];
+    if (lo > 0) {
+      const int kb = lo * B - 32 * u;                            // kept bits in this word
+      const uint32_t keep = kb >= 32 ? 0xffffffffu : (kb <= 0 ? 0u : ((1u << kb) - 1u));
+      if (keep) word |= out[u] & keep;
     }
-    lds_barrier();
-#pragma unroll 2
-    for (int kk = 0; kk < KCE; ++kk) {
-      double av[4], mv[8];
-      for (int aa = 0; aa < 4; ++aa) av[aa] = static_cast<double>(A[(tb * 4 + aa) * D + k0 + kk]);
-      for (int bb = 0; bb < 8; ++bb) mv[bb] = mchunk[kk * D + cb * 8 + bb];
-      for (int aa = 0; aa < 4; ++aa)
-        for (int bb = 0; bb < 8; ++bb) acc[aa][bb] = fma(av[aa], mv[bb], acc[aa][bb]);
-    }
+    out[u] = word;
   }
 }
 
-// The tiles of one workgroup; WHT selects the fast transform.  Not inlined, so that each form
-// gets its own register allocation (both together would spill).
+// A half tile's V words from its codes cs[channel][32 tokens]: word jj of field f is word
+// fw + half w + jj of the tile, holding the tokens the tile layout (include/aatc.h) gives it,
+// less 32 half; bits of tokens before lo keep their value.
+__device__ inline void write_v_words(const uint8_t* cs, uint32_t* out, int B, int half, int lo, int lane,
+                                     const uint16_t* t_hf, const uint16_t* t_fw, const uint8_t* t_fs,
+                                     const uint8_t* t_fc) {
+  for (int u = lane; u < B; u += 64) {
+    const int f = t_hf[u];
+    const int fw = t_fw[f], ws = t_fs[f], sh = ws >> 4, wd = ws & 15;
+    const int jj = u - fw / 2;
+    const uint8_t* col = cs + t_fc[f] * HT;
+    uint32_t word = 0;
+    if (wd == 4) {
+      // tokens 8 jj .. 8 jj + 7; token 8 jj + 4 rl + m at bits 8 m + 4 rl
+      const uint2 q = *reinterpret_cast<const uint2*>(col + 8 * jj);
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const uint32_t code = ((n < 4 ? q.x : q.y) >> (8 * (n & 3))) & 0xffu;
+        word |= ((code >> sh) & 15u) << (8 * (n & 3) + 4 * (n >> 2));
+      }
+    } else if (wd == 2) {
+      // tokens 16 jj + n: bits (8 m + 2 r + b + jj % 2) mod 32
+      const uint4 q = *reinterpret_cast<const uint4*>(col + 16 * jj);
+      const uint32_t uw[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int n = 0; n < 16; ++n) {
+        const uint32_t v2 = ((uw[n >> 2] >> (8 * (n & 3))) >> sh) & 3u;
+        const int base = (8 * (n & 3) + 2 * (n >> 2) + (jj & 1)) & 31;
+        word |= ((v2 & 1u) << base) | ((v2 >> 1) << ((base + 1) & 31));
+      }
+    } else {
+      // tokens n = 0..31: bit 8 m + 2 r + n / 16
+      const uint4* q2 = reinterpret_cast<const uint4*>(col);
+      const uint4 qa = q2[0], qb = q2[1];
+      const uint32_t uw[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+#pragma unroll
+      for (int n = 0; n < 32; ++n) {
+        const uint32_t v1 = ((uw[n >> 2] >> (8 * (n & 3))) >> sh) & 1u;
+        word |= v1 << (8 * (n & 3) + 2 * ((n >> 2) & 3) + (n >> 4));
+      }
+    }
+    const int wt = fw + half * wd + jj;
+    if (lo > 0) {
+      uint32_t keep = 0;
+      for (int q = 0; q < 32; ++q) {
+        int bit;
+        if (v_token(half * wd + jj, q, wd, &bit) - HT * half < lo) keep |= 1u << q;
+      }
+      if (keep) word |= out[wt] & keep;
+    }
+    out[wt] = word;
+  }
+}
+
 template <bool WHT>
-__device__ __attribute__((noinline)) void encode_tiles(const CodecArgs& a) {
+__device__ __attribute__((noinline)) void encode_waves(const CodecArgs& a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  float* xs = reinterpret_cast<float*>(smem);
-  double* mchunk = reinterpret_cast<double*>(smem + kXs);
-  uint32_t* S = reinterpret_cast<uint32_t*>(smem + kXs);                  // overlays mchunk
-  double* t_o = reinterpret_cast<double*>(smem + kTabO);
-  double* t_inv = t_o + D;
-  uint8_t* t_bits = smem + kTabBits;
-  uint16_t* t_pb = reinterpret_cast<uint16_t*>(smem + kTabPb);
-  uint16_t* t_fw = reinterpret_cast<uint16_t*>(smem + kTabFw);
-  uint8_t* t_fs = smem + kTabFs;
-  uint8_t* t_fc = smem + kTabFc;
-  uint16_t* t_wf = reinterpret_cast<uint16_t*>(smem + kTabWf);
-  double* t_th = reinterpret_cast<double*>(smem + kTabTh);
-  const int tid = threadIdx.x;
+  double* qtab = reinterpret_cast<double*>(smem + kQ);
+  uint8_t* t_bits = smem + kTBits;
+  uint16_t* t_pb = reinterpret_cast<uint16_t*>(smem + kTPb);
+  uint16_t* t_fw = reinterpret_cast<uint16_t*>(smem + kTFw);
+  uint8_t* t_fs = smem + kTFs;
+  uint8_t* t_fc = smem + kTFc;
+  uint16_t* t_hf = reinterpret_cast<uint16_t*>(smem + kTHf);
+  double* t_th = reinterpret_cast<double*>(smem + kTTh);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.y, b = blockIdx.z;
   const aatc_calib* c = a.calib + h;
   const int B = c->total_bits, nf = c->n_fields;
-  constexpr bool wht = WHT;
-  const double rs = c->R[0];                           // WHT: 1/sqrt(d) as the blob holds it
   const bool lm = c->quantizer == AATC_QUANT_LLOYD_MAX;
+  const bool isv = a.which == 1;
 
   // ---- tables, once per workgroup
   if (tid < D) {
-    t_o[tid] = c->o[tid];
-    t_inv[tid] = lm ? c->inv_scale[tid] : c->inv_delta[tid];
-    t_bits[tid] = c->bits[tid];
+    const int bi = c->bits[tid];
+    double* q = qtab + 4 * tid;
+    q[0] = c->o[tid];
+    q[1] = lm ? c->inv_scale[tid] : c->inv_delta[tid];
+    q[2] = static_cast<double>(bi ? 1 << (bi - 1) : 0);
+    q[3] = static_cast<double>((1 << bi) - 1);
+    t_bits[tid] = static_cast<uint8_t>(bi);
   }
   if (lm)
     for (int k = tid; k < AATC_LEVELS; k += THREADS) t_th[k] = c->thresh[k];
-  for (int f = tid; f < nf; f += THREADS) {
-    const int fw = c->field_word[f], wd = c->field_width[f];
-    t_fw[f] = static_cast<uint16_t>(fw);
-    t_fs[f] = static_cast<uint8_t>(wd | (c->field_shift[f] << 4));
-    t_fc[f] = static_cast<uint8_t>(c->field_channel[f]);
-    if (a.which == 1)
-      for (int j = 0; j < 2 * wd; ++j) t_wf[fw + j] = static_cast<uint16_t>(f);
-  }
-  lds_barrier();
+  if (isv)
+    for (int f = tid; f < nf; f += THREADS) {
+      const int fw = c->field_word[f], wd = c->field_width[f];
+      t_fw[f] = static_cast<uint16_t>(fw);
+      t_fs[f] = static_cast<uint8_t>(wd | (c->field_shift[f] << 4));
+      t_fc[f] = static_cast<uint8_t>(c->field_channel[f]);
+      for (int j = 0; j < wd; ++j) t_hf[fw / 2 + j] = static_cast<uint16_t>(f);   // fields are contiguous
+    }
+  __syncthreads();
   if (tid < D) {
     int s0 = 0;
     for (int i = 0; i < tid; ++i) s0 += t_bits[i];
     t_pb[tid] = static_cast<uint16_t>(s0);
   }
+  __syncthreads();
 
+  unsigned char* warea = smem + kWave + wave * kWaveBytes;
+  uint32_t* wb = reinterpret_cast<uint32_t*>(warea);           // K words of the half tile
+  uint8_t* cs = warea;                                          // V codes, [channel][32 tokens]
+  float* xs = reinterpret_cast<float*>(warea);                  // GEMM rows, [32][XLD] fp32
   const int64_t xrow = b * a.s_b + h * a.s_h - a.tok_off * a.s_t;    // + absolute token * s_t
-  const int64_t step = gridDim.x;
-  const bool bf16v = a.vec16 && a.dtype == AATC_BF16, f32v = a.vec16 && a.dtype == AATC_F32;
-  // rows of a tile held in registers: bf16 4 x 16 B per thread (row u >> 4, 8 channels),
-  // fp32 8 x 16 B (row u >> 5, 4 channels), u = tid + 256 r
-  uint4 pf[8];
-  auto tile_range = [&](int64_t tile, int& lo, int& hi) {
-    const int64_t tok0 = tile * T;
+  const bool bf16v = a.vec16 && a.dtype == AATC_BF16;
+  const int64_t ht_end = 2 * a.tile_end;                               // the last tile is completed
+  const int64_t hstep = static_cast<int64_t>(gridDim.x) * WAVES;
+  uint32_t* seq_out = a.codes + (static_cast<int64_t>(b) * a.n_kv_heads + h) * a.tiles_per_seq * (2 * B);
+  const uint16_t* xb = static_cast<const uint16_t*>(a.x);
+  // tokens [lo, hi) of half tile hti are written (half-local indices; hi <= lo: none)
+  auto half_range = [&](int64_t hti, int& lo, int& hi) {
+    const int64_t tok0 = hti * HT;
     lo = a.tok_off > tok0 ? static_cast<int>(a.tok_off - tok0) : 0;
-    const int64_t end = a.tok_off + a.n_tok - tok0;
-    hi = end < T ? static_cast<int>(end) : T;
+    const int64_t e = a.tok_off + a.n_tok - tok0;
+    hi = e < 0 ? 0 : (e < HT ? static_cast<int>(e) : HT);
   };
-  auto load_rows = [&](int64_t tile) {
-    int lo, hi;
-    tile_range(tile, lo, hi);
-    const int64_t tok0 = tile * T;
-    if (bf16v) {
-      const uint16_t* xb = static_cast<const uint16_t*>(a.x);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int u = tid + THREADS * r, t = u >> 4;
-        const int tc = t < lo ? lo : (t >= hi ? hi - 1 : t);         // always a written slot
-        pf[r] = *reinterpret_cast<const uint4*>(xb + xrow + (tok0 + tc) * a.s_t + 8 * (u & 15));
-      }
-    } else if (f32v) {
-      const float* xf = static_cast<const float*>(a.x);
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int u = tid + THREADS * r, t = u >> 5;
-        const int tc = t < lo ? lo : (t >= hi ? hi - 1 : t);
-        pf[r] = *reinterpret_cast<const uint4*>(xf + xrow + (tok0 + tc) * a.s_t + 4 * (u & 31));
-      }
-    }
+  // 16-byte piece of bf16 row t (half-local, clamped into [lo, hi)) at column col
+  auto piece = [&](int64_t hti, int lo, int hi, int t, int col) -> uint4 {
+    const int tc = t < lo ? lo : (t >= hi ? hi - 1 : t);
+    return *reinterpret_cast<const uint4*>(xb + xrow + (hti * HT + tc) * a.s_t + col);
   };
 
-  int64_t tile = a.tile0 + blockIdx.x;
-  if (tile < a.tile_end) load_rows(tile);
-  for (; tile < a.tile_end; tile += step) {
-    int lo, hi;
-    tile_range(tile, lo, hi);
-    const int64_t tok0 = tile * T;
-    lds_barrier();                                       // the previous tile is done with LDS
-    // ---- 1. x rows into LDS (slots outside [lo, hi) read as 0)
-    if (bf16v) {
+  int64_t ht = a.tok_off / HT + static_cast<int64_t>(blockIdx.x) * WAVES + wave;
+  if constexpr (WHT) {
+    // lane (tq, q4) = (lane >> 2, lane & 3); pass p of a half tile covers its tokens 16 p + tq.
+    // Slot k of the lane: channel (k & 7) | q4 << 3 | (k >> 3) << 5, read as 16-byte pieces
+    // 4 j + q4 of the row (j = k >> 3), so the four lanes of a token read 64 contiguous bytes.
+    const int tq = lane >> 2, q4 = lane & 3;
+    auto load_pass = [&](int64_t hti, int p, uint4 (&dst)[4]) {
+      int lo, hi;
+      half_range(hti, lo, hi);
+      if (hi <= lo) return;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int u = tid + THREADS * r, t = u >> 4;
+      for (int j = 0; j < 4; ++j) dst[j] = piece(hti, lo, hi, 16 * p + tq, 8 * (4 * j + q4));
+    };
+    uint4 pf[4];
+    if (bf16v && ht < ht_end) load_pass(ht, 0, pf);
+    const double rs = c->R[0];
+    for (; ht < ht_end; ht += hstep) {
+      int lo, hi;
+      half_range(ht, lo, hi);
+      const int half = static_cast<int>(ht & 1);
+      uint32_t* out = seq_out + (ht >> 1) * (2 * B);
+      if (!isv)
+        for (int u = lane; u < B; u += 64) wb[u] = 0u;
+#pragma unroll 1
+      for (int p = 0; p < 2; ++p) {
+        const int t = 16 * p + tq;
         const bool in = t >= lo && t < hi;
-        const uint32_t w[4] = {pf[r].x, pf[r].y, pf[r].z, pf[r].w};
-        float4* dst = reinterpret_cast<float4*>(xs + t * D + 8 * (u & 15));
-        dst[0] = in ? make_float4(__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
-                                  __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u))
-                    : make_float4(0.f, 0.f, 0.f, 0.f);
-        dst[1] = in ? make_float4(__uint_as_float(w[2] << 16), __uint_as_float(w[2] & 0xffff0000u),
-                                  __uint_as_float(w[3] << 16), __uint_as_float(w[3] & 0xffff0000u))
-                    : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-    } else if (f32v) {
+        double v[32];
+        if (bf16v) {
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int u = tid + THREADS * r, t = u >> 5;
-        const bool in = t >= lo && t < hi;
-        reinterpret_cast<uint4*>(xs + t * D)[u & 31] = in ? pf[r] : make_uint4(0u, 0u, 0u, 0u);
-      }
-    } else {
-      for (int e = tid; e < T * D; e += THREADS) {
-        const int t = e / D, j = e % D;
-        xs[e] = (t >= lo && t < hi) ? static_cast<float>(load_x(a.x, a.dtype, xrow + (tok0 + t) * a.s_t + j)) : 0.f;
-      }
-    }
-    if (tile + step < a.tile_end) load_rows(tile + step);   // next tile's rows, in flight from here
-    lds_barrier();
-
-    // ---- 2 + 3. rotate and quantize; codes packed four to a register
-    uint32_t cp[8];
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t w4[4] = {pf[j].x, pf[j].y, pf[j].z, pf[j].w};
 #pragma unroll
-    for (int k = 0; k < 8; ++k) cp[k] = 0u;
-    const int q4 = tid & 3, tb = tid >> 4, cb = tid & 15;
-    if constexpr (wht) {
-      const int tq = tid >> 2, i0 = 32 * q4;
-      double v[32];
-#pragma unroll
-      for (int k4 = 0; k4 < 8; ++k4) {
-        const float4 f = reinterpret_cast<const float4*>(xs + tq * D + i0)[k4];
-        v[4 * k4] = f.x;
-        v[4 * k4 + 1] = f.y;
-        v[4 * k4 + 2] = f.z;
-        v[4 * k4 + 3] = f.w;
-      }
-      // Sylvester order: y_i = sum_j (-1)^popcount(i & j) x_j; butterflies on index bits 0..4 in
-      // the thread, then bits 5 and 6 (lanes ^1 and ^2 hold the other channel quarters)
-#pragma unroll
-      for (int m = 1; m < 32; m <<= 1)
-#pragma unroll
-        for (int k = 0; k < 32; ++k)
-          if (!(k & m)) {
-            const double x0 = v[k], x1 = v[k + m];
-            v[k] = x0 + x1;
-            v[k + m] = x0 - x1;
+            for (int e = 0; e < 4; ++e) {
+              v[8 * j + 2 * e] = bf16_lo(w4[e]);
+              v[8 * j + 2 * e + 1] = bf16_hi(w4[e]);
+            }
           }
+          if (p == 0) load_pass(ht, 1, pf);                     // in flight from here
+          else if (ht + hstep < ht_end) load_pass(ht + hstep, 0, pf);
+        } else {
 #pragma unroll
-      for (int k = 0; k < 32; ++k) {
-        const double pv = quad_xor<0xB1>(v[k]);      // lane ^ 1
-        v[k] = (q4 & 1) ? pv - v[k] : v[k] + pv;
-      }
-#pragma unroll
-      for (int k = 0; k < 32; ++k) {
-        const double pv = quad_xor<0x4E>(v[k]);      // lane ^ 2
-        v[k] = (q4 & 2) ? pv - v[k] : v[k] + pv;
-      }
-#pragma unroll
-      for (int k = 0; k < 32; ++k)
-        cp[k >> 2] |= static_cast<uint32_t>(lm ? quantize_lm(v[k] * rs, t_o[i0 + k], t_inv[i0 + k], t_bits[i0 + k], t_th)
-                                                : quantize(v[k] * rs, t_o[i0 + k], t_inv[i0 + k], t_bits[i0 + k]))
-                      << (8 * (k & 3));
-    } else {
-      double acc[4][8];
-      tile_gemm_e(xs, c->E, mchunk, acc);
-#pragma unroll
-      for (int bb = 0; bb < 8; ++bb) {
-        const int i = 8 * cb + bb;
-#pragma unroll
-        for (int aa = 0; aa < 4; ++aa) {
-          const int n = 8 * aa + bb;
-          cp[n >> 2] |= static_cast<uint32_t>(lm ? quantize_lm(acc[aa][bb], t_o[i], t_inv[i], t_bits[i], t_th)
-                                                  : quantize(acc[aa][bb], t_o[i], t_inv[i], t_bits[i]))
-                        << (8 * (n & 3));
+          for (int k = 0; k < 32; ++k)
+            v[k] = in ? load_x(a.x, a.dtype, xrow + (ht * HT + t) * a.s_t + ((k & 7) | (q4 << 3) | ((k >> 3) << 5))) : 0.0;
         }
-      }
-    }
-    lds_barrier();                                       // x and the staging area are free
-    // codes over the x tile: K token-major [64][128], V channel-major [128][64]; slots outside
-    // [lo, hi) hold 0
-    uint8_t* cs = reinterpret_cast<uint8_t*>(xs);
-    if (wht) {
-      const int t = tid >> 2;
-      const bool in = t >= lo && t < hi;
-      if (a.which == 0) {
-        uint4* dst = reinterpret_cast<uint4*>(cs + t * D + 32 * q4);
-        dst[0] = in ? make_uint4(cp[0], cp[1], cp[2], cp[3]) : make_uint4(0u, 0u, 0u, 0u);
-        dst[1] = in ? make_uint4(cp[4], cp[5], cp[6], cp[7]) : make_uint4(0u, 0u, 0u, 0u);
-      } else {
+        // Sylvester order: y_i = sum_j (-1)^popcount(i & j) x_j, one butterfly per index bit; the
+        // stages commute, and on bf16 rows every sum is exact in fp64.  Channel bits 0-2 and 5-6
+        // in registers, bits 3 and 4 across the lanes of a quad (y0 = x0 + x1 on the lower lane,
+        // y1 = x0 - x1 on the upper one).
 #pragma unroll
-        for (int k = 0; k < 32; ++k) cs[(32 * q4 + k) * T + t] = in ? static_cast<uint8_t>(cp[k >> 2] >> (8 * (k & 3))) : 0;
-      }
-    } else {
+        for (int m = 1; m < 32; m <<= 1)
 #pragma unroll
-      for (int aa = 0; aa < 4; ++aa) {
-        const int t = 4 * tb + aa;
-        if (t < lo || t >= hi) {
-          cp[2 * aa] = 0u;
-          cp[2 * aa + 1] = 0u;
-        }
-      }
-      if (a.which == 0) {
+          for (int k = 0; k < 32; ++k)
+            if (!(k & m)) {
+              const double x0 = v[k], x1 = v[k + m];
+              v[k] = x0 + x1;
+              v[k + m] = x0 - x1;
+            }
+        const double s1 = (q4 & 1) ? -1.0 : 1.0, s2 = (q4 & 2) ? -1.0 : 1.0;
 #pragma unroll
-        for (int aa = 0; aa < 4; ++aa)
-          *reinterpret_cast<uint2*>(cs + (4 * tb + aa) * D + 8 * cb) = make_uint2(cp[2 * aa], cp[2 * aa + 1]);
-      } else {
-        // channel 8 cb + bb, tokens 4 tb .. 4 tb + 3: one dword
+        for (int k = 0; k < 32; ++k) v[k] = fma(s1, v[k], quad_xor<0xB1>(v[k]));
 #pragma unroll
-        for (int bb = 0; bb < 8; ++bb) {
-          uint32_t w4 = 0;
+        for (int k = 0; k < 32; ++k) v[k] = fma(s2, v[k], quad_xor<0x4E>(v[k]));
+        uint32_t cw[8];
 #pragma unroll
-          for (int aa = 0; aa < 4; ++aa) w4 |= ((cp[2 * aa + (bb >> 2)] >> (8 * (bb & 3))) & 0xffu) << (8 * aa);
-          *reinterpret_cast<uint32_t*>(cs + (8 * cb + bb) * T + 4 * tb) = w4;
-        }
-      }
-    }
-    if (a.which == 0)
-      for (int w = tid; w < 2 * B; w += THREADS) S[w] = 0u;
-    lds_barrier();
-
-    // ---- 4. K: OR each (token, quarter of the channels) run into the words; planes are
-    // ordered by channel, so a quarter's planes are one contiguous run of the token's bits
-    if (a.which == 0) {
-      const int t = tid >> 2, i0 = 32 * q4;
-      if (t >= lo && t < hi) {
-        const uint4* cr = reinterpret_cast<const uint4*>(cs + t * D + i0);
-        const uint4* br = reinterpret_cast<const uint4*>(t_bits + i0);
-        const uint4 c0 = cr[0], c1 = cr[1], b0 = br[0], b1 = br[1];
-        const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-        const uint32_t bw[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-        int pos = t * B + t_pb[i0];
-        uint64_t acc = 0;
-        int nb = 0;
+        for (int k = 0; k < 8; ++k) cw[k] = 0u;
 #pragma unroll
         for (int k = 0; k < 32; ++k) {
-          acc |= static_cast<uint64_t>((cw[k >> 2] >> (8 * (k & 3))) & 0xffu) << nb;
-          nb += (bw[k >> 2] >> (8 * (k & 3))) & 0xffu;
-          if (nb >= 32) {
-            or_bits(S, pos, static_cast<uint32_t>(acc));
-            pos += 32;
-            acc >>= 32;
-            nb -= 32;
-          }
+          const int i = (k & 7) | (q4 << 3) | ((k >> 3) << 5);
+          cw[k >> 2] |= static_cast<uint32_t>(code_of(v[k] * rs, tq_row(qtab, i), t_bits[i], lm, t_th)) << (8 * (k & 3));
         }
-        if (nb > 0) or_bits(S, pos, static_cast<uint32_t>(acc));
+        if (!in) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) cw[k] = 0u;
+        }
+        if (!isv) {
+          // four runs of 8 consecutive channels, 8 (4 j + q4) ..
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int i0 = 8 * (4 * j + q4);
+            uint64_t run = 0;
+            int nb = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              run |= static_cast<uint64_t>((cw[2 * j + (e >> 2)] >> (8 * (e & 3))) & 0xffu) << nb;
+              nb += t_bits[i0 + e];
+            }
+            or_run(wb, t * B + t_pb[i0], run);
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < 32; ++k)
+            cs[((k & 7) | (q4 << 3) | ((k >> 3) << 5)) * HT + t] = static_cast<uint8_t>(cw[k >> 2] >> (8 * (k & 3)));
+        }
       }
-      lds_barrier();
+      if (!isv) write_k_words(wb, out + half * B, B, lo, lane);
+      else write_v_words(cs, out, B, half, lo, lane, t_hf, t_fw, t_fs, t_fc);
     }
-
-    // ---- 5. one writer per word (V: gathered from the field's channel column); bits of tokens
-    // before lo keep their old value
-    uint32_t* out = a.codes + ((static_cast<int64_t>(b) * a.n_kv_heads + h) * a.tiles_per_seq + tile) * (2 * B);
-    for (int w = tid; w < 2 * B; w += THREADS) {
-      uint32_t word;
-      int f = 0, wd = 0, j = 0;
-      if (a.which == 0) {
-        word = S[w];
+  } else {
+    // GEMM: rows through the wave's LDS area as fp32 (coalesced loads: 16-byte piece 64 j + lane
+    // is row (64 j + lane) >> 4, column 8 ((64 j + lane) & 15)).  Lane (tt, g) = (lane & 15,
+    // lane >> 4); accumulator block (tb, cb), register r: token 16 tb + tt, channel 16 cb + 4 g + r.
+    const int tt = lane & 15, g = lane >> 4;
+    auto load_half = [&](int64_t hti, uint4 (&dst)[8]) {
+      int lo, hi;
+      half_range(hti, lo, hi);
+      if (hi <= lo) return;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int pc = 64 * j + lane;
+        dst[j] = piece(hti, lo, hi, pc >> 4, 8 * (pc & 15));
+      }
+    };
+    uint4 pf[8];
+    if (bf16v && ht < ht_end) load_half(ht, pf);
+    // v_mfma_f64_16x16x4f64 leaves D[i][j] in register i >> 2 of lane 16 (i & 3) + j, so the lane
+    // that feeds row i of A feeds E row 16 cb + 4 (i & 3) + (i >> 2): the output of lane (tt, g),
+    // register r is then channel 16 cb + 4 g + r, and a lane's four registers are adjacent channels
+    const double* erow = c->E + (4 * (tt & 3) + (tt >> 2)) * D + 32 * g;   // + 16 cb D + s
+    for (; ht < ht_end; ht += hstep) {
+      int lo, hi;
+      half_range(ht, lo, hi);
+      const int half = static_cast<int>(ht & 1);
+      uint32_t* out = seq_out + (ht >> 1) * (2 * B);
+      if (bf16v) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int pc = 64 * j + lane;
+          float4* dst = reinterpret_cast<float4*>(xs + (pc >> 4) * XLD + 8 * (pc & 15));
+          const uint32_t w4[4] = {pf[j].x, pf[j].y, pf[j].z, pf[j].w};
+          dst[0] = make_float4(__uint_as_float(w4[0] << 16), __uint_as_float(w4[0] & 0xffff0000u),
+                               __uint_as_float(w4[1] << 16), __uint_as_float(w4[1] & 0xffff0000u));
+          dst[1] = make_float4(__uint_as_float(w4[2] << 16), __uint_as_float(w4[2] & 0xffff0000u),
+                               __uint_as_float(w4[3] << 16), __uint_as_float(w4[3] & 0xffff0000u));
+        }
+        if (ht + hstep < ht_end) load_half(ht + hstep, pf);      // in flight from here
       } else {
-        f = t_wf[w];
-        const int ws = t_fs[f], sh = ws >> 4;
-        wd = ws & 15;
-        j = w - t_fw[f];
-        const uint8_t* col = cs + t_fc[f] * T;
-        word = 0;
-        if (wd == 4) {
-          // tokens 16 G + 4 r + m, r = 2 (j & 1) + (n >> 2), m = n & 3: bits 8 m + 4 (r & 1)
-          const uint2 u = *reinterpret_cast<const uint2*>(col + 8 * j);
+        for (int e = lane; e < HT * D; e += 64) {
+          const int t = e / D, i = e % D;
+          xs[t * XLD + i] = (t >= lo && t < hi) ? static_cast<float>(load_x(a.x, a.dtype, xrow + (ht * HT + t) * a.s_t + i)) : 0.f;
+        }
+      }
+      f64x4 acc[2][8];
 #pragma unroll
-          for (int n = 0; n < 8; ++n) {
-            const uint32_t code = ((n < 4 ? u.x : u.y) >> (8 * (n & 3))) & 0xffu;
-            word |= ((code >> sh) & 15u) << (8 * (n & 3) + 4 * (n >> 2));
-          }
-        } else if (wd == 2) {
-          // tokens 16 j + n: bits (8 m + 2 r + b + j % 2) mod 32
-          const uint4 u = *reinterpret_cast<const uint4*>(col + 16 * j);
-          const uint32_t uw[4] = {u.x, u.y, u.z, u.w};
+      for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-          for (int n = 0; n < 16; ++n) {
-            const uint32_t v = ((uw[n >> 2] >> (8 * (n & 3))) >> sh) & 3u;
-            const int base = (8 * (n & 3) + 2 * (n >> 2) + (j & 1)) & 31;
-            word |= ((v & 1u) << base) | ((v >> 1) << ((base + 1) & 31));
-          }
-        } else {
-          // tokens 32 j + n: bit 8 m + 2 r + n / 16
-          const uint4* u2 = reinterpret_cast<const uint4*>(col + 32 * j);
-          const uint4 ua = u2[0], ub = u2[1];
-          const uint32_t uw[8] = {ua.x, ua.y, ua.z, ua.w, ub.x, ub.y, ub.z, ub.w};
+        for (int cb = 0; cb < 8; ++cb) acc[tb][cb] = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 1
+      for (int s = 0; s < 32; s += 2) {
+        double2 e2[8];
 #pragma unroll
-          for (int n = 0; n < 32; ++n) {
-            const uint32_t v = ((uw[n >> 2] >> (8 * (n & 3))) >> sh) & 1u;
-            word |= v << (8 * (n & 3) + 2 * ((n >> 2) & 3) + (n >> 4));
+        for (int cb = 0; cb < 8; ++cb) e2[cb] = *reinterpret_cast<const double2*>(erow + 16 * cb * D + s);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const double x0 = static_cast<double>(xs[tt * XLD + 32 * g + s + u]);
+          const double x1 = static_cast<double>(xs[(16 + tt) * XLD + 32 * g + s + u]);
+#pragma unroll
+          for (int cb = 0; cb < 8; ++cb) {
+            const double ev = u ? e2[cb].y : e2[cb].x;
+            acc[0][cb] = __builtin_amdgcn_mfma_f64_16x16x4f64(ev, x0, acc[0][cb], 0, 0, 0);
+            acc[1][cb] = __builtin_amdgcn_mfma_f64_16x16x4f64(ev, x1, acc[1][cb], 0, 0, 0);
           }
         }
       }
-      if (lo > 0) {
-        uint32_t keep = 0;
-        if (a.which == 0) {
-          const int64_t kb = static_cast<int64_t>(lo) * B - 32 * w;     // kept bits in this word
-          keep = kb >= 32 ? 0xffffffffu : (kb <= 0 ? 0u : ((1u << kb) - 1u));
-        } else {
-          for (int q = 0; q < 32; ++q) {
-            int bit;
-            if (v_token(j, q, wd, &bit) < lo) keep |= 1u << q;
+      // the rows are consumed: the area now takes the K words or V codes
+      if (!isv)
+        for (int u = lane; u < B; u += 64) wb[u] = 0u;
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        const int t = 16 * tb + tt;
+        const bool in = t >= lo && t < hi;
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb) {
+          const int i0 = 16 * cb + 4 * g;
+          uint32_t cd[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            cd[r] = in ? static_cast<uint32_t>(code_of(acc[tb][cb][r], tq_row(qtab, i0 + r), t_bits[i0 + r], lm, t_th)) : 0u;
+          if (!isv) {
+            uint64_t run = 0;
+            int nb = 0;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              run |= static_cast<uint64_t>(cd[r]) << nb;
+              nb += t_bits[i0 + r];
+            }
+            or_run(wb, t * B + t_pb[i0], run);
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) cs[(i0 + r) * HT + t] = static_cast<uint8_t>(cd[r]);
           }
         }
-        if (keep) word |= out[w] & keep;
       }
-      out[w] = word;
+      if (!isv) write_k_words(wb, out + half * B, B, lo, lane);
+      else write_v_words(cs, out, B, half, lo, lane, t_hf, t_fw, t_fs, t_fc);
     }
   }
 }
 
-// Two waves per SIMD (two workgroups per CU): the fast transform keeps 32 fp64 values per thread.
+// Two waves per SIMD: the GEMM form keeps 16 accumulator blocks (128 registers) per lane.
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 8))) void k_encode(CodecArgs a) {
   const aatc_calib* c = a.calib + blockIdx.y;
   if (c->magic != AATC_MAGIC) return;
   if (c->rotation == AATC_ROT_WHT)
-    encode_tiles<true>(a);
+    encode_waves<true>(a);
   else
-    encode_tiles<false>(a);
+    encode_waves<false>(a);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -660,11 +680,14 @@ aatc_status launch_codec(bool encode, const aatc_cache* c, int which, const void
   }
   const int64_t tile_end = (off + n + AATC_TILE - 1) / AATC_TILE;
   a.tile_end = tile_end;
-  // encode: two workgroups per CU in all, each walking tiles of one (batch, head)
+  // encode: two workgroups per CU in all, each walking half tiles of one (batch, head) with its
+  // four waves
   int64_t gx = tile_end - a.tile0;
   if (encode) {
+    const int64_t halves = 2 * tile_end - off / 32;
     const int64_t per = (512 + static_cast<int64_t>(c->n_kv_heads) * c->batch - 1) /
                         (static_cast<int64_t>(c->n_kv_heads) * c->batch);
+    gx = (halves + 3) / 4;
     if (gx > per) gx = per;
   }
   dim3 grid(static_cast<unsigned>(gx), c->n_kv_heads, c->batch);
