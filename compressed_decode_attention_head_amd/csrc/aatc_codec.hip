@@ -157,11 +157,12 @@ constexpr size_t kTFs = kTFw + 2 * AATC_MAX_FIELDS;         // u8 width | shift 
 constexpr size_t kTFc = kTFs + AATC_MAX_FIELDS;             // u8 channel of each field
 constexpr size_t kTHf = kTFc + AATC_MAX_FIELDS;             // u16 field of each word of a half tile
 constexpr size_t kTTh = kTHf + 2 * AATC_D * AATC_MAX_BITS;  // fp64 Lloyd-Max thresholds
-constexpr size_t kWave = kTTh + 8 * AATC_LEVELS;            // per wave: rows, then K words or V codes
-constexpr int XLD = D + 4;                                  // fp32 row stride of the GEMM rows
-constexpr size_t kWaveBytes = HT * XLD * 4;                 // 32 fp32 rows; >= 4096 B of words or codes
-constexpr size_t kEncodeLds = kWave + WAVES * kWaveBytes;
-static_assert(kTTh % 16 == 0 && kWave % 16 == 0, "LDS tables aligned");
+constexpr size_t kWave = kTTh + 8 * AATC_LEVELS;            // per wave: a half tile's K words or V codes
+constexpr int XS = D + 8;                                   // bf16 row stride of the GEMM's staged rows
+constexpr size_t kWaveBytes = HT * XS * 2;                  // 32 bf16 rows; >= 32 x 128 code bytes, B <= 1024 words
+constexpr size_t kEch = kWave + WAVES * kWaveBytes;         // GEMM: two 8 KB chunks of E
+constexpr size_t kEncodeLds = kEch + 2 * 2 * AATC_D * 4 * 8;
+static_assert(kTTh % 16 == 0 && kWave % 16 == 0 && kEch % 16 == 0, "LDS tables aligned");
 static_assert(AATC_D * AATC_MAX_BITS * 4 <= kWaveBytes, "a half tile's K words (B <= 1024) fit the wave area");
 
 // Lloyd-Max: z = (y - o) * (1/s) as separately rounded fp64 operations; the code is the number
@@ -181,8 +182,8 @@ __device__ inline int quantize_lm(double y, double o, double inv, int bi, const 
 template <int CTRL>
 __device__ inline double quad_xor(double x) {
   const unsigned long long u = static_cast<unsigned long long>(__double_as_longlong(x));
-  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(u & 0xffffffffu), CTRL, 0xf, 0xf, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(u >> 32), CTRL, 0xf, 0xf, false);
+  const int lo = __builtin_amdgcn_mov_dpp(static_cast<int>(u & 0xffffffffu), CTRL, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_mov_dpp(static_cast<int>(u >> 32), CTRL, 0xf, 0xf, false);
   return __longlong_as_double(static_cast<long long>((static_cast<unsigned long long>(static_cast<unsigned>(hi)) << 32) |
                                                      static_cast<unsigned>(lo)));
 }
@@ -193,19 +194,38 @@ __device__ inline void lds_or(uint32_t* p, uint32_t v) {
 }
 
 typedef double f64x4 __attribute__((ext_vector_type(4)));
+// global-memory views of the encoder's pointers (a pointer reached through the argument struct
+// is otherwise a flat pointer)
+typedef __attribute__((address_space(1))) uint32_t gu32;
+typedef __attribute__((address_space(1))) uint16_t gu16;
+typedef __attribute__((address_space(1))) float gf32;
+typedef __attribute__((address_space(1))) double gf64;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) u32x4 gu4;
 
 __device__ inline double bf16_lo(uint32_t w) { return static_cast<double>(__uint_as_float(w << 16)); }
 __device__ inline double bf16_hi(uint32_t w) { return static_cast<double>(__uint_as_float(w & 0xffff0000u)); }
 
+// v_cvt_i32_f64: truncation toward zero, NaN -> 0, values beyond the int32 range clamped to it
+// (the instruction's own definition, which a C++ conversion does not promise).
+__device__ inline int cvt_i32_trunc(double u) {
+  int r;
+  asm("v_cvt_i32_f64_e32 %0, %1" : "=v"(r) : "v"(u));
+  return r;
+}
+
 // Code of value y of a channel whose table row is q = {o, 1/scale, 2^(b-1), 2^b - 1}.  Uniform:
-// clamp(floor((y - o) * (1/Delta) + 2^(b-1)), 0, 2^b - 1) with NaN -> 0; the clamp runs in fp64
-// (fmax returns 0 for NaN), so the conversion always truncates a value in [0, 2^b - 1].
+// clamp(floor((y - o) * (1/Delta) + 2^(b-1)), 0, 2^b - 1) with NaN -> 0.  Truncation toward zero
+// equals the floor on [0, 2^b - 1], and every value outside (NaN included) lands on the clamp's
+// side it belongs to, so the clamp runs on the truncated integer.
 // Lloyd-Max: the b-bit table's threshold count (quantize_lm).
 __device__ inline int code_of(double y, const double* q, int bi, bool lm, const double* thr) {
   if (lm) return quantize_lm(y, q[0], q[1], bi, thr);
   double u = (y - q[0]) * q[1];
   u = u + q[2];
-  return static_cast<int>(fmin(fmax(u, 0.0), q[3]));
+  const int top = (1 << bi) - 1;
+  const int ci = cvt_i32_trunc(u);
+  return ci < 0 ? 0 : (ci > top ? top : ci);
 }
 
 // OR the run v (at most 64 bits, higher bits zero) into the bit string S at bit position pos;
@@ -222,9 +242,17 @@ __device__ inline void or_run(uint32_t* S, int pos, uint64_t v) {
 
 __device__ inline const double* tq_row(const double* qtab, int i) { return qtab + 4 * i; }
 
+// Element i of the encoder's input (fp32 or bf16) through a global-memory pointer, so that the
+// load is not a flat access (which the LDS waits would also count).
+__device__ inline double gload_x(const void* x, int dt, int64_t i) {
+  if (dt == AATC_F32) return static_cast<double>(((const gf32*)(x))[i]);
+  const uint32_t u = static_cast<uint32_t>(((const gu16*)(x))[i]) << 16;
+  return static_cast<double>(__uint_as_float(u));
+}
+
 // A half tile's K words (the B words of its 32 tokens' bit string, built in S) to memory; bits
 // of tokens before lo keep their value.
-__device__ inline void write_k_words(const uint32_t* S, uint32_t* out, int B, int lo, int lane) {
+__device__ inline void write_k_words(const uint32_t* S, gu32* out, int B, int lo, int lane) {
   for (int u = lane; u < B; u += 64) {
     uint32_t word = S[u];
     if (lo > 0) {
@@ -239,7 +267,7 @@ __device__ inline void write_k_words(const uint32_t* S, uint32_t* out, int B, in
 // A half tile's V words from its codes cs[channel][32 tokens]: word jj of field f is word
 // fw + half w + jj of the tile, holding the tokens the tile layout (include/aatc.h) gives it,
 // less 32 half; bits of tokens before lo keep their value.
-__device__ inline void write_v_words(const uint8_t* cs, uint32_t* out, int B, int half, int lo, int lane,
+__device__ inline void write_v_words(const uint8_t* cs, gu32* out, int B, int half, int lo, int lane,
                                      const uint16_t* t_hf, const uint16_t* t_fw, const uint8_t* t_fs,
                                      const uint8_t* t_fc) {
   for (int u = lane; u < B; u += 64) {
@@ -339,13 +367,16 @@ __device__ __attribute__((noinline)) void encode_waves(const CodecArgs& a) {
   unsigned char* warea = smem + kWave + wave * kWaveBytes;
   uint32_t* wb = reinterpret_cast<uint32_t*>(warea);           // K words of the half tile
   uint8_t* cs = warea;                                          // V codes, [channel][32 tokens]
-  float* xs = reinterpret_cast<float*>(warea);                  // GEMM rows, [32][XLD] fp32
+  uint16_t* xsb = reinterpret_cast<uint16_t*>(warea);           // GEMM bf16 rows, [32][XS]
   const int64_t xrow = b * a.s_b + h * a.s_h - a.tok_off * a.s_t;    // + absolute token * s_t
+  const int64_t s_t = a.s_t;
+  const void* xp = a.x;
+  const int dtype = a.dtype;
   const bool bf16v = a.vec16 && a.dtype == AATC_BF16;
   const int64_t ht_end = 2 * a.tile_end;                               // the last tile is completed
   const int64_t hstep = static_cast<int64_t>(gridDim.x) * WAVES;
-  uint32_t* seq_out = a.codes + (static_cast<int64_t>(b) * a.n_kv_heads + h) * a.tiles_per_seq * (2 * B);
-  const uint16_t* xb = static_cast<const uint16_t*>(a.x);
+  gu32* seq_out = ((gu32*)(a.codes)) + (static_cast<int64_t>(b) * a.n_kv_heads + h) * a.tiles_per_seq * (2 * B);
+  const gu16* xb = ((const gu16*)(a.x));
   // tokens [lo, hi) of half tile hti are written (half-local indices; hi <= lo: none)
   auto half_range = [&](int64_t hti, int& lo, int& hi) {
     const int64_t tok0 = hti * HT;
@@ -354,9 +385,9 @@ __device__ __attribute__((noinline)) void encode_waves(const CodecArgs& a) {
     hi = e < 0 ? 0 : (e < HT ? static_cast<int>(e) : HT);
   };
   // 16-byte piece of bf16 row t (half-local, clamped into [lo, hi)) at column col
-  auto piece = [&](int64_t hti, int lo, int hi, int t, int col) -> uint4 {
+  auto piece = [&](int64_t hti, int lo, int hi, int t, int col) -> u32x4 {
     const int tc = t < lo ? lo : (t >= hi ? hi - 1 : t);
-    return *reinterpret_cast<const uint4*>(xb + xrow + (hti * HT + tc) * a.s_t + col);
+    return *reinterpret_cast<const gu4*>(xb + xrow + (hti * HT + tc) * a.s_t + col);
   };
 
   int64_t ht = a.tok_off / HT + static_cast<int64_t>(blockIdx.x) * WAVES + wave;
@@ -365,21 +396,21 @@ __device__ __attribute__((noinline)) void encode_waves(const CodecArgs& a) {
     // Slot k of the lane: channel (k & 7) | q4 << 3 | (k >> 3) << 5, read as 16-byte pieces
     // 4 j + q4 of the row (j = k >> 3), so the four lanes of a token read 64 contiguous bytes.
     const int tq = lane >> 2, q4 = lane & 3;
-    auto load_pass = [&](int64_t hti, int p, uint4 (&dst)[4]) {
+    auto load_pass = [&](int64_t hti, int p, u32x4 (&dst)[4]) {
       int lo, hi;
       half_range(hti, lo, hi);
       if (hi <= lo) return;
 #pragma unroll
       for (int j = 0; j < 4; ++j) dst[j] = piece(hti, lo, hi, 16 * p + tq, 8 * (4 * j + q4));
     };
-    uint4 pf[4];
+    u32x4 pf[4];
     if (bf16v && ht < ht_end) load_pass(ht, 0, pf);
     const double rs = c->R[0];
     for (; ht < ht_end; ht += hstep) {
       int lo, hi;
       half_range(ht, lo, hi);
       const int half = static_cast<int>(ht & 1);
-      uint32_t* out = seq_out + (ht >> 1) * (2 * B);
+      gu32* out = seq_out + (ht >> 1) * (2 * B);
       if (!isv)
         for (int u = lane; u < B; u += 64) wb[u] = 0u;
 #pragma unroll 1
@@ -402,7 +433,7 @@ __device__ __attribute__((noinline)) void encode_waves(const CodecArgs& a) {
         } else {
 #pragma unroll
           for (int k = 0; k < 32; ++k)
-            v[k] = in ? load_x(a.x, a.dtype, xrow + (ht * HT + t) * a.s_t + ((k & 7) | (q4 << 3) | ((k >> 3) << 5))) : 0.0;
+            v[k] = in ? gload_x(a.x, a.dtype, xrow + (ht * HT + t) * a.s_t + ((k & 7) | (q4 << 3) | ((k >> 3) << 5))) : 0.0;
         }
         // Sylvester order: y_i = sum_j (-1)^popcount(i & j) x_j, one butterfly per index bit; the
         // stages commute, and on bf16 rows every sum is exact in fp64.  Channel bits 0-2 and 5-6
@@ -458,47 +489,53 @@ __device__ __attribute__((noinline)) void encode_waves(const CodecArgs& a) {
       else write_v_words(cs, out, B, half, lo, lane, t_hf, t_fw, t_fs, t_fc);
     }
   } else {
-    // GEMM: rows through the wave's LDS area as fp32 (coalesced loads: 16-byte piece 64 j + lane
-    // is row (64 j + lane) >> 4, column 8 ((64 j + lane) & 15)).  Lane (tt, g) = (lane & 15,
-    // lane >> 4); accumulator block (tb, cb), register r: token 16 tb + tt, channel 16 cb + 4 g + r.
+    // GEMM.  The four waves run in step, one half tile each per round, and share E through LDS:
+    // per step pair sp the workgroup copies E[., 32 g + 2 sp .. + 1] of every row and g (8 KB)
+    // into one of two buffers, one barrier, and each wave runs its 32 MFMAs on it while the next
+    // chunk is loaded.  Lane (tt, g) = (lane & 15, lane >> 4) feeds rows 16 tb + tt of its half
+    // tile, channels 32 g + s; accumulator block (tb, cb), register r: token 16 tb + tt, channel
+    // 16 cb + 4 g + r.
     const int tt = lane & 15, g = lane >> 4;
-    auto load_half = [&](int64_t hti, uint4 (&dst)[8]) {
-      int lo, hi;
-      half_range(hti, lo, hi);
-      if (hi <= lo) return;
+    double2* ech = reinterpret_cast<double2*>(smem + kEch);    // [2][128 rows][4 g]
+    // chunk piece pc = 256 m + 64 wave + lane: row pc >> 2, g' = pc & 3, copied by global_load_lds
+    // (no registers) to ech[buffer][pc]
+    const gf64* esrc[2];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int pc = 64 * j + lane;
-        dst[j] = piece(hti, lo, hi, pc >> 4, 8 * (pc & 15));
-      }
+    for (int m = 0; m < 2; ++m) {
+      const int pc = THREADS * m + tid;
+      esrc[m] = ((const gf64*)(c->E)) + (pc >> 2) * D + 32 * (pc & 3);
+    }
+    auto copy_chunk = [&](int sp, int bi) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+        __builtin_amdgcn_global_load_lds((const void*)(esrc[m] + 2 * sp),
+                                         ech + bi * 512 + THREADS * m + 64 * wave, 16, 0, 0);
     };
-    uint4 pf[8];
-    if (bf16v && ht < ht_end) load_half(ht, pf);
     // v_mfma_f64_16x16x4f64 leaves D[i][j] in register i >> 2 of lane 16 (i & 3) + j, so the lane
     // that feeds row i of A feeds E row 16 cb + 4 (i & 3) + (i >> 2): the output of lane (tt, g),
     // register r is then channel 16 cb + 4 g + r, and a lane's four registers are adjacent channels
-    const double* erow = c->E + (4 * (tt & 3) + (tt >> 2)) * D + 32 * g;   // + 16 cb D + s
-    for (; ht < ht_end; ht += hstep) {
-      int lo, hi;
-      half_range(ht, lo, hi);
-      const int half = static_cast<int>(ht & 1);
-      uint32_t* out = seq_out + (ht >> 1) * (2 * B);
-      if (bf16v) {
+    const int arow = 4 * (tt & 3) + (tt >> 2);
+    copy_chunk(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const int64_t first = a.tok_off / HT + static_cast<int64_t>(blockIdx.x) * WAVES;
+    for (int64_t base = first; base < ht_end; base += hstep) {
+      const int64_t ht = base + wave;
+      const bool act = ht < ht_end;
+      int lo = 0, hi = 0;
+      if (act) half_range(ht, lo, hi);
+      // bf16 rows of the half tile into the wave's area, [32][XS] (coalesced: 16-byte piece
+      // 64 j + lane is row (64 j + lane) >> 4, column 8 ((64 j + lane) & 15))
+      if (act && bf16v && hi > lo) {
+        u32x4 pr[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int pc = 64 * j + lane;
-          float4* dst = reinterpret_cast<float4*>(xs + (pc >> 4) * XLD + 8 * (pc & 15));
-          const uint32_t w4[4] = {pf[j].x, pf[j].y, pf[j].z, pf[j].w};
-          dst[0] = make_float4(__uint_as_float(w4[0] << 16), __uint_as_float(w4[0] & 0xffff0000u),
-                               __uint_as_float(w4[1] << 16), __uint_as_float(w4[1] & 0xffff0000u));
-          dst[1] = make_float4(__uint_as_float(w4[2] << 16), __uint_as_float(w4[2] & 0xffff0000u),
-                               __uint_as_float(w4[3] << 16), __uint_as_float(w4[3] & 0xffff0000u));
+          pr[j] = piece(ht, lo, hi, pc >> 4, 8 * (pc & 15));
         }
-        if (ht + hstep < ht_end) load_half(ht + hstep, pf);      // in flight from here
-      } else {
-        for (int e = lane; e < HT * D; e += 64) {
-          const int t = e / D, i = e % D;
-          xs[t * XLD + i] = (t >= lo && t < hi) ? static_cast<float>(load_x(a.x, a.dtype, xrow + (ht * HT + t) * a.s_t + i)) : 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int pc = 64 * j + lane;
+          *reinterpret_cast<u32x4*>(xsb + (pc >> 4) * XS + 8 * (pc & 15)) = pr[j];
         }
       }
       f64x4 acc[2][8];
@@ -506,24 +543,51 @@ __device__ __attribute__((noinline)) void encode_waves(const CodecArgs& a) {
       for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
         for (int cb = 0; cb < 8; ++cb) acc[tb][cb] = f64x4{0.0, 0.0, 0.0, 0.0};
-#pragma unroll 1
-      for (int s = 0; s < 32; s += 2) {
-        double2 e2[8];
+      // one step pair: the barrier that publishes chunk sp (every wave waited for its own copies),
+      // the copies of the next chunk (or of the next round's first) into the other buffer, whose
+      // last readers passed this barrier, then 32 MFMAs
+      auto step_pair = [&](int sp, auto get_x) {
+        const double2* buf = ech + (sp & 1) * 512;
+        __syncthreads();
+        copy_chunk((sp + 1) & 15, (sp + 1) & 1);
+        if (act) {
+          const double* bd = reinterpret_cast<const double*>(buf);
 #pragma unroll
-        for (int cb = 0; cb < 8; ++cb) e2[cb] = *reinterpret_cast<const double2*>(erow + 16 * cb * D + s);
+          for (int u = 0; u < 2; ++u) {
+            double x0, x1;
+            get_x(2 * sp + u, x0, x1);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const double x0 = static_cast<double>(xs[tt * XLD + 32 * g + s + u]);
-          const double x1 = static_cast<double>(xs[(16 + tt) * XLD + 32 * g + s + u]);
-#pragma unroll
-          for (int cb = 0; cb < 8; ++cb) {
-            const double ev = u ? e2[cb].y : e2[cb].x;
-            acc[0][cb] = __builtin_amdgcn_mfma_f64_16x16x4f64(ev, x0, acc[0][cb], 0, 0, 0);
-            acc[1][cb] = __builtin_amdgcn_mfma_f64_16x16x4f64(ev, x1, acc[1][cb], 0, 0, 0);
+            for (int cb = 0; cb < 8; ++cb) {
+              const double ev = bd[2 * ((16 * cb + arow) * 4 + g) + u];
+              acc[0][cb] = __builtin_amdgcn_mfma_f64_16x16x4f64(ev, x0, acc[0][cb], 0, 0, 0);
+              acc[1][cb] = __builtin_amdgcn_mfma_f64_16x16x4f64(ev, x1, acc[1][cb], 0, 0, 0);
+            }
           }
         }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");       // this wave's copies have landed
+      };
+      if (bf16v) {
+#pragma unroll 1
+        for (int sp = 0; sp < 16; ++sp)
+          step_pair(sp, [&](int s, double& x0, double& x1) {
+            const uint32_t w0 = *reinterpret_cast<const uint32_t*>(xsb + tt * XS + 32 * g + (s & ~1));
+            const uint32_t w1 = *reinterpret_cast<const uint32_t*>(xsb + (16 + tt) * XS + 32 * g + (s & ~1));
+            x0 = (s & 1) ? bf16_hi(w0) : bf16_lo(w0);
+            x1 = (s & 1) ? bf16_hi(w1) : bf16_lo(w1);
+          });
+      } else {
+        const int64_t r0 = xrow + ht * HT * s_t;
+        const bool in0 = tt >= lo && tt < hi, in1 = 16 + tt >= lo && 16 + tt < hi;
+#pragma unroll 1
+        for (int sp = 0; sp < 16; ++sp)
+          step_pair(sp, [&](int s, double& x0, double& x1) {
+            x0 = in0 ? gload_x(xp, dtype, r0 + tt * s_t + 32 * g + s) : 0.0;
+            x1 = in1 ? gload_x(xp, dtype, r0 + (16 + tt) * s_t + 32 * g + s) : 0.0;
+          });
       }
-      // the rows are consumed: the area now takes the K words or V codes
+      if (!act) continue;
+      const int half = static_cast<int>(ht & 1);
+      gu32* out = seq_out + (ht >> 1) * (2 * B);
       if (!isv)
         for (int u = lane; u < B; u += 64) wb[u] = 0u;
 #pragma unroll
