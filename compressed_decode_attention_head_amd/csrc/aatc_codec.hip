@@ -219,8 +219,9 @@ __device__ inline int cvt_i32_trunc(double u) {
 // equals the floor on [0, 2^b - 1], and every value outside (NaN included) lands on the clamp's
 // side it belongs to, so the clamp runs on the truncated integer.
 // Lloyd-Max: the b-bit table's threshold count (quantize_lm).
-__device__ inline int code_of(double y, const double* q, int bi, bool lm, const double* thr) {
-  if (lm) return quantize_lm(y, q[0], q[1], bi, thr);
+template <bool LM>
+__device__ inline int code_of(double y, const double* q, int bi, const double* thr) {
+  if (LM) return quantize_lm(y, q[0], q[1], bi, thr);
   double u = (y - q[0]) * q[1];
   u = u + q[2];
   const int top = (1 << bi) - 1;
@@ -318,7 +319,7 @@ __device__ inline void write_v_words(const uint8_t* cs, gu32* out, int B, int ha
   }
 }
 
-template <bool WHT>
+template <bool WHT, bool LM>
 __device__ __attribute__((noinline)) void encode_waves(const CodecArgs& a) {
   extern __shared__ __align__(16) unsigned char smem[];
   double* qtab = reinterpret_cast<double*>(smem + kQ);
@@ -333,7 +334,7 @@ __device__ __attribute__((noinline)) void encode_waves(const CodecArgs& a) {
   const int h = blockIdx.y, b = blockIdx.z;
   const aatc_calib* c = a.calib + h;
   const int B = c->total_bits, nf = c->n_fields;
-  const bool lm = c->quantizer == AATC_QUANT_LLOYD_MAX;
+  constexpr bool lm = LM;
   const bool isv = a.which == 1;
 
   // ---- tables, once per workgroup
@@ -459,7 +460,7 @@ __device__ __attribute__((noinline)) void encode_waves(const CodecArgs& a) {
 #pragma unroll
         for (int k = 0; k < 32; ++k) {
           const int i = (k & 7) | (q4 << 3) | ((k >> 3) << 5);
-          cw[k >> 2] |= static_cast<uint32_t>(code_of(v[k] * rs, tq_row(qtab, i), t_bits[i], lm, t_th)) << (8 * (k & 3));
+          cw[k >> 2] |= static_cast<uint32_t>(code_of<LM>(v[k] * rs, tq_row(qtab, i), t_bits[i], t_th)) << (8 * (k & 3));
         }
         if (!in) {
 #pragma unroll
@@ -600,7 +601,7 @@ __device__ __attribute__((noinline)) void encode_waves(const CodecArgs& a) {
           uint32_t cd[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            cd[r] = in ? static_cast<uint32_t>(code_of(acc[tb][cb][r], tq_row(qtab, i0 + r), t_bits[i0 + r], lm, t_th)) : 0u;
+            cd[r] = in ? static_cast<uint32_t>(code_of<LM>(acc[tb][cb][r], tq_row(qtab, i0 + r), t_bits[i0 + r], t_th)) : 0u;
           if (!isv) {
             uint64_t run = 0;
             int nb = 0;
@@ -626,10 +627,18 @@ __device__ __attribute__((noinline)) void encode_waves(const CodecArgs& a) {
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 8))) void k_encode(CodecArgs a) {
   const aatc_calib* c = a.calib + blockIdx.y;
   if (c->magic != AATC_MAGIC) return;
-  if (c->rotation == AATC_ROT_WHT)
-    encode_waves<true>(a);
-  else
-    encode_waves<false>(a);
+  const bool lm = c->quantizer == AATC_QUANT_LLOYD_MAX;
+  if (c->rotation == AATC_ROT_WHT) {
+    if (lm)
+      encode_waves<true, true>(a);
+    else
+      encode_waves<true, false>(a);
+  } else {
+    if (lm)
+      encode_waves<false, true>(a);
+    else
+      encode_waves<false, false>(a);
+  }
 }
 
 // ---------------------------------------------------------------------------------------
