@@ -47,19 +47,23 @@ Plan make_plan(const aatc_cache* c, int n_q, int64_t max_seq) {
   Plan p;
   p.lm = c->quantizer != 0;
   if (p.lm) {
-    // the level pass: about two workgroups per CU, each a contiguous range of tiles
+    // the level pass: about one workgroup (eight waves) per CU, each a contiguous range of
+    // tiles of one sequence (tpw: tiles per workgroup)
     const int group = c->n_kv_heads > 0 ? n_q / c->n_kv_heads : 1;
     const int64_t ntiles = (max_seq + 63) / 64;
     const int64_t seqs = static_cast<int64_t>(c->batch) * c->n_kv_heads;
-    int64_t tpw = (ntiles * seqs + 511) / 512;
+    int64_t S = (256 + seqs - 1) / seqs;
+    if (S > ntiles) S = ntiles;
+    if (S < 1) S = 1;
+    int64_t tpw = (ntiles + S - 1) / S;
     if (tpw < 1) tpw = 1;
     p.tpw = static_cast<int>(tpw);
-    int64_t S = (ntiles + tpw - 1) / tpw;
+    S = (ntiles + tpw - 1) / tpw;
     p.S = static_cast<int>(S < 1 ? 1 : S);
     p.prec = aatc_lm::PHDR + AATC_D;
     p.NP = p.NVB = p.LIMBS = p.half = p.prod = 0;
     p.nslot = p.slot_bytes = p.ksz = p.gs = p.wave_bytes = 0;
-    p.lds = 0;
+    p.lds = aatc_lm::dyn_lds(c->k_bits, c->v_bits);
     p.fits = true;
     p.part_bytes = static_cast<size_t>(seqs) * p.S * group * p.prec * 4;
     p.offs_bytes = static_cast<size_t>(seqs) * 8 * 4;
@@ -209,7 +213,10 @@ aatc_status launch_level_pass(const aatc_cache* c, const Plan& p, const float* q
   a.kB = c->k_bits;
   a.vB = c->v_bits;
   a.quant = c->quantizer;
-  hipLaunchKernelGGL(aatc_lm::k_attn_lm, dim3(p.S, c->n_kv_heads, c->batch), dim3(aatc_lm::THREADS), 0, st, a,
+  const hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void*>(&aatc_lm::k_attn_lm),
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(p.lds));
+  if (ea != hipSuccess) return aatc::fail(AATC_ERR_HIP, "level pass LDS attribute: %s", hipGetErrorString(ea));
+  hipLaunchKernelGGL(aatc_lm::k_attn_lm, dim3(p.S, c->n_kv_heads, c->batch), dim3(aatc_lm::THREADS), p.lds, st, a,
                      static_cast<const aatc_calib*>(c->k_calib), static_cast<const aatc_calib*>(c->v_calib));
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return aatc::fail(AATC_ERR_HIP, "decode_attn level pass launch: %s", hipGetErrorString(err));
