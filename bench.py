@@ -46,6 +46,8 @@ def parse():
     p.add_argument("--no-loops", action="store_true", help="skip the append + decode loops")
     p.add_argument("--no-lloyd-max", action="store_true", help="skip the Lloyd-Max caches")
     p.add_argument("--only-headline", action="store_true", help="headline step and roofline only")
+    p.add_argument("--only", choices=["encode", "lloyd-max"], default=None,
+                   help="one side measurement alone (its JSON object only), for profiling")
     return p.parse_args()
 
 
@@ -687,6 +689,13 @@ def main():
         sys.exit(1)
     global USE_GRAPHS
     USE_GRAPHS = not args.no_graph
+    if args.only:
+        dev = torch.device("cuda", 0)
+        torch.cuda.set_device(dev)
+        st = torch.cuda.current_stream()
+        part = encode_rooflines(args, dev, st) if args.only == "encode" else lloyd_max_pass(args, dev, st)
+        print(json.dumps({"only": args.only, "result": part}))
+        return
     if args.only_headline:
         args.no_dense = args.no_tiers = args.no_cpu_baseline = args.no_encode = args.no_folded = args.no_loops = True
         args.no_lloyd_max = True
