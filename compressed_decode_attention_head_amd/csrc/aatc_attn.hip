@@ -20,6 +20,7 @@ namespace {
 using namespace aatc_attn;
 
 constexpr size_t kLdsLimit = 160 * 1024;
+constexpr size_t kLmStaticLds = 16 * 1024;  // k_attn_lm's static LDS (tables, q, merge headers), rounded up
 // __shared__ arrays of the kernel: the probability rows plus scalars (rounded up)
 constexpr size_t kStaticLds = static_cast<size_t>(CW) * TG * PROW_BYTES + 2048;
 
@@ -45,7 +46,8 @@ int round16(int64_t x) { return static_cast<int>((x + 15) / 16 * 16); }
 // each), as many as fit, at most its tile count.
 Plan make_plan(const aatc_cache* c, int n_q, int64_t max_seq) {
   Plan p;
-  p.lm = c->quantizer != 0;
+  // the level pass: a Lloyd-Max tensor, or more bits per vector than k_attn_main reads
+  p.lm = c->quantizer != 0 || c->k_bits > AATC_MAX_ATTN_BITS || c->v_bits > AATC_MAX_ATTN_BITS;
   if (p.lm) {
     // the level pass: about one workgroup (eight waves) per CU, each a contiguous range of
     // tiles of one sequence (tpw: tiles per workgroup)
@@ -63,8 +65,9 @@ Plan make_plan(const aatc_cache* c, int n_q, int64_t max_seq) {
     p.prec = aatc_lm::PHDR + AATC_D;
     p.NP = p.NVB = p.LIMBS = p.half = p.prod = 0;
     p.nslot = p.slot_bytes = p.ksz = p.gs = p.wave_bytes = 0;
-    p.lds = aatc_lm::dyn_lds(c->k_bits, c->v_bits);
-    p.fits = true;
+    p.nslot = aatc_lm::dyn_lds(c->k_bits, c->v_bits, 2) + kLmStaticLds <= kLdsLimit ? 2 : 1;
+    p.lds = aatc_lm::dyn_lds(c->k_bits, c->v_bits, p.nslot);
+    p.fits = p.lds + kLmStaticLds <= kLdsLimit;
     p.part_bytes = static_cast<size_t>(seqs) * p.S * group * p.prec * 4;
     p.offs_bytes = static_cast<size_t>(seqs) * 8 * 4;
     return p;
@@ -159,11 +162,11 @@ aatc_status check_cache_and_plan(const aatc_cache* c, int32_t n_q, int64_t max_s
   if (n_q % c->n_kv_heads) return aatc::fail(AATC_ERR_UNSUPPORTED, "n_q_heads %% n_kv_heads != 0");
   const int group = n_q / c->n_kv_heads;
   if (group > AATC_MAX_GROUP) return aatc::fail(AATC_ERR_UNSUPPORTED, "GQA group %d > 8", group);
-  if (c->k_bits < 0 || c->k_bits > AATC_MAX_ATTN_BITS || c->v_bits < 0 || c->v_bits > AATC_MAX_ATTN_BITS)
-    return aatc::fail(AATC_ERR_UNSUPPORTED, "k_bits %d / v_bits %d: decode attention handles 0..%d bits per vector",
-                      c->k_bits, c->v_bits, AATC_MAX_ATTN_BITS);
+  if (c->k_bits < 0 || c->k_bits > 8 * AATC_D || c->v_bits < 0 || c->v_bits > 8 * AATC_D)
+    return aatc::fail(AATC_ERR_BUDGET, "k_bits %d / v_bits %d outside 0..%d", c->k_bits, c->v_bits, 8 * AATC_D);
   if (c->quantizer < 0 || c->quantizer > 3) return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "quantizer %d", c->quantizer);
-  if (vtiles_bucket(c->v_tiles) < 0 || c->v_tiles < 0)
+  const bool summed = c->quantizer == 0 && c->k_bits <= AATC_MAX_ATTN_BITS && c->v_bits <= AATC_MAX_ATTN_BITS;
+  if (c->v_tiles < 0 || (summed && vtiles_bucket(c->v_tiles) < 0))
     return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "v_tiles %d", c->v_tiles);
   if (!c->k_calib || !c->v_calib || (!c->k_codes && c->k_bits > 0) || (!c->v_codes && c->v_bits > 0))
     return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "null cache pointer");
@@ -213,6 +216,7 @@ aatc_status launch_level_pass(const aatc_cache* c, const Plan& p, const float* q
   a.kB = c->k_bits;
   a.vB = c->v_bits;
   a.quant = c->quantizer;
+  a.nslot = p.nslot;
   const hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void*>(&aatc_lm::k_attn_lm),
                                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(p.lds));
   if (ea != hipSuccess) return aatc::fail(AATC_ERR_HIP, "level pass LDS attribute: %s", hipGetErrorString(ea));

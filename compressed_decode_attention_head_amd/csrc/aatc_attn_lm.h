@@ -15,7 +15,8 @@
 // 64-token tiles of one sequence; each wave takes every eighth tile and keeps its own online
 // softmax, with no barrier until the final merge.  Per tile a wave:
 //  1. copies the tile's K and V words into its own LDS slot with global_load_lds (no registers),
-//     one tile ahead;
+//     one tile ahead (two slots per wave; one slot, no overlap, when two would not fit LDS: more
+//     than about 1100 bits per K + V vector pair);
 //  2. scores on v_mfma_f32_16x16x32_bf16, as the dense kernel does: K levels as the A operand
 //     (row = token, 8 consecutive channels per lane, decoded from the token-major bit string: one
 //     64-bit window per 8 channels, then a mask and a table read per channel), the weights as B;
@@ -65,15 +66,16 @@ struct LmArgs {
   int S, tpw, prec;
   int kB, vB;
   int quant;                              // bit 0: K blobs Lloyd-Max, bit 1: V blobs
+  int nslot;                              // LDS slots per wave: 2 (the next tile in flight) or 1
 };
 
 // Bytes of a wave's slot for one tile: the K words, then the V words, each from the 16-byte unit
 // at or below its start, with 16 bytes of slack for the reads past the last word.
 __host__ __device__ inline int slot_region(int B) { return B > 0 ? ((8 * B + 8 + 16 + 15) / 16) * 16 : 0; }
 __host__ __device__ inline int slot_bytes(int kB, int vB) { return slot_region(kB) + slot_region(vB); }
-// dynamic LDS: two slots per wave (the merge reuses them: NW x MAXG x 128 floats)
-__host__ __device__ inline size_t dyn_lds(int kB, int vB) {
-  const size_t s = static_cast<size_t>(NW) * 2 * slot_bytes(kB, vB);
+// dynamic LDS: nslot slots per wave (the merge reuses them: NW x MAXG x 128 floats)
+__host__ __device__ inline size_t dyn_lds(int kB, int vB, int nslot) {
+  const size_t s = static_cast<size_t>(NW) * nslot * slot_bytes(kB, vB);
   const size_t m = static_cast<size_t>(NW) * MAXG * D * 4;
   return s > m ? s : m;
 }
@@ -121,12 +123,13 @@ __device__ inline float wave_sum(float x) {
   return x;
 }
 
-// s_waitcnt vmcnt(n) for a run-time n (0..63; larger waits for all)
+// s_waitcnt vmcnt(n) for a run-time n (0..23; larger waits for all)
 __device__ inline void wait_vm(int n) {
 #define AATC_LMW(k) case k: __builtin_amdgcn_s_waitcnt(((k) & 15) | (((k) >> 4) << 14) | (7 << 4) | (15 << 8)); break;
   switch (n) {
     AATC_LMW(0) AATC_LMW(1) AATC_LMW(2) AATC_LMW(3) AATC_LMW(4) AATC_LMW(5) AATC_LMW(6) AATC_LMW(7)
     AATC_LMW(8) AATC_LMW(9) AATC_LMW(10) AATC_LMW(11) AATC_LMW(12) AATC_LMW(13) AATC_LMW(14) AATC_LMW(15)
+    AATC_LMW(16) AATC_LMW(17) AATC_LMW(18) AATC_LMW(19) AATC_LMW(20) AATC_LMW(21) AATC_LMW(22) AATC_LMW(23)
     default: __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); break;
   }
 #undef AATC_LMW
@@ -179,7 +182,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 8)))
   const uint32_t* kseq = a.kcodes + static_cast<int64_t>(bh) * a.tiles_per_seq * kwords;
   const uint32_t* vseq = a.vcodes + static_cast<int64_t>(bh) * a.tiles_per_seq * vwords;
   const int sb = slot_bytes(Bk, Bv), kreg = slot_region(Bk);
-  unsigned char* slot0 = dyn + static_cast<size_t>(wave) * 2 * sb;
+  unsigned char* slot0 = dyn + static_cast<size_t>(wave) * a.nslot * sb;
   auto issue = [&](int tile, int si) -> int {
     unsigned char* sl = slot0 + si * sb;
     return copy_words(kseq + tile * kwords, static_cast<int>(kwords), sl, lane) +
@@ -200,14 +203,14 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 8)))
   }
   if (tid < D) {
     kbit[tid] = static_cast<uint8_t>(kc->bits[tid]);
-    // V fields: 16 bits each, word | log2(2 w) << 10 | shift << 12 (0: none)
+    // V fields: 16 bits each, word (< 2 x 1024) | log2(2 w) << 11 | shift << 13 (0: none)
     uint32_t f16[3] = {0u, 0u, 0u};
     for (int k = 0; k < 3; ++k) {
       const int f = vc->channel_field[3 * tid + k];
       if (f >= 0) {
         const int wd = vc->field_width[f];
         const uint32_t lw = wd == 4 ? 3u : (wd == 2 ? 2u : 1u);
-        f16[k] = static_cast<uint32_t>(vc->field_word[f]) | (lw << 10) | (static_cast<uint32_t>(vc->field_shift[f]) << 12);
+        f16[k] = static_cast<uint32_t>(vc->field_word[f]) | (lw << 11) | (static_cast<uint32_t>(vc->field_shift[f]) << 13);
       }
     }
     vdesc[tid] = make_uint2(f16[0] | (f16[1] << 16), f16[2] | (static_cast<uint32_t>(vc->bits[tid]) << 16));
@@ -287,9 +290,9 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 8)))
   float m_run = -INFINITY, l_run = 0.f;
 
   int si = 0;
-  for (; good && tile < t1; tile += NW, si ^= 1) {
+  for (; good && tile < t1; tile += NW) {
     const int nxt = tile + NW;
-    const int n_nxt = nxt < t1 ? issue(nxt, si ^ 1) : 0;
+    const int n_nxt = (a.nslot == 2 && nxt < t1) ? issue(nxt, si ^ 1) : 0;
     wait_vm(n_nxt);                                        // this tile's copies have landed
     const unsigned char* sl = slot0 + si * sb;
     const uint32_t* kw = reinterpret_cast<const uint32_t*>(sl + ((reinterpret_cast<uintptr_t>(kseq + tile * kwords)) & 15));
@@ -374,9 +377,9 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 8)))
 #pragma unroll
           for (int f = 0; f < 3; ++f) {
             const uint32_t fd = (f == 0 ? dsc.x : (f == 1 ? dsc.x >> 16 : dsc.y)) & 0xffffu;
-            const uint32_t lw = (fd >> 10) & 3u;
+            const uint32_t lw = (fd >> 11) & 3u;
             if (lw == 0) continue;
-            const int fw = static_cast<int>(fd & 1023u), sh = static_cast<int>(fd >> 12);
+            const int fw = static_cast<int>(fd & 2047u), sh = static_cast<int>(fd >> 13);
             const uint32_t wmask = lw == 3 ? 15u : (lw == 2 ? 3u : 1u);
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
@@ -409,6 +412,11 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 8)))
         }
       }
     }
+    // one slot: the next tile's copies go out once this tile's reads have been consumed
+    if (a.nslot == 2)
+      si ^= 1;
+    else if (nxt < t1)
+      issue(nxt, 0);
   }
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));        // vmcnt(0): no copy in flight into the slots
 

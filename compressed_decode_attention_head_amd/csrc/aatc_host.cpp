@@ -677,7 +677,7 @@ aatc_status aatc_joint_kv_split(const void* kblobs, const void* vblobs, int32_t 
       if (!std::isfinite(kw[i])) return fail(AATC_ERR_NUMERICAL, "k_weight[%lld] is not finite", (long long)i);
       if (kw[i] < 0.0) return fail(AATC_ERR_INVALID_ARGUMENT, "k_weight[%lld] < 0", (long long)i);
     }
-  // each tensor stays within what decode attention reads (AATC_MAX_ATTN_BITS per vector)
+  // each tensor stays on the summed-code cache pass of decode attention (AATC_MAX_ATTN_BITS per vector)
   const int cap_k = std::min(d * max_k, AATC_MAX_ATTN_BITS), cap_v = std::min(d * max_v, AATC_MAX_ATTN_BITS);
   if (total < 0 || total > cap_k + cap_v)
     return fail(AATC_ERR_BUDGET, "total_bits %d outside [0, %d] (each tensor at most %d bits per vector)", total,

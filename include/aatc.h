@@ -61,7 +61,8 @@ typedef enum { AATC_QUANT_UNIFORM = 0, AATC_QUANT_LLOYD_MAX = 1 } aatc_quantizer
 #define AATC_MAX_BITS 8
 #define AATC_MAX_FIELDS 384      /* 3 fields per channel at most (7 = 4+2+1) */
 #define AATC_MAX_GROUP 8         /* q heads per KV head handled by decode attention */
-#define AATC_MAX_ATTN_BITS 512   /* bits per K or V vector decode attention reads (4 per element) */
+#define AATC_MAX_ATTN_BITS 512   /* bits per K or V vector the summed-code cache pass reads (4 per
+                                    element); decode attention over more takes the level pass */
 #define AATC_MAGIC 0x43544141u   /* "AATC" */
 #define AATC_VERSION 3u
 #define AATC_LEVELS 510          /* level-table entries: 2^b for each b = 1..8, table b at 2^b - 2 */
@@ -279,7 +280,8 @@ aatc_status aatc_query_moment(const void* q_host, aatc_dtype dtype, int64_t n, i
  *   [n_heads][d] fp64 (aatc_query_channel_weights of each head; NULL for NOVA keys, whose
  *   coefficients already carry the query statistics).
  *   B_K and B_V are each limited to min(d max_bits, AATC_MAX_ATTN_BITS), so that the split
- *   never asks for a cache that aatc_decode_attn rejects.
+ *   keeps both tensors on decode attention's summed-code pass (past it a tensor takes the
+ *   slower level pass).
  *   Errors: a blob's aatc_calib_validate status; n_heads < 1, null pointers, a negative weight
  *   -> INVALID_ARGUMENT; a non-finite weight -> NUMERICAL; total_bits outside
  *   [0, min(d max_bits_K, AATC_MAX_ATTN_BITS) + min(d max_bits_V, AATC_MAX_ATTN_BITS)] -> BUDGET.
@@ -344,19 +346,22 @@ size_t aatc_decode_attn_workspace_bytes(const aatc_cache* cache, int32_t n_q_hea
  *   from the packed K bits weighted by q~ delta^K (the reconstruction offset cancels in the
  *   softmax); online softmax; softmax-weighted sums of the packed V codes; the affine V
  *   dequantization and R_V^T applied once to the sum.  When either tensor is Lloyd-Max
- *   (cache->quantizer != 0) the levels are not affine in the codes: the cache pass then decodes
- *   each tile's codes to levels through the blobs' level tables and sums probability-weighted V
- *   levels instead (a separate kernel, same arguments and results).  lse_dev (nullable): fp32
+ *   (cache->quantizer != 0) the levels are not affine in the codes, and when either tensor has
+ *   more than AATC_MAX_ATTN_BITS bits per vector the summed-code pass does not take it: the
+ *   cache pass then decodes each tile's codes to levels through the blobs' level tables (the
+ *   uniform quantizer's table is c - 2^(b-1) + 1/2) and sums probability-weighted V levels
+ *   instead (a separate kernel, same arguments and results).  lse_dev (nullable): fp32
  *   [batch][n_q_heads] natural-log sum of exp of the scores.  A sequence with 0 visible
  *   tokens yields out = 0, lse = -inf.
  *   workspace_dev: >= aatc_decode_attn_workspace_bytes(...) bytes of device memory, 256-byte
  *   aligned, for the per-split partial records of the two kernels the call launches on
  *   `stream`; its contents need no initialisation.  Calls that share a workspace must be
  *   ordered (same stream) or not overlap in time.
- *   Limits: k_bits and v_bits <= AATC_MAX_ATTN_BITS (512, 4 bits/element), q-head group <= 8,
- *   v_tiles <= 24.  (aatc_encode and aatc_decode take up to 8d bits.)
- *   Errors: group > 8 or not an integer, bits > AATC_MAX_ATTN_BITS -> UNSUPPORTED; bad pointers, seq length >
- *   capacity -> INVALID_ARGUMENT; workspace too small -> BUFFER_TOO_SMALL; launch -> HIP.
+ *   Limits: k_bits and v_bits <= 8d (1024), q-head group <= 8; the summed-code pass (uniform
+ *   blobs, both tensors <= AATC_MAX_ATTN_BITS) needs v_tiles <= 24.
+ *   Errors: group > 8 or not an integer -> UNSUPPORTED; bits outside 0..8d -> BUDGET; bad
+ *   pointers, v_tiles, seq length > capacity -> INVALID_ARGUMENT; workspace too small ->
+ *   BUFFER_TOO_SMALL; launch -> HIP.
  */
 aatc_status aatc_decode_attn(const aatc_cache* cache, const float* q_dev, int32_t n_q_heads,
                              const int32_t* seq_lens_dev, int64_t max_seq_len, float softmax_scale,

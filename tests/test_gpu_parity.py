@@ -242,8 +242,9 @@ def test_encode_unaligned_rows_and_wht_appends(dtype, cfg):
 def test_joint_kv_split_cache(cfg, bpe, aware):
     """A layer calibrated with the joint K/V split (library: query weights, split, calibration at
     B_K and B_V) at 2 x 256, 2 x 353 (attention-aware keys) and 2 x 512 bits: the split equals
-    the oracle's (both limited to the 512 bits decode attention reads, which binds at the last
-    two budgets), and the calibrate -> encode -> decode attention chain matches the oracle."""
+    the oracle's (both limited to the 512 bits the summed-code cache pass reads, which binds at
+    the last two budgets), and the calibrate -> encode -> decode attention chain matches the
+    oracle."""
     torch = _torch()
     from compressed_decode_attention_head_amd import api
     probe = Case(cfg=cfg, n_kv=2, group=4, n_tokens=64, rotation="klt", bpe_k=bpe, aware=aware)

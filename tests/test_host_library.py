@@ -176,7 +176,7 @@ def test_nova_errors(L):
                                                (2, "klt", 2.76, True), (3, "klt", 4.0, True)])
 def test_joint_kv_split_matches_oracle(cfg, rot, bpe, aware):
     """The layer's K/V split: library (C++) against the oracle on the same blobs' statistics,
-    both limited to the 512 bits per vector that decode attention reads."""
+    both limited to the 512 bits per vector that the summed-code cache pass reads."""
     n_kv = 3
     calk = [_cal(cfg, h, synth.K) for h in range(n_kv)]
     calv = [_cal(cfg, h, synth.V) for h in range(n_kv)]
@@ -200,7 +200,7 @@ def test_joint_kv_split_matches_oracle(cfg, rot, bpe, aware):
 
 def test_joint_kv_split_decode_cap_binds():
     """At 4 bits per element the unconstrained split gives V more than the 512 bits per vector
-    decode attention reads; the library's split is then the cap's corner (512, 512), which the
+    the summed-code cache pass reads; the library's split is then the cap's corner (512, 512), which the
     oracle's capped split also gives, and a budget past 2 x 512 is refused."""
     n_kv = 3
     calk = [_cal(3, h, synth.K) for h in range(n_kv)]
