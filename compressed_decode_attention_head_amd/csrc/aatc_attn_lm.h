@@ -379,31 +379,26 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 8)))
             const uint32_t fd = (f == 0 ? dsc.x : (f == 1 ? dsc.x >> 16 : dsc.y)) & 0xffffu;
             const uint32_t lw = (fd >> 11) & 3u;
             if (lw == 0) continue;
-            const int fw = static_cast<int>(fd & 2047u), sh = static_cast<int>(fd >> 13);
-            const uint32_t wmask = lw == 3 ? 15u : (lw == 2 ? 3u : 1u);
+            const int fw = static_cast<int>(fd & 2047u);
+            const uint32_t sh = fd >> 13, wbits = 1u << (lw - 1u);
+            const bool w4 = lw == 3u, w2 = lw == 2u;
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
+              // field group Gf = 2 blk + h2: w=4 word 2 Gf + qq/2, bits 4 (qq % 2) + 8 m; w=2 word
+              // Gf (rotated left by one when Gf is odd), bits 2 qq + 8 m; w=1 word Gf/2, bits
+              // 2 qq + Gf % 2 + 8 m (Gf % 2 = h2)
               const int Gf = 2 * blk + h2;
-              int wi, b0;
-              if (lw == 3) {
-                wi = fw + 2 * Gf + (qq >> 1);
-                b0 = 4 * (qq & 1);
-              } else if (lw == 2) {
-                wi = fw + Gf;
-                b0 = 2 * qq;
-              } else {
-                wi = fw + (Gf >> 1);
-                b0 = 2 * qq + (Gf & 1);
-              }
+              const int wi = fw + (w4 ? 2 * Gf + (qq >> 1) : (w2 ? Gf : blk));
+              const uint32_t b0 = w4 ? 4u * (qq & 1) : (w2 ? 2u * qq : 2u * qq + h2);
               uint32_t x = vw[wi];
-              if (lw == 2 && (Gf & 1)) x = __builtin_amdgcn_alignbit(x, x, 1u);   // undo the odd groups' rotation
+              if (h2 == 1 && w2) x = __builtin_amdgcn_alignbit(x, x, 1u);   // undo the odd groups' rotation
 #pragma unroll
-              for (int i = 0; i < 4; ++i) code[4 * h2 + i] |= ((x >> (8 * i + b0)) & wmask) << sh;
+              for (int i = 0; i < 4; ++i) code[4 * h2 + i] |= __builtin_amdgcn_ubfe(x, 8u * i + b0, wbits) << sh;
             }
           }
           uint32_t lvl[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) lvl[e] = lv[(code[e] & mask) + mask];
+          for (int e = 0; e < 8; ++e) lvl[e] = lv[code[e] + mask];   // code < 2^bits
           const uint4 vh = make_uint4(his(lvl[0], lvl[1]), his(lvl[2], lvl[3]), his(lvl[4], lvl[5]), his(lvl[6], lvl[7]));
           const uint4 vl = make_uint4(los(lvl[0], lvl[1]), los(lvl[2], lvl[3]), los(lvl[4], lvl[5]), los(lvl[6], lvl[7]));
           acc[j] = mfma(vh, ph, acc[j]);
