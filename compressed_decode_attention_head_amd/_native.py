@@ -103,15 +103,15 @@ def lib():
     L.aatc_decode_attn_workspace_bytes.restype = sz
     L.aatc_decode_attn_workspace_bytes.argtypes = [ctypes.POINTER(Cache), i32, i64]
     L.aatc_decode_attn.restype = ctypes.c_int
-    L.aatc_decode_attn.argtypes = [ctypes.POINTER(Cache), vp, i32, vp, i64, ctypes.c_float, vp, vp, vp, sz, vp]
+    L.aatc_decode_attn.argtypes = [ctypes.POINTER(Cache), vp, i32, i32, vp, i64, ctypes.c_float, vp, vp, vp, sz, vp]
     L.aatc_decode_attn_partial.restype = ctypes.c_int
     L.aatc_probe_read_sink_bytes.restype = sz
     L.aatc_probe_read_sink_bytes.argtypes = []
     L.aatc_probe_read.restype = ctypes.c_int
     L.aatc_probe_read.argtypes = [vp, sz, vp, vp]
     L.aatc_decode_attn_noalloc.restype = ctypes.c_int
-    L.aatc_decode_attn_noalloc.argtypes = [ctypes.POINTER(Cache), vp, i32, vp, i64, ctypes.c_float, vp, vp, vp]
-    L.aatc_decode_attn_partial.argtypes = [ctypes.POINTER(Cache), vp, i32, vp, i64, ctypes.c_float, vp, sz, vp]
+    L.aatc_decode_attn_noalloc.argtypes = [ctypes.POINTER(Cache), vp, i32, i32, vp, i64, ctypes.c_float, vp, vp, vp]
+    L.aatc_decode_attn_partial.argtypes = [ctypes.POINTER(Cache), vp, i32, i32, vp, i64, ctypes.c_float, vp, sz, vp]
     L.aatc_decode_attn_merge.restype = ctypes.c_int
     L.aatc_decode_attn_merge.argtypes = [ctypes.POINTER(Cache), i32, vp, i64, vp, vp, vp, sz, vp]
     L.aatc_tier_distortions.restype = ctypes.c_int

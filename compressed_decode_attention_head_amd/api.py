@@ -354,17 +354,24 @@ class CompressedKVCache:
         import torch
         return torch.empty(self.workspace_bytes(n_q_heads, max_seq_len), dtype=torch.uint8, device=self.device)
 
+    def _q_dtype(self, q):
+        import torch
+        if q.dtype not in (torch.float32, torch.bfloat16) or not q.is_contiguous() or q.dim() != 3 \
+                or q.shape[0] != self.batch:
+            raise ValueError("q must be a contiguous fp32 or bf16 [batch, n_q_heads, 128] tensor")
+        return N.DTYPE["f32"] if q.dtype == torch.float32 else N.DTYPE["bf16"]
+
     def decode_attn(self, q, max_seq_len, seq_lens=None, scale=0.0, workspace=None, out=None, lse=None,
                     stream=None):
-        """aatc_decode_attn: q [batch, n_q_heads, 128] fp32 -> (out [batch, n_q_heads, 128], lse [batch, n_q])."""
+        """aatc_decode_attn: q [batch, n_q_heads, 128] fp32 or bf16 -> (out [batch, n_q_heads, 128] fp32,
+        lse [batch, n_q])."""
         import torch
-        if q.dtype != torch.float32 or not q.is_contiguous() or q.dim() != 3 or q.shape[0] != self.batch:
-            raise ValueError("q must be a contiguous fp32 [batch, n_q_heads, 128] tensor")
+        qdt = self._q_dtype(q)
         n_q = q.shape[1]
         if workspace is None:
             workspace = self.new_workspace(n_q, max_seq_len)
         if out is None:
-            out = torch.empty_like(q)
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
         if lse is None:
             lse = torch.empty((self.batch, n_q), dtype=torch.float32, device=self.device)
         sl = 0
@@ -372,7 +379,7 @@ class CompressedKVCache:
             if seq_lens.dtype != torch.int32 or seq_lens.device != self.device or seq_lens.numel() != self.batch:
                 raise ValueError("seq_lens must be an int32 [batch] tensor on the cache's device")
             sl = seq_lens.data_ptr()
-        N.check(N.lib().aatc_decode_attn(ctypes.byref(self._struct), q.data_ptr(), int(n_q), sl or None,
+        N.check(N.lib().aatc_decode_attn(ctypes.byref(self._struct), q.data_ptr(), qdt, int(n_q), sl or None,
                                          int(max_seq_len), float(scale), out.data_ptr(), lse.data_ptr(),
                                          workspace.data_ptr(), workspace.numel(), _stream_ptr(stream)))
         return out, lse
@@ -381,13 +388,12 @@ class CompressedKVCache:
         """aatc_decode_attn_noalloc: aatc_decode_attn with the library's static per-GPU workspace;
         out (and lse, if given) are the caller's [batch, n_q_heads, 128] / [batch, n_q] fp32 tensors."""
         import torch
-        if q.dtype != torch.float32 or not q.is_contiguous() or q.dim() != 3 or q.shape[0] != self.batch:
-            raise ValueError("q must be a contiguous fp32 [batch, n_q_heads, 128] tensor")
+        qdt = self._q_dtype(q)
         if out.shape != q.shape or out.dtype != torch.float32 or not out.is_contiguous():
             raise ValueError("out must be a contiguous fp32 tensor shaped like q")
         if lse is not None and (lse.shape != q.shape[:2] or lse.dtype != torch.float32 or not lse.is_contiguous()):
             raise ValueError("lse must be a contiguous fp32 [batch, n_q_heads] tensor")
-        N.check(N.lib().aatc_decode_attn_noalloc(ctypes.byref(self._struct), q.data_ptr(), int(q.shape[1]),
+        N.check(N.lib().aatc_decode_attn_noalloc(ctypes.byref(self._struct), q.data_ptr(), qdt, int(q.shape[1]),
                                                  self._seq_ptr(seq_lens), int(max_seq_len), float(scale),
                                                  out.data_ptr(), None if lse is None else lse.data_ptr(),
                                                  _stream_ptr(stream)))
@@ -403,10 +409,8 @@ class CompressedKVCache:
 
     def decode_attn_partial(self, q, max_seq_len, workspace, seq_lens=None, scale=0.0, stream=None):
         """aatc_decode_attn_partial: the cache pass; partial records go to `workspace`."""
-        import torch
-        if q.dtype != torch.float32 or not q.is_contiguous() or q.dim() != 3 or q.shape[0] != self.batch:
-            raise ValueError("q must be a contiguous fp32 [batch, n_q_heads, 128] tensor")
-        N.check(N.lib().aatc_decode_attn_partial(ctypes.byref(self._struct), q.data_ptr(), int(q.shape[1]),
+        qdt = self._q_dtype(q)
+        N.check(N.lib().aatc_decode_attn_partial(ctypes.byref(self._struct), q.data_ptr(), qdt, int(q.shape[1]),
                                                  self._seq_ptr(seq_lens), int(max_seq_len), float(scale),
                                                  workspace.data_ptr(), workspace.numel(), _stream_ptr(stream)))
 

@@ -37,6 +37,7 @@ struct Plan {
   int nslot, slot_bytes, ksz, gs, wave_bytes;
   size_t lds;
   size_t part_bytes, offs_bytes;
+  size_t q_bytes;                        // fp32 copy of a bf16 q (batch x n_q x 128 floats)
   bool fits;
 };
 
@@ -46,6 +47,7 @@ int round16(int64_t x) { return static_cast<int>((x + 15) / 16 * 16); }
 // each), as many as fit, at most its tile count.
 Plan make_plan(const aatc_cache* c, int n_q, int64_t max_seq) {
   Plan p;
+  p.q_bytes = 0;
   // the level pass: a Lloyd-Max tensor, or more bits per vector than k_attn_main reads
   p.lm = c->quantizer != 0 || c->k_bits > AATC_MAX_ATTN_BITS || c->v_bits > AATC_MAX_ATTN_BITS;
   if (p.lm) {
@@ -147,7 +149,9 @@ extern "C" {
 size_t aatc_decode_attn_workspace_bytes(const aatc_cache* c, int32_t n_q_heads, int64_t max_seq_len) {
   if (!c || max_seq_len < 0 || n_q_heads < 1) return 0;
   const Plan p = make_plan(c, n_q_heads, max_seq_len);
-  return align256(p.part_bytes) + align256(p.offs_bytes);
+  // partial records, lse offsets, and room for an fp32 copy of a bf16 q
+  return align256(p.part_bytes) + align256(p.offs_bytes) +
+         align256(static_cast<size_t>(c->batch > 0 ? c->batch : 0) * n_q_heads * AATC_D * 4);
 }
 
 }  // extern "C"
@@ -175,11 +179,35 @@ aatc_status check_cache_and_plan(const aatc_cache* c, int32_t n_q, int64_t max_s
   if (max_seq < 0 || max_seq > c->capacity_tokens)
     return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "max_seq_len %lld > capacity", (long long)max_seq);
   *p = make_plan(c, n_q, max_seq);
+  p->q_bytes = static_cast<size_t>(c->batch) * n_q * AATC_D * 4;
   if (!p->fits) return aatc::fail(AATC_ERR_UNSUPPORTED, "tiles of %d+%d bits do not fit LDS", c->k_bits, c->v_bits);
   return AATC_OK;
 }
 
-size_t plan_workspace(const Plan& p) { return align256(p.part_bytes) + align256(p.offs_bytes); }
+size_t plan_workspace(const Plan& p) { return align256(p.part_bytes) + align256(p.offs_bytes) + align256(p.q_bytes); }
+
+// q as the kernels take it (fp32): the caller's buffer, or for bf16 an fp32 copy in the
+// workspace's last area (one small conversion kernel on the stream).
+__global__ void k_q_bf16_to_f32(const uint16_t* __restrict__ in, float* __restrict__ out, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = __uint_as_float(static_cast<uint32_t>(in[i]) << 16);
+}
+
+aatc_status prepare_q(const void* q, aatc_dtype qdt, const Plan& p, void* ws, hipStream_t st, const float** q32) {
+  if (qdt == AATC_F32) {
+    *q32 = static_cast<const float*>(q);
+    return AATC_OK;
+  }
+  if (qdt != AATC_BF16) return aatc::fail(AATC_ERR_UNSUPPORTED, "q dtype %d (fp32 or bf16)", static_cast<int>(qdt));
+  float* dst = reinterpret_cast<float*>(static_cast<char*>(ws) + align256(p.part_bytes) + align256(p.offs_bytes));
+  const int64_t n = static_cast<int64_t>(p.q_bytes / 4);
+  hipLaunchKernelGGL(k_q_bf16_to_f32, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(q), dst, n);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return aatc::fail(AATC_ERR_HIP, "q conversion launch: %s", hipGetErrorString(e));
+  *q32 = dst;
+  return AATC_OK;
+}
 
 aatc_status check_and_plan(const aatc_cache* c, int32_t n_q, int64_t max_seq, void* ws, size_t ws_bytes, Plan* p) {
   if (!ws) return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "null pointer");
@@ -295,16 +323,21 @@ aatc_status launch_merge(const aatc_cache* c, const Plan& p, int32_t n_q, const 
 
 extern "C" {
 
-aatc_status aatc_decode_attn(const aatc_cache* c, const float* q, int32_t n_q, const int32_t* seq_lens,
-                             int64_t max_seq, float scale, float* out, float* lse, void* ws, size_t ws_bytes,
-                             void* stream) {
+aatc_status aatc_decode_attn(const aatc_cache* c, const void* q, aatc_dtype q_dtype, int32_t n_q,
+                             const int32_t* seq_lens, int64_t max_seq, float scale, float* out, float* lse, void* ws,
+                             size_t ws_bytes, void* stream) {
   aatc::clear_error();
   if (!q || !out) return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "null pointer");
+  if (q_dtype != AATC_F32 && q_dtype != AATC_BF16)
+    return aatc::fail(AATC_ERR_UNSUPPORTED, "q dtype %d (fp32 or bf16)", static_cast<int>(q_dtype));
   Plan p;
   aatc_status r = check_and_plan(c, n_q, max_seq, ws, ws_bytes, &p);
   if (r != AATC_OK) return r;
   auto st = static_cast<hipStream_t>(stream);
-  r = launch_partial(c, p, q, n_q, seq_lens, 0, max_seq, scale, ws, st);
+  const float* q32 = nullptr;
+  r = prepare_q(q, q_dtype, p, ws, st, &q32);
+  if (r != AATC_OK) return r;
+  r = launch_partial(c, p, q32, n_q, seq_lens, 0, max_seq, scale, ws, st);
   if (r != AATC_OK) return r;
   return launch_merge(c, p, n_q, seq_lens, 0, max_seq, out, lse, ws, st);
 }
@@ -339,10 +372,13 @@ aatc_status scratch_address(void** out) {
 
 extern "C" {
 
-aatc_status aatc_decode_attn_noalloc(const aatc_cache* c, const float* q, int32_t n_q, const int32_t* seq_lens,
-                                     int64_t max_seq, float scale, float* out, float* lse, void* stream) {
+aatc_status aatc_decode_attn_noalloc(const aatc_cache* c, const void* q, aatc_dtype q_dtype, int32_t n_q,
+                                     const int32_t* seq_lens, int64_t max_seq, float scale, float* out, float* lse,
+                                     void* stream) {
   aatc::clear_error();
   if (!q || !out) return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "null pointer");
+  if (q_dtype != AATC_F32 && q_dtype != AATC_BF16)
+    return aatc::fail(AATC_ERR_UNSUPPORTED, "q dtype %d (fp32 or bf16)", static_cast<int>(q_dtype));
   // every argument is checked before the scratch address is looked up
   Plan p;
   aatc_status r = check_cache_and_plan(c, n_q, max_seq, &p);
@@ -357,19 +393,29 @@ aatc_status aatc_decode_attn_noalloc(const aatc_cache* c, const float* q, int32_
   r = scratch_address(&ws);
   if (r != AATC_OK) return r;
   auto st = static_cast<hipStream_t>(stream);
-  r = launch_partial(c, p, q, n_q, seq_lens, 0, max_seq, scale, ws, st);
+  const float* q32 = nullptr;
+  r = prepare_q(q, q_dtype, p, ws, st, &q32);
+  if (r != AATC_OK) return r;
+  r = launch_partial(c, p, q32, n_q, seq_lens, 0, max_seq, scale, ws, st);
   if (r != AATC_OK) return r;
   return launch_merge(c, p, n_q, seq_lens, 0, max_seq, out, lse, ws, st);
 }
 
-aatc_status aatc_decode_attn_partial(const aatc_cache* c, const float* q, int32_t n_q, const int32_t* seq_lens,
-                                     int64_t max_seq, float scale, void* ws, size_t ws_bytes, void* stream) {
+aatc_status aatc_decode_attn_partial(const aatc_cache* c, const void* q, aatc_dtype q_dtype, int32_t n_q,
+                                     const int32_t* seq_lens, int64_t max_seq, float scale, void* ws, size_t ws_bytes,
+                                     void* stream) {
   aatc::clear_error();
   if (!q) return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "null pointer");
+  if (q_dtype != AATC_F32 && q_dtype != AATC_BF16)
+    return aatc::fail(AATC_ERR_UNSUPPORTED, "q dtype %d (fp32 or bf16)", static_cast<int>(q_dtype));
   Plan p;
-  const aatc_status r = check_and_plan(c, n_q, max_seq, ws, ws_bytes, &p);
+  aatc_status r = check_and_plan(c, n_q, max_seq, ws, ws_bytes, &p);
   if (r != AATC_OK) return r;
-  return launch_partial(c, p, q, n_q, seq_lens, 0, max_seq, scale, ws, static_cast<hipStream_t>(stream));
+  auto st = static_cast<hipStream_t>(stream);
+  const float* q32 = nullptr;
+  r = prepare_q(q, q_dtype, p, ws, st, &q32);
+  if (r != AATC_OK) return r;
+  return launch_partial(c, p, q32, n_q, seq_lens, 0, max_seq, scale, ws, st);
 }
 
 aatc_status aatc_decode_attn_merge(const aatc_cache* c, int32_t n_q, const int32_t* seq_lens, int64_t max_seq,

@@ -337,7 +337,9 @@ size_t aatc_decode_attn_workspace_bytes(const aatc_cache* cache, int32_t n_q_hea
  * aatc_decode_attn -- device, async; one decode step over the compressed cache.
  * [SPECTRA Abstract and RDKV abstract: every decode step reads the whole cache again;
  *  NOVA-KV abstract: decode is bandwidth-bound]
- *   q_dev: fp32 [batch][n_q_heads][128]; q head g reads KV head g / (n_q_heads/n_kv_heads)
+ *   q_dev: [batch][n_q_heads][128] of q_dtype AATC_F32 or AATC_BF16 (a bf16 q is first widened
+ *   to an fp32 copy in the workspace by one small kernel; other dtypes -> UNSUPPORTED); q head g
+ *   reads KV head g / (n_q_heads/n_kv_heads)
  *   (contiguous groups, 1..8 q heads per KV head).  seq_lens_dev: int32 [batch] tokens
  *   visible per sequence (each <= max_seq_len <= capacity), or NULL for max_seq_len.
  *   softmax_scale <= 0 selects 1/sqrt(128).
@@ -354,8 +356,8 @@ size_t aatc_decode_attn_workspace_bytes(const aatc_cache* cache, int32_t n_q_hea
  *   [batch][n_q_heads] natural-log sum of exp of the scores.  A sequence with 0 visible
  *   tokens yields out = 0, lse = -inf.
  *   workspace_dev: >= aatc_decode_attn_workspace_bytes(...) bytes of device memory, 256-byte
- *   aligned, for the per-split partial records of the two kernels the call launches on
- *   `stream`; its contents need no initialisation.  Calls that share a workspace must be
+ *   aligned, for the per-split partial records of the kernels the call launches on `stream`
+ *   (and a bf16 q's fp32 copy); its contents need no initialisation.  Calls that share a workspace must be
  *   ordered (same stream) or not overlap in time.
  *   Limits: k_bits and v_bits <= 8d (1024), q-head group <= 8; the summed-code pass (uniform
  *   blobs, both tensors <= AATC_MAX_ATTN_BITS) needs v_tiles <= 24.
@@ -363,7 +365,7 @@ size_t aatc_decode_attn_workspace_bytes(const aatc_cache* cache, int32_t n_q_hea
  *   pointers, v_tiles, seq length > capacity -> INVALID_ARGUMENT; workspace too small ->
  *   BUFFER_TOO_SMALL; launch -> HIP.
  */
-aatc_status aatc_decode_attn(const aatc_cache* cache, const float* q_dev, int32_t n_q_heads,
+aatc_status aatc_decode_attn(const aatc_cache* cache, const void* q_dev, aatc_dtype q_dtype, int32_t n_q_heads,
                              const int32_t* seq_lens_dev, int64_t max_seq_len, float softmax_scale,
                              float* out_dev, float* lse_dev, void* workspace_dev,
                              size_t workspace_bytes, void* stream);
@@ -383,9 +385,9 @@ aatc_status aatc_decode_attn(const aatc_cache* cache, const float* q_dev, int32_
  *   the last call's records; nothing in it needs clearing between calls.
  */
 #define AATC_NOALLOC_SCRATCH_BYTES (8u << 20)
-aatc_status aatc_decode_attn_noalloc(const aatc_cache* cache, const float* q_dev, int32_t n_q_heads,
-                                     const int32_t* seq_lens_dev, int64_t max_seq_len, float softmax_scale,
-                                     float* out_dev, float* lse_dev, void* stream);
+aatc_status aatc_decode_attn_noalloc(const aatc_cache* cache, const void* q_dev, aatc_dtype q_dtype,
+                                     int32_t n_q_heads, const int32_t* seq_lens_dev, int64_t max_seq_len,
+                                     float softmax_scale, float* out_dev, float* lse_dev, void* stream);
 
 /*
  * aatc_decode_attn_partial and aatc_decode_attn_merge -- the two halves of aatc_decode_attn,
@@ -401,8 +403,8 @@ aatc_status aatc_decode_attn_noalloc(const aatc_cache* cache, const float* q_dev
  *   and writes out_dev / lse_dev exactly as aatc_decode_attn does.
  *   Arguments, ownership and errors as for aatc_decode_attn; each call validates them itself.
  */
-aatc_status aatc_decode_attn_partial(const aatc_cache* cache, const float* q_dev, int32_t n_q_heads,
-                                     const int32_t* seq_lens_dev, int64_t max_seq_len,
+aatc_status aatc_decode_attn_partial(const aatc_cache* cache, const void* q_dev, aatc_dtype q_dtype,
+                                     int32_t n_q_heads, const int32_t* seq_lens_dev, int64_t max_seq_len,
                                      float softmax_scale, void* workspace_dev, size_t workspace_bytes,
                                      void* stream);
 aatc_status aatc_decode_attn_merge(const aatc_cache* cache, int32_t n_q_heads,

@@ -487,3 +487,33 @@ def test_segments_raw_tier_appends_64_steps():
                 err, lerr = max(err, float(np.abs(o[g] - ref).max())), max(lerr, abs(float(l[g]) - lref))
             print("raw-tier append step %d: max abs err %.2e, lse err %.2e" % (s_ + 1, err, lerr), flush=True)
             assert err <= ATOL_ATTN and lerr <= 5e-3
+
+
+@pytest.mark.parametrize("quant", ["uniform", "lloyd-max"])
+def test_bf16_queries(quant):
+    """q in bf16 (the call widens it to fp32 in its workspace) gives the same outputs, bit for bit,
+    as the fp32 widening of the same values, through aatc_decode_attn, the no-alloc entry point and
+    partial + merge, on the summed-code pass and on the level pass; and it matches the oracle on
+    the bf16 values."""
+    torch = _torch()
+    case = Case(cfg=4, n_kv=2, group=7, n_tokens=900, rotation="wht", bpe_k=1.33, marginal="t3",
+                quant_k=quant, quant_v=quant)
+    cache = case.make_cache()
+    for t in (synth.K, synth.V):
+        cache.encode(t, case.torch_x(t))
+    qb = torch.from_numpy(case.q.astype(np.float32)).cuda().to(torch.bfloat16)
+    qf = qb.float()
+    o1, l1 = cache.decode_attn(qb, case.n)
+    o2, l2 = cache.decode_attn(qf, case.n)
+    o3 = torch.empty_like(o2)
+    l3 = torch.empty_like(l2)
+    cache.decode_attn_noalloc(qb, case.n, o3, l3)
+    ws = cache.new_workspace(case.n_q, case.n)
+    cache.decode_attn_partial(qb, case.n, ws)
+    o4, l4 = cache.decode_attn_merge(case.n_q, case.n, ws, torch.empty_like(o2), torch.empty_like(l2))
+    torch.cuda.synchronize()
+    for o, l in ((o1, l1), (o3, l3), (o4, l4)):
+        assert torch.equal(o, o2) and torch.equal(l, l2)
+    ref, lref = case.oracle_attention(q=qf.cpu().numpy().astype(np.float64))
+    assert np.abs(o1.cpu().numpy() - ref).max() <= ATOL_ATTN
+    assert np.abs(l1.cpu().numpy() - lref).max() <= 5e-3

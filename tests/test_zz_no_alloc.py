@@ -23,7 +23,7 @@ def test_noalloc_refuses_oversized_steps():
                 k_calib=256, v_calib=512, k_codes=1024, v_codes=2048)
     need = L.aatc_decode_attn_workspace_bytes(ctypes.byref(c), 32, 131072)
     assert need > (8 << 20)
-    st = L.aatc_decode_attn_noalloc(ctypes.byref(c), 4096, 32, None, 131072, 0.0, 8192, None, None)
+    st = L.aatc_decode_attn_noalloc(ctypes.byref(c), 4096, 0, 32, None, 131072, 0.0, 8192, None, None)
     assert N.STATUS[st] == "AATC_ERR_BUFFER_TOO_SMALL"
     assert b"static workspace" in L.aatc_last_error()
 
