@@ -149,7 +149,7 @@ struct CodecArgs {
 // ---------------------------------------------------------------------------------------
 constexpr int HT = 32;                                      // tokens of a half tile
 constexpr int WAVES = THREADS / 64;
-constexpr size_t kQ = 0;                                    // fp64 {o, 1/scale, 2^(b-1), 2^b - 1} per channel
+constexpr size_t kQ = 0;                                    // fp64 {o, 1/scale}, then 2^(b-1), per channel (padded rows)
 constexpr size_t kTBits = kQ + 32 * D;                      // u8 bits[128]
 constexpr size_t kTPb = kTBits + D;                         // u16 first plane of each channel
 constexpr size_t kTFw = kTPb + 2 * D;                       // u16 first word of each field
@@ -214,16 +214,25 @@ __device__ inline int cvt_i32_trunc(double u) {
   return r;
 }
 
-// Code of value y of a channel whose table row is q = {o, 1/scale, 2^(b-1), 2^b - 1}.  Uniform:
+// Quantizer table of a channel: {o, 1/scale} and 2^(b-1), at a padded position: the four lanes
+// of a token in the Walsh-Hadamard form read channels 8 apart, which the padding puts in
+// disjoint LDS banks (each 32 channels take 40 rows, each 8 of them 10).
+constexpr int kQRows = 40 * (D / 32);
+static_assert(24 * kQRows <= 32 * D, "padded quantizer table fits its LDS area");
+__device__ inline int qpos(int i) { return 40 * (i >> 5) + 10 * ((i >> 3) & 3) + (i & 7); }
+
+// Code of value y of a channel with table entries o, inv = 1/scale, half = 2^(b-1).  Uniform:
 // clamp(floor((y - o) * (1/Delta) + 2^(b-1)), 0, 2^b - 1) with NaN -> 0.  Truncation toward zero
 // equals the floor on [0, 2^b - 1], and every value outside (NaN included) lands on the clamp's
 // side it belongs to, so the clamp runs on the truncated integer.
 // Lloyd-Max: the b-bit table's threshold count (quantize_lm).
 template <bool LM>
-__device__ inline int code_of(double y, const double* q, int bi, const double* thr) {
-  if (LM) return quantize_lm(y, q[0], q[1], bi, thr);
-  double u = (y - q[0]) * q[1];
-  u = u + q[2];
+__device__ inline int code_of(double y, const double2* qoi, const double* qh, int i, int bi, const double* thr) {
+  const int p = qpos(i);
+  const double2 oi = qoi[p];
+  if (LM) return quantize_lm(y, oi.x, oi.y, bi, thr);
+  double u = (y - oi.x) * oi.y;
+  u = u + qh[p];
   const int top = (1 << bi) - 1;
   const int ci = cvt_i32_trunc(u);
   return ci < 0 ? 0 : (ci > top ? top : ci);
@@ -241,7 +250,6 @@ __device__ inline void or_run(uint32_t* S, int pos, uint64_t v) {
   if (top) lds_or(S + w + 2, top);
 }
 
-__device__ inline const double* tq_row(const double* qtab, int i) { return qtab + 4 * i; }
 
 // Element i of the encoder's input (fp32 or bf16) through a global-memory pointer, so that the
 // load is not a flat access (which the LDS waits would also count).
@@ -322,7 +330,8 @@ __device__ inline void write_v_words(const uint8_t* cs, gu32* out, int B, int ha
 template <bool WHT, bool LM>
 __device__ __attribute__((noinline)) void encode_waves(const CodecArgs& a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  double* qtab = reinterpret_cast<double*>(smem + kQ);
+  double2* qoi = reinterpret_cast<double2*>(smem + kQ);
+  double* qh = reinterpret_cast<double*>(smem + kQ + 16 * kQRows);
   uint8_t* t_bits = smem + kTBits;
   uint16_t* t_pb = reinterpret_cast<uint16_t*>(smem + kTPb);
   uint16_t* t_fw = reinterpret_cast<uint16_t*>(smem + kTFw);
@@ -340,11 +349,8 @@ __device__ __attribute__((noinline)) void encode_waves(const CodecArgs& a) {
   // ---- tables, once per workgroup
   if (tid < D) {
     const int bi = c->bits[tid];
-    double* q = qtab + 4 * tid;
-    q[0] = c->o[tid];
-    q[1] = lm ? c->inv_scale[tid] : c->inv_delta[tid];
-    q[2] = static_cast<double>(bi ? 1 << (bi - 1) : 0);
-    q[3] = static_cast<double>((1 << bi) - 1);
+    qoi[qpos(tid)] = make_double2(c->o[tid], lm ? c->inv_scale[tid] : c->inv_delta[tid]);
+    qh[qpos(tid)] = static_cast<double>(bi ? 1 << (bi - 1) : 0);
     t_bits[tid] = static_cast<uint8_t>(bi);
   }
   if (lm)
@@ -460,7 +466,7 @@ __device__ __attribute__((noinline)) void encode_waves(const CodecArgs& a) {
 #pragma unroll
         for (int k = 0; k < 32; ++k) {
           const int i = (k & 7) | (q4 << 3) | ((k >> 3) << 5);
-          cw[k >> 2] |= static_cast<uint32_t>(code_of<LM>(v[k] * rs, tq_row(qtab, i), t_bits[i], t_th)) << (8 * (k & 3));
+          cw[k >> 2] |= static_cast<uint32_t>(code_of<LM>(v[k] * rs, qoi, qh, i, t_bits[i], t_th)) << (8 * (k & 3));
         }
         if (!in) {
 #pragma unroll
@@ -601,7 +607,7 @@ __device__ __attribute__((noinline)) void encode_waves(const CodecArgs& a) {
           uint32_t cd[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            cd[r] = in ? static_cast<uint32_t>(code_of<LM>(acc[tb][cb][r], tq_row(qtab, i0 + r), t_bits[i0 + r], t_th)) : 0u;
+            cd[r] = in ? static_cast<uint32_t>(code_of<LM>(acc[tb][cb][r], qoi, qh, i0 + r, t_bits[i0 + r], t_th)) : 0u;
           if (!isv) {
             uint64_t run = 0;
             int nb = 0;
