@@ -286,6 +286,8 @@ aatc_status launch_partial(const aatc_cache* c, const Plan& p, const float* q, i
   a.ksz = p.ksz;
   a.gs = p.gs;
   a.prod = p.prod;
+  // K tiles of whole 16-byte units per token: swizzled in LDS (see dma_bytes)
+  a.kswz = (!p.half && (c->k_bits == 128 || c->k_bits == 256 || c->k_bits == 512)) ? c->k_bits / 32 - 1 : 0;
   const dim3 grid(p.S, c->n_kv_heads, c->batch);
   hipError_t err = hipSuccess;
   const bool ok = dispatch(p, a, kcal, vcal, grid, st, &err);

@@ -87,6 +87,8 @@ struct AttnArgs {
                                       // end) its [NVB][32][4] floats of the merge
   int gs;                             // tiles per score group, 1..TG, <= nslot
   int prod;                           // copy waves (0 or NPROD_MAX) issue every tile copy
+  int kswz;                           // K tiles of whole 16-byte units per token (B_K = 128 U,
+                                      // U = 1, 2, 4): 4U - 1, the unit swizzle mask; else 0
 };
 
 // Merge area per column group and wave: up to 12 groups every lane's raw int32 sums (both
@@ -348,14 +350,29 @@ __device__ inline int dma_words(const void* src, void* dst, int nwords, int k, i
 
 // Copies the 16-byte units covering bytes [p, p + n) (p rounded down to 16) to LDS dst, one
 // instruction per 64 units (lanes past the last unit idle).  Returns the instructions issued.
-__device__ inline int dma_bytes(const char* p, int n, uint8_t* dst, int lane) {
+// With swz != 0 (a K tile of B = 128 U bits, U = 1, 2 or 4, so 16-byte aligned and 64 U units)
+// LDS unit s holds source unit s ^ ((s >> 4) & swz): an involution within each 16-unit block
+// that puts the units one score instruction reads (tokens 16a + 4b + tau of a fixed tau, one
+// unit each) in 16 different bank groups instead of one (B = 512: the 64-byte token stride maps
+// them all to the same banks).
+__device__ inline int dma_bytes(const char* p, int n, uint8_t* dst, int lane, int swz = 0) {
   const char* a = reinterpret_cast<const char*>(reinterpret_cast<uintptr_t>(p) & ~static_cast<uintptr_t>(15));
   const int units = static_cast<int>((p + n - a + 15) >> 4);
   int ni = 0;
   for (int i = 0; i < units; i += 64, ++ni)
-    if (i + lane < units)
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(a + (i + lane) * 16), dst + i * 16, 16, 0, 0);
+    if (i + lane < units) {
+      const int s = i + lane;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(a + (s ^ ((s >> 4) & swz)) * 16), dst + i * 16, 16,
+                                       0, 0);
+    }
   return ni;
+}
+
+// Word of a K tile in LDS holding plane bits [o, o + 32) of the tile's string (o a multiple of
+// 32 when swz != 0): the unit o / 128 moved by dma_bytes' swizzle.
+__device__ inline int k_word(int o, int swz) {
+  const int pu = o >> 7;
+  return ((pu ^ ((pu >> 4) & swz)) << 2) | ((o >> 5) & 3);
 }
 
 template <int NP, bool HALF, int NVB, int LIMBS, int NPROD>
@@ -432,7 +449,7 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
   };
   auto copy_tile = [&](int w, int r) {
     uint8_t* sl = slot_of(w, r);
-    if (Bk > 0) dma_bytes(kaddr_w(w, r), static_cast<int>(kbytes), sl, lane);
+    if (Bk > 0) dma_bytes(kaddr_w(w, r), static_cast<int>(kbytes), sl, lane, a.kswz);
     if (Bv > 0) dma_bytes(vaddr_w(w, r), static_cast<int>(vbytes), sl + a.ksz, lane);
   };
   auto ninstr = [&](int r) { return ninstr_w(wave, r); };
@@ -736,26 +753,45 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
       asm volatile("" : "+v"(kt));
       const uint8_t* klt = ring + kt;
       v4i cc[4];
+      // swizzled K tiles (whole units per token, so every window is one aligned word) read one
+      // word at a moved address; the two forms are separate loops, so neither pays for the other
+      auto scores = [&](auto swz_tag) {
+        constexpr bool SWZ = decltype(swz_tag)::value;
 #pragma unroll
-      for (int tau = 0; tau < 4; ++tau) {
-        cc[tau] = v4i{0, 0, 0, 0};
+        for (int tau = 0; tau < 4; ++tau) {
+          cc[tau] = v4i{0, 0, 0, 0};
 #pragma unroll
-        for (int u = 0; u < NP; ++u) {
-          const bool hp = HALF && u == NP - 1;
-          const int o = kofs[u] + tau * Bk;
-          const uint32_t* w = reinterpret_cast<const uint32_t*>(klt) + (o >> 5);
-          const uint32_t dw = __builtin_amdgcn_alignbit(w[1], w[0], static_cast<uint32_t>(o));
-          v4i b0;
+          for (int u = 0; u < NP; ++u) {
+            const bool hp = HALF && u == NP - 1;
+            const int o = kofs[u] + tau * Bk;
+            const uint32_t* kwp = reinterpret_cast<const uint32_t*>(klt);
+            uint32_t dw;
+            if constexpr (SWZ) {
+              dw = kwp[k_word(o, a.kswz)];
+            } else {
+              const uint32_t* w = kwp + (o >> 5);
+              dw = __builtin_amdgcn_alignbit(w[1], w[0], static_cast<uint32_t>(o));
+            }
+            v4i b0;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) b0[j] = static_cast<int>((dw >> j) & 0x01010101u);
-          cc[tau] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa[u][0], b0, cc[tau], 0, 0, 0);
-          if (!hp) {
-            v4i b1;
+            for (int j = 0; j < 4; ++j) b0[j] = static_cast<int>((dw >> j) & 0x01010101u);
+            cc[tau] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa[u][0], b0, cc[tau], 0, 0, 0);
+            if (!hp) {
+              v4i b1;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) b1[j] = static_cast<int>((dw >> (j + 4)) & 0x01010101u);
-            cc[tau] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa[u][1], b1, cc[tau], 0, 0, 0);
+              for (int j = 0; j < 4; ++j) b1[j] = static_cast<int>((dw >> (j + 4)) & 0x01010101u);
+              cc[tau] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa[u][1], b1, cc[tau], 0, 0, 0);
+            }
           }
         }
+      };
+      if constexpr (!HALF) {
+        if (a.kswz != 0)
+          scores(std::true_type{});
+        else
+          scores(std::false_type{});
+      } else {
+        scores(std::false_type{});
       }
 #pragma unroll
       for (int tau = 0; tau < 4; ++tau) {
