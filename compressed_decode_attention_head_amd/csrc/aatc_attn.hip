@@ -286,8 +286,10 @@ aatc_status launch_partial(const aatc_cache* c, const Plan& p, const float* q, i
   a.ksz = p.ksz;
   a.gs = p.gs;
   a.prod = p.prod;
-  // K tiles of whole 16-byte units per token: swizzled in LDS (see dma_bytes)
-  a.kswz = (!p.half && (c->k_bits == 128 || c->k_bits == 256 || c->k_bits == 512)) ? c->k_bits / 32 - 1 : 0;
+  // K tiles of whole 16-byte units per token (U = B_K / 128 of them): swizzled in LDS (see
+  // dma_bytes) with the mask that spreads one score read over 16 bank groups for that U
+  const int ku = (!p.half && c->k_bits % 128 == 0) ? c->k_bits / 128 : 0;
+  a.kswz = ku == 1 || ku == 3 ? 3 : ku == 2 ? 7 : ku == 4 ? 15 : 0;
   const dim3 grid(p.S, c->n_kv_heads, c->batch);
   hipError_t err = hipSuccess;
   const bool ok = dispatch(p, a, kcal, vcal, grid, st, &err);

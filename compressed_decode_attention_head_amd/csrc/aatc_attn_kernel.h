@@ -88,7 +88,7 @@ struct AttnArgs {
   int gs;                             // tiles per score group, 1..TG, <= nslot
   int prod;                           // copy waves (0 or NPROD_MAX) issue every tile copy
   int kswz;                           // K tiles of whole 16-byte units per token (B_K = 128 U,
-                                      // U = 1, 2, 4): 4U - 1, the unit swizzle mask; else 0
+                                      // U = 1..4): the unit swizzle mask (3, 7, 3, 15); else 0
 };
 
 // Merge area per column group and wave: up to 12 groups every lane's raw int32 sums (both
@@ -350,11 +350,11 @@ __device__ inline int dma_words(const void* src, void* dst, int nwords, int k, i
 
 // Copies the 16-byte units covering bytes [p, p + n) (p rounded down to 16) to LDS dst, one
 // instruction per 64 units (lanes past the last unit idle).  Returns the instructions issued.
-// With swz != 0 (a K tile of B = 128 U bits, U = 1, 2 or 4, so 16-byte aligned and 64 U units)
-// LDS unit s holds source unit s ^ ((s >> 4) & swz): an involution within each 16-unit block
-// that puts the units one score instruction reads (tokens 16a + 4b + tau of a fixed tau, one
-// unit each) in 16 different bank groups instead of one (B = 512: the 64-byte token stride maps
-// them all to the same banks).
+// With swz != 0 (a K tile of B = 128 U bits, U = 1..4, so 16-byte aligned and 64 U units, a
+// whole number of 16-unit blocks) LDS unit s holds source unit s ^ ((s >> 4) & swz): an
+// involution within each 16-unit block that puts the units one score instruction reads (tokens
+// 16a + 4b + tau of a fixed tau, one unit each) in 16 different bank groups instead of four or
+// fewer (B = 512: the 64-byte token stride maps them all to the same banks).
 __device__ inline int dma_bytes(const char* p, int n, uint8_t* dst, int lane, int swz = 0) {
   const char* a = reinterpret_cast<const char*>(reinterpret_cast<uintptr_t>(p) & ~static_cast<uintptr_t>(15));
   const int units = static_cast<int>((p + n - a + 15) >> 4);

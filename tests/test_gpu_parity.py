@@ -146,6 +146,28 @@ def test_ragged_seq_lens_and_empty():
     assert np.abs(lse.cpu().numpy()[:2] - lref[:2]).max() <= 5e-3
 
 
+@pytest.mark.parametrize("bpe_k", [1.0, 2.0, 3.0, 4.0])
+def test_unit_aligned_k_tiles(bpe_k):
+    """K caches of 128, 256, 384 and 512 bits per vector (whole 16-byte units per token, the K
+    tiles that the cache pass stores permuted in LDS), over several tiles with a ragged tail and
+    per-sequence lengths that end inside a tile."""
+    torch = _torch()
+    case = Case(cfg=3, n_kv=2, group=4, n_tokens=837, batch=2, rotation="klt", bpe_k=bpe_k, bpe_v=2.0)
+    cache = case.make_cache()
+    assert cache.k_bits == int(128 * bpe_k)
+    for t in (synth.K, synth.V):
+        cache.encode(t, case.torch_x(t))
+    seq = np.array([837, 450], dtype=np.int32)
+    q = torch.from_numpy(case.q.astype(np.float32)).cuda()
+    out, lse = cache.decode_attn(q, 837, seq_lens=torch.from_numpy(seq).cuda())
+    torch.cuda.synchronize()
+    ref, lref = case.oracle_attention(seq_lens=seq)
+    err = float(np.abs(out.cpu().numpy() - ref).max())
+    print("k bits", cache.k_bits, "attn max abs err", err, flush=True)
+    assert err <= ATOL_ATTN
+    assert np.abs(lse.cpu().numpy() - lref).max() <= 5e-3
+
+
 @pytest.mark.parametrize("group", [1, 3, 8])
 def test_gqa_groups(group):
     torch = _torch()
