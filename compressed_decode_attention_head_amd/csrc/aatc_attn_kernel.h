@@ -300,16 +300,17 @@ __device__ inline unsigned shift_round(unsigned x, int k) {
 }
 
 // Exact rescale by 2^-k of a probability-weighted code sum held as two limbs: lanes 0..31 hold
-// the high limb (weight 128) and lane + 32 the low limb of the same (head, column).  The pair is
-// recombined, divided with one rounding and split again (high = value / 128, low = value % 128);
-// the value 128 * high + low stays below 2^31 while a wave streams at most 64 tiles.
-__device__ inline int shift_limbs(int x, int k, int lane) {
+// the high limb (weight 128) and lane + 32 the low limb of the same (head, column).  A 32-lane
+// swap of the register with itself hands every lane both limbs (high in the first result, low
+// in the second); the value 128 * high + low (below 2^31 while a wave streams at most 64 tiles)
+// is divided with one rounding, (v + rnd) >> k, and split again by a per-lane field extract:
+// bits 7.. on high-limb lanes (off 7, width 25), bits 0..6 on low-limb lanes (off 0, width 7).
+// The caller passes k <= 31 and rnd = 2^(k-1) (0 for k = 0); a shift of 32 or more, where the
+// value rounds to 0, is k = 31 with rnd = 0.
+__device__ inline int shift_limbs(int x, unsigned k, unsigned rnd, unsigned off, unsigned width) {
   const auto p = __builtin_amdgcn_permlane32_swap(static_cast<unsigned>(x), static_cast<unsigned>(x), false, false);
-  const unsigned partner = lane < 32 ? p[1] : p[0];
-  const unsigned hi = lane < 32 ? static_cast<unsigned>(x) : partner;
-  const unsigned lo = lane < 32 ? partner : static_cast<unsigned>(x);
-  const unsigned v = shift_round((hi << 7) + lo, k);
-  return static_cast<int>(lane < 32 ? (v >> 7) : (v & 127u));
+  const unsigned v = ((p[0] << 7) + p[1] + rnd) >> k;
+  return static_cast<int>(__builtin_amdgcn_ubfe(v, off, width));
 }
 
 // Plane base (within a token's B-bit string) of the K window that lane group `grp` reads for
@@ -852,24 +853,41 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
         lb = shift_round(lb, kb);
         ea = ldexpf(ea, -ka);
         eb = ldexpf(eb, -kb);
-        int kr[4];
+        // shift of each accumulator register, per lane, and whether any lane of it moves (a
+        // wave-uniform test: registers whose heads keep their reference are left alone)
+        int kr[4], kany[4];
         if (LIMBS == 2) {
           // acc register r of lane group grp holds head 4*(grp&1)+r; the shift of head hd
           // lives in pair a (heads {0,4,1,5} in lane groups 0..3) or pair b ({2,6,3,7})
           const bool odd = grp & 1;
-          kr[0] = odd ? __builtin_amdgcn_readlane(ka, 16) : __builtin_amdgcn_readlane(ka, 0);
-          kr[1] = odd ? __builtin_amdgcn_readlane(ka, 48) : __builtin_amdgcn_readlane(ka, 32);
-          kr[2] = odd ? __builtin_amdgcn_readlane(kb, 16) : __builtin_amdgcn_readlane(kb, 0);
-          kr[3] = odd ? __builtin_amdgcn_readlane(kb, 48) : __builtin_amdgcn_readlane(kb, 32);
+          const int a0 = __builtin_amdgcn_readlane(ka, 0), a1 = __builtin_amdgcn_readlane(ka, 16);
+          const int a2 = __builtin_amdgcn_readlane(ka, 32), a3 = __builtin_amdgcn_readlane(ka, 48);
+          const int b0 = __builtin_amdgcn_readlane(kb, 0), b1 = __builtin_amdgcn_readlane(kb, 16);
+          const int b2 = __builtin_amdgcn_readlane(kb, 32), b3 = __builtin_amdgcn_readlane(kb, 48);
+          kr[0] = odd ? a1 : a0;
+          kr[1] = odd ? a3 : a2;
+          kr[2] = odd ? b1 : b0;
+          kr[3] = odd ? b3 : b2;
+          kany[0] = a0 | a1;
+          kany[1] = a2 | a3;
+          kany[2] = b0 | b1;
+          kany[3] = b2 | b3;
         } else {
           // acc register r holds head r (rows 8l + r); head r's shift lives in lane group r
 #pragma unroll
-          for (int r = 0; r < 4; ++r) kr[r] = __builtin_amdgcn_readlane(ka, 16 * r);
+          for (int r = 0; r < 4; ++r) kany[r] = kr[r] = __builtin_amdgcn_readlane(ka, 16 * r);
         }
+        const unsigned off = lane < 32 ? 7u : 0u, width = lane < 32 ? 25u : 7u;
 #pragma unroll
-        for (int v = 0; v < NVB; ++v)
+        for (int r = 0; r < 4; ++r) {
+          if (kany[r] != 0) {
+            const unsigned k = static_cast<unsigned>(kr[r]);
+            const unsigned kk = k > 31u ? 31u : k;
+            const unsigned rnd = (k == 0u || k > 31u) ? 0u : (1u << (k - 1u));
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[v][r] = shift_limbs(acc[v][r], kr[r], lane);
+            for (int v = 0; v < NVB; ++v) acc[v][r] = shift_limbs(acc[v][r], kk, rnd, off, width);
+          }
+        }
         sha += ka;
         shb += kb;
         bia = PKN_BIAS - static_cast<float>(sha);
