@@ -21,8 +21,9 @@ using namespace aatc_attn;
 
 constexpr size_t kLdsLimit = 160 * 1024;
 constexpr size_t kLmStaticLds = 16 * 1024;  // k_attn_lm's static LDS (tables, q, merge headers), rounded up
-// __shared__ arrays of the kernel: the probability rows plus scalars (rounded up)
-constexpr size_t kStaticLds = static_cast<size_t>(CW) * TG * PROW_BYTES + 2048;
+// __shared__ arrays of the kernel: the probability rows of tg tiles per wave plus scalars
+// (rounded up)
+constexpr size_t static_lds(int tg) { return static_cast<size_t>(CW) * tg * PROW_BYTES + 2048; }
 
 int vtiles_bucket(int vt) {
   if (vt <= 12) return 12;
@@ -33,7 +34,7 @@ int vtiles_bucket(int vt) {
 
 struct Plan {
   bool lm;                               // the level pass (k_attn_lm): a Lloyd-Max tensor
-  int NP, NVB, LIMBS, S, tpw, half, prec, prod;
+  int NP, NVB, LIMBS, S, tpw, half, prec, prod, tg;
   int nslot, slot_bytes, ksz, gs, wave_bytes;
   size_t lds;
   size_t part_bytes, offs_bytes;
@@ -65,7 +66,7 @@ Plan make_plan(const aatc_cache* c, int n_q, int64_t max_seq) {
     S = (ntiles + tpw - 1) / tpw;
     p.S = static_cast<int>(S < 1 ? 1 : S);
     p.prec = aatc_lm::PHDR + AATC_D;
-    p.NP = p.NVB = p.LIMBS = p.half = p.prod = 0;
+    p.NP = p.NVB = p.LIMBS = p.half = p.prod = p.tg = 0;
     p.nslot = p.slot_bytes = p.ksz = p.gs = p.wave_bytes = 0;
     p.nslot = aatc_lm::dyn_lds(c->k_bits, c->v_bits, 2) + kLmStaticLds <= kLdsLimit ? 2 : 1;
     p.lds = aatc_lm::dyn_lds(c->k_bits, c->v_bits, p.nslot);
@@ -97,31 +98,43 @@ Plan make_plan(const aatc_cache* c, int n_q, int64_t max_seq) {
   p.ksz = kb > 0 ? round16(8LL * kb + 16) : 0;
   const int vsz = vb > 0 ? round16(8LL * vb + 16) : 0;
   p.slot_bytes = p.ksz + vsz > 0 ? p.ksz + vsz : 16;
-  const size_t avail = kLdsLimit - kStaticLds - FIXED_LDS - DMA_PAD;
-  int ns = static_cast<int>(avail / (static_cast<size_t>(CW) * p.slot_bytes));
-  if (ns > p.tpw) ns = p.tpw;
-  p.nslot = ns;
-  p.fits = ns >= 1;
-  // one score group per wave when its tiles all fit (no running-max rescale at all);
-  // otherwise groups of half the slots, so that the next group's copies fly meanwhile
+  // one score group per wave when its tiles all fit (no running-max rescale at all); otherwise
+  // the ring form: one tile per group, with probability rows for one tile per wave, so that
+  // the LDS they free holds more slots and the next tiles' copies fly meanwhile
+  auto slots = [&](int tg) {
+    const size_t avail = kLdsLimit - static_lds(tg) - FIXED_LDS - DMA_PAD;
+    return static_cast<int>(avail / (static_cast<size_t>(CW) * p.slot_bytes));
+  };
+  int ns = slots(TG);
   if (ns >= p.tpw) {
+    p.tg = TG;
+    ns = p.tpw;
     p.gs = p.tpw < TG ? p.tpw : TG;
-  } else {
+  } else if (p.NVB == 24) {
+    // the widest V bucket keeps groups of half the slots (its one-tile form spills registers)
+    p.tg = TG;
     p.gs = ns / 2 < TG ? ns / 2 : TG;
     if (p.gs < 1) p.gs = 1;
+  } else {
+    p.tg = 1;
+    ns = slots(1);
+    if (ns > p.tpw) ns = p.tpw;
+    p.gs = 1;
   }
+  p.nslot = ns;
+  p.fits = ns >= 1;
   // a wave's ring area holds its slots, and at the end its merge values
   p.wave_bytes = (ns > 0 ? ns : 1) * p.slot_bytes;
   if (p.wave_bytes < p.NVB * merge_group_bytes(p.NVB)) p.wave_bytes = p.NVB * merge_group_bytes(p.NVB);
   const size_t ring = static_cast<size_t>(CW) * p.wave_bytes + DMA_PAD;
   p.lds = FIXED_LDS + ring;
-  if (p.lds + kStaticLds > kLdsLimit) p.fits = false;
+  if (p.lds + static_lds(p.tg) > kLdsLimit) p.fits = false;
   // copy waves issue every tile when all of a wave's tiles have slots and the copy count of one
   // copy wave stays within what one wait can count
   {
     const int ik = kb > 0 ? (static_cast<int>((15 + 8LL * kb + 15) / 16) + 63) / 64 : 0;
     const int iv = vb > 0 ? (static_cast<int>((15 + 8LL * vb + 15) / 16) + 63) / 64 : 0;
-    p.prod = (p.NVB == 12 && p.NP <= 2 && ns >= p.tpw && (CW / NPROD_MAX) * p.tpw * (ik + iv) <= 60) ? NPROD_MAX : 0;
+    p.prod = (p.NVB == 12 && p.NP <= 2 && p.tg == TG && ns >= p.tpw && (CW / NPROD_MAX) * p.tpw * (ik + iv) <= 60) ? NPROD_MAX : 0;
   }
   p.part_bytes = static_cast<size_t>(seqs) * p.S * group * p.prec * 4;
   p.offs_bytes = static_cast<size_t>(seqs) * 8 * 4;
@@ -134,10 +147,10 @@ bool dispatch(const Plan& p, const AttnArgs& a, const aatc_calib* kc, const aatc
               hipError_t* err) {
   bool found = false;
   switch (p.NP) {
-    case 1: *err = launch_np<1>(p.half, p.NVB, p.LIMBS, a, kc, vc, grid, p.lds, st, &found); break;
-    case 2: *err = launch_np<2>(p.half, p.NVB, p.LIMBS, a, kc, vc, grid, p.lds, st, &found); break;
-    case 3: *err = launch_np<3>(p.half, p.NVB, p.LIMBS, a, kc, vc, grid, p.lds, st, &found); break;
-    case 4: *err = launch_np<4>(p.half, p.NVB, p.LIMBS, a, kc, vc, grid, p.lds, st, &found); break;
+    case 1: *err = launch_np<1>(p.half, p.NVB, p.LIMBS, p.tg, a, kc, vc, grid, p.lds, st, &found); break;
+    case 2: *err = launch_np<2>(p.half, p.NVB, p.LIMBS, p.tg, a, kc, vc, grid, p.lds, st, &found); break;
+    case 3: *err = launch_np<3>(p.half, p.NVB, p.LIMBS, p.tg, a, kc, vc, grid, p.lds, st, &found); break;
+    case 4: *err = launch_np<4>(p.half, p.NVB, p.LIMBS, p.tg, a, kc, vc, grid, p.lds, st, &found); break;
   }
   return found;
 }

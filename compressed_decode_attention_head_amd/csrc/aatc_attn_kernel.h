@@ -85,7 +85,7 @@ struct AttnArgs {
   int slot_bytes, ksz;                // bytes per slot (K area first, ksz bytes)
   int wave_bytes;                     // ring bytes per compute wave: its slots, then (at the
                                       // end) its [NVB][32][4] floats of the merge
-  int gs;                             // tiles per score group, 1..TG, <= nslot
+  int gs;                             // tiles per score group, 1..TGM, <= nslot
   int prod;                           // copy waves (0 or NPROD_MAX) issue every tile copy
   int kswz;                           // K tiles of whole 16-byte units per token (B_K = 128 U,
                                       // U = 1..4): the unit swizzle mask (3, 7, 3, 15); else 0
@@ -376,7 +376,7 @@ __device__ inline int k_word(int o, int swz) {
   return ((pu ^ ((pu >> 4) & swz)) << 2) | ((o >> 5) & 3);
 }
 
-template <int NP, bool HALF, int NVB, int LIMBS, int NPROD>
+template <int NP, bool HALF, int NVB, int LIMBS, int NPROD, int TGM>
 __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, const aatc_calib* __restrict__ kcal,
                                                                  const aatc_calib* __restrict__ vcal) {
   using LM = Lim<LIMBS>;
@@ -391,7 +391,7 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
   uint8_t* ring = smem + FIXED_LDS;                                 // [CW][wave_bytes]
   // probability limb rows live in their own static array: no tile copy can write them, so
   // reading them needs no wait on the copies in flight
-  __shared__ __align__(16) uint8_t pl[CW * TG * PROW_BYTES];        // [CW][TG][16][64]
+  __shared__ __align__(16) uint8_t pl[CW * TGM * PROW_BYTES];       // [CW][TGM][16][64]
   __shared__ float s_m[CW][8], s_l[CW][8], s_e[CW][8];
   __shared__ float esc[8];
   __shared__ Sync sy;
@@ -540,7 +540,7 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
   int kofs[NP];
 #pragma unroll
   for (int u = 0; u < NP; ++u) kofs[u] = tok0 * Bk + plane_base(u, grp, HALF && u == NP - 1);
-  uint8_t* pw = pl + wave * TG * PROW_BYTES;
+  uint8_t* pw = pl + wave * TGM * PROW_BYTES;
   // probability rows (limb l, head slot x) = row 8l + x; dword n16 of a row sits in 16-byte
   // quad (n16/4) ^ (row%4)
   auto prow_addr = [&](int row) { return row * 64 + 16 * ((n16 >> 2) ^ (row & 3)) + 4 * (n16 & 3); };
@@ -728,10 +728,10 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
     // register pair per column group out of the loop
     int cT4 = T4, cT42 = T4 + T2, cNV = NV;
     asm volatile("" : "+s"(cT4), "+s"(cT42), "+s"(cNV));
-    int sa[TG][4], sb[TG][4];
+    int sa[TGM][4], sb[TGM][4];
     // scores, tile by tile as each lands: 4 token groups of 16 = 4 independent MFMA chains
 #pragma unroll
-    for (int g = 0; g < TG; ++g) {
+    for (int g = 0; g < TGM; ++g) {
       if (g >= ng) {                                    // past the group's end: no tile, masked
 #pragma unroll
         for (int tau = 0; tau < 4; ++tau) {
@@ -817,10 +817,10 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
       }
     }
     // tiles past the group's end and tokens past the sequence's end take no part
-    const bool masked = ng < TG || seq - (tw0 + g0 + ng - 1) * 64 < 64;
+    const bool masked = ng < TGM || seq - (tw0 + g0 + ng - 1) * 64 < 64;
     if (masked) {
 #pragma unroll
-      for (int g = 0; g < TG; ++g) {
+      for (int g = 0; g < TGM; ++g) {
         const int nvalid = g < ng ? seq - (tw0 + g0 + g) * 64 : 0;
         if (nvalid < 64) {
 #pragma unroll
@@ -832,7 +832,7 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
     // group maxima (every tile has a visible token, so they are real scores)
     int mxa = INT_MIN, mxb = INT_MIN;
 #pragma unroll
-    for (int g = 0; g < TG; ++g) {
+    for (int g = 0; g < TGM; ++g) {
       mxa = max(mxa, max(max(sa[g][0], sa[g][1]), max(sa[g][2], sa[g][3])));
       if (LIMBS == 2) mxb = max(mxb, max(max(sb[g][0], sb[g][1]), max(sb[g][2], sb[g][3])));
     }
@@ -897,7 +897,7 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
     // probabilities in 14-bit fixed point (pknorm rounds 65535 * x), two 7-bit limbs; the
     // four tokens of this lane fill one dword per (head, limb); tile g uses rows at g*1024
 #pragma unroll
-    for (int g = 0; g < TG; ++g) {
+    for (int g = 0; g < TGM; ++g) {
       if (g < ng) {
         uint8_t* pg = pw + g * PROW_BYTES;
         {
@@ -944,7 +944,7 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
     // PV on packed V fields (width-uniform column groups: w4 | w2 | w1); columns past a
     // class's field count read neighbouring words and are never used
 #pragma unroll
-    for (int g = 0; g < TG; ++g) {
+    for (int g = 0; g < TGM; ++g) {
       if (g < ng) {
         const uint4 pv = *reinterpret_cast<const uint4*>(pw + g * PROW_BYTES + prd);
         const v4i pA = {static_cast<int>(pv.x), static_cast<int>(pv.y), static_cast<int>(pv.z), static_cast<int>(pv.w)};
@@ -1336,55 +1336,64 @@ __global__ __launch_bounds__(CNT) void k_attn_combine(CombArgs a, const aatc_cal
 }
 #endif
 
-template <int NP, bool HALF, int NVB, int LIMBS, int NPROD>
+template <int NP, bool HALF, int NVB, int LIMBS, int NPROD, int TGM>
 hipError_t launch_one(const AttnArgs& a, const aatc_calib* kcal, const aatc_calib* vcal, dim3 grid, size_t lds,
                       hipStream_t st) {
-  const void* fn = reinterpret_cast<const void*>(&k_attn_main<NP, HALF, NVB, LIMBS, NPROD>);
+  const void* fn = reinterpret_cast<const void*>(&k_attn_main<NP, HALF, NVB, LIMBS, NPROD, TGM>);
   const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_attn_main<NP, HALF, NVB, LIMBS, NPROD>), grid, dim3((CW + NPROD) * 64), lds, st, a, kcal,
-                     vcal);
+  hipLaunchKernelGGL((k_attn_main<NP, HALF, NVB, LIMBS, NPROD, TGM>), grid, dim3((CW + NPROD) * 64), lds, st, a,
+                     kcal, vcal);
   return hipGetLastError();
 }
 
 // The producer form runs 12 waves, 3 per SIMD, so only the smallest V bucket with at most two
-// bit-plane pairs fits its registers.
+// bit-plane pairs fits its registers; it is planned only when every tile has a slot, so it
+// always scores groups of up to TG tiles.  The ring form (tg = 1; not for the widest V bucket,
+// whose registers it would spill) scores one tile per group and keeps one probability row block
+// per wave, leaving the LDS to the ring.
 template <int NP, bool HALF, int NVB>
-hipError_t launch_limbs(int limbs, const AttnArgs& a, const aatc_calib* kcal, const aatc_calib* vcal, dim3 grid,
-                        size_t lds, hipStream_t st) {
+hipError_t launch_limbs(int limbs, int tg, const AttnArgs& a, const aatc_calib* kcal, const aatc_calib* vcal,
+                        dim3 grid, size_t lds, hipStream_t st) {
   if constexpr (NVB == 12 && NP <= 2) {
     if (a.prod)
-      return limbs == 3 ? launch_one<NP, HALF, NVB, 3, NPROD_MAX>(a, kcal, vcal, grid, lds, st)
-                        : launch_one<NP, HALF, NVB, 2, NPROD_MAX>(a, kcal, vcal, grid, lds, st);
+      return limbs == 3 ? launch_one<NP, HALF, NVB, 3, NPROD_MAX, TG>(a, kcal, vcal, grid, lds, st)
+                        : launch_one<NP, HALF, NVB, 2, NPROD_MAX, TG>(a, kcal, vcal, grid, lds, st);
   }
-  return limbs == 3 ? launch_one<NP, HALF, NVB, 3, 0>(a, kcal, vcal, grid, lds, st)
-                    : launch_one<NP, HALF, NVB, 2, 0>(a, kcal, vcal, grid, lds, st);
+  if constexpr (NVB != 24) {
+    if (tg == 1)
+      return limbs == 3 ? launch_one<NP, HALF, NVB, 3, 0, 1>(a, kcal, vcal, grid, lds, st)
+                        : launch_one<NP, HALF, NVB, 2, 0, 1>(a, kcal, vcal, grid, lds, st);
+  }
+  return limbs == 3 ? launch_one<NP, HALF, NVB, 3, 0, TG>(a, kcal, vcal, grid, lds, st)
+                    : launch_one<NP, HALF, NVB, 2, 0, TG>(a, kcal, vcal, grid, lds, st);
 }
 
 template <int NP, bool HALF>
-hipError_t launch_nvb(int nvb, int limbs, const AttnArgs& a, const aatc_calib* kcal, const aatc_calib* vcal, dim3 grid,
-                      size_t lds, hipStream_t st, bool* found) {
+hipError_t launch_nvb(int nvb, int limbs, int tg, const AttnArgs& a, const aatc_calib* kcal, const aatc_calib* vcal,
+                      dim3 grid, size_t lds, hipStream_t st, bool* found) {
   *found = true;
   switch (nvb) {
-    case 12: return launch_limbs<NP, HALF, 12>(limbs, a, kcal, vcal, grid, lds, st);
-    case 16: return launch_limbs<NP, HALF, 16>(limbs, a, kcal, vcal, grid, lds, st);
-    case 24: return launch_limbs<NP, HALF, 24>(limbs, a, kcal, vcal, grid, lds, st);
+    case 12: return launch_limbs<NP, HALF, 12>(limbs, tg, a, kcal, vcal, grid, lds, st);
+    case 16: return launch_limbs<NP, HALF, 16>(limbs, tg, a, kcal, vcal, grid, lds, st);
+    case 24: return launch_limbs<NP, HALF, 24>(limbs, tg, a, kcal, vcal, grid, lds, st);
   }
   *found = false;
   return hipSuccess;
 }
 
-// One translation unit per NP instantiates this (both pair kinds, all V buckets and limb modes).
+// One translation unit per NP instantiates this (both pair kinds, all V buckets, limb modes and
+// group sizes).
 template <int NP>
-hipError_t launch_np(int half, int nvb, int limbs, const AttnArgs& a, const aatc_calib* kcal, const aatc_calib* vcal,
-                     dim3 grid, size_t lds, hipStream_t st, bool* found) {
-  return half ? launch_nvb<NP, true>(nvb, limbs, a, kcal, vcal, grid, lds, st, found)
-              : launch_nvb<NP, false>(nvb, limbs, a, kcal, vcal, grid, lds, st, found);
+hipError_t launch_np(int half, int nvb, int limbs, int tg, const AttnArgs& a, const aatc_calib* kcal,
+                     const aatc_calib* vcal, dim3 grid, size_t lds, hipStream_t st, bool* found) {
+  return half ? launch_nvb<NP, true>(nvb, limbs, tg, a, kcal, vcal, grid, lds, st, found)
+              : launch_nvb<NP, false>(nvb, limbs, tg, a, kcal, vcal, grid, lds, st, found);
 }
 
-#define AATC_LAUNCH_NP_SIG(N)                                                                                \
-  hipError_t launch_np<N>(int, int, int, const AttnArgs&, const aatc_calib*, const aatc_calib*, dim3, size_t, \
-                          hipStream_t, bool*)
+#define AATC_LAUNCH_NP_SIG(N)                                                                     \
+  hipError_t launch_np<N>(int, int, int, int, const AttnArgs&, const aatc_calib*, const aatc_calib*, dim3, \
+                          size_t, hipStream_t, bool*)
 extern template AATC_LAUNCH_NP_SIG(1);
 extern template AATC_LAUNCH_NP_SIG(2);
 extern template AATC_LAUNCH_NP_SIG(3);
