@@ -469,7 +469,24 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
     const int n = static_cast<int>((a.max_seq + 63) / 64) - first_tile(w);
     return n < 0 ? 0 : (n < a.tpw ? n : a.tpw);
   };
-  if (NPROD == 0) issue_upto(NS, ncap_w(wave));
+  // Form without copy waves: the tables and, for KLT and NOVA caches, this thread's quarter
+  // row of R_K (into registers) are loaded first and the prologue runs on them before any tile
+  // copy is issued (the first stream group issues them).  Every wave issuing its first tiles at
+  // once saturates HBM, and issuing then blocks until the queue drains (about 3 us at 4 bits),
+  // so copies issued before the prologue would hold it back by that long.
+  constexpr int TPR = CW * 64 / D, CPT = D / TPR;
+  static_assert(TPR == 4, "threads per row");
+  float2 rrow[CPT / 2];
+  bool rpre = false;
+  if constexpr (NPROD == 0) {
+    const int rot0 = kc->rotation;
+    rpre = rot0 == AATC_ROT_KLT || rot0 == AATC_ROT_NOVA;
+    if (rpre) {
+      const float2* row = reinterpret_cast<const float2*>(kc->R32 + (tid / TPR) * D + CPT * (tid % TPR));
+#pragma unroll
+      for (int c2 = 0; c2 < CPT / 2; ++c2) rrow[c2] = row[c2];
+    }
+  }
   // producer form: a copy wave sustains only a few GB/s, so the compute waves copy their own
   // first SELF tiles (all eight waves issuing at once) and the copy waves the rest
   if (NPROD > 0 && wave < CW) issue_upto(SELF, ncap_w(wave));
@@ -583,29 +600,39 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
   // wave x (< 8) owns head slot x: q~ at channels lane and 64 + lane
   float y0 = 0.f, y1 = 0.f;
   if (rot == AATC_ROT_KLT) {
-    // row i of R_K: 4 threads per row, eight q heads per thread
-    constexpr int TPR = CW * 64 / D, CPT = D / TPR;
-    static_assert(TPR == 4, "threads per row");
+    // row i of R_K: 4 threads per row, GH q heads per thread (the head slots a group can use:
+    // 4 with three limbs, 8 with two)
+    constexpr int GH = LIMBS == 3 ? 4 : 8;
     const int i = tid / TPR, qq = tid % TPR;
-    float part[8];
+    float part[GH];
 #pragma unroll
-    for (int g = 0; g < 8; ++g) part[g] = 0.f;
+    for (int g = 0; g < GH; ++g) part[g] = 0.f;
     const float2* row = reinterpret_cast<const float2*>(kc->R32 + i * D + CPT * qq);
-#pragma unroll 4
-    for (int c2 = 0; c2 < CPT / 2; ++c2) {
-      const float2 rr = row[c2];
-      const int j = CPT * qq + 2 * c2;
+    if (NPROD == 0 && rpre) {
 #pragma unroll
-      for (int g = 0; g < 8; ++g) part[g] += rr.x * qs[g * D + j] + rr.y * qs[g * D + j + 1];
+      for (int c2 = 0; c2 < CPT / 2; ++c2) {
+        const float2 rr = rrow[c2];
+        const int j = CPT * qq + 2 * c2;
+#pragma unroll
+        for (int g = 0; g < GH; ++g) part[g] += rr.x * qs[g * D + j] + rr.y * qs[g * D + j + 1];
+      }
+    } else {
+#pragma unroll 4
+      for (int c2 = 0; c2 < CPT / 2; ++c2) {
+        const float2 rr = row[c2];
+        const int j = CPT * qq + 2 * c2;
+#pragma unroll
+        for (int g = 0; g < GH; ++g) part[g] += rr.x * qs[g * D + j] + rr.y * qs[g * D + j + 1];
+      }
     }
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
+    for (int g = 0; g < GH; ++g) {
       part[g] += xor_lanes<1>(part[g], lane);
       part[g] += xor_lanes<2>(part[g], lane);
     }
     if (qq == 0)
 #pragma unroll
-      for (int g = 0; g < 8; ++g) qt[g * D + i] = part[g];
+      for (int g = 0; g < GH; ++g) qt[g * D + i] = part[g];
     compute_barrier(&sy, phase, lane);
     y0 = qt[wave * D + lane];
     y1 = qt[wave * D + 64 + lane];
