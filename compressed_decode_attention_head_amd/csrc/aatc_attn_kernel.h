@@ -105,6 +105,7 @@ struct Sync {
   int landed[CW];                     // producer form: tiles of compute wave w in LDS
   int tabs[NPROD_MAX];                // producer form: copy wave p's table copies in LDS
   int broken;                         // a bounded wait gave up
+  int prog[CW];                       // stream steps done, per compute wave
 };
 
 
@@ -257,6 +258,20 @@ __device__ inline void lds_store(int* p, int v) {
   asm volatile("ds_write_b32 %0, %1" : : "v"(lds_addr(p)), "v"(v) : "memory");
 }
 
+// Compute waves w and w ^ 4 share a SIMD, whose arbiter favours the older wave throughout: on
+// the batch-16 layer the younger one finished its tiles 7 us later, and the merge waited for it.
+// At each stream step a wave publishes its step count and runs at the higher priority while it
+// is behind its partner.  (With copy waves on the same SIMDs, whose publishing the compute
+// waves wait for, it cost the headline 0.5 us; that form does without.)
+__device__ inline void balance_simd(Sync* sy, int wave, int step) {
+  lds_store(&sy->prog[wave], step);
+  const int other = __builtin_amdgcn_readfirstlane(lds_load_now(&sy->prog[wave ^ 4]));
+  if (step < other)
+    __builtin_amdgcn_s_setprio(1);
+  else
+    __builtin_amdgcn_s_setprio(0);
+}
+
 // Barrier of the CW waves on per-wave LDS flags (`phase` counts the barriers this wave has
 // passed).  Unlike s_barrier with a workgroup fence it does not wait for this wave's copies in
 // flight: a wave's LDS operations complete in issue order, so its writes before the flag are
@@ -402,6 +417,7 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
   if (tid < CW) {
     sy.arrive[tid] = 0;
     sy.landed[tid] = 0;
+    sy.prog[tid] = 0;
   }
   if (tid < NPROD_MAX) sy.tabs[tid] = 0;
   if (tid == 0) sy.broken = 0;
@@ -746,6 +762,8 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
 
   // ---- 2. stream this wave's tiles, groups of gs
   bool started = false;
+  int step = 0;                          // balance_simd steps (forms without copy waves): each tile's
+                                         // scores, each group's PV
 #pragma unroll 1
   for (int g0 = 0; g0 < nw; g0 += a.gs) {
     const int ng = nw - g0 < a.gs ? nw - g0 : a.gs;
@@ -775,6 +793,7 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
         wait_tile(g0 + g);
       }
       wave_sync_lds();
+      if (NPROD == 0) balance_simd(&sy, wave, ++step);
       const int64_t tile = tw0 + rr;
       // opaque slot offset: per-(tile, tau, pair) addresses are not worth registers
       int kt = static_cast<int>((slot_of(wave, rr) - ring) + ((reinterpret_cast<uintptr_t>(kseq) + tile * kbytes) & 15));
@@ -968,6 +987,7 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
       }
     }
     wave_sync_lds();
+    if (NPROD == 0) balance_simd(&sy, wave, ++step);
     // PV on packed V fields (width-uniform column groups: w4 | w2 | w1); columns past a
     // class's field count read neighbouring words and are never used
 #pragma unroll
@@ -1011,6 +1031,7 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
     wave_sync_lds();                     // the group's slots and rows are reused next
   }
 
+  __builtin_amdgcn_s_setprio(0);
   // ---- 3. workgroup merge in LDS: each wave parks its limb-merged code sums (unscaled) in its
   // own ring area once every copy into it has landed; one barrier; then every thread scales
   // and sums the CW waves' values of its record entries
