@@ -214,21 +214,25 @@ __device__ inline int cvt_i32_trunc(double u) {
   return r;
 }
 
-// Quantizer table of a channel: {o, 1/scale} and 2^(b-1), at a padded position: the four lanes
-// of a token in the Walsh-Hadamard form read channels 8 apart, which the padding puts in
-// disjoint LDS banks (each 32 channels take 40 rows, each 8 of them 10).
+// Quantizer table of a channel: {o, 1/scale} and 2^(b-1).  In the Walsh-Hadamard form it sits
+// at a padded position: the four lanes of a token read channels 8 apart, which the padding puts
+// in disjoint LDS banks (each 32 channels take 40 rows, each 8 of them 10).  The GEMM form's
+// lanes read four channels 4 apart, already in disjoint banks, at the plain position.
 constexpr int kQRows = 40 * (D / 32);
 static_assert(24 * kQRows <= 32 * D, "padded quantizer table fits its LDS area");
-__device__ inline int qpos(int i) { return 40 * (i >> 5) + 10 * ((i >> 3) & 3) + (i & 7); }
+template <bool PAD>
+__device__ inline int qpos(int i) {
+  return PAD ? 40 * (i >> 5) + 10 * ((i >> 3) & 3) + (i & 7) : i;
+}
 
 // Code of value y of a channel with table entries o, inv = 1/scale, half = 2^(b-1).  Uniform:
 // clamp(floor((y - o) * (1/Delta) + 2^(b-1)), 0, 2^b - 1) with NaN -> 0.  Truncation toward zero
 // equals the floor on [0, 2^b - 1], and every value outside (NaN included) lands on the clamp's
 // side it belongs to, so the clamp runs on the truncated integer.
 // Lloyd-Max: the b-bit table's threshold count (quantize_lm).
-template <bool LM>
+template <bool PAD, bool LM>
 __device__ inline int code_of(double y, const double2* qoi, const double* qh, int i, int bi, const double* thr) {
-  const int p = qpos(i);
+  const int p = qpos<PAD>(i);
   const double2 oi = qoi[p];
   if (LM) return quantize_lm(y, oi.x, oi.y, bi, thr);
   double u = (y - oi.x) * oi.y;
@@ -349,8 +353,8 @@ __device__ __attribute__((noinline)) void encode_waves(const CodecArgs& a) {
   // ---- tables, once per workgroup
   if (tid < D) {
     const int bi = c->bits[tid];
-    qoi[qpos(tid)] = make_double2(c->o[tid], lm ? c->inv_scale[tid] : c->inv_delta[tid]);
-    qh[qpos(tid)] = static_cast<double>(bi ? 1 << (bi - 1) : 0);
+    qoi[qpos<WHT>(tid)] = make_double2(c->o[tid], lm ? c->inv_scale[tid] : c->inv_delta[tid]);
+    qh[qpos<WHT>(tid)] = static_cast<double>(bi ? 1 << (bi - 1) : 0);
     t_bits[tid] = static_cast<uint8_t>(bi);
   }
   if (lm)
@@ -466,7 +470,7 @@ __device__ __attribute__((noinline)) void encode_waves(const CodecArgs& a) {
 #pragma unroll
         for (int k = 0; k < 32; ++k) {
           const int i = (k & 7) | (q4 << 3) | ((k >> 3) << 5);
-          cw[k >> 2] |= static_cast<uint32_t>(code_of<LM>(v[k] * rs, qoi, qh, i, t_bits[i], t_th)) << (8 * (k & 3));
+          cw[k >> 2] |= static_cast<uint32_t>(code_of<true, LM>(v[k] * rs, qoi, qh, i, t_bits[i], t_th)) << (8 * (k & 3));
         }
         if (!in) {
 #pragma unroll
@@ -607,7 +611,7 @@ __device__ __attribute__((noinline)) void encode_waves(const CodecArgs& a) {
           uint32_t cd[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            cd[r] = in ? static_cast<uint32_t>(code_of<LM>(acc[tb][cb][r], qoi, qh, i0 + r, t_bits[i0 + r], t_th)) : 0u;
+            cd[r] = in ? static_cast<uint32_t>(code_of<false, LM>(acc[tb][cb][r], qoi, qh, i0 + r, t_bits[i0 + r], t_th)) : 0u;
           if (!isv) {
             uint64_t run = 0;
             int nb = 0;
