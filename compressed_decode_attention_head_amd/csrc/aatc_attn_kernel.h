@@ -1183,8 +1183,10 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
 }
 
 // Merge of the S partial records of one (batch, KV head, q head); out and lse.
-constexpr int CNT = 1024;                // combine threads: 4 split quarters x 256 columns
-constexpr int SPC = 64;                  // splits per pass (16 per quarter, held in registers)
+constexpr int CNT = 1024;                // combine threads
+constexpr int SPC = 64;                  // splits per pass (one header per lane)
+constexpr int KPC = 4;                   // 16-byte pieces per loader and pass (a pass covers
+                                         // min(SPC, KPC * CNT / P) splits of P-piece records)
 constexpr int MAXCOL = 16 * 24;          // field columns of a record, at most
 
 struct CombArgs {
@@ -1203,8 +1205,7 @@ struct CombArgs {
 // Every input of the merge is read with ordinary loads issued at once at kernel entry (records,
 // V tables, R_V), so the kernel pays about one memory round trip before its arithmetic.
 __global__ __launch_bounds__(CNT) void k_attn_combine(CombArgs a, const aatc_calib* __restrict__ vcal) {
-  __shared__ float wsl[SPC];
-  __shared__ float part4[4][MAXCOL];
+  __shared__ float4 part[CNT];            // [split group q][piece p] partial sums, q * P + p
   __shared__ float csum[MAXCOL];
   __shared__ float t_o[D], t_delta[D];
   __shared__ int t_bits[D];
@@ -1212,7 +1213,6 @@ __global__ __launch_bounds__(CNT) void k_attn_combine(CombArgs a, const aatc_cal
   __shared__ uint8_t t_fs[AATC_MAX_FIELDS];
   __shared__ float yt[D], res[D];
   __shared__ float part8[8][D];
-  __shared__ float red[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int G = a.group, S = a.S, prec = a.prec;
@@ -1220,40 +1220,33 @@ __global__ __launch_bounds__(CNT) void k_attn_combine(CombArgs a, const aatc_cal
   const aatc_calib* vc = vcal + h;
   const float* rec0 = a.part + (static_cast<int64_t>(bh) * S * G + g) * prec;
   const int64_t stride = static_cast<int64_t>(G) * prec;
-  const int qtr = tid >> 8, cl = tid & 255;
+  // a record is P 16-byte pieces (its header first); thread t < Q P sums piece t % P of the
+  // splits t / P + k Q of each pass, one 16-byte load per split
+  const int P = prec >> 2, Q = CNT / P;
+  const int pp = tid % P, qq = tid / P;
+  const bool loader = qq < Q;
+  const int SPP = Q * KPC < SPC ? Q * KPC : SPC;   // splits per pass
 
-  // the first pass's records (headers and this thread's column values) before anything that
-  // depends on a load: these are the long pole
-  float hm = -INFINITY, hl = 0.f, he = 0.f;
-  float v0[SPC / 4], v1[SPC / 4];
+  // the first pass's records (every lane a header, every loader its pieces) before anything
+  // that depends on a load: these are the long pole
+  float4 hd = make_float4(-INFINITY, 0.f, 0.f, 0.f);
+  float4 xv[KPC];
   auto load_pass = [&](int s0) {
-    const int n = S - s0 < SPC ? S - s0 : SPC;
+    const int n = S - s0 < SPP ? S - s0 : SPP;
     // unconditional loads from clamped (always valid) addresses, masked afterwards: a load under
     // a branch makes the compiler wait for every load before it at the join
     const bool hv = lane < n;
-    const float* hp = rec0 + (s0 + (hv ? lane : 0)) * stride;
-    hm = hp[0];
-    hl = hp[1];
-    he = hp[2];
-    hm = hv ? hm : -INFINITY;
-    hl = hv ? hl : 0.f;
-    he = hv ? he : 0.f;
-    const bool cv0 = cl < prec - PHDR, cv1 = cl + 256 < prec - PHDR;   // record length: a kernel argument
-    const int o0 = PHDR + (cv0 ? cl : 0), o1 = PHDR + (cv1 ? cl + 256 : 0);
+    hd = *reinterpret_cast<const float4*>(rec0 + (s0 + (hv ? lane : 0)) * stride);
 #pragma unroll
-    for (int j = 0; j < SPC / 4; ++j) {
-      const int sp = qtr + 4 * j;
-      const bool sv = sp < n;
-      const float* rp = rec0 + (s0 + (sv ? sp : 0)) * stride;
-      v0[j] = rp[o0];
-      v1[j] = rp[o1];
+    for (int k = 0; k < KPC; ++k) {
+      const int sp = qq + Q * k;
+      const bool sv = loader && sp < n;
+      xv[k] = *reinterpret_cast<const float4*>(rec0 + (s0 + (sv ? sp : 0)) * stride + 4 * (sv ? pp : 0));
     }
+    if (!hv) hd = make_float4(-INFINITY, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int j = 0; j < SPC / 4; ++j) {
-      const bool sv = qtr + 4 * j < n;
-      v0[j] = (sv && cv0) ? v0[j] : 0.f;
-      v1[j] = (sv && cv1) ? v1[j] : 0.f;
-    }
+    for (int k = 0; k < KPC; ++k)
+      if (!(loader && qq + Q * k < n)) xv[k] = make_float4(0.f, 0.f, 0.f, 0.f);
   };
   load_pass(0);
   // tables and R_V, consumed last
@@ -1275,49 +1268,42 @@ __global__ __launch_bounds__(CNT) void k_attn_combine(CombArgs a, const aatc_cal
   const int ncol_blob = a.lm ? D : 16 * (T4 + T2 + ((n1 + 15) >> 4));
   bool bad = PHDR + ncol_blob > prec || ncol_blob > MAXCOL || n4 < 0 || n2 < 0 || n1 < 0;
   const int ncol = bad ? 0 : ncol_blob;
-  const int c0 = cl, c1 = cl + 256;       // this thread's columns
 
   // L sums the rounded probabilities that weighted the code sums (it normalises the output);
-  // LE the unrounded ones (the lse: rounding each token to 14 bits would bias it low)
-  float M = -INFINITY, L = 0.f, LE = 0.f, acc0 = 0.f, acc1 = 0.f;
-  for (int s0 = 0; s0 < S; s0 += SPC) {
+  // LE the unrounded ones (the lse: rounding each token to 14 bits would bias it low).  Every
+  // wave reduces the pass's headers itself (lane s holds split s0 + s), so the passes need no
+  // barrier; a loader takes its splits' factors from the lanes that hold them.
+  float M = -INFINITY, L = 0.f, LE = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0; s0 < S; s0 += SPP) {
     if (s0 > 0) load_pass(s0);
-    if (wave == 0) {
-      const bool nan = hm != hm;
-      const float m = wave_max_x(hm);
-      const float nM = fmaxf(M, m);
-      const float w = (hm == -INFINITY || nM == -INFINITY) ? 0.f : exp2f(hm - nM);
-      if (lane < SPC) wsl[lane] = w;
-      const float l = wave_sum_x(w * hl), le = wave_sum_x(w * he);
-      const bool anynan = __ballot(nan) != 0;
-      if (lane == 0) {
-        red[0] = nM;
-        red[1] = l;
-        red[2] = anynan ? 1.f : 0.f;
-        red[3] = le;
-      }
-    }
-    __syncthreads();
-    const float nM = red[0];
+    const float hm = hd.x;
+    bad |= __ballot(hm != hm) != 0;
+    const float m = wave_max_x(hm);
+    const float nM = fmaxf(M, m);
+    const float w = (hm == -INFINITY || nM == -INFINITY) ? 0.f : exp2f(hm - nM);
+    const float l = wave_sum_x(w * hd.y), le = wave_sum_x(w * hd.z);
     const float fold = (M == -INFINITY) ? 0.f : exp2f(M - nM);
-    bad |= red[2] != 0.f;
-    L = L * fold + red[1];
-    LE = LE * fold + red[3];
+    L = L * fold + l;
+    LE = LE * fold + le;
     M = nM;
-    float p0 = 0.f, p1 = 0.f;
+    float4 pv = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int j = 0; j < SPC / 4; ++j) {
-      const float w = wsl[(qtr + 4 * j) & (SPC - 1)];
-      p0 = fmaf(w, v0[j], p0);
-      p1 = fmaf(w, v1[j], p1);
+    for (int k = 0; k < KPC; ++k) {
+      const int src = (qq + Q * k) & (SPC - 1);
+      const float wk = __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(w)));
+      pv.x = fmaf(wk, xv[k].x, pv.x);
+      pv.y = fmaf(wk, xv[k].y, pv.y);
+      pv.z = fmaf(wk, xv[k].z, pv.z);
+      pv.w = fmaf(wk, xv[k].w, pv.w);
     }
-    acc0 = acc0 * fold + p0;
-    acc1 = acc1 * fold + p1;
-    __syncthreads();                     // wsl and red are rewritten by the next pass
+    acc.x = fmaf(acc.x, fold, pv.x);
+    acc.y = fmaf(acc.y, fold, pv.y);
+    acc.z = fmaf(acc.z, fold, pv.z);
+    acc.w = fmaf(acc.w, fold, pv.w);
   }
-  // quarters -> column sums; tables -> LDS
-  if (c0 < MAXCOL) part4[qtr][c0] = acc0;
-  if (c1 < MAXCOL) part4[qtr][c1] = acc1;
+  // split groups -> column sums; tables -> LDS
+  if (loader) part[qq * P + pp] = acc;
   if (tid < D) {
     t_o[tid] = r_o;
     t_delta[tid] = r_d;
@@ -1326,7 +1312,13 @@ __global__ __launch_bounds__(CNT) void k_attn_combine(CombArgs a, const aatc_cal
   if (tid < 3 * D) t_cf[tid] = static_cast<int16_t>(r_cf);
   if (tid < AATC_MAX_FIELDS) t_fs[tid] = static_cast<uint8_t>(r_fs);
   __syncthreads();
-  if (tid < ncol) csum[tid] = (part4[0][tid] + part4[1][tid]) + (part4[2][tid] + part4[3][tid]);
+  if (tid < ncol) {
+    // column tid is component (tid + PHDR) % 4 of piece (tid + PHDR) / 4
+    const float* pf = reinterpret_cast<const float*>(part) + 4 * ((tid + PHDR) >> 2) + ((tid + PHDR) & 3);
+    float cs = 0.f;
+    for (int q = 0; q < Q; ++q) cs += pf[4 * P * q];
+    csum[tid] = cs;
+  }
   __syncthreads();
   // fold field columns into channel code sums; y = o + delta (c_bar - 2^(b-1) + 1/2); records
   // of the level pass hold each channel's weighted level sum: y = o + scale l_bar
