@@ -262,7 +262,7 @@ __device__ inline void lds_store(int* p, int v) {
 // the batch-16 layer the younger one finished its tiles 7 us later, and the merge waited for it.
 // At each stream step a wave publishes its step count and runs at the higher priority while it
 // is behind its partner.  (With copy waves on the same SIMDs, whose publishing the compute
-// waves wait for, it cost the headline 0.5 us; that form does without.)
+// waves wait for, it cost the headline 0.5 us; that form alternates by tile instead.)
 __device__ inline void balance_simd(Sync* sy, int wave, int step) {
   lds_store(&sy->prog[wave], step);
   const int other = __builtin_amdgcn_readfirstlane(lds_load_now(&sy->prog[wave ^ 4]));
@@ -794,6 +794,14 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
       }
       wave_sync_lds();
       if (NPROD == 0) balance_simd(&sy, wave, ++step);
+      // producer form: the flag round trips of balance_simd cost more than they even out (the
+      // copy waves share the SIMDs); the two compute waves of a SIMD take turns by tile instead
+      if (NPROD > 0) {
+        if ((g + (wave >> 2)) & 1)
+          __builtin_amdgcn_s_setprio(1);
+        else
+          __builtin_amdgcn_s_setprio(0);
+      }
       const int64_t tile = tw0 + rr;
       // opaque slot offset: per-(tile, tau, pair) addresses are not worth registers
       int kt = static_cast<int>((slot_of(wave, rr) - ring) + ((reinterpret_cast<uintptr_t>(kseq) + tile * kbytes) & 15));
@@ -988,6 +996,12 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
     }
     wave_sync_lds();
     if (NPROD == 0) balance_simd(&sy, wave, ++step);
+    if (NPROD > 0) {                     // and the younger wave leads the PV
+      if (wave >> 2)
+        __builtin_amdgcn_s_setprio(1);
+      else
+        __builtin_amdgcn_s_setprio(0);
+    }
     // PV on packed V fields (width-uniform column groups: w4 | w2 | w1); columns past a
     // class's field count read neighbouring words and are never used
 #pragma unroll
