@@ -613,7 +613,11 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
   }
 
   // ---- 1. prologue: q~ = R_K q, alpha, exponents, lse offsets, limb weights
-  // wave x (< 8) owns head slot x: q~ at channels lane and 64 + lane
+  // wave x (< 8) owns head slot x: q~ at channels lane and 64 + lane.  With three limbs (at most
+  // four head slots) and the rotation's barrier to order them, waves x and x + 4 share head slot
+  // x: both zero the limb rows beforehand, and each writes the planes of one half of the channels.
+  const bool halves = LIMBS == 3 && rot == AATC_ROT_KLT;
+  const int hslot = halves ? (wave & 3) : wave;
   float y0 = 0.f, y1 = 0.f;
   if (rot == AATC_ROT_KLT) {
     // row i of R_K: 4 threads per row, GH q heads per thread (the head slots a group can use:
@@ -649,9 +653,11 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
     if (qq == 0)
 #pragma unroll
       for (int g = 0; g < GH; ++g) qt[g * D + i] = part[g];
+    if (halves)
+      for (int k = tid; k < NP * 2 * 4 * 64; k += CW * 64) wa_lds[k] = 0;
     compute_barrier(&sy, phase, lane);
-    y0 = qt[wave * D + lane];
-    y1 = qt[wave * D + 64 + lane];
+    y0 = qt[hslot * D + lane];
+    y1 = qt[hslot * D + 64 + lane];
   } else {
     y0 = qs[wave * D + lane];
     y1 = qs[wave * D + 64 + lane];
@@ -663,8 +669,8 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
     }
   }
   {
-    // alpha, the lse offset and the weight exponent of head slot `wave` (zero past G)
-    const int g = wave;
+    // alpha, the lse offset and the weight exponent of head slot hslot (zero past G)
+    const int g = hslot;
     if (g >= G) {
       y0 = 0.f;
       y1 = 0.f;
@@ -696,20 +702,22 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
       frexpf(m, &e);
       e = LM::WBITS - e;                 // m * 2^e in [2^(WBITS-1), 2^WBITS)
     }
-    if (lane == 0) {
+    if (lane == 0 && (!halves || wave < 4)) {
       esc[g] = (m > 0.f) ? ldexpf(1.f, -e) : 0.f;
       if (s == 0 && g < G) a.offs[bh * 8 + g] = off;
     }
-    // limb operand rows of head slot g (the wave's own, so no other wave writes their dwords):
-    // LIMBS=2 rows g and 8+g; LIMBS=3 rows g, 4+g, 8+g for g < 4 and the spare row 8+g else.
-    // Operand dword (pair u, half hh, dword j, lane) holds bytes m of row lane%16, lane group
-    // lane/16 (the plane_base windows).  First zero them, then write each plane's limbs.
+    // limb operand rows of head slot g (the wave's own, or with halves its and its partner's,
+    // which writes other bytes): LIMBS=2 rows g and 8+g; LIMBS=3 rows g, 4+g, 8+g for g < 4 and
+    // the spare row 8+g else.  Operand dword (pair u, half hh, dword j, lane) holds bytes m of
+    // row lane%16, lane group lane/16 (the plane_base windows).  First zero them (with halves,
+    // every row before the rotation's barrier), then write each plane's limbs.
     const int nrows = (LIMBS == 3 && g >= 4) ? 1 : LIMBS;
     auto row_of = [&](int l) { return LIMBS == 2 ? 8 * l + g : (g < 4 ? 4 * l + g : 8 + g); };
-    for (int k = lane; k < nrows * NP * 32; k += 64) {
-      const int l = k / (NP * 32), c = (k >> 2) % (NP * 8), lg = k & 3;
-      wa_lds[c * 64 + lg * 16 + row_of(l)] = 0;
-    }
+    if (!halves)
+      for (int k = lane; k < nrows * NP * 32; k += 64) {
+        const int l = k / (NP * 32), c = (k >> 2) % (NP * 8), lg = k & 3;
+        wa_lds[c * 64 + lg * 16 + row_of(l)] = 0;
+      }
     // plane index of this lane's channels' bit 0: prefix sums of the bit counts, one ballot
     // per bit level
     const uint64_t below = (1ull << lane) - 1ull;
@@ -730,7 +738,7 @@ __global__ __launch_bounds__((CW + NPROD) * 64) void k_attn_main(AttnArgs a, con
       for (int kb = 0; kb < kmax; ++kb) {
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
-          if (kb < bir[r]) {
+          if (kb < bir[r] && (!halves || r == (wave >> 2))) {
             const int p = (r ? pb1 : pb0) + kb;
             const int u = p >> 7, pp = p & 127, q = pp & 31;
             const bool hp = HALF && u == NP - 1;
