@@ -262,7 +262,7 @@ __device__ inline void lds_store(int* p, int v) {
 // the batch-16 layer the younger one finished its tiles 7 us later, and the merge waited for it.
 // At each stream step a wave publishes its step count and runs at the higher priority while it
 // is behind its partner.  (With copy waves on the same SIMDs, whose publishing the compute
-// waves wait for, it cost the headline 0.5 us; that form alternates by tile instead.)
+// waves wait for, it cost the 128K 1.33-bit layer 0.5 us; that form alternates by tile instead.)
 __device__ inline void balance_simd(Sync* sy, int wave, int step) {
   lds_store(&sy->prog[wave], step);
   const int other = __builtin_amdgcn_readfirstlane(lds_load_now(&sy->prog[wave ^ 4]));
