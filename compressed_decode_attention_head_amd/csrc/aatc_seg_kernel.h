@@ -1,7 +1,7 @@
 // Merge kernel of multi-segment decode attention (gfx950).
 //
-// Page "SPHERICAL KV ..." (RDKV abstract): after prefill every token gets a bit width from
-// full precision down to zero.  Here a KV head's tokens are split into segments by tier --
+// Page "SPHERICAL KV ..." (RDKV abstract): after prefill each token is kept uncompressed,
+// coded at some width, or evicted.  Here a KV head's tokens are split into segments by tier --
 // coded segments (their own packed caches and bit allocations) and a raw bf16 segment in the
 // original basis; evicted tokens are in none.  One softmax runs over the union: softmax is
 // invariant to token order, so each segment (or split of one) yields a normalised output

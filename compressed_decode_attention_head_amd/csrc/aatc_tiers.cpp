@@ -1,7 +1,7 @@
 // Token tiers: a joint token x channel allocation of the bit budget (host, fp64).
 //
-// Page "SPHERICAL KV ..." (RDKV abstract): bit widths range from full precision down to zero
-// bits per token, chosen by reverse water-filling once after prefill.  Page "KV Cache
+// Page "SPHERICAL KV ..." (RDKV abstract): a token's width may be anything from uncompressed to
+// nothing (eviction), set by reverse water-filling once after prefill.  Page "KV Cache
 // Compression Through the Lens of Transform Coding" (Key points): the attention output's
 // distortion factors over tokens and channels.
 //

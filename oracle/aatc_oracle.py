@@ -8,8 +8,8 @@ Sources (cited by page title and section; no line numbers):
             Coding" -- Abstract: rotate the cache into a coordinate system computed from
             its own statistics (removing channel correlations), then spend the bit budget
             on the few channels that carry the signal.
-  [RDKV]    "SPHERICAL KV: ..." page, first abstract (RDKV): bit widths from full
-            precision down to zero bits per token or channel by reverse water-filling,
+  [RDKV]    "SPHERICAL KV: ..." page, first abstract (RDKV): each token or channel gets
+            a width between uncompressed and none at all, set by reverse water-filling,
             once after prefill; every decode step reads the cache from HBM again.
   [NOVA]    same page, third abstract (NOVA-KV): decode is bandwidth-bound; a fixed
             per-token bit count / fixed-width layout is required; the key transform that
