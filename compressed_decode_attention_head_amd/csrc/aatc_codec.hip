@@ -13,6 +13,8 @@
 // separately rounded fp64 sequence of the format definition; the GEMM uses explicit fma().
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include <cmath>
 #include <cstdint>
 
@@ -86,29 +88,6 @@ __device__ inline int v_bit(int t, int w, int b) {
   return 64 * G + 32 * (r >> 1) + 8 * m + 4 * (r & 1) + b;
 }
 
-// Token and value bit held by bit q of word j of a field string (the inverse of v_bit).
-__device__ inline int v_token(int j, int q, int w, int* bit) {
-  int G, r, m;
-  if (w == 1) {
-    G = 2 * j + (q & 1);
-    m = q >> 3;
-    r = (q & 7) >> 1;
-    *bit = 0;
-  } else if (w == 2) {
-    const int u = (q - (j & 1)) & 31;
-    G = j;
-    m = u >> 3;
-    r = (u & 7) >> 1;
-    *bit = u & 1;
-  } else {
-    G = j >> 1;
-    m = q >> 3;
-    r = 2 * (j & 1) + ((q & 7) >> 2);
-    *bit = q & 3;
-  }
-  return 16 * G + 4 * r + m;
-}
-
 struct CodecArgs {
   const aatc_calib* calib;     // n_kv_heads blobs
   uint32_t* codes;             // packed words
@@ -160,10 +139,18 @@ constexpr size_t kTTh = kTHf + 2 * AATC_D * AATC_MAX_BITS;  // fp64 Lloyd-Max th
 constexpr size_t kWave = kTTh + 8 * AATC_LEVELS;            // per wave: a half tile's K words or V codes
 constexpr int XS = D + 8;                                   // bf16 row stride of the GEMM's staged rows
 constexpr size_t kWaveBytes = HT * XS * 2;                  // 32 bf16 rows; >= 32 x 128 code bytes, B <= 1024 words
-constexpr size_t kEch = kWave + WAVES * kWaveBytes;         // GEMM: two 8 KB chunks of E
-constexpr size_t kEncodeLds = kEch + 2 * 2 * AATC_D * 4 * 8;
+constexpr int NECH = 4;                                     // GEMM: 8 KB chunks of E in LDS ...
+constexpr int ECH_AHEAD = NECH - 1;                         // ... copied this many steps ahead
+constexpr int SMALL_N = 8;                                  // GEMM form: launches of at most this many
+                                                            // tokens per sequence transform on the VALU
+constexpr size_t kEch = kWave + WAVES * kWaveBytes;
+constexpr size_t kEncodeLds = kEch + NECH * 2 * AATC_D * 4 * 8;
+// two workgroups per CU
+static_assert(2 * kEncodeLds <= 160 * 1024, "two encode workgroups fit one CU's LDS");
+static_assert(3 * SMALL_N * AATC_D * 8 <= NECH * 2 * AATC_D * 4 * 8, "small-launch products and inputs fit the E ring");
 static_assert(kTTh % 16 == 0 && kWave % 16 == 0 && kEch % 16 == 0, "LDS tables aligned");
 static_assert(AATC_D * AATC_MAX_BITS * 4 <= kWaveBytes, "a half tile's K words (B <= 1024) fit the wave area");
+static_assert(AATC_D * HT + AATC_D * AATC_MAX_BITS * 4 <= kWaveBytes, "V codes and the kept V words fit the wave area");
 
 // Lloyd-Max: z = (y - o) * (1/s) as separately rounded fp64 operations; the code is the number
 // of the b-bit table's 2^b - 1 ascending thresholds at or below z, by a b-step binary search
@@ -279,23 +266,44 @@ __device__ inline void write_k_words(const uint32_t* S, gu32* out, int B, int lo
 
 // A half tile's V words from its codes cs[channel][32 tokens]: word jj of field f is word
 // fw + half w + jj of the tile, holding the tokens the tile layout (include/aatc.h) gives it,
-// less 32 half; bits of tokens before lo keep their value.
+// less 32 half; bits of tokens before lo keep their value.  The words that hold such tokens are
+// all read first (one memory round trip, parked in the wave's free LDS at oldw), so a partial
+// half tile costs one round trip, not one per word.
 __device__ inline void write_v_words(const uint8_t* cs, gu32* out, int B, int half, int lo, int lane,
                                      const uint16_t* t_hf, const uint16_t* t_fw, const uint8_t* t_fs,
-                                     const uint8_t* t_fc) {
+                                     const uint8_t* t_fc, uint32_t* oldw) {
+  auto word_of = [&](int u) {        // tile word of half-tile word u
+    const int f = t_hf[u];
+    const int fw = t_fw[f], wd = t_fs[f] & 15;
+    return fw + half * wd + (u - fw / 2);
+  };
+  if (lo > 0) {
+    constexpr int PER = AATC_D * AATC_MAX_BITS / 64;    // words per lane, at most
+    uint32_t old[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int u = lane + 64 * k;
+      old[k] = out[word_of(u < B ? u : 0)];   // clamped, unconditional: the loads fly together
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k)
+      if (lane + 64 * k < B) oldw[lane + 64 * k] = old[k];
+  }
   for (int u = lane; u < B; u += 64) {
     const int f = t_hf[u];
     const int fw = t_fw[f], ws = t_fs[f], sh = ws >> 4, wd = ws & 15;
     const int jj = u - fw / 2;
     const uint8_t* col = cs + t_fc[f] * HT;
-    uint32_t word = 0;
+    uint32_t word = 0, keep = 0;          // keep: the bits of tokens before lo
     if (wd == 4) {
       // tokens 8 jj .. 8 jj + 7; token 8 jj + 4 rl + m at bits 8 m + 4 rl
       const uint2 q = *reinterpret_cast<const uint2*>(col + 8 * jj);
 #pragma unroll
       for (int n = 0; n < 8; ++n) {
         const uint32_t code = ((n < 4 ? q.x : q.y) >> (8 * (n & 3))) & 0xffu;
-        word |= ((code >> sh) & 15u) << (8 * (n & 3) + 4 * (n >> 2));
+        const int pos = 8 * (n & 3) + 4 * (n >> 2);
+        word |= ((code >> sh) & 15u) << pos;
+        if (8 * jj + n < lo) keep |= 15u << pos;
       }
     } else if (wd == 2) {
       // tokens 16 jj + n: bits (8 m + 2 r + b + jj % 2) mod 32
@@ -306,6 +314,7 @@ __device__ inline void write_v_words(const uint8_t* cs, gu32* out, int B, int ha
         const uint32_t v2 = ((uw[n >> 2] >> (8 * (n & 3))) >> sh) & 3u;
         const int base = (8 * (n & 3) + 2 * (n >> 2) + (jj & 1)) & 31;
         word |= ((v2 & 1u) << base) | ((v2 >> 1) << ((base + 1) & 31));
+        if (16 * jj + n < lo) keep |= (1u << base) | (1u << ((base + 1) & 31));
       }
     } else {
       // tokens n = 0..31: bit 8 m + 2 r + n / 16
@@ -315,19 +324,13 @@ __device__ inline void write_v_words(const uint8_t* cs, gu32* out, int B, int ha
 #pragma unroll
       for (int n = 0; n < 32; ++n) {
         const uint32_t v1 = ((uw[n >> 2] >> (8 * (n & 3))) >> sh) & 1u;
-        word |= v1 << (8 * (n & 3) + 2 * ((n >> 2) & 3) + (n >> 4));
+        const int pos = 8 * (n & 3) + 2 * ((n >> 2) & 3) + (n >> 4);
+        word |= v1 << pos;
+        if (n < lo) keep |= 1u << pos;
       }
     }
-    const int wt = fw + half * wd + jj;
-    if (lo > 0) {
-      uint32_t keep = 0;
-      for (int q = 0; q < 32; ++q) {
-        int bit;
-        if (v_token(half * wd + jj, q, wd, &bit) - HT * half < lo) keep |= 1u << q;
-      }
-      if (keep) word |= out[wt] & keep;
-    }
-    out[wt] = word;
+    if (lo > 0) word |= oldw[u] & keep;
+    out[fw + half * wd + jj] = word;
   }
 }
 
@@ -368,16 +371,28 @@ __device__ __attribute__((noinline)) void encode_waves(const CodecArgs& a) {
       for (int j = 0; j < wd; ++j) t_hf[fw / 2 + j] = static_cast<uint16_t>(f);   // fields are contiguous
     }
   __syncthreads();
-  if (tid < D) {
-    int s0 = 0;
-    for (int i = 0; i < tid; ++i) s0 += t_bits[i];
-    t_pb[tid] = static_cast<uint16_t>(s0);
+  if (wave == 0) {
+    // first plane of each channel: prefix sums of the bit counts, one ballot per bit level
+    // (channel lane and 64 + lane)
+    const int b0 = t_bits[lane], b1 = t_bits[64 + lane];
+    const uint64_t below = (1ull << lane) - 1ull;
+    int p0 = 0, p1 = 0, tot0 = 0;
+#pragma unroll
+    for (int k = 1; k <= AATC_MAX_BITS; ++k) {
+      const uint64_t m0 = __ballot(b0 >= k), m1 = __ballot(b1 >= k);
+      p0 += __popcll(m0 & below);
+      p1 += __popcll(m1 & below);
+      tot0 += __popcll(m0);
+    }
+    t_pb[lane] = static_cast<uint16_t>(p0);
+    t_pb[64 + lane] = static_cast<uint16_t>(tot0 + p1);
   }
   __syncthreads();
 
   unsigned char* warea = smem + kWave + wave * kWaveBytes;
   uint32_t* wb = reinterpret_cast<uint32_t*>(warea);           // K words of the half tile
   uint8_t* cs = warea;                                          // V codes, [channel][32 tokens]
+  uint32_t* oldw = reinterpret_cast<uint32_t*>(warea + D * HT);   // V words kept in part, B <= 1024
   uint16_t* xsb = reinterpret_cast<uint16_t*>(warea);           // GEMM bf16 rows, [32][XS]
   const int64_t xrow = b * a.s_b + h * a.s_h - a.tok_off * a.s_t;    // + absolute token * s_t
   const int64_t s_t = a.s_t;
@@ -497,13 +512,14 @@ __device__ __attribute__((noinline)) void encode_waves(const CodecArgs& a) {
         }
       }
       if (!isv) write_k_words(wb, out + half * B, B, lo, lane);
-      else write_v_words(cs, out, B, half, lo, lane, t_hf, t_fw, t_fs, t_fc);
+      else write_v_words(cs, out, B, half, lo, lane, t_hf, t_fw, t_fs, t_fc, oldw);
     }
   } else {
     // GEMM.  The four waves run in step, one half tile each per round, and share E through LDS:
-    // per step pair sp the workgroup copies E[., 32 g + 2 sp .. + 1] of every row and g (8 KB)
-    // into one of two buffers, one barrier, and each wave runs its 32 MFMAs on it while the next
-    // chunk is loaded.  Lane (tt, g) = (lane & 15, lane >> 4) feeds rows 16 tb + tt of its half
+    // chunk sp (step pair sp) is E[., 32 g + 2 sp .. + 1] of every row and g (8 KB).  Chunks go
+    // round a ring of NECH buffers, copied ECH_AHEAD steps before they are used, so the copies'
+    // L2 latency hides behind the MFMAs of the steps between; each step waits for its own chunk
+    // only, then one barrier, then its 32 MFMAs (16 when one token block has no token).  Lane (tt, g) = (lane & 15, lane >> 4) feeds rows 16 tb + tt of its half
     // tile, channels 32 g + s; accumulator block (tb, cb), register r: token 16 tb + tt, channel
     // 16 cb + 4 g + r.
     const int tt = lane & 15, g = lane >> 4;
@@ -526,8 +542,21 @@ __device__ __attribute__((noinline)) void encode_waves(const CodecArgs& a) {
     // that feeds row i of A feeds E row 16 cb + 4 (i & 3) + (i >> 2): the output of lane (tt, g),
     // register r is then channel 16 cb + 4 g + r, and a lane's four registers are adjacent channels
     const int arow = 4 * (tt & 3) + (tt >> 2);
-    copy_chunk(0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // the first ECH_AHEAD chunks; every later step copies the chunk ECH_AHEAD ahead (wrapping to
+    // the next round's first ones), so ECH_AHEAD chunks' copies (2 instructions each) are always
+    // in flight behind the one a step waits for
+    static_assert(ECH_AHEAD == 3, "the step's wait counts 2 * (ECH_AHEAD - 1) copy instructions");
+    // A launch of at most SMALL_N tokens per sequence (a decode step's append) takes the
+    // transform on the vector ALU instead: one workgroup per (batch, head) holds all of them (at
+    // most two half tiles), so its 256 threads share E = 128 rows x 2 halves, each thread one half
+    // row in registers (one memory round trip), and the products land in the E ring's LDS.  The
+    // MFMA form would stream all of E through 16 barrier steps for a 16-token block per token.
+    const bool small = a.n_tok <= SMALL_N;
+    double* ysm = reinterpret_cast<double*>(smem + kEch);      // [2 halves][SMALL_N][128] products
+    double* xsm = ysm + 2 * SMALL_N * D;                        // [SMALL_N][128] inputs
+    if (!small)
+#pragma unroll
+      for (int k = 0; k < ECH_AHEAD; ++k) copy_chunk(k, k);
     const int64_t first = a.tok_off / HT + static_cast<int64_t>(blockIdx.x) * WAVES;
     for (int64_t base = first; base < ht_end; base += hstep) {
       const int64_t ht = base + wave;
@@ -536,7 +565,7 @@ __device__ __attribute__((noinline)) void encode_waves(const CodecArgs& a) {
       if (act) half_range(ht, lo, hi);
       // bf16 rows of the half tile into the wave's area, [32][XS] (coalesced: 16-byte piece
       // 64 j + lane is row (64 j + lane) >> 4, column 8 ((64 j + lane) & 15))
-      if (act && bf16v && hi > lo) {
+      if (!small && act && bf16v && hi > lo) {
         u32x4 pr[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -549,20 +578,51 @@ __device__ __attribute__((noinline)) void encode_waves(const CodecArgs& a) {
           *reinterpret_cast<u32x4*>(xsb + (pc >> 4) * XS + 8 * (pc & 15)) = pr[j];
         }
       }
+      if (small) {
+        // all of the launch's tokens (one round: they span at most two half tiles), before any
+        // accumulator is live
+        const int nt = static_cast<int>(a.n_tok);
+        for (int e = tid; e < nt * D; e += THREADS)
+          xsm[e] = gload_x(xp, dtype, xrow + (a.tok_off + e / D) * s_t + (e % D));
+        const int ec = tid & (D - 1), eh = tid >> 7;              // E row, half of its columns
+        double ev[D / 2];
+        const gf64* erow = ((const gf64*)(c->E)) + ec * D + (D / 2) * eh;
+#pragma unroll
+        for (int j = 0; j < D / 2; ++j) ev[j] = erow[j];
+        __syncthreads();
+        for (int k = 0; k < nt; ++k) {
+          const double* xr = xsm + k * D + (D / 2) * eh;
+          double p0 = 0.0, p1 = 0.0;
+#pragma unroll
+          for (int j = 0; j < D / 2; j += 2) {
+            p0 = fma(ev[j], xr[j], p0);
+            p1 = fma(ev[j + 1], xr[j + 1], p1);
+          }
+          ysm[(eh * SMALL_N + k) * D + ec] = p0 + p1;
+        }
+        __syncthreads();
+      }
       f64x4 acc[2][8];
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
         for (int cb = 0; cb < 8; ++cb) acc[tb][cb] = f64x4{0.0, 0.0, 0.0, 0.0};
-      // one step pair: the barrier that publishes chunk sp (every wave waited for its own copies),
-      // the copies of the next chunk (or of the next round's first) into the other buffer, whose
-      // last readers passed this barrier, then 32 MFMAs
+      // token blocks with a token of the half tile in range (the others' MFMAs are skipped: their
+      // accumulators stay zero and no code is taken from them)
+      const bool blk0 = act && hi > lo && lo < 16, blk1 = act && hi > 16;
+      // one step pair: this wave's copies of chunk sp have landed once at most the 4 copy
+      // instructions of chunks sp + 1 and sp + 2 are outstanding (any vector-memory instruction
+      // issued since only makes the wait longer); the barrier then publishes everyone's, and its
+      // readers of the buffer chunk sp + 3 goes to (chunk sp - 1) have passed it.  The barrier is
+      // written out: a workgroup fence would also wait for the chunks still in flight.
       auto step_pair = [&](int sp, auto get_x) {
-        const double2* buf = ech + (sp & 1) * 512;
-        __syncthreads();
-        copy_chunk((sp + 1) & 15, (sp + 1) & 1);
-        if (act) {
-          const double* bd = reinterpret_cast<const double*>(buf);
+        const double2* buf = ech + (sp & (NECH - 1)) * 512;
+        asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        copy_chunk((sp + ECH_AHEAD) & 15, (sp + ECH_AHEAD) & (NECH - 1));
+        const double* bd = reinterpret_cast<const double*>(buf);
+        // the MFMAs of token blocks B0 and B1 (wave-uniform choice, one branch per step)
+        auto mfmas = [&](auto b0_tag, auto b1_tag) {
+          constexpr bool B0 = decltype(b0_tag)::value, B1 = decltype(b1_tag)::value;
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             double x0, x1;
@@ -570,14 +630,35 @@ __device__ __attribute__((noinline)) void encode_waves(const CodecArgs& a) {
 #pragma unroll
             for (int cb = 0; cb < 8; ++cb) {
               const double ev = bd[2 * ((16 * cb + arow) * 4 + g) + u];
-              acc[0][cb] = __builtin_amdgcn_mfma_f64_16x16x4f64(ev, x0, acc[0][cb], 0, 0, 0);
-              acc[1][cb] = __builtin_amdgcn_mfma_f64_16x16x4f64(ev, x1, acc[1][cb], 0, 0, 0);
+              if (B0) acc[0][cb] = __builtin_amdgcn_mfma_f64_16x16x4f64(ev, x0, acc[0][cb], 0, 0, 0);
+              if (B1) acc[1][cb] = __builtin_amdgcn_mfma_f64_16x16x4f64(ev, x1, acc[1][cb], 0, 0, 0);
             }
           }
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");       // this wave's copies have landed
+        };
+        using T_ = std::true_type;
+        using F_ = std::false_type;
+        if (blk0 && blk1) mfmas(T_(), T_());
+        else if (blk0) mfmas(T_(), F_());
+        else if (blk1) mfmas(F_(), T_());
       };
-      if (bf16v) {
+      if (small) {
+        // this wave's accumulators from the products
+        if (act) {
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb) {
+            const int t = 16 * tb + tt;
+            const int k = static_cast<int>(ht * HT + t - a.tok_off);    // launch-local token
+            if (t >= lo && t < hi)
+#pragma unroll
+              for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                  const int ch = 16 * cb + 4 * g + r;
+                  acc[tb][cb][r] = ysm[k * D + ch] + ysm[(SMALL_N + k) * D + ch];
+                }
+          }
+        }
+      } else if (bf16v) {
 #pragma unroll 1
         for (int sp = 0; sp < 16; ++sp)
           step_pair(sp, [&](int s, double& x0, double& x1) {
@@ -628,8 +709,11 @@ __device__ __attribute__((noinline)) void encode_waves(const CodecArgs& a) {
         }
       }
       if (!isv) write_k_words(wb, out + half * B, B, lo, lane);
-      else write_v_words(cs, out, B, half, lo, lane, t_hf, t_fw, t_fs, t_fc);
+      else write_v_words(cs, out, B, half, lo, lane, t_hf, t_fw, t_fs, t_fc, oldw);
     }
+    // the last steps' copies of the next round's first chunks: landed before the wave ends (no
+    // copy may write the LDS of a workgroup that follows on this CU)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
 }
 

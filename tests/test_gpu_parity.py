@@ -330,6 +330,30 @@ def test_append_matches_one_shot_pack():
     assert np.abs(out.cpu().numpy() - ref).max() <= ATOL_ATTN
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_small_appends_cross_half_tiles(dtype):
+    """Appends of 1 to 8 tokens (launches that small transform on the vector ALU instead of the
+    fp64 MFMA) that start and end on both sides of half-tile and tile boundaries, onto a KLT
+    cache: K and V words equal a one-shot encode of the same rows, and the codes match the
+    oracle's."""
+    torch = _torch()
+    case = Case(cfg=3, n_kv=2, group=4, n_tokens=200, batch=2, dtype=dtype, rotation="klt", bpe_k=4.0)
+    steps = [27, 1, 2, 3, 8, 8, 7, 8, 5, 1, 6, 8, 8, 8, 4, 96]
+    assert sum(steps) == case.n
+    for t in (synth.K, synth.V):
+        x = case.torch_x(t)
+        whole = case.make_cache(capacity=256)
+        whole.encode(t, x)
+        parts = case.make_cache(capacity=256)
+        off = 0
+        for n in steps:
+            parts.encode(t, x[:, :, off:off + n], token_offset=off)
+            off += n
+        torch.cuda.synchronize()
+        assert torch.equal(whole.codes(t), parts.codes(t)), t
+        _check_codes(case, parts, t)
+
+
 def test_device_error_paths():
     torch = _torch()
     from compressed_decode_attention_head_amd import api
