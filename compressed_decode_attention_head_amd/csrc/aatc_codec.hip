@@ -588,7 +588,7 @@ __device__ __attribute__((noinline)) void encode_waves(const CodecArgs& a) {
         double ev[D / 2];
         const gf64* erow = ((const gf64*)(c->E)) + ec * D + (D / 2) * eh;
 #pragma unroll
-        for (int j = 0; j < D / 2; ++j) ev[j] = erow[j];
+        for (int j = 0; j < D / 2; ++j) ev[j] = erow[j];           // E is 8-byte aligned in the blob
         __syncthreads();
         for (int k = 0; k < nt; ++k) {
           const double* xr = xsm + k * D + (D / 2) * eh;
@@ -642,22 +642,7 @@ __device__ __attribute__((noinline)) void encode_waves(const CodecArgs& a) {
         else if (blk1) mfmas(F_(), T_());
       };
       if (small) {
-        // this wave's accumulators from the products
-        if (act) {
-#pragma unroll
-          for (int tb = 0; tb < 2; ++tb) {
-            const int t = 16 * tb + tt;
-            const int k = static_cast<int>(ht * HT + t - a.tok_off);    // launch-local token
-            if (t >= lo && t < hi)
-#pragma unroll
-              for (int cb = 0; cb < 8; ++cb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                  const int ch = 16 * cb + 4 * g + r;
-                  acc[tb][cb][r] = ysm[k * D + ch] + ysm[(SMALL_N + k) * D + ch];
-                }
-          }
-        }
+        // (quantized straight from the products below)
       } else if (bf16v) {
 #pragma unroll 1
         for (int sp = 0; sp < 16; ++sp)
@@ -682,8 +667,25 @@ __device__ __attribute__((noinline)) void encode_waves(const CodecArgs& a) {
       gu32* out = seq_out + (ht >> 1) * (2 * B);
       if (!isv)
         for (int u = lane; u < B; u += 64) wb[u] = 0u;
+      if (small) {
+        // this wave's tokens of the launch, channels lane and 64 + lane of each: codes straight
+        // from the products (V: every other token of the half tile gets code 0, as below)
+        if (isv)
+          for (int u = lane; u < D * HT / 4; u += 64) reinterpret_cast<uint32_t*>(cs)[u] = 0u;
+        for (int t = lo; t < hi; ++t) {
+          const int k = static_cast<int>(ht * HT + t - a.tok_off);      // launch-local token
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
+          for (int hh = 0; hh < 2; ++hh) {
+            const int i = lane + 64 * hh;
+            const double y = ysm[k * D + i] + ysm[(SMALL_N + k) * D + i];
+            const uint32_t cd = static_cast<uint32_t>(code_of<false, LM>(y, qoi, qh, i, t_bits[i], t_th));
+            if (!isv) or_run(wb, t * B + t_pb[i], cd);
+            else cs[i * HT + t] = static_cast<uint8_t>(cd);
+          }
+        }
+      }
+#pragma unroll
+      for (int tb = 0; tb < 2 && !small; ++tb) {
         const int t = 16 * tb + tt;
         const bool in = t >= lo && t < hi;
 #pragma unroll
