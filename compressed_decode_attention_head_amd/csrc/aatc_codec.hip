@@ -147,7 +147,7 @@ constexpr size_t kEch = kWave + WAVES * kWaveBytes;
 constexpr size_t kEncodeLds = kEch + NECH * 2 * AATC_D * 4 * 8;
 // two workgroups per CU
 static_assert(2 * kEncodeLds <= 160 * 1024, "two encode workgroups fit one CU's LDS");
-static_assert(3 * SMALL_N * AATC_D * 8 <= NECH * 2 * AATC_D * 4 * 8, "small-launch products and inputs fit the E ring");
+static_assert(2 * SMALL_N * AATC_D * 8 <= NECH * 2 * AATC_D * 4 * 8, "small-launch products and inputs fit the E ring");
 static_assert(kTTh % 16 == 0 && kWave % 16 == 0 && kEch % 16 == 0, "LDS tables aligned");
 static_assert(AATC_D * AATC_MAX_BITS * 4 <= kWaveBytes, "a half tile's K words (B <= 1024) fit the wave area");
 static_assert(AATC_D * HT + AATC_D * AATC_MAX_BITS * 4 <= kWaveBytes, "V codes and the kept V words fit the wave area");
@@ -552,8 +552,8 @@ __device__ __attribute__((noinline)) void encode_waves(const CodecArgs& a) {
     // row in registers (one memory round trip), and the products land in the E ring's LDS.  The
     // MFMA form would stream all of E through 16 barrier steps for a 16-token block per token.
     const bool small = a.n_tok <= SMALL_N;
-    double* ysm = reinterpret_cast<double*>(smem + kEch);      // [2 halves][SMALL_N][128] products
-    double* xsm = ysm + 2 * SMALL_N * D;                        // [SMALL_N][128] inputs
+    double* ysm = reinterpret_cast<double*>(smem + kEch);      // [SMALL_N][128] products
+    double* xsm = ysm + SMALL_N * D;                            // [SMALL_N][128] inputs
     if (!small)
 #pragma unroll
       for (int k = 0; k < ECH_AHEAD; ++k) copy_chunk(k, k);
@@ -584,21 +584,55 @@ __device__ __attribute__((noinline)) void encode_waves(const CodecArgs& a) {
         const int nt = static_cast<int>(a.n_tok);
         for (int e = tid; e < nt * D; e += THREADS)
           xsm[e] = gload_x(xp, dtype, xrow + (a.tok_off + e / D) * s_t + (e % D));
-        const int ec = tid & (D - 1), eh = tid >> 7;              // E row, half of its columns
-        double ev[D / 2];
-        const gf64* erow = ((const gf64*)(c->E)) + ec * D + (D / 2) * eh;
+        // wave w holds E rows 32 w .. 32 w + 31, lane l columns l and 64 + l of each (each read is
+        // 512 contiguous bytes); a token's 32 row sums are then halved across the lanes five times (each lane
+        // keeps the half of the rows its lane bit selects and adds its partner's) and finished
+        // with lane l ^ 1: lane l ends with row 32 w + ((l >> 1) & 31)
+        double ev[64];
+        // the wave's first row in scalar registers, so each read is that base plus a scalar row
+        // offset plus the lane's column (no 64-bit address per read)
+        const uint64_t e0 = reinterpret_cast<uint64_t>(c->E) + static_cast<uint64_t>(32 * wave) * D * sizeof(double);
+        // (readfirstlane returns int: each half goes back through uint32_t, or a low word with
+        // bit 31 set would sign-extend over the high word)
+        const uint32_t e_hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(e0 >> 32)));
+        const uint32_t e_lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(e0)));
+        const gf64* eb = reinterpret_cast<const gf64*>((static_cast<uint64_t>(e_hi) << 32) | e_lo);
 #pragma unroll
-        for (int j = 0; j < D / 2; ++j) ev[j] = erow[j];           // E is 8-byte aligned in the blob
+        for (int r = 0; r < 32; ++r) {
+          ev[2 * r] = eb[r * D + lane];
+          ev[2 * r + 1] = eb[r * D + 64 + lane];
+        }
         __syncthreads();
         for (int k = 0; k < nt; ++k) {
-          const double* xr = xsm + k * D + (D / 2) * eh;
-          double p0 = 0.0, p1 = 0.0;
+          const double x0 = xsm[k * D + lane], x1 = xsm[k * D + 64 + lane];
+          // the first halving takes the products as it goes: rows r and r + 16 of the wave's
+          double v[16];
+          {
+            const bool up = (lane & 32) != 0;
 #pragma unroll
-          for (int j = 0; j < D / 2; j += 2) {
-            p0 = fma(ev[j], xr[j], p0);
-            p1 = fma(ev[j + 1], xr[j + 1], p1);
+            for (int r = 0; r < 16; ++r) {
+              const double lo_r = fma(ev[2 * r + 1], x1, ev[2 * r] * x0);
+              const double hi_r = fma(ev[2 * r + 33], x1, ev[2 * r + 32] * x0);
+              v[r] = (up ? hi_r : lo_r) + __shfl_xor(up ? lo_r : hi_r, 32);
+            }
           }
-          ysm[(eh * SMALL_N + k) * D + ec] = p0 + p1;
+          // one halving: the lanes with bit 2N set keep rows [N, 2N) of the current set
+          auto halve = [&](auto n_tag) {
+            constexpr int N = decltype(n_tag)::value;
+            const bool up = (lane & (2 * N)) != 0;
+#pragma unroll
+            for (int r = 0; r < N; ++r) {
+              const double send = up ? v[r] : v[r + N];
+              const double keep = up ? v[r + N] : v[r];
+              v[r] = keep + __shfl_xor(send, 2 * N);
+            }
+          };
+          halve(std::integral_constant<int, 8>());
+          halve(std::integral_constant<int, 4>());
+          halve(std::integral_constant<int, 2>());
+          halve(std::integral_constant<int, 1>());
+          const double y = v[0] + __shfl_xor(v[0], 1);
+          if ((lane & 1) == 0) ysm[k * D + 32 * wave + ((lane >> 1) & 31)] = y;
         }
         __syncthreads();
       }
@@ -677,7 +711,7 @@ __device__ __attribute__((noinline)) void encode_waves(const CodecArgs& a) {
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
             const int i = lane + 64 * hh;
-            const double y = ysm[k * D + i] + ysm[(SMALL_N + k) * D + i];
+            const double y = ysm[k * D + i];
             const uint32_t cd = static_cast<uint32_t>(code_of<false, LM>(y, qoi, qh, i, t_bits[i], t_th));
             if (!isv) or_run(wb, t * B + t_pb[i], cd);
             else cs[i * HT + t] = static_cast<uint8_t>(cd);
