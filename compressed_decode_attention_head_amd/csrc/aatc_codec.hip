@@ -269,7 +269,7 @@ __device__ inline void write_k_words(const uint32_t* S, gu32* out, int B, int lo
 // less 32 half; bits of tokens before lo keep their value.  The words that hold such tokens are
 // all read first (one memory round trip, parked in the wave's free LDS at oldw), so a partial
 // half tile costs one round trip, not one per word.
-__device__ inline void write_v_words(const uint8_t* cs, gu32* out, int B, int half, int lo, int lane,
+__device__ __attribute__((noinline)) void write_v_words(const uint8_t* cs, gu32* out, int B, int half, int lo, int lane,
                                      const uint16_t* t_hf, const uint16_t* t_fw, const uint8_t* t_fs,
                                      const uint8_t* t_fc, uint32_t* oldw) {
   auto word_of = [&](int u) {        // tile word of half-tile word u
@@ -289,44 +289,38 @@ __device__ inline void write_v_words(const uint8_t* cs, gu32* out, int B, int ha
     for (int k = 0; k < PER; ++k)
       if (lane + 64 * k < B) oldw[lane + 64 * k] = old[k];
   }
+  // Each of a column's 4-byte groups q (tokens 4 q .. 4 q + 3, one code byte each) lands in the
+  // word by one shift and mask: a w-bit field's code bits of token 4 q + m sit at bit 8 m + (a
+  // position set by q, jj and w) of its word.  The kept bits are the same positions of the
+  // tokens before lo, taken from bytes that are all ones for those tokens (ow).
+  auto ow = [&](int q) {
+    const int cnt = lo - 4 * q;
+    return cnt >= 4 ? 0xffffffffu : (cnt <= 0 ? 0u : (1u << (8 * cnt)) - 1u);
+  };
+  auto rotl = [](uint32_t x, int k) { return k ? (x << k) | (x >> (32 - k)) : x; };
   for (int u = lane; u < B; u += 64) {
     const int f = t_hf[u];
     const int fw = t_fw[f], ws = t_fs[f], sh = ws >> 4, wd = ws & 15;
     const int jj = u - fw / 2;
-    const uint8_t* col = cs + t_fc[f] * HT;
+    const uint32_t* col = reinterpret_cast<const uint32_t*>(cs + t_fc[f] * HT);
     uint32_t word = 0, keep = 0;          // keep: the bits of tokens before lo
     if (wd == 4) {
       // tokens 8 jj .. 8 jj + 7; token 8 jj + 4 rl + m at bits 8 m + 4 rl
-      const uint2 q = *reinterpret_cast<const uint2*>(col + 8 * jj);
-#pragma unroll
-      for (int n = 0; n < 8; ++n) {
-        const uint32_t code = ((n < 4 ? q.x : q.y) >> (8 * (n & 3))) & 0xffu;
-        const int pos = 8 * (n & 3) + 4 * (n >> 2);
-        word |= ((code >> sh) & 15u) << pos;
-        if (8 * jj + n < lo) keep |= 15u << pos;
-      }
+      word = ((col[2 * jj] >> sh) & 0x0f0f0f0fu) | (((col[2 * jj + 1] >> sh) & 0x0f0f0f0fu) << 4);
+      keep = (ow(2 * jj) & 0x0f0f0f0fu) | ((ow(2 * jj + 1) & 0x0f0f0f0fu) << 4);
     } else if (wd == 2) {
-      // tokens 16 jj + n: bits (8 m + 2 r + b + jj % 2) mod 32
-      const uint4 q = *reinterpret_cast<const uint4*>(col + 16 * jj);
-      const uint32_t uw[4] = {q.x, q.y, q.z, q.w};
+      // tokens 16 jj + 4 r + m: bits (8 m + 2 r + b + jj % 2) mod 32
 #pragma unroll
-      for (int n = 0; n < 16; ++n) {
-        const uint32_t v2 = ((uw[n >> 2] >> (8 * (n & 3))) >> sh) & 3u;
-        const int base = (8 * (n & 3) + 2 * (n >> 2) + (jj & 1)) & 31;
-        word |= ((v2 & 1u) << base) | ((v2 >> 1) << ((base + 1) & 31));
-        if (16 * jj + n < lo) keep |= (1u << base) | (1u << ((base + 1) & 31));
+      for (int r = 0; r < 4; ++r) {
+        word |= rotl((col[4 * jj + r] >> sh) & 0x03030303u, 2 * r + (jj & 1));
+        keep |= rotl(ow(4 * jj + r) & 0x03030303u, 2 * r + (jj & 1));
       }
     } else {
-      // tokens n = 0..31: bit 8 m + 2 r + n / 16
-      const uint4* q2 = reinterpret_cast<const uint4*>(col);
-      const uint4 qa = q2[0], qb = q2[1];
-      const uint32_t uw[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+      // tokens 4 q + m = 0..31: bit 8 m + 2 (q % 4) + q / 4
 #pragma unroll
-      for (int n = 0; n < 32; ++n) {
-        const uint32_t v1 = ((uw[n >> 2] >> (8 * (n & 3))) >> sh) & 1u;
-        const int pos = 8 * (n & 3) + 2 * ((n >> 2) & 3) + (n >> 4);
-        word |= v1 << pos;
-        if (n < lo) keep |= 1u << pos;
+      for (int q = 0; q < 8; ++q) {
+        word |= ((col[q] >> sh) & 0x01010101u) << (2 * (q & 3) + (q >> 2));
+        keep |= (ow(q) & 0x01010101u) << (2 * (q & 3) + (q >> 2));
       }
     }
     if (lo > 0) word |= oldw[u] & keep;
