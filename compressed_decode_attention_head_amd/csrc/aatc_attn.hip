@@ -329,14 +329,8 @@ aatc_status launch_merge(const aatc_cache* c, const Plan& p, int32_t n_q, const 
   cb.out = out;
   cb.lse = lse;
   cb.lm = p.lm ? 1 : 0;
-  // more workgroups than CUs: the lean form fits two per CU, so the grid runs in one round
-  const int64_t nwg = static_cast<int64_t>(group) * c->n_kv_heads * c->batch;
-  if (nwg > 256)
-    hipLaunchKernelGGL(k_attn_combine<true>, dim3(group, c->n_kv_heads, c->batch), dim3(CNT), 0, st, cb,
-                       static_cast<const aatc_calib*>(c->v_calib));
-  else
-    hipLaunchKernelGGL(k_attn_combine<false>, dim3(group, c->n_kv_heads, c->batch), dim3(CNT), 0, st, cb,
-                       static_cast<const aatc_calib*>(c->v_calib));
+  hipLaunchKernelGGL(k_attn_combine, dim3(group, c->n_kv_heads, c->batch), dim3(CNT), 0, st, cb,
+                     static_cast<const aatc_calib*>(c->v_calib));
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return aatc::fail(AATC_ERR_HIP, "decode_attn combine launch: %s", hipGetErrorString(err));
   return AATC_OK;

@@ -1226,11 +1226,7 @@ struct CombArgs {
 #ifdef AATC_ATTN_COMBINE_TU   // defined by the one translation unit that launches it
 // Every input of the merge is read with ordinary loads issued at once at kernel entry (records,
 // V tables, R_V), so the kernel pays about one memory round trip before its arithmetic.
-// LEAN (grids of more workgroups than the chip has CUs): registers capped so that two
-// workgroups share a CU (8 waves per SIMD), and a KLT blob's R_V rows are read where they are
-// used rather than ahead, in registers.
-template <bool LEAN>
-__global__ __launch_bounds__(CNT, LEAN ? 8 : 1) void k_attn_combine(CombArgs a, const aatc_calib* __restrict__ vcal) {
+__global__ __launch_bounds__(CNT) void k_attn_combine(CombArgs a, const aatc_calib* __restrict__ vcal) {
   __shared__ float4 part[CNT];            // [split group q][piece p] partial sums, q * P + p
   __shared__ float csum[MAXCOL];
   __shared__ float t_o[D], t_delta[D];
@@ -1282,7 +1278,7 @@ __global__ __launch_bounds__(CNT, LEAN ? 8 : 1) void k_attn_combine(CombArgs a, 
   // NOVA: R_V^T is E^-1, applied by the same GEMV as a KLT blob's R^T
   const int rot = vc->rotation == AATC_ROT_NOVA ? AATC_ROT_KLT : vc->rotation;
   float rv[16];
-  if (!LEAN && rot == AATC_ROT_KLT) {
+  if (rot == AATC_ROT_KLT) {
     const int j = tid & (D - 1), e8 = tid >> 7;
 #pragma unroll
     for (int k = 0; k < 16; ++k) rv[k] = vc->R32[(16 * e8 + k) * D + j];
@@ -1381,7 +1377,7 @@ __global__ __launch_bounds__(CNT, LEAN ? 8 : 1) void k_attn_combine(CombArgs a, 
     const int j = tid & (D - 1), e8 = tid >> 7;
     float o = 0.f;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) o = fmaf(LEAN ? vc->R32[(16 * e8 + k) * D + j] : rv[k], yt[16 * e8 + k], o);
+    for (int k = 0; k < 16; ++k) o = fmaf(rv[k], yt[16 * e8 + k], o);
     part8[e8][j] = o;
     __syncthreads();
     if (tid < D)

@@ -298,14 +298,7 @@ __device__ __attribute__((noinline)) void write_v_words(const uint8_t* cs, gu32*
     return cnt >= 4 ? 0xffffffffu : (cnt <= 0 ? 0u : (1u << (8 * cnt)) - 1u);
   };
   auto rotl = [](uint32_t x, int k) { return k ? (x << k) | (x >> (32 - k)) : x; };
-  // every word of the lane at once (clamped index, the store predicated), so the table look-ups
-  // of all of them are in flight together
-  constexpr int PER = AATC_D * AATC_MAX_BITS / 64;
-#pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    const int uu = lane + 64 * k;
-    if (64 * k >= B) break;                // wave-uniform
-    const int u = uu < B ? uu : 0;
+  for (int u = lane; u < B; u += 64) {
     const int f = t_hf[u];
     const int fw = t_fw[f], ws = t_fs[f], sh = ws >> 4, wd = ws & 15;
     const int jj = u - fw / 2;
@@ -331,7 +324,7 @@ __device__ __attribute__((noinline)) void write_v_words(const uint8_t* cs, gu32*
       }
     }
     if (lo > 0) word |= oldw[u] & keep;
-    if (uu < B) out[fw + half * wd + jj] = word;
+    out[fw + half * wd + jj] = word;
   }
 }
 
