@@ -46,7 +46,7 @@ def parse():
     p.add_argument("--no-loops", action="store_true", help="skip the append + decode loops")
     p.add_argument("--no-lloyd-max", action="store_true", help="skip the Lloyd-Max caches")
     p.add_argument("--only-headline", action="store_true", help="headline step and roofline only")
-    p.add_argument("--only", choices=["encode", "lloyd-max"], default=None,
+    p.add_argument("--only", choices=["encode", "lloyd-max", "append-loop"], default=None,
                    help="one side measurement alone (its JSON object only), for profiling")
     return p.parse_args()
 
@@ -420,12 +420,22 @@ def append_decode_loop(args, dev, st):
     e1.record(st)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
+    # the appends alone (the same tokens written again: encoding is idempotent)
+    e0.record(st)
+    for s_ in range(steps):
+        for cache, q, new, ws, out, lse in lays:
+            for t in (synth.K, synth.V):
+                cache.encode(t, new[t][:, :, s_:s_ + 1], token_offset=n0 + s_)
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms_enc = e0.elapsed_time(e1) / steps
     kb, vb = lays[0][0].k_bits, lays[0][0].v_bits
     avg_tokens = n0 + (steps + 1) / 2.0
     nbytes = cfg.n_layers * cfg.batch * cfg.n_kv_heads * avg_tokens * (kb + vb) / 8.0
     del lays
     return {"workload": cfg.name, "layers": cfg.n_layers, "steps": steps, "prefill_tokens": n0,
             "ms_per_step": round(ms, 4), "us_per_layer_step": round(ms * 1e3 / cfg.n_layers, 2),
+            "append_us_per_layer_step": round(ms_enc * 1e3 / cfg.n_layers, 2),
             "decode_tokens_per_s": round(cfg.batch * 1e3 / ms, 1),
             "cache_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
             "calls_per_layer_step": "aatc_encode K + aatc_encode V (1 token per sequence and head) + aatc_decode_attn",
@@ -693,7 +703,8 @@ def main():
         dev = torch.device("cuda", 0)
         torch.cuda.set_device(dev)
         st = torch.cuda.current_stream()
-        part = encode_rooflines(args, dev, st) if args.only == "encode" else lloyd_max_pass(args, dev, st)
+        part = {"encode": encode_rooflines, "lloyd-max": lloyd_max_pass,
+                "append-loop": append_decode_loop}[args.only](args, dev, st)
         print(json.dumps({"only": args.only, "result": part}))
         return
     if args.only_headline:
