@@ -311,6 +311,173 @@ aatc_status launch_partial(const aatc_cache* c, const Plan& p, const float* q, i
   return AATC_OK;
 }
 
+// Merge for launches with few splits per sequence (batch decoding, where the grid has one
+// workgroup per sequence and KV head or a few): one workgroup of 256 threads per (batch, KV head)
+// merges the records of all its q heads, so the KLT or NOVA R_V is read once for all of them
+// (the per-q-head merge reads it once per q head: 64 KB each) and the grid launches a sixteenth
+// of the waves.  Inputs, outputs and arithmetic as k_attn_combine; wave w takes q heads w, w + 4.
+constexpr int CH_THREADS = 256;
+constexpr int CH_MAXS = 8;                 // splits per sequence this form takes
+constexpr int CH_COLS = MAXCOL / 64;       // column sums per lane, at most
+
+__global__ __launch_bounds__(CH_THREADS) void k_attn_combine_heads(CombArgs a, const aatc_calib* __restrict__ vcal) {
+  __shared__ float csum[4][MAXCOL];        // per wave: column sums of its q head
+  __shared__ float yt[8][D];               // per q head: the rotated-domain output
+  __shared__ float part2[2][8][D];         // KLT: the two half sums of every output
+  __shared__ float hml[8][4];              // per q head: M, L, LE, bad
+  __shared__ float t_o[D], t_d[D];
+  __shared__ int t_bits[D];
+  __shared__ int16_t t_cf[3 * D];
+  __shared__ uint8_t t_fs[AATC_MAX_FIELDS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int G = a.group, S = a.S, prec = a.prec;
+  const int bh = b * a.n_kv + h;
+  const aatc_calib* vc = vcal + h;
+  const int64_t stride = static_cast<int64_t>(G) * prec;      // split s of q head g at s * stride
+  // ---- every load that does not depend on another, at once: one memory round trip
+  // this wave's first q head's records (lane s < S a header, every lane its columns of every
+  // split, from clamped addresses)
+  float4 hd0;
+  float x[CH_COLS][CH_MAXS];
+  auto load_head = [&](int g) {
+    const float* rec0 = a.part + (static_cast<int64_t>(bh) * S * G + g) * prec;
+    hd0 = *reinterpret_cast<const float4*>(rec0 + (lane < S ? lane : 0) * stride);
+#pragma unroll
+    for (int k = 0; k < CH_COLS; ++k)
+#pragma unroll
+      for (int sp = 0; sp < CH_MAXS; ++sp) {
+        const int col = lane + 64 * k;     // clamped to the record's end below
+        x[k][sp] = rec0[(sp < S ? sp : 0) * stride + PHDR + (PHDR + col < prec ? col : 0)];
+      }
+  };
+  if (wave < G) load_head(wave);
+  // tables, and for a KLT or NOVA blob this thread's 64 rows of R_V column j
+  const int ti = tid & (D - 1);
+  const float r_o = vc->o32[ti], r_d = a.lm ? vc->scale32[ti] : vc->delta32[ti];
+  const int r_b = vc->bits[ti];
+  const int c0 = vc->channel_field[tid], c1 = vc->channel_field[tid < D ? 2 * D + tid : 0];
+  const int f0 = vc->field_shift[tid], f1 = vc->field_shift[tid < D ? 2 * D + tid : 0];
+  const int rot = vc->rotation == AATC_ROT_NOVA ? AATC_ROT_KLT : vc->rotation;
+  const int j = tid & (D - 1), hf = tid >> 7;
+  float rv[64];
+  if (rot == AATC_ROT_KLT) {
+    const float* rcol = vc->R32 + (64 * hf) * D + j;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) rv[i] = rcol[i * D];
+  }
+  const int n4 = vc->n_fields4, n2 = vc->n_fields2, n1 = vc->n_fields1;
+  const int T4 = (n4 + 15) >> 4, T2 = (n2 + 15) >> 4;
+  const int ncol_blob = a.lm ? D : 16 * (T4 + T2 + ((n1 + 15) >> 4));
+  const bool bad0 = PHDR + ncol_blob > prec || ncol_blob > MAXCOL || n4 < 0 || n2 < 0 || n1 < 0;
+  const int ncol = bad0 ? 0 : ncol_blob;
+  int64_t seq = a.seq_lens ? static_cast<int64_t>(a.seq_lens[a.seq_per_head ? bh : b]) : a.max_seq;
+  seq = seq < 0 ? 0 : (seq > a.max_seq ? a.max_seq : seq);
+  if (tid < D) {
+    t_o[tid] = r_o;
+    t_d[tid] = r_d;
+    t_bits[tid] = r_b;
+    t_cf[2 * D + tid] = static_cast<int16_t>(c1);
+    t_fs[2 * D + tid] = static_cast<uint8_t>(f1);
+  }
+  t_cf[tid] = static_cast<int16_t>(c0);
+  t_fs[tid] = static_cast<uint8_t>(f0);
+  __syncthreads();
+
+  for (int g = wave; g < G; g += 4) {
+    if (g != wave) load_head(g);
+    const float4 hd = lane < S ? hd0 : make_float4(-INFINITY, 0.f, 0.f, 0.f);
+    const bool bad = bad0 || __ballot(hd.x != hd.x) != 0;
+    const float M = wave_max_x(hd.x);
+    const float w = (hd.x == -INFINITY || M == -INFINITY) ? 0.f : exp2f(hd.x - M);
+    const float L = wave_sum_x(w * hd.y), LE = wave_sum_x(w * hd.z);
+#pragma unroll
+    for (int k = 0; k < CH_COLS; ++k) {
+      const int col = lane + 64 * k;
+      float cs = 0.f;
+#pragma unroll
+      for (int sp = 0; sp < CH_MAXS; ++sp) {
+        const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), sp));   // 0 past S
+        cs = fmaf(ws, x[k][sp], cs);
+      }
+      if (col < ncol) csum[wave][col] = cs;
+    }
+    wave_sync_lds();
+    // fold field columns into channel code sums and dequantize (channels lane, 64 + lane)
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int i = lane + 64 * r;
+      const int bi = t_bits[i];
+      const float o = t_o[i];
+      float y = o;
+      if (a.lm) {
+        if (bi && L > 0.f && i < ncol) y = o + t_d[i] * (csum[wave][i] / L);
+      } else {
+        float cs = 0.f;
+        for (int kk = 0; kk < 3; ++kk) {
+          const int f = t_cf[3 * i + kk];
+          if (f < 0 || f >= AATC_MAX_FIELDS) break;
+          int col;
+          if (f < n4) col = f;
+          else if (f < n4 + n2) col = 16 * T4 + (f - n4);
+          else col = 16 * (T4 + T2) + (f - n4 - n2);
+          if (col < ncol) cs += ldexpf(csum[wave][col], t_fs[f]);
+        }
+        if (bi && L > 0.f) y = o + t_d[i] * (cs / L - (static_cast<float>(1 << (bi - 1)) - 0.5f));
+      }
+      yt[g][i] = y;
+    }
+    if (lane == 0) {
+      hml[g][0] = M;
+      hml[g][1] = L;
+      hml[g][2] = LE;
+      hml[g][3] = bad ? 1.f : 0.f;
+    }
+    wave_sync_lds();                       // csum is this wave's again for its next q head
+  }
+  __syncthreads();
+  // R_V^T for every q head: an FWHT per q head (wave w: q heads w, w + 4), or the GEMV with the
+  // rows held in registers: thread (output j, half of the rows) sums every q head
+  if (rot == AATC_ROT_WHT) {
+    for (int g = wave; g < G; g += 4) {
+      float x0 = yt[g][lane], x1 = yt[g][64 + lane];
+      fwht128(x0, x1, lane);
+      part2[0][g][lane] = x0 * 0.08838834764831845f;
+      part2[0][g][64 + lane] = x1 * 0.08838834764831845f;
+    }
+  } else if (rot == AATC_ROT_KLT) {
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      if (g < G) {
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < 64; ++i) acc = fmaf(rv[i], yt[g][64 * hf + i], acc);
+        part2[hf][g][j] = acc;
+      }
+    }
+  } else {
+    for (int e = tid; e < G * D; e += CH_THREADS) part2[0][e / D][e % D] = yt[e / D][e % D];
+  }
+  __syncthreads();
+  const bool empty = seq == 0;
+  for (int e = tid; e < G * D; e += CH_THREADS) {
+    const int g = e / D, jj = e % D;
+    const float res = rot == AATC_ROT_KLT ? part2[0][g][jj] + part2[1][g][jj] : part2[0][g][jj];
+    const float L = hml[g][1];
+    const bool bad = hml[g][3] != 0.f;
+    const int64_t qh = static_cast<int64_t>(b) * a.n_q + h * G + g;
+    a.out[qh * D + jj] = bad ? NAN : (L > 0.f ? res : (empty ? 0.f : NAN));
+  }
+  if (a.lse && tid < G) {
+    const int g = tid;
+    const float M = hml[g][0], L = hml[g][1], LE = hml[g][2];
+    const bool bad = hml[g][3] != 0.f;
+    const float l2 = bad ? NAN : (L > 0.f ? M + log2f(LE / static_cast<float>(PS)) + a.offs[bh * 8 + g]
+                                          : (empty ? -INFINITY : NAN));
+    a.lse[static_cast<int64_t>(b) * a.n_q + h * G + g] = l2 * 0.69314718055994530942f;
+  }
+}
+
 aatc_status launch_merge(const aatc_cache* c, const Plan& p, int32_t n_q, const int32_t* seq_lens, int seq_per_head,
                          int64_t max_seq, float* out, float* lse, void* ws, hipStream_t st) {
   const int group = n_q / c->n_kv_heads;
@@ -329,8 +496,12 @@ aatc_status launch_merge(const aatc_cache* c, const Plan& p, int32_t n_q, const 
   cb.out = out;
   cb.lse = lse;
   cb.lm = p.lm ? 1 : 0;
-  hipLaunchKernelGGL(k_attn_combine, dim3(group, c->n_kv_heads, c->batch), dim3(CNT), 0, st, cb,
-                     static_cast<const aatc_calib*>(c->v_calib));
+  if (p.S <= CH_MAXS && group <= 8)
+    hipLaunchKernelGGL(k_attn_combine_heads, dim3(c->n_kv_heads, c->batch), dim3(CH_THREADS), 0, st, cb,
+                       static_cast<const aatc_calib*>(c->v_calib));
+  else
+    hipLaunchKernelGGL(k_attn_combine, dim3(group, c->n_kv_heads, c->batch), dim3(CNT), 0, st, cb,
+                       static_cast<const aatc_calib*>(c->v_calib));
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return aatc::fail(AATC_ERR_HIP, "decode_attn combine launch: %s", hipGetErrorString(err));
   return AATC_OK;
