@@ -234,6 +234,29 @@ def test_nova_key_transform(cfg, group, bpe, v_rot, marginal):
     assert lerr <= 5e-3
 
 
+@pytest.mark.parametrize("batch,group", [(1, 4), (3, 8)])
+def test_identity_rotation_end_to_end(batch, group):
+    """Per-channel coding without a rotation (E = R = I): the encoder's GEMM form, the cache pass
+    and both merge forms' identity branch against the oracle.  Batch 3 leaves few splits per
+    sequence (the per-KV-head merge); batch 1 with 20K tokens, many (the per-q-head merge)."""
+    torch = _torch()
+    n = 20000 if batch == 1 else 300
+    case = Case(cfg=2, n_kv=2, group=group, n_tokens=n, batch=batch, rotation="identity", bpe_k=2.76)
+    cache = case.make_cache()
+    for t in (synth.K, synth.V):
+        cache.encode(t, case.torch_x(t))
+    for t in (synth.K, synth.V):
+        _check_codes(case, cache, t)
+    out, lse = cache.decode_attn(torch.from_numpy(case.q.astype(np.float32)).cuda(), case.n)
+    torch.cuda.synchronize()
+    ref, lref = case.oracle_attention()
+    err = np.abs(out.cpu().numpy() - ref).max()
+    lerr = np.abs(lse.cpu().numpy() - lref).max()
+    print("identity rotation batch", batch, "attn max abs err", err, "lse err", lerr, flush=True)
+    assert err <= ATOL_ATTN
+    assert lerr <= 5e-3
+
+
 @pytest.mark.parametrize("dtype,cfg", [("bf16", 4), ("f32", 1)])
 def test_encode_unaligned_rows_and_wht_appends(dtype, cfg):
     """Encoder paths the other cases do not take: rows that are not 16-byte aligned (a view with
