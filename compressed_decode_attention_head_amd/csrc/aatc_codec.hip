@@ -513,11 +513,11 @@ __device__ __attribute__((noinline)) void encode_waves(const CodecArgs& a) {
     // chunk sp (step pair sp) is E[., 32 g + 2 sp .. + 1] of every row and g (8 KB).  Chunks go
     // round a ring of NECH buffers, copied ECH_AHEAD steps before they are used, so the copies'
     // L2 latency hides behind the MFMAs of the steps between; each step waits for its own chunk
-    // only, then one barrier, then its 32 MFMAs (16 when one token block has no token).  Lane (tt, g) = (lane & 15, lane >> 4) feeds rows 16 tb + tt of its half
-    // tile, channels 32 g + s; accumulator block (tb, cb), register r: token 16 tb + tt, channel
-    // 16 cb + 4 g + r.
+    // only, then one barrier, then its 32 MFMAs (16 when one token block has no token).
+    // Lane (tt, g) = (lane & 15, lane >> 4) feeds rows 16 tb + tt of its half tile, channels
+    // 32 g + s; accumulator block (tb, cb), register r: token 16 tb + tt, channel 16 cb + 4 g + r.
     const int tt = lane & 15, g = lane >> 4;
-    double2* ech = reinterpret_cast<double2*>(smem + kEch);    // [2][128 rows][4 g]
+    double2* ech = reinterpret_cast<double2*>(smem + kEch);    // [NECH][128 rows][4 g]
     // chunk piece pc = 256 m + 64 wave + lane: row pc >> 2, g' = pc & 3, copied by global_load_lds
     // (no registers) to ech[buffer][pc]
     const gf64* esrc[2];
