@@ -363,7 +363,10 @@ size_t aatc_decode_attn_workspace_bytes(const aatc_cache* cache, int32_t n_q_hea
  *   blobs, both tensors <= AATC_MAX_ATTN_BITS) needs v_tiles <= 24.
  *   Errors: group > 8 or not an integer -> UNSUPPORTED; bits outside 0..8d -> BUDGET; bad
  *   pointers, v_tiles, seq length > capacity -> INVALID_ARGUMENT; workspace too small ->
- *   BUFFER_TOO_SMALL; launch -> HIP.
+ *   BUFFER_TOO_SMALL; launch -> HIP.  The status is the launch's: errors inside the kernels
+ *   reach the caller as values.  A blob that fails the kernels' header checks, and a workgroup
+ *   whose bounded wait on another wave gives up (the bound only keeps a fault from hanging the
+ *   GPU; a correct launch never reaches it), make the affected q heads' out and lse NaN.
  */
 aatc_status aatc_decode_attn(const aatc_cache* cache, const void* q_dev, aatc_dtype q_dtype, int32_t n_q_heads,
                              const int32_t* seq_lens_dev, int64_t max_seq_len, float softmax_scale,
