@@ -217,16 +217,19 @@ __device__ inline int qpos(int i) {
 // equals the floor on [0, 2^b - 1], and every value outside (NaN included) lands on the clamp's
 // side it belongs to, so the clamp runs on the truncated integer.
 // Lloyd-Max: the b-bit table's threshold count (quantize_lm).
-template <bool PAD, bool LM>
-__device__ inline int code_of(double y, const double2* qoi, const double* qh, int i, int bi, const double* thr) {
-  const int p = qpos<PAD>(i);
-  const double2 oi = qoi[p];
+template <bool LM>
+__device__ inline int code_with(double y, double2 oi, double half, int bi, const double* thr) {
   if (LM) return quantize_lm(y, oi.x, oi.y, bi, thr);
   double u = (y - oi.x) * oi.y;
-  u = u + qh[p];
+  u = u + half;
   const int top = (1 << bi) - 1;
   const int ci = cvt_i32_trunc(u);
   return ci < 0 ? 0 : (ci > top ? top : ci);
+}
+template <bool PAD, bool LM>
+__device__ inline int code_of(double y, const double2* qoi, const double* qh, int i, int bi, const double* thr) {
+  const int p = qpos<PAD>(i);
+  return code_with<LM>(y, qoi[p], qh[p], bi, thr);
 }
 
 // OR the run v (at most 64 bits, higher bits zero) into the bit string S at bit position pos;
@@ -712,26 +715,37 @@ __device__ __attribute__((noinline)) void encode_waves(const CodecArgs& a) {
           }
         }
       }
+      // per channel block, its four channels' tables once for both token blocks
 #pragma unroll
-      for (int tb = 0; tb < 2 && !small; ++tb) {
-        const int t = 16 * tb + tt;
-        const bool in = t >= lo && t < hi;
+      for (int cb = 0; cb < 8 && !small; ++cb) {
+        const int i0 = 16 * cb + 4 * g;
+        double2 oi[4];
+        double hh[4];
+        int bb[4];
 #pragma unroll
-        for (int cb = 0; cb < 8; ++cb) {
-          const int i0 = 16 * cb + 4 * g;
+        for (int r = 0; r < 4; ++r) {
+          oi[r] = qoi[qpos<false>(i0 + r)];
+          hh[r] = qh[qpos<false>(i0 + r)];
+          bb[r] = t_bits[i0 + r];
+        }
+        const int pb = t_pb[i0];
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+          const int t = 16 * tb + tt;
+          const bool in = t >= lo && t < hi;
           uint32_t cd[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            cd[r] = in ? static_cast<uint32_t>(code_of<false, LM>(acc[tb][cb][r], qoi, qh, i0 + r, t_bits[i0 + r], t_th)) : 0u;
+            cd[r] = in ? static_cast<uint32_t>(code_with<LM>(acc[tb][cb][r], oi[r], hh[r], bb[r], t_th)) : 0u;
           if (!isv) {
             uint64_t run = 0;
             int nb = 0;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               run |= static_cast<uint64_t>(cd[r]) << nb;
-              nb += t_bits[i0 + r];
+              nb += bb[r];
             }
-            or_run(wb, t * B + t_pb[i0], run);
+            or_run(wb, t * B + pb, run);
           } else {
 #pragma unroll
             for (int r = 0; r < 4; ++r) cs[(i0 + r) * HT + t] = static_cast<uint8_t>(cd[r]);
