@@ -353,14 +353,16 @@ def test_append_matches_one_shot_pack():
     assert np.abs(out.cpu().numpy() - ref).max() <= ATOL_ATTN
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_small_appends_cross_half_tiles(dtype):
+@pytest.mark.parametrize("dtype,rotation,quant", [("bf16", "klt", "uniform"), ("f32", "klt", "uniform"),
+                                                  ("bf16", "nova", "uniform"), ("bf16", "klt", "lloyd-max")])
+def test_small_appends_cross_half_tiles(dtype, rotation, quant):
     """Appends of 1 to 8 tokens (launches that small transform on the vector ALU instead of the
-    fp64 MFMA) that start and end on both sides of half-tile and tile boundaries, onto a KLT
-    cache: K and V words equal a one-shot encode of the same rows, and the codes match the
-    oracle's."""
+    fp64 MFMA) that start and end on both sides of half-tile and tile boundaries, onto KLT and
+    NOVA caches and Lloyd-Max codes: K and V words equal a one-shot encode of the same rows, and
+    the codes match the oracle's."""
     torch = _torch()
-    case = Case(cfg=3, n_kv=2, group=4, n_tokens=200, batch=2, dtype=dtype, rotation="klt", bpe_k=4.0)
+    case = Case(cfg=3, n_kv=2, group=4, n_tokens=200, batch=2, dtype=dtype, rotation=rotation, bpe_k=4.0,
+                quant_k=quant, quant_v=quant, v_rotation="klt")     # NOVA is a key transform
     steps = [27, 1, 2, 3, 8, 8, 7, 8, 5, 1, 6, 8, 8, 8, 4, 96]
     assert sum(steps) == case.n
     for t in (synth.K, synth.V):
