@@ -382,7 +382,7 @@ def folded_launch(args, cfg, layers, dev, st, n_tokens):
 def append_decode_loop(args, dev, st):
     """The batch-16 workload as a decode loop: 4 layers of 16 sequences x 8 KV heads with 8192
     prefill tokens (KLT, 4 bits per element), then 64 steps; each step appends one encoded K and V
-    token per sequence and head to every layer (aatc_encode at the next offset) and runs every
+    token per sequence and head to every layer (aatc_encode_kv at the next offset) and runs every
     layer's decode attention over the grown cache.  Eager launches, timed with HIP events."""
     import torch
     import synth
@@ -407,8 +407,7 @@ def append_decode_loop(args, dev, st):
 
     def run(s):
         for cache, q, new, ws, out, lse in lays:
-            for t in (synth.K, synth.V):
-                cache.encode(t, new[t][:, :, s:s + 1], token_offset=n0 + s)
+            cache.encode_kv(new[synth.K][:, :, s:s + 1], new[synth.V][:, :, s:s + 1], token_offset=n0 + s)
             cache.decode_attn(q, n0 + s + 1, workspace=ws, out=out, lse=lse)
 
     run(0)                                         # warm: the first step's encode rewrites the same token
@@ -424,8 +423,7 @@ def append_decode_loop(args, dev, st):
     e0.record(st)
     for s_ in range(steps):
         for cache, q, new, ws, out, lse in lays:
-            for t in (synth.K, synth.V):
-                cache.encode(t, new[t][:, :, s_:s_ + 1], token_offset=n0 + s_)
+            cache.encode_kv(new[synth.K][:, :, s_:s_ + 1], new[synth.V][:, :, s_:s_ + 1], token_offset=n0 + s_)
     e1.record(st)
     torch.cuda.synchronize()
     ms_enc = e0.elapsed_time(e1) / steps
@@ -438,7 +436,7 @@ def append_decode_loop(args, dev, st):
             "append_us_per_layer_step": round(ms_enc * 1e3 / cfg.n_layers, 2),
             "decode_tokens_per_s": round(cfg.batch * 1e3 / ms, 1),
             "cache_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
-            "calls_per_layer_step": "aatc_encode K + aatc_encode V (1 token per sequence and head) + aatc_decode_attn",
+            "calls_per_layer_step": "aatc_encode_kv (K and V, 1 token per sequence and head) + aatc_decode_attn",
             "timing": "eager launches, HIP events around all steps"}
 
 

@@ -98,6 +98,9 @@ def lib():
     L.aatc_calib_v_tiles.argtypes = [vp]
     L.aatc_encode.restype = ctypes.c_int
     L.aatc_encode.argtypes = [ctypes.POINTER(Cache), i32, vp, ctypes.c_int, ctypes.POINTER(i64), i64, i64, vp]
+    L.aatc_encode_kv.restype = ctypes.c_int
+    L.aatc_encode_kv.argtypes = [ctypes.POINTER(Cache), vp, vp, ctypes.c_int, ctypes.POINTER(i64), ctypes.POINTER(i64),
+                                 i64, i64, vp]
     L.aatc_decode.restype = ctypes.c_int
     L.aatc_decode.argtypes = [ctypes.POINTER(Cache), i32, i64, i64, vp, ctypes.c_int, ctypes.POINTER(i64), vp]
     L.aatc_decode_attn_workspace_bytes.restype = sz
@@ -146,7 +149,7 @@ def check(status):
 EXPORTS = ["aatc_status_string", "aatc_last_error", "aatc_calib_bytes", "aatc_bits_budget",
            "aatc_packed_bytes", "aatc_calibrate", "aatc_query_channel_weights", "aatc_calib_validate",
            "aatc_calib_v_tiles",
-           "aatc_encode", "aatc_decode", "aatc_decode_attn_workspace_bytes", "aatc_decode_attn", "aatc_decode_attn_noalloc",
+           "aatc_encode", "aatc_encode_kv", "aatc_decode", "aatc_decode_attn_workspace_bytes", "aatc_decode_attn", "aatc_decode_attn_noalloc",
            "aatc_probe_read_sink_bytes", "aatc_probe_read",
            "aatc_decode_attn_partial", "aatc_decode_attn_merge", "aatc_tier_distortions",
            "aatc_token_tiers", "aatc_decode_attn_segments_workspace_bytes", "aatc_decode_attn_segments",

@@ -335,6 +335,22 @@ class CompressedKVCache:
         N.check(N.lib().aatc_encode(ctypes.byref(self._struct), int(which), x.data_ptr(), self._dt(x), st,
                                     int(token_offset), int(x.shape[2]), _stream_ptr(stream)))
 
+    def encode_kv(self, k, v, token_offset=0, stream=None):
+        """aatc_encode_kv: K and V rows [batch, n_kv, n, 128] of one dtype, one launch."""
+        for x in (k, v):
+            if x.dim() != 4 or x.shape[0] != self.batch or x.shape[1] != self.n_kv or x.shape[3] != 128:
+                raise ValueError("k and v must be [batch, n_kv_heads, n, 128]")
+            if x.stride(3) != 1:
+                raise ValueError("channel stride must be 1")
+            if x.device != self.device:
+                raise ValueError("k and v must live on the cache's device")
+        if k.shape != v.shape or k.dtype != v.dtype:
+            raise ValueError("k and v must have one shape and dtype")
+        sk = (ctypes.c_int64 * 3)(k.stride(0), k.stride(1), k.stride(2))
+        sv = (ctypes.c_int64 * 3)(v.stride(0), v.stride(1), v.stride(2))
+        N.check(N.lib().aatc_encode_kv(ctypes.byref(self._struct), k.data_ptr(), v.data_ptr(), self._dt(k), sk, sv,
+                                       int(token_offset), int(k.shape[2]), _stream_ptr(stream)))
+
     def decode(self, which, token_offset, n_tokens, out_dtype="f32", stream=None):
         """aatc_decode: reconstruction x_hat [batch, n_kv, n, 128]."""
         import torch

@@ -332,7 +332,7 @@ __device__ __attribute__((noinline)) void write_v_words(const uint8_t* cs, gu32*
 }
 
 template <bool WHT, bool LM>
-__device__ __attribute__((noinline)) void encode_waves(const CodecArgs& a) {
+__device__ __attribute__((noinline)) void encode_waves(const CodecArgs& a, int b) {
   extern __shared__ __align__(16) unsigned char smem[];
   double2* qoi = reinterpret_cast<double2*>(smem + kQ);
   double* qh = reinterpret_cast<double*>(smem + kQ + 16 * kQRows);
@@ -344,7 +344,7 @@ __device__ __attribute__((noinline)) void encode_waves(const CodecArgs& a) {
   uint16_t* t_hf = reinterpret_cast<uint16_t*>(smem + kTHf);
   double* t_th = reinterpret_cast<double*>(smem + kTTh);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = blockIdx.y, b = blockIdx.z;
+  const int h = blockIdx.y;
   const aatc_calib* c = a.calib + h;
   const int B = c->total_bits, nf = c->n_fields;
   constexpr bool lm = LM;
@@ -762,21 +762,36 @@ __device__ __attribute__((noinline)) void encode_waves(const CodecArgs& a) {
 }
 
 // Two waves per SIMD: the GEMM form keeps 16 accumulator blocks (128 registers) per lane.
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 8))) void k_encode(CodecArgs a) {
+__device__ inline void encode_tensor(const CodecArgs& a, int b) {
   const aatc_calib* c = a.calib + blockIdx.y;
   if (c->magic != AATC_MAGIC) return;
   const bool lm = c->quantizer == AATC_QUANT_LLOYD_MAX;
   if (c->rotation == AATC_ROT_WHT) {
     if (lm)
-      encode_waves<true, true>(a);
+      encode_waves<true, true>(a, b);
     else
-      encode_waves<true, false>(a);
+      encode_waves<true, false>(a, b);
   } else {
     if (lm)
-      encode_waves<false, true>(a);
+      encode_waves<false, true>(a, b);
     else
-      encode_waves<false, false>(a);
+      encode_waves<false, false>(a, b);
   }
+}
+
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 8))) void k_encode(CodecArgs a) {
+  encode_tensor(a, blockIdx.z);
+}
+
+// K and V of the same token range in one launch: grid z = 2 x batch, K's workgroups first.
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 8))) void k_encode_kv(CodecArgs ak,
+                                                                                                  CodecArgs av,
+                                                                                                  int batch) {
+  const int z = blockIdx.z;
+  if (z < batch)
+    encode_tensor(ak, z);
+  else
+    encode_tensor(av, z - batch);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -858,9 +873,11 @@ aatc_status check_cache(const aatc_cache* c, int which) {
   return AATC_OK;
 }
 
-aatc_status launch_codec(bool encode, const aatc_cache* c, int which, const void* x, aatc_dtype dt,
-                         const int64_t* strides, int64_t off, int64_t n, void* stream) {
-  aatc::clear_error();
+// Validated arguments and grid width of one tensor's encode or decode; *none when there is
+// nothing to do (no tokens, or an encode of a 0-bit tensor).
+aatc_status codec_args(bool encode, const aatc_cache* c, int which, const void* x, aatc_dtype dt,
+                       const int64_t* strides, int64_t off, int64_t n, CodecArgs* out, int64_t* gx_out, bool* none) {
+  *none = false;
   aatc_status s = check_cache(c, which);
   if (s != AATC_OK) return s;
   if (!x || !strides) return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "null x/strides");
@@ -868,8 +885,10 @@ aatc_status launch_codec(bool encode, const aatc_cache* c, int which, const void
   if (off < 0 || n < 0 || off + n > c->capacity_tokens)
     return aatc::fail(AATC_ERR_INVALID_ARGUMENT, "token range [%lld, %lld) outside capacity %lld",
                       (long long)off, (long long)(off + n), (long long)c->capacity_tokens);
-  if (n == 0) return AATC_OK;
-  if (encode && (which ? c->v_bits : c->k_bits) == 0) return AATC_OK;   // 0 bits: no words to write
+  if (n == 0 || (encode && (which ? c->v_bits : c->k_bits) == 0)) {   // 0 bits: no words to write
+    *none = true;
+    return AATC_OK;
+  }
   CodecArgs a;
   a.calib = static_cast<const aatc_calib*>(which ? c->v_calib : c->k_calib);
   a.codes = static_cast<uint32_t*>(which ? c->v_codes : c->k_codes);
@@ -901,6 +920,19 @@ aatc_status launch_codec(bool encode, const aatc_cache* c, int which, const void
     gx = (halves + 3) / 4;
     if (gx > per) gx = per;
   }
+  *out = a;
+  *gx_out = gx;
+  return AATC_OK;
+}
+
+aatc_status launch_codec(bool encode, const aatc_cache* c, int which, const void* x, aatc_dtype dt,
+                         const int64_t* strides, int64_t off, int64_t n, void* stream) {
+  aatc::clear_error();
+  CodecArgs a;
+  int64_t gx = 0;
+  bool none = false;
+  const aatc_status s = codec_args(encode, c, which, x, dt, strides, off, n, &a, &gx, &none);
+  if (s != AATC_OK || none) return s;
   dim3 grid(static_cast<unsigned>(gx), c->n_kv_heads, c->batch);
   auto st = static_cast<hipStream_t>(stream);
   const size_t lds = encode ? kEncodeLds : kDecodeLds;
@@ -925,6 +957,34 @@ extern "C" {
 aatc_status aatc_encode(const aatc_cache* cache, int32_t which, const void* x_dev, aatc_dtype dtype,
                         const int64_t strides[3], int64_t token_offset, int64_t n_tokens, void* stream) {
   return launch_codec(true, cache, which, x_dev, dtype, strides, token_offset, n_tokens, stream);
+}
+
+aatc_status aatc_encode_kv(const aatc_cache* cache, const void* k_dev, const void* v_dev, aatc_dtype dtype,
+                           const int64_t k_strides[3], const int64_t v_strides[3], int64_t token_offset,
+                           int64_t n_tokens, void* stream) {
+  aatc::clear_error();
+  CodecArgs ak, av;
+  int64_t gk = 0, gv = 0;
+  bool nk = false, nv = false;
+  aatc_status s = codec_args(true, cache, 0, k_dev, dtype, k_strides, token_offset, n_tokens, &ak, &gk, &nk);
+  if (s != AATC_OK) return s;
+  s = codec_args(true, cache, 1, v_dev, dtype, v_strides, token_offset, n_tokens, &av, &gv, &nv);
+  if (s != AATC_OK) return s;
+  if (nk || nv) {                           // a 0-bit tensor (or no tokens): the other one alone
+    if (!nk) return launch_codec(true, cache, 0, k_dev, dtype, k_strides, token_offset, n_tokens, stream);
+    if (!nv) return launch_codec(true, cache, 1, v_dev, dtype, v_strides, token_offset, n_tokens, stream);
+    return AATC_OK;
+  }
+  // the grid width depends on the token range and the cache shape only: the same for both
+  const dim3 grid(static_cast<unsigned>(gk), cache->n_kv_heads, 2 * cache->batch);
+  const hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_encode_kv),
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kEncodeLds));
+  if (ea != hipSuccess) return aatc::fail(AATC_ERR_HIP, "LDS attribute: %s", hipGetErrorString(ea));
+  hipLaunchKernelGGL(k_encode_kv, grid, dim3(THREADS), kEncodeLds, static_cast<hipStream_t>(stream), ak, av,
+                     static_cast<int>(cache->batch));
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return aatc::fail(AATC_ERR_HIP, "encode_kv launch: %s", hipGetErrorString(e));
+  return AATC_OK;
 }
 
 aatc_status aatc_decode(const aatc_cache* cache, int32_t which, int64_t token_offset, int64_t n_tokens,

@@ -319,6 +319,19 @@ aatc_status aatc_encode(const aatc_cache* cache, int32_t which, const void* x_de
                         void* stream);
 
 /*
+ * aatc_encode_kv -- device, async.  [page "SPHERICAL KV ...", RDKV abstract: the bit allocation
+ * is fixed after prefill, and every decode step then appends a token's K and V]  aatc_encode of
+ * K (k_dev, k_strides) and of V (v_dev, v_strides) over the same tokens [token_offset,
+ * token_offset + n_tokens), in one launch: a decode step's append costs one launch, and the two
+ * tensors' memory round trips overlap.  Results are those of the two aatc_encode calls, word for
+ * word.  dtype applies to both; a 0-bit tensor is skipped as aatc_encode skips it.
+ *   Errors: as aatc_encode, for either tensor (K checked first).
+ */
+aatc_status aatc_encode_kv(const aatc_cache* cache, const void* k_dev, const void* v_dev, aatc_dtype dtype,
+                           const int64_t k_strides[3], const int64_t v_strides[3], int64_t token_offset,
+                           int64_t n_tokens, void* stream);
+
+/*
  * aatc_decode -- device, async.  Reconstructs x_hat = R^T y_hat (fp64, stored as F32 or BF16)
  * for tokens [token_offset, token_offset + n_tokens) of every (b,h) into out_dev with the
  * same stride convention as aatc_encode.  Used for checks and for promoting tokens back to

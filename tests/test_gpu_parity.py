@@ -379,6 +379,27 @@ def test_small_appends_cross_half_tiles(dtype, rotation, quant):
         _check_codes(case, parts, t)
 
 
+@pytest.mark.parametrize("rotation,cfg,bpe,marginal", [("klt", 3, 4.0, "gauss"), ("wht", 4, 1.33, "t3")])
+def test_encode_kv_equals_two_encodes(rotation, cfg, bpe, marginal):
+    """aatc_encode_kv (K and V in one launch) writes the same words as aatc_encode of K and of V,
+    through a prefill and appends of 1, 7 and 3 tokens (the small-launch form for KLT) and a
+    longer one."""
+    torch = _torch()
+    case = Case(cfg=cfg, n_kv=2, group=4, n_tokens=300, batch=2, rotation=rotation, bpe_k=bpe, marginal=marginal)
+    xk, xv = case.torch_x(synth.K), case.torch_x(synth.V)
+    two, one = case.make_cache(capacity=320), case.make_cache(capacity=320)
+    off = 0
+    for n in (100, 1, 7, 3, 189):
+        two.encode(synth.K, xk[:, :, off:off + n], token_offset=off)
+        two.encode(synth.V, xv[:, :, off:off + n], token_offset=off)
+        one.encode_kv(xk[:, :, off:off + n], xv[:, :, off:off + n], token_offset=off)
+        off += n
+    torch.cuda.synchronize()
+    for t in (synth.K, synth.V):
+        assert torch.equal(two.codes(t), one.codes(t)), t
+        _check_codes(case, one, t)
+
+
 def test_device_error_paths():
     torch = _torch()
     from compressed_decode_attention_head_amd import api
