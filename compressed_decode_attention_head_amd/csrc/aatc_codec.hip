@@ -6,9 +6,10 @@
 // coordinate system; page "Ablation, Statistical Inference, and Validation for KV-Cache
 // Compression" (first abstract): a scalar MSE quantizer after the rotation.
 //
-// One workgroup owns one 64-token tile of one (batch, KV head) sequence, so every packed
-// word has exactly one writer.  Rotation and quantization run in fp64 so that codes agree
-// with an fp64 definition except for values within rounding distance of a bin edge.
+// Every packed word has exactly one writer: in the encoder one wave per 32-token half tile,
+// in the decoder one workgroup per 64-token tile.  Rotation and quantization run in fp64 so
+// that codes agree with an fp64 definition except for values within rounding distance of a
+// bin edge.
 // This file is compiled with -ffp-contract=off: the quantizer expression must be the
 // separately rounded fp64 sequence of the format definition; the GEMM uses explicit fma().
 #include <hip/hip_runtime.h>
@@ -104,7 +105,8 @@ struct CodecArgs {
 };
 
 // ---------------------------------------------------------------------------------------
-// Encode.  Grid (G, KV heads, batch) of 4-wave workgroups.  A workgroup loads its head's
+// Encode.  Grid (G, KV heads, batch) of 4-wave workgroups (K and V in one launch: batch
+// doubled, K's workgroups first).  A workgroup loads its head's
 // quantizer and packing tables into LDS once (its only barriers); after that every wave works
 // alone on half tiles: 32 consecutive tokens of one sequence, whose packed words no other half
 // tile touches (K: the 32 B bits of the half tile are B whole words; V: w words of every w-bit
@@ -112,15 +114,17 @@ struct CodecArgs {
 //  1. rows straight from memory into registers (16-byte aligned bf16 rows of a Walsh-Hadamard
 //     blob: the next half tile's rows are in flight while this one computes);
 //  2. y = E x in fp64:
-//     - Walsh-Hadamard: lane = (token, half of the channels, split on channel bit 3); six
-//       butterfly stages in registers over the other channel bits and one with the partner lane
-//       (a DPP quad permutation), all exact on bf16 rows, then one multiply by the blob's
-//       1/sqrt(d) (its R[0]);
+//     - Walsh-Hadamard: lane = (token, quarter of the channels, on channel bits 3 and 4); five
+//       butterfly stages in registers over the other channel bits and two across the quad (DPP
+//       moves), all exact on bf16 rows, then one multiply by the blob's 1/sqrt(d) (its R[0]);
 //     - other rotations: v_mfma_f64_16x16x4f64 with E as the A operand (16 output channels x 4
 //       input channels) and the rows as B (4 input channels x 16 tokens), two token blocks x 8
 //       channel blocks of accumulators per wave.  The contraction runs over the input channels
 //       in the order 32 g + s (g = the lane's k slot, s = the step), so each lane reads one
-//       contiguous 32-channel chunk of its rows and one of each E row it needs;
+//       contiguous 32-channel chunk of its rows and one of each E row it needs; E streams
+//       through a ring of LDS chunks shared by the four waves;
+//     - launches of at most 8 tokens per sequence (decode-step appends): the same product on
+//       the vector ALU, E rows in registers, all of the workgroup's tokens at once;
 //  3. the quantizer in fp64, separately rounded (this file is built without contraction);
 //  4. packing in the wave's own LDS area: K runs of consecutive channels OR-ed into the half
 //     tile's token-major bit string, V codes stored channel-major and gathered per word;
