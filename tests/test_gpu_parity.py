@@ -330,6 +330,12 @@ def test_zero_bit_tensors():
         out, _ = cache.decode_attn(torch.from_numpy(case.q.astype(np.float32)).cuda(), case.n)
         ref, _ = case.oracle_attention()
         assert np.abs(out.cpu().numpy() - ref).max() <= ATOL_ATTN, (bk, bv)
+        # the fused K+V encode skips the 0-bit tensor the same way
+        fused = case.make_cache()
+        fused.encode_kv(case.torch_x(synth.K), case.torch_x(synth.V))
+        torch.cuda.synchronize()
+        for t in (synth.K, synth.V):
+            assert torch.equal(fused.codes(t), cache.codes(t)), (bk, bv, t)
 
 
 def test_append_matches_one_shot_pack():
@@ -408,6 +414,9 @@ def test_device_error_paths():
     x = case.torch_x(synth.K)
     with pytest.raises(api.AatcError) as e:
         cache.encode(0, x, token_offset=10)            # beyond capacity
+    assert e.value.name == "AATC_ERR_INVALID_ARGUMENT"
+    with pytest.raises(api.AatcError) as e:
+        cache.encode_kv(x, case.torch_x(synth.V), token_offset=10)
     assert e.value.name == "AATC_ERR_INVALID_ARGUMENT"
     q = torch.zeros((1, 9, 128), dtype=torch.float32, device="cuda")
     with pytest.raises(api.AatcError) as e:
