@@ -687,7 +687,7 @@ def tiered_append_loop(cfg, calls, raws, dev, st):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+        print("bench.py measures one GPU only: the library has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
     import torch

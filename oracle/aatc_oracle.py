@@ -20,7 +20,7 @@ Sources (cited by page title and section; no line numbers):
   [OCTOPUS] same page, third abstract: keys are reconstructed on the fly inside the
             attention kernel instead of being materialized.
 
-Where the pages are silent the readings below are used (each is listed in the design doc):
+Where the pages are silent the readings below are used:
 centred covariance with 1/M, eigenvectors in descending eigenvalue order with a sign
 rule, Sylvester-ordered WHT, budget B = floor(b*d + 1/2) bits per vector, greedy integer
 water-filling with a fixed tie order, a mid-rise uniform quantizer with the Gaussian
